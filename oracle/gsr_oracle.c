@@ -1,0 +1,962 @@
+/*
+ * gsr_oracle.c -- CPU oracle for the tile-binned Gaussian-splat render and the
+ * analytic score replay.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test-suite, the package smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code with the HIP path.
+ *
+ * Source of the method: the page "Research Proposal: Renderer Score Tokens for
+ * Recurrent Gaussian Splatting" -- section "Two-Stage Algorithm" (Stage 1
+ * standard render, residual equation; Stage 2 analytic score replay, suffix
+ * equation, masks), section "Exact Score Operators" (alpha/weight definitions,
+ * residual-suffix contrast and support, opacity-logit score, SH score, 2D
+ * Gaussian kernel and its centre gradient, projected-centre mean score,
+ * projection Jacobian, cross-view weight, covector pullback, conditioning
+ * matrix and its statistics, appearance aggregation) and "Final Token and
+ * Updater" (token layout).  The 3D Gaussian primitive is the one of the ATSplat
+ * summary page ("前置知识: 3DGS").
+ *
+ * How it computes:
+ *  - Every floating-point DECISION (culling, radius, tile rectangle, the SH
+ *    colour clamp, alpha skip, alpha clamp, early termination, the suffix
+ *    denominator mask) is taken in float32 following the written canonical
+ *    operation order, so that an independent GPU implementation of the same
+ *    order reaches the same integers.  The float32 exponential used by those
+ *    decisions is the published range-reduction + Taylor method (exp2 split
+ *    into an integer power and a fraction in [-1/2, 1/2], degree-7 Taylor
+ *    polynomial of 2^f in Horner form with fused multiply-adds).
+ *  - Every VALUE (colours, alpha, transmittance, suffix composites, scores,
+ *    tokens) is computed in float64 from float64 copies of the inputs, with
+ *    the float32 decisions frozen.  This is also what makes the finite
+ *    difference pins exact: the loss is a smooth function of the values once
+ *    the contributor sets and clamp states are fixed.
+ *  - Candidate lists are brute force (every Gaussian whose tile rectangle
+ *    holds the tile), ordered by (depth bits, Gaussian index).
+ *  - The suffix composite is computed by explicit back-to-front summation,
+ *    never by the subtraction formula of the replay.
+ *  - Scores are the literal per-pixel sums of the score operators; tokens are
+ *    the literal cross-view formulas; eigenvalues by cyclic Jacobi rotations.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ----------------------------------------------------------------------------
+ * Fixed readings shared with the GPU path by specification (not by code).
+ * ------------------------------------------------------------------------- */
+#define TILE 16
+#define ALPHA_MAX_F 0.99f
+#define ALPHA_MAX_D 0.99
+#define T_MIN_F 1e-4f
+#define DILATION_F 0.3f
+#define EIG_FLOOR_F 0.1f
+#define FOV_CLAMP_F 1.3f
+#define E_CUTOFF_F (-8.0f)
+
+static float g_alpha_min;     /* float32 nearest to 1/255 */
+static float g_exp2_coef[8];  /* float32 nearest to ln(2)^j / j! */
+static float g_nl2e;          /* float32 nearest to -log2(e) */
+static float g_nhl2e;         /* float32 nearest to -log2(e) / 2 */
+static float g_sh32[16];      /* float32 SH normalisation constants (signed) */
+static double g_sh64[16];
+
+static void init_constants(void)
+{
+    static int done = 0;
+    if (done) return;
+    g_alpha_min = (float)(1.0L / 255.0L);
+    long double c = 1.0L;
+    const long double ln2 = 0.693147180559945309417232121458176568L;
+    for (int j = 0; j < 8; ++j) {
+        g_exp2_coef[j] = (float)c;
+        c = c * ln2 / (long double)(j + 1);
+    }
+    const long double log2e = 1.442695040888963407359924681001892137L;
+    g_nl2e = (float)(-log2e);
+    g_nhl2e = (float)(-0.5L * log2e);
+    const long double pi = 3.141592653589793238462643383279502884L;
+    long double k[16];
+    /* real spherical harmonics, l <= 3, m = -l..l, classic graphics sign convention */
+    k[0] = 0.5L * sqrtl(1.0L / pi);
+    k[1] = -sqrtl(3.0L / (4.0L * pi));
+    k[2] = sqrtl(3.0L / (4.0L * pi));
+    k[3] = -sqrtl(3.0L / (4.0L * pi));
+    k[4] = 0.5L * sqrtl(15.0L / pi);
+    k[5] = -0.5L * sqrtl(15.0L / pi);
+    k[6] = 0.25L * sqrtl(5.0L / pi);
+    k[7] = -0.5L * sqrtl(15.0L / pi);
+    k[8] = 0.25L * sqrtl(15.0L / pi);
+    k[9] = -0.25L * sqrtl(35.0L / (2.0L * pi));
+    k[10] = 0.5L * sqrtl(105.0L / pi);
+    k[11] = -0.25L * sqrtl(21.0L / (2.0L * pi));
+    k[12] = 0.25L * sqrtl(7.0L / pi);
+    k[13] = -0.25L * sqrtl(21.0L / (2.0L * pi));
+    k[14] = 0.25L * sqrtl(105.0L / pi);
+    k[15] = -0.25L * sqrtl(35.0L / (2.0L * pi));
+    for (int i = 0; i < 16; ++i) {
+        g_sh32[i] = (float)k[i];
+        g_sh64[i] = (double)k[i];
+    }
+    done = 1;
+}
+
+/* float32 2^e for e in [-8, 1/2]: e = k + f with k = rint(e) and |f| <= 1/2 exact,
+ * 2^f by the degree-7 Taylor polynomial in Horner form with fused multiply-adds,
+ * then an exact scaling by 2^k. */
+float orc_exp2f(float e)
+{
+    init_constants();
+    float k = rintf(e);
+    float f = e - k;
+    float p = g_exp2_coef[7];
+    for (int j = 6; j >= 0; --j) p = fmaf(p, f, g_exp2_coef[j]);
+    return ldexpf(p, (int)k);
+}
+
+void orc_exp2f_array(const float* in, float* out, int64_t n)
+{
+    init_constants();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_exp2f(in[i]);
+}
+
+void orc_constants(float* out /* [28] */)
+{
+    init_constants();
+    out[0] = g_alpha_min;
+    for (int j = 0; j < 8; ++j) out[1 + j] = g_exp2_coef[j];
+    out[9] = g_nl2e;
+    out[10] = g_nhl2e;
+    for (int i = 0; i < 16; ++i) out[11 + i] = g_sh32[i];
+    out[27] = 0.0f;
+}
+
+/* ----------------------------------------------------------------------------
+ * SH basis (degree <= 3) in float32 canonical order and in float64.
+ * ------------------------------------------------------------------------- */
+static void sh_basis32(float x, float y, float z, int d, float* B)
+{
+    const float* K = g_sh32;
+    B[0] = K[0];
+    if (d <= 1) return;
+    B[1] = K[1] * y;
+    B[2] = K[2] * z;
+    B[3] = K[3] * x;
+    if (d <= 4) return;
+    float xx = x * x, yy = y * y, zz = z * z;
+    float xy = x * y, yz = y * z, xz = x * z;
+    B[4] = K[4] * xy;
+    B[5] = K[5] * yz;
+    B[6] = K[6] * ((2.0f * zz - xx) - yy);
+    B[7] = K[7] * xz;
+    B[8] = K[8] * (xx - yy);
+    if (d <= 9) return;
+    B[9] = (K[9] * y) * (3.0f * xx - yy);
+    B[10] = (K[10] * xy) * z;
+    B[11] = (K[11] * y) * ((4.0f * zz - xx) - yy);
+    B[12] = (K[12] * z) * ((2.0f * zz - 3.0f * xx) - 3.0f * yy);
+    B[13] = (K[13] * x) * ((4.0f * zz - xx) - yy);
+    B[14] = (K[14] * z) * (xx - yy);
+    B[15] = (K[15] * x) * (xx - 3.0f * yy);
+}
+
+static void sh_basis64(double x, double y, double z, int d, double* B)
+{
+    const double* K = g_sh64;
+    B[0] = K[0];
+    if (d <= 1) return;
+    B[1] = K[1] * y;
+    B[2] = K[2] * z;
+    B[3] = K[3] * x;
+    if (d <= 4) return;
+    double xx = x * x, yy = y * y, zz = z * z;
+    B[4] = K[4] * x * y;
+    B[5] = K[5] * y * z;
+    B[6] = K[6] * (2.0 * zz - xx - yy);
+    B[7] = K[7] * x * z;
+    B[8] = K[8] * (xx - yy);
+    if (d <= 9) return;
+    B[9] = K[9] * y * (3.0 * xx - yy);
+    B[10] = K[10] * x * y * z;
+    B[11] = K[11] * y * (4.0 * zz - xx - yy);
+    B[12] = K[12] * z * (2.0 * zz - 3.0 * xx - 3.0 * yy);
+    B[13] = K[13] * x * (4.0 * zz - xx - yy);
+    B[14] = K[14] * z * (xx - yy);
+    B[15] = K[15] * x * (xx - 3.0 * yy);
+}
+
+void orc_sh_basis64(const double* dirs, int64_t n, int d, double* out)
+{
+    init_constants();
+    for (int64_t i = 0; i < n; ++i)
+        sh_basis64(dirs[3 * i], dirs[3 * i + 1], dirs[3 * i + 2], d, out + i * d);
+}
+
+/* ----------------------------------------------------------------------------
+ * Scene, per-(Gaussian, view) records.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    int culled;
+    float mx, my;        /* projected centre, pixels */
+    float ca, cb, cc;    /* conic: inverse of the dilated 2D covariance */
+    float qa, qb, qc;    /* G = 2^(qa dx^2 + qb dx dy + qc dy^2) */
+    float opac;
+    float pre[3];        /* SH colour + 0.5 before the clamp */
+    float col[3];        /* clamped colour */
+    int clamp_ok[3];     /* 1 where pre >= 0 (clamp inactive) */
+    float depth;
+    float radius;
+    int rect[4];         /* x0, y0, x1, y1 in tiles, half-open */
+} rec32;
+
+typedef struct {
+    double mx, my;       /* projected centre */
+    double ca, cb, cc;   /* conic */
+    double opac;
+    double col[3];       /* colour value with the float32 clamp decision frozen */
+    double J[6];         /* d(pixel)/d(mean), unclamped, row-major 2x3 */
+    double B[16];        /* SH basis at the view direction */
+} rec64;
+
+typedef struct {
+    int G, d, V, W, H, TX, TY;
+    float near_plane, far_plane;
+    double bg[3];
+    float* means;  /* [G,3] */
+    float* quats;  /* [G,4] */
+    float* scales; /* [G,3] */
+    float* opac;   /* [G] */
+    float* sh;     /* [G,d,3] */
+    double* sh64;  /* [G,d,3] value copy (finite-difference probes edit it) */
+    float* cams;   /* [V,16] */
+    rec32* r32;    /* [V*G] */
+    rec64* r64;    /* [V*G] */
+    rec64* r64_base;
+    /* tile lists */
+    int64_t* starts; /* [V*T+1] */
+    int32_t* ids;    /* [P] */
+    int64_t n_pairs;
+    /* score accumulation for selected Gaussians */
+    int32_t* slot;   /* [G], -1 if not selected */
+    int n_sel;
+    int32_t* sel;    /* [n_sel] gids */
+    double* acc;     /* [n_sel][V][NACC] */
+} scene;
+
+#define NACC_FIXED 8   /* W, Aa, Amu_x, Amu_y, |Aa|, |Amu_x|, |Amu_y|, n_pix */
+static int nacc(const scene* s) { return NACC_FIXED + 6 * s->d; } /* + ASH[d][3] + |ASH|[d][3] */
+
+static void project32(const scene* s, int g, int v, rec32* r)
+{
+    const float* mu = s->means + 3 * (int64_t)g;
+    const float* qi = s->quats + 4 * (int64_t)g;
+    const float* sc = s->scales + 3 * (int64_t)g;
+    const float op = s->opac[g];
+    const float* sh = s->sh + (int64_t)g * s->d * 3;
+    const float* cam = s->cams + 16 * v;
+    const float* R = cam;
+    const float* t = cam + 9;
+    const float fx = cam[12], fy = cam[13], cx = cam[14], cy = cam[15];
+
+    memset(r, 0, sizeof *r);
+    r->culled = 1;
+    float tx = ((R[0] * mu[0] + R[1] * mu[1]) + R[2] * mu[2]) + t[0];
+    float ty = ((R[3] * mu[0] + R[4] * mu[1]) + R[5] * mu[2]) + t[1];
+    float tz = ((R[6] * mu[0] + R[7] * mu[1]) + R[8] * mu[2]) + t[2];
+    if (!(tz >= s->near_plane) || !(tz <= s->far_plane)) return;
+    if (!(op >= 0.0f) || !(op <= 1.0f)) return;
+
+    float n2 = ((qi[0] * qi[0] + qi[1] * qi[1]) + qi[2] * qi[2]) + qi[3] * qi[3];
+    if (!(n2 > 0.0f) || !(n2 <= FLT_MAX)) return;
+    float inv = 1.0f / sqrtf(n2);
+    float w = qi[0] * inv, x = qi[1] * inv, y = qi[2] * inv, z = qi[3] * inv;
+    float Rq[9];
+    Rq[0] = 1.0f - 2.0f * (y * y + z * z);
+    Rq[1] = 2.0f * (x * y - w * z);
+    Rq[2] = 2.0f * (x * z + w * y);
+    Rq[3] = 2.0f * (x * y + w * z);
+    Rq[4] = 1.0f - 2.0f * (x * x + z * z);
+    Rq[5] = 2.0f * (y * z - w * x);
+    Rq[6] = 2.0f * (x * z - w * y);
+    Rq[7] = 2.0f * (y * z + w * x);
+    Rq[8] = 1.0f - 2.0f * (x * x + y * y);
+    float M[9];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) M[3 * i + j] = Rq[3 * i + j] * sc[j];
+    float S3[9];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            S3[3 * i + j] = (M[3 * i] * M[3 * j] + M[3 * i + 1] * M[3 * j + 1]) + M[3 * i + 2] * M[3 * j + 2];
+    float Tm[9], Cc[9];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            Tm[3 * i + j] = (R[3 * i] * S3[j] + R[3 * i + 1] * S3[3 + j]) + R[3 * i + 2] * S3[6 + j];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            Cc[3 * i + j] = (Tm[3 * i] * R[3 * j] + Tm[3 * i + 1] * R[3 * j + 1]) + Tm[3 * i + 2] * R[3 * j + 2];
+
+    float limx = FOV_CLAMP_F * ((0.5f * (float)s->W) / fx);
+    float limy = FOV_CLAMP_F * ((0.5f * (float)s->H) / fy);
+    float ux = tx / tz, uy = ty / tz;
+    float uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
+    float uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
+    float txc = uxc * tz, tyc = uyc * tz;
+    float tz2 = tz * tz;
+    float j00 = fx / tz, j02 = -(fx * txc) / tz2;
+    float j11 = fy / tz, j12 = -(fy * tyc) / tz2;
+    float u00 = j00 * Cc[0] + j02 * Cc[6];
+    float u01 = j00 * Cc[1] + j02 * Cc[7];
+    float u02 = j00 * Cc[2] + j02 * Cc[8];
+    float u11 = j11 * Cc[4] + j12 * Cc[7];
+    float u12 = j11 * Cc[5] + j12 * Cc[8];
+    float a = (u00 * j00 + u02 * j02) + DILATION_F;
+    float b = u01 * j11 + u02 * j12;
+    float c = (u11 * j11 + u12 * j12) + DILATION_F;
+    float det = a * c - b * b;
+    if (!(det > 0.0f)) return;
+    float idet = 1.0f / det;
+    float ca = c * idet, cb = -b * idet, cc = a * idet;
+    float mid = 0.5f * (a + c);
+    float disc = mid * mid - det;
+    float lam = mid + sqrtf(disc > EIG_FLOOR_F ? disc : EIG_FLOOR_F);
+    float rad = ceilf(3.0f * sqrtf(lam));
+    float mx = fx * (tx / tz) + cx;
+    float my = fy * (ty / tz) + cy;
+
+    float fx0 = (mx - rad) * 0.0625f, fx1 = ((mx + rad) + 15.0f) * 0.0625f;
+    float fy0 = (my - rad) * 0.0625f, fy1 = ((my + rad) + 15.0f) * 0.0625f;
+#define CLAMP_TILE(f, n) (!((f) > 0.0f) ? 0 : ((f) >= (float)(n) ? (n) : (int)(f)))
+    int x0 = CLAMP_TILE(fx0, s->TX), x1 = CLAMP_TILE(fx1, s->TX);
+    int y0 = CLAMP_TILE(fy0, s->TY), y1 = CLAMP_TILE(fy1, s->TY);
+#undef CLAMP_TILE
+    if (x1 <= x0 || y1 <= y0) return;
+
+    /* view direction from the camera centre -R^T t */
+    float ccx = -((R[0] * t[0] + R[3] * t[1]) + R[6] * t[2]);
+    float ccy = -((R[1] * t[0] + R[4] * t[1]) + R[7] * t[2]);
+    float ccz = -((R[2] * t[0] + R[5] * t[1]) + R[8] * t[2]);
+    float dx = mu[0] - ccx, dy = mu[1] - ccy, dz = mu[2] - ccz;
+    float len = sqrtf((dx * dx + dy * dy) + dz * dz);
+    float il = 1.0f / len;
+    float B[16];
+    sh_basis32(dx * il, dy * il, dz * il, s->d, B);
+    for (int ch = 0; ch < 3; ++ch) {
+        float acc = B[0] * sh[ch];
+        for (int k = 1; k < s->d; ++k) acc = acc + B[k] * sh[3 * k + ch];
+        float pre = acc + 0.5f;
+        r->pre[ch] = pre;
+        r->clamp_ok[ch] = pre >= 0.0f;
+        r->col[ch] = pre >= 0.0f ? pre : 0.0f;
+    }
+    r->culled = 0;
+    r->mx = mx;
+    r->my = my;
+    r->ca = ca;
+    r->cb = cb;
+    r->cc = cc;
+    r->qa = ca * g_nhl2e;
+    r->qb = cb * g_nl2e;
+    r->qc = cc * g_nhl2e;
+    r->opac = op;
+    r->depth = tz;
+    r->radius = rad;
+    r->rect[0] = x0;
+    r->rect[1] = y0;
+    r->rect[2] = x1;
+    r->rect[3] = y1;
+}
+
+/* float64 values of one (Gaussian, view): same formulas as above, no rounding to float32 */
+static void project64(const scene* s, int g, int v, const rec32* r32, rec64* r)
+{
+    memset(r, 0, sizeof *r);
+    const float* mu32 = s->means + 3 * (int64_t)g;
+    const float* qi = s->quats + 4 * (int64_t)g;
+    const float* sc = s->scales + 3 * (int64_t)g;
+    const double* sh = s->sh64 + (int64_t)g * s->d * 3;
+    const float* cam = s->cams + 16 * v;
+    double R[9], t[3];
+    for (int i = 0; i < 9; ++i) R[i] = cam[i];
+    for (int i = 0; i < 3; ++i) t[i] = cam[9 + i];
+    double fx = cam[12], fy = cam[13], cx = cam[14], cy = cam[15];
+    double mu[3] = {mu32[0], mu32[1], mu32[2]};
+    double tc[3];
+    for (int i = 0; i < 3; ++i) tc[i] = R[3 * i] * mu[0] + R[3 * i + 1] * mu[1] + R[3 * i + 2] * mu[2] + t[i];
+    double tx = tc[0], ty = tc[1], tz = tc[2];
+    r->opac = s->opac[g];
+    if (r32->culled) return;
+
+    double qn = sqrt((double)qi[0] * qi[0] + (double)qi[1] * qi[1] + (double)qi[2] * qi[2] + (double)qi[3] * qi[3]);
+    double w = qi[0] / qn, x = qi[1] / qn, y = qi[2] / qn, z = qi[3] / qn;
+    double Rq[9] = {1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y),
+                    2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x),
+                    2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)};
+    double S3[9], Tm[9], Cc[9];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            double acc = 0;
+            for (int k = 0; k < 3; ++k) acc += Rq[3 * i + k] * sc[k] * Rq[3 * j + k] * sc[k];
+            S3[3 * i + j] = acc;
+        }
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            double acc = 0;
+            for (int k = 0; k < 3; ++k) acc += R[3 * i + k] * S3[3 * k + j];
+            Tm[3 * i + j] = acc;
+        }
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) {
+            double acc = 0;
+            for (int k = 0; k < 3; ++k) acc += Tm[3 * i + k] * R[3 * j + k];
+            Cc[3 * i + j] = acc;
+        }
+    double limx = 1.3 * (0.5 * s->W / fx), limy = 1.3 * (0.5 * s->H / fy);
+    double ux = tx / tz, uy = ty / tz;
+    double uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
+    double uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
+    double Jc[6] = {fx / tz, 0, -fx * uxc / tz, 0, fy / tz, -fy * uyc / tz};
+    double S2[4] = {0, 0, 0, 0};
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) {
+            double acc = 0;
+            for (int k = 0; k < 3; ++k)
+                for (int l = 0; l < 3; ++l) acc += Jc[3 * i + k] * Cc[3 * k + l] * Jc[3 * j + l];
+            S2[2 * i + j] = acc;
+        }
+    double a = S2[0] + 0.3, b = 0.5 * (S2[1] + S2[2]), c = S2[3] + 0.3;
+    double det = a * c - b * b;
+    r->ca = c / det;
+    r->cb = -b / det;
+    r->cc = a / det;
+    r->mx = fx * tx / tz + cx;
+    r->my = fy * ty / tz + cy;
+    /* unclamped pixel-projection Jacobian d pi / d mu = Jp(t) R */
+    double Jp[6] = {fx / tz, 0, -fx * tx / (tz * tz), 0, fy / tz, -fy * ty / (tz * tz)};
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 3; ++j) {
+            double acc = 0;
+            for (int k = 0; k < 3; ++k) acc += Jp[3 * i + k] * R[3 * k + j];
+            r->J[3 * i + j] = acc;
+        }
+    double cc3[3];
+    for (int j = 0; j < 3; ++j) cc3[j] = -(R[j] * t[0] + R[3 + j] * t[1] + R[6 + j] * t[2]);
+    double dv[3] = {mu[0] - cc3[0], mu[1] - cc3[1], mu[2] - cc3[2]};
+    double len = sqrt(dv[0] * dv[0] + dv[1] * dv[1] + dv[2] * dv[2]);
+    sh_basis64(dv[0] / len, dv[1] / len, dv[2] / len, s->d, r->B);
+    for (int ch = 0; ch < 3; ++ch) {
+        double acc = 0.5;
+        for (int k = 0; k < s->d; ++k) acc += r->B[k] * sh[3 * k + ch];
+        r->col[ch] = r32->clamp_ok[ch] ? acc : 0.0;
+    }
+}
+
+void* orc_scene_new(int G, int sh_degree, const float* means, const float* quats, const float* scales,
+                    const float* opac, const float* sh, int V, const float* cams, int W, int H,
+                    float near_plane, float far_plane, const float* bg)
+{
+    init_constants();
+    if (G < 0 || V <= 0 || W <= 0 || H <= 0 || sh_degree < 0 || sh_degree > 3) return NULL;
+    scene* s = (scene*)calloc(1, sizeof(scene));
+    s->G = G;
+    s->d = (sh_degree + 1) * (sh_degree + 1);
+    s->V = V;
+    s->W = W;
+    s->H = H;
+    s->TX = (W + TILE - 1) / TILE;
+    s->TY = (H + TILE - 1) / TILE;
+    s->near_plane = near_plane;
+    s->far_plane = far_plane;
+    for (int i = 0; i < 3; ++i) s->bg[i] = bg[i];
+    size_t Gs = (size_t)G;
+    s->means = (float*)malloc(sizeof(float) * 3 * Gs + 1);
+    s->quats = (float*)malloc(sizeof(float) * 4 * Gs + 1);
+    s->scales = (float*)malloc(sizeof(float) * 3 * Gs + 1);
+    s->opac = (float*)malloc(sizeof(float) * Gs + 1);
+    s->sh = (float*)malloc(sizeof(float) * 3 * s->d * Gs + 1);
+    s->sh64 = (double*)malloc(sizeof(double) * 3 * s->d * Gs + 1);
+    s->cams = (float*)malloc(sizeof(float) * 16 * V);
+    memcpy(s->means, means, sizeof(float) * 3 * Gs);
+    memcpy(s->quats, quats, sizeof(float) * 4 * Gs);
+    memcpy(s->scales, scales, sizeof(float) * 3 * Gs);
+    memcpy(s->opac, opac, sizeof(float) * Gs);
+    memcpy(s->sh, sh, sizeof(float) * 3 * s->d * Gs);
+    for (size_t i = 0; i < 3 * s->d * Gs; ++i) s->sh64[i] = sh[i];
+    memcpy(s->cams, cams, sizeof(float) * 16 * V);
+    size_t VG = (size_t)V * Gs;
+    s->r32 = (rec32*)malloc(sizeof(rec32) * VG + 1);
+    s->r64 = (rec64*)malloc(sizeof(rec64) * VG + 1);
+    s->r64_base = (rec64*)malloc(sizeof(rec64) * VG + 1);
+    s->slot = (int32_t*)malloc(sizeof(int32_t) * Gs + 1);
+    for (size_t i = 0; i < Gs; ++i) s->slot[i] = -1;
+#pragma omp parallel for schedule(dynamic, 256)
+    for (int64_t i = 0; i < (int64_t)VG; ++i) {
+        int v = (int)(i / G), g = (int)(i % G);
+        project32(s, g, v, &s->r32[i]);
+        project64(s, g, v, &s->r32[i], &s->r64[i]);
+    }
+    memcpy(s->r64_base, s->r64, sizeof(rec64) * VG);
+    return s;
+}
+
+void orc_scene_free(void* p)
+{
+    scene* s = (scene*)p;
+    if (!s) return;
+    free(s->means); free(s->quats); free(s->scales); free(s->opac); free(s->sh); free(s->sh64);
+    free(s->cams); free(s->r32); free(s->r64); free(s->r64_base); free(s->starts); free(s->ids);
+    free(s->slot); free(s->sel); free(s->acc);
+    free(s);
+}
+
+/* Export the float32 records: per (v, g) 20 floats
+ * [culled, mx, my, ca, cb, cc, qa, qb, qc, opac, pre r, g, b, depth, radius, x0, y0, x1, y1, clamp bits] */
+void orc_get_records32(const void* p, float* out)
+{
+    const scene* s = (const scene*)p;
+    int64_t VG = (int64_t)s->V * s->G;
+    for (int64_t i = 0; i < VG; ++i) {
+        const rec32* r = &s->r32[i];
+        float* o = out + 20 * i;
+        o[0] = (float)r->culled;
+        o[1] = r->mx; o[2] = r->my;
+        o[3] = r->ca; o[4] = r->cb; o[5] = r->cc;
+        o[6] = r->qa; o[7] = r->qb; o[8] = r->qc;
+        o[9] = r->opac;
+        o[10] = r->pre[0]; o[11] = r->pre[1]; o[12] = r->pre[2];
+        o[13] = r->depth; o[14] = r->radius;
+        o[15] = (float)r->rect[0]; o[16] = (float)r->rect[1];
+        o[17] = (float)r->rect[2]; o[18] = (float)r->rect[3];
+        o[19] = (float)(r->clamp_ok[0] | (r->clamp_ok[1] << 1) | (r->clamp_ok[2] << 2));
+    }
+}
+
+/* Export float64 values: per (v, g) 12 doubles [mx, my, ca, cb, cc, opac, col r, g, b, J...] -> 6 + 3 + 6 = 15 */
+void orc_get_records64(const void* p, double* out)
+{
+    const scene* s = (const scene*)p;
+    int64_t VG = (int64_t)s->V * s->G;
+    for (int64_t i = 0; i < VG; ++i) {
+        const rec64* r = &s->r64[i];
+        double* o = out + 15 * i;
+        o[0] = r->mx; o[1] = r->my; o[2] = r->ca; o[3] = r->cb; o[4] = r->cc; o[5] = r->opac;
+        o[6] = r->col[0]; o[7] = r->col[1]; o[8] = r->col[2];
+        for (int k = 0; k < 6; ++k) o[9 + k] = r->J[k];
+    }
+}
+
+/* ----------------------------------------------------------------------------
+ * Candidate lists per tile, brute force, ordered by (depth bits, Gaussian id).
+ * ------------------------------------------------------------------------- */
+static uint32_t fbits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+
+static int cmp_u64(const void* a, const void* b)
+{
+    uint64_t x = *(const uint64_t*)a, y = *(const uint64_t*)b;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+int64_t orc_build_lists(void* p)
+{
+    scene* s = (scene*)p;
+    int T = s->TX * s->TY;
+    int64_t nt = (int64_t)s->V * T;
+    int64_t* count = (int64_t*)calloc((size_t)nt + 1, sizeof(int64_t));
+    for (int v = 0; v < s->V; ++v)
+        for (int g = 0; g < s->G; ++g) {
+            const rec32* r = &s->r32[(int64_t)v * s->G + g];
+            if (r->culled) continue;
+            for (int ty = r->rect[1]; ty < r->rect[3]; ++ty)
+                for (int tx = r->rect[0]; tx < r->rect[2]; ++tx) count[(int64_t)v * T + ty * s->TX + tx]++;
+        }
+    free(s->starts);
+    free(s->ids);
+    s->starts = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nt + 1));
+    s->starts[0] = 0;
+    for (int64_t i = 0; i < nt; ++i) s->starts[i + 1] = s->starts[i] + count[i];
+    s->n_pairs = s->starts[nt];
+    uint64_t* keys = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)s->n_pairs + 1);
+    int64_t* fill = count;
+    for (int64_t i = 0; i < nt; ++i) fill[i] = s->starts[i];
+    for (int v = 0; v < s->V; ++v)
+        for (int g = 0; g < s->G; ++g) {
+            const rec32* r = &s->r32[(int64_t)v * s->G + g];
+            if (r->culled) continue;
+            uint64_t key = ((uint64_t)fbits(r->depth) << 32) | (uint32_t)g;
+            for (int ty = r->rect[1]; ty < r->rect[3]; ++ty)
+                for (int tx = r->rect[0]; tx < r->rect[2]; ++tx) keys[fill[(int64_t)v * T + ty * s->TX + tx]++] = key;
+        }
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t i = 0; i < nt; ++i)
+        qsort(keys + s->starts[i], (size_t)(s->starts[i + 1] - s->starts[i]), sizeof(uint64_t), cmp_u64);
+    s->ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)s->n_pairs + 1);
+    for (int64_t i = 0; i < s->n_pairs; ++i) s->ids[i] = (int32_t)(keys[i] & 0xffffffffu);
+    free(keys);
+    free(count);
+    return s->n_pairs;
+}
+
+void orc_get_lists(const void* p, int64_t* starts, int32_t* ids)
+{
+    const scene* s = (const scene*)p;
+    int64_t nt = (int64_t)s->V * s->TX * s->TY;
+    memcpy(starts, s->starts, sizeof(int64_t) * (size_t)(nt + 1));
+    memcpy(ids, s->ids, sizeof(int32_t) * (size_t)s->n_pairs);
+}
+
+/* One tile's list by scanning every Gaussian of the view (used to pin orc_build_lists). */
+int64_t orc_tile_list_scan(const void* p, int64_t tile, int32_t* out)
+{
+    const scene* s = (const scene*)p;
+    int T = s->TX * s->TY;
+    int v = (int)(tile / T), t = (int)(tile % T);
+    int tx = t % s->TX, ty = t / s->TX;
+    int64_t n = 0;
+    uint64_t* keys = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)s->G + 1);
+    for (int g = 0; g < s->G; ++g) {
+        const rec32* r = &s->r32[(int64_t)v * s->G + g];
+        if (r->culled) continue;
+        if (tx >= r->rect[0] && tx < r->rect[2] && ty >= r->rect[1] && ty < r->rect[3])
+            keys[n++] = ((uint64_t)fbits(r->depth) << 32) | (uint32_t)g;
+    }
+    qsort(keys, (size_t)n, sizeof(uint64_t), cmp_u64);
+    for (int64_t i = 0; i < n; ++i) out[i] = (int32_t)(keys[i] & 0xffffffffu);
+    free(keys);
+    return n;
+}
+
+/* ----------------------------------------------------------------------------
+ * Per-pixel front-to-back composite, back-to-front suffix, literal score sums.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    int g;
+    double alpha, T, G;  /* float64 values */
+    float tT32;          /* float32 transmittance after this contribution */
+    int clamped;         /* alpha clamp active (o G >= 0.99 in float32) */
+} contrib;
+
+void orc_select(void* p, const int32_t* gids, int n)
+{
+    scene* s = (scene*)p;
+    for (int g = 0; g < s->G; ++g) s->slot[g] = -1;
+    free(s->sel);
+    free(s->acc);
+    if (n < 0) { /* all */
+        n = s->G;
+        s->sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)n + 1);
+        for (int g = 0; g < n; ++g) s->sel[g] = g;
+    } else {
+        s->sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)n + 1);
+        memcpy(s->sel, gids, sizeof(int32_t) * (size_t)n);
+    }
+    s->n_sel = n;
+    for (int i = 0; i < n; ++i) s->slot[s->sel[i]] = i;
+    s->acc = (double*)calloc((size_t)n * s->V * nacc(s) + 1, sizeof(double));
+}
+
+static void add(double* a, double x)
+{
+#pragma omp atomic
+    *a += x;
+}
+
+/* Render (and, with obs != NULL, replay) the pixels of the given tiles.
+ * Pixel outputs are written at [v, y, x]; score sums accumulate into the selected slots. */
+void orc_render_tiles(void* p, const int64_t* tiles, int64_t n_tiles, const float* obs, float eps,
+                      float den_min, double* color, float* T_out, int32_t* n_out, double* T64_out)
+{
+    scene* s = (scene*)p;
+    const int T = s->TX * s->TY;
+    const int d = s->d;
+    const int na = nacc(s);
+    int64_t maxlen = 0;
+    for (int64_t i = 0; i < (int64_t)s->V * T; ++i)
+        if (s->starts[i + 1] - s->starts[i] > maxlen) maxlen = s->starts[i + 1] - s->starts[i];
+
+#pragma omp parallel
+    {
+        contrib* cl = (contrib*)malloc(sizeof(contrib) * (size_t)maxlen + 1);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < n_tiles; ++it) {
+            int64_t tile = tiles[it];
+            int v = (int)(tile / T), t = (int)(tile % T);
+            int tx = t % s->TX, ty = t / s->TX;
+            const int32_t* list = s->ids + s->starts[tile];
+            int64_t L = s->starts[tile + 1] - s->starts[tile];
+            for (int yy = 0; yy < TILE; ++yy)
+                for (int xx = 0; xx < TILE; ++xx) {
+                    int x = tx * TILE + xx, y = ty * TILE + yy;
+                    if (x >= s->W || y >= s->H) continue;
+                    float px = (float)x + 0.5f, py = (float)y + 0.5f;
+                    double pxd = x + 0.5, pyd = y + 0.5;
+                    float T32 = 1.0f;
+                    double T64 = 1.0;
+                    double C[3] = {0, 0, 0};
+                    int n = 0;
+                    /* Stage 1: front-to-back composite */
+                    for (int64_t k = 0; k < L; ++k) {
+                        int g = list[k];
+                        const rec32* r = &s->r32[(int64_t)v * s->G + g];
+                        float dx = px - r->mx, dy = py - r->my;
+                        float e = fmaf(dx, fmaf(r->qa, dx, r->qb * dy), (r->qc * dy) * dy);
+                        if (!(e >= E_CUTOFF_F)) continue;
+                        float aG = r->opac * orc_exp2f(e);
+                        int clamped = !(aG < ALPHA_MAX_F);
+                        float a32 = clamped ? ALPHA_MAX_F : aG;
+                        if (!(a32 >= g_alpha_min)) continue;
+                        float tT = T32 * (1.0f - a32);
+                        if (tT < T_MIN_F) break;
+                        const rec64* q = &s->r64[(int64_t)v * s->G + g];
+                        double ddx = pxd - q->mx, ddy = pyd - q->my;
+                        double sig = 0.5 * (q->ca * ddx * ddx + 2.0 * q->cb * ddx * ddy + q->cc * ddy * ddy);
+                        double G64 = exp(-sig);
+                        double a64 = clamped ? ALPHA_MAX_D : q->opac * G64;
+                        for (int ch = 0; ch < 3; ++ch) C[ch] += q->col[ch] * a64 * T64;
+                        cl[n].g = g;
+                        cl[n].alpha = a64;
+                        cl[n].T = T64;
+                        cl[n].G = G64;
+                        cl[n].tT32 = tT;
+                        cl[n].clamped = clamped;
+                        n++;
+                        T64 = T64 * (1.0 - a64);
+                        T32 = tT;
+                    }
+                    for (int ch = 0; ch < 3; ++ch) C[ch] += T64 * s->bg[ch];
+                    int64_t pix = ((int64_t)v * s->H + y) * s->W + x;
+                    if (color) for (int ch = 0; ch < 3; ++ch) color[3 * pix + ch] = C[ch];
+                    if (T_out) T_out[pix] = T32;
+                    if (n_out) n_out[pix] = n;
+                    if (T64_out) T64_out[pix] = T64;
+                    if (!obs) continue;
+
+                    /* residual r = C_hat - C_obs */
+                    double rr[3];
+                    for (int ch = 0; ch < 3; ++ch) rr[ch] = C[ch] - (double)obs[3 * pix + ch];
+                    /* Stage 2: explicit back-to-front suffix */
+                    double S[3];
+                    for (int ch = 0; ch < 3; ++ch) S[ch] = T64 * s->bg[ch];
+                    for (int k = n - 1; k >= 0; --k) {
+                        const contrib* c = &cl[k];
+                        const rec64* q = &s->r64[(int64_t)v * s->G + c->g];
+                        double den = c->T * (1.0 - c->alpha) + (double)eps;
+                        double Cp[3];
+                        int finite = 1;
+                        for (int ch = 0; ch < 3; ++ch) {
+                            Cp[ch] = S[ch] / den;
+                            if (!isfinite(Cp[ch])) finite = 0;
+                        }
+                        double w = c->T * c->alpha;
+                        for (int ch = 0; ch < 3; ++ch) S[ch] += w * q->col[ch];
+                        int sl = s->slot[c->g];
+                        if (sl < 0) continue;
+                        double rho = 0;
+                        for (int ch = 0; ch < 3; ++ch) rho += rr[ch] * (q->col[ch] - Cp[ch]);
+                        int Ma = !c->clamped && (c->tT32 >= den_min) && finite;
+                        double* A = s->acc + ((int64_t)sl * s->V + v) * na;
+                        add(&A[0], w);
+                        add(&A[7], 1.0);
+                        if (Ma) {
+                            /* opacity logit: T alpha (1 - o) rho */
+                            double ta = c->T * c->alpha * (1.0 - q->opac) * rho;
+                            /* projected centre: T o grad G rho, grad G = G conic (p - mu) */
+                            double dx = pxd - q->mx, dy = pyd - q->my;
+                            double gx = c->G * (q->ca * dx + q->cb * dy);
+                            double gy = c->G * (q->cb * dx + q->cc * dy);
+                            double tmx = c->T * q->opac * gx * rho;
+                            double tmy = c->T * q->opac * gy * rho;
+                            add(&A[1], ta);
+                            add(&A[2], tmx);
+                            add(&A[3], tmy);
+                            add(&A[4], fabs(ta));
+                            add(&A[5], fabs(tmx));
+                            add(&A[6], fabs(tmy));
+                        }
+                        const rec32* r = &s->r32[(int64_t)v * s->G + c->g];
+                        for (int k2 = 0; k2 < d; ++k2)
+                            for (int ch = 0; ch < 3; ++ch) {
+                                if (!r->clamp_ok[ch]) continue;
+                                double tsh = w * q->B[k2] * rr[ch];
+                                add(&A[NACC_FIXED + 3 * k2 + ch], tsh);
+                                add(&A[NACC_FIXED + 3 * d + 3 * k2 + ch], fabs(tsh));
+                            }
+                    }
+                }
+        }
+        free(cl);
+    }
+}
+
+void orc_get_acc(const void* p, double* out)
+{
+    const scene* s = (const scene*)p;
+    memcpy(out, s->acc, sizeof(double) * (size_t)s->n_sel * s->V * nacc(s));
+}
+
+/* ----------------------------------------------------------------------------
+ * Token: cross-view weights, pullback, conditioning statistics.
+ * ------------------------------------------------------------------------- */
+/* eigenvalues of a symmetric 3x3 matrix by cyclic Jacobi rotations, descending */
+void orc_eig3(const double* Ain, double* ev)
+{
+    double a[3][3];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j) a[i][j] = Ain[3 * i + j];
+    for (int sweep = 0; sweep < 64; ++sweep) {
+        double off = a[0][1] * a[0][1] + a[0][2] * a[0][2] + a[1][2] * a[1][2];
+        double dia = a[0][0] * a[0][0] + a[1][1] * a[1][1] + a[2][2] * a[2][2];
+        if (off <= 1e-34 * dia || off == 0.0) break;
+        for (int p = 0; p < 2; ++p)
+            for (int q = p + 1; q < 3; ++q) {
+                if (a[p][q] == 0.0) continue;
+                double theta = (a[q][q] - a[p][p]) / (2.0 * a[p][q]);
+                double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+                double c = 1.0 / sqrt(t * t + 1.0), sn = t * c;
+                for (int k = 0; k < 3; ++k) { /* columns p, q */
+                    double akp = a[k][p], akq = a[k][q];
+                    a[k][p] = c * akp - sn * akq;
+                    a[k][q] = sn * akp + c * akq;
+                }
+                for (int k = 0; k < 3; ++k) { /* rows p, q */
+                    double apk = a[p][k], aqk = a[q][k];
+                    a[p][k] = c * apk - sn * aqk;
+                    a[q][k] = sn * apk + c * aqk;
+                }
+            }
+    }
+    ev[0] = a[0][0];
+    ev[1] = a[1][1];
+    ev[2] = a[2][2];
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (ev[j] > ev[i]) {
+                double tmp = ev[i];
+                ev[i] = ev[j];
+                ev[j] = tmp;
+            }
+}
+
+/* tokens [n_sel][9 + 3d] for the selected Gaussians; optional A matrices [n_sel][9] and q [n_sel][V] */
+void orc_tokens(const void* p, double eps, double lambda, double* tok, double* Aout, double* qout)
+{
+    const scene* s = (const scene*)p;
+    const int d = s->d, V = s->V, na = nacc(s);
+    const int D = 9 + 3 * d;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int i = 0; i < s->n_sel; ++i) {
+        int g = s->sel[i];
+        const double* acc = s->acc + (int64_t)i * V * na;
+        double Q = eps;
+        for (int v = 0; v < V; ++v) Q += eps + acc[v * na + 0];
+        double b[3] = {0, 0, 0}, sa = 0, A[9] = {0};
+        double* z = tok + (int64_t)i * D;
+        for (int k = 0; k < 3 * d; ++k) z[4 + k] = 0.0;
+        for (int v = 0; v < V; ++v) {
+            const double* a = acc + v * na;
+            const rec32* r32 = &s->r32[(int64_t)v * s->G + g];
+            const rec64* r64 = &s->r64[(int64_t)v * s->G + g];
+            double q = eps + a[0];
+            double gamma = q / Q;
+            if (qout) qout[(int64_t)i * V + v] = q;
+            double J[6] = {0, 0, 0, 0, 0, 0};
+            if (!r32->culled)
+                for (int k = 0; k < 6; ++k) J[k] = r64->J[k];
+            double s_alpha = a[1] / q;
+            double s_mu[2] = {a[2] / q, a[3] / q};
+            for (int j = 0; j < 3; ++j) b[j] += gamma * (J[j] * s_mu[0] + J[3 + j] * s_mu[1]);
+            sa += gamma * s_alpha;
+            for (int k = 0; k < 3 * d; ++k) z[4 + k] += gamma * (a[NACC_FIXED + k] / q);
+            for (int r = 0; r < 3; ++r)
+                for (int c = 0; c < 3; ++c) A[3 * r + c] += gamma * (J[r] * J[c] + J[3 + r] * J[3 + c]);
+        }
+        for (int r = 0; r < 3; ++r) A[4 * r] += lambda;
+        double ev[3];
+        orc_eig3(A, ev);
+        double tr = A[0] + A[4] + A[8];
+        z[0] = b[0];
+        z[1] = b[1];
+        z[2] = b[2];
+        z[3] = sa;
+        z[4 + 3 * d] = log(Q);
+        for (int k = 0; k < 3; ++k) z[5 + 3 * d + k] = ev[k] / (tr + eps);
+        z[8 + 3 * d] = log(tr + eps);
+        if (Aout)
+            for (int k = 0; k < 9; ++k) Aout[(int64_t)i * 9 + k] = A[k];
+    }
+}
+
+/* ----------------------------------------------------------------------------
+ * Value probes for finite differences (float32 decisions stay frozen).
+ * ------------------------------------------------------------------------- */
+void orc_values_reset(void* p)
+{
+    scene* s = (scene*)p;
+    memcpy(s->r64, s->r64_base, sizeof(rec64) * (size_t)s->V * s->G);
+    for (size_t i = 0; i < (size_t)3 * s->d * s->G; ++i) s->sh64[i] = s->sh[i];
+}
+
+void orc_set_opacity64(void* p, int g, double o)
+{
+    scene* s = (scene*)p;
+    for (int v = 0; v < s->V; ++v) s->r64[(int64_t)v * s->G + g].opac = o;
+}
+
+void orc_set_sh64(void* p, int g, int k, int ch, double value)
+{
+    scene* s = (scene*)p;
+    s->sh64[((int64_t)g * s->d + k) * 3 + ch] = value;
+    const double* sh = s->sh64 + (int64_t)g * s->d * 3;
+    for (int v = 0; v < s->V; ++v) {
+        rec64* r = &s->r64[(int64_t)v * s->G + g];
+        const rec32* r32 = &s->r32[(int64_t)v * s->G + g];
+        if (r32->culled) continue;
+        for (int c = 0; c < 3; ++c) {
+            double acc = 0.5;
+            for (int kk = 0; kk < s->d; ++kk) acc += r->B[kk] * sh[3 * kk + c];
+            r->col[c] = r32->clamp_ok[c] ? acc : 0.0;
+        }
+    }
+}
+
+void orc_set_mean2d64(void* p, int g, int v, double mx, double my)
+{
+    scene* s = (scene*)p;
+    rec64* r = &s->r64[(int64_t)v * s->G + g];
+    r->mx = mx;
+    r->my = my;
+}
+
+/* move the 3D mean; only the projected centres follow (covariance and colour frozen) */
+void orc_set_mean3d64(void* p, int g, const double* mu)
+{
+    scene* s = (scene*)p;
+    for (int v = 0; v < s->V; ++v) {
+        const float* cam = s->cams + 16 * v;
+        double t[3];
+        for (int i = 0; i < 3; ++i)
+            t[i] = cam[3 * i] * mu[0] + (double)cam[3 * i + 1] * mu[1] + (double)cam[3 * i + 2] * mu[2] + cam[9 + i];
+        rec64* r = &s->r64[(int64_t)v * s->G + g];
+        r->mx = cam[12] * t[0] / t[2] + cam[14];
+        r->my = cam[13] * t[1] / t[2] + cam[15];
+    }
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
