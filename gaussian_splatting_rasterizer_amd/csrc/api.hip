@@ -1,0 +1,350 @@
+// api.hip -- the C ABI declared in include/gsr.h.
+//
+// Host code only: argument validation, workspace carve-up, state checks and
+// kernel launches on the caller's stream.  No device memory is allocated or
+// freed here; the only host/device synchronisation is the read of the pair
+// count in gs_bin_sort.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "gsr_internal.hpp"
+
+using namespace gsr;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gs_status fail(gs_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+gs_status hip_fail(hipError_t e, const char* where) {
+    return fail(GS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+enum State { kCreated = 0, kProjected = 1, kBinned = 2, kRendered = 3 };
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int bits_for(uint64_t n) {  // bits needed to represent values 0..n-1
+    int b = 0;
+    while (b < 64 && (1ull << b) < n) ++b;
+    return b;
+}
+
+constexpr int64_t kBlockItems = 4096;  // items per scan / radix block
+
+}  // namespace
+
+struct gs_context {
+    Sizes s;
+    Workspace ws;
+    int state;
+    gs_gaussians scene;
+    CamPack cams;
+    gs_params params;
+    uint64_t n_pairs;
+    const uint32_t* sorted_keys;
+};
+
+namespace gsr {
+
+Sizes make_sizes(const gs_dims& d) {
+    Sizes s;
+    s.G = d.n_gaussians;
+    s.d = (d.sh_degree + 1) * (d.sh_degree + 1);
+    s.V = d.n_views;
+    s.W = d.width;
+    s.H = d.height;
+    s.TX = (d.width + kTile - 1) / kTile;
+    s.TY = (d.height + kTile - 1) / kTile;
+    s.T = s.TX * s.TY;
+    s.VG = (int64_t)s.V * s.G;
+    s.max_pairs = d.max_pairs;
+    const int64_t nmax = s.VG > (int64_t)s.max_pairs ? s.VG : (int64_t)s.max_pairs;
+    const int64_t radix_blocks = (nmax + kBlockItems - 1) / kBlockItems;
+    s.hist_cap = 256 * radix_blocks;
+    int64_t scan_n = s.hist_cap > s.VG ? s.hist_cap : s.VG;
+    s.scan_blocks_cap = (scan_n + kBlockItems - 1) / kBlockItems + 1;
+    return s;
+}
+
+size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        off = (off + 255) & ~(size_t)255;
+        char* p = base ? base + off : nullptr;
+        off += bytes;
+        return p;
+    };
+    const size_t VG = (size_t)s.VG, P = (size_t)s.max_pairs;
+    const size_t tiles = (size_t)s.V * s.T, pixels = (size_t)s.V * s.W * s.H;
+    ws->rec0 = (float4*)take(16 * VG);
+    ws->rec1 = (float4*)take(16 * VG);
+    ws->rec2 = (float4*)take(16 * VG);
+    ws->depth_key = (uint32_t*)take(4 * VG);
+    ws->tiles_touched = (uint32_t*)take(4 * VG);
+    ws->dkey_b = (uint32_t*)take(4 * VG);
+    ws->drid_a = (uint32_t*)take(4 * VG);
+    ws->drid_b = (uint32_t*)take(4 * VG);
+    ws->offsets = (uint32_t*)take(4 * VG);
+    ws->scan_blocks = (uint64_t*)take(8 * (size_t)s.scan_blocks_cap);
+    ws->scan_total = (uint64_t*)take(8 * 4);
+    ws->hist = (uint32_t*)take(4 * (size_t)s.hist_cap);
+    ws->pkey_a = (uint32_t*)take(4 * P);
+    ws->pkey_b = (uint32_t*)take(4 * P);
+    ws->pval_a = (uint32_t*)take(4 * P);
+    ws->pval_b = (uint32_t*)take(4 * P);
+    ws->pair_g = (uint32_t*)take(4 * P);
+    ws->sorted_g = (uint32_t*)take(4 * P);
+    ws->inv = (uint32_t*)take(4 * P);
+    ws->ranges = (uint2*)take(8 * tiles);
+    ws->tile_done = (uint32_t*)take(4 * tiles);
+    ws->partials = (float4*)take(32 * P);
+    ws->pixel = (float4*)take(16 * pixels);
+    return (off + 255) & ~(size_t)255;
+}
+
+}  // namespace gsr
+
+namespace {
+
+gs_status check_dims(const gs_dims* d) {
+    if (!d) return fail(GS_ERR_INVALID_ARGUMENT, "dims is null");
+    if (d->n_gaussians < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n_gaussians < 0");
+    if (d->sh_degree < 0 || d->sh_degree > 3) return fail(GS_ERR_INVALID_ARGUMENT, "sh_degree must be 0..3");
+    if (d->n_views < 1) return fail(GS_ERR_INVALID_ARGUMENT, "n_views must be >= 1");
+    if (d->n_views > GS_MAX_VIEWS) return fail(GS_ERR_UNSUPPORTED, "n_views > %d", GS_MAX_VIEWS);
+    if (d->width <= 0 || d->height <= 0) return fail(GS_ERR_INVALID_ARGUMENT, "image size must be positive");
+    if (d->width > 65535 * 16 || d->height > 65535 * 16) return fail(GS_ERR_UNSUPPORTED, "image too large");
+    if (d->max_pairs < 1) return fail(GS_ERR_INVALID_ARGUMENT, "max_pairs must be >= 1");
+    if (d->max_pairs >= (1ull << 32)) return fail(GS_ERR_UNSUPPORTED, "max_pairs must be < 2^32");
+    const uint64_t VG = (uint64_t)d->n_gaussians * (uint64_t)d->n_views;
+    if (VG >= (1ull << 32)) return fail(GS_ERR_UNSUPPORTED, "n_gaussians * n_views must be < 2^32");
+    const uint64_t TX = (d->width + 15) / 16, TY = (d->height + 15) / 16;
+    if (TX * TY * (uint64_t)d->n_views >= (1ull << 31)) return fail(GS_ERR_UNSUPPORTED, "too many tiles");
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gs_status gs_default_params(gs_params* out) {
+    if (!out) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
+    out->eps = 1e-6f;
+    out->den_min = 1e-3f;
+    out->lambda = 1.0f;
+    out->near_plane = 0.01f;
+    out->far_plane = 1e10f;
+    out->background[0] = out->background[1] = out->background[2] = 0.0f;
+    return GS_OK;
+}
+
+gs_status gs_workspace_size(const gs_dims* dims, size_t* bytes_out) {
+    gs_status st = check_dims(dims);
+    if (st != GS_OK) return st;
+    if (!bytes_out) return fail(GS_ERR_INVALID_ARGUMENT, "bytes_out is null");
+    Sizes s = make_sizes(*dims);
+    Workspace ws;
+    *bytes_out = carve_workspace(s, nullptr, &ws);
+    return GS_OK;
+}
+
+gs_status gs_context_create(const gs_dims* dims, void* workspace, size_t workspace_bytes, gs_context** out) {
+    gs_status st = check_dims(dims);
+    if (st != GS_OK) return st;
+    if (!out) return fail(GS_ERR_INVALID_ARGUMENT, "out is null");
+    if (!workspace) return fail(GS_ERR_INVALID_ARGUMENT, "workspace is null");
+    if (!aligned(workspace, 256)) return fail(GS_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+    Sizes s = make_sizes(*dims);
+    Workspace ws;
+    const size_t need = carve_workspace(s, nullptr, &ws);
+    if (workspace_bytes < need)
+        return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    gs_context* c = (gs_context*)calloc(1, sizeof(gs_context));
+    if (!c) return fail(GS_ERR_INVALID_ARGUMENT, "out of host memory");
+    c->s = s;
+    carve_workspace(s, (char*)workspace, &c->ws);
+    c->state = kCreated;
+    *out = c;
+    return GS_OK;
+}
+
+gs_status gs_context_destroy(gs_context* ctx) {
+    free(ctx);
+    return GS_OK;
+}
+
+gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* cams, const gs_params* params,
+                     hipStream_t stream) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    if (!sc || !cams || !params) return fail(GS_ERR_INVALID_ARGUMENT, "null scene, cameras or params");
+    const Sizes& s = ctx->s;
+    if (sc->n != s.G) return fail(GS_ERR_INVALID_ARGUMENT, "scene has %lld Gaussians, context %lld",
+                                  (long long)sc->n, (long long)s.G);
+    if ((sc->sh_degree + 1) * (sc->sh_degree + 1) != s.d)
+        return fail(GS_ERR_INVALID_ARGUMENT, "scene SH degree differs from the context");
+    if (s.G > 0) {
+        const void* ptrs[5] = {sc->means, sc->quats, sc->scales, sc->opacities, sc->sh};
+        for (const void* p : ptrs) {
+            if (!p) return fail(GS_ERR_INVALID_ARGUMENT, "null Gaussian parameter pointer");
+            if (!aligned(p, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned Gaussian parameter pointer");
+        }
+    }
+    if (!(params->eps >= 0.0f) || !(params->den_min >= 0.0f) || !(params->lambda >= 0.0f) ||
+        !(params->near_plane > 0.0f) || !(params->far_plane > params->near_plane))
+        return fail(GS_ERR_INVALID_ARGUMENT, "invalid params");
+    for (int v = 0; v < s.V; ++v) {
+        const gs_camera& c = cams[v];
+        for (int k = 0; k < 9; ++k) ctx->cams.c[v][k] = c.R[k];
+        for (int k = 0; k < 3; ++k) ctx->cams.c[v][9 + k] = c.t[k];
+        ctx->cams.c[v][12] = c.fx;
+        ctx->cams.c[v][13] = c.fy;
+        ctx->cams.c[v][14] = c.cx;
+        ctx->cams.c[v][15] = c.cy;
+        if (!(c.fx > 0.0f) || !(c.fy > 0.0f)) return fail(GS_ERR_INVALID_ARGUMENT, "focal lengths must be > 0");
+    }
+    ctx->scene = *sc;
+    ctx->params = *params;
+    ctx->state = kCreated;
+    hipError_t e = launch_project(*sc, ctx->cams, s, params->near_plane, params->far_plane, ctx->ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "project");
+    ctx->state = kProjected;
+    return GS_OK;
+}
+
+gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    if (ctx->state < kProjected) return fail(GS_ERR_STATE, "gs_bin_sort before gs_project");
+    const Sizes& s = ctx->s;
+    Workspace& ws = ctx->ws;
+    hipError_t e;
+    // 1. depth sort of the records (keys ping-pong through offsets, which the scan rewrites next)
+    uint32_t* rid_sorted = nullptr;
+    e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b, nullptr,
+                          nullptr, nullptr, ws.hist, ws.scan_blocks, ws.scan_total, stream, nullptr, &rid_sorted);
+    if (e != hipSuccess) return hip_fail(e, "depth sort");
+    // 2. pair offsets in depth order
+    e = launch_scan_u32(ws.tiles_touched, rid_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream);
+    if (e != hipSuccess) return hip_fail(e, "scan");
+    uint64_t total = 0;
+    e = hipMemcpyAsync(&total, ws.scan_total, sizeof total, hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "pair count copy");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "pair count sync");
+    if (n_pairs_out) *n_pairs_out = total;
+    ctx->n_pairs = total;
+    if (total > s.max_pairs) {
+        ctx->state = kCreated;
+        return fail(GS_ERR_WORKSPACE_TOO_SMALL, "%llu pairs exceed max_pairs %llu", (unsigned long long)total,
+                    (unsigned long long)s.max_pairs);
+    }
+    // 3. emit pairs in depth order, 4. stable sort by tile, 5. ranges
+    e = launch_emit(s, ws, rid_sorted, stream);
+    if (e != hipSuccess) return hip_fail(e, "emit");
+    const int64_t tiles = (int64_t)s.V * s.T;
+    uint32_t* sorted_keys = nullptr;
+    e = launch_radix_sort(ws.pkey_a, nullptr, (int64_t)total, bits_for((uint64_t)tiles), ws.pkey_b, ws.pkey_a,
+                          ws.pval_a, ws.pval_b, ws.pair_g, ws.sorted_g, ws.inv, ws.hist, ws.scan_blocks,
+                          ws.scan_total, stream, &sorted_keys, nullptr);
+    if (e != hipSuccess) return hip_fail(e, "tile sort");
+    e = launch_ranges(sorted_keys, (int64_t)total, ws.ranges, tiles, stream);
+    if (e != hipSuccess) return hip_fail(e, "ranges");
+    ctx->state = kBinned;
+    return GS_OK;
+}
+
+gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_contrib, hipStream_t stream) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    if (ctx->state < kBinned) return fail(GS_ERR_STATE, "gs_render before gs_bin_sort");
+    if ((color && !aligned(color, 4)) || (T_final && !aligned(T_final, 4)) || (n_contrib && !aligned(n_contrib, 4)))
+        return fail(GS_ERR_INVALID_ARGUMENT, "misaligned output pointer");
+    hipError_t e = launch_render(ctx->s, ctx->ws, ctx->params.background, color, T_final, n_contrib, stream);
+    if (e != hipSuccess) return hip_fail(e, "render");
+    ctx->state = kRendered;
+    return GS_OK;
+}
+
+gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens, hipStream_t stream) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    if (ctx->state < kRendered) return fail(GS_ERR_STATE, "gs_score_replay before gs_render");
+    if (!observed || !tokens) return fail(GS_ERR_INVALID_ARGUMENT, "null observed or tokens");
+    if (!aligned(observed, 4) || !aligned(tokens, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    hipError_t e = launch_replay(ctx->s, ctx->ws, observed, ctx->params.eps, ctx->params.den_min, stream);
+    if (e != hipSuccess) return hip_fail(e, "replay");
+    e = launch_finalize(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.eps, ctx->params.lambda, tokens, stream);
+    if (e != hipSuccess) return hip_fail(e, "finalize");
+    return GS_OK;
+}
+
+const char* gs_status_string(gs_status s) {
+    switch (s) {
+        case GS_OK: return "GS_OK";
+        case GS_ERR_INVALID_ARGUMENT: return "GS_ERR_INVALID_ARGUMENT";
+        case GS_ERR_WORKSPACE_TOO_SMALL: return "GS_ERR_WORKSPACE_TOO_SMALL";
+        case GS_ERR_STATE: return "GS_ERR_STATE";
+        case GS_ERR_HIP: return "GS_ERR_HIP";
+        case GS_ERR_UNSUPPORTED: return "GS_ERR_UNSUPPORTED";
+    }
+    return "GS_ERR_UNKNOWN";
+}
+
+const char* gs_last_error(void) { return g_err; }
+
+gs_status gs_debug_exp2(const float* in, float* out, int64_t n, hipStream_t stream) {
+    if (n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
+    if (n > 0 && (!in || !out)) return fail(GS_ERR_INVALID_ARGUMENT, "null pointer");
+    hipError_t e = launch_exp2(in, out, n, stream);
+    if (e != hipSuccess) return hip_fail(e, "exp2");
+    return GS_OK;
+}
+
+gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes, hipStream_t stream) {
+    if (!ctx || !dst) return fail(GS_ERR_INVALID_ARGUMENT, "null context or destination");
+    const Sizes& s = ctx->s;
+    const Workspace& ws = ctx->ws;
+    const size_t VG = (size_t)s.VG;
+    hipError_t e = hipSuccess;
+    switch (kind) {
+        case GS_EXPORT_RECORDS: {
+            if (ctx->state < kProjected) return fail(GS_ERR_STATE, "records exist after gs_project");
+            if (bytes < 48 * VG) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
+            char* d = (char*)dst;
+            e = hipMemcpyAsync(d, ws.rec0, 16 * VG, hipMemcpyDeviceToDevice, stream);
+            if (e == hipSuccess) e = hipMemcpyAsync(d + 16 * VG, ws.rec1, 16 * VG, hipMemcpyDeviceToDevice, stream);
+            if (e == hipSuccess) e = hipMemcpyAsync(d + 32 * VG, ws.rec2, 16 * VG, hipMemcpyDeviceToDevice, stream);
+            break;
+        }
+        case GS_EXPORT_DEPTH_KEYS:
+            if (ctx->state < kProjected) return fail(GS_ERR_STATE, "depth keys exist after gs_project");
+            if (bytes < 4 * VG) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
+            e = hipMemcpyAsync(dst, ws.depth_key, 4 * VG, hipMemcpyDeviceToDevice, stream);
+            break;
+        case GS_EXPORT_SORTED_IDS:
+            if (ctx->state < kBinned) return fail(GS_ERR_STATE, "lists exist after gs_bin_sort");
+            if (bytes < 4 * (size_t)ctx->n_pairs) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
+            if (ctx->n_pairs) e = hipMemcpyAsync(dst, ws.sorted_g, 4 * (size_t)ctx->n_pairs, hipMemcpyDeviceToDevice, stream);
+            break;
+        case GS_EXPORT_RANGES: {
+            const size_t tiles = (size_t)s.V * s.T;
+            if (ctx->state < kBinned) return fail(GS_ERR_STATE, "ranges exist after gs_bin_sort");
+            if (bytes < 8 * tiles) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
+            e = hipMemcpyAsync(dst, ws.ranges, 8 * tiles, hipMemcpyDeviceToDevice, stream);
+            break;
+        }
+        default:
+            return fail(GS_ERR_INVALID_ARGUMENT, "unknown export kind %d", kind);
+    }
+    if (e != hipSuccess) return hip_fail(e, "export copy");
+    return GS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,148 @@
+// gsr_device.hpp -- device-side definitions shared by the gfx950 kernels.
+//
+// Floating-point decisions (culling, radius, tile rectangle, colour clamp,
+// alpha skip/clamp, early termination, suffix-denominator mask) follow a fixed
+// float32 operation order with no FMA contraction (the library is compiled
+// with -ffp-contract=off; fused multiply-adds appear only where written as
+// __builtin_fmaf).  This makes every such integer decision reproducible by any
+// implementation of the same order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gsr {
+
+constexpr int kTile = 16;
+constexpr int kMaxViews = 32;
+
+// Thresholds of the standard 3DGS compositing rule (readings of "the original
+// gsplat tile binning and front-to-back compositing" of the Stage 1 step).
+constexpr float kAlphaMax = 0.99f;
+constexpr float kAlphaMin = 0x1.010102p-8f;   // float32 nearest to 1/255
+constexpr float kTMin = 1e-4f;
+constexpr float kDilation = 0.3f;
+constexpr float kEigFloor = 0.1f;
+constexpr float kFovClamp = 1.3f;
+constexpr float kECutoff = -8.0f;             // 2^-8 < 1/255: no alpha can pass below this
+constexpr float kNegLog2e = -0x1.715476p+0f;  // float32 nearest to -log2(e)
+constexpr float kNegHalfLog2e = -0x1.715476p-1f;
+
+// 2^e for e in [-8, 1/2]: k = rint(e), f = e - k (exact, |f| <= 1/2), 2^f by
+// the degree-7 Taylor polynomial sum_j (f ln 2)^j / j! with each coefficient
+// rounded to float32 (Horner, fused multiply-adds), then exact scaling by 2^k.
+__device__ __forceinline__ float exp2_spec(float e) {
+    const float k = __builtin_rintf(e);
+    const float f = e - k;
+    float p = 0x1.ffcbfcp-17f;
+    p = __builtin_fmaf(p, f, 0x1.430912p-13f);
+    p = __builtin_fmaf(p, f, 0x1.5d87fep-10f);
+    p = __builtin_fmaf(p, f, 0x1.3b2ab6p-7f);
+    p = __builtin_fmaf(p, f, 0x1.c6b08ep-5f);
+    p = __builtin_fmaf(p, f, 0x1.ebfbe0p-3f);
+    p = __builtin_fmaf(p, f, 0x1.62e430p-1f);
+    p = __builtin_fmaf(p, f, 1.0f);
+    return __builtin_amdgcn_ldexpf(p, (int)k);
+}
+
+// Real spherical harmonics up to degree 3 (m = -l..l order, graphics sign
+// convention), float32 normalisation constants.
+constexpr float kSH0 = 0x1.20dd76p-2f;     // 1/(2 sqrt(pi))
+constexpr float kSH1 = 0x1.f45438p-2f;     // sqrt(3/(4 pi))
+constexpr float kSH2a = 0x1.17b142p+0f;    // sqrt(15/pi)/2
+constexpr float kSH2b = 0x1.42f602p-2f;    // sqrt(5/pi)/4
+constexpr float kSH2c = 0x1.17b142p-1f;    // sqrt(15/pi)/4
+constexpr float kSH3a = 0x1.2e1a32p-1f;    // sqrt(35/(2 pi))/4
+constexpr float kSH3b = 0x1.71ff8ep+1f;    // sqrt(105/pi)/2
+constexpr float kSH3c = 0x1.d403d0p-2f;    // sqrt(21/(2 pi))/4
+constexpr float kSH3d = 0x1.7e21f0p-2f;    // sqrt(7/pi)/4
+constexpr float kSH3e = 0x1.71ff8ep+0f;    // sqrt(105/pi)/4
+
+__device__ __forceinline__ void sh_basis_f32(float x, float y, float z, int d, float* B) {
+    B[0] = kSH0;
+    if (d <= 1) return;
+    B[1] = -kSH1 * y;
+    B[2] = kSH1 * z;
+    B[3] = -kSH1 * x;
+    if (d <= 4) return;
+    const float xx = x * x, yy = y * y, zz = z * z;
+    const float xy = x * y, yz = y * z, xz = x * z;
+    B[4] = kSH2a * xy;
+    B[5] = -kSH2a * yz;
+    B[6] = kSH2b * ((2.0f * zz - xx) - yy);
+    B[7] = -kSH2a * xz;
+    B[8] = kSH2c * (xx - yy);
+    if (d <= 9) return;
+    B[9] = (-kSH3a * y) * (3.0f * xx - yy);
+    B[10] = (kSH3b * xy) * z;
+    B[11] = (-kSH3c * y) * ((4.0f * zz - xx) - yy);
+    B[12] = (kSH3d * z) * ((2.0f * zz - 3.0f * xx) - 3.0f * yy);
+    B[13] = (-kSH3c * x) * ((4.0f * zz - xx) - yy);
+    B[14] = (kSH3e * z) * (xx - yy);
+    B[15] = (-kSH3a * x) * (xx - 3.0f * yy);
+}
+
+__device__ __forceinline__ void sh_basis_f64(double x, double y, double z, int d, double* B) {
+    const double c0 = 0.28209479177387814, c1 = 0.48860251190291992;
+    const double c2a = 1.0925484305920792, c2b = 0.31539156525252005, c2c = 0.54627421529603959;
+    const double c3a = 0.59004358992664352, c3b = 2.8906114426405538, c3c = 0.45704579946446572;
+    const double c3d = 0.3731763325901154, c3e = 1.4453057213202769;
+    B[0] = c0;
+    if (d <= 1) return;
+    B[1] = -c1 * y;
+    B[2] = c1 * z;
+    B[3] = -c1 * x;
+    if (d <= 4) return;
+    const double xx = x * x, yy = y * y, zz = z * z;
+    B[4] = c2a * x * y;
+    B[5] = -c2a * y * z;
+    B[6] = c2b * (2.0 * zz - xx - yy);
+    B[7] = -c2a * x * z;
+    B[8] = c2c * (xx - yy);
+    if (d <= 9) return;
+    B[9] = -c3a * y * (3.0 * xx - yy);
+    B[10] = c3b * x * y * z;
+    B[11] = -c3c * y * (4.0 * zz - xx - yy);
+    B[12] = c3d * z * (2.0 * zz - 3.0 * xx - 3.0 * yy);
+    B[13] = -c3c * x * (4.0 * zz - xx - yy);
+    B[14] = c3e * z * (xx - yy);
+    B[15] = -c3a * x * (xx - 3.0 * yy);
+}
+
+// Camera as passed by value to the kernels: [R (9), t (3), fx, fy, cx, cy].
+struct CamPack {
+    float c[kMaxViews][16];
+};
+
+// Per-(view, Gaussian) record, three float4 (48 B) at index rid = v * G + g:
+//   r0 = {mx, my, qa, qb}
+//   r1 = {qc, opacity, pre_r, pre_g}
+//   r2 = {pre_b, bits(pair offset), bits(x0 | y0 << 16), bits(x1 | y1 << 16)}
+// The Gaussian weight at pixel offset (dx, dy) = p - mu is 2^(qa dx^2 + qb dx dy + qc dy^2),
+// i.e. qa = -log2(e)/2 A, qb = -log2(e) B, qc = -log2(e)/2 C for the conic [[A, B], [B, C]].
+
+__device__ __forceinline__ float clamp_colour(float pre) { return pre >= 0.0f ? pre : 0.0f; }
+
+// Evaluate one list entry at one pixel with the canonical float32 order.
+// Returns false when the entry is skipped (too far or alpha below 1/255).
+__device__ __forceinline__ bool eval_alpha(float4 r0, float qc, float opac, float px, float py,
+                                           float& dx, float& dy, float& alpha, bool& clamped) {
+    dx = px - r0.x;
+    dy = py - r0.y;
+    const float e = __builtin_fmaf(dx, __builtin_fmaf(r0.z, dx, r0.w * dy), (qc * dy) * dy);
+    if (!(e >= kECutoff)) return false;
+    const float aG = opac * exp2_spec(e);
+    clamped = !(aG < kAlphaMax);
+    alpha = clamped ? kAlphaMax : aG;
+    return alpha >= kAlphaMin;
+}
+
+// Compensated (Kahan) accumulation of the prefix colour; the true sum is hi - comp.
+__device__ __forceinline__ void kahan_add(float& hi, float& comp, float x) {
+    const float y = x - comp;
+    const float t = hi + y;
+    comp = (t - hi) - y;
+    hi = t;
+}
+
+}  // namespace gsr

@@ -1,0 +1,87 @@
+// gsr_internal.hpp -- host-side context and kernel launchers (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gsr.h"
+#include "gsr_device.hpp"
+
+namespace gsr {
+
+// Workspace carve-up.  Every array lives in caller-owned device memory.
+struct Workspace {
+    // per (view, Gaussian) record, rid = v * G + g
+    float4* rec0;
+    float4* rec1;
+    float4* rec2;
+    uint32_t* depth_key;   // depth bits, 0xffffffff when culled
+    uint32_t* tiles_touched;
+    // depth sort (ping-pong) and the pair offsets in depth order
+    uint32_t* dkey_b;
+    uint32_t* drid_a;
+    uint32_t* drid_b;
+    uint32_t* offsets;     // exclusive scan of tiles_touched in depth order
+    // scan / histogram scratch
+    uint64_t* scan_blocks; // per-block sums (u64), then exclusive offsets
+    uint64_t* scan_total;  // total of the last scan
+    uint32_t* hist;        // radix histograms, digit-major
+    // (tile, Gaussian) pairs
+    uint32_t* pkey_a;
+    uint32_t* pkey_b;
+    uint32_t* pval_a;
+    uint32_t* pval_b;
+    uint32_t* pair_g;      // Gaussian of each emitted pair (emit order)
+    uint32_t* sorted_g;    // Gaussian of each pair in (tile, depth, id) order
+    uint32_t* inv;         // emit index -> sorted position
+    uint2* ranges;         // per tile [start, end)
+    uint32_t* tile_done;   // per tile: end of the prefix the replay processed
+    float4* partials;      // per sorted pair: {W, U_a, U_mx, U_my}, {U_r, U_g, U_b, n_pix}
+    float4* pixel;         // per pixel: rendered colour (rgb), final transmittance
+};
+
+struct Sizes {
+    int64_t G;
+    int32_t d;
+    int32_t V;
+    int32_t W, H, TX, TY, T;
+    int64_t VG;
+    uint64_t max_pairs;
+    int64_t scan_blocks_cap;
+    int64_t hist_cap;
+};
+
+size_t carve_workspace(const Sizes& s, char* base, Workspace* ws);  // base == nullptr: size only
+Sizes make_sizes(const gs_dims& d);
+
+// ---- launchers (return hipGetLastError of the launch) ----------------------
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
+hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, float near_plane,
+                          float far_plane, Workspace& ws, hipStream_t st);
+// exclusive scan of in[idx[k]] (idx may be null) into out (u32); total -> *total (device u64)
+hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, int64_t n, uint32_t* out,
+                           uint64_t* block_scratch, uint64_t* total, hipStream_t st);
+// Stable LSD radix sort of (keys, vals) on bits [0, bits); vals_in == null means
+// identity values (the input index).  Pass p writes kbuf[p & 1] / vbuf[p & 1], so
+// the buffers must differ from each other and from keys_in/vals_in except that
+// kbuf1/vbuf1 may alias keys_in/vals_in (consumed by pass 0).  With gather != null
+// the final pass stores gather_out[pos] = gather[val] and inv[val] = pos instead
+// of the value.  *keys_out / *vals_out receive the arrays holding the result.
+hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
+                             uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
+                             const uint32_t* gather, uint32_t* gather_out, uint32_t* inv, uint32_t* hist,
+                             uint64_t* block_scratch, uint64_t* total, hipStream_t st, uint32_t** keys_out,
+                             uint32_t** vals_out);
+hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st);
+hipError_t launch_ranges(const uint32_t* sorted_keys, int64_t n, uint2* ranges, int64_t n_tiles,
+                         hipStream_t st);
+hipError_t launch_render(const Sizes& s, const Workspace& ws, const float bg[3], float* color,
+                         float* T_final, int32_t* n_contrib, hipStream_t st);
+hipError_t launch_replay(const Sizes& s, const Workspace& ws, const float* observed, float eps,
+                         float den_min, hipStream_t st);
+hipError_t launch_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s,
+                           const Workspace& ws, float eps, float lambda, float* tokens, hipStream_t st);
+hipError_t launch_exp2(const float* in, float* out, int64_t n, hipStream_t st);
+
+}  // namespace gsr

@@ -1,0 +1,108 @@
+// render.hip -- front-to-back compositing per 16x16 tile on gfx950.
+//
+// Stage 1 of the Renderer Score Tokens proposal ("Two-Stage Algorithm",
+// Standard Render): rendered colour, final transmittance and contributor count
+// per pixel, over the depth-ordered tile lists built by the binning pass.
+//
+// One 256-thread block per tile; the four wave64s each own an 8x8 pixel
+// quadrant, so a wave's lanes stay spatially coherent and a wave whose 64
+// pixels are all saturated skips the evaluation entirely.  Batches of 256 list
+// entries are gathered (one per thread) into LDS -- 36 bytes per entry:
+// centre, exponent coefficients, opacity, clamped colour -- and read back as
+// broadcasts.  Alpha decisions use the float32 canonical order and the
+// specified exponential; the prefix colour is accumulated with compensated
+// (Kahan) summation so that the replay can recover the suffix accurately.
+#include "gsr_internal.hpp"
+
+namespace gsr {
+
+constexpr int kRenderBatch = 256;
+
+__global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
+                                                const float4* __restrict__ rec0, const float4* __restrict__ rec1,
+                                                const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
+                                                float bg0, float bg1, float bg2, float* __restrict__ color,
+                                                float* __restrict__ T_out, int32_t* __restrict__ n_out,
+                                                float4* __restrict__ pixel) {
+    __shared__ float4 s0[kRenderBatch];
+    __shared__ float4 s1[kRenderBatch];  // {qc, opacity, colour r, colour g}
+    __shared__ float s2[kRenderBatch];   // colour b
+
+    const int tile = blockIdx.x;
+    const int v = tile / T;
+    const int t = tile - v * T;
+    const int ty = t / TX, tx = t - ty * TX;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pxi = tx * kTile + (wave & 1) * 8 + (lane & 7);
+    const int pyi = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
+    const bool inside = pxi < W && pyi < H;
+    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    const uint2 rg = ranges[tile];
+    const int64_t vG = (int64_t)v * G;
+
+    float Tr = 1.0f;
+    float h0 = 0.f, h1 = 0.f, h2 = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
+    int n = 0;
+    bool done = !inside;
+
+    for (uint32_t base = rg.x; base < rg.y; base += kRenderBatch) {
+        if (__syncthreads_count(!done) == 0) break;
+        const uint32_t i = base + threadIdx.x;
+        if (i < rg.y) {
+            const int64_t rid = vG + sorted_g[i];
+            const float4 a = rec0[rid];
+            const float4 b = rec1[rid];
+            const float cb = rec2[rid].x;
+            s0[threadIdx.x] = a;
+            s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
+            s2[threadIdx.x] = clamp_colour(cb);
+        }
+        __syncthreads();
+        const int cnt = (int)min((uint32_t)kRenderBatch, rg.y - base);
+        if (!done) {
+            for (int j = 0; j < cnt; ++j) {
+                const float4 a = s0[j];
+                const float4 b = s1[j];
+                float dx, dy, alpha;
+                bool clamped;
+                if (!eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped)) continue;
+                const float tT = Tr * (1.0f - alpha);
+                if (tT < kTMin) {
+                    done = true;
+                    break;
+                }
+                const float w = alpha * Tr;
+                kahan_add(h0, c0, b.z * w);
+                kahan_add(h1, c1, b.w * w);
+                kahan_add(h2, c2, s2[j] * w);
+                Tr = tT;
+                ++n;
+            }
+        }
+    }
+    if (!inside) return;
+    kahan_add(h0, c0, Tr * bg0);
+    kahan_add(h1, c1, Tr * bg1);
+    kahan_add(h2, c2, Tr * bg2);
+    const float o0 = h0 - c0, o1 = h1 - c1, o2 = h2 - c2;
+    const int64_t pix = ((int64_t)v * H + pyi) * W + pxi;
+    if (color) {
+        color[3 * pix] = o0;
+        color[3 * pix + 1] = o1;
+        color[3 * pix + 2] = o2;
+    }
+    if (T_out) T_out[pix] = Tr;
+    if (n_out) n_out[pix] = n;
+    pixel[pix] = make_float4(o0, o1, o2, Tr);
+}
+
+hipError_t launch_render(const Sizes& s, const Workspace& ws, const float bg[3], float* color, float* T_final,
+                         int32_t* n_contrib, hipStream_t st) {
+    const int64_t tiles = (int64_t)s.V * s.T;
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, ws.sorted_g, ws.rec0, ws.rec1,
+                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel);
+    return hipGetLastError();
+}
+
+}  // namespace gsr

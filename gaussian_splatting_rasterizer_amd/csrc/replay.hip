@@ -1,0 +1,400 @@
+// replay.hip -- analytic score replay and token assembly on gfx950.
+//
+// Stage 2 of the Renderer Score Tokens proposal ("Two-Stage Algorithm",
+// Analytic Score Replay) and the "Exact Score Operators" / "Final Token".
+//
+// k_replay: the same tiles, lists, order and float32 decisions as the render.
+// Each pixel re-walks its list keeping the prefix colour P (compensated, so it
+// is bit-identical to the render's) and the transmittance T, and for every
+// contribution forms
+//     S   = C_hat - P - T alpha c                     (suffix times T(1-alpha))
+//     C+  = S / (T (1 - alpha) + eps)                 (suffix equation)
+//     rho = <r, c - C+>,  r = C_hat - C_obs            (residual-suffix contrast)
+//     w   = T alpha                                   (visibility weight)
+//     M   = [o G < 0.99] and [T (1 - alpha) >= den_min]   (mask)
+// and the eight per-pixel partials
+//     W += w, U_a += M w rho, U_mu += M w rho (p - mu), U_c += w r, n_pix += 1.
+// These suffice for every score block: with M set, alpha = o G, so
+// T o grad_mu G rho = conic (p - mu) w rho and T alpha (1 - o) rho = (1 - o) w rho;
+// the colour clamp mask and the SH basis are constant over a (Gaussian, view).
+// The 64 lanes of a wave are reduced with a reduce-scatter butterfly (four
+// exchange steps leave lane l holding component l >> 3 summed over 64 lanes,
+// then three in-group steps), only when some lane contributed; the four waves
+// meet in LDS and one 32-byte partial per (tile, Gaussian) pair is stored at
+// the pair's sorted position -- no atomics, so the result is deterministic.
+// Pairs after the tile's early termination are never written; tile_done
+// records where each tile stopped.
+//
+// k_finalize: one thread per Gaussian sums its pairs per view (through the
+// emit-order -> sorted-position map), then in float64
+//     q_v = eps + W_v,  Q = eps + sum_v q_v,  gamma_v = q_v / Q
+//     b_mu = sum_v gamma_v J_v^T s_mu_v = (1/Q) sum_v J_v^T conic_v U_mu_v
+//     s_a  = (1/Q) sum_v (1 - o) U_a_v,   s_SH = (1/Q) sum_v M_color (B_v (x) U_c_v)
+//     A    = lambda I + (1/Q) sum_v q_v J_v^T J_v
+// with J_v the unclamped pixel-projection Jacobian, eigenvalues of A by the
+// closed-form trigonometric solution for symmetric 3x3 matrices (descending),
+// and writes z = [b_mu, s_a, s_SH, log Q, eig/(tr A + eps), log(tr A + eps)].
+#include "gsr_internal.hpp"
+
+namespace gsr {
+
+constexpr int kReplayBatch = 128;
+
+// Reduce eight values over the 64 lanes; returns in every lane the total of
+// component (lane >> 3) & 7.
+__device__ __forceinline__ float wave_reduce8(const float (&x)[8], int lane) {
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+    float a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float send = b5 ? x[i] : x[i + 4];
+        const float keep = b5 ? x[i + 4] : x[i];
+        a[i] = keep + __shfl_xor(send, 32, 64);
+    }
+    float b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = b4 ? a[i] : a[i + 2];
+        const float keep = b4 ? a[i + 2] : a[i];
+        b[i] = keep + __shfl_xor(send, 16, 64);
+    }
+    const float send = b3 ? b[0] : b[1];
+    float c = (b3 ? b[1] : b[0]) + __shfl_xor(send, 8, 64);
+    c += __shfl_xor(c, 4, 64);
+    c += __shfl_xor(c, 2, 64);
+    c += __shfl_xor(c, 1, 64);
+    return c;
+}
+
+__global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
+                                                const float4* __restrict__ rec0, const float4* __restrict__ rec1,
+                                                const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
+                                                const float4* __restrict__ pixel, const float* __restrict__ observed,
+                                                float eps, float den_min, float4* __restrict__ partials,
+                                                uint32_t* __restrict__ tile_done) {
+    __shared__ float4 s0[kReplayBatch];
+    __shared__ float4 s1[kReplayBatch];
+    __shared__ float s2[kReplayBatch];
+    __shared__ __align__(16) float sp[4][kReplayBatch][8];
+
+    const int tile = blockIdx.x;
+    const int v = tile / T;
+    const int t = tile - v * T;
+    const int ty = t / TX, tx = t - ty * TX;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pxi = tx * kTile + (wave & 1) * 8 + (lane & 7);
+    const int pyi = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
+    const bool inside = pxi < W && pyi < H;
+    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    const uint2 rg = ranges[tile];
+    const int64_t vG = (int64_t)v * G;
+
+    float Ch0 = 0.f, Ch1 = 0.f, Ch2 = 0.f, r0 = 0.f, r1 = 0.f, r2 = 0.f;
+    if (inside) {
+        const int64_t pix = ((int64_t)v * H + pyi) * W + pxi;
+        const float4 c = pixel[pix];
+        Ch0 = c.x;
+        Ch1 = c.y;
+        Ch2 = c.z;
+        r0 = Ch0 - observed[3 * pix];
+        r1 = Ch1 - observed[3 * pix + 1];
+        r2 = Ch2 - observed[3 * pix + 2];
+    }
+    float Tr = 1.0f;
+    float h0 = 0.f, h1 = 0.f, h2 = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
+    bool done = !inside;
+
+    uint32_t base = rg.x;
+    for (; base < rg.y; base += kReplayBatch) {
+        if (__syncthreads_count(!done) == 0) break;
+        const uint32_t i = base + threadIdx.x;
+        if (threadIdx.x < kReplayBatch && i < rg.y) {
+            const int64_t rid = vG + sorted_g[i];
+            const float4 a = rec0[rid];
+            const float4 b = rec1[rid];
+            const float cb = rec2[rid].x;
+            s0[threadIdx.x] = a;
+            s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
+            s2[threadIdx.x] = clamp_colour(cb);
+        }
+        __syncthreads();
+        const int cnt = (int)min((uint32_t)kReplayBatch, rg.y - base);
+        const bool wave_live = __ballot(!done) != 0ull;
+        if (wave_live) {
+            for (int j = 0; j < cnt; ++j) {
+                float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                bool contrib = false;
+                if (!done) {
+                    const float4 a = s0[j];
+                    const float4 b = s1[j];
+                    float dx, dy, alpha;
+                    bool clamped;
+                    if (eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped)) {
+                        const float tT = Tr * (1.0f - alpha);
+                        if (tT < kTMin) {
+                            done = true;
+                        } else {
+                            contrib = true;
+                            const float cr = b.z, cg = b.w, cbl = s2[j];
+                            const float w = alpha * Tr;
+                            const float x0 = cr * w, x1 = cg * w, x2 = cbl * w;
+                            // suffix (times T (1 - alpha)) from the compensated prefix hi - comp
+                            const float S0 = ((Ch0 - h0) + c0) - x0;
+                            const float S1 = ((Ch1 - h1) + c1) - x1;
+                            const float S2 = ((Ch2 - h2) + c2) - x2;
+                            const float inv_den = __builtin_amdgcn_rcpf(tT + eps);
+                            const float rho = r0 * (cr - S0 * inv_den) + r1 * (cg - S1 * inv_den) +
+                                              r2 * (cbl - S2 * inv_den);
+                            const bool m = !clamped && (tT >= den_min);
+                            const float mw = m ? w * rho : 0.0f;
+                            x[0] = w;
+                            x[1] = mw;
+                            x[2] = mw * dx;
+                            x[3] = mw * dy;
+                            x[4] = w * r0;
+                            x[5] = w * r1;
+                            x[6] = w * r2;
+                            x[7] = 1.0f;
+                            kahan_add(h0, c0, x0);
+                            kahan_add(h1, c1, x1);
+                            kahan_add(h2, c2, x2);
+                            Tr = tT;
+                        }
+                    }
+                }
+                float red = 0.0f;
+                if (__ballot(contrib) != 0ull) red = wave_reduce8(x, lane);
+                if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
+            }
+        } else {
+            for (int e = lane; e < cnt * 8; e += 64) (&sp[wave][0][0])[e] = 0.0f;
+        }
+        __syncthreads();
+        if (threadIdx.x < 2 * cnt) {
+            const int j = threadIdx.x >> 1, h = threadIdx.x & 1;
+            float4 acc = *reinterpret_cast<const float4*>(&sp[0][j][4 * h]);
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                const float4 q = *reinterpret_cast<const float4*>(&sp[w][j][4 * h]);
+                acc.x += q.x;
+                acc.y += q.y;
+                acc.z += q.z;
+                acc.w += q.w;
+            }
+            partials[2 * (int64_t)(base + j) + h] = acc;
+        }
+    }
+    if (threadIdx.x == 0) tile_done[tile] = base < rg.y ? base : rg.y;
+}
+
+hipError_t launch_replay(const Sizes& s, const Workspace& ws, const float* observed, float eps, float den_min,
+                         hipStream_t st) {
+    const int64_t tiles = (int64_t)s.V * s.T;
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, ws.sorted_g, ws.rec0, ws.rec1,
+                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, eps, den_min, ws.partials,
+                       ws.tile_done);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// finalize
+// ---------------------------------------------------------------------------
+__device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */, double ev[3]) {
+    const double a00 = A[0], a01 = A[1], a02 = A[2], a11 = A[3], a12 = A[4], a22 = A[5];
+    const double p1 = a01 * a01 + a02 * a02 + a12 * a12;
+    const double q = (a00 + a11 + a22) / 3.0;
+    double e0, e1, e2;
+    if (p1 == 0.0) {
+        e0 = a00;
+        e1 = a11;
+        e2 = a22;
+    } else {
+        const double b00 = a00 - q, b11 = a11 - q, b22 = a22 - q;
+        const double p2 = b00 * b00 + b11 * b11 + b22 * b22 + 2.0 * p1;
+        const double p = sqrt(p2 / 6.0);
+        const double ip = 1.0 / p;
+        const double c00 = b00 * ip, c11 = b11 * ip, c22 = b22 * ip;
+        const double c01 = a01 * ip, c02 = a02 * ip, c12 = a12 * ip;
+        double r = 0.5 * (c00 * (c11 * c22 - c12 * c12) - c01 * (c01 * c22 - c12 * c02) +
+                          c02 * (c01 * c12 - c11 * c02));
+        r = r < -1.0 ? -1.0 : (r > 1.0 ? 1.0 : r);
+        const double phi = acos(r) / 3.0;
+        e0 = q + 2.0 * p * cos(phi);
+        e2 = q + 2.0 * p * cos(phi + 2.0943951023931954923);
+        e1 = 3.0 * q - e0 - e2;
+    }
+    // sort descending
+    double t;
+    if (e0 < e1) { t = e0; e0 = e1; e1 = t; }
+    if (e1 < e2) { t = e1; e1 = e2; e2 = t; }
+    if (e0 < e1) { t = e0; e0 = e1; e1 = t; }
+    ev[0] = e0;
+    ev[1] = e1;
+    ev[2] = e2;
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void k_finalize(const float* __restrict__ means, const float* __restrict__ opac,
+                                                  int64_t G, int V, CamPack cams, int T, int TX,
+                                                  const float4* __restrict__ rec0, const float4* __restrict__ rec1,
+                                                  const float4* __restrict__ rec2, const uint32_t* __restrict__ inv,
+                                                  const uint32_t* __restrict__ tile_done,
+                                                  const float4* __restrict__ partials, double eps, double lambda,
+                                                  float* __restrict__ tokens) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= G) return;
+    const double mu[3] = {means[3 * g], means[3 * g + 1], means[3 * g + 2]};
+    const double one_minus_o = 1.0 - (double)opac[g];
+
+    double Q = eps;
+    double bnum[3] = {0.0, 0.0, 0.0};
+    double anum = 0.0;
+    double shnum[3 * D];
+#pragma unroll
+    for (int k = 0; k < 3 * D; ++k) shnum[k] = 0.0;
+    double Anum[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+
+    for (int v = 0; v < V; ++v) {
+        const int64_t rid = (int64_t)v * G + g;
+        const float4 r2 = rec2[rid];
+        const uint32_t lo = __float_as_uint(r2.z), hi = __float_as_uint(r2.w);
+        const int x0 = (int)(lo & 0xffffu), y0 = (int)(lo >> 16);
+        const int x1 = (int)(hi & 0xffffu), y1 = (int)(hi >> 16);
+        const int wx = x1 - x0;
+        const int cnt = wx * (y1 - y0);
+        const uint32_t off = __float_as_uint(r2.y);
+        double W = 0.0, Ua = 0.0, Umx = 0.0, Umy = 0.0, Uc0 = 0.0, Uc1 = 0.0, Uc2 = 0.0;
+        for (int j = 0; j < cnt; ++j) {
+            const uint32_t pos = inv[off + j];
+            const int tl = v * T + (y0 + j / wx) * TX + (x0 + j % wx);
+            if (pos >= tile_done[tl]) continue;
+            const float4 p0 = partials[2 * (int64_t)pos];
+            const float4 p1 = partials[2 * (int64_t)pos + 1];
+            W += p0.x;
+            Ua += p0.y;
+            Umx += p0.z;
+            Umy += p0.w;
+            Uc0 += p1.x;
+            Uc1 += p1.y;
+            Uc2 += p1.z;
+        }
+        const double q = eps + W;
+        Q += q;
+        if (cnt == 0) continue;  // culled in this view: J = 0, no scores
+
+        const float4 a0 = rec0[rid];
+        const float4 a1 = rec1[rid];
+        const double ca = (double)a0.z / (double)kNegHalfLog2e;
+        const double cb = (double)a0.w / (double)kNegLog2e;
+        const double cc = (double)a1.x / (double)kNegHalfLog2e;
+        const double smx = ca * Umx + cb * Umy;
+        const double smy = cb * Umx + cc * Umy;
+
+        const float* cam = cams.c[v];
+        double R[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) R[k] = cam[k];
+        const double t0 = cam[9], t1 = cam[10], t2 = cam[11];
+        const double fx = cam[12], fy = cam[13];
+        const double tcx = R[0] * mu[0] + R[1] * mu[1] + R[2] * mu[2] + t0;
+        const double tcy = R[3] * mu[0] + R[4] * mu[1] + R[5] * mu[2] + t1;
+        const double tcz = R[6] * mu[0] + R[7] * mu[1] + R[8] * mu[2] + t2;
+        const double iz = 1.0 / tcz;
+        const double jp00 = fx * iz, jp02 = -fx * tcx * iz * iz;
+        const double jp11 = fy * iz, jp12 = -fy * tcy * iz * iz;
+        double J0[3], J1[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            J0[k] = jp00 * R[k] + jp02 * R[6 + k];
+            J1[k] = jp11 * R[3 + k] + jp12 * R[6 + k];
+        }
+#pragma unroll
+        for (int k = 0; k < 3; ++k) bnum[k] += J0[k] * smx + J1[k] * smy;
+        anum += one_minus_o * Ua;
+        Anum[0] += q * (J0[0] * J0[0] + J1[0] * J1[0]);
+        Anum[1] += q * (J0[0] * J0[1] + J1[0] * J1[1]);
+        Anum[2] += q * (J0[0] * J0[2] + J1[0] * J1[2]);
+        Anum[3] += q * (J0[1] * J0[1] + J1[1] * J1[1]);
+        Anum[4] += q * (J0[1] * J0[2] + J1[1] * J1[2]);
+        Anum[5] += q * (J0[2] * J0[2] + J1[2] * J1[2]);
+
+        // SH basis along the view direction; clamp mask from the colour sign
+        const double ccx = -(R[0] * t0 + R[3] * t1 + R[6] * t2);
+        const double ccy = -(R[1] * t0 + R[4] * t1 + R[7] * t2);
+        const double ccz = -(R[2] * t0 + R[5] * t1 + R[8] * t2);
+        const double dx = mu[0] - ccx, dy = mu[1] - ccy, dz = mu[2] - ccz;
+        const double il = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
+        double B[D];
+        sh_basis_f64(dx * il, dy * il, dz * il, D, B);
+        const double m0 = a1.z >= 0.0f ? Uc0 : 0.0;
+        const double m1 = a1.w >= 0.0f ? Uc1 : 0.0;
+        const double m2 = r2.x >= 0.0f ? Uc2 : 0.0;
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+            shnum[3 * k] += B[k] * m0;
+            shnum[3 * k + 1] += B[k] * m1;
+            shnum[3 * k + 2] += B[k] * m2;
+        }
+    }
+
+    const double iQ = 1.0 / Q;
+    double A[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) A[k] = Anum[k] * iQ;
+    A[0] += lambda;
+    A[3] += lambda;
+    A[5] += lambda;
+    double ev[3];
+    sym3_eigen_desc(A, ev);
+    const double tr = A[0] + A[3] + A[5];
+    float* z = tokens + (int64_t)g * (9 + 3 * D);
+    z[0] = (float)(bnum[0] * iQ);
+    z[1] = (float)(bnum[1] * iQ);
+    z[2] = (float)(bnum[2] * iQ);
+    z[3] = (float)(anum * iQ);
+#pragma unroll
+    for (int k = 0; k < 3 * D; ++k) z[4 + k] = (float)(shnum[k] * iQ);
+    z[4 + 3 * D] = (float)log(Q);
+    const double itr = 1.0 / (tr + eps);
+    z[5 + 3 * D] = (float)(ev[0] * itr);
+    z[6 + 3 * D] = (float)(ev[1] * itr);
+    z[7 + 3 * D] = (float)(ev[2] * itr);
+    z[8 + 3 * D] = (float)log(tr + eps);
+}
+
+hipError_t launch_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
+                           float eps, float lambda, float* tokens, hipStream_t st) {
+    if (s.G == 0) return hipSuccess;
+    const dim3 block(128), grid((unsigned)((s.G + 127) / 128));
+#define GSR_LAUNCH_FINALIZE(DD)                                                                               \
+    hipLaunchKernelGGL(k_finalize<DD>, grid, block, 0, st, sc.means, sc.opacities, s.G, s.V, cams, s.T, s.TX, \
+                       ws.rec0, ws.rec1, ws.rec2, ws.inv, ws.tile_done, ws.partials, (double)eps,           \
+                       (double)lambda, tokens)
+    switch (s.d) {
+        case 1: GSR_LAUNCH_FINALIZE(1); break;
+        case 4: GSR_LAUNCH_FINALIZE(4); break;
+        case 9: GSR_LAUNCH_FINALIZE(9); break;
+        default: GSR_LAUNCH_FINALIZE(16); break;
+    }
+#undef GSR_LAUNCH_FINALIZE
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// diagnostic: the decision exponential over an array
+// ---------------------------------------------------------------------------
+__global__ void k_exp2(const float* __restrict__ in, float* __restrict__ out, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        out[i] = exp2_spec(in[i]);
+}
+
+hipError_t launch_exp2(const float* in, float* out, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_exp2, dim3((unsigned)blocks), dim3(256), 0, st, in, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace gsr

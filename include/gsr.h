@@ -1,0 +1,199 @@
+/*
+ * gsr.h -- C ABI of the MI355X (gfx950) Gaussian-splat renderer with analytic
+ * score replay.
+ *
+ * The method is the one of the page "Research Proposal: Renderer Score Tokens
+ * for Recurrent Gaussian Splatting":
+ *   Stage 1 (section "Two-Stage Algorithm", Stage 1: Standard Render): tile
+ *     binning and contributor sorting, front-to-back compositing giving the
+ *     rendered colour, the final transmittance and the contributor count; the
+ *     tile bins and sorted contributor indices stay inside the renderer
+ *     workspace and are never exposed as a per-pixel contributor tensor.
+ *   Stage 2 (Stage 2: Analytic Score Replay, suffix equation and masks): a
+ *     second traversal of the same bins in the same order that recovers the
+ *     suffix composite behind each contribution and accumulates per-Gaussian
+ *     scores, emitting only fixed-dimensional tokens.
+ *   Scores and tokens: section "Exact Score Operators" (opacity-logit score,
+ *     SH score, projected-centre mean score, projection Jacobian, cross-view
+ *     weight, covector pullback, conditioning matrix statistics, appearance
+ *     aggregation) and "Final Token and Updater" (token layout, dimension
+ *     9 + 3 d_SH).
+ *
+ * Calling sequence, all on one stream:  gs_project -> gs_bin_sort -> gs_render
+ * [-> gs_score_replay].  Each call returns a status and never aborts.
+ *
+ * Memory: every array argument is a DEVICE pointer unless marked "host".
+ * The caller owns every buffer (inputs, outputs and the workspace); the
+ * library never allocates or frees device memory.  Input pointers given to
+ * gs_project are borrowed until gs_score_replay (or the next gs_project)
+ * returns: the replay re-reads means and opacities.
+ *
+ * Errors: a call that returns anything but GS_OK has launched no work when the
+ * error is GS_ERR_INVALID_ARGUMENT or GS_ERR_STATE; gs_last_error() gives a
+ * thread-local message for the last failure on the calling thread.
+ *
+ * Threading: a context is used from one thread and one stream at a time.
+ */
+#ifndef GSR_H
+#define GSR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GSR_API __attribute__((visibility("default")))
+
+typedef enum {
+    GS_OK = 0,
+    GS_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size, unsupported degree */
+    GS_ERR_WORKSPACE_TOO_SMALL = 2, /* more (tile, Gaussian) pairs than the workspace holds */
+    GS_ERR_STATE = 3,              /* call out of order (e.g. render before bin_sort) */
+    GS_ERR_HIP = 4,                /* a HIP runtime call failed; see gs_last_error() */
+    GS_ERR_UNSUPPORTED = 5         /* size beyond the implementation limits */
+} gs_status;
+
+/* Limits of this implementation. */
+#define GS_MAX_VIEWS 32
+#define GS_TILE 16
+
+/* Scene: n Gaussians, parameters already activated.
+ *   means      [n,3]    world-space centres
+ *   quats      [n,4]    rotation quaternions (w, x, y, z); normalised inside
+ *   scales     [n,3]    positive axis scales (already exp-activated)
+ *   opacities  [n]      opacity o = sigmoid(a) in [0, 1]
+ *   sh         [n,d,3]  SH coefficients, d = (sh_degree + 1)^2, channel fastest
+ * All float32, contiguous, 4-byte aligned device arrays.  Non-finite values are
+ * not an error: the affected (Gaussian, view) pairs are culled or masked. */
+typedef struct {
+    const float* means;
+    const float* quats;
+    const float* scales;
+    const float* opacities;
+    const float* sh;
+    int64_t n;
+    int32_t sh_degree; /* 0..3 */
+} gs_gaussians;
+
+/* Pinhole camera (host memory): x_cam = R x_world + t (R row-major), pixel
+ * u = fx x/z + cx, v = fy y/z + cy; the pixel (i, j) centre is (i + 0.5, j + 0.5). */
+typedef struct {
+    float R[9];
+    float t[3];
+    float fx, fy, cx, cy;
+} gs_camera;
+
+/* Problem sizes fixed for the lifetime of a context. */
+typedef struct {
+    int64_t n_gaussians;
+    int32_t sh_degree;  /* 0..3 */
+    int32_t n_views;    /* 1..GS_MAX_VIEWS, all views share width x height */
+    int32_t width;
+    int32_t height;
+    uint64_t max_pairs; /* capacity for (tile, Gaussian) pairs, >= 1 */
+} gs_dims;
+
+/* Numerical parameters (the pages name these constants but give no values).
+ *   eps        epsilon of the suffix denominator, the support q and the
+ *              cross-view weight (default 1e-6)
+ *   den_min    a contribution whose suffix denominator T(1-alpha) is below
+ *              this is masked out of the opacity and mean scores (default 1e-3)
+ *   lambda     ridge of the conditioning matrix A = lambda I + ... (default 1)
+ *   near_plane, far_plane   depth culling range (defaults 0.01, 1e10)
+ *   background colour added behind the last contributor (default 0). */
+typedef struct {
+    float eps;
+    float den_min;
+    float lambda;
+    float near_plane;
+    float far_plane;
+    float background[3];
+} gs_params;
+
+typedef struct gs_context gs_context;
+
+/* Fill *out with the defaults above.  Never fails for a non-null pointer. */
+GSR_API gs_status gs_default_params(gs_params* out);
+
+/* Bytes of device workspace a context with these sizes needs (host-only call). */
+GSR_API gs_status gs_workspace_size(const gs_dims* dims, size_t* bytes_out);
+
+/* Create a context over caller-owned device memory `workspace` (>= the size
+ * above, 256-byte aligned).  The context itself is host memory. */
+GSR_API gs_status gs_context_create(const gs_dims* dims, void* workspace, size_t workspace_bytes,
+                            gs_context** out);
+GSR_API gs_status gs_context_destroy(gs_context* ctx);
+
+/* Preprocess every (Gaussian, view): EWA projection of the 3D covariance to
+ * the image (+0.3 px^2 dilation), inverse 2D covariance, 3-sigma radius and
+ * tile rectangle, depth, SH colour along the view direction (+0.5, clamped at
+ * 0, clamp state kept for the SH score).  `cams` is a host array [n_views].
+ * Asynchronous on `stream`. */
+GSR_API gs_status gs_project(gs_context* ctx, const gs_gaussians* scene, const gs_camera* cams,
+                     const gs_params* params, hipStream_t stream);
+
+/* Tile binning and contributor sorting: order (Gaussian, view) records by
+ * depth, emit one (tile, Gaussian) pair per covered tile, stable-sort the pairs
+ * by tile and build per-tile ranges.  Blocks the host once to read the pair
+ * count (written to *n_pairs_out, which may be null).  Returns
+ * GS_ERR_WORKSPACE_TOO_SMALL (with the count) when it exceeds max_pairs; the
+ * caller then creates a larger context and starts again from gs_project. */
+GSR_API gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out);
+
+/* Front-to-back compositing per 16x16 tile.  Outputs (any may be null):
+ *   color      [n_views, height, width, 3] rendered colour incl. background
+ *   T_final    [n_views, height, width]    final transmittance
+ *   n_contrib  [n_views, height, width]    accepted contributions (int32)
+ * The rendered colour is also kept in the workspace for gs_score_replay. */
+GSR_API gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_contrib,
+                    hipStream_t stream);
+
+/* Analytic score replay against `observed` [n_views, height, width, 3]: the
+ * residual r = C_hat - C, the suffix C+ = (C_hat - P - T alpha c) /
+ * (T (1 - alpha) + eps), masked per-Gaussian partial scores, cross-view
+ * aggregation and the token
+ *   tokens [n, 9 + 3 d] = [ b_mu (3), s_alpha (1), s_SH (3 d, index k*3 + channel),
+ *                           log Q (1), eig(A) / (tr A + eps) (3, descending),
+ *                           log(tr A + eps) (1) ]
+ * with Q = eps + sum_v q_gv the cross-view support. */
+GSR_API gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens, hipStream_t stream);
+
+GSR_API const char* gs_status_string(gs_status s);
+GSR_API const char* gs_last_error(void);
+
+/* ---- diagnostics used by the test-suite ---------------------------------- */
+
+/* The float32 exponential used by every alpha decision: out[i] = 2^in[i],
+ * valid for in[i] in [-8, 0.5] (device arrays of n floats). */
+GSR_API gs_status gs_debug_exp2(const float* in, float* out, int64_t n, hipStream_t stream);
+
+/* Copy an internal workspace array into the caller's device buffer `dst`
+ * (`bytes` must be at least the array size; the call fails otherwise):
+ *   GS_EXPORT_RECORDS   after gs_project:  [3, n_views*n, 4] float32, planes
+ *       {mx, my, qa, qb}, {qc, opacity, pre_r, pre_g},
+ *       {pre_b, <pair offset bits>, <x0 | y0 << 16>, <x1 | y1 << 16>}, record
+ *       index v*n + g, qa..qc scaled so that the Gaussian weight at offset
+ *       (dx, dy) = pixel - centre is 2^(qa dx^2 + qb dx dy + qc dy^2); culled
+ *       records are all zero
+ *   GS_EXPORT_DEPTH_KEYS after gs_project: [n_views*n] uint32 depth bits
+ *       (0xffffffff when culled)
+ *   GS_EXPORT_SORTED_IDS after gs_bin_sort: [n_pairs] uint32 Gaussian index
+ *   GS_EXPORT_RANGES    after gs_bin_sort: [n_views*tiles] x 2 uint32 [start, end)
+ */
+typedef enum {
+    GS_EXPORT_RECORDS = 1,
+    GS_EXPORT_DEPTH_KEYS = 2,
+    GS_EXPORT_SORTED_IDS = 3,
+    GS_EXPORT_RANGES = 4
+} gs_export_kind;
+GSR_API gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSR_H */
