@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the render + analytic score replay path on one MI355X.
+
+One step = gs_project -> gs_bin_sort -> gs_render -> gs_score_replay (tokens
+written) over one synthetic scene whose parameters and observation already sit
+in HBM.  Prints ONE JSON line with the throughput (rendered+replayed Mpix/s),
+Gaussian-pixel contributions/s, per-stage times (HIP events on the stream the
+kernels run on), the roofline of the dominant kernel and the CPU oracle timed
+on a bounded sample on the host cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5]
+
+The default workload is the ReSplat-like step: 8 views 256x448, 917,504
+pixel-aligned Gaussians, SH degree 3.  Only one GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12     # fp32 VALU lane-ops/s (256 CU x 4 SIMD x 16 lanes x 2.4 GHz)
+
+# Algorithmic fp32 operations of the specified arithmetic (one VALU op per lane each):
+OPS_EVAL = 8        # dx, dy, the quadratic form (2 mul, 2 fma, 1 mul) and the distance cut
+OPS_NEAR = 15       # the exponential (rint, sub, 7 fma, cvt, ldexp), o*G, clamp (cmp, select), alpha cut
+OPS_CONTRIB_FWD = 20    # 1-alpha, T(1-alpha), cut, w, 3 products, 3 compensated adds (4 each), count
+OPS_CONTRIB_REPLAY = 58  # the same plus suffix, reciprocal, rho, mask, the 8 partials and their sums
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
+                   help="budget of rendering work for the CPU oracle sample (0 disables)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def stage_bytes(stage, c):
+    """Algorithmic HBM bytes per launch of an HBM-bound stage."""
+    G, V, d, P, VG = c["G"], c["V"], c["d"], c["P"], c["G"] * c["V"]
+    if stage == "project":
+        return G * (44 + 12 * d) + VG * (48 + 4 + 4)
+    if stage == "depth_sort":      # 4 passes: histogram read 4 B, scatter read 8 B (4 B first pass), write 8 B
+        return VG * (4 * (4 + 8 + 8) - 4)
+    if stage == "scan":            # reduce + down sweep gather tt through the sorted ids, write offsets
+        return VG * (8 + 8 + 4)
+    if stage == "emit":
+        return VG * (4 + 4 + 4 + 16) + c["n_live"] * 4 + P * 8
+    if stage == "tile_sort":       # histogram read 4 B + scatter read 8 B + write 8 B, final pass also gather + inv
+        passes = max(1, (max(1, (V * c["T"] - 1).bit_length()) + 7) // 8)
+        return P * (passes * (4 + 8 + 8) + 8)
+    if stage == "ranges":
+        return P * 4 + V * c["T"] * 8
+    if stage == "finalize":
+        return G * (16 + 4 * (9 + 3 * d)) + VG * 48 + P * (4 + 32)
+    return None
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the multi-GPU sharding is described in DESIGN.md but not implemented)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import scenes
+    from gaussian_splatting_rasterizer_amd import binding
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    t_gen = time.perf_counter()
+    sc = scenes.make_scene(args.config)
+    t_gen = time.perf_counter() - t_gen
+
+    with torch.cuda.stream(stream):
+        # observation: render of the scene with perturbed means + pixel noise (setup, untimed)
+        rp = binding.rasterizer_for_scene(sc.perturbed(), device=dev)
+        rp.project_and_bin()
+        obs_col, _, _ = rp.render()
+        obs = (obs_col + torch.from_numpy(sc.pixel_noise).to(dev)).contiguous()
+        rp.close()
+        del rp, obs_col
+
+        r = binding.rasterizer_for_scene(sc, device=dev)
+        r.project_and_bin()
+        r._alloc(int(r.n_pairs * 1.1) + 4096)      # right-size the workspace once
+        outputs = r.new_outputs()
+        tokens = torch.empty((sc.n, 9 + 3 * sc.d), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            r.step(obs, outputs, tokens)
+        stream.synchronize()
+
+        binding.gs_profile_enable(r.ctx, True)
+        binding.gs_profile_read(r.ctx)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            r.step(obs, outputs, tokens)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        prof = binding.gs_profile_read(r.ctx)
+        binding.gs_profile_enable(r.ctx, False)
+
+        color, T, n = outputs
+        stats = r.export(binding.GS_EXPORT_PIXEL_STATS).view(-1, 2).to(torch.int64)
+        K = int(n.to(torch.int64).sum().item())
+        E = int(stats[:, 0].sum().item())
+        E_near = int(stats[:, 1].sum().item())
+        P = int(r.n_pairs)
+        finite = bool(torch.isfinite(tokens).all().item())
+        rec = r.export(binding.GS_EXPORT_RECORDS)
+        n_live = int((rec[2, :, 3] != 0).sum().item())
+
+    V, H, W = sc.n_views, sc.height, sc.width
+    T_tiles = ((W + 15) // 16) * ((H + 15) // 16)
+    ms_step = 1e3 * elapsed / args.steps
+    mpix = V * H * W / (elapsed / args.steps) / 1e6
+    contribs = K / (elapsed / args.steps)
+
+    c = dict(G=sc.n, V=V, d=sc.d, P=P, T=T_tiles, n_live=n_live)
+    stages = {k: (ms / max(cnt, 1), cnt) for k, (ms, cnt) in prof.items()}
+    dominant = max(stages, key=lambda k: stages[k][0])
+    t_dom = stages[dominant][0] * 1e-3
+    if dominant in ("render", "replay"):
+        ops = OPS_EVAL * E + OPS_NEAR * E_near + (OPS_CONTRIB_FWD if dominant == "render" else OPS_CONTRIB_REPLAY) * K
+        achieved = ops / t_dom / 1e12
+        roofline = {"kernel": dominant, "bound": "alu", "achieved": round(achieved, 3), "peak": round(ALU_PEAK_TOPS, 2),
+                    "unit": "Top/s (fp32 VALU lane-ops)", "frac": round(achieved / ALU_PEAK_TOPS, 4),
+                    "traffic": None, "avg_launch_ms": round(stages[dominant][0], 4),
+                    "units": {"evaluations": E, "near_evaluations": E_near, "contributions": K}}
+    else:
+        by = stage_bytes(dominant, c)
+        achieved = by / t_dom / 1e9
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_ms": round(stages[dominant][0], 4), "bytes_per_launch": by}
+
+    out = {
+        "metric": "render+score-replay Mpix/s",
+        "value": round(mpix, 2),
+        "unit": "Mpix/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": scenes.CONFIG_NAMES[args.config], "views": V, "height": H, "width": W,
+                   "gaussians": sc.n, "sh_degree": sc.sh_degree, "pairs": P, "parallelism": "none"},
+        "contribs_per_s": round(contribs, 1),
+        "contributions_per_step": K,
+        "stages_ms": {k: round(v[0], 4) for k, v in stages.items()},
+        "roofline": roofline,
+        "tokens_finite": finite,
+    }
+
+    if not args.no_cpu_baseline and args.cpu_baseline_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(sc, args.cpu_baseline_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(sc, budget_s):
+    """The oracle as it stands, timed on the host cores on a bounded sample of the
+    same workload: full preprocess + tile lists, then render + replay of an
+    evenly spaced subset of tiles (with score sums for every Gaussian), then
+    tokens; the per-tile part is scaled to the whole frame."""
+    import numpy as np
+
+    import oracle
+
+    obs = (0.5 + sc.pixel_noise).astype(np.float32)   # the oracle is only timed here
+    t0 = time.perf_counter()
+    o = oracle.OracleScene(sc)
+    o.build_lists()
+    t_fixed = time.perf_counter() - t0
+    o.select(None)
+    n_tiles = o.V * o.T
+    probe = np.arange(0, n_tiles, max(1, n_tiles // 64), dtype=np.int64)
+    t1 = time.perf_counter()
+    o.render(tiles=probe, obs=obs)
+    t_probe = time.perf_counter() - t1
+    per_tile = t_probe / len(probe)
+    want = int(min(n_tiles, max(len(probe), budget_s / max(per_tile, 1e-9))))
+    stride = max(1, n_tiles // want)
+    sample = np.arange(stride // 2, n_tiles, stride, dtype=np.int64)
+    o.select(None)
+    t2 = time.perf_counter()
+    o.render(tiles=sample, obs=obs)
+    t_tiles = time.perf_counter() - t2
+    t3 = time.perf_counter()
+    o.tokens()
+    t_tok = time.perf_counter() - t3
+    full = t_fixed + t_tiles * (n_tiles / len(sample)) + t_tok
+    pixels = o.V * o.H * o.W
+    threads = oracle.num_threads()
+    o.close()
+    return {"value": round(pixels / full / 1e6, 4), "unit": "Mpix/s", "cores": threads, "kind": "oracle",
+            "sample": f"preprocess + lists of all {sc.n} Gaussians x {sc.n_views} views, render+replay of "
+                      f"{len(sample)}/{n_tiles} tiles (every {stride}th) scaled to the frame, tokens of all",
+            "seconds": {"preprocess_lists": round(t_fixed, 3), "tiles": round(t_tiles, 3),
+                        "tokens": round(t_tok, 3), "extrapolated_frame": round(full, 3)}}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

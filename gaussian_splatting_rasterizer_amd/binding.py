@@ -30,10 +30,12 @@ GS_EXPORT_RECORDS = 1
 GS_EXPORT_DEPTH_KEYS = 2
 GS_EXPORT_SORTED_IDS = 3
 GS_EXPORT_RANGES = 4
+GS_EXPORT_PIXEL_STATS = 5
+STAGES = ("project", "depth_sort", "scan", "emit", "tile_sort", "ranges", "render", "replay", "finalize")
 
 ABI_SYMBOLS = ("gs_default_params", "gs_workspace_size", "gs_context_create", "gs_context_destroy",
                "gs_project", "gs_bin_sort", "gs_render", "gs_score_replay", "gs_status_string",
-               "gs_last_error", "gs_debug_exp2", "gs_debug_export")
+               "gs_last_error", "gs_debug_exp2", "gs_debug_export", "gs_profile_enable", "gs_profile_read")
 
 
 class gs_gaussians(ctypes.Structure):
@@ -101,6 +103,10 @@ def load_library(path: str = LIB_PATH):
     lib.gs_debug_exp2.argtypes = [P, P, ctypes.c_int64, P]
     lib.gs_debug_export.restype = St
     lib.gs_debug_export.argtypes = [P, ctypes.c_int32, P, ctypes.c_size_t, P]
+    lib.gs_profile_enable.restype = St
+    lib.gs_profile_enable.argtypes = [P, ctypes.c_int32]
+    lib.gs_profile_read.restype = St
+    lib.gs_profile_read.argtypes = [P, P, P]
     _lib = lib
     return lib
 
@@ -184,6 +190,18 @@ def gs_debug_exp2(inp, out, stream=None) -> None:
 def gs_debug_export(ctx, kind, dst, stream=None) -> None:
     _check(load_library().gs_debug_export(ctx, int(kind), _dev_ptr(dst), dst.numel() * dst.element_size(),
                                           _stream_handle(stream)), "gs_debug_export")
+
+
+def gs_profile_enable(ctx, enable=True) -> None:
+    _check(load_library().gs_profile_enable(ctx, int(bool(enable))), "gs_profile_enable")
+
+
+def gs_profile_read(ctx) -> dict:
+    """{stage: (total ms, launches)} accumulated since the previous read."""
+    ms = (ctypes.c_double * len(STAGES))()
+    calls = (ctypes.c_int64 * len(STAGES))()
+    _check(load_library().gs_profile_read(ctx, ms, calls), "gs_profile_read")
+    return {name: (float(ms[i]), int(calls[i])) for i, name in enumerate(STAGES)}
 
 
 # ---- convenience wrapper ----------------------------------------------------------------------------
@@ -300,6 +318,8 @@ class Rasterizer:
         elif kind == GS_EXPORT_RANGES:
             T = ((self.W + 15) // 16) * ((self.H + 15) // 16)
             dst = torch.empty((self.V * T, 2), dtype=torch.int32, device=self.device)
+        elif kind == GS_EXPORT_PIXEL_STATS:
+            dst = torch.empty((self.V, self.H, self.W, 2), dtype=torch.int32, device=self.device)
         else:
             raise ValueError(kind)
         gs_debug_export(self.ctx, kind, dst)

@@ -9,6 +9,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <new>
+#include <vector>
+
 #include "gsr_internal.hpp"
 
 using namespace gsr;
@@ -43,6 +46,65 @@ constexpr int64_t kBlockItems = 4096;  // items per scan / radix block
 
 }  // namespace
 
+// Per-stage HIP-event timers (host objects; no device memory).
+struct StageTimer {
+    struct Rec {
+        int stage;
+        hipEvent_t a, b;
+    };
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    std::vector<Rec> pending;
+    double ms[GS_NUM_STAGES] = {};
+    int64_t calls[GS_NUM_STAGES] = {};
+    hipEvent_t open_ev = nullptr;
+
+    hipEvent_t take() {
+        if (pool.empty()) {
+            hipEvent_t e = nullptr;
+            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            return e;
+        }
+        hipEvent_t e = pool.back();
+        pool.pop_back();
+        return e;
+    }
+    void begin(hipStream_t st) {
+        if (!on) return;
+        open_ev = take();
+        if (open_ev) (void)hipEventRecord(open_ev, st);
+    }
+    void end(int stage, hipStream_t st) {
+        if (!on || !open_ev) return;
+        hipEvent_t e = take();
+        if (!e) return;
+        (void)hipEventRecord(e, st);
+        pending.push_back({stage, open_ev, e});
+        open_ev = nullptr;
+        if (pending.size() > 4096) fold();
+    }
+    void fold() {
+        for (const Rec& r : pending) {
+            float t = 0.0f;
+            (void)hipEventSynchronize(r.b);
+            if (hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+                ms[r.stage] += t;
+                calls[r.stage] += 1;
+            }
+            pool.push_back(r.a);
+            pool.push_back(r.b);
+        }
+        pending.clear();
+    }
+    void destroy() {
+        fold();
+        for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+        pool.clear();
+        if (open_ev) (void)hipEventDestroy(open_ev);
+        open_ev = nullptr;
+    }
+};
+
 struct gs_context {
     Sizes s;
     Workspace ws;
@@ -51,7 +113,7 @@ struct gs_context {
     CamPack cams;
     gs_params params;
     uint64_t n_pairs;
-    const uint32_t* sorted_keys;
+    StageTimer timer;
 };
 
 namespace gsr {
@@ -109,6 +171,7 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->tile_done = (uint32_t*)take(4 * tiles);
     ws->partials = (float4*)take(32 * P);
     ws->pixel = (float4*)take(16 * pixels);
+    ws->pixel_stats = (uint2*)take(8 * pixels);
     return (off + 255) & ~(size_t)255;
 }
 
@@ -169,7 +232,7 @@ gs_status gs_context_create(const gs_dims* dims, void* workspace, size_t workspa
     const size_t need = carve_workspace(s, nullptr, &ws);
     if (workspace_bytes < need)
         return fail(GS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-    gs_context* c = (gs_context*)calloc(1, sizeof(gs_context));
+    gs_context* c = new (std::nothrow) gs_context();
     if (!c) return fail(GS_ERR_INVALID_ARGUMENT, "out of host memory");
     c->s = s;
     carve_workspace(s, (char*)workspace, &c->ws);
@@ -179,7 +242,8 @@ gs_status gs_context_create(const gs_dims* dims, void* workspace, size_t workspa
 }
 
 gs_status gs_context_destroy(gs_context* ctx) {
-    free(ctx);
+    if (ctx) ctx->timer.destroy();
+    delete ctx;
     return GS_OK;
 }
 
@@ -215,8 +279,10 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
     ctx->scene = *sc;
     ctx->params = *params;
     ctx->state = kCreated;
+    ctx->timer.begin(stream);
     hipError_t e = launch_project(*sc, ctx->cams, s, params->near_plane, params->far_plane, ctx->ws, stream);
     if (e != hipSuccess) return hip_fail(e, "project");
+    ctx->timer.end(GS_STAGE_PROJECT, stream);
     ctx->state = kProjected;
     return GS_OK;
 }
@@ -229,12 +295,17 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     hipError_t e;
     // 1. depth sort of the records (keys ping-pong through offsets, which the scan rewrites next)
     uint32_t* rid_sorted = nullptr;
+    StageTimer& tm = ctx->timer;
+    tm.begin(stream);
     e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b, nullptr,
                           nullptr, nullptr, ws.hist, ws.scan_blocks, ws.scan_total, stream, nullptr, &rid_sorted);
     if (e != hipSuccess) return hip_fail(e, "depth sort");
+    tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
+    tm.begin(stream);
     e = launch_scan_u32(ws.tiles_touched, rid_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream);
     if (e != hipSuccess) return hip_fail(e, "scan");
+    tm.end(GS_STAGE_SCAN, stream);
     uint64_t total = 0;
     e = hipMemcpyAsync(&total, ws.scan_total, sizeof total, hipMemcpyDeviceToHost, stream);
     if (e != hipSuccess) return hip_fail(e, "pair count copy");
@@ -248,16 +319,22 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
                     (unsigned long long)s.max_pairs);
     }
     // 3. emit pairs in depth order, 4. stable sort by tile, 5. ranges
+    tm.begin(stream);
     e = launch_emit(s, ws, rid_sorted, stream);
     if (e != hipSuccess) return hip_fail(e, "emit");
+    tm.end(GS_STAGE_EMIT, stream);
     const int64_t tiles = (int64_t)s.V * s.T;
     uint32_t* sorted_keys = nullptr;
+    tm.begin(stream);
     e = launch_radix_sort(ws.pkey_a, nullptr, (int64_t)total, bits_for((uint64_t)tiles), ws.pkey_b, ws.pkey_a,
                           ws.pval_a, ws.pval_b, ws.pair_g, ws.sorted_g, ws.inv, ws.hist, ws.scan_blocks,
                           ws.scan_total, stream, &sorted_keys, nullptr);
     if (e != hipSuccess) return hip_fail(e, "tile sort");
+    tm.end(GS_STAGE_TILE_SORT, stream);
+    tm.begin(stream);
     e = launch_ranges(sorted_keys, (int64_t)total, ws.ranges, tiles, stream);
     if (e != hipSuccess) return hip_fail(e, "ranges");
+    tm.end(GS_STAGE_RANGES, stream);
     ctx->state = kBinned;
     return GS_OK;
 }
@@ -267,8 +344,10 @@ gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_co
     if (ctx->state < kBinned) return fail(GS_ERR_STATE, "gs_render before gs_bin_sort");
     if ((color && !aligned(color, 4)) || (T_final && !aligned(T_final, 4)) || (n_contrib && !aligned(n_contrib, 4)))
         return fail(GS_ERR_INVALID_ARGUMENT, "misaligned output pointer");
+    ctx->timer.begin(stream);
     hipError_t e = launch_render(ctx->s, ctx->ws, ctx->params.background, color, T_final, n_contrib, stream);
     if (e != hipSuccess) return hip_fail(e, "render");
+    ctx->timer.end(GS_STAGE_RENDER, stream);
     ctx->state = kRendered;
     return GS_OK;
 }
@@ -278,10 +357,14 @@ gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens,
     if (ctx->state < kRendered) return fail(GS_ERR_STATE, "gs_score_replay before gs_render");
     if (!observed || !tokens) return fail(GS_ERR_INVALID_ARGUMENT, "null observed or tokens");
     if (!aligned(observed, 4) || !aligned(tokens, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    ctx->timer.begin(stream);
     hipError_t e = launch_replay(ctx->s, ctx->ws, observed, ctx->params.eps, ctx->params.den_min, stream);
     if (e != hipSuccess) return hip_fail(e, "replay");
+    ctx->timer.end(GS_STAGE_REPLAY, stream);
+    ctx->timer.begin(stream);
     e = launch_finalize(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.eps, ctx->params.lambda, tokens, stream);
     if (e != hipSuccess) return hip_fail(e, "finalize");
+    ctx->timer.end(GS_STAGE_FINALIZE, stream);
     return GS_OK;
 }
 
@@ -340,10 +423,35 @@ gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes
             e = hipMemcpyAsync(dst, ws.ranges, 8 * tiles, hipMemcpyDeviceToDevice, stream);
             break;
         }
+        case GS_EXPORT_PIXEL_STATS: {
+            const size_t pixels = (size_t)s.V * s.W * s.H;
+            if (ctx->state < kRendered) return fail(GS_ERR_STATE, "pixel stats exist after gs_render");
+            if (bytes < 8 * pixels) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
+            e = hipMemcpyAsync(dst, ws.pixel_stats, 8 * pixels, hipMemcpyDeviceToDevice, stream);
+            break;
+        }
         default:
             return fail(GS_ERR_INVALID_ARGUMENT, "unknown export kind %d", kind);
     }
     if (e != hipSuccess) return hip_fail(e, "export copy");
+    return GS_OK;
+}
+
+gs_status gs_profile_enable(gs_context* ctx, int32_t enable) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    ctx->timer.on = enable != 0;
+    return GS_OK;
+}
+
+gs_status gs_profile_read(gs_context* ctx, double* ms, int64_t* calls) {
+    if (!ctx || !ms || !calls) return fail(GS_ERR_INVALID_ARGUMENT, "null argument");
+    ctx->timer.fold();
+    for (int i = 0; i < GS_NUM_STAGES; ++i) {
+        ms[i] = ctx->timer.ms[i];
+        calls[i] = ctx->timer.calls[i];
+        ctx->timer.ms[i] = 0.0;
+        ctx->timer.calls[i] = 0;
+    }
     return GS_OK;
 }
 

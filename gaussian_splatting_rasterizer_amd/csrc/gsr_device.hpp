@@ -124,17 +124,18 @@ struct CamPack {
 __device__ __forceinline__ float clamp_colour(float pre) { return pre >= 0.0f ? pre : 0.0f; }
 
 // Evaluate one list entry at one pixel with the canonical float32 order.
-// Returns false when the entry is skipped (too far or alpha below 1/255).
-__device__ __forceinline__ bool eval_alpha(float4 r0, float qc, float opac, float px, float py,
-                                           float& dx, float& dy, float& alpha, bool& clamped) {
+// Returns 0 when the pixel is beyond the distance cut, 1 when alpha < 1/255,
+// 2 when the entry contributes (alpha, clamped and the offset (dx, dy) set).
+__device__ __forceinline__ int eval_alpha(float4 r0, float qc, float opac, float px, float py, float& dx,
+                                          float& dy, float& alpha, bool& clamped) {
     dx = px - r0.x;
     dy = py - r0.y;
     const float e = __builtin_fmaf(dx, __builtin_fmaf(r0.z, dx, r0.w * dy), (qc * dy) * dy);
-    if (!(e >= kECutoff)) return false;
+    if (!(e >= kECutoff)) return 0;
     const float aG = opac * exp2_spec(e);
     clamped = !(aG < kAlphaMax);
     alpha = clamped ? kAlphaMax : aG;
-    return alpha >= kAlphaMin;
+    return alpha >= kAlphaMin ? 2 : 1;
 }
 
 // Compensated (Kahan) accumulation of the prefix colour; the true sum is hi - comp.

@@ -39,6 +39,7 @@ struct Workspace {
     uint32_t* tile_done;   // per tile: end of the prefix the replay processed
     float4* partials;      // per sorted pair: {W, U_a, U_mx, U_my}, {U_r, U_g, U_b, n_pix}
     float4* pixel;         // per pixel: rendered colour (rgb), final transmittance
+    uint2* pixel_stats;    // per pixel: entries evaluated, entries past the distance cut
 };
 
 struct Sizes {

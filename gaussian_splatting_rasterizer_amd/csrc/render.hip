@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                                                 const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
                                                 float bg0, float bg1, float bg2, float* __restrict__ color,
                                                 float* __restrict__ T_out, int32_t* __restrict__ n_out,
-                                                float4* __restrict__ pixel) {
+                                                float4* __restrict__ pixel, uint2* __restrict__ pixel_stats) {
     __shared__ float4 s0[kRenderBatch];
     __shared__ float4 s1[kRenderBatch];  // {qc, opacity, colour r, colour g}
     __shared__ float s2[kRenderBatch];   // colour b
@@ -43,6 +43,8 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     float Tr = 1.0f;
     float h0 = 0.f, h1 = 0.f, h2 = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
     int n = 0;
+    uint32_t n_near = 0;          // entries past the distance cut
+    uint32_t stop = 0xffffffffu;  // list index at which the pixel saturated
     bool done = !inside;
 
     for (uint32_t base = rg.x; base < rg.y; base += kRenderBatch) {
@@ -65,10 +67,13 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                 const float4 b = s1[j];
                 float dx, dy, alpha;
                 bool clamped;
-                if (!eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped)) continue;
+                const int code = eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped);
+                n_near += code != 0;
+                if (code != 2) continue;
                 const float tT = Tr * (1.0f - alpha);
                 if (tT < kTMin) {
                     done = true;
+                    stop = base + (uint32_t)j;
                     break;
                 }
                 const float w = alpha * Tr;
@@ -94,6 +99,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     if (T_out) T_out[pix] = Tr;
     if (n_out) n_out[pix] = n;
     pixel[pix] = make_float4(o0, o1, o2, Tr);
+    pixel_stats[pix] = make_uint2(stop != 0xffffffffu ? stop - rg.x + 1u : rg.y - rg.x, n_near);
 }
 
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const float bg[3], float* color, float* T_final,
@@ -101,7 +107,8 @@ hipError_t launch_render(const Sizes& s, const Workspace& ws, const float bg[3],
     const int64_t tiles = (int64_t)s.V * s.T;
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, ws.sorted_g, ws.rec0, ws.rec1,
-                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel);
+                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel,
+                       ws.pixel_stats);
     return hipGetLastError();
 }
 

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                     const float4 b = s1[j];
                     float dx, dy, alpha;
                     bool clamped;
-                    if (eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped)) {
+                    if (eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped) == 2) {
                         const float tT = Tr * (1.0f - alpha);
                         if (tT < kTMin) {
                             done = true;

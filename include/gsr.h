@@ -183,14 +183,38 @@ GSR_API gs_status gs_debug_exp2(const float* in, float* out, int64_t n, hipStrea
  *       (0xffffffff when culled)
  *   GS_EXPORT_SORTED_IDS after gs_bin_sort: [n_pairs] uint32 Gaussian index
  *   GS_EXPORT_RANGES    after gs_bin_sort: [n_views*tiles] x 2 uint32 [start, end)
+ *   GS_EXPORT_PIXEL_STATS after gs_render: [n_views*height*width] x 2 uint32:
+ *       list entries evaluated before the pixel stopped, and how many of those
+ *       passed the distance cut (exponent >= -8) -- the work counts of the pass
  */
 typedef enum {
     GS_EXPORT_RECORDS = 1,
     GS_EXPORT_DEPTH_KEYS = 2,
     GS_EXPORT_SORTED_IDS = 3,
-    GS_EXPORT_RANGES = 4
+    GS_EXPORT_RANGES = 4,
+    GS_EXPORT_PIXEL_STATS = 5
 } gs_export_kind;
 GSR_API gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes, hipStream_t stream);
+
+/* Per-stage timing with HIP events recorded on the caller's stream around each
+ * stage's launches (events are created by the library on first use and kept
+ * until gs_context_destroy).  gs_profile_read waits for the recorded events,
+ * writes the milliseconds and launch counts accumulated since the previous read
+ * (arrays of GS_NUM_STAGES), and resets them. */
+typedef enum {
+    GS_STAGE_PROJECT = 0,
+    GS_STAGE_DEPTH_SORT = 1,
+    GS_STAGE_SCAN = 2,
+    GS_STAGE_EMIT = 3,
+    GS_STAGE_TILE_SORT = 4,
+    GS_STAGE_RANGES = 5,
+    GS_STAGE_RENDER = 6,
+    GS_STAGE_REPLAY = 7,
+    GS_STAGE_FINALIZE = 8,
+    GS_NUM_STAGES = 9
+} gs_stage;
+GSR_API gs_status gs_profile_enable(gs_context* ctx, int32_t enable);
+GSR_API gs_status gs_profile_read(gs_context* ctx, double* ms, int64_t* calls);
 
 #ifdef __cplusplus
 }
