@@ -172,7 +172,7 @@ def main():
         "config": {"workload": scenes.CONFIG_NAMES[args.config], "views": V, "height": H, "width": W,
                    "gaussians": sc.n, "sh_degree": sc.sh_degree, "pairs": P, "parallelism": "none"},
         "contribs_per_s": round(contribs, 1),
-        "contributions_per_step": K,
+        "work_per_step": {"contributions": K, "evaluations": E, "near_evaluations": E_near, "pairs": P},
         "stages_ms": {k: round(v[0], 4) for k, v in stages.items()},
         "roofline": roofline,
         "tokens_finite": finite,

@@ -42,7 +42,7 @@ int bits_for(uint64_t n) {  // bits needed to represent values 0..n-1
     return b;
 }
 
-constexpr int64_t kBlockItems = 4096;  // items per scan / radix block
+constexpr int64_t kBlockItems = 4096;  // items per scan block (radix blocks are larger)
 
 }  // namespace
 
@@ -113,6 +113,7 @@ struct gs_context {
     CamPack cams;
     gs_params params;
     uint64_t n_pairs;
+    const uint32_t* sorted_g;     // Gaussian of each pair in (tile, depth, id) order (set by gs_bin_sort)
     StageTimer timer;
 };
 
@@ -132,7 +133,7 @@ Sizes make_sizes(const gs_dims& d) {
     s.max_pairs = d.max_pairs;
     const int64_t nmax = s.VG > (int64_t)s.max_pairs ? s.VG : (int64_t)s.max_pairs;
     const int64_t radix_blocks = (nmax + kBlockItems - 1) / kBlockItems;
-    s.hist_cap = 256 * radix_blocks;
+    s.hist_cap = 256 * radix_blocks;  // up to 8-bit digits
     int64_t scan_n = s.hist_cap > s.VG ? s.hist_cap : s.VG;
     s.scan_blocks_cap = (scan_n + kBlockItems - 1) / kBlockItems + 1;
     return s;
@@ -153,23 +154,26 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->rec2 = (float4*)take(16 * VG);
     ws->depth_key = (uint32_t*)take(4 * VG);
     ws->tiles_touched = (uint32_t*)take(4 * VG);
+    ws->slot_base = (uint32_t*)take(4 * VG);
     ws->dkey_b = (uint32_t*)take(4 * VG);
     ws->drid_a = (uint32_t*)take(4 * VG);
     ws->drid_b = (uint32_t*)take(4 * VG);
+    ws->rect_sorted = (uint2*)take(8 * VG);
+    ws->tt_sorted = (uint32_t*)take(4 * VG);
     ws->offsets = (uint32_t*)take(4 * VG);
     ws->scan_blocks = (uint64_t*)take(8 * (size_t)s.scan_blocks_cap);
     ws->scan_total = (uint64_t*)take(8 * 4);
     ws->hist = (uint32_t*)take(4 * (size_t)s.hist_cap);
-    ws->pkey_a = (uint32_t*)take(4 * P);
+    ws->pkey_emit = (uint32_t*)take(4 * P);
     ws->pkey_b = (uint32_t*)take(4 * P);
+    ws->pkey_c = (uint32_t*)take(4 * P);
     ws->pval_a = (uint32_t*)take(4 * P);
     ws->pval_b = (uint32_t*)take(4 * P);
     ws->pair_g = (uint32_t*)take(4 * P);
-    ws->sorted_g = (uint32_t*)take(4 * P);
-    ws->inv = (uint32_t*)take(4 * P);
     ws->ranges = (uint2*)take(8 * tiles);
-    ws->tile_done = (uint32_t*)take(4 * tiles);
+    ws->tile_stop = (uint64_t*)take(8 * tiles);
     ws->partials = (float4*)take(32 * P);
+    ws->gv_sums = (float4*)take(32 * VG);
     ws->pixel = (float4*)take(16 * pixels);
     ws->pixel_stats = (uint2*)take(8 * pixels);
     return (off + 255) & ~(size_t)255;
@@ -293,17 +297,22 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     const Sizes& s = ctx->s;
     Workspace& ws = ctx->ws;
     hipError_t e;
-    // 1. depth sort of the records (keys ping-pong through offsets, which the scan rewrites next)
-    uint32_t* rid_sorted = nullptr;
     StageTimer& tm = ctx->timer;
+    // 0. slot bases of the replay's partials: tile counts scanned in record order
     tm.begin(stream);
-    e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b, nullptr,
-                          nullptr, nullptr, ws.hist, ws.scan_blocks, ws.scan_total, stream, nullptr, &rid_sorted);
+    e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream);
+    if (e != hipSuccess) return hip_fail(e, "slot scan");
+    // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
+    //    scan rewrites next); the last pass also gathers the rectangles and tile counts
+    uint32_t* rid_sorted = nullptr;
+    e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b,
+                          reinterpret_cast<const uint2*>(ws.rec2), ws.rect_sorted, ws.tt_sorted, ws.hist,
+                          ws.scan_blocks, ws.scan_total + 2, stream, nullptr, &rid_sorted);
     if (e != hipSuccess) return hip_fail(e, "depth sort");
     tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
     tm.begin(stream);
-    e = launch_scan_u32(ws.tiles_touched, rid_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream);
+    e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream);
     if (e != hipSuccess) return hip_fail(e, "scan");
     tm.end(GS_STAGE_SCAN, stream);
     uint64_t total = 0;
@@ -325,16 +334,18 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     tm.end(GS_STAGE_EMIT, stream);
     const int64_t tiles = (int64_t)s.V * s.T;
     uint32_t* sorted_keys = nullptr;
+    uint32_t* sorted_g = nullptr;
     tm.begin(stream);
-    e = launch_radix_sort(ws.pkey_a, nullptr, (int64_t)total, bits_for((uint64_t)tiles), ws.pkey_b, ws.pkey_a,
-                          ws.pval_a, ws.pval_b, ws.pair_g, ws.sorted_g, ws.inv, ws.hist, ws.scan_blocks,
-                          ws.scan_total, stream, &sorted_keys, nullptr);
+    e = launch_radix_sort(ws.pkey_emit, ws.pair_g, (int64_t)total, bits_for((uint64_t)tiles), ws.pkey_b, ws.pkey_c,
+                          ws.pval_a, ws.pval_b, nullptr, nullptr, nullptr, ws.hist, ws.scan_blocks, ws.scan_total + 2,
+                          stream, &sorted_keys, &sorted_g);
     if (e != hipSuccess) return hip_fail(e, "tile sort");
     tm.end(GS_STAGE_TILE_SORT, stream);
     tm.begin(stream);
     e = launch_ranges(sorted_keys, (int64_t)total, ws.ranges, tiles, stream);
     if (e != hipSuccess) return hip_fail(e, "ranges");
     tm.end(GS_STAGE_RANGES, stream);
+    ctx->sorted_g = sorted_g;
     ctx->state = kBinned;
     return GS_OK;
 }
@@ -345,7 +356,8 @@ gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_co
     if ((color && !aligned(color, 4)) || (T_final && !aligned(T_final, 4)) || (n_contrib && !aligned(n_contrib, 4)))
         return fail(GS_ERR_INVALID_ARGUMENT, "misaligned output pointer");
     ctx->timer.begin(stream);
-    hipError_t e = launch_render(ctx->s, ctx->ws, ctx->params.background, color, T_final, n_contrib, stream);
+    hipError_t e = launch_render(ctx->s, ctx->ws, ctx->sorted_g, ctx->params.background, color, T_final, n_contrib,
+                                 stream);
     if (e != hipSuccess) return hip_fail(e, "render");
     ctx->timer.end(GS_STAGE_RENDER, stream);
     ctx->state = kRendered;
@@ -358,12 +370,15 @@ gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens,
     if (!observed || !tokens) return fail(GS_ERR_INVALID_ARGUMENT, "null observed or tokens");
     if (!aligned(observed, 4) || !aligned(tokens, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
     ctx->timer.begin(stream);
-    hipError_t e = launch_replay(ctx->s, ctx->ws, observed, ctx->params.eps, ctx->params.den_min, stream);
+    hipError_t e = launch_replay(ctx->s, ctx->ws, ctx->sorted_g, observed, ctx->params.eps, ctx->params.den_min,
+                                 stream);
     if (e != hipSuccess) return hip_fail(e, "replay");
     ctx->timer.end(GS_STAGE_REPLAY, stream);
     ctx->timer.begin(stream);
-    e = launch_finalize(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.eps, ctx->params.lambda, tokens, stream);
-    if (e != hipSuccess) return hip_fail(e, "finalize");
+    e = launch_gather_slots(ctx->s, ctx->ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "gather");
+    e = launch_tokens(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.eps, ctx->params.lambda, tokens, stream);
+    if (e != hipSuccess) return hip_fail(e, "tokens");
     ctx->timer.end(GS_STAGE_FINALIZE, stream);
     return GS_OK;
 }
@@ -414,7 +429,8 @@ gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes
         case GS_EXPORT_SORTED_IDS:
             if (ctx->state < kBinned) return fail(GS_ERR_STATE, "lists exist after gs_bin_sort");
             if (bytes < 4 * (size_t)ctx->n_pairs) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
-            if (ctx->n_pairs) e = hipMemcpyAsync(dst, ws.sorted_g, 4 * (size_t)ctx->n_pairs, hipMemcpyDeviceToDevice, stream);
+            if (ctx->n_pairs)
+                e = hipMemcpyAsync(dst, ctx->sorted_g, 4 * (size_t)ctx->n_pairs, hipMemcpyDeviceToDevice, stream);
             break;
         case GS_EXPORT_RANGES: {
             const size_t tiles = (size_t)s.V * s.T;

@@ -2,35 +2,45 @@
 //
 // Order of work (Stage 1, step "tile binning and contributor sorting" of the
 // Renderer Score Tokens proposal; the order within a tile is front to back):
+//   0. exclusive scan of the per-record tile counts in record order (v * G + g):
+//      the base of each record's partial-score slots for the replay;
 //   1. stable LSD radix sort of the (view, Gaussian) records by float32 depth
-//      bits (culled records carry 0xffffffff and sink to the end);
-//   2. exclusive scan of the per-record tile counts in that depth order;
+//      bits (culled records carry 0xffffffff and sink to the end); the last
+//      pass also gathers each record's tile rectangle and count into depth order;
+//   2. exclusive scan of the tile counts in depth order -> pair offsets;
 //   3. emission of one (tile, Gaussian) pair per covered tile, in depth order,
 //      row-major over each record's tile rectangle;
 //   4. stable LSD radix sort of the pairs by global tile id (view * tiles +
-//      tile): because emission was in (depth bits, Gaussian) order and the
-//      sort is stable, each tile's list ends up ordered by (depth bits,
-//      Gaussian index) -- a total order, so the lists are unique;
+//      tile) carrying the Gaussian index: because emission was in (depth bits,
+//      Gaussian) order and the sort is stable, each tile's list ends up ordered
+//      by (depth bits, Gaussian index) -- a total order, so the lists are unique;
 //   5. per-tile [start, end) ranges.
-// Only the pairs (2 x 4 bytes per pass) go through the tile sort; the depth
-// sort runs once over the records instead of over every pair.
+// Only the pairs (a 4-byte tile key and a 4-byte Gaussian index per pass) go
+// through the tile sort; the depth sort runs once over the records instead of
+// over every pair.
 //
-// Radix passes: per 4096-key block a digit histogram (per-wave LDS counters),
-// one device-wide exclusive scan of the digit-major histogram table, then a
-// scatter that ranks keys stably inside the block: each wave takes 64 keys at a
-// time in index order, finds the lanes holding the same digit with one ballot
-// per digit bit, and counts in per-wave LDS counters; waves own consecutive
-// 1024-key slices so wave order is index order.
+// Radix passes (8-bit digits; 4 passes for depths, 2 x 6 bits for 4096 tiles):
+// per 8192-key block a digit histogram (per-wave counts aggregated by ballot
+// matching, so skewed digits cost nothing), one device-wide exclusive scan of
+// the digit-major histogram table, then a scatter that ranks keys stably inside
+// the block -- each wave takes 64 keys at a time in index order, finds the lanes
+// holding the same digit with one ballot per digit bit and counts in per-wave
+// LDS counters; waves own consecutive 1024-key slices so wave order is index
+// order -- and reorders the block's keys in LDS so that each digit's run leaves
+// as one contiguous, coalesced span (32 keys per run on average at 8 bits).
 #include "gsr_internal.hpp"
 
 namespace gsr {
 
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
-constexpr int kScanTile = kScanThreads * kScanItems;  // 4096
-constexpr int kRadixThreads = 256;
+constexpr int kScanTile = kScanThreads * kScanItems;     // 4096
+constexpr int kRadixThreads = 512;
+constexpr int kRadixWaves = kRadixThreads / 64;
 constexpr int kRadixItems = 16;
-constexpr int kRadixTile = kRadixThreads * kRadixItems;  // 4096
+constexpr int kRadixTile = kRadixThreads * kRadixItems;  // 8192
+constexpr int kMaxDigitBits = 8;
+constexpr int kMaxBins = 1 << kMaxDigitBits;
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -58,7 +68,7 @@ __device__ __forceinline__ T wave_inclusive_scan(T x, int lane) {
     return x;
 }
 
-// exclusive scan across the block (blockDim.x = 256 or 1024), returns the block total via *total
+// exclusive scan across the block (NT threads), returns the block total via *total
 template <typename T, int NT>
 __device__ __forceinline__ T block_exclusive_scan(T x, T* total, T* lds /* NT/64 entries */) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -77,13 +87,7 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T* total, T* lds /* NT/64
     return base + inc - x;
 }
 
-__device__ __forceinline__ uint32_t scan_load(const uint32_t* __restrict__ in, const uint32_t* __restrict__ idx,
-                                              int64_t k) {
-    return idx ? in[idx[k]] : in[k];
-}
-
-__global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __restrict__ in,
-                                                              const uint32_t* __restrict__ idx, int64_t n,
+__global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __restrict__ in, int64_t n,
                                                               uint64_t* __restrict__ bsum) {
     __shared__ uint64_t lds[kScanThreads / 64];
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
@@ -91,7 +95,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const int64_t k = base + i * kScanThreads + threadIdx.x;
-        if (k < n) s += scan_load(in, idx, k);
+        if (k < n) s += in[k];
     }
     uint64_t tot;
     block_exclusive_scan<uint64_t, kScanThreads>(s, &tot, lds);
@@ -114,9 +118,8 @@ __global__ __launch_bounds__(1024) void k_scan_top(uint64_t* __restrict__ bsum, 
 }
 
 // `in` and `out` may alias (each block reads its whole slice before writing it)
-__global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, const uint32_t* __restrict__ idx,
-                                                            int64_t n, const uint64_t* __restrict__ boff,
-                                                            uint32_t* out) {
+__global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, int64_t n,
+                                                            const uint64_t* __restrict__ boff, uint32_t* out) {
     // padded so that thread t's 16 consecutive items (t*17 + i) are bank-conflict free
     __shared__ uint32_t s[kScanTile + kScanTile / 16];
     __shared__ uint32_t lds[kScanThreads / 64];
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
     for (int i = 0; i < kScanItems; ++i) {
         const int e = i * kScanThreads + threadIdx.x;
         const int64_t k = base + e;
-        s[e + e / 16] = k < n ? scan_load(in, idx, k) : 0u;
+        s[e + e / 16] = k < n ? in[k] : 0u;
     }
     __syncthreads();
     const int t = threadIdx.x;
@@ -149,50 +152,82 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
     }
 }
 
-hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, int64_t n, uint32_t* out,
-                           uint64_t* block_scratch, uint64_t* total, hipStream_t st) {
+hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
+                           hipStream_t st) {
     const int64_t nb = (n + kScanTile - 1) / kScanTile;
-    if (nb > 0) hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, idx, n, block_scratch);
+    if (nb > 0) hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch);
     hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(1024), 0, st, block_scratch, nb, total);
-    if (nb > 0) hipLaunchKernelGGL(k_scan_down, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, idx, n, block_scratch, out);
+    if (nb > 0) hipLaunchKernelGGL(k_scan_down, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch, out);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // radix sort
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n, int shift,
-                                                              int bits, uint32_t* __restrict__ hist, int64_t nb) {
-    __shared__ uint32_t h[4][256];
-    const int nbins = 1 << bits;
-    const uint32_t mask = (uint32_t)nbins - 1u;
-    const int wave = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < 4 * 256; i += kRadixThreads) (&h[0][0])[i] = 0u;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kRadixTile;
-#pragma unroll 4
-    for (int i = 0; i < kRadixItems; ++i) {
-        const int64_t k = base + i * kRadixThreads + threadIdx.x;
-        if (k < n) atomicAdd(&h[wave][(keys[k] >> shift) & mask], 1u);
+// Lanes of the wave holding the same digit (one ballot per digit bit); invalid lanes never match.
+__device__ __forceinline__ uint64_t match_peers(uint32_t dgt, int bits, bool valid) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+        const bool bit = (dgt >> b) & 1u;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
     }
-    __syncthreads();
-    for (int dgt = threadIdx.x; dgt < nbins; dgt += kRadixThreads)
-        hist[(int64_t)dgt * nb + blockIdx.x] = h[0][dgt] + h[1][dgt] + h[2][dgt] + h[3][dgt];
+    return peers;
 }
 
-__global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
-    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift, int bits,
-    const uint32_t* __restrict__ hist_scan, int64_t nb, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, const uint32_t* __restrict__ gather, uint32_t* __restrict__ inv) {
-    __shared__ uint32_t cnt[4][256];
-    __shared__ uint32_t gbase[4][256];
+// Per-block digit counts, written digit-major: hist[digit * nb + block].
+__global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n, int shift,
+                                                              int bits, uint32_t* __restrict__ hist, int64_t nb) {
+    __shared__ uint32_t h[kRadixWaves][kMaxBins];
     const int nbins = 1 << bits;
     const uint32_t mask = (uint32_t)nbins - 1u;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < 4 * 256; i += kRadixThreads) (&cnt[0][0])[i] = 0u;
+    for (int i = threadIdx.x; i < kRadixWaves * kMaxBins; i += kRadixThreads) (&h[0][0])[i] = 0u;
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t base = (int64_t)blockIdx.x * kRadixTile + (int64_t)wave * (kRadixTile / kRadixWaves);
+    uint32_t dg[kRadixItems];
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const int64_t k = base + i * 64 + lane;
+        dg[i] = k < n ? (keys[k] >> shift) & mask : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const bool valid = base + i * 64 + lane < n;
+        const uint64_t peers = match_peers(dg[i], bits, valid);
+        if (valid && (peers & lt_mask) == 0ull) h[wave][dg[i]] += (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    for (int dgt = threadIdx.x; dgt < nbins; dgt += kRadixThreads) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int w = 0; w < kRadixWaves; ++w) t += h[w][dgt];
+        hist[(int64_t)dgt * nb + blockIdx.x] = t;
+    }
+}
+
+// Stable scatter of one radix pass (see the file header).  Optional final-pass
+// extras: rect_src != null gathers rect_out[pos] = rect_src[2 * val + 1] (the
+// packed tile rectangle of record `val`) and tt_out[pos] = its tile count.
+__global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift, int bits,
+    const uint32_t* __restrict__ hist_scan, int64_t nb, uint32_t* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out, const uint2* __restrict__ rect_src, uint2* __restrict__ rect_out,
+    uint32_t* __restrict__ tt_out) {
+    __shared__ uint32_t cnt[kRadixWaves][kMaxBins];  // per-wave counts, then per-wave block-local bases
+    __shared__ uint32_t gdelta[kMaxBins];            // global position - block-local position, per digit
+    __shared__ uint32_t scan_lds[kRadixThreads / 64];
+    __shared__ uint32_t skey[kRadixTile];
+    __shared__ uint32_t sval[kRadixTile];
+    const int nbins = 1 << bits;
+    const uint32_t mask = (uint32_t)nbins - 1u;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < kRadixWaves * kMaxBins; i += kRadixThreads) (&cnt[0][0])[i] = 0u;
     __syncthreads();
 
-    const int64_t base = (int64_t)blockIdx.x * kRadixTile + (int64_t)wave * (kRadixTile / 4);
+    const int64_t bbase = (int64_t)blockIdx.x * kRadixTile;
+    const int64_t base = bbase + (int64_t)wave * (kRadixTile / kRadixWaves);
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t key[kRadixItems], val[kRadixItems], rank[kRadixItems];
 #pragma unroll
@@ -201,57 +236,79 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
         const bool valid = k < n;
         key[i] = valid ? keys_in[k] : 0u;
         val[i] = valid ? (vals_in ? vals_in[k] : (uint32_t)k) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const bool valid = base + i * 64 + lane < n;
         const uint32_t dgt = (key[i] >> shift) & mask;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < bits; ++b) {
-            const bool bit = (dgt >> b) & 1u;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
+        const uint64_t peers = match_peers(dgt, bits, valid);
         const uint64_t lower = peers & lt_mask;
         const uint32_t c = valid ? cnt[wave][dgt] : 0u;
         rank[i] = c + (uint32_t)__popcll(lower);
         if (valid && lower == 0ull) cnt[wave][dgt] = c + (uint32_t)__popcll(peers);
     }
     __syncthreads();
-    for (int dgt = threadIdx.x; dgt < nbins; dgt += kRadixThreads) {
-        uint32_t s = hist_scan[(int64_t)dgt * nb + blockIdx.x];
+    {
+        // block-local digit offsets (kRadixThreads >= kMaxBins: one digit per thread)
+        const int dgt = threadIdx.x;
+        uint32_t tot = 0;
+        if (dgt < nbins) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            gbase[w][dgt] = s;
-            s += cnt[w][dgt];
+            for (int w = 0; w < kRadixWaves; ++w) tot += cnt[w][dgt];
+        }
+        uint32_t block_total;
+        const uint32_t loff = block_exclusive_scan<uint32_t, kRadixThreads>(tot, &block_total, scan_lds);
+        if (dgt < nbins) {
+            gdelta[dgt] = hist_scan[(int64_t)dgt * nb + blockIdx.x] - loff;
+            uint32_t s = loff;
+#pragma unroll
+            for (int w = 0; w < kRadixWaves; ++w) {
+                const uint32_t c = cnt[w][dgt];
+                cnt[w][dgt] = s;
+                s += c;
+            }
         }
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kRadixItems; ++i) {
-        const int64_t k = base + i * 64 + lane;
-        if (k >= n) continue;
-        const uint32_t dgt = (key[i] >> shift) & mask;
-        const uint32_t pos = gbase[wave][dgt] + rank[i];
-        keys_out[pos] = key[i];
-        if (gather) {
-            vals_out[pos] = gather[val[i]];
-            inv[val[i]] = pos;
-        } else {
-            vals_out[pos] = val[i];
+        if (base + i * 64 + lane >= n) continue;
+        const uint32_t lp = cnt[wave][(key[i] >> shift) & mask] + rank[i];
+        skey[lp] = key[i];
+        sval[lp] = val[i];
+    }
+    __syncthreads();
+    const int64_t nblk = n - bbase < kRadixTile ? n - bbase : kRadixTile;
+#pragma unroll 4
+    for (int i = 0; i < kRadixItems; ++i) {
+        const int lp = i * kRadixThreads + threadIdx.x;
+        if (lp >= nblk) break;
+        const uint32_t k = skey[lp];
+        const uint32_t v = sval[lp];
+        const uint32_t pos = gdelta[(k >> shift) & mask] + (uint32_t)lp;
+        if (keys_out) keys_out[pos] = k;
+        vals_out[pos] = v;
+        if (rect_src) {
+            const uint2 r = rect_src[2 * (int64_t)v + 1];
+            rect_out[pos] = r;
+            tt_out[pos] = ((r.y & 0xffffu) - (r.x & 0xffffu)) * ((r.y >> 16) - (r.x >> 16));
         }
     }
 }
 
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const uint32_t* gather, uint32_t* gather_out, uint32_t* inv, uint32_t* hist,
+                             const uint2* rect_src, uint2* rect_out, uint32_t* tt_out, uint32_t* hist,
                              uint64_t* block_scratch, uint64_t* total, hipStream_t st, uint32_t** keys_out,
                              uint32_t** vals_out) {
     if (bits < 1) bits = 1;
-    const int passes = (bits + 7) / 8;
+    const int passes = (bits + kMaxDigitBits - 1) / kMaxDigitBits;
     const int dbits = (bits + passes - 1) / passes;
     const int64_t nb = (n + kRadixTile - 1) / kRadixTile;
     uint32_t* kb[2] = {kbuf0, kbuf1};
     uint32_t* vb[2] = {vbuf0, vbuf1};
     if (keys_out) *keys_out = kb[(passes - 1) & 1];
-    if (vals_out) *vals_out = gather ? gather_out : vb[(passes - 1) & 1];
+    if (vals_out) *vals_out = vb[(passes - 1) & 1];
     if (n <= 0) return hipSuccess;
     const uint32_t* ksrc = keys_in;
     const uint32_t* vsrc = vals_in;
@@ -260,12 +317,13 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
         const int pb = (shift + dbits <= bits) ? dbits : bits - shift;
         const bool last = p == passes - 1;
         uint32_t* kdst = kb[p & 1];
-        uint32_t* vdst = (last && gather) ? gather_out : vb[p & 1];
+        uint32_t* vdst = vb[p & 1];
         hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, n, shift, pb, hist, nb);
-        hipError_t e = launch_scan_u32(hist, nullptr, (int64_t)(1 << pb) * nb, hist, block_scratch, total, st);
+        hipError_t e = launch_scan_u32(hist, (int64_t)(1 << pb) * nb, hist, block_scratch, total, st);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, vsrc, n, shift, pb,
-                           hist, nb, kdst, vdst, last ? gather : nullptr, last ? inv : nullptr);
+                           hist, nb, kdst, vdst, last ? rect_src : nullptr, last ? rect_out : nullptr,
+                           last ? tt_out : nullptr);
         ksrc = kdst;
         vsrc = vdst;
     }
@@ -275,35 +333,53 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
 // ---------------------------------------------------------------------------
 // pair emission and ranges
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_sorted, const uint32_t* __restrict__ offsets,
-                                              const uint32_t* __restrict__ tiles_touched, float4* __restrict__ rec2,
-                                              int64_t VG, int64_t G, int T, int TX, uint32_t* __restrict__ pkey,
-                                              uint32_t* __restrict__ pair_g) {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= VG) return;
-    const uint32_t rid = rid_sorted[k];
-    const uint32_t cnt = tiles_touched[rid];
-    if (cnt == 0) return;
-    const uint32_t off = offsets[k];
-    const float4 r2 = rec2[rid];
-    const uint32_t lo = __float_as_uint(r2.z), hi = __float_as_uint(r2.w);
-    const int x0 = (int)(lo & 0xffffu), y0 = (int)(lo >> 16), x1 = (int)(hi & 0xffffu);
-    const uint32_t v = (uint32_t)(rid / G);
-    const uint32_t g = (uint32_t)(rid - (int64_t)v * G);
-    reinterpret_cast<float*>(rec2 + rid)[1] = __uint_as_float(off);
-    const int wx = x1 - x0;
-    const uint32_t vbase = v * (uint32_t)T;
-    for (uint32_t j = 0; j < cnt; ++j) {
-        const int ty = y0 + (int)(j / (uint32_t)wx), tx = x0 + (int)(j % (uint32_t)wx);
-        pkey[off + j] = vbase + (uint32_t)(ty * TX + tx);
-        pair_g[off + j] = g;
+// One block per 256 consecutive records (depth order).  The block's pairs form
+// one contiguous span of the output; each thread takes every 256th pair of the
+// span, finds its record by binary search over the records' offsets in LDS, and
+// writes the pair's global tile id and Gaussian: coalesced stores whatever the
+// records' tile counts are.
+__global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_sorted,
+                                              const uint2* __restrict__ rect_sorted,
+                                              const uint32_t* __restrict__ tt_sorted,
+                                              const uint32_t* __restrict__ offsets, int64_t VG, uint32_t G, int T,
+                                              int TX, uint32_t* __restrict__ pkey, uint32_t* __restrict__ pair_g) {
+    __shared__ uint32_t s_off[256];
+    __shared__ uint32_t s_rid[256];
+    __shared__ uint2 s_rect[256];
+    __shared__ uint32_t s_end;
+    const int64_t k0 = (int64_t)blockIdx.x * 256;
+    const int64_t k = k0 + threadIdx.x;
+    const int last = (int)((VG - 1 - k0) < 255 ? (VG - 1 - k0) : 255);
+    if (k < VG) {
+        s_off[threadIdx.x] = offsets[k];
+        s_rid[threadIdx.x] = rid_sorted[k];
+        s_rect[threadIdx.x] = rect_sorted[k];
+        if (threadIdx.x == last) s_end = offsets[k] + tt_sorted[k];
+    }
+    __syncthreads();
+    const uint32_t pstart = s_off[0], pend = s_end;
+    for (uint32_t p = pstart + threadIdx.x; p < pend; p += 256) {
+        int lo = 0, hi = last;
+        while (lo < hi) {  // largest t with s_off[t] <= p (it has a non-empty rectangle holding p)
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= p) lo = mid;
+            else hi = mid - 1;
+        }
+        const uint32_t j = p - s_off[lo];
+        const uint32_t rid = s_rid[lo];
+        const uint2 r = s_rect[lo];
+        const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
+        const uint32_t wx = x1 - x0;
+        const uint32_t v = rid / G;
+        pkey[p] = v * (uint32_t)T + (y0 + j / wx) * (uint32_t)TX + x0 + j % wx;
+        pair_g[p] = rid - v * G;
     }
 }
 
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_emit, dim3((unsigned)((s.VG + 255) / 256)), dim3(256), 0, st, rid_sorted, ws.offsets,
-                       ws.tiles_touched, ws.rec2, s.VG, s.G, s.T, s.TX, ws.pkey_a, ws.pair_g);
+    hipLaunchKernelGGL(k_emit, dim3((unsigned)((s.VG + 255) / 256)), dim3(256), 0, st, rid_sorted, ws.rect_sorted,
+                       ws.tt_sorted, ws.offsets, s.VG, (uint32_t)s.G, s.T, s.TX, ws.pkey_emit, ws.pair_g);
     return hipGetLastError();
 }
 

@@ -18,26 +18,29 @@ struct Workspace {
     float4* rec2;
     uint32_t* depth_key;   // depth bits, 0xffffffff when culled
     uint32_t* tiles_touched;
+    uint32_t* slot_base;   // exclusive scan of tiles_touched in record order: the record's first partial slot
     // depth sort (ping-pong) and the pair offsets in depth order
     uint32_t* dkey_b;
     uint32_t* drid_a;
     uint32_t* drid_b;
-    uint32_t* offsets;     // exclusive scan of tiles_touched in depth order
+    uint2* rect_sorted;    // tile rectangles in depth order
+    uint32_t* tt_sorted;   // tile counts in depth order
+    uint32_t* offsets;     // exclusive scan of tt_sorted (also the depth sort's key scratch)
     // scan / histogram scratch
     uint64_t* scan_blocks; // per-block sums (u64), then exclusive offsets
-    uint64_t* scan_total;  // total of the last scan
+    uint64_t* scan_total;  // [0] pair count, [1] slot total, [2] scratch of the radix scans
     uint32_t* hist;        // radix histograms, digit-major
     // (tile, Gaussian) pairs
-    uint32_t* pkey_a;
+    uint32_t* pkey_emit;   // global tile id of each pair, depth order
     uint32_t* pkey_b;
+    uint32_t* pkey_c;
     uint32_t* pval_a;
     uint32_t* pval_b;
-    uint32_t* pair_g;      // Gaussian of each emitted pair (emit order)
-    uint32_t* sorted_g;    // Gaussian of each pair in (tile, depth, id) order
-    uint32_t* inv;         // emit index -> sorted position
+    uint32_t* pair_g;      // Gaussian of each emitted pair, depth order
     uint2* ranges;         // per tile [start, end)
-    uint32_t* tile_done;   // per tile: end of the prefix the replay processed
-    float4* partials;      // per sorted pair: {W, U_a, U_mx, U_my}, {U_r, U_g, U_b, n_pix}
+    uint64_t* tile_stop;   // per tile: (depth bits, Gaussian) key of the first entry the replay skipped
+    float4* partials;      // per slot: {W, U_a, U_mx, U_my}, {U_r, U_g, U_b, n_pix}
+    float4* gv_sums;       // per record: the same eight sums over the pairs the replay reached
     float4* pixel;         // per pixel: rendered colour (rgb), final transmittance
     uint2* pixel_stats;    // per pixel: entries evaluated, entries past the distance cut
 };
@@ -60,29 +63,31 @@ Sizes make_sizes(const gs_dims& d);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, float near_plane,
                           float far_plane, Workspace& ws, hipStream_t st);
-// exclusive scan of in[idx[k]] (idx may be null) into out (u32); total -> *total (device u64)
-hipError_t launch_scan_u32(const uint32_t* in, const uint32_t* idx, int64_t n, uint32_t* out,
-                           uint64_t* block_scratch, uint64_t* total, hipStream_t st);
-// Stable LSD radix sort of (keys, vals) on bits [0, bits); vals_in == null means
-// identity values (the input index).  Pass p writes kbuf[p & 1] / vbuf[p & 1], so
-// the buffers must differ from each other and from keys_in/vals_in except that
-// kbuf1/vbuf1 may alias keys_in/vals_in (consumed by pass 0).  With gather != null
-// the final pass stores gather_out[pos] = gather[val] and inv[val] = pos instead
-// of the value.  *keys_out / *vals_out receive the arrays holding the result.
+// exclusive scan of in (u32) into out (may alias); total -> *total (device u64)
+hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
+                           hipStream_t st);
+// Stable LSD radix sort of (keys, vals) on bits [0, bits), digits of up to 8
+// bits; vals_in == null means identity values (the input index).  Pass p writes
+// kbuf[p & 1] / vbuf[p & 1], so these must differ from each other and from
+// keys_in/vals_in except that kbuf1/vbuf1 may alias keys_in/vals_in (consumed
+// by pass 0).  With rect_src != null the final pass also gathers
+// rect_out[pos] = rect_src[2 * val + 1] and tt_out[pos] = its tile count.
+// *keys_out / *vals_out receive the arrays holding the result.
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const uint32_t* gather, uint32_t* gather_out, uint32_t* inv, uint32_t* hist,
+                             const uint2* rect_src, uint2* rect_out, uint32_t* tt_out, uint32_t* hist,
                              uint64_t* block_scratch, uint64_t* total, hipStream_t st, uint32_t** keys_out,
                              uint32_t** vals_out);
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st);
 hipError_t launch_ranges(const uint32_t* sorted_keys, int64_t n, uint2* ranges, int64_t n_tiles,
                          hipStream_t st);
-hipError_t launch_render(const Sizes& s, const Workspace& ws, const float bg[3], float* color,
-                         float* T_final, int32_t* n_contrib, hipStream_t st);
-hipError_t launch_replay(const Sizes& s, const Workspace& ws, const float* observed, float eps,
-                         float den_min, hipStream_t st);
-hipError_t launch_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s,
-                           const Workspace& ws, float eps, float lambda, float* tokens, hipStream_t st);
+hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float bg[3],
+                         float* color, float* T_final, int32_t* n_contrib, hipStream_t st);
+hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* observed,
+                         float eps, float den_min, hipStream_t st);
+hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, hipStream_t st);
+hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
+                         float eps, float lambda, float* tokens, hipStream_t st);
 hipError_t launch_exp2(const float* in, float* out, int64_t n, hipStream_t st);
 
 }  // namespace gsr

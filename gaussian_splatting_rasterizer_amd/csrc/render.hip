@@ -102,11 +102,11 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     pixel_stats[pix] = make_uint2(stop != 0xffffffffu ? stop - rg.x + 1u : rg.y - rg.x, n_near);
 }
 
-hipError_t launch_render(const Sizes& s, const Workspace& ws, const float bg[3], float* color, float* T_final,
-                         int32_t* n_contrib, hipStream_t st) {
+hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float bg[3], float* color,
+                         float* T_final, int32_t* n_contrib, hipStream_t st) {
     const int64_t tiles = (int64_t)s.V * s.T;
     if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, ws.sorted_g, ws.rec0, ws.rec1,
+    hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1,
                        ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel,
                        ws.pixel_stats);
     return hipGetLastError();

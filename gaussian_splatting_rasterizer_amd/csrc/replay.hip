@@ -20,13 +20,17 @@
 // The 64 lanes of a wave are reduced with a reduce-scatter butterfly (four
 // exchange steps leave lane l holding component l >> 3 summed over 64 lanes,
 // then three in-group steps), only when some lane contributed; the four waves
-// meet in LDS and one 32-byte partial per (tile, Gaussian) pair is stored at
-// the pair's sorted position -- no atomics, so the result is deterministic.
-// Pairs after the tile's early termination are never written; tile_done
-// records where each tile stopped.
+// meet in LDS and one 32-byte partial per (tile, Gaussian) pair is stored with
+// plain stores -- no atomics, so the result is deterministic.  The partial's
+// slot is the record's slot base (a scan of tile counts in record order) plus
+// the tile's row-major index in the record's rectangle, so one Gaussian's
+// slots are contiguous per view and adjacent Gaussians' slots are adjacent.
+// Pairs after the tile's early termination are never written; tile_stop keeps
+// the (depth bits, Gaussian) list key at which each tile stopped.
 //
-// k_finalize: one thread per Gaussian sums its pairs per view (through the
-// emit-order -> sorted-position map), then in float64
+// k_gather_slots: per record (record order, coalesced), the sums of the pairs
+// the replay reached.
+// k_tokens: one thread per Gaussian, in float64
 //     q_v = eps + W_v,  Q = eps + sum_v q_v,  gamma_v = q_v / Q
 //     b_mu = sum_v gamma_v J_v^T s_mu_v = (1/Q) sum_v J_v^T conic_v U_mu_v
 //     s_a  = (1/Q) sum_v (1 - o) U_a_v,   s_SH = (1/Q) sum_v M_color (B_v (x) U_c_v)
@@ -67,14 +71,17 @@ __device__ __forceinline__ float wave_reduce8(const float (&x)[8], int lane) {
 }
 
 __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
+                                                const uint32_t* __restrict__ depth_key,
+                                                const uint32_t* __restrict__ slot_base,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
                                                 const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
                                                 const float4* __restrict__ pixel, const float* __restrict__ observed,
                                                 float eps, float den_min, float4* __restrict__ partials,
-                                                uint32_t* __restrict__ tile_done) {
+                                                uint64_t* __restrict__ tile_stop) {
     __shared__ float4 s0[kReplayBatch];
     __shared__ float4 s1[kReplayBatch];
     __shared__ float s2[kReplayBatch];
+    __shared__ uint32_t s_emit[kReplayBatch];  // partial slot of each staged pair
     __shared__ __align__(16) float sp[4][kReplayBatch][8];
 
     const int tile = blockIdx.x;
@@ -112,10 +119,14 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
-            const float cb = rec2[rid].x;
+            const float4 c = rec2[rid];
             s0[threadIdx.x] = a;
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
-            s2[threadIdx.x] = clamp_colour(cb);
+            s2[threadIdx.x] = clamp_colour(c.x);
+            // slot of this (tile, Gaussian) pair: the record's slot base + row-major tile index
+            const uint32_t lo = __float_as_uint(c.z), hi = __float_as_uint(c.w);
+            const uint32_t x0 = lo & 0xffffu, y0 = lo >> 16, wx = (hi & 0xffffu) - x0;
+            s_emit[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kReplayBatch, rg.y - base);
@@ -181,19 +192,27 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 acc.z += q.z;
                 acc.w += q.w;
             }
-            partials[2 * (int64_t)(base + j) + h] = acc;
+            partials[2 * (int64_t)s_emit[j] + h] = acc;
         }
     }
-    if (threadIdx.x == 0) tile_done[tile] = base < rg.y ? base : rg.y;
+    if (threadIdx.x == 0) {
+        uint64_t stop = ~0ull;
+        if (base < rg.y) {
+            const uint32_t g = sorted_g[base];
+            stop = ((uint64_t)depth_key[vG + g] << 32) | g;
+        }
+        tile_stop[tile] = stop;
+    }
 }
 
-hipError_t launch_replay(const Sizes& s, const Workspace& ws, const float* observed, float eps, float den_min,
-                         hipStream_t st) {
+hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* observed,
+                         float eps, float den_min, hipStream_t st) {
     const int64_t tiles = (int64_t)s.V * s.T;
     if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, ws.sorted_g, ws.rec0, ws.rec1,
+    hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.depth_key,
+                       ws.slot_base, ws.rec0, ws.rec1,
                        ws.rec2, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, eps, den_min, ws.partials,
-                       ws.tile_done);
+                       ws.tile_stop);
     return hipGetLastError();
 }
 
@@ -234,150 +253,195 @@ __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */,
     ev[2] = e2;
 }
 
-template <int D>
-__global__ __launch_bounds__(128) void k_finalize(const float* __restrict__ means, const float* __restrict__ opac,
-                                                  int64_t G, int V, CamPack cams, int T, int TX,
-                                                  const float4* __restrict__ rec0, const float4* __restrict__ rec1,
-                                                  const float4* __restrict__ rec2, const uint32_t* __restrict__ inv,
-                                                  const uint32_t* __restrict__ tile_done,
-                                                  const float4* __restrict__ partials, double eps, double lambda,
-                                                  float* __restrict__ tokens) {
-    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (g >= G) return;
-    const double mu[3] = {means[3 * g], means[3 * g + 1], means[3 * g + 2]};
-    const double one_minus_o = 1.0 - (double)opac[g];
-
-    double Q = eps;
-    double bnum[3] = {0.0, 0.0, 0.0};
-    double anum = 0.0;
-    double shnum[3 * D];
-#pragma unroll
-    for (int k = 0; k < 3 * D; ++k) shnum[k] = 0.0;
-    double Anum[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-
-    for (int v = 0; v < V; ++v) {
-        const int64_t rid = (int64_t)v * G + g;
-        const float4 r2 = rec2[rid];
-        const uint32_t lo = __float_as_uint(r2.z), hi = __float_as_uint(r2.w);
-        const int x0 = (int)(lo & 0xffffu), y0 = (int)(lo >> 16);
-        const int x1 = (int)(hi & 0xffffu), y1 = (int)(hi >> 16);
-        const int wx = x1 - x0;
-        const int cnt = wx * (y1 - y0);
-        const uint32_t off = __float_as_uint(r2.y);
-        double W = 0.0, Ua = 0.0, Umx = 0.0, Umy = 0.0, Uc0 = 0.0, Uc1 = 0.0, Uc2 = 0.0;
-        for (int j = 0; j < cnt; ++j) {
-            const uint32_t pos = inv[off + j];
-            const int tl = v * T + (y0 + j / wx) * TX + (x0 + j % wx);
-            if (pos >= tile_done[tl]) continue;
-            const float4 p0 = partials[2 * (int64_t)pos];
-            const float4 p1 = partials[2 * (int64_t)pos + 1];
-            W += p0.x;
-            Ua += p0.y;
-            Umx += p0.z;
-            Umy += p0.w;
-            Uc0 += p1.x;
-            Uc1 += p1.y;
-            Uc2 += p1.z;
-        }
-        const double q = eps + W;
-        Q += q;
-        if (cnt == 0) continue;  // culled in this view: J = 0, no scores
-
-        const float4 a0 = rec0[rid];
-        const float4 a1 = rec1[rid];
-        const double ca = (double)a0.z / (double)kNegHalfLog2e;
-        const double cb = (double)a0.w / (double)kNegLog2e;
-        const double cc = (double)a1.x / (double)kNegHalfLog2e;
-        const double smx = ca * Umx + cb * Umy;
-        const double smy = cb * Umx + cc * Umy;
-
-        const float* cam = cams.c[v];
-        double R[9];
-#pragma unroll
-        for (int k = 0; k < 9; ++k) R[k] = cam[k];
-        const double t0 = cam[9], t1 = cam[10], t2 = cam[11];
-        const double fx = cam[12], fy = cam[13];
-        const double tcx = R[0] * mu[0] + R[1] * mu[1] + R[2] * mu[2] + t0;
-        const double tcy = R[3] * mu[0] + R[4] * mu[1] + R[5] * mu[2] + t1;
-        const double tcz = R[6] * mu[0] + R[7] * mu[1] + R[8] * mu[2] + t2;
-        const double iz = 1.0 / tcz;
-        const double jp00 = fx * iz, jp02 = -fx * tcx * iz * iz;
-        const double jp11 = fy * iz, jp12 = -fy * tcy * iz * iz;
-        double J0[3], J1[3];
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            J0[k] = jp00 * R[k] + jp02 * R[6 + k];
-            J1[k] = jp11 * R[3 + k] + jp12 * R[6 + k];
-        }
-#pragma unroll
-        for (int k = 0; k < 3; ++k) bnum[k] += J0[k] * smx + J1[k] * smy;
-        anum += one_minus_o * Ua;
-        Anum[0] += q * (J0[0] * J0[0] + J1[0] * J1[0]);
-        Anum[1] += q * (J0[0] * J0[1] + J1[0] * J1[1]);
-        Anum[2] += q * (J0[0] * J0[2] + J1[0] * J1[2]);
-        Anum[3] += q * (J0[1] * J0[1] + J1[1] * J1[1]);
-        Anum[4] += q * (J0[1] * J0[2] + J1[1] * J1[2]);
-        Anum[5] += q * (J0[2] * J0[2] + J1[2] * J1[2]);
-
-        // SH basis along the view direction; clamp mask from the colour sign
-        const double ccx = -(R[0] * t0 + R[3] * t1 + R[6] * t2);
-        const double ccy = -(R[1] * t0 + R[4] * t1 + R[7] * t2);
-        const double ccz = -(R[2] * t0 + R[5] * t1 + R[8] * t2);
-        const double dx = mu[0] - ccx, dy = mu[1] - ccy, dz = mu[2] - ccz;
-        const double il = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
-        double B[D];
-        sh_basis_f64(dx * il, dy * il, dz * il, D, B);
-        const double m0 = a1.z >= 0.0f ? Uc0 : 0.0;
-        const double m1 = a1.w >= 0.0f ? Uc1 : 0.0;
-        const double m2 = r2.x >= 0.0f ? Uc2 : 0.0;
-#pragma unroll
-        for (int k = 0; k < D; ++k) {
-            shnum[3 * k] += B[k] * m0;
-            shnum[3 * k + 1] += B[k] * m1;
-            shnum[3 * k + 2] += B[k] * m2;
+// Per (view, Gaussian) record, in record order: the eight sums over the record's
+// tiles that the replay reached.  The record's slots are contiguous and
+// consecutive records' slots are adjacent, so reads and writes are coalesced.
+// Tile lists are ordered by the (depth bits, Gaussian) key, so a pair was
+// reached iff its key is below the key at which its tile's replay stopped.
+__global__ __launch_bounds__(256) void k_gather_slots(int64_t VG, uint32_t G, int T, int TX,
+                                                      const float4* __restrict__ rec2,
+                                                      const uint32_t* __restrict__ depth_key,
+                                                      const uint32_t* __restrict__ slot_base,
+                                                      const uint64_t* __restrict__ tile_stop,
+                                                      const float4* __restrict__ partials,
+                                                      float4* __restrict__ gv_sums) {
+    const int64_t rid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (rid >= VG) return;
+    const float4 r2 = rec2[rid];
+    const uint32_t lo = __float_as_uint(r2.z), hi = __float_as_uint(r2.w);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (hi != 0u) {
+        const uint32_t v = (uint32_t)rid / G;
+        const uint32_t g = (uint32_t)rid - v * G;
+        const uint64_t key = ((uint64_t)depth_key[rid] << 32) | (uint64_t)g;
+        const int x0 = (int)(lo & 0xffffu), y0 = (int)(lo >> 16), x1 = (int)(hi & 0xffffu), y1 = (int)(hi >> 16);
+        int64_t slot = slot_base[rid];
+        for (int ty = y0; ty < y1; ++ty) {
+            const uint64_t* stop_row = tile_stop + (int64_t)v * T + (int64_t)ty * TX;
+            for (int tx = x0; tx < x1; ++tx, ++slot) {
+                if (key >= stop_row[tx]) continue;
+                const float4 p0 = partials[2 * slot];
+                const float4 p1 = partials[2 * slot + 1];
+                a.x += p0.x;
+                a.y += p0.y;
+                a.z += p0.z;
+                a.w += p0.w;
+                b.x += p1.x;
+                b.y += p1.y;
+                b.z += p1.z;
+                b.w += p1.w;
+            }
         }
     }
-
-    const double iQ = 1.0 / Q;
-    double A[6];
-#pragma unroll
-    for (int k = 0; k < 6; ++k) A[k] = Anum[k] * iQ;
-    A[0] += lambda;
-    A[3] += lambda;
-    A[5] += lambda;
-    double ev[3];
-    sym3_eigen_desc(A, ev);
-    const double tr = A[0] + A[3] + A[5];
-    float* z = tokens + (int64_t)g * (9 + 3 * D);
-    z[0] = (float)(bnum[0] * iQ);
-    z[1] = (float)(bnum[1] * iQ);
-    z[2] = (float)(bnum[2] * iQ);
-    z[3] = (float)(anum * iQ);
-#pragma unroll
-    for (int k = 0; k < 3 * D; ++k) z[4 + k] = (float)(shnum[k] * iQ);
-    z[4 + 3 * D] = (float)log(Q);
-    const double itr = 1.0 / (tr + eps);
-    z[5 + 3 * D] = (float)(ev[0] * itr);
-    z[6 + 3 * D] = (float)(ev[1] * itr);
-    z[7 + 3 * D] = (float)(ev[2] * itr);
-    z[8 + 3 * D] = (float)log(tr + eps);
+    gv_sums[2 * rid] = a;
+    gv_sums[2 * rid + 1] = b;
 }
 
-hipError_t launch_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
-                           float eps, float lambda, float* tokens, hipStream_t st) {
-    if (s.G == 0) return hipSuccess;
-    const dim3 block(128), grid((unsigned)((s.G + 127) / 128));
-#define GSR_LAUNCH_FINALIZE(DD)                                                                               \
-    hipLaunchKernelGGL(k_finalize<DD>, grid, block, 0, st, sc.means, sc.opacities, s.G, s.V, cams, s.T, s.TX, \
-                       ws.rec0, ws.rec1, ws.rec2, ws.inv, ws.tile_done, ws.partials, (double)eps,           \
-                       (double)lambda, tokens)
-    switch (s.d) {
-        case 1: GSR_LAUNCH_FINALIZE(1); break;
-        case 4: GSR_LAUNCH_FINALIZE(4); break;
-        case 9: GSR_LAUNCH_FINALIZE(9); break;
-        default: GSR_LAUNCH_FINALIZE(16); break;
+hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, hipStream_t st) {
+    if (s.VG == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_gather_slots, dim3((unsigned)((s.VG + 255) / 256)), dim3(256), 0, st, s.VG, (uint32_t)s.G,
+                       s.T, s.TX, ws.rec2, ws.depth_key, ws.slot_base, ws.tile_stop, ws.partials, ws.gv_sums);
+    return hipGetLastError();
+}
+
+// One thread per Gaussian: cross-view aggregation and the token, staged through
+// LDS so that the block's tokens leave as one coalesced span.
+constexpr int kTokThreads = 128;
+
+template <int D>
+__global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict__ means, const float* __restrict__ opac,
+                                                        int64_t G, int V, CamPack cams,
+                                                        const float4* __restrict__ rec0, const float4* __restrict__ rec1,
+                                                        const float4* __restrict__ rec2,
+                                                        const float4* __restrict__ gv_sums, double eps, double lambda,
+                                                        float* __restrict__ tokens) {
+    constexpr int DT = 9 + 3 * D;
+    __shared__ float s_tok[kTokThreads * DT];
+    const int64_t g0 = (int64_t)blockIdx.x * kTokThreads;
+    const int64_t g = g0 + threadIdx.x;
+    float* z = s_tok + threadIdx.x * DT;
+    if (g < G) {
+        const double mu[3] = {means[3 * g], means[3 * g + 1], means[3 * g + 2]};
+        const double one_minus_o = 1.0 - (double)opac[g];
+        double Q = eps;
+        double bnum[3] = {0.0, 0.0, 0.0};
+        double anum = 0.0;
+        double Anum[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+        float shnum[3 * D];
+#pragma unroll
+        for (int k = 0; k < 3 * D; ++k) shnum[k] = 0.0f;
+
+        for (int v = 0; v < V; ++v) {
+            const int64_t rid = (int64_t)v * G + g;
+            const float4 r2 = rec2[rid];
+            const uint32_t hi = __float_as_uint(r2.w);
+            if (hi == 0u) {  // culled in this view: q = eps, J = 0, no scores
+                Q += eps;
+                continue;
+            }
+            const float4 p0 = gv_sums[2 * rid];
+            const float4 p1 = gv_sums[2 * rid + 1];
+            const double q = eps + (double)p0.x;
+            Q += q;
+            const float4 a0 = rec0[rid];
+            const float4 a1 = rec1[rid];
+            const double ca = (double)a0.z / (double)kNegHalfLog2e;
+            const double cb = (double)a0.w / (double)kNegLog2e;
+            const double cc = (double)a1.x / (double)kNegHalfLog2e;
+            const double smx = ca * p0.z + cb * p0.w;
+            const double smy = cb * p0.z + cc * p0.w;
+
+            const float* cam = cams.c[v];
+            double R[9];
+#pragma unroll
+            for (int k = 0; k < 9; ++k) R[k] = cam[k];
+            const double t0 = cam[9], t1 = cam[10], t2 = cam[11];
+            const double fx = cam[12], fy = cam[13];
+            const double tcx = R[0] * mu[0] + R[1] * mu[1] + R[2] * mu[2] + t0;
+            const double tcy = R[3] * mu[0] + R[4] * mu[1] + R[5] * mu[2] + t1;
+            const double tcz = R[6] * mu[0] + R[7] * mu[1] + R[8] * mu[2] + t2;
+            const double iz = 1.0 / tcz;
+            const double jp00 = fx * iz, jp02 = -fx * tcx * iz * iz;
+            const double jp11 = fy * iz, jp12 = -fy * tcy * iz * iz;
+            double J0[3], J1[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                J0[k] = jp00 * R[k] + jp02 * R[6 + k];
+                J1[k] = jp11 * R[3 + k] + jp12 * R[6 + k];
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) bnum[k] += J0[k] * smx + J1[k] * smy;
+            anum += one_minus_o * (double)p0.y;
+            Anum[0] += q * (J0[0] * J0[0] + J1[0] * J1[0]);
+            Anum[1] += q * (J0[0] * J0[1] + J1[0] * J1[1]);
+            Anum[2] += q * (J0[0] * J0[2] + J1[0] * J1[2]);
+            Anum[3] += q * (J0[1] * J0[1] + J1[1] * J1[1]);
+            Anum[4] += q * (J0[1] * J0[2] + J1[1] * J1[2]);
+            Anum[5] += q * (J0[2] * J0[2] + J1[2] * J1[2]);
+
+            // SH basis along the view direction; clamp mask from the sign of the pre-clamp colour
+            const double ccx = -(R[0] * t0 + R[3] * t1 + R[6] * t2);
+            const double ccy = -(R[1] * t0 + R[4] * t1 + R[7] * t2);
+            const double ccz = -(R[2] * t0 + R[5] * t1 + R[8] * t2);
+            const double dx = mu[0] - ccx, dy = mu[1] - ccy, dz = mu[2] - ccz;
+            const double il = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
+            float B[D];
+            sh_basis_f32((float)(dx * il), (float)(dy * il), (float)(dz * il), D, B);
+            const float m0 = a1.z >= 0.0f ? p1.x : 0.0f;
+            const float m1 = a1.w >= 0.0f ? p1.y : 0.0f;
+            const float m2 = r2.x >= 0.0f ? p1.z : 0.0f;
+#pragma unroll
+            for (int k = 0; k < D; ++k) {
+                shnum[3 * k] += B[k] * m0;
+                shnum[3 * k + 1] += B[k] * m1;
+                shnum[3 * k + 2] += B[k] * m2;
+            }
+        }
+
+        const double iQ = 1.0 / Q;
+        double A[6];
+#pragma unroll
+        for (int k = 0; k < 6; ++k) A[k] = Anum[k] * iQ;
+        A[0] += lambda;
+        A[3] += lambda;
+        A[5] += lambda;
+        double ev[3];
+        sym3_eigen_desc(A, ev);
+        const double tr = A[0] + A[3] + A[5];
+        z[0] = (float)(bnum[0] * iQ);
+        z[1] = (float)(bnum[1] * iQ);
+        z[2] = (float)(bnum[2] * iQ);
+        z[3] = (float)(anum * iQ);
+        const float fiQ = (float)iQ;
+#pragma unroll
+        for (int k = 0; k < 3 * D; ++k) z[4 + k] = shnum[k] * fiQ;
+        z[4 + 3 * D] = (float)log(Q);
+        const double itr = 1.0 / (tr + eps);
+        z[5 + 3 * D] = (float)(ev[0] * itr);
+        z[6 + 3 * D] = (float)(ev[1] * itr);
+        z[7 + 3 * D] = (float)(ev[2] * itr);
+        z[8 + 3 * D] = (float)log(tr + eps);
     }
-#undef GSR_LAUNCH_FINALIZE
+    __syncthreads();
+    const int64_t nvalid = (G - g0 < kTokThreads ? G - g0 : kTokThreads) * DT;
+    float* out = tokens + g0 * DT;
+    for (int64_t i = threadIdx.x; i < nvalid; i += kTokThreads) out[i] = s_tok[i];
+}
+
+hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws, float eps,
+                         float lambda, float* tokens, hipStream_t st) {
+    if (s.G == 0) return hipSuccess;
+    const dim3 block(kTokThreads), grid((unsigned)((s.G + kTokThreads - 1) / kTokThreads));
+#define GSR_LAUNCH_TOKENS(DD)                                                                              \
+    hipLaunchKernelGGL(k_tokens<DD>, grid, block, 0, st, sc.means, sc.opacities, s.G, s.V, cams, ws.rec0, \
+                       ws.rec1, ws.rec2, ws.gv_sums, (double)eps, (double)lambda, tokens)
+    switch (s.d) {
+        case 1: GSR_LAUNCH_TOKENS(1); break;
+        case 4: GSR_LAUNCH_TOKENS(4); break;
+        case 9: GSR_LAUNCH_TOKENS(9); break;
+        default: GSR_LAUNCH_TOKENS(16); break;
+    }
+#undef GSR_LAUNCH_TOKENS
     return hipGetLastError();
 }
 
