@@ -138,6 +138,41 @@ __device__ __forceinline__ int eval_alpha(float4 r0, float qc, float opac, float
     return alpha >= kAlphaMin ? 2 : 1;
 }
 
+// Conservative pixel bounding box of the region where an entry can pass the
+// alpha test, used only to skip entries that cannot pass anywhere in a block
+// of pixels.  With Q(d) = a' dx^2 + 2 b' dx dy + c' dy^2 (a' = -qa, b' = -qb/2,
+// c' = -qc, positive definite) the exact exponent is -Q(d), and alpha = o G >=
+// 1/255 needs it to be >= -t with t = min(8, log2(255 o)).  The float32
+// evaluation of the exponent (offsets rounded once, then three products and two
+// fused multiply-adds) differs from -Q(d) by at most 3u Qabs(d) + 3u Q(d) with
+// u = 2^-24 and Qabs <= cond(A) Q, and the float32 exponential and product
+// o * G add a few more units of u; so a pixel can pass only if
+// Q(d) <= t_eff = (t + 1e-5) / (1 - 8 u (cond + 1)).  The region Q <= t_eff has
+// half-widths sqrt(t_eff c' / det) and sqrt(t_eff a' / det); all of this is
+// computed in float64 from the exact float32 coefficients and widened by 0.01
+// px plus 1e-6 relative before rounding to float32.  When 8 u (cond + 1) >= 1/2
+// the box is unbounded (never skip).  Returns {x0, x1, y0, y1}; an empty box
+// when the entry can never pass (o <= 1/255).
+__device__ __forceinline__ float4 entry_box(float4 r0, float qc, float opac) {
+    const double a = -(double)r0.z, b = -0.5 * (double)r0.w, c = -(double)qc;
+    const double det = a * c - b * b;
+    const double tt = log2(255.0 * (double)opac);
+    const float4 all = make_float4(-3.0e38f, 3.0e38f, -3.0e38f, 3.0e38f);
+    if (!(tt > -1e-5)) return make_float4(3.0e38f, -3.0e38f, 3.0e38f, -3.0e38f);
+    if (!(det > 0.0) || !(a > 0.0) || !(c > 0.0)) return all;
+    const double t = (tt < 8.0 ? tt : 8.0) + 1e-5;
+    const double mid = 0.5 * (a + c), hd = sqrt(0.25 * (a - c) * (a - c) + b * b);
+    const double lmax = mid + hd, lmin = det / lmax;
+    const double grow = 8.0 * 5.9604644775390625e-8 * (lmax / lmin + 1.0);
+    if (!(grow < 0.5)) return all;
+    const double te = t / (1.0 - grow);
+    const double ex = sqrt(te * c / det), ey = sqrt(te * a / det);
+    const double mx = r0.x, my = r0.y;
+    auto lo = [](double v) { return (float)(v - 0.01 - 1e-6 * fabs(v)); };
+    auto hi = [](double v) { return (float)(v + 0.01 + 1e-6 * fabs(v)); };
+    return make_float4(lo(mx - ex), hi(mx + ex), lo(my - ey), hi(my + ey));
+}
+
 // Compensated (Kahan) accumulation of the prefix colour; the true sum is hi - comp.
 __device__ __forceinline__ void kahan_add(float& hi, float& comp, float x) {
     const float y = x - comp;

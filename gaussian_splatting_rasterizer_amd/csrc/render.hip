@@ -6,10 +6,13 @@
 //
 // One 256-thread block per tile; the four wave64s each own an 8x8 pixel
 // quadrant, so a wave's lanes stay spatially coherent and a wave whose 64
-// pixels are all saturated skips the evaluation entirely.  Batches of 256 list
-// entries are gathered (one per thread) into LDS -- 36 bytes per entry:
-// centre, exponent coefficients, opacity, clamped colour -- and read back as
-// broadcasts.  Alpha decisions use the float32 canonical order and the
+// pixels are all saturated stops.  Batches of 256 list entries are gathered
+// (one per thread) into LDS -- centre, exponent coefficients, opacity, clamped
+// colour, and a conservative box of the pixels the entry can reach -- and each
+// wave compacts, in list order, the entries whose box meets its quadrant, then
+// walks only those with broadcast LDS reads.  The box is conservative for the
+// float32 evaluation, so the skipped entries are exactly ones every pixel of
+// the quadrant would have skipped.  Alpha decisions use the float32 canonical order and the
 // specified exponential; the prefix colour is accumulated with compensated
 // (Kahan) summation so that the replay can recover the suffix accurately.
 #include "gsr_internal.hpp"
@@ -24,21 +27,27 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                                                 float bg0, float bg1, float bg2, float* __restrict__ color,
                                                 float* __restrict__ T_out, int32_t* __restrict__ n_out,
                                                 float4* __restrict__ pixel, uint2* __restrict__ pixel_stats) {
-    __shared__ float4 s0[kRenderBatch];
-    __shared__ float4 s1[kRenderBatch];  // {qc, opacity, colour r, colour g}
-    __shared__ float s2[kRenderBatch];   // colour b
+    __shared__ float4 s0[kRenderBatch];   // {mx, my, qa, qb}
+    __shared__ float4 s1[kRenderBatch];   // {qc, opacity, colour r, colour g}
+    __shared__ float s2[kRenderBatch];    // colour b
+    __shared__ float4 sbox[kRenderBatch]; // conservative box of the pixels the entry can reach
+    __shared__ uint8_t slist[4][kRenderBatch];
 
     const int tile = blockIdx.x;
     const int v = tile / T;
     const int t = tile - v * T;
     const int ty = t / TX, tx = t - ty * TX;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int pxi = tx * kTile + (wave & 1) * 8 + (lane & 7);
-    const int pyi = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
+    const int qx = tx * kTile + (wave & 1) * 8, qy = ty * kTile + (wave >> 1) * 8;
+    const int pxi = qx + (lane & 7);
+    const int pyi = qy + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
     const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    // pixel-centre range of this wave's 8x8 quadrant
+    const float qx0 = (float)qx + 0.5f, qx1 = (float)qx + 7.5f, qy0 = (float)qy + 0.5f, qy1 = (float)qy + 7.5f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     float Tr = 1.0f;
     float h0 = 0.f, h1 = 0.f, h2 = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
@@ -58,31 +67,52 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
             s0[threadIdx.x] = a;
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(cb);
+            sbox[threadIdx.x] = entry_box(a, b.x, b.y);
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kRenderBatch, rg.y - base);
-        if (!done) {
-            for (int j = 0; j < cnt; ++j) {
+        if (__ballot(!done) == 0ull) continue;  // this wave is finished; keep the block's barriers
+        // this wave's entries, in list order: those whose box meets the quadrant
+        int nw = 0;
+        for (int c = 0; c < cnt; c += 64) {
+            const int j = c + lane;
+            bool hit = false;
+            if (j < cnt) {
+                const float4 bx = sbox[j];
+                hit = bx.x <= qx1 && bx.y >= qx0 && bx.z <= qy1 && bx.w >= qy0;
+            }
+            const uint64_t m = __ballot(hit);
+            if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
+            nw += __popcll(m);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int k = 0; k < nw; ++k) {
+            const int j = slist[wave][k];
+            if (!done) {
                 const float4 a = s0[j];
                 const float4 b = s1[j];
                 float dx, dy, alpha;
                 bool clamped;
                 const int code = eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped);
                 n_near += code != 0;
-                if (code != 2) continue;
-                const float tT = Tr * (1.0f - alpha);
-                if (tT < kTMin) {
-                    done = true;
-                    stop = base + (uint32_t)j;
-                    break;
+                if (code == 2) {
+                    const float tT = Tr * (1.0f - alpha);
+                    if (tT < kTMin) {
+                        done = true;
+                        stop = base + (uint32_t)j;
+                    } else {
+                        const float w = alpha * Tr;
+                        kahan_add(h0, c0, b.z * w);
+                        kahan_add(h1, c1, b.w * w);
+                        kahan_add(h2, c2, s2[j] * w);
+                        Tr = tT;
+                        ++n;
+                    }
                 }
-                const float w = alpha * Tr;
-                kahan_add(h0, c0, b.z * w);
-                kahan_add(h1, c1, b.w * w);
-                kahan_add(h2, c2, s2[j] * w);
-                Tr = tT;
-                ++n;
             }
+            if (__ballot(!done) == 0ull) break;
         }
     }
     if (!inside) return;

@@ -81,7 +81,9 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     __shared__ float4 s0[kReplayBatch];
     __shared__ float4 s1[kReplayBatch];
     __shared__ float s2[kReplayBatch];
-    __shared__ uint32_t s_emit[kReplayBatch];  // partial slot of each staged pair
+    __shared__ float4 sbox[kReplayBatch];
+    __shared__ uint32_t s_slot[kReplayBatch];  // partial slot of each staged pair
+    __shared__ uint8_t slist[4][kReplayBatch];
     __shared__ __align__(16) float sp[4][kReplayBatch][8];
 
     const int tile = blockIdx.x;
@@ -89,12 +91,15 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     const int t = tile - v * T;
     const int ty = t / TX, tx = t - ty * TX;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int pxi = tx * kTile + (wave & 1) * 8 + (lane & 7);
-    const int pyi = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
+    const int qx = tx * kTile + (wave & 1) * 8, qy = ty * kTile + (wave >> 1) * 8;
+    const int pxi = qx + (lane & 7);
+    const int pyi = qy + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
     const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    const float qx0 = (float)qx + 0.5f, qx1 = (float)qx + 7.5f, qy0 = (float)qy + 0.5f, qy1 = (float)qy + 7.5f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     float Ch0 = 0.f, Ch1 = 0.f, Ch2 = 0.f, r0 = 0.f, r1 = 0.f, r2 = 0.f;
     if (inside) {
@@ -123,16 +128,34 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             s0[threadIdx.x] = a;
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(c.x);
+            sbox[threadIdx.x] = entry_box(a, b.x, b.y);
             // slot of this (tile, Gaussian) pair: the record's slot base + row-major tile index
             const uint32_t lo = __float_as_uint(c.z), hi = __float_as_uint(c.w);
             const uint32_t x0 = lo & 0xffffu, y0 = lo >> 16, wx = (hi & 0xffffu) - x0;
-            s_emit[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
+            s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
         }
-        __syncthreads();
         const int cnt = (int)min((uint32_t)kReplayBatch, rg.y - base);
-        const bool wave_live = __ballot(!done) != 0ull;
-        if (wave_live) {
-            for (int j = 0; j < cnt; ++j) {
+        // this wave's partial rows start at zero; entries it contributes to overwrite theirs
+        for (int e = lane; e < cnt * 8; e += 64) (&sp[wave][0][0])[e] = 0.0f;
+        __syncthreads();
+        if (__ballot(!done) != 0ull) {
+            int nw = 0;
+            for (int c = 0; c < cnt; c += 64) {
+                const int j = c + lane;
+                bool hit = false;
+                if (j < cnt) {
+                    const float4 bx = sbox[j];
+                    hit = bx.x <= qx1 && bx.y >= qx0 && bx.z <= qy1 && bx.w >= qy0;
+                }
+                const uint64_t m = __ballot(hit);
+                if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
+                nw += __popcll(m);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int k = 0; k < nw; ++k) {
+                const int j = slist[wave][k];
                 float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                 bool contrib = false;
                 if (!done) {
@@ -173,12 +196,12 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                         }
                     }
                 }
-                float red = 0.0f;
-                if (__ballot(contrib) != 0ull) red = wave_reduce8(x, lane);
-                if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
+                if (__ballot(contrib) != 0ull) {
+                    const float red = wave_reduce8(x, lane);
+                    if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
+                }
+                if (__ballot(!done) == 0ull) break;
             }
-        } else {
-            for (int e = lane; e < cnt * 8; e += 64) (&sp[wave][0][0])[e] = 0.0f;
         }
         __syncthreads();
         if (threadIdx.x < 2 * cnt) {
@@ -192,7 +215,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 acc.z += q.z;
                 acc.w += q.w;
             }
-            partials[2 * (int64_t)s_emit[j] + h] = acc;
+            partials[2 * (int64_t)s_slot[j] + h] = acc;
         }
     }
     if (threadIdx.x == 0) {

@@ -1,0 +1,124 @@
+"""Parity at the full sizes of the five workloads, on samples the oracle computes
+one by one: every pixel of a set of sampled tiles (colour <= 1e-5, counts and
+final transmittance bit-exact), the complete tile lists (bit-exact, checked on
+the sampled tiles against per-tile brute-force scans), and the tokens of sampled
+Gaussians (<= 1e-3 relative L2; the oracle renders every tile their rectangles
+touch, in every view).  The GPU runs the same launch configuration as bench.py.
+
+The observation here is a synthetic image (0.5 plus the workload's pixel noise
+scaled by 5) rather than a render of the perturbed scene, so that the oracle
+never has to render a whole full-size frame; the residual's values do not
+change which code paths run.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import scenes
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+TOKEN_RTOL = 1e-3
+COLOR_ATOL = 1e-5
+N_TILES = 40
+N_GAUSS = 24
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+_CACHE = {}
+
+
+def _run(config):
+    if config in _CACHE:
+        return _CACHE[config]
+    _need_gpu()
+    from gaussian_splatting_rasterizer_amd import binding
+    sc = scenes.make_scene(config)
+    obs = (0.5 + 5.0 * sc.pixel_noise).astype(np.float32)
+    r = binding.rasterizer_for_scene(sc)
+    r.project_and_bin()
+    ids = r.export(binding.GS_EXPORT_SORTED_IDS).cpu().numpy()[: r.n_pairs]
+    ranges = r.export(binding.GS_EXPORT_RANGES).cpu().numpy()
+    color, T, n = r.render()
+    tok = r.score_replay(torch.from_numpy(obs).cuda())
+    torch.cuda.synchronize()
+    gpu = dict(ids=ids, ranges=ranges, n_pairs=r.n_pairs, color=color.cpu().numpy(), T=T.cpu().numpy(),
+               n=n.cpu().numpy(), tokens=tok.cpu().numpy())
+    r.close()
+    del r
+    torch.cuda.empty_cache()
+
+    o = oracle.OracleScene(sc)
+    o.build_lists()
+    rng = np.random.default_rng(100 + config)
+    tiles = np.sort(rng.choice(o.V * o.T, size=min(N_TILES, o.V * o.T), replace=False)).astype(np.int64)
+    # Gaussians with some support in the GPU result (log Q above the floor), plus a few random ones
+    logq = gpu["tokens"][:, 4 + 3 * sc.d]
+    floor = np.log((sc.n_views + 2) * 1e-6)
+    supported = np.nonzero(logq > floor)[0]
+    pick = np.concatenate([rng.choice(supported, size=min(N_GAUSS - 4, supported.size), replace=False),
+                           rng.choice(sc.n, size=4, replace=False)])
+    pick = np.unique(pick).astype(np.int32)
+    o.select(pick)
+    render_tiles = np.union1d(tiles, o.tiles_of(pick))
+    c_ref, T_ref, n_ref, _ = o.render(tiles=render_tiles, obs=obs)
+    tok_ref = o.tokens()
+    starts, _ = o.lists()
+    ref = dict(o=o, tiles=tiles, pick=pick, color=c_ref, T=T_ref, n=n_ref, tokens=tok_ref, starts=starts)
+    _CACHE[config] = (sc, obs, ref, gpu)
+    return _CACHE[config]
+
+
+def _tile_pixels(o, tiles):
+    sel = np.zeros((o.V, o.H, o.W), dtype=bool)
+    for tile in tiles:
+        v, t = divmod(int(tile), o.T)
+        ty, tx = divmod(t, o.TX)
+        sel[v, ty * 16:(ty + 1) * 16, tx * 16:(tx + 1) * 16] = True
+    return sel
+
+
+CONFIGS = [1, 2, 3, 4, 5]
+
+
+@pytest.mark.parametrize("config", CONFIGS)
+def test_fullsize_lists(config):
+    sc, obs, ref, gpu = _run(config)
+    o = ref["o"]
+    starts = ref["starts"]
+    assert gpu["n_pairs"] == starts[-1]
+    rg = gpu["ranges"].astype(np.int64)
+    counts = np.diff(starts)
+    nonempty = counts > 0
+    assert np.array_equal(rg[nonempty, 0], starts[:-1][nonempty])
+    assert np.array_equal(rg[nonempty, 1], starts[1:][nonempty])
+    for tile in ref["tiles"]:
+        got = gpu["ids"][starts[tile]:starts[tile + 1]]
+        assert np.array_equal(got, o.tile_list_scan(int(tile))), tile
+
+
+@pytest.mark.parametrize("config", CONFIGS)
+def test_fullsize_render(config):
+    sc, obs, ref, gpu = _run(config)
+    sel = _tile_pixels(ref["o"], ref["tiles"])
+    assert np.array_equal(gpu["n"][sel], ref["n"][sel])
+    assert np.array_equal(gpu["T"][sel].view(np.uint32), ref["T"][sel].view(np.uint32))
+    err = np.abs(gpu["color"][sel] - ref["color"][sel]).max()
+    print(f"config {config}: max colour error {err:.3e} over {sel.sum()} pixels")
+    assert err <= COLOR_ATOL, err
+
+
+@pytest.mark.parametrize("config", CONFIGS)
+def test_fullsize_tokens(config):
+    sc, obs, ref, gpu = _run(config)
+    z = gpu["tokens"][ref["pick"]].astype(np.float64)
+    zr = ref["tokens"]
+    rel = np.linalg.norm(z - zr, axis=1) / np.maximum(np.linalg.norm(zr, axis=1), 1e-6)
+    print(f"config {config}: max token rel err {rel.max():.3e} over {len(rel)} Gaussians")
+    assert np.all(np.isfinite(z))
+    assert rel.max() <= TOKEN_RTOL, (rel.max(), ref["pick"][rel.argmax()])

@@ -64,6 +64,9 @@ def _small_scenes():
         "c5_small": lambda: scenes.c5_multiview_layers(n_views=3, W=100, H=56, n=12000),
         "tiny_bg_deg1": lambda: scenes.tiny_scene(seed=5, n=30, n_views=3, W=33, H=17, sh_degree=1,
                                                   background=(0.3, 0.6, 0.1)),
+        # very anisotropic Gaussians (log-scales N(-3, 1.6)): needle-like footprints across many tiles
+        "elongated": lambda: scenes.tiny_scene(seed=8, n=400, n_views=2, W=96, H=80, sh_degree=3,
+                                               log_scale=(-3.0, 1.6), spread=0.6),
     }
 
 
@@ -121,13 +124,22 @@ def test_tile_lists_bit_exact(name):
     assert np.all(rg[~nonempty, 0] == rg[~nonempty, 1])
 
 
+# The needle-like stress scene has conics with condition numbers up to ~7e4; the
+# float32 quadratic form of the exponent (like the float32 conic entries
+# themselves) then carries a relative error of order 2^-24 * cond, so its colour
+# is held to 1e-3 instead of 1e-5.  Its decisions (counts, transmittance, lists)
+# remain bit-exact.  Every workload configuration is held to 1e-5.
+COLOR_ATOL_OVERRIDE = {"elongated": 1e-3}
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_render_parity(name):
     sc, obs, ref, gpu = _case(name)
     assert np.array_equal(gpu["n"], ref["n"]), np.argwhere(gpu["n"] != ref["n"])[:5]
     assert np.array_equal(gpu["T"].view(np.uint32), ref["T"].view(np.uint32))
     err = np.abs(gpu["color"] - ref["color"]).max()
-    assert err <= COLOR_ATOL, err
+    print(name, "max colour error", err)
+    assert err <= COLOR_ATOL_OVERRIDE.get(name, COLOR_ATOL), err
 
 
 def token_errors(z, zr, d):
@@ -147,10 +159,33 @@ def token_errors(z, zr, d):
 @pytest.mark.parametrize("name", SMALL)
 def test_token_parity(name):
     sc, obs, ref, gpu = _case(name)
-    rel, per_block = token_errors(gpu["tokens"].astype(np.float64), ref["tokens"], sc.d)
+    z = gpu["tokens"].astype(np.float64)
+    zr = ref["tokens"]
+    rel, per_block = token_errors(z, zr, sc.d)
     print(name, "max rel", rel.max(), "per block", per_block)
     assert np.all(np.isfinite(gpu["tokens"]))
     assert rel.max() <= TOKEN_RTOL, (rel.max(), int(rel.argmax()), per_block)
+    # Per block, each score is a sum of signed per-pixel terms, so the block is
+    # held to 1e-3 of its value, plus 1e-4 of the sum of the terms' magnitudes
+    # (float32 sums may cancel; the oracle accumulates both), plus what the
+    # colour tolerance (1e-5 on C_hat, hence on r) moves it: |B| <= 1 and
+    # |c - C+| <= 2 give 1e-5 W / Q for the SH block and 2e-5 (1 - o) W / Q for
+    # the opacity block.
+    acc = ref["oracle"].acc()                       # [G, V, 8 + 6d]
+    d = sc.d
+    W = acc[:, :, 0].sum(axis=1)
+    Q = 1e-6 + np.sum(1e-6 + acc[:, :, 0], axis=1)
+    o = sc.opacities.astype(np.float64)
+    abs_alpha = acc[:, :, 4].sum(axis=1) / Q
+    catol = COLOR_ATOL_OVERRIDE.get(name, COLOR_ATOL)
+    bound_a = 1e-3 * np.abs(zr[:, 3]) + 1e-4 * abs_alpha + 2 * catol * (1 - o) * W / Q + 1e-9
+    ratio_a = np.abs(z[:, 3] - zr[:, 3]) / bound_a
+    assert ratio_a.max() <= 1.0, (ratio_a.max(), int(ratio_a.argmax()))
+    abs_sh = acc[:, :, 8 + 3 * d: 8 + 6 * d].sum(axis=1) / Q[:, None]
+    bound = 1e-3 * np.abs(zr[:, 4:4 + 3 * d]) + 1e-4 * abs_sh + (catol * W / Q)[:, None] + 1e-9
+    ratio = np.abs(z[:, 4:4 + 3 * d] - zr[:, 4:4 + 3 * d]) / bound
+    g, k = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, (ratio.max(), int(g), int(k), z[g, 4 + k], zr[g, 4 + k], abs_sh[g, k])
 
 
 def test_exp2_bit_identical():
