@@ -17,9 +17,10 @@
 // These suffice for every score block: with M set, alpha = o G, so
 // T o grad_mu G rho = conic (p - mu) w rho and T alpha (1 - o) rho = (1 - o) w rho;
 // the colour clamp mask and the SH basis are constant over a (Gaussian, view).
-// The 64 lanes of a wave are reduced with a reduce-scatter butterfly (four
-// exchange steps leave lane l holding component l >> 3 summed over 64 lanes,
-// then three in-group steps), only when some lane contributed; the four waves
+// The 64 lanes of a wave are reduced with a reduce-scatter built on the
+// gfx950 lane permutations (permlane32/16 swaps, DPP row rotations) that leaves
+// lane l holding component l >> 3 summed over the wave, only when some lane
+// contributed; the four waves
 // meet in LDS and one 32-byte partial per (tile, Gaussian) pair is stored with
 // plain stores -- no atomics, so the result is deterministic.  The partial's
 // slot is the record's slot base (a scan of tile counts in record order) plus
@@ -45,28 +46,31 @@ namespace gsr {
 constexpr int kReplayBatch = 128;
 
 // Reduce eight values over the 64 lanes; returns in every lane the total of
-// component (lane >> 3) & 7.
+// component (lane >> 3) & 7.  Reduce-scatter with gfx950 lane permutations:
+//   permlane32_swap pairs component i (kept in lanes 0-31) with i + 4 (lanes 32-63),
+//   permlane16_swap pairs rows, a row_ror:8 exchange splits each row in halves,
+//   then quad_perm / row_half_mirror adds finish the sum inside 8-lane groups.
+template <int CTRL>
+__device__ __forceinline__ float fadd_dpp(float keep, float send) {
+    return keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ float wave_reduce8(const float (&x)[8], int lane) {
-    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
     float a[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float send = b5 ? x[i] : x[i + 4];
-        const float keep = b5 ? x[i + 4] : x[i];
-        a[i] = keep + __shfl_xor(send, 32, 64);
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + 4]), false, false);
+        a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
-    float b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float send = b4 ? a[i] : a[i + 2];
-        const float keep = b4 ? a[i + 2] : a[i];
-        b[i] = keep + __shfl_xor(send, 16, 64);
-    }
-    const float send = b3 ? b[0] : b[1];
-    float c = (b3 ? b[1] : b[0]) + __shfl_xor(send, 8, 64);
-    c += __shfl_xor(c, 4, 64);
-    c += __shfl_xor(c, 2, 64);
-    c += __shfl_xor(c, 1, 64);
+    const auto s0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[0]), __float_as_uint(a[2]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[1]), __float_as_uint(a[3]), false, false);
+    const float b0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);  // rows hold components 0, 2, 4, 6
+    const float b1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);  // rows hold components 1, 3, 5, 7
+    const bool hi8 = lane & 8;
+    float c = fadd_dpp<0x128>(hi8 ? b1 : b0, hi8 ? b0 : b1);  // row_ror:8
+    c = fadd_dpp<0xB1>(c, c);                                  // quad_perm [1,0,3,2]
+    c = fadd_dpp<0x4E>(c, c);                                  // quad_perm [2,3,0,1]
+    c = fadd_dpp<0x141>(c, c);                                 // row_half_mirror
     return c;
 }
 
