@@ -2,8 +2,8 @@
 //
 // Host code only: argument validation, workspace carve-up, state checks and
 // kernel launches on the caller's stream.  No device memory is allocated or
-// freed here; the only host/device synchronisation is the read of the pair
-// count in gs_bin_sort.
+// freed here (a context holds one pinned host word for the pair count); the
+// only host/device synchronisation is the read of that count in gs_bin_sort.
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -115,6 +115,9 @@ struct gs_context {
     uint64_t n_pairs;
     const uint32_t* sorted_g;     // Gaussian of each pair in (tile, depth, id) order (set by gs_bin_sort)
     StageTimer timer;
+    uint32_t epoch;               // last radix pass epoch; 0 = look-back words not cleared yet
+    uint64_t* host_count;         // pinned host word receiving the pair count (allocated on first use)
+    hipEvent_t count_ev;
 };
 
 namespace gsr {
@@ -132,10 +135,8 @@ Sizes make_sizes(const gs_dims& d) {
     s.VG = (int64_t)s.V * s.G;
     s.max_pairs = d.max_pairs;
     const int64_t nmax = s.VG > (int64_t)s.max_pairs ? s.VG : (int64_t)s.max_pairs;
-    const int64_t radix_blocks = (nmax + kBlockItems - 1) / kBlockItems;
-    s.hist_cap = 256 * radix_blocks;  // up to 8-bit digits
-    int64_t scan_n = s.hist_cap > s.VG ? s.hist_cap : s.VG;
-    s.scan_blocks_cap = (scan_n + kBlockItems - 1) / kBlockItems + 1;
+    s.sort_tiles_cap = (nmax + kSortTile - 1) / kSortTile;
+    s.scan_blocks_cap = (s.VG + kBlockItems - 1) / kBlockItems + 1;
     return s;
 }
 
@@ -163,7 +164,9 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->offsets = (uint32_t*)take(4 * VG);
     ws->scan_blocks = (uint64_t*)take(8 * (size_t)s.scan_blocks_cap);
     ws->scan_total = (uint64_t*)take(8 * 4);
-    ws->hist = (uint32_t*)take(4 * (size_t)s.hist_cap);
+    ws->lookback = (uint64_t*)take(8 * 256 * (size_t)s.sort_tiles_cap);
+    ws->sort_ctl = (uint32_t*)take(4 * (size_t)kSortCtlWords);
+    ws->sort_part = (uint32_t*)take(4 * (size_t)kSortPartBlocks * kSortMaxPasses * 256);
     ws->pkey_emit = (uint32_t*)take(4 * P);
     ws->pkey_b = (uint32_t*)take(4 * P);
     ws->pkey_c = (uint32_t*)take(4 * P);
@@ -246,7 +249,11 @@ gs_status gs_context_create(const gs_dims* dims, void* workspace, size_t workspa
 }
 
 gs_status gs_context_destroy(gs_context* ctx) {
-    if (ctx) ctx->timer.destroy();
+    if (ctx) {
+        ctx->timer.destroy();
+        if (ctx->count_ev) (void)hipEventDestroy(ctx->count_ev);
+        if (ctx->host_count) (void)hipHostFree(ctx->host_count);
+    }
     delete ctx;
     return GS_OK;
 }
@@ -298,16 +305,35 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     Workspace& ws = ctx->ws;
     hipError_t e;
     StageTimer& tm = ctx->timer;
+    // look-back words: cleared on the first sort of the context and before the epoch wraps
+    if (ctx->epoch == 0 || ctx->epoch > kEpochLimit) {
+        e = launch_fill_u32(reinterpret_cast<uint32_t*>(ws.lookback), 2 * 256 * s.sort_tiles_cap, 0u, stream);
+        if (e != hipSuccess) return hip_fail(e, "look-back clear");
+        ctx->epoch = 0;
+    }
+    if (!ctx->host_count) {
+        e = hipHostMalloc((void**)&ctx->host_count, 64, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            ctx->host_count = nullptr;
+            return hip_fail(e, "pinned count word");
+        }
+        e = hipEventCreateWithFlags(&ctx->count_ev, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            ctx->count_ev = nullptr;
+            return hip_fail(e, "count event");
+        }
+    }
+    const SortScratch sort_scratch{ws.lookback, ws.sort_ctl, ws.sort_part};
     // 0. slot bases of the replay's partials: tile counts scanned in record order
     tm.begin(stream);
     e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream);
     if (e != hipSuccess) return hip_fail(e, "slot scan");
     // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
-    //    scan rewrites next); the last pass also gathers the rectangles and tile counts
+    //    scan rewrites next); the last pass gathers the rectangles and tile counts and writes no keys
     uint32_t* rid_sorted = nullptr;
     e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b,
-                          reinterpret_cast<const uint2*>(ws.rec2), ws.rect_sorted, ws.tt_sorted, ws.hist,
-                          ws.scan_blocks, ws.scan_total + 2, stream, nullptr, &rid_sorted);
+                          reinterpret_cast<const uint2*>(ws.rec2), ws.rect_sorted, ws.tt_sorted, sort_scratch,
+                          &ctx->epoch, stream, nullptr, &rid_sorted);
     if (e != hipSuccess) return hip_fail(e, "depth sort");
     tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
@@ -315,11 +341,17 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream);
     if (e != hipSuccess) return hip_fail(e, "scan");
     tm.end(GS_STAGE_SCAN, stream);
-    uint64_t total = 0;
-    e = hipMemcpyAsync(&total, ws.scan_total, sizeof total, hipMemcpyDeviceToHost, stream);
+    // the pair count: copied into pinned host memory, waited for by polling the event
+    e = hipMemcpyAsync(ctx->host_count, ws.scan_total, sizeof(uint64_t), hipMemcpyDeviceToHost, stream);
     if (e != hipSuccess) return hip_fail(e, "pair count copy");
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e, "pair count sync");
+    e = hipEventRecord(ctx->count_ev, stream);
+    if (e != hipSuccess) return hip_fail(e, "pair count event");
+    for (;;) {
+        e = hipEventQuery(ctx->count_ev);
+        if (e == hipSuccess) break;
+        if (e != hipErrorNotReady) return hip_fail(e, "pair count wait");
+    }
+    const uint64_t total = *(volatile uint64_t*)ctx->host_count;
     if (n_pairs_out) *n_pairs_out = total;
     ctx->n_pairs = total;
     if (total > s.max_pairs) {
@@ -337,8 +369,8 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     uint32_t* sorted_g = nullptr;
     tm.begin(stream);
     e = launch_radix_sort(ws.pkey_emit, ws.pair_g, (int64_t)total, bits_for((uint64_t)tiles), ws.pkey_b, ws.pkey_c,
-                          ws.pval_a, ws.pval_b, nullptr, nullptr, nullptr, ws.hist, ws.scan_blocks, ws.scan_total + 2,
-                          stream, &sorted_keys, &sorted_g);
+                          ws.pval_a, ws.pval_b, nullptr, nullptr, nullptr, sort_scratch, &ctx->epoch, stream,
+                          &sorted_keys, &sorted_g);
     if (e != hipSuccess) return hip_fail(e, "tile sort");
     tm.end(GS_STAGE_TILE_SORT, stream);
     tm.begin(stream);

@@ -39,8 +39,11 @@ constexpr int kRadixThreads = 512;
 constexpr int kRadixWaves = kRadixThreads / 64;
 constexpr int kRadixItems = 16;
 constexpr int kRadixTile = kRadixThreads * kRadixItems;  // 8192
+static_assert(kRadixTile == kSortTile, "radix tile size");
 constexpr int kMaxDigitBits = 8;
 constexpr int kMaxBins = 1 << kMaxDigitBits;
+constexpr int kMaxPasses = kSortMaxPasses;
+constexpr int kCtlTotals = kSortCtlTotals;
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -175,58 +178,130 @@ __device__ __forceinline__ uint64_t match_peers(uint32_t dgt, int bits, bool val
     return peers;
 }
 
-// Per-block digit counts, written digit-major: hist[digit * nb + block].
-__global__ __launch_bounds__(kRadixThreads) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n, int shift,
-                                                              int bits, uint32_t* __restrict__ hist, int64_t nb) {
-    __shared__ uint32_t h[kRadixWaves][kMaxBins];
-    const int nbins = 1 << bits;
-    const uint32_t mask = (uint32_t)nbins - 1u;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < kRadixWaves * kMaxBins; i += kRadixThreads) (&h[0][0])[i] = 0u;
-    __syncthreads();
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int64_t base = (int64_t)blockIdx.x * kRadixTile + (int64_t)wave * (kRadixTile / kRadixWaves);
-    uint32_t dg[kRadixItems];
+// Digit counts of every pass in one read of the keys: per-block LDS
+// histograms, written per block to part[block][pass * 256 + digit].  Each
+// thread reads two 4-key vectors per step and keeps, per pass, a run of equal
+// digits in registers that it adds to LDS only when the digit changes, so
+// skewed digits (the exponent byte of depths) do not pile atomics on one bin.
+constexpr int kHistThreads = 1024;
+constexpr int kHistMaxBlocks = kSortPartBlocks;
+
+template <int PASSES>
+__device__ __forceinline__ void hist_count(uint32_t key, int dbits, int bits, uint32_t (&cur)[PASSES],
+                                           uint32_t (&run)[PASSES], uint32_t* h) {
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
-        const int64_t k = base + i * 64 + lane;
-        dg[i] = k < n ? (keys[k] >> shift) & mask : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
-        const bool valid = base + i * 64 + lane < n;
-        const uint64_t peers = match_peers(dg[i], bits, valid);
-        if (valid && (peers & lt_mask) == 0ull) h[wave][dg[i]] += (uint32_t)__popcll(peers);
-    }
-    __syncthreads();
-    for (int dgt = threadIdx.x; dgt < nbins; dgt += kRadixThreads) {
-        uint32_t t = 0;
-#pragma unroll
-        for (int w = 0; w < kRadixWaves; ++w) t += h[w][dgt];
-        hist[(int64_t)dgt * nb + blockIdx.x] = t;
+    for (int p = 0; p < PASSES; ++p) {
+        const int shift = p * dbits;
+        const int pb = shift + dbits <= bits ? dbits : bits - shift;
+        const uint32_t d = (key >> shift) & ((1u << pb) - 1u);
+        if (d != cur[p]) {
+            if (run[p]) atomicAdd(&h[p * kMaxBins + cur[p]], run[p]);
+            cur[p] = d;
+            run[p] = 1u;
+        } else {
+            ++run[p];
+        }
     }
 }
 
-// Stable scatter of one radix pass (see the file header).  Optional final-pass
-// extras: rect_src != null gathers rect_out[pos] = rect_src[2 * val + 1] (the
-// packed tile rectangle of record `val`) and tt_out[pos] = its tile count.
-__global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
+template <int PASSES>
+__global__ __launch_bounds__(kHistThreads) void k_digit_hist(const uint32_t* __restrict__ keys, int64_t n, int dbits,
+                                                             int bits, uint32_t* __restrict__ part) {
+    __shared__ uint32_t h[kMaxPasses * kMaxBins];
+    for (int i = threadIdx.x; i < kMaxPasses * kMaxBins; i += kHistThreads) h[i] = 0u;
+    __syncthreads();
+    uint32_t cur[PASSES], run[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        cur[p] = 0u;
+        run[p] = 0u;
+    }
+    const int64_t n4 = n >> 2;
+    const uint4* k4 = reinterpret_cast<const uint4*>(keys);
+    const int64_t stride = (int64_t)gridDim.x * kHistThreads;
+    for (int64_t q = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; q < n4; q += 2 * stride) {
+        const bool second = q + stride < n4;
+        const uint4 x = k4[q];
+        const uint4 y = second ? k4[q + stride] : make_uint4(0u, 0u, 0u, 0u);
+        hist_count<PASSES>(x.x, dbits, bits, cur, run, h);
+        hist_count<PASSES>(x.y, dbits, bits, cur, run, h);
+        hist_count<PASSES>(x.z, dbits, bits, cur, run, h);
+        hist_count<PASSES>(x.w, dbits, bits, cur, run, h);
+        if (second) {
+            hist_count<PASSES>(y.x, dbits, bits, cur, run, h);
+            hist_count<PASSES>(y.y, dbits, bits, cur, run, h);
+            hist_count<PASSES>(y.z, dbits, bits, cur, run, h);
+            hist_count<PASSES>(y.w, dbits, bits, cur, run, h);
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (n & 3)) hist_count<PASSES>(keys[4 * n4 + threadIdx.x], dbits, bits, cur, run, h);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+        if (run[p]) atomicAdd(&h[p * kMaxBins + cur[p]], run[p]);
+    __syncthreads();
+    for (int i = threadIdx.x; i < PASSES * kMaxBins; i += kHistThreads)
+        part[(int64_t)blockIdx.x * (kMaxPasses * kMaxBins) + i] = h[i];
+}
+
+// Totals of the per-block histograms: block b sums bins [64 b, 64 b + 64) of
+// the pass-major table, its 16 waves over 16 histogram blocks each with every
+// load in flight at once; block 0 also zeroes the passes' tile tickets.
+__global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restrict__ part, int nblocks,
+                                                       uint32_t* __restrict__ ctl) {
+    static_assert(kHistMaxBlocks <= 16 * 16, "one load per wave and row");
+    __shared__ uint32_t s[16][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int bin = blockIdx.x * 64 + lane;
+    uint32_t x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int r = wave * 16 + u;
+        x[u] = r < nblocks ? part[(int64_t)r * (kMaxPasses * kMaxBins) + bin] : 0u;
+    }
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc += x[u];
+    s[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) t += s[w][lane];
+        ctl[kCtlTotals + bin] = t;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < kMaxPasses) ctl[threadIdx.x] = 0u;
+}
+
+// One radix pass (see the file header).  Blocks take their tile of keys in
+// the order they start (a ticket counter), publish their per-digit counts and
+// resolve their global offsets by looking back over earlier tiles' published
+// counts: a word per (tile, digit) holding the count and a tag -- the pass's
+// epoch and whether the count is the inclusive prefix of all tiles up to this
+// one or only this tile's own.  A tile only waits on tiles that started before
+// it, and every tile publishes its own counts before it waits, so the chain
+// always resolves.  Optional final-pass extras: rect_src != null gathers
+// rect_out[pos] = rect_src[2 * val + 1] (the packed tile rectangle of record
+// `val`) and tt_out[pos] = its tile count; keys_out may be null.
+__global__ __launch_bounds__(kRadixThreads) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift, int bits,
-    const uint32_t* __restrict__ hist_scan, int64_t nb, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, const uint2* __restrict__ rect_src, uint2* __restrict__ rect_out,
-    uint32_t* __restrict__ tt_out) {
+    uint32_t* __restrict__ ticket, const uint32_t* __restrict__ digit_tot, uint64_t* __restrict__ lookback,
+    uint32_t epoch, uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
+    const uint2* __restrict__ rect_src, uint2* __restrict__ rect_out, uint32_t* __restrict__ tt_out) {
     __shared__ uint32_t cnt[kRadixWaves][kMaxBins];  // per-wave counts, then per-wave block-local bases
     __shared__ uint32_t gdelta[kMaxBins];            // global position - block-local position, per digit
-    __shared__ uint32_t scan_lds[kRadixThreads / 64];
+    __shared__ uint64_t scan_lds[kRadixThreads / 64];
     __shared__ uint32_t skey[kRadixTile];
     __shared__ uint32_t sval[kRadixTile];
+    __shared__ uint32_t s_tile;
     const int nbins = 1 << bits;
     const uint32_t mask = (uint32_t)nbins - 1u;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < kRadixWaves * kMaxBins; i += kRadixThreads) (&cnt[0][0])[i] = 0u;
+    if (threadIdx.x == 0) s_tile = atomicAdd(ticket, 1u);
     __syncthreads();
+    const int64_t tile = s_tile;
 
-    const int64_t bbase = (int64_t)blockIdx.x * kRadixTile;
+    const int64_t bbase = tile * kRadixTile;
     const int64_t base = bbase + (int64_t)wave * (kRadixTile / kRadixWaves);
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t key[kRadixItems], val[kRadixItems], rank[kRadixItems];
@@ -249,17 +324,21 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     }
     __syncthreads();
     {
-        // block-local digit offsets (kRadixThreads >= kMaxBins: one digit per thread)
+        // block-local digit offsets and the pass's global digit offsets in one
+        // 64-bit scan: (digit total << 32) + block count, one digit per thread
         const int dgt = threadIdx.x;
-        uint32_t tot = 0;
+        uint32_t tot = 0, gtot = 0;
         if (dgt < nbins) {
 #pragma unroll
             for (int w = 0; w < kRadixWaves; ++w) tot += cnt[w][dgt];
+            gtot = digit_tot[dgt];
         }
-        uint32_t block_total;
-        const uint32_t loff = block_exclusive_scan<uint32_t, kRadixThreads>(tot, &block_total, scan_lds);
+        uint64_t both_total;
+        const uint64_t both = block_exclusive_scan<uint64_t, kRadixThreads>(((uint64_t)gtot << 32) | tot, &both_total,
+                                                                            scan_lds);
+        const uint32_t loff = (uint32_t)both;
+        const uint32_t digit_off = (uint32_t)(both >> 32);
         if (dgt < nbins) {
-            gdelta[dgt] = hist_scan[(int64_t)dgt * nb + blockIdx.x] - loff;
             uint32_t s = loff;
 #pragma unroll
             for (int w = 0; w < kRadixWaves; ++w) {
@@ -267,6 +346,30 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
                 cnt[w][dgt] = s;
                 s += c;
             }
+            uint64_t* mine = lookback + tile * kMaxBins + dgt;
+            const uint32_t tag = epoch << 1;
+            uint32_t excl = 0;
+            if (tile == 0) {
+                __hip_atomic_store(mine, ((uint64_t)(tag | 1u) << 32) | tot, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                __hip_atomic_store(mine, ((uint64_t)tag << 32) | tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t* prev = mine - kMaxBins;
+                for (;;) {
+                    const uint64_t w = __hip_atomic_load(prev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const uint32_t h = (uint32_t)(w >> 32);
+                    if ((h & ~1u) != tag) {
+                        __builtin_amdgcn_s_sleep(1);
+                        continue;
+                    }
+                    excl += (uint32_t)w;
+                    if (h & 1u) break;
+                    prev -= kMaxBins;
+                }
+                __hip_atomic_store(mine, ((uint64_t)(tag | 1u) << 32) | (excl + tot), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            gdelta[dgt] = digit_off + excl - loff;
         }
     }
     __syncthreads();
@@ -279,28 +382,49 @@ __global__ __launch_bounds__(kRadixThreads) void k_radix_scatter(
     }
     __syncthreads();
     const int64_t nblk = n - bbase < kRadixTile ? n - bbase : kRadixTile;
+    if (rect_src) {
+        // final depth pass: all of the thread's gathers are in flight together
+        uint32_t pos[kRadixItems], v[kRadixItems];
+        uint2 r[kRadixItems];
+#pragma unroll
+        for (int i = 0; i < kRadixItems; ++i) {
+            const int lp = i * kRadixThreads + threadIdx.x;
+            const bool ok = lp < nblk;
+            const uint32_t k = ok ? skey[lp] : 0u;
+            v[i] = ok ? sval[lp] : 0u;
+            pos[i] = gdelta[(k >> shift) & mask] + (uint32_t)lp;
+            if (ok && keys_out) keys_out[pos[i]] = k;
+        }
+#pragma unroll
+        for (int i = 0; i < kRadixItems; ++i) {
+            const int lp = i * kRadixThreads + threadIdx.x;
+            r[i] = lp < nblk ? rect_src[2 * (int64_t)v[i] + 1] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < kRadixItems; ++i) {
+            const int lp = i * kRadixThreads + threadIdx.x;
+            if (lp >= nblk) continue;
+            vals_out[pos[i]] = v[i];
+            rect_out[pos[i]] = r[i];
+            tt_out[pos[i]] = ((r[i].y & 0xffffu) - (r[i].x & 0xffffu)) * ((r[i].y >> 16) - (r[i].x >> 16));
+        }
+        return;
+    }
 #pragma unroll 4
     for (int i = 0; i < kRadixItems; ++i) {
         const int lp = i * kRadixThreads + threadIdx.x;
         if (lp >= nblk) break;
         const uint32_t k = skey[lp];
-        const uint32_t v = sval[lp];
         const uint32_t pos = gdelta[(k >> shift) & mask] + (uint32_t)lp;
         if (keys_out) keys_out[pos] = k;
-        vals_out[pos] = v;
-        if (rect_src) {
-            const uint2 r = rect_src[2 * (int64_t)v + 1];
-            rect_out[pos] = r;
-            tt_out[pos] = ((r.y & 0xffffu) - (r.x & 0xffffu)) * ((r.y >> 16) - (r.x >> 16));
-        }
+        vals_out[pos] = sval[lp];
     }
 }
 
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const uint2* rect_src, uint2* rect_out, uint32_t* tt_out, uint32_t* hist,
-                             uint64_t* block_scratch, uint64_t* total, hipStream_t st, uint32_t** keys_out,
-                             uint32_t** vals_out) {
+                             const uint2* rect_src, uint2* rect_out, uint32_t* tt_out, const SortScratch& sc,
+                             uint32_t* epoch, hipStream_t st, uint32_t** keys_out, uint32_t** vals_out) {
     if (bits < 1) bits = 1;
     const int passes = (bits + kMaxDigitBits - 1) / kMaxDigitBits;
     const int dbits = (bits + passes - 1) / passes;
@@ -310,20 +434,28 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
     if (keys_out) *keys_out = kb[(passes - 1) & 1];
     if (vals_out) *vals_out = vb[(passes - 1) & 1];
     if (n <= 0) return hipSuccess;
+    int64_t hb = (n + 8 * kHistThreads - 1) / (8 * kHistThreads);
+    if (hb > kHistMaxBlocks) hb = kHistMaxBlocks;
+    switch (passes) {
+        case 1: hipLaunchKernelGGL(k_digit_hist<1>, dim3((unsigned)hb), dim3(kHistThreads), 0, st, keys_in, n, dbits, bits, sc.part); break;
+        case 2: hipLaunchKernelGGL(k_digit_hist<2>, dim3((unsigned)hb), dim3(kHistThreads), 0, st, keys_in, n, dbits, bits, sc.part); break;
+        case 3: hipLaunchKernelGGL(k_digit_hist<3>, dim3((unsigned)hb), dim3(kHistThreads), 0, st, keys_in, n, dbits, bits, sc.part); break;
+        default: hipLaunchKernelGGL(k_digit_hist<4>, dim3((unsigned)hb), dim3(kHistThreads), 0, st, keys_in, n, dbits, bits, sc.part); break;
+    }
+    hipLaunchKernelGGL(k_digit_totals, dim3((unsigned)(passes * kMaxBins / 64)), dim3(1024), 0, st, sc.part, (int)hb,
+                       sc.ctl);
     const uint32_t* ksrc = keys_in;
     const uint32_t* vsrc = vals_in;
     for (int p = 0; p < passes; ++p) {
         const int shift = p * dbits;
         const int pb = (shift + dbits <= bits) ? dbits : bits - shift;
         const bool last = p == passes - 1;
-        uint32_t* kdst = kb[p & 1];
+        uint32_t* kdst = (last && !keys_out) ? nullptr : kb[p & 1];
         uint32_t* vdst = vb[p & 1];
-        hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, n, shift, pb, hist, nb);
-        hipError_t e = launch_scan_u32(hist, (int64_t)(1 << pb) * nb, hist, block_scratch, total, st);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, vsrc, n, shift, pb,
-                           hist, nb, kdst, vdst, last ? rect_src : nullptr, last ? rect_out : nullptr,
-                           last ? tt_out : nullptr);
+        const uint32_t ep = next_epoch(epoch);
+        hipLaunchKernelGGL(k_onesweep, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, vsrc, n, shift, pb,
+                           sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins, sc.lookback, ep, kdst, vdst,
+                           last ? rect_src : nullptr, last ? rect_out : nullptr, last ? tt_out : nullptr);
         ksrc = kdst;
         vsrc = vdst;
     }

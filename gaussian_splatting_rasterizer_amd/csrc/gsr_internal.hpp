@@ -29,7 +29,9 @@ struct Workspace {
     // scan / histogram scratch
     uint64_t* scan_blocks; // per-block sums (u64), then exclusive offsets
     uint64_t* scan_total;  // [0] pair count, [1] slot total, [2] scratch of the radix scans
-    uint32_t* hist;        // radix histograms, digit-major
+    uint64_t* lookback;    // radix look-back words, [radix tile][256 digits]
+    uint32_t* sort_ctl;    // radix control: per-pass tile tickets, then per-pass digit offsets
+    uint32_t* sort_part;   // per-block digit histograms of the radix sorts
     // (tile, Gaussian) pairs
     uint32_t* pkey_emit;   // global tile id of each pair, depth order
     uint32_t* pkey_b;
@@ -53,8 +55,25 @@ struct Sizes {
     int64_t VG;
     uint64_t max_pairs;
     int64_t scan_blocks_cap;
-    int64_t hist_cap;
+    int64_t sort_tiles_cap;   // radix tiles of the larger of the two sorts
 };
+
+// Radix sort layout shared by the launcher and the workspace carve-up.
+constexpr int kSortTile = 8192;       // keys per radix tile (512 threads x 16)
+constexpr int kSortMaxPasses = 4;     // 8-bit digits of 32-bit keys
+constexpr int kSortCtlTotals = 8;     // sort_ctl: [0, 8) tickets, then kSortMaxPasses x 256 digit totals
+constexpr int kSortCtlWords = kSortCtlTotals + kSortMaxPasses * 256;
+constexpr int kSortPartBlocks = 256;  // blocks of the digit histogram
+struct SortScratch {
+    uint64_t* lookback;
+    uint32_t* ctl;
+    uint32_t* part;
+};
+// Look-back words are tagged with a per-pass epoch (31 bits, never 0), so they
+// need no clearing between passes; the owner clears them once before the
+// first pass and again before the epoch would wrap.
+inline uint32_t next_epoch(uint32_t* e) { return ++*e; }
+constexpr uint32_t kEpochLimit = 0x7fff0000u;
 
 size_t carve_workspace(const Sizes& s, char* base, Workspace* ws);  // base == nullptr: size only
 Sizes make_sizes(const gs_dims& d);
@@ -72,12 +91,13 @@ hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_
 // keys_in/vals_in except that kbuf1/vbuf1 may alias keys_in/vals_in (consumed
 // by pass 0).  With rect_src != null the final pass also gathers
 // rect_out[pos] = rect_src[2 * val + 1] and tt_out[pos] = its tile count.
-// *keys_out / *vals_out receive the arrays holding the result.
+// *keys_out / *vals_out receive the arrays holding the result; with
+// keys_out == null the final pass does not write keys.  Each pass takes a new
+// epoch from *epoch.
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const uint2* rect_src, uint2* rect_out, uint32_t* tt_out, uint32_t* hist,
-                             uint64_t* block_scratch, uint64_t* total, hipStream_t st, uint32_t** keys_out,
-                             uint32_t** vals_out);
+                             const uint2* rect_src, uint2* rect_out, uint32_t* tt_out, const SortScratch& sc,
+                             uint32_t* epoch, hipStream_t st, uint32_t** keys_out, uint32_t** vals_out);
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st);
 hipError_t launch_ranges(const uint32_t* sorted_keys, int64_t n, uint2* ranges, int64_t n_tiles,
                          hipStream_t st);

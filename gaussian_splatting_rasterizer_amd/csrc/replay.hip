@@ -285,49 +285,123 @@ __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */,
 // consecutive records' slots are adjacent, so reads and writes are coalesced.
 // Tile lists are ordered by the (depth bits, Gaussian) key, so a pair was
 // reached iff its key is below the key at which its tile's replay stopped.
-__global__ __launch_bounds__(256) void k_gather_slots(int64_t VG, uint32_t G, int T, int TX,
-                                                      const float4* __restrict__ rec2,
-                                                      const uint32_t* __restrict__ depth_key,
-                                                      const uint32_t* __restrict__ slot_base,
-                                                      const uint64_t* __restrict__ tile_stop,
-                                                      const float4* __restrict__ partials,
-                                                      float4* __restrict__ gv_sums) {
-    const int64_t rid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (rid >= VG) return;
-    const float4 r2 = rec2[rid];
-    const uint32_t lo = __float_as_uint(r2.z), hi = __float_as_uint(r2.w);
+// The partial slots of a block's 256 consecutive records form one contiguous
+// range (slot_base is a scan in record order).  The block streams that range
+// through LDS in chunks: each loading thread finds its slot's record by binary
+// search over the block's slot bases, and fetches the slot's partials only if
+// the replay reached that pair (else stores zeros), so loads are coalesced and
+// unreached slots cost no HBM traffic; each thread then sums its own record's
+// slots from LDS in slot order.
+constexpr int kGatherThreads = 256;
+constexpr int kGatherChunk = 1024;  // slots per LDS chunk (32 KiB)
+constexpr int kGatherPer = kGatherChunk / kGatherThreads;
+
+__global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uint32_t G, int T, int TX,
+                                                                 const float4* __restrict__ rec2,
+                                                                 const uint32_t* __restrict__ depth_key,
+                                                                 const uint32_t* __restrict__ slot_base,
+                                                                 const uint64_t* __restrict__ tile_stop,
+                                                                 const float4* __restrict__ partials,
+                                                                 float4* __restrict__ gv_sums) {
+    __shared__ float4 buf[2 * kGatherChunk];
+    __shared__ uint32_t s_sb[kGatherThreads];    // first slot of each record
+    __shared__ uint32_t s_tile0[kGatherThreads]; // global tile id of the rectangle's first tile
+    __shared__ uint32_t s_w[kGatherThreads];     // rectangle width in tiles
+    __shared__ uint64_t s_key[kGatherThreads];   // (depth bits, Gaussian) list key
+    __shared__ uint32_t s_end;
+    const int t = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * kGatherThreads;
+    const int64_t rid = r0 + t;
+    const int last = (int)(VG - r0 < kGatherThreads ? VG - r0 : kGatherThreads) - 1;
+    uint32_t tt = 0, sb = 0;
+    if (rid < VG) {
+        const float4 r2 = rec2[rid];
+        const uint32_t lo = __float_as_uint(r2.z), hi = __float_as_uint(r2.w);
+        sb = slot_base[rid];
+        uint32_t w = 1, tile0 = 0;
+        uint64_t key = 0;
+        if (hi != 0u) {
+            const uint32_t v = (uint32_t)rid / G;
+            const uint32_t g = (uint32_t)rid - v * G;
+            key = ((uint64_t)depth_key[rid] << 32) | (uint64_t)g;
+            const uint32_t x0 = lo & 0xffffu, y0 = lo >> 16;
+            w = (hi & 0xffffu) - x0;
+            tt = w * ((hi >> 16) - y0);
+            tile0 = v * (uint32_t)T + y0 * (uint32_t)TX + x0;
+        }
+        s_sb[t] = sb;
+        s_tile0[t] = tile0;
+        s_w[t] = w;
+        s_key[t] = key;
+        if (t == last) s_end = sb + tt;
+    }
+    __syncthreads();
+    const uint32_t first = s_sb[0], end = s_end;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (hi != 0u) {
-        const uint32_t v = (uint32_t)rid / G;
-        const uint32_t g = (uint32_t)rid - v * G;
-        const uint64_t key = ((uint64_t)depth_key[rid] << 32) | (uint64_t)g;
-        const int x0 = (int)(lo & 0xffffu), y0 = (int)(lo >> 16), x1 = (int)(hi & 0xffffu), y1 = (int)(hi >> 16);
-        int64_t slot = slot_base[rid];
-        for (int ty = y0; ty < y1; ++ty) {
-            const uint64_t* stop_row = tile_stop + (int64_t)v * T + (int64_t)ty * TX;
-            for (int tx = x0; tx < x1; ++tx, ++slot) {
-                if (key >= stop_row[tx]) continue;
-                const float4 p0 = partials[2 * slot];
-                const float4 p1 = partials[2 * slot + 1];
-                a.x += p0.x;
-                a.y += p0.y;
-                a.z += p0.z;
-                a.w += p0.w;
-                b.x += p1.x;
-                b.y += p1.y;
-                b.z += p1.z;
-                b.w += p1.w;
+    for (uint32_t c0 = first; c0 < end; c0 += kGatherChunk) {
+        const uint32_t n = end - c0 < (uint32_t)kGatherChunk ? end - c0 : (uint32_t)kGatherChunk;
+        bool reach[kGatherPer];
+#pragma unroll
+        for (int k = 0; k < kGatherPer; ++k) {
+            const uint32_t i = (uint32_t)(t + k * kGatherThreads);
+            reach[k] = false;
+            if (i < n) {
+                const uint32_t s = c0 + i;
+                int lo = 0, hi = last;
+                while (lo < hi) {  // last record whose first slot is <= s: the one holding s
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_sb[mid] <= s) lo = mid;
+                    else hi = mid - 1;
+                }
+                const uint32_t j = s - s_sb[lo];
+                const uint32_t w = s_w[lo];
+                const uint32_t q = j / w;
+                reach[k] = s_key[lo] < tile_stop[s_tile0[lo] + q * (uint32_t)TX + (j - q * w)];
             }
         }
+        float4 p0[kGatherPer], p1[kGatherPer];
+#pragma unroll
+        for (int k = 0; k < kGatherPer; ++k) {
+            const int64_t s = (int64_t)c0 + t + k * kGatherThreads;
+            p0[k] = reach[k] ? partials[2 * s] : make_float4(0.f, 0.f, 0.f, 0.f);
+            p1[k] = reach[k] ? partials[2 * s + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int k = 0; k < kGatherPer; ++k) {
+            const uint32_t i = (uint32_t)(t + k * kGatherThreads);
+            if (i < n) {
+                buf[2 * i] = p0[k];
+                buf[2 * i + 1] = p1[k];
+            }
+        }
+        __syncthreads();
+        const uint32_t s_lo = sb > c0 ? sb : c0;
+        const uint32_t s_hi = (sb + tt < c0 + n) ? sb + tt : c0 + n;
+        for (uint32_t s = s_lo; s < s_hi; ++s) {
+            const float4 q0 = buf[2 * (s - c0)];
+            const float4 q1 = buf[2 * (s - c0) + 1];
+            a.x += q0.x;
+            a.y += q0.y;
+            a.z += q0.z;
+            a.w += q0.w;
+            b.x += q1.x;
+            b.y += q1.y;
+            b.z += q1.z;
+            b.w += q1.w;
+        }
+        __syncthreads();
     }
-    gv_sums[2 * rid] = a;
-    gv_sums[2 * rid + 1] = b;
+    if (rid < VG) {
+        gv_sums[2 * rid] = a;
+        gv_sums[2 * rid + 1] = b;
+    }
 }
 
 hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gather_slots, dim3((unsigned)((s.VG + 255) / 256)), dim3(256), 0, st, s.VG, (uint32_t)s.G,
-                       s.T, s.TX, ws.rec2, ws.depth_key, ws.slot_base, ws.tile_stop, ws.partials, ws.gv_sums);
+    hipLaunchKernelGGL(k_gather_slots, dim3((unsigned)((s.VG + kGatherThreads - 1) / kGatherThreads)),
+                       dim3(kGatherThreads), 0, st, s.VG, (uint32_t)s.G, s.T, s.TX, ws.rec2, ws.depth_key,
+                       ws.slot_base, ws.tile_stop, ws.partials, ws.gv_sums);
     return hipGetLastError();
 }
 
