@@ -149,28 +149,43 @@ __device__ __forceinline__ int eval_alpha(float4 r0, float qc, float opac, float
 // o * G add a few more units of u; so a pixel can pass only if
 // Q(d) <= t_eff = (t + 1e-5) / (1 - 8 u (cond + 1)).  The region Q <= t_eff has
 // half-widths sqrt(t_eff c' / det) and sqrt(t_eff a' / det); all of this is
-// computed in float64 from the exact float32 coefficients and widened by 0.01
-// px plus 1e-6 relative before rounding to float32.  When 8 u (cond + 1) >= 1/2
-// the box is unbounded (never skip).  Returns {x0, x1, y0, y1}; an empty box
-// when the entry can never pass (o <= 1/255).
-__device__ __forceinline__ float4 entry_box(float4 r0, float qc, float opac) {
+// computed in float64 from the exact float32 coefficients, once per record, and
+// the half-widths are widened by 0.01 px plus 1e-6 of (|centre| + half-width)
+// -- more than the rounding of the float32 centre +- half-width at use -- and
+// stored as two binary16 values rounded up (infinite when too large or when
+// 8 u (cond + 1) >= 1/2: never skip; -infinity when the entry can never pass,
+// o <= 1/255: the box is empty).
+__device__ __forceinline__ uint32_t half_bits_up(double v) {  // least binary16 >= v, for v > 0
+    if (!(v <= 65504.0)) return 0x7c00u;
+    const _Float16 h = (_Float16)(float)v;
+    uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, h);
+    if ((double)(float)h < v) ++b;
+    return b;
+}
+
+__device__ __forceinline__ uint32_t entry_box_pack(float4 r0, float qc, float opac) {
     const double a = -(double)r0.z, b = -0.5 * (double)r0.w, c = -(double)qc;
     const double det = a * c - b * b;
     const double tt = log2(255.0 * (double)opac);
-    const float4 all = make_float4(-3.0e38f, 3.0e38f, -3.0e38f, 3.0e38f);
-    if (!(tt > -1e-5)) return make_float4(3.0e38f, -3.0e38f, 3.0e38f, -3.0e38f);
-    if (!(det > 0.0) || !(a > 0.0) || !(c > 0.0)) return all;
+    if (!(tt > -1e-5)) return 0xfc00fc00u;
+    if (!(det > 0.0) || !(a > 0.0) || !(c > 0.0)) return 0x7c007c00u;
     const double t = (tt < 8.0 ? tt : 8.0) + 1e-5;
     const double mid = 0.5 * (a + c), hd = sqrt(0.25 * (a - c) * (a - c) + b * b);
     const double lmax = mid + hd, lmin = det / lmax;
     const double grow = 8.0 * 5.9604644775390625e-8 * (lmax / lmin + 1.0);
-    if (!(grow < 0.5)) return all;
+    if (!(grow < 0.5)) return 0x7c007c00u;
     const double te = t / (1.0 - grow);
     const double ex = sqrt(te * c / det), ey = sqrt(te * a / det);
-    const double mx = r0.x, my = r0.y;
-    auto lo = [](double v) { return (float)(v - 0.01 - 1e-6 * fabs(v)); };
-    auto hi = [](double v) { return (float)(v + 0.01 + 1e-6 * fabs(v)); };
-    return make_float4(lo(mx - ex), hi(mx + ex), lo(my - ey), hi(my + ey));
+    const double wx = ex + 0.01 + 1e-6 * (fabs((double)r0.x) + ex);
+    const double wy = ey + 0.01 + 1e-6 * (fabs((double)r0.y) + ey);
+    return half_bits_up(wx) | (half_bits_up(wy) << 16);
+}
+
+// {x0, x1, y0, y1} of the packed box around the centre (mx, my).
+__device__ __forceinline__ float4 entry_box_unpack(float mx, float my, uint32_t packed) {
+    const float ex = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed & 0xffffu));
+    const float ey = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed >> 16));
+    return make_float4(mx - ex, mx + ex, my - ey, my + ey);
 }
 
 // Compensated (Kahan) accumulation of the prefix colour; the true sum is hi - comp.

@@ -160,9 +160,12 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
             pre[ch] = acc + 0.5f;
         }
 
-        rec0[rid] = make_float4(mx, my, ca * kNegHalfLog2e, cb * kNegLog2e);
-        rec1[rid] = make_float4(cc * kNegHalfLog2e, op, pre[0], pre[1]);
-        rec2[rid] = make_float4(pre[2], __uint_as_float(0u), __uint_as_float((uint32_t)x0 | ((uint32_t)y0 << 16)),
+        const float4 r0v = make_float4(mx, my, ca * kNegHalfLog2e, cb * kNegLog2e);
+        const float qcv = cc * kNegHalfLog2e;
+        rec0[rid] = r0v;
+        rec1[rid] = make_float4(qcv, op, pre[0], pre[1]);
+        rec2[rid] = make_float4(pre[2], __uint_as_float(entry_box_pack(r0v, qcv, op)),
+                                __uint_as_float((uint32_t)x0 | ((uint32_t)y0 << 16)),
                                 __uint_as_float((uint32_t)x1 | ((uint32_t)y1 << 16)));
         depth_key[rid] = __float_as_uint(tz);
         tiles_touched[rid] = (uint32_t)((x1 - x0) * (y1 - y0));

@@ -63,11 +63,11 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
-            const float cb = rec2[rid].x;
+            const float2 c = reinterpret_cast<const float2*>(rec2)[2 * rid];
             s0[threadIdx.x] = a;
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
-            s2[threadIdx.x] = clamp_colour(cb);
-            sbox[threadIdx.x] = entry_box(a, b.x, b.y);
+            s2[threadIdx.x] = clamp_colour(c.x);
+            sbox[threadIdx.x] = entry_box_unpack(a.x, a.y, __float_as_uint(c.y));
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kRenderBatch, rg.y - base);
@@ -90,27 +90,30 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         for (int k = 0; k < nw; ++k) {
             const int j = slist[wave][k];
-            if (!done) {
-                const float4 a = s0[j];
-                const float4 b = s1[j];
-                float dx, dy, alpha;
-                bool clamped;
-                const int code = eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped);
-                n_near += code != 0;
-                if (code == 2) {
-                    const float tT = Tr * (1.0f - alpha);
-                    if (tT < kTMin) {
-                        done = true;
-                        stop = base + (uint32_t)j;
-                    } else {
-                        const float w = alpha * Tr;
-                        kahan_add(h0, c0, b.z * w);
-                        kahan_add(h1, c1, b.w * w);
-                        kahan_add(h2, c2, s2[j] * w);
-                        Tr = tT;
-                        ++n;
-                    }
-                }
+            const float4 a = s0[j];
+            const float4 b = s1[j];
+            // evaluated in every lane; the decisions below mask lanes that are done or beyond the cut
+            const float dx = px - a.x, dy = py - a.y;
+            const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
+            const bool near = !done && e >= kECutoff;
+            const float aG = b.y * exp2_spec(e);
+            const float alpha = aG < kAlphaMax ? aG : kAlphaMax;
+            const bool pass = near && alpha >= kAlphaMin;
+            const float tT = Tr * (1.0f - alpha);
+            const bool sat = pass && tT < kTMin;
+            const bool contrib = pass && !sat;
+            n_near += near ? 1u : 0u;
+            if (sat) {
+                done = true;
+                stop = base + (uint32_t)j;
+            }
+            if (contrib) {
+                const float w = alpha * Tr;
+                kahan_add(h0, c0, b.z * w);
+                kahan_add(h1, c1, b.w * w);
+                kahan_add(h2, c2, s2[j] * w);
+                Tr = tT;
+                ++n;
             }
             if (__ballot(!done) == 0ull) break;
         }

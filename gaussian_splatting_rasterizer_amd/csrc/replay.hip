@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             s0[threadIdx.x] = a;
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(c.x);
-            sbox[threadIdx.x] = entry_box(a, b.x, b.y);
+            sbox[threadIdx.x] = entry_box_unpack(a.x, a.y, __float_as_uint(c.y));
             // slot of this (tile, Gaussian) pair: the record's slot base + row-major tile index
             const uint32_t lo = __float_as_uint(c.z), hi = __float_as_uint(c.w);
             const uint32_t x0 = lo & 0xffffu, y0 = lo >> 16, wx = (hi & 0xffffu) - x0;
@@ -160,49 +160,41 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             for (int k = 0; k < nw; ++k) {
                 const int j = slist[wave][k];
-                float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                bool contrib = false;
-                if (!done) {
-                    const float4 a = s0[j];
-                    const float4 b = s1[j];
-                    float dx, dy, alpha;
-                    bool clamped;
-                    if (eval_alpha(a, b.x, b.y, px, py, dx, dy, alpha, clamped) == 2) {
-                        const float tT = Tr * (1.0f - alpha);
-                        if (tT < kTMin) {
-                            done = true;
-                        } else {
-                            contrib = true;
-                            const float cr = b.z, cg = b.w, cbl = s2[j];
-                            const float w = alpha * Tr;
-                            const float x0 = cr * w, x1 = cg * w, x2 = cbl * w;
-                            // suffix (times T (1 - alpha)) from the compensated prefix hi - comp
-                            const float S0 = ((Ch0 - h0) + c0) - x0;
-                            const float S1 = ((Ch1 - h1) + c1) - x1;
-                            const float S2 = ((Ch2 - h2) + c2) - x2;
-                            const float inv_den = __builtin_amdgcn_rcpf(tT + eps);
-                            const float rho = r0 * (cr - S0 * inv_den) + r1 * (cg - S1 * inv_den) +
-                                              r2 * (cbl - S2 * inv_den);
-                            const bool m = !clamped && (tT >= den_min);
-                            const float mw = m ? w * rho : 0.0f;
-                            x[0] = w;
-                            x[1] = mw;
-                            x[2] = mw * dx;
-                            x[3] = mw * dy;
-                            x[4] = w * r0;
-                            x[5] = w * r1;
-                            x[6] = w * r2;
-                            x[7] = 1.0f;
-                            kahan_add(h0, c0, x0);
-                            kahan_add(h1, c1, x1);
-                            kahan_add(h2, c2, x2);
-                            Tr = tT;
-                        }
-                    }
-                }
+                const float4 a = s0[j];
+                const float4 b = s1[j];
+                // evaluated in every lane; the decisions mask lanes that are done or beyond the cut
+                const float dx = px - a.x, dy = py - a.y;
+                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
+                const bool near = !done && e >= kECutoff;
+                const float aG = b.y * exp2_spec(e);
+                const bool clamped = !(aG < kAlphaMax);
+                const float alpha = clamped ? kAlphaMax : aG;
+                const bool pass = near && alpha >= kAlphaMin;
+                const float tT = Tr * (1.0f - alpha);
+                const bool sat = pass && tT < kTMin;
+                const bool contrib = pass && !sat;
+                done = done || sat;
                 if (__ballot(contrib) != 0ull) {
+                    const float cr = b.z, cg = b.w, cbl = s2[j];
+                    const float w = contrib ? alpha * Tr : 0.0f;
+                    const float x0 = cr * w, x1 = cg * w, x2 = cbl * w;
+                    // suffix (times T (1 - alpha)) from the compensated prefix hi - comp
+                    const float S0 = ((Ch0 - h0) + c0) - x0;
+                    const float S1 = ((Ch1 - h1) + c1) - x1;
+                    const float S2 = ((Ch2 - h2) + c2) - x2;
+                    const float inv_den = __builtin_amdgcn_rcpf(tT + eps);
+                    const float rho = r0 * (cr - S0 * inv_den) + r1 * (cg - S1 * inv_den) +
+                                      r2 * (cbl - S2 * inv_den);
+                    const float mw = (contrib && !clamped && tT >= den_min) ? w * rho : 0.0f;
+                    const float x[8] = {w, mw, mw * dx, mw * dy, w * r0, w * r1, w * r2, contrib ? 1.0f : 0.0f};
                     const float red = wave_reduce8(x, lane);
                     if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
+                    if (contrib) {
+                        kahan_add(h0, c0, x0);
+                        kahan_add(h1, c1, x1);
+                        kahan_add(h2, c2, x2);
+                        Tr = tT;
+                    }
                 }
                 if (__ballot(!done) == 0ull) break;
             }
