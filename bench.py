@@ -44,6 +44,9 @@ def parse_args():
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                    help="budget of rendering work for the CPU oracle sample (0 disables)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="before the steps, copy a buffer of this many MiB once (untimed), so that "
+                        "hardware byte counters can be scaled against a copy of known size")
     return p.parse_args()
 
 
@@ -100,6 +103,14 @@ def main():
         obs = (obs_col + torch.from_numpy(sc.pixel_noise).to(dev)).contiguous()
         rp.close()
         del rp, obs_col
+
+        if args.copy_calibration_mib > 0:
+            n = args.copy_calibration_mib * (1 << 20) // 4
+            src_buf = torch.ones(n, dtype=torch.float32, device=dev)
+            dst_buf = torch.empty_like(src_buf)
+            dst_buf.copy_(src_buf)
+            stream.synchronize()
+            del src_buf, dst_buf
 
         r = binding.rasterizer_for_scene(sc, device=dev)
         r.project_and_bin()

@@ -277,9 +277,11 @@ __global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restric
 // resolve their global offsets by looking back over earlier tiles' published
 // counts: a word per (tile, digit) holding the count and a tag -- the pass's
 // epoch and whether the count is the inclusive prefix of all tiles up to this
-// one or only this tile's own.  A tile only waits on tiles that started before
-// it, and every tile publishes its own counts before it waits, so the chain
-// always resolves.  Optional final-pass extras: rect_src != null gathers
+// one or only this tile's own.  A tile publishes its own counts as soon as it
+// has ranked its keys, orders them in LDS, and only then looks back, so the
+// wait overlaps its own work.  A tile only waits on tiles that started before
+// it, and every tile publishes before it waits, so the chain always resolves.
+// Optional final-pass extras: rect_src != null gathers
 // rect_out[pos] = rect_src[2 * val + 1] (the packed tile rectangle of record
 // `val`) and tt_out[pos] = its tile count; keys_out may be null.
 __global__ __launch_bounds__(kRadixThreads) void k_onesweep(
@@ -323,62 +325,64 @@ __global__ __launch_bounds__(kRadixThreads) void k_onesweep(
         if (valid && lower == 0ull) cnt[wave][dgt] = c + (uint32_t)__popcll(peers);
     }
     __syncthreads();
-    {
-        // block-local digit offsets and the pass's global digit offsets in one
-        // 64-bit scan: (digit total << 32) + block count, one digit per thread
-        const int dgt = threadIdx.x;
-        uint32_t tot = 0, gtot = 0;
-        if (dgt < nbins) {
+    // publish this tile's digit counts first, so later tiles can look past it
+    // while this one is still ordering its keys
+    const int dgt = threadIdx.x;
+    uint32_t tot = 0, gtot = 0;
+    uint64_t* mine = lookback + tile * kMaxBins + dgt;
+    const uint32_t tag = epoch << 1;
+    if (dgt < nbins) {
 #pragma unroll
-            for (int w = 0; w < kRadixWaves; ++w) tot += cnt[w][dgt];
-            gtot = digit_tot[dgt];
-        }
-        uint64_t both_total;
-        const uint64_t both = block_exclusive_scan<uint64_t, kRadixThreads>(((uint64_t)gtot << 32) | tot, &both_total,
-                                                                            scan_lds);
-        const uint32_t loff = (uint32_t)both;
-        const uint32_t digit_off = (uint32_t)(both >> 32);
-        if (dgt < nbins) {
-            uint32_t s = loff;
+        for (int w = 0; w < kRadixWaves; ++w) tot += cnt[w][dgt];
+        gtot = digit_tot[dgt];
+        __hip_atomic_store(mine, ((uint64_t)(tile == 0 ? tag | 1u : tag) << 32) | tot, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // block-local digit offsets and the pass's global digit offsets in one
+    // 64-bit scan: (digit total << 32) + block count, one digit per thread
+    uint64_t both_total;
+    const uint64_t both = block_exclusive_scan<uint64_t, kRadixThreads>(((uint64_t)gtot << 32) | tot, &both_total,
+                                                                        scan_lds);
+    const uint32_t loff = (uint32_t)both;
+    const uint32_t digit_off = (uint32_t)(both >> 32);
+    if (dgt < nbins) {
+        uint32_t s = loff;
 #pragma unroll
-            for (int w = 0; w < kRadixWaves; ++w) {
-                const uint32_t c = cnt[w][dgt];
-                cnt[w][dgt] = s;
-                s += c;
-            }
-            uint64_t* mine = lookback + tile * kMaxBins + dgt;
-            const uint32_t tag = epoch << 1;
-            uint32_t excl = 0;
-            if (tile == 0) {
-                __hip_atomic_store(mine, ((uint64_t)(tag | 1u) << 32) | tot, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-                __hip_atomic_store(mine, ((uint64_t)tag << 32) | tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t* prev = mine - kMaxBins;
-                for (;;) {
-                    const uint64_t w = __hip_atomic_load(prev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const uint32_t h = (uint32_t)(w >> 32);
-                    if ((h & ~1u) != tag) {
-                        __builtin_amdgcn_s_sleep(1);
-                        continue;
-                    }
-                    excl += (uint32_t)w;
-                    if (h & 1u) break;
-                    prev -= kMaxBins;
-                }
-                __hip_atomic_store(mine, ((uint64_t)(tag | 1u) << 32) | (excl + tot), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-            gdelta[dgt] = digit_off + excl - loff;
+        for (int w = 0; w < kRadixWaves; ++w) {
+            const uint32_t c = cnt[w][dgt];
+            cnt[w][dgt] = s;
+            s += c;
         }
     }
     __syncthreads();
+    // block-local reorder: each digit's keys become one contiguous run
 #pragma unroll
     for (int i = 0; i < kRadixItems; ++i) {
         if (base + i * 64 + lane >= n) continue;
         const uint32_t lp = cnt[wave][(key[i] >> shift) & mask] + rank[i];
         skey[lp] = key[i];
         sval[lp] = val[i];
+    }
+    // decoupled look-back over the earlier tiles' published counts
+    if (dgt < nbins) {
+        uint32_t excl = 0;
+        if (tile > 0) {
+            const uint64_t* prev = mine - kMaxBins;
+            for (;;) {
+                const uint64_t w = __hip_atomic_load(prev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t h = (uint32_t)(w >> 32);
+                if ((h & ~1u) != tag) {
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                excl += (uint32_t)w;
+                if (h & 1u) break;
+                prev -= kMaxBins;
+            }
+            __hip_atomic_store(mine, ((uint64_t)(tag | 1u) << 32) | (excl + tot), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        gdelta[dgt] = digit_off + excl - loff;
     }
     __syncthreads();
     const int64_t nblk = n - bbase < kRadixTile ? n - bbase : kRadixTile;

@@ -277,16 +277,22 @@ __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */,
 // consecutive records' slots are adjacent, so reads and writes are coalesced.
 // Tile lists are ordered by the (depth bits, Gaussian) key, so a pair was
 // reached iff its key is below the key at which its tile's replay stopped.
-// The partial slots of a block's 256 consecutive records form one contiguous
-// range (slot_base is a scan in record order).  The block streams that range
-// through LDS in chunks: each loading thread finds its slot's record by binary
-// search over the block's slot bases, and fetches the slot's partials only if
-// the replay reached that pair (else stores zeros), so loads are coalesced and
-// unreached slots cost no HBM traffic; each thread then sums its own record's
-// slots from LDS in slot order.
+// The partial slots of consecutive records form one contiguous range (slot_base
+// is a scan in record order).  Each wave takes 64 consecutive records and
+// streams their slot range through a wave-private LDS buffer, 64 slots at a
+// time: lane i finds the record of slot c0 + i by binary search over the
+// wave's slot bases and fetches the slot's partials only if the replay reached
+// that pair (else zeros), so loads are coalesced and unreached slots cost no
+// HBM traffic; each lane then sums its own record's slots from LDS, in slot
+// order.  Waves synchronise only with themselves.
 constexpr int kGatherThreads = 256;
-constexpr int kGatherChunk = 1024;  // slots per LDS chunk (32 KiB)
-constexpr int kGatherPer = kGatherChunk / kGatherThreads;
+constexpr int kGatherWaves = kGatherThreads / 64;
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uint32_t G, int T, int TX,
                                                                  const float4* __restrict__ rec2,
@@ -295,16 +301,16 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
                                                                  const uint64_t* __restrict__ tile_stop,
                                                                  const float4* __restrict__ partials,
                                                                  float4* __restrict__ gv_sums) {
-    __shared__ float4 buf[2 * kGatherChunk];
-    __shared__ uint32_t s_sb[kGatherThreads];    // first slot of each record
-    __shared__ uint32_t s_tile0[kGatherThreads]; // global tile id of the rectangle's first tile
-    __shared__ uint32_t s_w[kGatherThreads];     // rectangle width in tiles
-    __shared__ uint64_t s_key[kGatherThreads];   // (depth bits, Gaussian) list key
-    __shared__ uint32_t s_end;
-    const int t = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.x * kGatherThreads;
-    const int64_t rid = r0 + t;
-    const int last = (int)(VG - r0 < kGatherThreads ? VG - r0 : kGatherThreads) - 1;
+    __shared__ float4 buf[kGatherWaves][128];        // 64 slots x 2 float4 per wave
+    __shared__ uint32_t s_sb[kGatherWaves][64];      // first slot of each record
+    __shared__ uint32_t s_tile0[kGatherWaves][64];   // global tile id of the rectangle's first tile
+    __shared__ uint32_t s_w[kGatherWaves][64];       // rectangle width in tiles
+    __shared__ uint64_t s_key[kGatherWaves][64];     // (depth bits, Gaussian) list key
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r0 = (int64_t)blockIdx.x * kGatherThreads + wave * 64;
+    if (r0 >= VG) return;
+    const int64_t rid = r0 + lane;
+    const int last = (int)(VG - r0 < 64 ? VG - r0 : 64) - 1;
     uint32_t tt = 0, sb = 0;
     if (rid < VG) {
         const float4 r2 = rec2[rid];
@@ -321,57 +327,40 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
             tt = w * ((hi >> 16) - y0);
             tile0 = v * (uint32_t)T + y0 * (uint32_t)TX + x0;
         }
-        s_sb[t] = sb;
-        s_tile0[t] = tile0;
-        s_w[t] = w;
-        s_key[t] = key;
-        if (t == last) s_end = sb + tt;
+        s_sb[wave][lane] = sb;
+        s_tile0[wave][lane] = tile0;
+        s_w[wave][lane] = w;
+        s_key[wave][lane] = key;
     }
-    __syncthreads();
-    const uint32_t first = s_sb[0], end = s_end;
+    const uint32_t first = (uint32_t)__builtin_amdgcn_readfirstlane((int)sb);
+    const uint32_t end = (uint32_t)__builtin_amdgcn_readlane((int)(sb + tt), last);
+    wave_lds_sync();
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (uint32_t c0 = first; c0 < end; c0 += kGatherChunk) {
-        const uint32_t n = end - c0 < (uint32_t)kGatherChunk ? end - c0 : (uint32_t)kGatherChunk;
-        bool reach[kGatherPer];
-#pragma unroll
-        for (int k = 0; k < kGatherPer; ++k) {
-            const uint32_t i = (uint32_t)(t + k * kGatherThreads);
-            reach[k] = false;
-            if (i < n) {
-                const uint32_t s = c0 + i;
-                int lo = 0, hi = last;
-                while (lo < hi) {  // last record whose first slot is <= s: the one holding s
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (s_sb[mid] <= s) lo = mid;
-                    else hi = mid - 1;
-                }
-                const uint32_t j = s - s_sb[lo];
-                const uint32_t w = s_w[lo];
-                const uint32_t q = j / w;
-                reach[k] = s_key[lo] < tile_stop[s_tile0[lo] + q * (uint32_t)TX + (j - q * w)];
+    for (uint32_t c0 = first; c0 < end; c0 += 64) {
+        const uint32_t s = c0 + (uint32_t)lane;
+        bool reach = false;
+        if (s < end) {
+            int lo = 0, hi = last;
+            while (lo < hi) {  // last record whose first slot is <= s: the one holding s
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_sb[wave][mid] <= s) lo = mid;
+                else hi = mid - 1;
             }
+            const uint32_t j = s - s_sb[wave][lo];
+            const uint32_t w = s_w[wave][lo];
+            const uint32_t q = j / w;
+            reach = s_key[wave][lo] < tile_stop[s_tile0[wave][lo] + q * (uint32_t)TX + (j - q * w)];
         }
-        float4 p0[kGatherPer], p1[kGatherPer];
-#pragma unroll
-        for (int k = 0; k < kGatherPer; ++k) {
-            const int64_t s = (int64_t)c0 + t + k * kGatherThreads;
-            p0[k] = reach[k] ? partials[2 * s] : make_float4(0.f, 0.f, 0.f, 0.f);
-            p1[k] = reach[k] ? partials[2 * s + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int k = 0; k < kGatherPer; ++k) {
-            const uint32_t i = (uint32_t)(t + k * kGatherThreads);
-            if (i < n) {
-                buf[2 * i] = p0[k];
-                buf[2 * i + 1] = p1[k];
-            }
-        }
-        __syncthreads();
+        const float4 p0 = reach ? partials[2 * (int64_t)s] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 p1 = reach ? partials[2 * (int64_t)s + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        buf[wave][2 * lane] = p0;
+        buf[wave][2 * lane + 1] = p1;
+        wave_lds_sync();
         const uint32_t s_lo = sb > c0 ? sb : c0;
-        const uint32_t s_hi = (sb + tt < c0 + n) ? sb + tt : c0 + n;
-        for (uint32_t s = s_lo; s < s_hi; ++s) {
-            const float4 q0 = buf[2 * (s - c0)];
-            const float4 q1 = buf[2 * (s - c0) + 1];
+        const uint32_t s_hi = (sb + tt < c0 + 64) ? sb + tt : c0 + 64;
+        for (uint32_t u = s_lo; u < s_hi; ++u) {
+            const float4 q0 = buf[wave][2 * (u - c0)];
+            const float4 q1 = buf[wave][2 * (u - c0) + 1];
             a.x += q0.x;
             a.y += q0.y;
             a.z += q0.z;
@@ -381,7 +370,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
             b.z += q1.z;
             b.w += q1.w;
         }
-        __syncthreads();
+        wave_lds_sync();
     }
     if (rid < VG) {
         gv_sums[2 * rid] = a;
