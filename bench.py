@@ -51,24 +51,58 @@ def parse_args():
 
 
 def stage_bytes(stage, c):
-    """Algorithmic HBM bytes per launch of an HBM-bound stage."""
+    """Algorithmic HBM bytes per launch of a stage: every array the stage must
+    read or write once, at its element size (the counts behind each term are in
+    DESIGN.md)."""
     G, V, d, P, VG = c["G"], c["V"], c["d"], c["P"], c["G"] * c["V"]
-    if stage == "project":
-        return G * (44 + 12 * d) + VG * (48 + 4 + 4)
-    if stage == "depth_sort":      # 4 passes: histogram read 4 B, scatter read 8 B (4 B first pass), write 8 B
-        return VG * (4 * (4 + 8 + 8) - 4)
-    if stage == "scan":            # reduce + down sweep gather tt through the sorted ids, write offsets
-        return VG * (8 + 8 + 4)
-    if stage == "emit":
-        return VG * (4 + 4 + 4 + 16) + c["n_live"] * 4 + P * 8
-    if stage == "tile_sort":       # histogram read 4 B + scatter read 8 B + write 8 B, final pass also gather + inv
-        passes = max(1, (max(1, (V * c["T"] - 1).bit_length()) + 7) // 8)
-        return P * (passes * (4 + 8 + 8) + 8)
+    if stage == "project":       # Gaussian parameters in; records, depth keys, tile counts out
+        return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (48 + 4 + 4)
+    if stage == "depth_sort":    # slot scan (8 B), histogram (4 B), 4 passes of key+value in and out, rect gather
+        return VG * (8 + 4 + 4 * 16 - 4 - 4 + 8 + 12)
+    if stage == "scan":
+        return VG * 8
+    if stage == "emit":          # per record: id, rect, offset in; per pair: tile key and Gaussian out
+        return VG * (4 + 8 + 4) + P * 8
+    if stage == "tile_sort":     # histogram + 2 passes of key+value in and out
+        return P * (4 + 2 * 16)
     if stage == "ranges":
         return P * 4 + V * c["T"] * 8
-    if stage == "finalize":
-        return G * (16 + 4 * (9 + 3 * d)) + VG * 48 + P * (4 + 32)
     return None
+
+
+def _sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gaussian_splatting_rasterizer_amd", "csrc")
+    for n in ["gsr_device.hpp", "gsr_internal.hpp"] + list(names):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(ROOT, "include", "gsr.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+KERNEL_SOURCES = {"k_project": ["project.hip"], "k_render": ["render.hip"], "k_replay": ["replay.hip"],
+                  "k_gather_slots": ["replay.hip"], "k_tokens": ["replay.hip"], "k_onesweep": ["binning.hip"],
+                  "k_emit": ["binning.hip"], "k_ranges": ["binning.hip"], "k_digit_hist": ["binning.hip"]}
+
+
+def kernel_source_sha256(kernel):
+    return _sources_sha256(KERNEL_SOURCES[kernel])
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary of this workload,
+    or None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get("kernels", {}).get(kernel)
+    if not entry or entry.get("source_sha256") != kernel_source_sha256(kernel):
+        return None
+    return int(entry["bytes_per_launch"])
 
 
 def main():
@@ -151,21 +185,29 @@ def main():
 
     c = dict(G=sc.n, V=V, d=sc.d, P=P, T=T_tiles, n_live=n_live)
     stages = {k: (ms / max(cnt, 1), cnt) for k, (ms, cnt) in prof.items()}
-    dominant = max(stages, key=lambda k: stages[k][0])
-    t_dom = stages[dominant][0] * 1e-3
-    if dominant in ("render", "replay"):
-        ops = OPS_EVAL * E + OPS_NEAR * E_near + (OPS_CONTRIB_FWD if dominant == "render" else OPS_CONTRIB_REPLAY) * K
-        achieved = ops / t_dom / 1e12
-        roofline = {"kernel": dominant, "bound": "alu", "achieved": round(achieved, 3), "peak": round(ALU_PEAK_TOPS, 2),
-                    "unit": "Top/s (fp32 VALU lane-ops)", "frac": round(achieved / ALU_PEAK_TOPS, 4),
-                    "traffic": None, "avg_launch_ms": round(stages[dominant][0], 4),
-                    "units": {"evaluations": E, "near_evaluations": E_near, "contributions": K}}
-    else:
-        by = stage_bytes(dominant, c)
-        achieved = by / t_dom / 1e9
-        roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "avg_launch_ms": round(stages[dominant][0], 4), "bytes_per_launch": by}
+    # The dominant single kernel is the score replay (one launch per step, the
+    # "replay" stage): bound by fp32 VALU work, counted algorithmically.
+    t_rep = stages["replay"][0] * 1e-3
+    ops = OPS_EVAL * E + OPS_NEAR * E_near + OPS_CONTRIB_REPLAY * K
+    achieved = ops / t_rep / 1e12
+    workload = scenes.CONFIG_NAMES[args.config]
+    roofline = {"kernel": "k_replay", "bound": "alu", "achieved": round(achieved, 3), "peak": round(ALU_PEAK_TOPS, 2),
+                "unit": "T lane-ops/s (fp32 VALU)", "frac": round(achieved / ALU_PEAK_TOPS, 4),
+                "traffic": measured_traffic("k_replay", workload), "avg_launch_ms": round(stages["replay"][0], 4),
+                "ops_per_launch": ops,
+                "units": {"evaluations": E, "near_evaluations": E_near, "contributions": K}}
+    t_ren = stages["render"][0] * 1e-3
+    ops_r = OPS_EVAL * E + OPS_NEAR * E_near + OPS_CONTRIB_FWD * K
+    secondary = {"k_render": {"bound": "alu", "achieved": round(ops_r / t_ren / 1e12, 3),
+                              "frac": round(ops_r / t_ren / 1e12 / ALU_PEAK_TOPS, 4),
+                              "traffic": measured_traffic("k_render", workload),
+                              "avg_launch_ms": round(stages["render"][0], 4)}}
+    for st in ("project", "depth_sort", "emit", "tile_sort", "ranges"):
+        by = stage_bytes(st, c)
+        t = stages[st][0] * 1e-3
+        secondary[st] = {"bound": "hbm", "achieved_gbs": round(by / t / 1e9, 1),
+                         "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": by,
+                         "avg_launch_ms": round(stages[st][0], 4)}
 
     out = {
         "metric": "render+score-replay Mpix/s",
@@ -186,6 +228,7 @@ def main():
         "work_per_step": {"contributions": K, "evaluations": E, "near_evaluations": E_near, "pairs": P},
         "stages_ms": {k: round(v[0], 4) for k, v in stages.items()},
         "roofline": roofline,
+        "stage_rooflines": secondary,
         "tokens_finite": finite,
     }
 

@@ -152,7 +152,8 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     const size_t tiles = (size_t)s.V * s.T, pixels = (size_t)s.V * s.W * s.H;
     ws->rec0 = (float4*)take(16 * VG);
     ws->rec1 = (float4*)take(16 * VG);
-    ws->rec2 = (float4*)take(16 * VG);
+    ws->rec2 = (float2*)take(8 * VG);
+    ws->rect = (uint2*)take(8 * VG);
     ws->depth_key = (uint32_t*)take(4 * VG);
     ws->tiles_touched = (uint32_t*)take(4 * VG);
     ws->slot_base = (uint32_t*)take(4 * VG);
@@ -177,6 +178,7 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->tile_stop = (uint64_t*)take(8 * tiles);
     ws->partials = (float4*)take(32 * P);
     ws->gv_sums = (float4*)take(32 * VG);
+    ws->rec_masks = (uint64_t*)take(16 * ((VG + 63) / 64));
     ws->pixel = (float4*)take(16 * pixels);
     ws->pixel_stats = (uint2*)take(8 * pixels);
     return (off + 255) & ~(size_t)255;
@@ -332,7 +334,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     //    scan rewrites next); the last pass gathers the rectangles and tile counts and writes no keys
     uint32_t* rid_sorted = nullptr;
     e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b,
-                          reinterpret_cast<const uint2*>(ws.rec2), ws.rect_sorted, ws.tt_sorted, sort_scratch,
+                          ws.rect, ws.rect_sorted, ws.tt_sorted, sort_scratch,
                           &ctx->epoch, stream, nullptr, &rid_sorted);
     if (e != hipSuccess) return hip_fail(e, "depth sort");
     tm.end(GS_STAGE_DEPTH_SORT, stream);
@@ -450,7 +452,11 @@ gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes
             char* d = (char*)dst;
             e = hipMemcpyAsync(d, ws.rec0, 16 * VG, hipMemcpyDeviceToDevice, stream);
             if (e == hipSuccess) e = hipMemcpyAsync(d + 16 * VG, ws.rec1, 16 * VG, hipMemcpyDeviceToDevice, stream);
-            if (e == hipSuccess) e = hipMemcpyAsync(d + 32 * VG, ws.rec2, 16 * VG, hipMemcpyDeviceToDevice, stream);
+            // third plane {colour b, entry box, rect lo, rect hi} interleaved from its two arrays
+            if (e == hipSuccess && VG > 0)
+                e = hipMemcpy2DAsync(d + 32 * VG, 16, ws.rec2, 8, 8, VG, hipMemcpyDeviceToDevice, stream);
+            if (e == hipSuccess && VG > 0)
+                e = hipMemcpy2DAsync(d + 32 * VG + 8, 16, ws.rect, 8, 8, VG, hipMemcpyDeviceToDevice, stream);
             break;
         }
         case GS_EXPORT_DEPTH_KEYS:

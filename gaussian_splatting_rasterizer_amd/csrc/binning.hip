@@ -282,8 +282,8 @@ __global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restric
 // wait overlaps its own work.  A tile only waits on tiles that started before
 // it, and every tile publishes before it waits, so the chain always resolves.
 // Optional final-pass extras: rect_src != null gathers
-// rect_out[pos] = rect_src[2 * val + 1] (the packed tile rectangle of record
-// `val`) and tt_out[pos] = its tile count; keys_out may be null.
+// rect_out[pos] = rect_src[val] (the packed tile rectangle of record `val`)
+// and tt_out[pos] = its tile count; keys_out may be null.
 __global__ __launch_bounds__(kRadixThreads) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift, int bits,
     uint32_t* __restrict__ ticket, const uint32_t* __restrict__ digit_tot, uint64_t* __restrict__ lookback,
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kRadixThreads) void k_onesweep(
 #pragma unroll
         for (int i = 0; i < kRadixItems; ++i) {
             const int lp = i * kRadixThreads + threadIdx.x;
-            r[i] = lp < nblk ? rect_src[2 * (int64_t)v[i] + 1] : make_uint2(0u, 0u);
+            r[i] = lp < nblk ? rect_src[v[i]] : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int i = 0; i < kRadixItems; ++i) {

@@ -13,9 +13,10 @@ namespace gsr {
 // Workspace carve-up.  Every array lives in caller-owned device memory.
 struct Workspace {
     // per (view, Gaussian) record, rid = v * G + g
-    float4* rec0;
-    float4* rec1;
-    float4* rec2;
+    float4* rec0;          // {mx, my, qa, qb}: centre and exponent coefficients (x, y terms)
+    float4* rec1;          // {qc, opacity, colour r, colour g} (colour before clamping)
+    float2* rec2;          // {colour b, entry box: two binary16 half-widths}
+    uint2* rect;           // tile rectangle: {x0 | y0 << 16, x1 | y1 << 16}, zero when culled
     uint32_t* depth_key;   // depth bits, 0xffffffff when culled
     uint32_t* tiles_touched;
     uint32_t* slot_base;   // exclusive scan of tiles_touched in record order: the record's first partial slot
@@ -41,8 +42,9 @@ struct Workspace {
     uint32_t* pair_g;      // Gaussian of each emitted pair, depth order
     uint2* ranges;         // per tile [start, end)
     uint64_t* tile_stop;   // per tile: (depth bits, Gaussian) key of the first entry the replay skipped
-    float4* partials;      // per slot: {W, U_a, U_mx, U_my}, {U_r, U_g, U_b, n_pix}
-    float4* gv_sums;       // per record: the same eight sums over the pairs the replay reached
+    float4* partials;      // per slot: {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix}
+    float4* gv_sums;       // per reached record: {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix}
+    uint64_t* rec_masks;   // per 64 records: {live mask, reached mask}
     float4* pixel;         // per pixel: rendered colour (rgb), final transmittance
     uint2* pixel_stats;    // per pixel: entries evaluated, entries past the distance cut
 };
@@ -90,7 +92,7 @@ hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_
 // kbuf[p & 1] / vbuf[p & 1], so these must differ from each other and from
 // keys_in/vals_in except that kbuf1/vbuf1 may alias keys_in/vals_in (consumed
 // by pass 0).  With rect_src != null the final pass also gathers
-// rect_out[pos] = rect_src[2 * val + 1] and tt_out[pos] = its tile count.
+// rect_out[pos] = rect_src[val] and tt_out[pos] = its tile count.
 // *keys_out / *vals_out receive the arrays holding the result; with
 // keys_out == null the final pass does not write keys.  Each pass takes a new
 // epoch from *epoch.

@@ -2,8 +2,9 @@
 //
 // One thread per Gaussian reads its parameters once (SH coefficients in
 // registers, the degree is a template parameter so nothing is indexed
-// dynamically) and loops over the views, writing one 48-byte record, the depth
-// sort key and the tile count per (view, Gaussian) with coalesced stores.
+// dynamically) and loops over the views, writing per (view, Gaussian) a 40-byte
+// record, its tile rectangle, the depth sort key and the tile count with
+// coalesced stores.
 //
 // Math: EWA splatting of the 3D covariance R(q) S S^T R(q)^T through the
 // view rotation and the perspective Jacobian (lateral offset clamped to 1.3x the
@@ -25,7 +26,8 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
                                                   const float* __restrict__ sh, int64_t G, int V, CamPack cams,
                                                   int W, int H, int TX, int TY, float near_plane, float far_plane,
                                                   float4* __restrict__ rec0, float4* __restrict__ rec1,
-                                                  float4* __restrict__ rec2, uint32_t* __restrict__ depth_key,
+                                                  float2* __restrict__ rec2, uint2* __restrict__ rect,
+                                                  uint32_t* __restrict__ depth_key,
                                                   uint32_t* __restrict__ tiles_touched) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= G) return;
@@ -136,7 +138,8 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         if (!ok) {
             rec0[rid] = make_float4(0.f, 0.f, 0.f, 0.f);
             rec1[rid] = make_float4(0.f, 0.f, 0.f, 0.f);
-            rec2[rid] = make_float4(0.f, 0.f, 0.f, 0.f);
+            rec2[rid] = make_float2(0.f, 0.f);
+            rect[rid] = make_uint2(0u, 0u);
             depth_key[rid] = 0xffffffffu;
             tiles_touched[rid] = 0u;
             continue;
@@ -164,9 +167,8 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         const float qcv = cc * kNegHalfLog2e;
         rec0[rid] = r0v;
         rec1[rid] = make_float4(qcv, op, pre[0], pre[1]);
-        rec2[rid] = make_float4(pre[2], __uint_as_float(entry_box_pack(r0v, qcv, op)),
-                                __uint_as_float((uint32_t)x0 | ((uint32_t)y0 << 16)),
-                                __uint_as_float((uint32_t)x1 | ((uint32_t)y1 << 16)));
+        rec2[rid] = make_float2(pre[2], __uint_as_float(entry_box_pack(r0v, qcv, op)));
+        rect[rid] = make_uint2((uint32_t)x0 | ((uint32_t)y0 << 16), (uint32_t)x1 | ((uint32_t)y1 << 16));
         depth_key[rid] = __float_as_uint(tz);
         tiles_touched[rid] = (uint32_t)((x1 - x0) * (y1 - y0));
     }
@@ -179,7 +181,7 @@ hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Siz
 #define GSR_LAUNCH_PROJECT(DD)                                                                             \
     hipLaunchKernelGGL(k_project<DD>, grid, block, 0, st, sc.means, sc.quats, sc.scales, sc.opacities, sc.sh, \
                        s.G, s.V, cams, s.W, s.H, s.TX, s.TY, near_plane, far_plane, ws.rec0, ws.rec1,     \
-                       ws.rec2, ws.depth_key, ws.tiles_touched)
+                       ws.rec2, ws.rect, ws.depth_key, ws.tiles_touched)
     switch (s.d) {
         case 1: GSR_LAUNCH_PROJECT(1); break;
         case 4: GSR_LAUNCH_PROJECT(4); break;

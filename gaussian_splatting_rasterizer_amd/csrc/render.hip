@@ -23,7 +23,7 @@ constexpr int kRenderBatch = 256;
 
 __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
-                                                const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
+                                                const float2* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
                                                 float bg0, float bg1, float bg2, float* __restrict__ color,
                                                 float* __restrict__ T_out, int32_t* __restrict__ n_out,
                                                 float4* __restrict__ pixel, uint2* __restrict__ pixel_stats) {
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
-            const float2 c = reinterpret_cast<const float2*>(rec2)[2 * rid];
+            const float2 c = rec2[rid];
             s0[threadIdx.x] = a;
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(c.x);

@@ -13,7 +13,9 @@
 //     w   = T alpha                                   (visibility weight)
 //     M   = [o G < 0.99] and [T (1 - alpha) >= den_min]   (mask)
 // and the eight per-pixel partials
-//     W += w, U_a += M w rho, U_mu += M w rho (p - mu), U_c += w r, n_pix += 1.
+//     W += w, U_a += M w rho, U_mu += M w rho (p - mu), U_c += w r, n_pix += 1;
+// the pair's partial then gets the conic applied to U_mu and the colour clamp
+// mask applied to U_c (both constant over the pair).
 // These suffice for every score block: with M set, alpha = o G, so
 // T o grad_mu G rho = conic (p - mu) w rho and T alpha (1 - o) rho = (1 - o) w rho;
 // the colour clamp mask and the SH basis are constant over a (Gaussian, view).
@@ -30,10 +32,12 @@
 // the (depth bits, Gaussian) list key at which each tile stopped.
 //
 // k_gather_slots: per record (record order, coalesced), the sums of the pairs
-// the replay reached.
+// the replay reached, written only for records with a reached pair; plus, per
+// 64 records, a mask of the records that are live (not culled) and one of those
+// with a reached pair.
 // k_tokens: one thread per Gaussian, in float64
 //     q_v = eps + W_v,  Q = eps + sum_v q_v,  gamma_v = q_v / Q
-//     b_mu = sum_v gamma_v J_v^T s_mu_v = (1/Q) sum_v J_v^T conic_v U_mu_v
+//     b_mu = sum_v gamma_v J_v^T s_mu_v = (1/Q) sum_v J_v^T (conic_v U_mu_v)
 //     s_a  = (1/Q) sum_v (1 - o) U_a_v,   s_SH = (1/Q) sum_v M_color (B_v (x) U_c_v)
 //     A    = lambda I + (1/Q) sum_v q_v J_v^T J_v
 // with J_v the unclamped pixel-projection Jacobian, eigenvalues of A by the
@@ -78,8 +82,8 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                                                 const uint32_t* __restrict__ depth_key,
                                                 const uint32_t* __restrict__ slot_base,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
-                                                const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
-                                                const float4* __restrict__ pixel, const float* __restrict__ observed,
+                                                const float2* __restrict__ rec2, const uint2* __restrict__ rect,
+                                                int64_t G, int T, int TX, int W, int H, const float4* __restrict__ pixel, const float* __restrict__ observed,
                                                 float eps, float den_min, float4* __restrict__ partials,
                                                 uint64_t* __restrict__ tile_stop) {
     __shared__ float4 s0[kReplayBatch];
@@ -87,6 +91,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     __shared__ float s2[kReplayBatch];
     __shared__ float4 sbox[kReplayBatch];
     __shared__ uint32_t s_slot[kReplayBatch];  // partial slot of each staged pair
+    __shared__ uint8_t s_mask[kReplayBatch];   // colour clamp mask bits (pre-clamp colour >= 0), r g b
     __shared__ uint8_t slist[4][kReplayBatch];
     __shared__ __align__(16) float sp[4][kReplayBatch][8];
 
@@ -128,15 +133,16 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
-            const float4 c = rec2[rid];
+            const float2 c = rec2[rid];
+            const uint2 rc = rect[rid];
             s0[threadIdx.x] = a;
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(c.x);
             sbox[threadIdx.x] = entry_box_unpack(a.x, a.y, __float_as_uint(c.y));
             // slot of this (tile, Gaussian) pair: the record's slot base + row-major tile index
-            const uint32_t lo = __float_as_uint(c.z), hi = __float_as_uint(c.w);
-            const uint32_t x0 = lo & 0xffffu, y0 = lo >> 16, wx = (hi & 0xffffu) - x0;
+            const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16, wx = (rc.y & 0xffffu) - x0;
             s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
+            s_mask[threadIdx.x] = (uint8_t)((b.z >= 0.0f ? 1u : 0u) | (b.w >= 0.0f ? 2u : 0u) | (c.x >= 0.0f ? 4u : 0u));
         }
         const int cnt = (int)min((uint32_t)kReplayBatch, rg.y - base);
         // this wave's partial rows start at zero; entries it contributes to overwrite theirs
@@ -211,6 +217,15 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 acc.z += q.z;
                 acc.w += q.w;
             }
+            // per pair: the conic applied to U_mu (undoing the exponent scaling of the
+            // stored coefficients) and the colour clamp mask applied to U_c
+            if (h == 0) {
+                const float ca = s0[j].z / kNegHalfLog2e, cb = s0[j].w / kNegLog2e, cc = s1[j].x / kNegHalfLog2e;
+                acc = make_float4(acc.x, acc.y, ca * acc.z + cb * acc.w, cb * acc.z + cc * acc.w);
+            } else {
+                const uint32_t m = s_mask[j];
+                acc = make_float4(m & 1u ? acc.x : 0.0f, m & 2u ? acc.y : 0.0f, m & 4u ? acc.z : 0.0f, acc.w);
+            }
             partials[2 * (int64_t)s_slot[j] + h] = acc;
         }
     }
@@ -230,7 +245,7 @@ hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* so
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.depth_key,
                        ws.slot_base, ws.rec0, ws.rec1,
-                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, eps, den_min, ws.partials,
+                       ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, eps, den_min, ws.partials,
                        ws.tile_stop);
     return hipGetLastError();
 }
@@ -295,13 +310,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uint32_t G, int T, int TX,
-                                                                 const float4* __restrict__ rec2,
+                                                                 const uint2* __restrict__ rect,
                                                                  const uint32_t* __restrict__ depth_key,
                                                                  const uint32_t* __restrict__ slot_base,
                                                                  const uint64_t* __restrict__ tile_stop,
                                                                  const float4* __restrict__ partials,
-                                                                 float4* __restrict__ gv_sums) {
+                                                                 float4* __restrict__ gv_sums,
+                                                                 uint64_t* __restrict__ rec_masks) {
     __shared__ float4 buf[kGatherWaves][128];        // 64 slots x 2 float4 per wave
+    __shared__ uint8_t s_reach[kGatherWaves][64];    // whether each staged slot was reached
     __shared__ uint32_t s_sb[kGatherWaves][64];      // first slot of each record
     __shared__ uint32_t s_tile0[kGatherWaves][64];   // global tile id of the rectangle's first tile
     __shared__ uint32_t s_w[kGatherWaves][64];       // rectangle width in tiles
@@ -312,19 +329,20 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
     const int64_t rid = r0 + lane;
     const int last = (int)(VG - r0 < 64 ? VG - r0 : 64) - 1;
     uint32_t tt = 0, sb = 0;
+    bool live = false;
     if (rid < VG) {
-        const float4 r2 = rec2[rid];
-        const uint32_t lo = __float_as_uint(r2.z), hi = __float_as_uint(r2.w);
+        const uint2 rc = rect[rid];
         sb = slot_base[rid];
         uint32_t w = 1, tile0 = 0;
         uint64_t key = 0;
-        if (hi != 0u) {
+        live = rc.y != 0u;
+        if (live) {
             const uint32_t v = (uint32_t)rid / G;
             const uint32_t g = (uint32_t)rid - v * G;
             key = ((uint64_t)depth_key[rid] << 32) | (uint64_t)g;
-            const uint32_t x0 = lo & 0xffffu, y0 = lo >> 16;
-            w = (hi & 0xffffu) - x0;
-            tt = w * ((hi >> 16) - y0);
+            const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16;
+            w = (rc.y & 0xffffu) - x0;
+            tt = w * ((rc.y >> 16) - y0);
             tile0 = v * (uint32_t)T + y0 * (uint32_t)TX + x0;
         }
         s_sb[wave][lane] = sb;
@@ -336,6 +354,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
     const uint32_t end = (uint32_t)__builtin_amdgcn_readlane((int)(sb + tt), last);
     wave_lds_sync();
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool reached = false;
     for (uint32_t c0 = first; c0 < end; c0 += 64) {
         const uint32_t s = c0 + (uint32_t)lane;
         bool reach = false;
@@ -355,12 +374,14 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
         const float4 p1 = reach ? partials[2 * (int64_t)s + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
         buf[wave][2 * lane] = p0;
         buf[wave][2 * lane + 1] = p1;
+        s_reach[wave][lane] = reach ? 1 : 0;
         wave_lds_sync();
         const uint32_t s_lo = sb > c0 ? sb : c0;
         const uint32_t s_hi = (sb + tt < c0 + 64) ? sb + tt : c0 + 64;
         for (uint32_t u = s_lo; u < s_hi; ++u) {
             const float4 q0 = buf[wave][2 * (u - c0)];
             const float4 q1 = buf[wave][2 * (u - c0) + 1];
+            reached = reached || s_reach[wave][u - c0] != 0;
             a.x += q0.x;
             a.y += q0.y;
             a.z += q0.z;
@@ -372,7 +393,13 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
         }
         wave_lds_sync();
     }
-    if (rid < VG) {
+    const uint64_t live_mask = __ballot(live);
+    const uint64_t reached_mask = __ballot(reached);
+    if (lane == 0) {
+        rec_masks[2 * (r0 >> 6)] = live_mask;
+        rec_masks[2 * (r0 >> 6) + 1] = reached_mask;
+    }
+    if (reached) {
         gv_sums[2 * rid] = a;
         gv_sums[2 * rid + 1] = b;
     }
@@ -381,8 +408,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
 hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
     hipLaunchKernelGGL(k_gather_slots, dim3((unsigned)((s.VG + kGatherThreads - 1) / kGatherThreads)),
-                       dim3(kGatherThreads), 0, st, s.VG, (uint32_t)s.G, s.T, s.TX, ws.rec2, ws.depth_key,
-                       ws.slot_base, ws.tile_stop, ws.partials, ws.gv_sums);
+                       dim3(kGatherThreads), 0, st, s.VG, (uint32_t)s.G, s.T, s.TX, ws.rect, ws.depth_key,
+                       ws.slot_base, ws.tile_stop, ws.partials, ws.gv_sums, ws.rec_masks);
     return hipGetLastError();
 }
 
@@ -393,8 +420,7 @@ constexpr int kTokThreads = 128;
 template <int D>
 __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict__ means, const float* __restrict__ opac,
                                                         int64_t G, int V, CamPack cams,
-                                                        const float4* __restrict__ rec0, const float4* __restrict__ rec1,
-                                                        const float4* __restrict__ rec2,
+                                                        const uint64_t* __restrict__ rec_masks,
                                                         const float4* __restrict__ gv_sums, double eps, double lambda,
                                                         float* __restrict__ tokens) {
     constexpr int DT = 9 + 3 * D;
@@ -415,23 +441,22 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
 
         for (int v = 0; v < V; ++v) {
             const int64_t rid = (int64_t)v * G + g;
-            const float4 r2 = rec2[rid];
-            const uint32_t hi = __float_as_uint(r2.w);
-            if (hi == 0u) {  // culled in this view: q = eps, J = 0, no scores
+            const uint64_t bit = 1ull << (rid & 63);
+            const uint64_t live_w = rec_masks[2 * (rid >> 6)];
+            const uint64_t reach_w = rec_masks[2 * (rid >> 6) + 1];
+            if (!(live_w & bit)) {  // culled in this view: q = eps, J = 0, no scores
                 Q += eps;
                 continue;
             }
-            const float4 p0 = gv_sums[2 * rid];
-            const float4 p1 = gv_sums[2 * rid + 1];
+            const bool reached = (reach_w & bit) != 0;
+            float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (reached) {
+                p0 = gv_sums[2 * rid];
+                p1 = gv_sums[2 * rid + 1];
+            }
             const double q = eps + (double)p0.x;
             Q += q;
-            const float4 a0 = rec0[rid];
-            const float4 a1 = rec1[rid];
-            const double ca = (double)a0.z / (double)kNegHalfLog2e;
-            const double cb = (double)a0.w / (double)kNegLog2e;
-            const double cc = (double)a1.x / (double)kNegHalfLog2e;
-            const double smx = ca * p0.z + cb * p0.w;
-            const double smy = cb * p0.z + cc * p0.w;
+            const double smx = p0.z, smy = p0.w;  // conic * U_mu
 
             const float* cam = cams.c[v];
             double R[9];
@@ -461,22 +486,21 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
             Anum[4] += q * (J0[1] * J0[2] + J1[1] * J1[2]);
             Anum[5] += q * (J0[2] * J0[2] + J1[2] * J1[2]);
 
-            // SH basis along the view direction; clamp mask from the sign of the pre-clamp colour
-            const double ccx = -(R[0] * t0 + R[3] * t1 + R[6] * t2);
-            const double ccy = -(R[1] * t0 + R[4] * t1 + R[7] * t2);
-            const double ccz = -(R[2] * t0 + R[5] * t1 + R[8] * t2);
-            const double dx = mu[0] - ccx, dy = mu[1] - ccy, dz = mu[2] - ccz;
-            const double il = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
-            float B[D];
-            sh_basis_f32((float)(dx * il), (float)(dy * il), (float)(dz * il), D, B);
-            const float m0 = a1.z >= 0.0f ? p1.x : 0.0f;
-            const float m1 = a1.w >= 0.0f ? p1.y : 0.0f;
-            const float m2 = r2.x >= 0.0f ? p1.z : 0.0f;
+            if (reached) {
+                // SH basis along the view direction times the masked colour sums
+                const double ccx = -(R[0] * t0 + R[3] * t1 + R[6] * t2);
+                const double ccy = -(R[1] * t0 + R[4] * t1 + R[7] * t2);
+                const double ccz = -(R[2] * t0 + R[5] * t1 + R[8] * t2);
+                const double dx = mu[0] - ccx, dy = mu[1] - ccy, dz = mu[2] - ccz;
+                const double il = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
+                float B[D];
+                sh_basis_f32((float)(dx * il), (float)(dy * il), (float)(dz * il), D, B);
 #pragma unroll
-            for (int k = 0; k < D; ++k) {
-                shnum[3 * k] += B[k] * m0;
-                shnum[3 * k + 1] += B[k] * m1;
-                shnum[3 * k + 2] += B[k] * m2;
+                for (int k = 0; k < D; ++k) {
+                    shnum[3 * k] += B[k] * p1.x;
+                    shnum[3 * k + 1] += B[k] * p1.y;
+                    shnum[3 * k + 2] += B[k] * p1.z;
+                }
             }
         }
 
@@ -515,8 +539,8 @@ hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Size
     if (s.G == 0) return hipSuccess;
     const dim3 block(kTokThreads), grid((unsigned)((s.G + kTokThreads - 1) / kTokThreads));
 #define GSR_LAUNCH_TOKENS(DD)                                                                              \
-    hipLaunchKernelGGL(k_tokens<DD>, grid, block, 0, st, sc.means, sc.opacities, s.G, s.V, cams, ws.rec0, \
-                       ws.rec1, ws.rec2, ws.gv_sums, (double)eps, (double)lambda, tokens)
+    hipLaunchKernelGGL(k_tokens<DD>, grid, block, 0, st, sc.means, sc.opacities, s.G, s.V, cams, ws.rec_masks, \
+                       ws.gv_sums, (double)eps, (double)lambda, tokens)
     switch (s.d) {
         case 1: GSR_LAUNCH_TOKENS(1); break;
         case 4: GSR_LAUNCH_TOKENS(4); break;
