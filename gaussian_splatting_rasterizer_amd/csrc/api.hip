@@ -181,6 +181,7 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->rec_masks = (uint64_t*)take(16 * ((VG + 63) / 64));
     ws->pixel = (float4*)take(16 * pixels);
     ws->pixel_stats = (uint2*)take(8 * pixels);
+    ws->events = (uint8_t*)take(P);
     return (off + 255) & ~(size_t)255;
 }
 
@@ -197,7 +198,8 @@ gs_status check_dims(const gs_dims* d) {
     if (d->width <= 0 || d->height <= 0) return fail(GS_ERR_INVALID_ARGUMENT, "image size must be positive");
     if (d->width > 65535 * 16 || d->height > 65535 * 16) return fail(GS_ERR_UNSUPPORTED, "image too large");
     if (d->max_pairs < 1) return fail(GS_ERR_INVALID_ARGUMENT, "max_pairs must be >= 1");
-    if (d->max_pairs >= (1ull << 32)) return fail(GS_ERR_UNSUPPORTED, "max_pairs must be < 2^32");
+    // pair indices are u32 and the per-tile loops step past the list end by one batch
+    if (d->max_pairs > (1ull << 32) - (1ull << 16)) return fail(GS_ERR_UNSUPPORTED, "max_pairs must be <= 2^32 - 2^16");
     const uint64_t VG = (uint64_t)d->n_gaussians * (uint64_t)d->n_views;
     if (VG >= (1ull << 32)) return fail(GS_ERR_UNSUPPORTED, "n_gaussians * n_views must be < 2^32");
     const uint64_t TX = (d->width + 15) / 16, TY = (d->height + 15) / 16;

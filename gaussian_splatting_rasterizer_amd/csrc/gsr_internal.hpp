@@ -47,6 +47,8 @@ struct Workspace {
     uint64_t* rec_masks;   // per 64 records: {live mask, reached mask}
     float4* pixel;         // per pixel: rendered colour (rgb), final transmittance
     uint2* pixel_stats;    // per pixel: entries evaluated, entries past the distance cut
+    uint8_t* events;       // per sorted pair the render processed: bit w set when some pixel of wave w
+                           // contributed or saturated at that entry
 };
 
 struct Sizes {

@@ -15,6 +15,9 @@
 // the quadrant would have skipped.  Alpha decisions use the float32 canonical order and the
 // specified exponential; the prefix colour is accumulated with compensated
 // (Kahan) summation so that the replay can recover the suffix accurately.
+// For every entry it processes, the render also leaves one byte whose bit w
+// says whether any pixel of wave w contributed or saturated there: the replay
+// walks only those entries, since at every other one no pixel's state changes.
 #include "gsr_internal.hpp"
 
 namespace gsr {
@@ -26,12 +29,14 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                                                 const float2* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
                                                 float bg0, float bg1, float bg2, float* __restrict__ color,
                                                 float* __restrict__ T_out, int32_t* __restrict__ n_out,
-                                                float4* __restrict__ pixel, uint2* __restrict__ pixel_stats) {
+                                                float4* __restrict__ pixel, uint2* __restrict__ pixel_stats,
+                                                uint8_t* __restrict__ events) {
     __shared__ float4 s0[kRenderBatch];   // {mx, my, qa, qb}
     __shared__ float4 s1[kRenderBatch];   // {qc, opacity, colour r, colour g}
     __shared__ float s2[kRenderBatch];    // colour b
     __shared__ float4 sbox[kRenderBatch]; // conservative box of the pixels the entry can reach
     __shared__ uint8_t slist[4][kRenderBatch];
+    __shared__ uint8_t s_ev[4][kRenderBatch];  // per wave: some pixel contributed or saturated at the entry
 
     const int tile = blockIdx.x;
     const int v = tile / T;
@@ -56,8 +61,17 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     uint32_t stop = 0xffffffffu;  // list index at which the pixel saturated
     bool done = !inside;
 
-    for (uint32_t base = rg.x; base < rg.y; base += kRenderBatch) {
-        if (__syncthreads_count(!done) == 0) break;
+    uint32_t prev_base = 0;
+    int prev_cnt = 0;
+    for (uint32_t base = rg.x;; base += kRenderBatch) {
+        const int live = __syncthreads_count(!done);
+        // the previous batch's event bits (every wave finished it at the barrier above)
+        if ((int)threadIdx.x < prev_cnt)
+            events[prev_base + threadIdx.x] = (uint8_t)(s_ev[0][threadIdx.x] | (s_ev[1][threadIdx.x] << 1) |
+                                                        (s_ev[2][threadIdx.x] << 2) | (s_ev[3][threadIdx.x] << 3));
+        if (base >= rg.y || live == 0) break;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) s_ev[w][threadIdx.x] = 0;
         const uint32_t i = base + threadIdx.x;
         if (i < rg.y) {
             const int64_t rid = vG + sorted_g[i];
@@ -71,52 +85,56 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kRenderBatch, rg.y - base);
-        if (__ballot(!done) == 0ull) continue;  // this wave is finished; keep the block's barriers
-        // this wave's entries, in list order: those whose box meets the quadrant
-        int nw = 0;
-        for (int c = 0; c < cnt; c += 64) {
-            const int j = c + lane;
-            bool hit = false;
-            if (j < cnt) {
-                const float4 bx = sbox[j];
-                hit = bx.x <= qx1 && bx.y >= qx0 && bx.z <= qy1 && bx.w >= qy0;
+        if (__ballot(!done) != 0ull) {
+            // this wave's entries, in list order: those whose box meets the quadrant
+            int nw = 0;
+            for (int c = 0; c < cnt; c += 64) {
+                const int j = c + lane;
+                bool hit = false;
+                if (j < cnt) {
+                    const float4 bx = sbox[j];
+                    hit = bx.x <= qx1 && bx.y >= qx0 && bx.z <= qy1 && bx.w >= qy0;
+                }
+                const uint64_t m = __ballot(hit);
+                if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
+                nw += __popcll(m);
             }
-            const uint64_t m = __ballot(hit);
-            if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
-            nw += __popcll(m);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int k = 0; k < nw; ++k) {
+                const int j = slist[wave][k];
+                const float4 a = s0[j];
+                const float4 b = s1[j];
+                // evaluated in every lane; the decisions below mask lanes that are done or beyond the cut
+                const float dx = px - a.x, dy = py - a.y;
+                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
+                const bool near = !done && e >= kECutoff;
+                const float aG = b.y * exp2_spec(e);
+                const float alpha = aG < kAlphaMax ? aG : kAlphaMax;
+                const bool pass = near && alpha >= kAlphaMin;
+                const float tT = Tr * (1.0f - alpha);
+                const bool sat = pass && tT < kTMin;
+                const bool contrib = pass && !sat;
+                n_near += near ? 1u : 0u;
+                if (sat) {
+                    done = true;
+                    stop = base + (uint32_t)j;
+                }
+                if (contrib) {
+                    const float w = alpha * Tr;
+                    kahan_add(h0, c0, b.z * w);
+                    kahan_add(h1, c1, b.w * w);
+                    kahan_add(h2, c2, s2[j] * w);
+                    Tr = tT;
+                    ++n;
+                }
+                if (pass) s_ev[wave][j] = 1;  // contributed or saturated (every such lane writes the same byte)
+                if (__ballot(!done) == 0ull) break;
+            }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int k = 0; k < nw; ++k) {
-            const int j = slist[wave][k];
-            const float4 a = s0[j];
-            const float4 b = s1[j];
-            // evaluated in every lane; the decisions below mask lanes that are done or beyond the cut
-            const float dx = px - a.x, dy = py - a.y;
-            const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
-            const bool near = !done && e >= kECutoff;
-            const float aG = b.y * exp2_spec(e);
-            const float alpha = aG < kAlphaMax ? aG : kAlphaMax;
-            const bool pass = near && alpha >= kAlphaMin;
-            const float tT = Tr * (1.0f - alpha);
-            const bool sat = pass && tT < kTMin;
-            const bool contrib = pass && !sat;
-            n_near += near ? 1u : 0u;
-            if (sat) {
-                done = true;
-                stop = base + (uint32_t)j;
-            }
-            if (contrib) {
-                const float w = alpha * Tr;
-                kahan_add(h0, c0, b.z * w);
-                kahan_add(h1, c1, b.w * w);
-                kahan_add(h2, c2, s2[j] * w);
-                Tr = tT;
-                ++n;
-            }
-            if (__ballot(!done) == 0ull) break;
-        }
+        prev_base = base;
+        prev_cnt = cnt;
     }
     if (!inside) return;
     kahan_add(h0, c0, Tr * bg0);
@@ -141,7 +159,7 @@ hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* so
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1,
                        ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel,
-                       ws.pixel_stats);
+                       ws.pixel_stats, ws.events);
     return hipGetLastError();
 }
 

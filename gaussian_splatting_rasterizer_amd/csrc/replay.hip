@@ -84,12 +84,12 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
                                                 const float2* __restrict__ rec2, const uint2* __restrict__ rect,
                                                 int64_t G, int T, int TX, int W, int H, const float4* __restrict__ pixel, const float* __restrict__ observed,
-                                                float eps, float den_min, float4* __restrict__ partials,
-                                                uint64_t* __restrict__ tile_stop) {
+                                                const uint8_t* __restrict__ events, float eps, float den_min,
+                                                float4* __restrict__ partials, uint64_t* __restrict__ tile_stop) {
     __shared__ float4 s0[kReplayBatch];
     __shared__ float4 s1[kReplayBatch];
     __shared__ float s2[kReplayBatch];
-    __shared__ float4 sbox[kReplayBatch];
+    __shared__ uint8_t s_evb[kReplayBatch];    // event bits of each staged entry (bit w: wave w)
     __shared__ uint32_t s_slot[kReplayBatch];  // partial slot of each staged pair
     __shared__ uint8_t s_mask[kReplayBatch];   // colour clamp mask bits (pre-clamp colour >= 0), r g b
     __shared__ uint8_t slist[4][kReplayBatch];
@@ -105,7 +105,6 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     const int pyi = qy + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
     const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
-    const float qx0 = (float)qx + 0.5f, qx1 = (float)qx + 7.5f, qy0 = (float)qy + 0.5f, qy1 = (float)qy + 7.5f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -138,7 +137,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             s0[threadIdx.x] = a;
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(c.x);
-            sbox[threadIdx.x] = entry_box_unpack(a.x, a.y, __float_as_uint(c.y));
+            s_evb[threadIdx.x] = events[i];
             // slot of this (tile, Gaussian) pair: the record's slot base + row-major tile index
             const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16, wx = (rc.y & 0xffffu) - x0;
             s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
@@ -152,11 +151,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             int nw = 0;
             for (int c = 0; c < cnt; c += 64) {
                 const int j = c + lane;
-                bool hit = false;
-                if (j < cnt) {
-                    const float4 bx = sbox[j];
-                    hit = bx.x <= qx1 && bx.y >= qx0 && bx.z <= qy1 && bx.w >= qy0;
-                }
+                const bool hit = j < cnt && ((s_evb[j] >> wave) & 1u);
                 const uint64_t m = __ballot(hit);
                 if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
                 nw += __popcll(m);
@@ -245,8 +240,8 @@ hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* so
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.depth_key,
                        ws.slot_base, ws.rec0, ws.rec1,
-                       ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, eps, den_min, ws.partials,
-                       ws.tile_stop);
+                       ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, ws.events, eps, den_min,
+                       ws.partials, ws.tile_stop);
     return hipGetLastError();
 }
 

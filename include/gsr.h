@@ -94,7 +94,7 @@ typedef struct {
     int32_t n_views;    /* 1..GS_MAX_VIEWS, all views share width x height */
     int32_t width;
     int32_t height;
-    uint64_t max_pairs; /* capacity for (tile, Gaussian) pairs, >= 1 */
+    uint64_t max_pairs; /* capacity for (tile, Gaussian) pairs, 1 .. 2^32 - 2^16 */
 } gs_dims;
 
 /* Numerical parameters (the pages name these constants but give no values).

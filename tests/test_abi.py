@@ -62,6 +62,7 @@ def test_workspace_size_validation():
     assert _size_status(n_gaussians=-5)[0] == b.GS_ERR_INVALID_ARGUMENT
     assert _size_status(max_pairs=0)[0] == b.GS_ERR_INVALID_ARGUMENT
     assert _size_status(max_pairs=1 << 32)[0] == b.GS_ERR_UNSUPPORTED
+    assert _size_status(max_pairs=(1 << 32) - (1 << 16) + 1)[0] == b.GS_ERR_UNSUPPORTED
     assert _size_status(n_gaussians=0)[0] == b.GS_OK
     # the size grows with the pair capacity and the image
     assert _size_status(max_pairs=20000)[1] > n and _size_status(width=128)[1] > n
