@@ -179,21 +179,31 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                     const float cr = b.z, cg = b.w, cbl = s2[j];
                     const float w = contrib ? alpha * Tr : 0.0f;
                     const float x0 = cr * w, x1 = cg * w, x2 = cbl * w;
-                    // suffix (times T (1 - alpha)) from the compensated prefix hi - comp
-                    const float S0 = ((Ch0 - h0) + c0) - x0;
-                    const float S1 = ((Ch1 - h1) + c1) - x1;
-                    const float S2 = ((Ch2 - h2) + c2) - x2;
+                    // prefix including this entry (compensated: true value hi - comp); the suffix
+                    // times T (1 - alpha) is then C_hat minus that prefix
+                    float n0 = h0, n1 = h1, n2 = h2, k0 = c0, k1 = c1, k2 = c2;
+                    kahan_add(n0, k0, x0);
+                    kahan_add(n1, k1, x1);
+                    kahan_add(n2, k2, x2);
+                    const float S0 = (Ch0 - n0) + k0;
+                    const float S1 = (Ch1 - n1) + k1;
+                    const float S2 = (Ch2 - n2) + k2;
                     const float inv_den = __builtin_amdgcn_rcpf(tT + eps);
-                    const float rho = r0 * (cr - S0 * inv_den) + r1 * (cg - S1 * inv_den) +
-                                      r2 * (cbl - S2 * inv_den);
+                    // rho = <r, c - S / den> = <r, c> - <r, S> / den
+                    const float rc = __builtin_fmaf(r2, cbl, __builtin_fmaf(r1, cg, r0 * cr));
+                    const float rS = __builtin_fmaf(r2, S2, __builtin_fmaf(r1, S1, r0 * S0));
+                    const float rho = __builtin_fmaf(-rS, inv_den, rc);
                     const float mw = (contrib && !clamped && tT >= den_min) ? w * rho : 0.0f;
                     const float x[8] = {w, mw, mw * dx, mw * dy, w * r0, w * r1, w * r2, contrib ? 1.0f : 0.0f};
                     const float red = wave_reduce8(x, lane);
                     if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
                     if (contrib) {
-                        kahan_add(h0, c0, x0);
-                        kahan_add(h1, c1, x1);
-                        kahan_add(h2, c2, x2);
+                        h0 = n0;
+                        h1 = n1;
+                        h2 = n2;
+                        c0 = k0;
+                        c1 = k1;
+                        c2 = k2;
                         Tr = tT;
                     }
                 }
@@ -313,10 +323,10 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
                                                                  float4* __restrict__ gv_sums,
                                                                  uint64_t* __restrict__ rec_masks) {
     __shared__ float4 buf[kGatherWaves][128];        // 64 slots x 2 float4 per wave
-    __shared__ uint8_t s_reach[kGatherWaves][64];    // whether each staged slot was reached
     __shared__ uint32_t s_sb[kGatherWaves][64];      // first slot of each record
     __shared__ uint32_t s_tile0[kGatherWaves][64];   // global tile id of the rectangle's first tile
     __shared__ uint32_t s_w[kGatherWaves][64];       // rectangle width in tiles
+    __shared__ float s_rw[kGatherWaves][64];         // 1 / width
     __shared__ uint64_t s_key[kGatherWaves][64];     // (depth bits, Gaussian) list key
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t r0 = (int64_t)blockIdx.x * kGatherThreads + wave * 64;
@@ -343,6 +353,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
         s_sb[wave][lane] = sb;
         s_tile0[wave][lane] = tile0;
         s_w[wave][lane] = w;
+        s_rw[wave][lane] = 1.0f / (float)w;
         s_key[wave][lane] = key;
     }
     const uint32_t first = (uint32_t)__builtin_amdgcn_readfirstlane((int)sb);
@@ -362,21 +373,39 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
             }
             const uint32_t j = s - s_sb[wave][lo];
             const uint32_t w = s_w[wave][lo];
-            const uint32_t q = j / w;
-            reach = s_key[wave][lo] < tile_stop[s_tile0[wave][lo] + q * (uint32_t)TX + (j - q * w)];
+            // row j / w: a float estimate, off by at most one, then corrected
+            uint32_t q = (uint32_t)((float)j * s_rw[wave][lo]);
+            int32_t rem = (int32_t)(j - q * w);
+            if (rem < 0) {
+                --q;
+                rem += (int32_t)w;
+            } else if (rem >= (int32_t)w) {
+                ++q;
+                rem -= (int32_t)w;
+            }
+            reach = s_key[wave][lo] < tile_stop[s_tile0[wave][lo] + q * (uint32_t)TX + (uint32_t)rem];
         }
-        const float4 p0 = reach ? partials[2 * (int64_t)s] : make_float4(0.f, 0.f, 0.f, 0.f);
-        const float4 p1 = reach ? partials[2 * (int64_t)s + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
-        buf[wave][2 * lane] = p0;
-        buf[wave][2 * lane + 1] = p1;
-        s_reach[wave][lane] = reach ? 1 : 0;
+        const uint64_t rmask = __ballot(reach);
+        if (rmask == 0ull) continue;  // nothing in this chunk was reached
+        if (reach) {
+            buf[wave][2 * lane] = partials[2 * (int64_t)s];
+            buf[wave][2 * lane + 1] = partials[2 * (int64_t)s + 1];
+        }
         wave_lds_sync();
-        const uint32_t s_lo = sb > c0 ? sb : c0;
-        const uint32_t s_hi = (sb + tt < c0 + 64) ? sb + tt : c0 + 64;
-        for (uint32_t u = s_lo; u < s_hi; ++u) {
-            const float4 q0 = buf[wave][2 * (u - c0)];
-            const float4 q1 = buf[wave][2 * (u - c0) + 1];
-            reached = reached || s_reach[wave][u - c0] != 0;
+        // this record's reached slots in the chunk, in slot order
+        const uint32_t s_lo = sb > c0 ? sb - c0 : 0u;
+        const uint32_t s_hi = (sb + tt < c0 + 64) ? (sb + tt > c0 ? sb + tt - c0 : 0u) : 64u;
+        uint64_t m = 0ull;
+        if (s_hi > s_lo) {
+            const uint64_t below_hi = s_hi >= 64 ? ~0ull : ((1ull << s_hi) - 1ull);
+            m = rmask & below_hi & ~((1ull << s_lo) - 1ull);
+        }
+        while (m) {
+            const int i = __builtin_ctzll(m);
+            m &= m - 1ull;
+            const float4 q0 = buf[wave][2 * i];
+            const float4 q1 = buf[wave][2 * i + 1];
+            reached = true;
             a.x += q0.x;
             a.y += q0.y;
             a.z += q0.z;
