@@ -163,6 +163,8 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->rect_sorted = (uint2*)take(8 * VG);
     ws->tt_sorted = (uint32_t*)take(4 * VG);
     ws->offsets = (uint32_t*)take(4 * VG);
+    ws->pay_a = (uint32_t*)take(4 * VG);
+    ws->pay_b = (uint32_t*)take(4 * VG);
     ws->scan_blocks = (uint64_t*)take(8 * (size_t)s.scan_blocks_cap);
     ws->scan_total = (uint64_t*)take(8 * 4);
     ws->lookback = (uint64_t*)take(8 * 256 * (size_t)s.sort_tiles_cap);
@@ -333,11 +335,14 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream);
     if (e != hipSuccess) return hip_fail(e, "slot scan");
     // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
-    //    scan rewrites next); the last pass gathers the rectangles and tile counts and writes no keys
+    //    scan rewrites next); the tile rectangles ride along (packed, or gathered by the last pass), and
+    //    the last pass writes rectangles and tile counts in depth order but no keys
     uint32_t* rid_sorted = nullptr;
-    e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b,
-                          ws.rect, ws.rect_sorted, ws.tt_sorted, sort_scratch,
-                          &ctx->epoch, stream, nullptr, &rid_sorted);
+    const bool packable = s.TX <= 256 && s.TY <= 256;
+    const RectSort rs{ws.rect, ws.rect_sorted, ws.tt_sorted, packable ? ws.pay_a : nullptr,
+                      packable ? ws.pay_b : nullptr};
+    e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b, &rs,
+                          sort_scratch, &ctx->epoch, stream, nullptr, &rid_sorted);
     if (e != hipSuccess) return hip_fail(e, "depth sort");
     tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
@@ -373,8 +378,8 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     uint32_t* sorted_g = nullptr;
     tm.begin(stream);
     e = launch_radix_sort(ws.pkey_emit, ws.pair_g, (int64_t)total, bits_for((uint64_t)tiles), ws.pkey_b, ws.pkey_c,
-                          ws.pval_a, ws.pval_b, nullptr, nullptr, nullptr, sort_scratch, &ctx->epoch, stream,
-                          &sorted_keys, &sorted_g);
+                          ws.pval_a, ws.pval_b, nullptr, sort_scratch, &ctx->epoch, stream, &sorted_keys,
+                          &sorted_g);
     if (e != hipSuccess) return hip_fail(e, "tile sort");
     tm.end(GS_STAGE_TILE_SORT, stream);
     tm.begin(stream);

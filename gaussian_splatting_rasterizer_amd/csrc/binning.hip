@@ -272,6 +272,22 @@ __global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restric
     if (blockIdx.x == 0 && threadIdx.x < kMaxPasses) ctl[threadIdx.x] = 0u;
 }
 
+// A tile rectangle in 32 bits, for tile grids of at most 256 x 256: x0, y0,
+// width - 1, height - 1 in bytes; 0xffffffff marks an empty rectangle (culled
+// record), which no real rectangle can encode (x0 + width <= 256).
+__device__ __forceinline__ uint32_t pack_rect(uint2 r) {
+    if (r.y == 0u) return 0xffffffffu;
+    const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu, y1 = r.y >> 16;
+    return x0 | (y0 << 8) | ((x1 - x0 - 1u) << 16) | ((y1 - y0 - 1u) << 24);
+}
+
+__device__ __forceinline__ uint2 unpack_rect(uint32_t q) {
+    if (q == 0xffffffffu) return make_uint2(0u, 0u);
+    const uint32_t x0 = q & 0xffu, y0 = (q >> 8) & 0xffu, x1 = x0 + ((q >> 16) & 0xffu) + 1u,
+                   y1 = y0 + (q >> 24) + 1u;
+    return make_uint2(x0 | (y0 << 16), x1 | (y1 << 16));
+}
+
 // One radix pass (see the file header).  Blocks take their tile of keys in
 // the order they start (a ticket counter), publish their per-digit counts and
 // resolve their global offsets by looking back over earlier tiles' published
@@ -281,14 +297,18 @@ __global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restric
 // has ranked its keys, orders them in LDS, and only then looks back, so the
 // wait overlaps its own work.  A tile only waits on tiles that started before
 // it, and every tile publishes before it waits, so the chain always resolves.
-// Optional final-pass extras: rect_src != null gathers
-// rect_out[pos] = rect_src[val] (the packed tile rectangle of record `val`)
-// and tt_out[pos] = its tile count; keys_out may be null.
-__global__ __launch_bounds__(kRadixThreads) void k_onesweep(
+// Tile rectangles of the records can ride along (RectCarry): packed to 32 bits
+// from the record-order array in the first pass, reordered through LDS in a
+// second round after the keys, and unpacked with their tile counts in the last
+// pass; or, when the tile grid is too large to pack, gathered by record in the
+// last pass.  keys_out may be null.
+enum RadixMode { kPlain = 0, kCarryRect = 1, kGatherRect = 2 };
+
+template <int MODE>
+__global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift, int bits,
     uint32_t* __restrict__ ticket, const uint32_t* __restrict__ digit_tot, uint64_t* __restrict__ lookback,
-    uint32_t epoch, uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out,
-    const uint2* __restrict__ rect_src, uint2* __restrict__ rect_out, uint32_t* __restrict__ tt_out) {
+    uint32_t epoch, uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, RectCarry rc) {
     __shared__ uint32_t cnt[kRadixWaves][kMaxBins];  // per-wave counts, then per-wave block-local bases
     __shared__ uint32_t gdelta[kMaxBins];            // global position - block-local position, per digit
     __shared__ uint64_t scan_lds[kRadixThreads / 64];
@@ -355,13 +375,18 @@ __global__ __launch_bounds__(kRadixThreads) void k_onesweep(
         }
     }
     __syncthreads();
-    // block-local reorder: each digit's keys become one contiguous run
+    // block-local reorder: each digit's keys become one contiguous run; the LDS
+    // positions (< 8192) are kept two to a register for a carried second reorder
+    uint32_t lpk[kRadixItems / 2];
+#pragma unroll
+    for (int i = 0; i < kRadixItems / 2; ++i) lpk[i] = 0u;
 #pragma unroll
     for (int i = 0; i < kRadixItems; ++i) {
         if (base + i * 64 + lane >= n) continue;
         const uint32_t lp = cnt[wave][(key[i] >> shift) & mask] + rank[i];
         skey[lp] = key[i];
         sval[lp] = val[i];
+        lpk[i >> 1] |= lp << (16 * (i & 1));
     }
     // decoupled look-back over the earlier tiles' published counts
     if (dgt < nbins) {
@@ -386,49 +411,83 @@ __global__ __launch_bounds__(kRadixThreads) void k_onesweep(
     }
     __syncthreads();
     const int64_t nblk = n - bbase < kRadixTile ? n - bbase : kRadixTile;
-    if (rect_src) {
-        // final depth pass: all of the thread's gathers are in flight together
-        uint32_t pos[kRadixItems], v[kRadixItems];
+    if (MODE == kCarryRect) {
+        // keys and values out; each element's output position is parked in the value buffer
+#pragma unroll 4
+        for (int i = 0; i < kRadixItems; ++i) {
+            const int lp = i * kRadixThreads + threadIdx.x;
+            if (lp >= nblk) break;
+            const uint32_t k = skey[lp];
+            const uint32_t pos = gdelta[(k >> shift) & mask] + (uint32_t)lp;
+            if (keys_out) keys_out[pos] = k;
+            vals_out[pos] = sval[lp];
+            sval[lp] = pos;
+        }
+        // second reorder, through the key buffer: the carried rectangles, loaded only now
+        __syncthreads();
+        uint32_t q[kRadixItems];
+#pragma unroll
+        for (int i = 0; i < kRadixItems; ++i) {  // all loads in flight, then the LDS stores
+            const int64_t k = base + i * 64 + lane;
+            q[i] = 0u;
+            if (k < n) q[i] = rc.pack_src ? pack_rect(rc.pack_src[k]) : rc.pay_in[k];
+        }
+#pragma unroll
+        for (int i = 0; i < kRadixItems; ++i) {
+            if (base + i * 64 + lane >= n) continue;
+            skey[(lpk[i >> 1] >> (16 * (i & 1))) & 0xffffu] = q[i];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int i = 0; i < kRadixItems; ++i) {
+            const int lp = i * kRadixThreads + threadIdx.x;
+            if (lp >= nblk) break;
+            const uint32_t q = skey[lp];
+            const uint32_t pos = sval[lp];
+            if (rc.pay_out) {
+                rc.pay_out[pos] = q;
+            } else {
+                const uint2 r = unpack_rect(q);
+                rc.rect_out[pos] = r;
+                rc.tt_out[pos] = ((r.y & 0xffffu) - (r.x & 0xffffu)) * ((r.y >> 16) - (r.x >> 16));
+            }
+        }
+        return;
+    }
+    uint32_t pos[kRadixItems];
+#pragma unroll
+    for (int i = 0; i < kRadixItems; ++i) {
+        const int lp = i * kRadixThreads + threadIdx.x;
+        const bool ok = lp < nblk;
+        const uint32_t k = ok ? skey[lp] : 0u;
+        pos[i] = gdelta[(k >> shift) & mask] + (uint32_t)lp;
+        if (ok) {
+            if (keys_out) keys_out[pos[i]] = k;
+            vals_out[pos[i]] = sval[lp];
+        }
+    }
+    if (MODE == kGatherRect) {
+        // final depth pass without a carried rectangle: gather it by record, all gathers in flight together
         uint2 r[kRadixItems];
 #pragma unroll
         for (int i = 0; i < kRadixItems; ++i) {
             const int lp = i * kRadixThreads + threadIdx.x;
-            const bool ok = lp < nblk;
-            const uint32_t k = ok ? skey[lp] : 0u;
-            v[i] = ok ? sval[lp] : 0u;
-            pos[i] = gdelta[(k >> shift) & mask] + (uint32_t)lp;
-            if (ok && keys_out) keys_out[pos[i]] = k;
-        }
-#pragma unroll
-        for (int i = 0; i < kRadixItems; ++i) {
-            const int lp = i * kRadixThreads + threadIdx.x;
-            r[i] = lp < nblk ? rect_src[v[i]] : make_uint2(0u, 0u);
+            r[i] = lp < nblk ? rc.gather_src[sval[lp]] : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int i = 0; i < kRadixItems; ++i) {
             const int lp = i * kRadixThreads + threadIdx.x;
             if (lp >= nblk) continue;
-            vals_out[pos[i]] = v[i];
-            rect_out[pos[i]] = r[i];
-            tt_out[pos[i]] = ((r[i].y & 0xffffu) - (r[i].x & 0xffffu)) * ((r[i].y >> 16) - (r[i].x >> 16));
+            rc.rect_out[pos[i]] = r[i];
+            rc.tt_out[pos[i]] = ((r[i].y & 0xffffu) - (r[i].x & 0xffffu)) * ((r[i].y >> 16) - (r[i].x >> 16));
         }
-        return;
-    }
-#pragma unroll 4
-    for (int i = 0; i < kRadixItems; ++i) {
-        const int lp = i * kRadixThreads + threadIdx.x;
-        if (lp >= nblk) break;
-        const uint32_t k = skey[lp];
-        const uint32_t pos = gdelta[(k >> shift) & mask] + (uint32_t)lp;
-        if (keys_out) keys_out[pos] = k;
-        vals_out[pos] = sval[lp];
     }
 }
 
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const uint2* rect_src, uint2* rect_out, uint32_t* tt_out, const SortScratch& sc,
-                             uint32_t* epoch, hipStream_t st, uint32_t** keys_out, uint32_t** vals_out) {
+                             const RectSort* rs, const SortScratch& sc, uint32_t* epoch, hipStream_t st,
+                             uint32_t** keys_out, uint32_t** vals_out) {
     if (bits < 1) bits = 1;
     const int passes = (bits + kMaxDigitBits - 1) / kMaxDigitBits;
     const int dbits = (bits + passes - 1) / passes;
@@ -457,9 +516,33 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
         uint32_t* kdst = (last && !keys_out) ? nullptr : kb[p & 1];
         uint32_t* vdst = vb[p & 1];
         const uint32_t ep = next_epoch(epoch);
-        hipLaunchKernelGGL(k_onesweep, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, vsrc, n, shift, pb,
-                           sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins, sc.lookback, ep, kdst, vdst,
-                           last ? rect_src : nullptr, last ? rect_out : nullptr, last ? tt_out : nullptr);
+        RectCarry rc{};
+        if (rs && rs->pay_a) {  // carried: pack in pass 0, ping-pong, unpack in the last pass
+            if (p == 0) rc.pack_src = rs->rect;
+            else rc.pay_in = p & 1 ? rs->pay_a : rs->pay_b;
+            if (last) {
+                rc.rect_out = rs->rect_out;
+                rc.tt_out = rs->tt_out;
+            } else {
+                rc.pay_out = p & 1 ? rs->pay_b : rs->pay_a;
+            }
+            if (passes == 1) {  // a single pass packs and unpacks
+                rc.pack_src = rs->rect;
+                rc.pay_in = nullptr;
+            }
+        } else if (rs && last) {
+            rc.gather_src = rs->rect;
+            rc.rect_out = rs->rect_out;
+            rc.tt_out = rs->tt_out;
+        }
+        const int mode = (rc.pack_src || rc.pay_in) ? kCarryRect : rc.gather_src ? kGatherRect : kPlain;
+#define GSR_ONESWEEP(M)                                                                                       \
+    hipLaunchKernelGGL(k_onesweep<M>, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, vsrc, n, shift, pb, \
+                       sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins, sc.lookback, ep, kdst, vdst, rc)
+        if (mode == kCarryRect) GSR_ONESWEEP(kCarryRect);
+        else if (mode == kGatherRect) GSR_ONESWEEP(kGatherRect);
+        else GSR_ONESWEEP(kPlain);
+#undef GSR_ONESWEEP
         ksrc = kdst;
         vsrc = vdst;
     }

@@ -27,6 +27,8 @@ struct Workspace {
     uint2* rect_sorted;    // tile rectangles in depth order
     uint32_t* tt_sorted;   // tile counts in depth order
     uint32_t* offsets;     // exclusive scan of tt_sorted (also the depth sort's key scratch)
+    uint32_t* pay_a;       // packed rectangles carried through the depth sort (ping-pong)
+    uint32_t* pay_b;
     // scan / histogram scratch
     uint64_t* scan_blocks; // per-block sums (u64), then exclusive offsets
     uint64_t* scan_total;  // [0] pair count, [1] slot total, [2] scratch of the radix scans
@@ -89,19 +91,38 @@ hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Siz
 // exclusive scan of in (u32) into out (may alias); total -> *total (device u64)
 hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
                            hipStream_t st);
+// Tile rectangles that a record sort moves into sorted order with the values:
+// rect[val] becomes rect_out[pos] with its tile count tt_out[pos].  With
+// pay_a/pay_b (u32, n each) the rectangles are carried through the passes
+// packed to 32 bits (tile grids of at most 256 x 256 only); without, the last
+// pass gathers rect[val].
+struct RectSort {
+    const uint2* rect;
+    uint2* rect_out;
+    uint32_t* tt_out;
+    uint32_t* pay_a;
+    uint32_t* pay_b;
+};
+// Per-launch form of the same (device side).
+struct RectCarry {
+    const uint2* pack_src;   // pass 0: rectangles in input order, packed on load
+    const uint32_t* pay_in;  // later passes: packed rectangles in input order
+    uint32_t* pay_out;       // packed rectangles in output order (all but the last pass)
+    const uint2* gather_src; // last pass without carrying: gather rect[val]
+    uint2* rect_out;         // last pass: unpacked rectangles
+    uint32_t* tt_out;        // last pass: tile counts
+};
 // Stable LSD radix sort of (keys, vals) on bits [0, bits), digits of up to 8
 // bits; vals_in == null means identity values (the input index).  Pass p writes
 // kbuf[p & 1] / vbuf[p & 1], so these must differ from each other and from
 // keys_in/vals_in except that kbuf1/vbuf1 may alias keys_in/vals_in (consumed
-// by pass 0).  With rect_src != null the final pass also gathers
-// rect_out[pos] = rect_src[val] and tt_out[pos] = its tile count.
-// *keys_out / *vals_out receive the arrays holding the result; with
-// keys_out == null the final pass does not write keys.  Each pass takes a new
-// epoch from *epoch.
+// by pass 0).  rs (optional) moves tile rectangles along.  *keys_out /
+// *vals_out receive the arrays holding the result; with keys_out == null the
+// final pass does not write keys.  Each pass takes a new epoch from *epoch.
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const uint2* rect_src, uint2* rect_out, uint32_t* tt_out, const SortScratch& sc,
-                             uint32_t* epoch, hipStream_t st, uint32_t** keys_out, uint32_t** vals_out);
+                             const RectSort* rs, const SortScratch& sc, uint32_t* epoch, hipStream_t st,
+                             uint32_t** keys_out, uint32_t** vals_out);
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st);
 hipError_t launch_ranges(const uint32_t* sorted_keys, int64_t n, uint2* ranges, int64_t n_tiles,
                          hipStream_t st);
