@@ -52,17 +52,17 @@ def parse_args():
 
 def stage_bytes(stage, c):
     """Algorithmic HBM bytes per launch of a stage: every array the stage must
-    read or write once, at its element size (the counts behind each term are in
-    DESIGN.md)."""
+    read or write once, at its element size (the per-record and per-pair terms
+    are listed in the design doc)."""
     G, V, d, P, VG = c["G"], c["V"], c["d"], c["P"], c["G"] * c["V"]
-    if stage == "project":       # Gaussian parameters in; records, depth keys, tile counts out
-        return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (48 + 4 + 4)
-    if stage == "depth_sort":    # slot scan (8 B), histogram (4 B), 4 passes of key+value in and out, rect gather
-        return VG * (8 + 4 + 4 * 16 - 4 - 4 + 8 + 12)
+    if stage == "project":       # Gaussian parameters in; 40-byte record, rectangle, depth key, tile count out
+        return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (40 + 8 + 4 + 4)
+    if stage == "depth_sort":    # slot scan 8, histogram 4, pass 0 (key+rect in, key+id+rect out) 24,
+        return VG * (8 + 4 + 24 + 2 * 24 + 28)   # passes 1-2 24 each, pass 3 (-> id, rect, tile count) 28
     if stage == "scan":
         return VG * 8
-    if stage == "emit":          # per record: id, rect, offset in; per pair: tile key and Gaussian out
-        return VG * (4 + 8 + 4) + P * 8
+    if stage == "emit":          # per record: id, rect, tile count, offset in; per pair: tile key and Gaussian out
+        return VG * (4 + 8 + 4 + 4) + P * 8
     if stage == "tile_sort":     # histogram + 2 passes of key+value in and out
         return P * (4 + 2 * 16)
     if stage == "ranges":

@@ -139,7 +139,8 @@ GSR_API gs_status gs_project(gs_context* ctx, const gs_gaussians* scene, const g
 /* Tile binning and contributor sorting: order (Gaussian, view) records by
  * depth, emit one (tile, Gaussian) pair per covered tile, stable-sort the pairs
  * by tile and build per-tile ranges.  Blocks the host once to read the pair
- * count (written to *n_pairs_out, which may be null).  Returns
+ * count (through a pinned host word the context allocates on its first call;
+ * written to *n_pairs_out, which may be null).  Returns
  * GS_ERR_WORKSPACE_TOO_SMALL (with the count) when it exceeds max_pairs; the
  * caller then creates a larger context and starts again from gs_project. */
 GSR_API gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out);
@@ -148,7 +149,9 @@ GSR_API gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_p
  *   color      [n_views, height, width, 3] rendered colour incl. background
  *   T_final    [n_views, height, width]    final transmittance
  *   n_contrib  [n_views, height, width]    accepted contributions (int32)
- * The rendered colour is also kept in the workspace for gs_score_replay. */
+ * The rendered colour is also kept in the workspace for gs_score_replay, with
+ * one byte per processed list entry marking the 8x8 pixel blocks in which some
+ * pixel's state changed there (the replay walks only those entries). */
 GSR_API gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_contrib,
                     hipStream_t stream);
 
@@ -175,8 +178,9 @@ GSR_API gs_status gs_debug_exp2(const float* in, float* out, int64_t n, hipStrea
  * (`bytes` must be at least the array size; the call fails otherwise):
  *   GS_EXPORT_RECORDS   after gs_project:  [3, n_views*n, 4] float32, planes
  *       {mx, my, qa, qb}, {qc, opacity, pre_r, pre_g},
- *       {pre_b, <pair offset bits>, <x0 | y0 << 16>, <x1 | y1 << 16>}, record
- *       index v*n + g, qa..qc scaled so that the Gaussian weight at offset
+ *       {pre_b, <entry box: two binary16 half-widths, x low>, <x0 | y0 << 16>,
+ *       <x1 | y1 << 16>} (tile rectangle [x0, x1) x [y0, y1)), record index
+ *       v*n + g, qa..qc scaled so that the Gaussian weight at offset
  *       (dx, dy) = pixel - centre is 2^(qa dx^2 + qb dx dy + qc dy^2); culled
  *       records are all zero
  *   GS_EXPORT_DEPTH_KEYS after gs_project: [n_views*n] uint32 depth bits
