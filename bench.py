@@ -44,6 +44,9 @@ def parse_args():
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                    help="budget of rendering work for the CPU oracle sample (0 disables)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sweep", action="store_true",
+                   help="instead of the benchmark line: view-count / resolution scaling (4, 8, 16, 32 views at "
+                        "256x448 and 512x960 over a fixed Gaussian set), one JSON line per point")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="before the steps, copy a buffer of this many MiB once (untimed), so that "
                         "hardware byte counters can be scaled against a copy of known size")
@@ -124,6 +127,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
+    if args.sweep:
+        return sweep(args, dev, stream)
 
     t_gen = time.perf_counter()
     sc = scenes.make_scene(args.config)
@@ -235,6 +240,63 @@ def main():
     if not args.no_cpu_baseline and args.cpu_baseline_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(sc, args.cpu_baseline_seconds)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+RENDER_STAGES = ("project", "depth_sort", "scan", "emit", "tile_sort", "ranges", "render")
+SCORE_STAGES = ("replay", "finalize")
+
+
+def sweep(args, dev, stream):
+    """View-count and resolution scaling of the whole step over a fixed Gaussian
+    set (the ReSplat-like pixel-aligned Gaussians of 8 source views), with the
+    score-replay overhead = (replay + gather + tokens) / (project .. render)."""
+    import numpy as np
+    import torch
+
+    import scenes
+    from gaussian_splatting_rasterizer_amd import binding
+
+    steps = max(1, min(args.steps, 10))
+    for (W, H) in ((448, 256), (960, 512)):
+        for V in (4, 8, 16, 32):
+            sc = scenes.view_sweep(n_views=V, W=W, H=H)
+            with torch.cuda.stream(stream):
+                r = binding.rasterizer_for_scene(sc, device=dev)
+                obs = torch.from_numpy(0.5 + sc.pixel_noise).to(dev)
+                r.project_and_bin()
+                r._alloc(int(r.n_pairs * 1.1) + 4096)
+                outputs = r.new_outputs()
+                tokens = torch.empty((sc.n, 9 + 3 * sc.d), dtype=torch.float32, device=dev)
+                for _ in range(2):
+                    r.step(obs, outputs, tokens)
+                stream.synchronize()
+                binding.gs_profile_enable(r.ctx, True)
+                binding.gs_profile_read(r.ctx)
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    r.step(obs, outputs, tokens)
+                stream.synchronize()
+                elapsed = (time.perf_counter() - t0) / steps
+                prof = binding.gs_profile_read(r.ctx)
+                binding.gs_profile_enable(r.ctx, False)
+                K = int(outputs[2].to(torch.int64).sum().item())
+                P = int(r.n_pairs)
+                r.close()
+            del r, obs, outputs, tokens
+            torch.cuda.empty_cache()
+            st = {k: ms / max(cnt, 1) for k, (ms, cnt) in prof.items()}
+            render_ms = sum(st[k] for k in RENDER_STAGES)
+            score_ms = sum(st[k] for k in SCORE_STAGES)
+            pix = V * H * W
+            print(json.dumps({"sweep": "views_resolution", "views": V, "width": W, "height": H,
+                              "gaussians": sc.n, "pairs": P, "contributions": K,
+                              "ms_per_step": round(1e3 * elapsed, 4), "render_path_ms": round(render_ms, 4),
+                              "score_ms": round(score_ms, 4), "score_overhead": round(score_ms / render_ms, 4),
+                              "mpix_per_s": round(pix / elapsed / 1e6, 2),
+                              "ns_per_pixel": round(1e9 * elapsed / pix, 3),
+                              "stages_ms": {k: round(v, 4) for k, v in st.items()}}), flush=True)
+            del sc
     return 0
 
 

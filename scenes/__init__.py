@@ -33,7 +33,7 @@ import math
 import numpy as np
 
 __all__ = ["Scene", "make_scene", "CONFIG_NAMES", "c1_occlusion_toy", "c2_resplat_step",
-           "c3_atsplat_compact", "c4_dense_pixel_aligned", "c5_multiview_layers"]
+           "c3_atsplat_compact", "c4_dense_pixel_aligned", "c5_multiview_layers", "view_sweep"]
 
 SH_C0 = 0.28209479177387814  # 1 / (2 sqrt(pi)); used only to draw degree-0 colours
 
@@ -255,6 +255,28 @@ def c5_multiview_layers(seed=5, n_views=8, W=448, H=256, n=500_000) -> Scene:
     return _finish("c5_multiview_layers", rng, means, quats, log_scales, logits, sh, 3, cams, W, H,
                    {"layer_counts": counts, "layer_depths": depths, "layer_area_fracs": fracs,
                     "three_layer_pixel_fraction": fracs[2]})
+
+
+def view_sweep(n_views=8, W=448, H=256, n_sources=8, seed=6) -> Scene:
+    """View/resolution scaling scene: the Gaussians of the ReSplat-like step
+    (one pixel-aligned Gaussian per pixel of `n_sources` source views 0.1 m apart,
+    depth U(1, 10), log-scales N(-4.5, 0.5), logits N(0, 1), SH degree 3 N(0, 0.2^2))
+    rendered by `n_views` target cameras spread evenly over the same baseline, so
+    the Gaussian set is fixed while the view count and resolution vary."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f = float(W)
+    src = np.stack([_camera((0.1 * (i - (n_sources - 1) / 2.0), 0, 0), f, W, H) for i in range(n_sources)])
+    half = 0.05 * (n_sources - 1)
+    xs = np.linspace(-half, half, n_views) if n_views > 1 else np.zeros(1)
+    cams = np.stack([_camera((float(x), 0, 0), f, W, H) for x in xs])
+    means = _pixel_aligned(rng, src, W, H, f, 1.0, 10.0)
+    n = means.shape[0]
+    quats = _unit_quats(rng, n)
+    log_scales = rng.normal(-4.5, 0.5, size=(n, 3))
+    logits = rng.normal(0.0, 1.0, size=n)
+    sh = rng.normal(0.0, 0.2, size=(n, 16, 3))
+    return _finish("view_sweep", rng, means, quats, log_scales, logits, sh, 3, cams, W, H,
+                   {"placement": "pixel-aligned", "depth": [1, 10], "sources": n_sources})
 
 
 CONFIG_NAMES = {
