@@ -177,13 +177,13 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->pval_b = (uint32_t*)take(4 * P);
     ws->pair_g = (uint32_t*)take(4 * P);
     ws->ranges = (uint2*)take(8 * tiles);
-    ws->tile_stop = (uint64_t*)take(8 * tiles);
     ws->partials = (float4*)take(32 * P);
     ws->gv_sums = (float4*)take(32 * VG);
     ws->rec_masks = (uint64_t*)take(16 * ((VG + 63) / 64));
     ws->pixel = (float4*)take(16 * pixels);
     ws->pixel_stats = (uint2*)take(8 * pixels);
     ws->events = (uint8_t*)take(P);
+    ws->slot_bits = (uint32_t*)take(4 * ((P + 31) / 32));
     return (off + 255) & ~(size_t)255;
 }
 
@@ -397,8 +397,8 @@ gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_co
     if ((color && !aligned(color, 4)) || (T_final && !aligned(T_final, 4)) || (n_contrib && !aligned(n_contrib, 4)))
         return fail(GS_ERR_INVALID_ARGUMENT, "misaligned output pointer");
     ctx->timer.begin(stream);
-    hipError_t e = launch_render(ctx->s, ctx->ws, ctx->sorted_g, ctx->params.background, color, T_final, n_contrib,
-                                 stream);
+    hipError_t e = launch_render(ctx->s, ctx->ws, ctx->sorted_g, ctx->n_pairs, ctx->params.background, color,
+                                 T_final, n_contrib, stream);
     if (e != hipSuccess) return hip_fail(e, "render");
     ctx->timer.end(GS_STAGE_RENDER, stream);
     ctx->state = kRendered;

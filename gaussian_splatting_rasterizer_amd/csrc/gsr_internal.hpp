@@ -43,7 +43,6 @@ struct Workspace {
     uint32_t* pval_b;
     uint32_t* pair_g;      // Gaussian of each emitted pair, depth order
     uint2* ranges;         // per tile [start, end)
-    uint64_t* tile_stop;   // per tile: (depth bits, Gaussian) key of the first entry the replay skipped
     float4* partials;      // per slot: {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix}
     float4* gv_sums;       // per reached record: {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix}
     uint64_t* rec_masks;   // per 64 records: {live mask, reached mask}
@@ -51,6 +50,7 @@ struct Workspace {
     uint2* pixel_stats;    // per pixel: entries evaluated, entries past the distance cut
     uint8_t* events;       // per sorted pair the render processed: bit w set when some pixel of wave w
                            // contributed or saturated at that entry
+    uint32_t* slot_bits;   // per slot: set when the replay wrote the slot's partial (cleared by the render)
 };
 
 struct Sizes {
@@ -126,8 +126,8 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st);
 hipError_t launch_ranges(const uint32_t* sorted_keys, int64_t n, uint2* ranges, int64_t n_tiles,
                          hipStream_t st);
-hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float bg[3],
-                         float* color, float* T_final, int32_t* n_contrib, hipStream_t st);
+hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
+                         const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st);
 hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* observed,
                          float eps, float den_min, hipStream_t st);
 hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, hipStream_t st);

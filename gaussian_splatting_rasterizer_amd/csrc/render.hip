@@ -30,7 +30,12 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                                                 float bg0, float bg1, float bg2, float* __restrict__ color,
                                                 float* __restrict__ T_out, int32_t* __restrict__ n_out,
                                                 float4* __restrict__ pixel, uint2* __restrict__ pixel_stats,
-                                                uint8_t* __restrict__ events) {
+                                                uint8_t* __restrict__ events, uint32_t* __restrict__ slot_bits,
+                                                int64_t n_slot_words) {
+    // clear the replay's written-slot bits (a grid-stride share per block)
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slot_words;
+         i += (int64_t)gridDim.x * blockDim.x)
+        slot_bits[i] = 0u;
     __shared__ float4 s0[kRenderBatch];   // {mx, my, qa, qb}
     __shared__ float4 s1[kRenderBatch];   // {qc, opacity, colour r, colour g}
     __shared__ float s2[kRenderBatch];    // colour b
@@ -153,13 +158,13 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     pixel_stats[pix] = make_uint2(stop != 0xffffffffu ? stop - rg.x + 1u : rg.y - rg.x, n_near);
 }
 
-hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float bg[3], float* color,
-                         float* T_final, int32_t* n_contrib, hipStream_t st) {
+hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
+                         const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st) {
     const int64_t tiles = (int64_t)s.V * s.T;
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1,
                        ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel,
-                       ws.pixel_stats, ws.events);
+                       ws.pixel_stats, ws.events, ws.slot_bits, (int64_t)((n_pairs + 31) / 32));
     return hipGetLastError();
 }
 

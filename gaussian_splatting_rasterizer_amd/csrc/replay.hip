@@ -28,13 +28,12 @@
 // slot is the record's slot base (a scan of tile counts in record order) plus
 // the tile's row-major index in the record's rectangle, so one Gaussian's
 // slots are contiguous per view and adjacent Gaussians' slots are adjacent.
-// Pairs after the tile's early termination are never written; tile_stop keeps
-// the (depth bits, Gaussian) list key at which each tile stopped.
+// Only pairs at which some wave had an event are written (every other pair's
+// partial is zero), and each written slot sets its bit in slot_bits.
 //
-// k_gather_slots: per record (record order, coalesced), the sums of the pairs
-// the replay reached, written only for records with a reached pair; plus, per
-// 64 records, a mask of the records that are live (not culled) and one of those
-// with a reached pair.
+// k_gather_slots: per record (record order), the sums of the pairs the replay
+// wrote, stored only for records with such a pair; plus, per 64 records, a
+// mask of the records that are live (not culled) and one of those reached.
 // k_tokens: one thread per Gaussian, in float64
 //     q_v = eps + W_v,  Q = eps + sum_v q_v,  gamma_v = q_v / Q
 //     b_mu = sum_v gamma_v J_v^T s_mu_v = (1/Q) sum_v J_v^T (conic_v U_mu_v)
@@ -79,13 +78,12 @@ __device__ __forceinline__ float wave_reduce8(const float (&x)[8], int lane) {
 }
 
 __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
-                                                const uint32_t* __restrict__ depth_key,
                                                 const uint32_t* __restrict__ slot_base,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
                                                 const float2* __restrict__ rec2, const uint2* __restrict__ rect,
                                                 int64_t G, int T, int TX, int W, int H, const float4* __restrict__ pixel, const float* __restrict__ observed,
                                                 const uint8_t* __restrict__ events, float eps, float den_min,
-                                                float4* __restrict__ partials, uint64_t* __restrict__ tile_stop) {
+                                                float4* __restrict__ partials, uint32_t* __restrict__ slot_bits) {
     __shared__ float4 s0[kReplayBatch];
     __shared__ float4 s1[kReplayBatch];
     __shared__ float s2[kReplayBatch];
@@ -211,7 +209,9 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             }
         }
         __syncthreads();
-        if (threadIdx.x < 2 * cnt) {
+        // one partial per entry at which some wave had an event (every other entry's partial is zero),
+        // flagged in the slot bits for the gather
+        if (threadIdx.x < 2 * cnt && s_evb[threadIdx.x >> 1] != 0) {
             const int j = threadIdx.x >> 1, h = threadIdx.x & 1;
             float4 acc = *reinterpret_cast<const float4*>(&sp[0][j][4 * h]);
 #pragma unroll
@@ -231,16 +231,10 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 const uint32_t m = s_mask[j];
                 acc = make_float4(m & 1u ? acc.x : 0.0f, m & 2u ? acc.y : 0.0f, m & 4u ? acc.z : 0.0f, acc.w);
             }
-            partials[2 * (int64_t)s_slot[j] + h] = acc;
+            const uint32_t slot = s_slot[j];
+            partials[2 * (int64_t)slot + h] = acc;
+            if (h == 0) atomicOr(&slot_bits[slot >> 5], 1u << (slot & 31u));
         }
-    }
-    if (threadIdx.x == 0) {
-        uint64_t stop = ~0ull;
-        if (base < rg.y) {
-            const uint32_t g = sorted_g[base];
-            stop = ((uint64_t)depth_key[vG + g] << 32) | g;
-        }
-        tile_stop[tile] = stop;
     }
 }
 
@@ -248,10 +242,10 @@ hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* so
                          float eps, float den_min, hipStream_t st) {
     const int64_t tiles = (int64_t)s.V * s.T;
     if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.depth_key,
+    hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,
                        ws.slot_base, ws.rec0, ws.rec1,
                        ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, ws.events, eps, den_min,
-                       ws.partials, ws.tile_stop);
+                       ws.partials, ws.slot_bits);
     return hipGetLastError();
 }
 
@@ -297,131 +291,58 @@ __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */,
 // consecutive records' slots are adjacent, so reads and writes are coalesced.
 // Tile lists are ordered by the (depth bits, Gaussian) key, so a pair was
 // reached iff its key is below the key at which its tile's replay stopped.
-// The partial slots of consecutive records form one contiguous range (slot_base
-// is a scan in record order).  Each wave takes 64 consecutive records and
-// streams their slot range through a wave-private LDS buffer, 64 slots at a
-// time: lane i finds the record of slot c0 + i by binary search over the
-// wave's slot bases and fetches the slot's partials only if the replay reached
-// that pair (else zeros), so loads are coalesced and unreached slots cost no
-// HBM traffic; each lane then sums its own record's slots from LDS, in slot
-// order.  Waves synchronise only with themselves.
+// The slot gather: one thread per record, in record order.  A record's slots
+// [slot_base, slot_base + tile count) are contiguous and the replay set a bit
+// for every slot it wrote, so each thread reads the one or two bit words of its
+// range and adds the partials of the set bits in slot order.
 constexpr int kGatherThreads = 256;
-constexpr int kGatherWaves = kGatherThreads / 64;
 
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uint32_t G, int T, int TX,
-                                                                 const uint2* __restrict__ rect,
-                                                                 const uint32_t* __restrict__ depth_key,
+__global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
+                                                                 const uint32_t* __restrict__ tiles_touched,
                                                                  const uint32_t* __restrict__ slot_base,
-                                                                 const uint64_t* __restrict__ tile_stop,
+                                                                 const uint32_t* __restrict__ slot_bits,
                                                                  const float4* __restrict__ partials,
                                                                  float4* __restrict__ gv_sums,
                                                                  uint64_t* __restrict__ rec_masks) {
-    __shared__ float4 buf[kGatherWaves][128];        // 64 slots x 2 float4 per wave
-    __shared__ uint32_t s_sb[kGatherWaves][64];      // first slot of each record
-    __shared__ uint32_t s_tile0[kGatherWaves][64];   // global tile id of the rectangle's first tile
-    __shared__ uint32_t s_w[kGatherWaves][64];       // rectangle width in tiles
-    __shared__ float s_rw[kGatherWaves][64];         // 1 / width
-    __shared__ uint64_t s_key[kGatherWaves][64];     // (depth bits, Gaussian) list key
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t r0 = (int64_t)blockIdx.x * kGatherThreads + wave * 64;
-    if (r0 >= VG) return;
-    const int64_t rid = r0 + lane;
-    const int last = (int)(VG - r0 < 64 ? VG - r0 : 64) - 1;
-    uint32_t tt = 0, sb = 0;
-    bool live = false;
-    if (rid < VG) {
-        const uint2 rc = rect[rid];
-        sb = slot_base[rid];
-        uint32_t w = 1, tile0 = 0;
-        uint64_t key = 0;
-        live = rc.y != 0u;
-        if (live) {
-            const uint32_t v = (uint32_t)rid / G;
-            const uint32_t g = (uint32_t)rid - v * G;
-            key = ((uint64_t)depth_key[rid] << 32) | (uint64_t)g;
-            const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16;
-            w = (rc.y & 0xffffu) - x0;
-            tt = w * ((rc.y >> 16) - y0);
-            tile0 = v * (uint32_t)T + y0 * (uint32_t)TX + x0;
-        }
-        s_sb[wave][lane] = sb;
-        s_tile0[wave][lane] = tile0;
-        s_w[wave][lane] = w;
-        s_rw[wave][lane] = 1.0f / (float)w;
-        s_key[wave][lane] = key;
-    }
-    const uint32_t first = (uint32_t)__builtin_amdgcn_readfirstlane((int)sb);
-    const uint32_t end = (uint32_t)__builtin_amdgcn_readlane((int)(sb + tt), last);
-    wave_lds_sync();
+    const int64_t rid = (int64_t)blockIdx.x * kGatherThreads + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    if (rid - lane >= VG) return;  // the whole wave is past the end
+    bool live = false, reached = false;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
-    bool reached = false;
-    for (uint32_t c0 = first; c0 < end; c0 += 64) {
-        const uint32_t s = c0 + (uint32_t)lane;
-        bool reach = false;
-        if (s < end) {
-            int lo = 0, hi = last;
-            while (lo < hi) {  // last record whose first slot is <= s: the one holding s
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_sb[wave][mid] <= s) lo = mid;
-                else hi = mid - 1;
+    if (rid < VG) {
+        const uint32_t tt = tiles_touched[rid];
+        live = tt != 0u;  // culled records touch no tile
+        if (live) {
+            const uint32_t s0 = slot_base[rid], s1 = s0 + tt;
+            for (uint32_t w = s0 >> 5; w <= (s1 - 1u) >> 5; ++w) {
+                uint32_t bits = slot_bits[w];
+                const uint32_t lo = s0 > 32u * w ? s0 - 32u * w : 0u;
+                const uint32_t hi = s1 < 32u * w + 32u ? s1 - 32u * w : 32u;
+                bits &= (hi >= 32u ? ~0u : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
+                while (bits) {
+                    const uint32_t slot = 32u * w + (uint32_t)__builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    const float4 p0 = partials[2 * (int64_t)slot];
+                    const float4 p1 = partials[2 * (int64_t)slot + 1];
+                    reached = true;
+                    a.x += p0.x;
+                    a.y += p0.y;
+                    a.z += p0.z;
+                    a.w += p0.w;
+                    b.x += p1.x;
+                    b.y += p1.y;
+                    b.z += p1.z;
+                    b.w += p1.w;
+                }
             }
-            const uint32_t j = s - s_sb[wave][lo];
-            const uint32_t w = s_w[wave][lo];
-            // row j / w: a float estimate, off by at most one, then corrected
-            uint32_t q = (uint32_t)((float)j * s_rw[wave][lo]);
-            int32_t rem = (int32_t)(j - q * w);
-            if (rem < 0) {
-                --q;
-                rem += (int32_t)w;
-            } else if (rem >= (int32_t)w) {
-                ++q;
-                rem -= (int32_t)w;
-            }
-            reach = s_key[wave][lo] < tile_stop[s_tile0[wave][lo] + q * (uint32_t)TX + (uint32_t)rem];
         }
-        const uint64_t rmask = __ballot(reach);
-        if (rmask == 0ull) continue;  // nothing in this chunk was reached
-        if (reach) {
-            buf[wave][2 * lane] = partials[2 * (int64_t)s];
-            buf[wave][2 * lane + 1] = partials[2 * (int64_t)s + 1];
-        }
-        wave_lds_sync();
-        // this record's reached slots in the chunk, in slot order
-        const uint32_t s_lo = sb > c0 ? sb - c0 : 0u;
-        const uint32_t s_hi = (sb + tt < c0 + 64) ? (sb + tt > c0 ? sb + tt - c0 : 0u) : 64u;
-        uint64_t m = 0ull;
-        if (s_hi > s_lo) {
-            const uint64_t below_hi = s_hi >= 64 ? ~0ull : ((1ull << s_hi) - 1ull);
-            m = rmask & below_hi & ~((1ull << s_lo) - 1ull);
-        }
-        while (m) {
-            const int i = __builtin_ctzll(m);
-            m &= m - 1ull;
-            const float4 q0 = buf[wave][2 * i];
-            const float4 q1 = buf[wave][2 * i + 1];
-            reached = true;
-            a.x += q0.x;
-            a.y += q0.y;
-            a.z += q0.z;
-            a.w += q0.w;
-            b.x += q1.x;
-            b.y += q1.y;
-            b.z += q1.z;
-            b.w += q1.w;
-        }
-        wave_lds_sync();
     }
+    // live / reached masks of the wave's 64 records (blocks start at multiples of 64)
     const uint64_t live_mask = __ballot(live);
     const uint64_t reached_mask = __ballot(reached);
     if (lane == 0) {
-        rec_masks[2 * (r0 >> 6)] = live_mask;
-        rec_masks[2 * (r0 >> 6) + 1] = reached_mask;
+        rec_masks[2 * ((rid - lane) >> 6)] = live_mask;
+        rec_masks[2 * ((rid - lane) >> 6) + 1] = reached_mask;
     }
     if (reached) {
         gv_sums[2 * rid] = a;
@@ -432,8 +353,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG, uin
 hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
     hipLaunchKernelGGL(k_gather_slots, dim3((unsigned)((s.VG + kGatherThreads - 1) / kGatherThreads)),
-                       dim3(kGatherThreads), 0, st, s.VG, (uint32_t)s.G, s.T, s.TX, ws.rect, ws.depth_key,
-                       ws.slot_base, ws.tile_stop, ws.partials, ws.gv_sums, ws.rec_masks);
+                       dim3(kGatherThreads), 0, st, s.VG, ws.tiles_touched, ws.slot_base, ws.slot_bits, ws.partials,
+                       ws.gv_sums, ws.rec_masks);
     return hipGetLastError();
 }
 
