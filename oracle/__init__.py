@@ -7,7 +7,8 @@ imports it; the two meet only through the seeded inputs of ``scenes``.
 
 The arithmetic lives in ``gsr_oracle.c`` (plain C, float64 values, float32
 canonical decisions, brute-force lists, explicit back-to-front suffix, literal
-score sums, Jacobi eigenvalues); this module builds it with gcc and wraps it
+score sums, Jacobi eigenvalues, an explicit chain-rule renderer backward);
+this module builds it with gcc and wraps it
 with ctypes.  Everything here follows the page "Research Proposal: Renderer
 Score Tokens for Recurrent Gaussian Splatting" (Two-Stage Algorithm, Exact
 Score Operators, Final Token and Updater).
@@ -90,6 +91,9 @@ def _load():
         lib.orc_set_sh64.argtypes = [P, I32, I32, I32, F64]
         lib.orc_set_mean2d64.argtypes = [P, I32, I32, F64, F64]
         lib.orc_set_mean3d64.argtypes = [P, I32, P]
+        lib.orc_set_params64.argtypes = [P, I32, P]
+        lib.orc_backward.argtypes = [P, P, P, P]
+        lib.orc_sh_basis_grad64.argtypes = [P, I64, I32, P]
         lib.orc_num_threads.restype = I32
         _lib = lib
         return lib
@@ -121,6 +125,15 @@ def sh_basis64(dirs: np.ndarray, d: int) -> np.ndarray:
     dirs = np.ascontiguousarray(dirs, dtype=np.float64).reshape(-1, 3)
     out = np.empty((dirs.shape[0], d), dtype=np.float64)
     lib.orc_sh_basis64(_ptr(dirs), dirs.shape[0], d, _ptr(out))
+    return out
+
+
+def sh_basis_grad64(dirs: np.ndarray, d: int) -> np.ndarray:
+    """d B_k / d(x, y, z) of the SH polynomials, [n, d, 3] (no unit-norm projection)."""
+    lib = _load()
+    dirs = np.ascontiguousarray(dirs, dtype=np.float64).reshape(-1, 3)
+    out = np.empty((dirs.shape[0], d, 3), dtype=np.float64)
+    lib.orc_sh_basis_grad64(_ptr(dirs), dirs.shape[0], d, _ptr(out))
     return out
 
 
@@ -265,6 +278,31 @@ class OracleScene:
                     for tx in range(x0, x1):
                         out.add(v * self.T + ty * self.TX + tx)
         return np.array(sorted(out), dtype=np.int64)
+
+    # -- renderer backward -----------------------------------------------------
+    def backward(self, grad_color, with_image_sums=False):
+        """Vector-Jacobian product of the colour image with `grad_color` [V,H,W,3]:
+        gradients [G, 11 + 3 d] = [mean 3, quaternion 4, scale 3, opacity 1, SH d*3]
+        (float64).  With `with_image_sums`, also the per-(view, Gaussian) image-space
+        sums [V, G, 9] = dL/d(mx, my, ca, cb, cc, o, c_r, c_g, c_b)."""
+        if self.n_pairs is None:
+            self.build_lists()
+        gC = np.ascontiguousarray(grad_color, dtype=np.float32)
+        assert gC.shape == (self.V, self.H, self.W, 3)
+        out = np.empty((self.G, 11 + 3 * self.d), dtype=np.float64)
+        g2d = np.empty((self.V, self.G, 9), dtype=np.float64) if with_image_sums else None
+        self.lib.orc_backward(self.handle, _ptr(gC), _ptr(out), _ptr(g2d) if with_image_sums else None)
+        return (out, g2d) if with_image_sums else out
+
+    def params64(self, g) -> np.ndarray:
+        """The 11 float64 parameter values of Gaussian g: mean, quaternion, scale, opacity."""
+        return np.concatenate([self._keep[0][g], self._keep[1][g], self._keep[2][g],
+                               self._keep[3][g:g + 1]]).astype(np.float64)
+
+    def set_params64(self, g, prm):
+        prm = np.ascontiguousarray(prm, dtype=np.float64)
+        assert prm.shape == (11,)
+        self.lib.orc_set_params64(self.handle, int(g), _ptr(prm))
 
     # -- finite-difference probes ---------------------------------------------
     def values_reset(self):

@@ -37,6 +37,12 @@
  *    never by the subtraction formula of the replay.
  *  - Scores are the literal per-pixel sums of the score operators; tokens are
  *    the literal cross-view formulas; eigenvalues by cyclic Jacobi rotations.
+ *  - The renderer backward (the gradient of the image through the composite,
+ *    the 2D Gaussian, the EWA projection, the covariance from quaternion and
+ *    scales, and the SH colour including its view direction) is an explicit
+ *    chain rule per contribution and per (Gaussian, view), in float64, with the
+ *    same frozen decisions; the forward formulas it differentiates are those
+ *    of the ATSplat summary page's 3DGS primitive.
  */
 #include <float.h>
 #include <math.h>
@@ -235,6 +241,7 @@ typedef struct {
     float* opac;   /* [G] */
     float* sh;     /* [G,d,3] */
     double* sh64;  /* [G,d,3] value copy (finite-difference probes edit it) */
+    double* p64;   /* [G,11] value copies of mean (3), quaternion (4), scale (3), opacity (1) */
     float* cams;   /* [V,16] */
     rec32* r32;    /* [V*G] */
     rec64* r64;    /* [V*G] */
@@ -374,82 +381,142 @@ static void project32(const scene* s, int g, int v, rec32* r)
 }
 
 /* float64 values of one (Gaussian, view): same formulas as above, no rounding to float32 */
-static void project64(const scene* s, int g, int v, const rec32* r32, rec64* r)
+static void params64_from_inputs(scene* s)
 {
-    memset(r, 0, sizeof *r);
-    const float* mu32 = s->means + 3 * (int64_t)g;
-    const float* qi = s->quats + 4 * (int64_t)g;
-    const float* sc = s->scales + 3 * (int64_t)g;
-    const double* sh = s->sh64 + (int64_t)g * s->d * 3;
-    const float* cam = s->cams + 16 * v;
-    double R[9], t[3];
-    for (int i = 0; i < 9; ++i) R[i] = cam[i];
-    for (int i = 0; i < 3; ++i) t[i] = cam[9 + i];
-    double fx = cam[12], fy = cam[13], cx = cam[14], cy = cam[15];
-    double mu[3] = {mu32[0], mu32[1], mu32[2]};
-    double tc[3];
-    for (int i = 0; i < 3; ++i) tc[i] = R[3 * i] * mu[0] + R[3 * i + 1] * mu[1] + R[3 * i + 2] * mu[2] + t[i];
-    double tx = tc[0], ty = tc[1], tz = tc[2];
-    r->opac = s->opac[g];
-    if (r32->culled) return;
+    for (int64_t g = 0; g < s->G; ++g) {
+        double* prm = s->p64 + 11 * g;
+        for (int i = 0; i < 3; ++i) prm[i] = s->means[3 * g + i];
+        for (int i = 0; i < 4; ++i) prm[3 + i] = s->quats[4 * g + i];
+        for (int i = 0; i < 3; ++i) prm[7 + i] = s->scales[3 * g + i];
+        prm[10] = s->opac[g];
+    }
+}
 
-    double qn = sqrt((double)qi[0] * qi[0] + (double)qi[1] * qi[1] + (double)qi[2] * qi[2] + (double)qi[3] * qi[3]);
-    double w = qi[0] / qn, x = qi[1] / qn, y = qi[2] / qn, z = qi[3] / qn;
-    double Rq[9] = {1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y),
-                    2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x),
-                    2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)};
-    double S3[9], Tm[9], Cc[9];
+/* Every float64 intermediate of one (Gaussian, view) projection, kept for the
+ * backward: EWA splatting of the 3D covariance R_q S S^T R_q^T through the
+ * camera rotation and the perspective Jacobian (evaluated at the centre
+ * clamped to 1.3x the half field of view), plus the 0.3 px^2 dilation. */
+typedef struct {
+    double R[9], t[3], fx, fy, cx, cy;
+    double tc[3];          /* camera-space centre */
+    double qn, qh[4];      /* quaternion norm and the normalised quaternion (w, x, y, z) */
+    double Rq[9], sc[3];   /* rotation of the quaternion, axis scales */
+    double M[9];           /* Rq diag(sc) */
+    double S3[9], Cc[9];   /* world and camera covariance */
+    double uxc, uyc;       /* clamped tan-space centre */
+    int clip_x, clip_y;    /* 1 where that clamp is active */
+    double Jc[6];          /* perspective Jacobian at the clamped centre, 2x3 row-major */
+    double a, b, c, det;   /* dilated 2D covariance [[a, b], [b, c]] and its determinant */
+    double dir[3], len;    /* unit view direction from the camera centre, distance */
+} fwd64;
+
+static void forward64(const scene* s, int g, int v, fwd64* f)
+{
+    const double* prm = s->p64 + 11 * (int64_t)g;
+    const double* mu = prm;      /* value copies (float32 inputs unless a probe moved them) */
+    const double* qi = prm + 3;
+    const float* cam = s->cams + 16 * v;
+    for (int i = 0; i < 9; ++i) f->R[i] = cam[i];
+    for (int i = 0; i < 3; ++i) f->t[i] = cam[9 + i];
+    f->fx = cam[12];
+    f->fy = cam[13];
+    f->cx = cam[14];
+    f->cy = cam[15];
+    const double* R = f->R;
+    for (int i = 0; i < 3; ++i)
+        f->tc[i] = R[3 * i] * mu[0] + R[3 * i + 1] * mu[1] + R[3 * i + 2] * mu[2] + f->t[i];
+    const double tx = f->tc[0], ty = f->tc[1], tz = f->tc[2];
+
+    f->qn = sqrt(qi[0] * qi[0] + qi[1] * qi[1] + qi[2] * qi[2] + qi[3] * qi[3]);
+    for (int i = 0; i < 4; ++i) f->qh[i] = qi[i] / f->qn;
+    const double w = f->qh[0], x = f->qh[1], y = f->qh[2], z = f->qh[3];
+    double* Rq = f->Rq;
+    Rq[0] = 1 - 2 * (y * y + z * z);
+    Rq[1] = 2 * (x * y - w * z);
+    Rq[2] = 2 * (x * z + w * y);
+    Rq[3] = 2 * (x * y + w * z);
+    Rq[4] = 1 - 2 * (x * x + z * z);
+    Rq[5] = 2 * (y * z - w * x);
+    Rq[6] = 2 * (x * z - w * y);
+    Rq[7] = 2 * (y * z + w * x);
+    Rq[8] = 1 - 2 * (x * x + y * y);
+    for (int k = 0; k < 3; ++k) f->sc[k] = prm[7 + k];
+    for (int i = 0; i < 3; ++i)
+        for (int k = 0; k < 3; ++k) f->M[3 * i + k] = Rq[3 * i + k] * f->sc[k];
+    double Tm[9];
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j) {
             double acc = 0;
-            for (int k = 0; k < 3; ++k) acc += Rq[3 * i + k] * sc[k] * Rq[3 * j + k] * sc[k];
-            S3[3 * i + j] = acc;
+            for (int k = 0; k < 3; ++k) acc += Rq[3 * i + k] * f->sc[k] * Rq[3 * j + k] * f->sc[k];
+            f->S3[3 * i + j] = acc;
         }
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j) {
             double acc = 0;
-            for (int k = 0; k < 3; ++k) acc += R[3 * i + k] * S3[3 * k + j];
+            for (int k = 0; k < 3; ++k) acc += R[3 * i + k] * f->S3[3 * k + j];
             Tm[3 * i + j] = acc;
         }
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j) {
             double acc = 0;
             for (int k = 0; k < 3; ++k) acc += Tm[3 * i + k] * R[3 * j + k];
-            Cc[3 * i + j] = acc;
+            f->Cc[3 * i + j] = acc;
         }
-    double limx = 1.3 * (0.5 * s->W / fx), limy = 1.3 * (0.5 * s->H / fy);
-    double ux = tx / tz, uy = ty / tz;
-    double uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
-    double uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
-    double Jc[6] = {fx / tz, 0, -fx * uxc / tz, 0, fy / tz, -fy * uyc / tz};
+    const double limx = 1.3 * (0.5 * s->W / f->fx), limy = 1.3 * (0.5 * s->H / f->fy);
+    const double ux = tx / tz, uy = ty / tz;
+    f->clip_x = ux < -limx || ux > limx;
+    f->clip_y = uy < -limy || uy > limy;
+    f->uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
+    f->uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
+    double* Jc = f->Jc;
+    Jc[0] = f->fx / tz;
+    Jc[1] = 0;
+    Jc[2] = -f->fx * f->uxc / tz;
+    Jc[3] = 0;
+    Jc[4] = f->fy / tz;
+    Jc[5] = -f->fy * f->uyc / tz;
     double S2[4] = {0, 0, 0, 0};
     for (int i = 0; i < 2; ++i)
         for (int j = 0; j < 2; ++j) {
             double acc = 0;
             for (int k = 0; k < 3; ++k)
-                for (int l = 0; l < 3; ++l) acc += Jc[3 * i + k] * Cc[3 * k + l] * Jc[3 * j + l];
+                for (int l = 0; l < 3; ++l) acc += Jc[3 * i + k] * f->Cc[3 * k + l] * Jc[3 * j + l];
             S2[2 * i + j] = acc;
         }
-    double a = S2[0] + 0.3, b = 0.5 * (S2[1] + S2[2]), c = S2[3] + 0.3;
-    double det = a * c - b * b;
-    r->ca = c / det;
-    r->cb = -b / det;
-    r->cc = a / det;
-    r->mx = fx * tx / tz + cx;
-    r->my = fy * ty / tz + cy;
+    f->a = S2[0] + 0.3;
+    f->b = 0.5 * (S2[1] + S2[2]);
+    f->c = S2[3] + 0.3;
+    f->det = f->a * f->c - f->b * f->b;
+    double cc3[3];
+    for (int j = 0; j < 3; ++j) cc3[j] = -(R[j] * f->t[0] + R[3 + j] * f->t[1] + R[6 + j] * f->t[2]);
+    double dv[3] = {mu[0] - cc3[0], mu[1] - cc3[1], mu[2] - cc3[2]};
+    f->len = sqrt(dv[0] * dv[0] + dv[1] * dv[1] + dv[2] * dv[2]);
+    for (int j = 0; j < 3; ++j) f->dir[j] = dv[j] / f->len;
+}
+
+static void project64(const scene* s, int g, int v, const rec32* r32, rec64* r)
+{
+    memset(r, 0, sizeof *r);
+    const double* sh = s->sh64 + (int64_t)g * s->d * 3;
+    r->opac = s->p64[11 * (int64_t)g + 10];
+    if (r32->culled) return;
+    fwd64 f;
+    forward64(s, g, v, &f);
+    const double tx = f.tc[0], ty = f.tc[1], tz = f.tc[2];
+    r->ca = f.c / f.det;
+    r->cb = -f.b / f.det;
+    r->cc = f.a / f.det;
+    r->mx = f.fx * tx / tz + f.cx;
+    r->my = f.fy * ty / tz + f.cy;
     /* unclamped pixel-projection Jacobian d pi / d mu = Jp(t) R */
-    double Jp[6] = {fx / tz, 0, -fx * tx / (tz * tz), 0, fy / tz, -fy * ty / (tz * tz)};
+    double Jp[6] = {f.fx / tz, 0, -f.fx * tx / (tz * tz), 0, f.fy / tz, -f.fy * ty / (tz * tz)};
     for (int i = 0; i < 2; ++i)
         for (int j = 0; j < 3; ++j) {
             double acc = 0;
-            for (int k = 0; k < 3; ++k) acc += Jp[3 * i + k] * R[3 * k + j];
+            for (int k = 0; k < 3; ++k) acc += Jp[3 * i + k] * f.R[3 * k + j];
             r->J[3 * i + j] = acc;
         }
-    double cc3[3];
-    for (int j = 0; j < 3; ++j) cc3[j] = -(R[j] * t[0] + R[3 + j] * t[1] + R[6 + j] * t[2]);
-    double dv[3] = {mu[0] - cc3[0], mu[1] - cc3[1], mu[2] - cc3[2]};
-    double len = sqrt(dv[0] * dv[0] + dv[1] * dv[1] + dv[2] * dv[2]);
-    sh_basis64(dv[0] / len, dv[1] / len, dv[2] / len, s->d, r->B);
+    sh_basis64(f.dir[0], f.dir[1], f.dir[2], s->d, r->B);
     for (int ch = 0; ch < 3; ++ch) {
         double acc = 0.5;
         for (int k = 0; k < s->d; ++k) acc += r->B[k] * sh[3 * k + ch];
@@ -481,6 +548,7 @@ void* orc_scene_new(int G, int sh_degree, const float* means, const float* quats
     s->opac = (float*)malloc(sizeof(float) * Gs + 1);
     s->sh = (float*)malloc(sizeof(float) * 3 * s->d * Gs + 1);
     s->sh64 = (double*)malloc(sizeof(double) * 3 * s->d * Gs + 1);
+    s->p64 = (double*)malloc(sizeof(double) * 11 * Gs + 1);
     s->cams = (float*)malloc(sizeof(float) * 16 * V);
     memcpy(s->means, means, sizeof(float) * 3 * Gs);
     memcpy(s->quats, quats, sizeof(float) * 4 * Gs);
@@ -488,6 +556,7 @@ void* orc_scene_new(int G, int sh_degree, const float* means, const float* quats
     memcpy(s->opac, opac, sizeof(float) * Gs);
     memcpy(s->sh, sh, sizeof(float) * 3 * s->d * Gs);
     for (size_t i = 0; i < 3 * s->d * Gs; ++i) s->sh64[i] = sh[i];
+    params64_from_inputs(s);
     memcpy(s->cams, cams, sizeof(float) * 16 * V);
     size_t VG = (size_t)V * Gs;
     s->r32 = (rec32*)malloc(sizeof(rec32) * VG + 1);
@@ -509,7 +578,7 @@ void orc_scene_free(void* p)
 {
     scene* s = (scene*)p;
     if (!s) return;
-    free(s->means); free(s->quats); free(s->scales); free(s->opac); free(s->sh); free(s->sh64);
+    free(s->means); free(s->quats); free(s->scales); free(s->opac); free(s->sh); free(s->sh64); free(s->p64);
     free(s->cams); free(s->r32); free(s->r64); free(s->r64_base); free(s->starts); free(s->ids);
     free(s->slot); free(s->sel); free(s->acc);
     free(s);
@@ -671,6 +740,53 @@ static void add(double* a, double x)
     *a += x;
 }
 
+/* Stage 1 for one pixel (x, y) of view v over its tile list: float32 decisions
+ * (distance cut, alpha clamp and floor, transmittance stop), float64 values.
+ * Fills the accepted contributions in front-to-back order and returns their
+ * count; C gets the colour including the background. */
+static int composite_pixel(const scene* s, int v, int x, int y, const int32_t* list, int64_t L, contrib* cl,
+                           double C[3], float* T32_out, double* T64_out)
+{
+    float px = (float)x + 0.5f, py = (float)y + 0.5f;
+    double pxd = x + 0.5, pyd = y + 0.5;
+    float T32 = 1.0f;
+    double T64 = 1.0;
+    int n = 0;
+    C[0] = C[1] = C[2] = 0.0;
+    for (int64_t k = 0; k < L; ++k) {
+        int g = list[k];
+        const rec32* r = &s->r32[(int64_t)v * s->G + g];
+        float dx = px - r->mx, dy = py - r->my;
+        float e = fmaf(dx, fmaf(r->qa, dx, r->qb * dy), (r->qc * dy) * dy);
+        if (!(e >= E_CUTOFF_F)) continue;
+        float aG = r->opac * orc_exp2f(e);
+        int clamped = !(aG < ALPHA_MAX_F);
+        float a32 = clamped ? ALPHA_MAX_F : aG;
+        if (!(a32 >= g_alpha_min)) continue;
+        float tT = T32 * (1.0f - a32);
+        if (tT < T_MIN_F) break;
+        const rec64* q = &s->r64[(int64_t)v * s->G + g];
+        double ddx = pxd - q->mx, ddy = pyd - q->my;
+        double sig = 0.5 * (q->ca * ddx * ddx + 2.0 * q->cb * ddx * ddy + q->cc * ddy * ddy);
+        double G64 = exp(-sig);
+        double a64 = clamped ? ALPHA_MAX_D : q->opac * G64;
+        for (int ch = 0; ch < 3; ++ch) C[ch] += q->col[ch] * a64 * T64;
+        cl[n].g = g;
+        cl[n].alpha = a64;
+        cl[n].T = T64;
+        cl[n].G = G64;
+        cl[n].tT32 = tT;
+        cl[n].clamped = clamped;
+        n++;
+        T64 = T64 * (1.0 - a64);
+        T32 = tT;
+    }
+    for (int ch = 0; ch < 3; ++ch) C[ch] += T64 * s->bg[ch];
+    *T32_out = T32;
+    *T64_out = T64;
+    return n;
+}
+
 /* Render (and, with obs != NULL, replay) the pixels of the given tiles.
  * Pixel outputs are written at [v, y, x]; score sums accumulate into the selected slots. */
 void orc_render_tiles(void* p, const int64_t* tiles, int64_t n_tiles, const float* obs, float eps,
@@ -698,42 +814,11 @@ void orc_render_tiles(void* p, const int64_t* tiles, int64_t n_tiles, const floa
                 for (int xx = 0; xx < TILE; ++xx) {
                     int x = tx * TILE + xx, y = ty * TILE + yy;
                     if (x >= s->W || y >= s->H) continue;
-                    float px = (float)x + 0.5f, py = (float)y + 0.5f;
                     double pxd = x + 0.5, pyd = y + 0.5;
-                    float T32 = 1.0f;
-                    double T64 = 1.0;
-                    double C[3] = {0, 0, 0};
-                    int n = 0;
-                    /* Stage 1: front-to-back composite */
-                    for (int64_t k = 0; k < L; ++k) {
-                        int g = list[k];
-                        const rec32* r = &s->r32[(int64_t)v * s->G + g];
-                        float dx = px - r->mx, dy = py - r->my;
-                        float e = fmaf(dx, fmaf(r->qa, dx, r->qb * dy), (r->qc * dy) * dy);
-                        if (!(e >= E_CUTOFF_F)) continue;
-                        float aG = r->opac * orc_exp2f(e);
-                        int clamped = !(aG < ALPHA_MAX_F);
-                        float a32 = clamped ? ALPHA_MAX_F : aG;
-                        if (!(a32 >= g_alpha_min)) continue;
-                        float tT = T32 * (1.0f - a32);
-                        if (tT < T_MIN_F) break;
-                        const rec64* q = &s->r64[(int64_t)v * s->G + g];
-                        double ddx = pxd - q->mx, ddy = pyd - q->my;
-                        double sig = 0.5 * (q->ca * ddx * ddx + 2.0 * q->cb * ddx * ddy + q->cc * ddy * ddy);
-                        double G64 = exp(-sig);
-                        double a64 = clamped ? ALPHA_MAX_D : q->opac * G64;
-                        for (int ch = 0; ch < 3; ++ch) C[ch] += q->col[ch] * a64 * T64;
-                        cl[n].g = g;
-                        cl[n].alpha = a64;
-                        cl[n].T = T64;
-                        cl[n].G = G64;
-                        cl[n].tT32 = tT;
-                        cl[n].clamped = clamped;
-                        n++;
-                        T64 = T64 * (1.0 - a64);
-                        T32 = tT;
-                    }
-                    for (int ch = 0; ch < 3; ++ch) C[ch] += T64 * s->bg[ch];
+                    float T32;
+                    double T64;
+                    double C[3];
+                    int n = composite_pixel(s, v, x, y, list, L, cl, C, &T32, &T64);
                     int64_t pix = ((int64_t)v * s->H + y) * s->W + x;
                     if (color) for (int ch = 0; ch < 3; ++ch) color[3 * pix + ch] = C[ch];
                     if (T_out) T_out[pix] = T32;
@@ -897,6 +982,284 @@ void orc_tokens(const void* p, double eps, double lambda, double* tok, double* A
 }
 
 /* ----------------------------------------------------------------------------
+ * Renderer backward: the vector-Jacobian product of the colour image with an
+ * upstream gradient dL/dC_hat, through the composite, the 2D Gaussian, the EWA
+ * projection, the quaternion/scale covariance and the SH colour (view
+ * direction included), with the float32 decisions frozen.
+ * ------------------------------------------------------------------------- */
+#define NB2D 9  /* per (Gaussian, view): dL/dmx, dL/dmy, dL/dca, dL/dcb, dL/dcc, dL/do, dL/dcol[3] */
+
+/* d B_k / d(x, y, z) of the SH polynomials of sh_basis64, (x, y, z) taken as
+ * independent variables (the unit-norm constraint is applied by the caller) */
+static void sh_basis_grad64(double x, double y, double z, int d, double (*dB)[3])
+{
+    const double* K = g_sh64;
+    for (int k = 0; k < d; ++k) dB[k][0] = dB[k][1] = dB[k][2] = 0.0;
+    if (d <= 1) return;
+    dB[1][1] = K[1];
+    dB[2][2] = K[2];
+    dB[3][0] = K[3];
+    if (d <= 4) return;
+    dB[4][0] = K[4] * y;
+    dB[4][1] = K[4] * x;
+    dB[5][1] = K[5] * z;
+    dB[5][2] = K[5] * y;
+    dB[6][0] = -2.0 * K[6] * x;
+    dB[6][1] = -2.0 * K[6] * y;
+    dB[6][2] = 4.0 * K[6] * z;
+    dB[7][0] = K[7] * z;
+    dB[7][2] = K[7] * x;
+    dB[8][0] = 2.0 * K[8] * x;
+    dB[8][1] = -2.0 * K[8] * y;
+    if (d <= 9) return;
+    double xx = x * x, yy = y * y, zz = z * z;
+    dB[9][0] = 6.0 * K[9] * x * y;
+    dB[9][1] = K[9] * (3.0 * xx - 3.0 * yy);
+    dB[10][0] = K[10] * y * z;
+    dB[10][1] = K[10] * x * z;
+    dB[10][2] = K[10] * x * y;
+    dB[11][0] = -2.0 * K[11] * x * y;
+    dB[11][1] = K[11] * (4.0 * zz - xx - 3.0 * yy);
+    dB[11][2] = 8.0 * K[11] * y * z;
+    dB[12][0] = -6.0 * K[12] * x * z;
+    dB[12][1] = -6.0 * K[12] * y * z;
+    dB[12][2] = K[12] * (6.0 * zz - 3.0 * xx - 3.0 * yy);
+    dB[13][0] = K[13] * (4.0 * zz - 3.0 * xx - yy);
+    dB[13][1] = -2.0 * K[13] * x * y;
+    dB[13][2] = 8.0 * K[13] * x * z;
+    dB[14][0] = 2.0 * K[14] * x * z;
+    dB[14][1] = -2.0 * K[14] * y * z;
+    dB[14][2] = K[14] * (xx - yy);
+    dB[15][0] = K[15] * (3.0 * xx - 3.0 * yy);
+    dB[15][1] = -6.0 * K[15] * x * y;
+}
+
+void orc_sh_basis_grad64(const double* dirs, int64_t n, int d, double* out /* [n][d][3] */)
+{
+    init_constants();
+    for (int64_t i = 0; i < n; ++i)
+        sh_basis_grad64(dirs[3 * i], dirs[3 * i + 1], dirs[3 * i + 2], d, (double(*)[3])(out + i * d * 3));
+}
+
+/* Image-space gradients: for every pixel of every tile, Stage 1 again, then
+ * the contributions back to front with the explicit suffix S (everything
+ * composited behind the contribution, background included):
+ *   dC/dalpha_k = T_k c_k - S_k / (1 - alpha_k)
+ * and, where the alpha clamp is inactive, alpha = o G with
+ *   G = exp(-1/2 d^T conic d), d = p - mu2D,
+ *   dG/dmu2D = G conic d,  dG/d(ca, cb, cc) = -G (dx^2 / 2, dx dy, dy^2 / 2);
+ * the colour gets dC/dc_k = T_k alpha_k.  Sums per (Gaussian, view) into
+ * g2d[v*G + g][NB2D]. */
+static void backward_image(scene* s, const float* gC, double* g2d)
+{
+    const int T = s->TX * s->TY;
+    int64_t maxlen = 0;
+    for (int64_t i = 0; i < (int64_t)s->V * T; ++i)
+        if (s->starts[i + 1] - s->starts[i] > maxlen) maxlen = s->starts[i + 1] - s->starts[i];
+    const int64_t n_tiles = (int64_t)s->V * T;
+#pragma omp parallel
+    {
+        contrib* cl = (contrib*)malloc(sizeof(contrib) * (size_t)maxlen + 1);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t tile = 0; tile < n_tiles; ++tile) {
+            int v = (int)(tile / T), t = (int)(tile % T);
+            int tx = t % s->TX, ty = t / s->TX;
+            const int32_t* list = s->ids + s->starts[tile];
+            int64_t L = s->starts[tile + 1] - s->starts[tile];
+            for (int yy = 0; yy < TILE; ++yy)
+                for (int xx = 0; xx < TILE; ++xx) {
+                    int x = tx * TILE + xx, y = ty * TILE + yy;
+                    if (x >= s->W || y >= s->H) continue;
+                    double C[3], T64;
+                    float T32;
+                    int n = composite_pixel(s, v, x, y, list, L, cl, C, &T32, &T64);
+                    int64_t pix = ((int64_t)v * s->H + y) * s->W + x;
+                    double gp[3] = {gC[3 * pix], gC[3 * pix + 1], gC[3 * pix + 2]};
+                    double S[3];
+                    for (int ch = 0; ch < 3; ++ch) S[ch] = T64 * s->bg[ch];
+                    for (int k = n - 1; k >= 0; --k) {
+                        const contrib* c = &cl[k];
+                        const rec64* q = &s->r64[(int64_t)v * s->G + c->g];
+                        double* A = g2d + ((int64_t)v * s->G + c->g) * NB2D;
+                        double w = c->T * c->alpha;
+                        for (int ch = 0; ch < 3; ++ch) add(&A[6 + ch], gp[ch] * w);
+                        if (!c->clamped) {
+                            double dLda = 0.0;
+                            for (int ch = 0; ch < 3; ++ch)
+                                dLda += gp[ch] * (c->T * q->col[ch] - S[ch] / (1.0 - c->alpha));
+                            double dx = (x + 0.5) - q->mx, dy = (y + 0.5) - q->my;
+                            double dLdG = dLda * q->opac;
+                            add(&A[5], dLda * c->G);
+                            add(&A[0], dLdG * c->G * (q->ca * dx + q->cb * dy));
+                            add(&A[1], dLdG * c->G * (q->cb * dx + q->cc * dy));
+                            add(&A[2], -0.5 * dLdG * c->G * dx * dx);
+                            add(&A[3], -dLdG * c->G * dx * dy);
+                            add(&A[4], -0.5 * dLdG * c->G * dy * dy);
+                        }
+                        for (int ch = 0; ch < 3; ++ch) S[ch] += w * q->col[ch];
+                    }
+                }
+        }
+        free(cl);
+    }
+}
+
+/* Per Gaussian: chain rule from the image-space gradients of every view to the
+ * parameters, out[g] = [mean (3), quaternion (4), scale (3), opacity (1),
+ * SH (d x 3, channel fastest)]. */
+static void backward_params(scene* s, const double* g2d, double* out)
+{
+    const int d = s->d, NP = 11 + 3 * d;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int g = 0; g < s->G; ++g) {
+        double* o = out + (int64_t)g * NP;
+        for (int i = 0; i < NP; ++i) o[i] = 0.0;
+        const double* sh = s->sh64 + (int64_t)g * d * 3;
+        for (int v = 0; v < s->V; ++v) {
+            const int64_t rid = (int64_t)v * s->G + g;
+            if (s->r32[rid].culled) continue;
+            const double* A = g2d + rid * NB2D;
+            fwd64 f;
+            forward64(s, g, v, &f);
+            const double tx = f.tc[0], ty = f.tc[1], tz = f.tc[2];
+            double gmu[3] = {0, 0, 0}, gt[3] = {0, 0, 0};
+
+            /* opacity */
+            o[10] += A[5];
+
+            /* colour = max(0.5 + sum_k B_k(dir) sh_k, 0), clamp state frozen */
+            double gpre[3];
+            for (int ch = 0; ch < 3; ++ch) gpre[ch] = s->r32[rid].clamp_ok[ch] ? A[6 + ch] : 0.0;
+            double B[16], dB[16][3];
+            sh_basis64(f.dir[0], f.dir[1], f.dir[2], d, B);
+            sh_basis_grad64(f.dir[0], f.dir[1], f.dir[2], d, dB);
+            double gdir[3] = {0, 0, 0};
+            for (int k = 0; k < d; ++k) {
+                double gB = 0.0;
+                for (int ch = 0; ch < 3; ++ch) {
+                    o[11 + 3 * k + ch] += B[k] * gpre[ch];
+                    gB += sh[3 * k + ch] * gpre[ch];
+                }
+                for (int j = 0; j < 3; ++j) gdir[j] += gB * dB[k][j];
+            }
+            /* dir = (mu - camera centre) / len:  d dir / d mu = (I - dir dir^T) / len */
+            double dd = gdir[0] * f.dir[0] + gdir[1] * f.dir[1] + gdir[2] * f.dir[2];
+            for (int j = 0; j < 3; ++j) gmu[j] += (gdir[j] - f.dir[j] * dd) / f.len;
+
+            /* projected centre: mx = fx tx / tz + cx, my = fy ty / tz + cy */
+            gt[0] += A[0] * f.fx / tz;
+            gt[1] += A[1] * f.fy / tz;
+            gt[2] += -A[0] * f.fx * tx / (tz * tz) - A[1] * f.fy * ty / (tz * tz);
+
+            /* conic (ca, cb, cc) = (c, -b, a) / (a c - b^2) */
+            const double a = f.a, b = f.b, c = f.c, D2 = f.det * f.det;
+            const double gca = A[2], gcb = A[3], gcc = A[4];
+            const double ga = (-c * c * gca + b * c * gcb - b * b * gcc) / D2;
+            const double gb = (2.0 * b * c * gca - (a * c + b * b) * gcb + 2.0 * a * b * gcc) / D2;
+            const double gc = (-b * b * gca + a * b * gcb - a * a * gcc) / D2;
+            /* a, b, c are the entries of S2 = Jc Cc Jc^T (+ dilation), b the mean of the two off-diagonals */
+            const double G2[4] = {ga, 0.5 * gb, 0.5 * gb, gc};
+            /* dL/dCc = Jc^T G2 Jc,  dL/dJc = 2 G2 Jc Cc (G2, Cc symmetric) */
+            double GC[9], GJ[6], JCc[6];
+            for (int k = 0; k < 3; ++k)
+                for (int l = 0; l < 3; ++l) {
+                    double acc = 0;
+                    for (int i = 0; i < 2; ++i)
+                        for (int j = 0; j < 2; ++j) acc += f.Jc[3 * i + k] * G2[2 * i + j] * f.Jc[3 * j + l];
+                    GC[3 * k + l] = acc;
+                }
+            for (int i = 0; i < 2; ++i)
+                for (int l = 0; l < 3; ++l) {
+                    double acc = 0;
+                    for (int k = 0; k < 3; ++k) acc += f.Jc[3 * i + k] * f.Cc[3 * k + l];
+                    JCc[3 * i + l] = acc;
+                }
+            for (int i = 0; i < 2; ++i)
+                for (int l = 0; l < 3; ++l) {
+                    double acc = 0;
+                    for (int j = 0; j < 2; ++j) acc += G2[2 * i + j] * JCc[3 * j + l];
+                    GJ[3 * i + l] = 2.0 * acc;
+                }
+            /* Jc = [[fx/tz, 0, -fx uxc/tz], [0, fy/tz, -fy uyc/tz]], uxc = tx/tz unless clamped */
+            gt[2] += -GJ[0] * f.fx / (tz * tz) - GJ[4] * f.fy / (tz * tz);
+            if (f.clip_x) {
+                gt[2] += GJ[2] * f.fx * f.uxc / (tz * tz);
+            } else {
+                gt[0] += -GJ[2] * f.fx / (tz * tz);
+                gt[2] += GJ[2] * 2.0 * f.fx * tx / (tz * tz * tz);
+            }
+            if (f.clip_y) {
+                gt[2] += GJ[5] * f.fy * f.uyc / (tz * tz);
+            } else {
+                gt[1] += -GJ[5] * f.fy / (tz * tz);
+                gt[2] += GJ[5] * 2.0 * f.fy * ty / (tz * tz * tz);
+            }
+            /* t = R mu + t0 */
+            for (int j = 0; j < 3; ++j) gmu[j] += f.R[j] * gt[0] + f.R[3 + j] * gt[1] + f.R[6 + j] * gt[2];
+            for (int j = 0; j < 3; ++j) o[j] += gmu[j];
+
+            /* Cc = R S3 R^T:  dL/dS3 = R^T GC R */
+            double GS[9], tmp[9];
+            for (int i = 0; i < 3; ++i)
+                for (int l = 0; l < 3; ++l) {
+                    double acc = 0;
+                    for (int k = 0; k < 3; ++k) acc += f.R[3 * k + i] * GC[3 * k + l];
+                    tmp[3 * i + l] = acc;
+                }
+            for (int i = 0; i < 3; ++i)
+                for (int j = 0; j < 3; ++j) {
+                    double acc = 0;
+                    for (int l = 0; l < 3; ++l) acc += tmp[3 * i + l] * f.R[3 * l + j];
+                    GS[3 * i + j] = acc;
+                }
+            /* S3 = M M^T:  dL/dM = (GS + GS^T) M */
+            double GM[9];
+            for (int i = 0; i < 3; ++i)
+                for (int k = 0; k < 3; ++k) {
+                    double acc = 0;
+                    for (int j = 0; j < 3; ++j) acc += (GS[3 * i + j] + GS[3 * j + i]) * f.M[3 * j + k];
+                    GM[3 * i + k] = acc;
+                }
+            /* M = Rq diag(sc) */
+            double GR[9];
+            for (int k = 0; k < 3; ++k) {
+                double acc = 0;
+                for (int i = 0; i < 3; ++i) acc += GM[3 * i + k] * f.Rq[3 * i + k];
+                o[7 + k] += acc;
+            }
+            for (int i = 0; i < 3; ++i)
+                for (int k = 0; k < 3; ++k) GR[3 * i + k] = GM[3 * i + k] * f.sc[k];
+            /* Rq of the unit quaternion (w, x, y, z), entry by entry */
+            const double w = f.qh[0], x = f.qh[1], y = f.qh[2], z = f.qh[3];
+            double gq[4];
+            gq[0] = 2.0 * (-z * GR[1] + y * GR[2] + z * GR[3] - x * GR[5] - y * GR[6] + x * GR[7]);
+            gq[1] = 2.0 * (y * GR[1] + z * GR[2] + y * GR[3] - 2.0 * x * GR[4] - w * GR[5] + z * GR[6] + w * GR[7] -
+                           2.0 * x * GR[8]);
+            gq[2] = 2.0 * (-2.0 * y * GR[0] + x * GR[1] + w * GR[2] + x * GR[3] + z * GR[5] - w * GR[6] + z * GR[7] -
+                           2.0 * y * GR[8]);
+            gq[3] = 2.0 * (-2.0 * z * GR[0] - w * GR[1] + x * GR[2] + w * GR[3] - 2.0 * z * GR[4] + y * GR[5] +
+                           x * GR[6] + y * GR[7]);
+            /* normalisation q -> q / |q| */
+            double qg = 0;
+            for (int i = 0; i < 4; ++i) qg += f.qh[i] * gq[i];
+            for (int i = 0; i < 4; ++i) o[3 + i] += (gq[i] - f.qh[i] * qg) / f.qn;
+        }
+    }
+}
+
+/* Full backward: out [G][11 + 3 d]; g2d (optional) receives the image-space
+ * sums [V*G][NB2D] (record index v*G + g).  Needs the lists. */
+void orc_backward(void* p, const float* gC, double* out, double* g2d_out)
+{
+    scene* s = (scene*)p;
+    double* g2d = (double*)calloc((size_t)s->V * s->G * NB2D + 1, sizeof(double));
+    backward_image(s, gC, g2d);
+    backward_params(s, g2d, out);
+    if (g2d_out) memcpy(g2d_out, g2d, sizeof(double) * (size_t)s->V * s->G * NB2D);
+    free(g2d);
+}
+
+/* ----------------------------------------------------------------------------
  * Value probes for finite differences (float32 decisions stay frozen).
  * ------------------------------------------------------------------------- */
 void orc_values_reset(void* p)
@@ -904,11 +1267,25 @@ void orc_values_reset(void* p)
     scene* s = (scene*)p;
     memcpy(s->r64, s->r64_base, sizeof(rec64) * (size_t)s->V * s->G);
     for (size_t i = 0; i < (size_t)3 * s->d * s->G; ++i) s->sh64[i] = s->sh[i];
+    params64_from_inputs(s);
+}
+
+/* move every parameter of Gaussian g (mean 3, quaternion 4, scale 3, opacity 1):
+ * all its float64 values are recomputed, the float32 decisions stay frozen */
+void orc_set_params64(void* p, int g, const double* prm)
+{
+    scene* s = (scene*)p;
+    memcpy(s->p64 + 11 * (int64_t)g, prm, sizeof(double) * 11);
+    for (int v = 0; v < s->V; ++v) {
+        const int64_t i = (int64_t)v * s->G + g;
+        project64(s, g, v, &s->r32[i], &s->r64[i]);
+    }
 }
 
 void orc_set_opacity64(void* p, int g, double o)
 {
     scene* s = (scene*)p;
+    s->p64[11 * (int64_t)g + 10] = o;
     for (int v = 0; v < s->V; ++v) s->r64[(int64_t)v * s->G + g].opac = o;
 }
 
