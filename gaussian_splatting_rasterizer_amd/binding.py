@@ -31,10 +31,11 @@ GS_EXPORT_DEPTH_KEYS = 2
 GS_EXPORT_SORTED_IDS = 3
 GS_EXPORT_RANGES = 4
 GS_EXPORT_PIXEL_STATS = 5
-STAGES = ("project", "depth_sort", "scan", "emit", "tile_sort", "ranges", "render", "replay", "finalize")
+STAGES = ("project", "depth_sort", "scan", "emit", "tile_sort", "ranges", "render", "replay", "finalize",
+          "backward", "backward_finalize")
 
 ABI_SYMBOLS = ("gs_default_params", "gs_workspace_size", "gs_context_create", "gs_context_destroy",
-               "gs_project", "gs_bin_sort", "gs_render", "gs_score_replay", "gs_status_string",
+               "gs_project", "gs_bin_sort", "gs_render", "gs_score_replay", "gs_backward", "gs_status_string",
                "gs_last_error", "gs_debug_exp2", "gs_debug_export", "gs_profile_enable", "gs_profile_read")
 
 
@@ -42,6 +43,11 @@ class gs_gaussians(ctypes.Structure):
     _fields_ = [("means", ctypes.c_void_p), ("quats", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("opacities", ctypes.c_void_p), ("sh", ctypes.c_void_p), ("n", ctypes.c_int64),
                 ("sh_degree", ctypes.c_int32)]
+
+
+class gs_gaussian_grads(ctypes.Structure):
+    _fields_ = [("means", ctypes.c_void_p), ("quats", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("opacities", ctypes.c_void_p), ("sh", ctypes.c_void_p)]
 
 
 class gs_camera(ctypes.Structure):
@@ -95,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.gs_render.argtypes = [P, P, P, P, P]
     lib.gs_score_replay.restype = St
     lib.gs_score_replay.argtypes = [P, P, P, P]
+    lib.gs_backward.restype = St
+    lib.gs_backward.argtypes = [P, P, ctypes.POINTER(gs_gaussian_grads), P]
     lib.gs_status_string.restype = ctypes.c_char_p
     lib.gs_status_string.argtypes = [St]
     lib.gs_last_error.restype = ctypes.c_char_p
@@ -106,7 +114,7 @@ def load_library(path: str = LIB_PATH):
     lib.gs_profile_enable.restype = St
     lib.gs_profile_enable.argtypes = [P, ctypes.c_int32]
     lib.gs_profile_read.restype = St
-    lib.gs_profile_read.argtypes = [P, P, P]
+    lib.gs_profile_read.argtypes = [P, P, P, ctypes.c_int32]
     _lib = lib
     return lib
 
@@ -182,6 +190,11 @@ def gs_score_replay(ctx, observed, tokens, stream=None) -> None:
            "gs_score_replay")
 
 
+def gs_backward(ctx, grad_color, grads: gs_gaussian_grads, stream=None) -> None:
+    _check(load_library().gs_backward(ctx, _dev_ptr(grad_color), ctypes.byref(grads), _stream_handle(stream)),
+           "gs_backward")
+
+
 def gs_debug_exp2(inp, out, stream=None) -> None:
     _check(load_library().gs_debug_exp2(_dev_ptr(inp), _dev_ptr(out), inp.numel(), _stream_handle(stream)),
            "gs_debug_exp2")
@@ -200,7 +213,7 @@ def gs_profile_read(ctx) -> dict:
     """{stage: (total ms, launches)} accumulated since the previous read."""
     ms = (ctypes.c_double * len(STAGES))()
     calls = (ctypes.c_int64 * len(STAGES))()
-    _check(load_library().gs_profile_read(ctx, ms, calls), "gs_profile_read")
+    _check(load_library().gs_profile_read(ctx, ms, calls, len(STAGES)), "gs_profile_read")
     return {name: (float(ms[i]), int(calls[i])) for i, name in enumerate(STAGES)}
 
 
@@ -298,6 +311,27 @@ class Rasterizer:
         obs = torch.as_tensor(observed, dtype=torch.float32, device=self.device).contiguous()
         gs_score_replay(self.ctx, obs, tokens, stream)
         return tokens
+
+    def new_grads(self):
+        """Gradient tensors shaped like the scene parameters."""
+        torch = self.torch
+        return {name: torch.empty_like(getattr(self, name))
+                for name in ("means", "quats", "scales", "opacities", "sh")}
+
+    def backward(self, grad_color, grads=None, stream=None):
+        """Renderer backward: dL/d(means, quats, scales, opacities, sh) for dL/dC_hat = grad_color."""
+        torch = self.torch
+        grads = grads if grads is not None else self.new_grads()
+        gC = torch.as_tensor(grad_color, dtype=torch.float32, device=self.device).contiguous()
+        for name in ("means", "quats", "scales", "opacities", "sh"):
+            t = grads.get(name)
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()
+                                  or t.shape != getattr(self, name).shape):
+                raise ValueError(f"gradient buffer {name} must be contiguous float32 of the parameter shape")
+        ptrs = gs_gaussian_grads(*[grads[k].data_ptr() if grads.get(k) is not None else None
+                                   for k in ("means", "quats", "scales", "opacities", "sh")])
+        gs_backward(self.ctx, gC, ptrs, stream)
+        return grads
 
     def step(self, observed, outputs=None, tokens=None, stream=None):
         """One pass of the whole path: project, bin/sort, render, replay -> tokens."""

@@ -177,8 +177,8 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->pval_b = (uint32_t*)take(4 * P);
     ws->pair_g = (uint32_t*)take(4 * P);
     ws->ranges = (uint2*)take(8 * tiles);
-    ws->partials = (float4*)take(32 * P);
-    ws->gv_sums = (float4*)take(32 * VG);
+    ws->partials = (float4*)take(48 * P);
+    ws->gv_sums = (float4*)take(48 * VG);
     ws->rec_masks = (uint64_t*)take(16 * ((VG + 63) / 64));
     ws->pixel = (float4*)take(16 * pixels);
     ws->pixel_stats = (uint2*)take(8 * pixels);
@@ -416,11 +416,32 @@ gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens,
     if (e != hipSuccess) return hip_fail(e, "replay");
     ctx->timer.end(GS_STAGE_REPLAY, stream);
     ctx->timer.begin(stream);
-    e = launch_gather_slots(ctx->s, ctx->ws, stream);
+    e = launch_gather_slots(ctx->s, ctx->ws, 2, stream);
     if (e != hipSuccess) return hip_fail(e, "gather");
     e = launch_tokens(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.eps, ctx->params.lambda, tokens, stream);
     if (e != hipSuccess) return hip_fail(e, "tokens");
     ctx->timer.end(GS_STAGE_FINALIZE, stream);
+    return GS_OK;
+}
+
+gs_status gs_backward(gs_context* ctx, const float* grad_color, const gs_gaussian_grads* grads, hipStream_t stream) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    if (ctx->state < kRendered) return fail(GS_ERR_STATE, "gs_backward before gs_render");
+    if (!grad_color || !grads) return fail(GS_ERR_INVALID_ARGUMENT, "null grad_color or grads");
+    if (!aligned(grad_color, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned grad_color");
+    const float* outs[5] = {grads->means, grads->quats, grads->scales, grads->opacities, grads->sh};
+    for (const float* p : outs)
+        if (p && !aligned(p, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned gradient pointer");
+    ctx->timer.begin(stream);
+    hipError_t e = launch_backward(ctx->s, ctx->ws, ctx->sorted_g, grad_color, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward");
+    ctx->timer.end(GS_STAGE_BACKWARD, stream);
+    ctx->timer.begin(stream);
+    e = launch_gather_slots(ctx->s, ctx->ws, 3, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward gather");
+    e = launch_grads(ctx->scene, ctx->cams, ctx->s, ctx->ws, *grads, stream);
+    if (e != hipSuccess) return hip_fail(e, "gradients");
+    ctx->timer.end(GS_STAGE_BACKWARD_FINALIZE, stream);
     return GS_OK;
 }
 
@@ -504,12 +525,15 @@ gs_status gs_profile_enable(gs_context* ctx, int32_t enable) {
     return GS_OK;
 }
 
-gs_status gs_profile_read(gs_context* ctx, double* ms, int64_t* calls) {
+gs_status gs_profile_read(gs_context* ctx, double* ms, int64_t* calls, int32_t n_stages) {
     if (!ctx || !ms || !calls) return fail(GS_ERR_INVALID_ARGUMENT, "null argument");
+    if (n_stages < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n_stages < 0");
     ctx->timer.fold();
     for (int i = 0; i < GS_NUM_STAGES; ++i) {
-        ms[i] = ctx->timer.ms[i];
-        calls[i] = ctx->timer.calls[i];
+        if (i < n_stages) {
+            ms[i] = ctx->timer.ms[i];
+            calls[i] = ctx->timer.calls[i];
+        }
         ctx->timer.ms[i] = 0.0;
         ctx->timer.calls[i] = 0;
     }

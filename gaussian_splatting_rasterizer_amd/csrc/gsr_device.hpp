@@ -196,4 +196,89 @@ __device__ __forceinline__ void kahan_add(float& hi, float& comp, float x) {
     hi = t;
 }
 
+// Reduce eight values over the 64 lanes; returns in every lane the total of
+// component (lane >> 3) & 7.  Reduce-scatter with gfx950 lane permutations:
+//   permlane32_swap pairs component i (kept in lanes 0-31) with i + 4 (lanes 32-63),
+//   permlane16_swap pairs rows, a row_ror:8 exchange splits each row in halves,
+//   then quad_perm / row_half_mirror adds finish the sum inside 8-lane groups.
+template <int CTRL>
+__device__ __forceinline__ float fadd_dpp(float keep, float send) {
+    return keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_reduce8(const float (&x)[8], int lane) {
+    float a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + 4]), false, false);
+        a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const auto s0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[0]), __float_as_uint(a[2]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[1]), __float_as_uint(a[3]), false, false);
+    const float b0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);  // rows hold components 0, 2, 4, 6
+    const float b1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);  // rows hold components 1, 3, 5, 7
+    const bool hi8 = lane & 8;
+    float c = fadd_dpp<0x128>(hi8 ? b1 : b0, hi8 ? b0 : b1);  // row_ror:8
+    c = fadd_dpp<0xB1>(c, c);                                  // quad_perm [1,0,3,2]
+    c = fadd_dpp<0x4E>(c, c);                                  // quad_perm [2,3,0,1]
+    c = fadd_dpp<0x141>(c, c);                                 // row_half_mirror
+    return c;
+}
+
+// Sum of one value over the 64 lanes, in every lane: the same permutation
+// sequence with each value paired with itself.
+__device__ __forceinline__ float wave_sum1(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float a = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+    const float b = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    float c = fadd_dpp<0x128>(b, b);  // row_ror:8
+    c = fadd_dpp<0xB1>(c, c);          // quad_perm [1,0,3,2]
+    c = fadd_dpp<0x4E>(c, c);          // quad_perm [2,3,0,1]
+    c = fadd_dpp<0x141>(c, c);         // row_half_mirror
+    return c;
+}
+
+// d B_k / d(x, y, z) of sh_basis_f32, (x, y, z) as independent variables; dB[3 k + j].
+__device__ __forceinline__ void sh_basis_grad_f32(float x, float y, float z, int d, float* dB) {
+    for (int i = 0; i < 3 * d; ++i) dB[i] = 0.0f;
+    if (d <= 1) return;
+    dB[3 * 1 + 1] = -kSH1;
+    dB[3 * 2 + 2] = kSH1;
+    dB[3 * 3 + 0] = -kSH1;
+    if (d <= 4) return;
+    dB[3 * 4 + 0] = kSH2a * y;
+    dB[3 * 4 + 1] = kSH2a * x;
+    dB[3 * 5 + 1] = -kSH2a * z;
+    dB[3 * 5 + 2] = -kSH2a * y;
+    dB[3 * 6 + 0] = -2.0f * kSH2b * x;
+    dB[3 * 6 + 1] = -2.0f * kSH2b * y;
+    dB[3 * 6 + 2] = 4.0f * kSH2b * z;
+    dB[3 * 7 + 0] = -kSH2a * z;
+    dB[3 * 7 + 2] = -kSH2a * x;
+    dB[3 * 8 + 0] = 2.0f * kSH2c * x;
+    dB[3 * 8 + 1] = -2.0f * kSH2c * y;
+    if (d <= 9) return;
+    const float xx = x * x, yy = y * y, zz = z * z;
+    dB[3 * 9 + 0] = -6.0f * kSH3a * x * y;
+    dB[3 * 9 + 1] = -kSH3a * (3.0f * xx - 3.0f * yy);
+    dB[3 * 10 + 0] = kSH3b * y * z;
+    dB[3 * 10 + 1] = kSH3b * x * z;
+    dB[3 * 10 + 2] = kSH3b * x * y;
+    dB[3 * 11 + 0] = 2.0f * kSH3c * x * y;
+    dB[3 * 11 + 1] = -kSH3c * (4.0f * zz - xx - 3.0f * yy);
+    dB[3 * 11 + 2] = -8.0f * kSH3c * y * z;
+    dB[3 * 12 + 0] = -6.0f * kSH3d * x * z;
+    dB[3 * 12 + 1] = -6.0f * kSH3d * y * z;
+    dB[3 * 12 + 2] = kSH3d * (6.0f * zz - 3.0f * xx - 3.0f * yy);
+    dB[3 * 13 + 0] = -kSH3c * (4.0f * zz - 3.0f * xx - yy);
+    dB[3 * 13 + 1] = 2.0f * kSH3c * x * y;
+    dB[3 * 13 + 2] = -8.0f * kSH3c * x * z;
+    dB[3 * 14 + 0] = 2.0f * kSH3e * x * z;
+    dB[3 * 14 + 1] = -2.0f * kSH3e * y * z;
+    dB[3 * 14 + 2] = kSH3e * (xx - yy);
+    dB[3 * 15 + 0] = -kSH3a * (3.0f * xx - 3.0f * yy);
+    dB[3 * 15 + 1] = 6.0f * kSH3a * x * y;
+}
+
 }  // namespace gsr

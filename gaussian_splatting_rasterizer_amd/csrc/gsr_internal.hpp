@@ -43,8 +43,9 @@ struct Workspace {
     uint32_t* pval_b;
     uint32_t* pair_g;      // Gaussian of each emitted pair, depth order
     uint2* ranges;         // per tile [start, end)
-    float4* partials;      // per slot: {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix}
-    float4* gv_sums;       // per reached record: {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix}
+    float4* partials;      // per slot, score replay (2 float4): {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix};
+                           // backward (3 float4): {U, U_x, U_y, U_xx}, {U_xy, U_yy, masked V_rg}, {masked V_b, 0, 0, 0}
+    float4* gv_sums;       // per reached record: the sums of the same layout (2 or 3 float4)
     uint64_t* rec_masks;   // per 64 records: {live mask, reached mask}
     float4* pixel;         // per pixel: rendered colour (rgb), final transmittance
     uint2* pixel_stats;    // per pixel: entries evaluated, entries past the distance cut
@@ -130,7 +131,13 @@ hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* so
                          const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st);
 hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* observed,
                          float eps, float den_min, hipStream_t st);
-hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, hipStream_t st);
+// per record, the sums of the NQ-float4 partials of the slots flagged in slot_bits, plus the
+// live / reached masks (nq = 2: score replay, 3: backward)
+hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, int nq, hipStream_t st);
+hipError_t launch_backward(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* grad_color,
+                           hipStream_t st);
+hipError_t launch_grads(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
+                        const gs_gaussian_grads& out, hipStream_t st);
 hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
                          float eps, float lambda, float* tokens, hipStream_t st);
 hipError_t launch_exp2(const float* in, float* out, int64_t n, hipStream_t st);

@@ -48,35 +48,6 @@ namespace gsr {
 
 constexpr int kReplayBatch = 128;
 
-// Reduce eight values over the 64 lanes; returns in every lane the total of
-// component (lane >> 3) & 7.  Reduce-scatter with gfx950 lane permutations:
-//   permlane32_swap pairs component i (kept in lanes 0-31) with i + 4 (lanes 32-63),
-//   permlane16_swap pairs rows, a row_ror:8 exchange splits each row in halves,
-//   then quad_perm / row_half_mirror adds finish the sum inside 8-lane groups.
-template <int CTRL>
-__device__ __forceinline__ float fadd_dpp(float keep, float send) {
-    return keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ float wave_reduce8(const float (&x)[8], int lane) {
-    float a[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[i]), __float_as_uint(x[i + 4]), false, false);
-        a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    const auto s0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[0]), __float_as_uint(a[2]), false, false);
-    const auto s1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[1]), __float_as_uint(a[3]), false, false);
-    const float b0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);  // rows hold components 0, 2, 4, 6
-    const float b1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);  // rows hold components 1, 3, 5, 7
-    const bool hi8 = lane & 8;
-    float c = fadd_dpp<0x128>(hi8 ? b1 : b0, hi8 ? b0 : b1);  // row_ror:8
-    c = fadd_dpp<0xB1>(c, c);                                  // quad_perm [1,0,3,2]
-    c = fadd_dpp<0x4E>(c, c);                                  // quad_perm [2,3,0,1]
-    c = fadd_dpp<0x141>(c, c);                                 // row_half_mirror
-    return c;
-}
-
 __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
                                                 const uint32_t* __restrict__ slot_base,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
@@ -297,6 +268,8 @@ __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */,
 // range and adds the partials of the set bits in slot order.
 constexpr int kGatherThreads = 256;
 
+// NQ float4 per slot and per record: 2 for the score replay, 3 for the backward.
+template <int NQ>
 __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                                                                  const uint32_t* __restrict__ tiles_touched,
                                                                  const uint32_t* __restrict__ slot_base,
@@ -308,7 +281,9 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
     const int lane = threadIdx.x & 63;
     if (rid - lane >= VG) return;  // the whole wave is past the end
     bool live = false, reached = false;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 a[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) a[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (rid < VG) {
         const uint32_t tt = tiles_touched[rid];
         live = tt != 0u;  // culled records touch no tile
@@ -322,17 +297,17 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                 while (bits) {
                     const uint32_t slot = 32u * w + (uint32_t)__builtin_ctz(bits);
                     bits &= bits - 1u;
-                    const float4 p0 = partials[2 * (int64_t)slot];
-                    const float4 p1 = partials[2 * (int64_t)slot + 1];
+                    float4 p[NQ];
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) p[q] = partials[NQ * (int64_t)slot + q];
                     reached = true;
-                    a.x += p0.x;
-                    a.y += p0.y;
-                    a.z += p0.z;
-                    a.w += p0.w;
-                    b.x += p1.x;
-                    b.y += p1.y;
-                    b.z += p1.z;
-                    b.w += p1.w;
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        a[q].x += p[q].x;
+                        a[q].y += p[q].y;
+                        a[q].z += p[q].z;
+                        a[q].w += p[q].w;
+                    }
                 }
             }
         }
@@ -345,16 +320,20 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
         rec_masks[2 * ((rid - lane) >> 6) + 1] = reached_mask;
     }
     if (reached) {
-        gv_sums[2 * rid] = a;
-        gv_sums[2 * rid + 1] = b;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) gv_sums[NQ * rid + q] = a[q];
     }
 }
 
-hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, hipStream_t st) {
+hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, int nq, hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gather_slots, dim3((unsigned)((s.VG + kGatherThreads - 1) / kGatherThreads)),
-                       dim3(kGatherThreads), 0, st, s.VG, ws.tiles_touched, ws.slot_base, ws.slot_bits, ws.partials,
-                       ws.gv_sums, ws.rec_masks);
+    const dim3 grid((unsigned)((s.VG + kGatherThreads - 1) / kGatherThreads)), block(kGatherThreads);
+    if (nq == 3)
+        hipLaunchKernelGGL(k_gather_slots<3>, grid, block, 0, st, s.VG, ws.tiles_touched, ws.slot_base,
+                           ws.slot_bits, ws.partials, ws.gv_sums, ws.rec_masks);
+    else
+        hipLaunchKernelGGL(k_gather_slots<2>, grid, block, 0, st, s.VG, ws.tiles_touched, ws.slot_base,
+                           ws.slot_bits, ws.partials, ws.gv_sums, ws.rec_masks);
     return hipGetLastError();
 }
 

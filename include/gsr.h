@@ -20,7 +20,7 @@
  *     9 + 3 d_SH).
  *
  * Calling sequence, all on one stream:  gs_project -> gs_bin_sort -> gs_render
- * [-> gs_score_replay].  Each call returns a status and never aborts.
+ * [-> gs_score_replay] [-> gs_backward].  Each call returns a status and never aborts.
  *
  * Memory: every array argument is a DEVICE pointer unless marked "host".
  * The caller owns every buffer (inputs, outputs and the workspace); the
@@ -165,6 +165,40 @@ GSR_API gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32
  * with Q = eps + sum_v q_gv the cross-view support. */
 GSR_API gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens, hipStream_t stream);
 
+/* Gradients of a scalar loss with respect to the scene parameters, laid out
+ * like the gs_gaussians arrays they belong to (float32 device arrays, written,
+ * not accumulated; a null member is skipped):
+ *   means [n,3], quats [n,4] (of the quaternion as given, before its
+ *   normalisation), scales [n,3], opacities [n], sh [n,d,3]. */
+typedef struct {
+    float* means;
+    float* quats;
+    float* scales;
+    float* opacities;
+    float* sh;
+} gs_gaussian_grads;
+
+/* Renderer backward: the vector-Jacobian product of the rendered colour with
+ * `grad_color` = dL/dC_hat [n_views, height, width, 3] (float32 device), i.e.
+ * the exact gradient of the colour image of gs_render through the
+ * front-to-back composite, the 2D Gaussian, the EWA projection (covariance
+ * Jacobian at the field-of-view-clamped centre, 0.3 px^2 dilation), the
+ * covariance R_q diag(s)^2 R_q^T of the normalised quaternion and the scales,
+ * and the SH colour including its dependence on the view direction, with the
+ * render's float32 decisions held fixed (contributor sets and early stop,
+ * alpha clamp at 0.99 -- a clamped contribution passes no gradient to
+ * opacity or shape --, colour clamp at 0, field-of-view clamp).  The forward
+ * is Stage 1 of the page "Research Proposal: Renderer Score Tokens for
+ * Recurrent Gaussian Splatting" ("Two-Stage Algorithm", Standard Render) with
+ * the 3DGS primitive of the ATSplat summary page ("前置知识: 3DGS").
+ * Traverses the same tile bins and order as gs_render (valid after gs_render,
+ * before or after gs_score_replay), reading the scene arrays given to
+ * gs_project.  Asynchronous on `stream`; uses the workspace's partial and
+ * per-record sum areas, so it must not overlap gs_score_replay on the same
+ * context. */
+GSR_API gs_status gs_backward(gs_context* ctx, const float* grad_color, const gs_gaussian_grads* grads,
+                              hipStream_t stream);
+
 GSR_API const char* gs_status_string(gs_status s);
 GSR_API const char* gs_last_error(void);
 
@@ -204,7 +238,8 @@ GSR_API gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size
  * stage's launches (events are created by the library on first use and kept
  * until gs_context_destroy).  gs_profile_read waits for the recorded events,
  * writes the milliseconds and launch counts accumulated since the previous read
- * (arrays of GS_NUM_STAGES), and resets them. */
+ * for the first min(n_stages, GS_NUM_STAGES) stages into the host arrays ms and
+ * calls (n_stages entries each), and resets every stage's totals. */
 typedef enum {
     GS_STAGE_PROJECT = 0,
     GS_STAGE_DEPTH_SORT = 1,
@@ -215,10 +250,12 @@ typedef enum {
     GS_STAGE_RENDER = 6,
     GS_STAGE_REPLAY = 7,
     GS_STAGE_FINALIZE = 8,
-    GS_NUM_STAGES = 9
+    GS_STAGE_BACKWARD = 9,          /* gs_backward traversal */
+    GS_STAGE_BACKWARD_FINALIZE = 10, /* gs_backward slot gather and per-Gaussian chain rule */
+    GS_NUM_STAGES = 11
 } gs_stage;
 GSR_API gs_status gs_profile_enable(gs_context* ctx, int32_t enable);
-GSR_API gs_status gs_profile_read(gs_context* ctx, double* ms, int64_t* calls);
+GSR_API gs_status gs_profile_read(gs_context* ctx, double* ms, int64_t* calls, int32_t n_stages);
 
 #ifdef __cplusplus
 }

@@ -92,7 +92,7 @@ def _load():
         lib.orc_set_mean2d64.argtypes = [P, I32, I32, F64, F64]
         lib.orc_set_mean3d64.argtypes = [P, I32, P]
         lib.orc_set_params64.argtypes = [P, I32, P]
-        lib.orc_backward.argtypes = [P, P, P, P]
+        lib.orc_backward.argtypes = [P, P, P, I64, P, P]
         lib.orc_sh_basis_grad64.argtypes = [P, I64, I32, P]
         lib.orc_num_threads.restype = I32
         _lib = lib
@@ -280,18 +280,24 @@ class OracleScene:
         return np.array(sorted(out), dtype=np.int64)
 
     # -- renderer backward -----------------------------------------------------
-    def backward(self, grad_color, with_image_sums=False):
+    def backward(self, grad_color, with_image_sums=False, tiles=None):
         """Vector-Jacobian product of the colour image with `grad_color` [V,H,W,3]:
         gradients [G, 11 + 3 d] = [mean 3, quaternion 4, scale 3, opacity 1, SH d*3]
         (float64).  With `with_image_sums`, also the per-(view, Gaussian) image-space
-        sums [V, G, 9] = dL/d(mx, my, ca, cb, cc, o, c_r, c_g, c_b)."""
+        sums [V, G, 9] = dL/d(mx, my, ca, cb, cc, o, c_r, c_g, c_b).  With `tiles`
+        (global tile ids), only those tiles are walked: exact for the Gaussians
+        whose rectangles they cover (`tiles_of`)."""
         if self.n_pairs is None:
             self.build_lists()
         gC = np.ascontiguousarray(grad_color, dtype=np.float32)
         assert gC.shape == (self.V, self.H, self.W, 3)
         out = np.empty((self.G, 11 + 3 * self.d), dtype=np.float64)
         g2d = np.empty((self.V, self.G, 9), dtype=np.float64) if with_image_sums else None
-        self.lib.orc_backward(self.handle, _ptr(gC), _ptr(out), _ptr(g2d) if with_image_sums else None)
+        if tiles is not None:
+            tiles = np.ascontiguousarray(tiles, dtype=np.int64)
+        self.lib.orc_backward(self.handle, _ptr(gC), _ptr(tiles) if tiles is not None else None,
+                              0 if tiles is None else tiles.size, _ptr(out),
+                              _ptr(g2d) if with_image_sums else None)
         return (out, g2d) if with_image_sums else out
 
     def params64(self, g) -> np.ndarray:

@@ -1050,18 +1050,18 @@ void orc_sh_basis_grad64(const double* dirs, int64_t n, int d, double* out /* [n
  *   dG/dmu2D = G conic d,  dG/d(ca, cb, cc) = -G (dx^2 / 2, dx dy, dy^2 / 2);
  * the colour gets dC/dc_k = T_k alpha_k.  Sums per (Gaussian, view) into
  * g2d[v*G + g][NB2D]. */
-static void backward_image(scene* s, const float* gC, double* g2d)
+static void backward_image(scene* s, const float* gC, const int64_t* tiles, int64_t n_tiles, double* g2d)
 {
     const int T = s->TX * s->TY;
     int64_t maxlen = 0;
     for (int64_t i = 0; i < (int64_t)s->V * T; ++i)
         if (s->starts[i + 1] - s->starts[i] > maxlen) maxlen = s->starts[i + 1] - s->starts[i];
-    const int64_t n_tiles = (int64_t)s->V * T;
 #pragma omp parallel
     {
         contrib* cl = (contrib*)malloc(sizeof(contrib) * (size_t)maxlen + 1);
 #pragma omp for schedule(dynamic, 1)
-        for (int64_t tile = 0; tile < n_tiles; ++tile) {
+        for (int64_t it = 0; it < n_tiles; ++it) {
+            const int64_t tile = tiles ? tiles[it] : it;
             int v = (int)(tile / T), t = (int)(tile % T);
             int tx = t % s->TX, ty = t / s->TX;
             const int32_t* list = s->ids + s->starts[tile];
@@ -1248,12 +1248,15 @@ static void backward_params(scene* s, const double* g2d, double* out)
 }
 
 /* Full backward: out [G][11 + 3 d]; g2d (optional) receives the image-space
- * sums [V*G][NB2D] (record index v*G + g).  Needs the lists. */
-void orc_backward(void* p, const float* gC, double* out, double* g2d_out)
+ * sums [V*G][NB2D] (record index v*G + g).  With tiles != NULL only those
+ * tiles' pixels are walked: the result is complete for every Gaussian whose
+ * tile rectangles (in every view) lie inside them.  Needs the lists. */
+void orc_backward(void* p, const float* gC, const int64_t* tiles, int64_t n_tiles, double* out, double* g2d_out)
 {
     scene* s = (scene*)p;
     double* g2d = (double*)calloc((size_t)s->V * s->G * NB2D + 1, sizeof(double));
-    backward_image(s, gC, g2d);
+    if (!tiles) n_tiles = (int64_t)s->V * s->TX * s->TY;
+    backward_image(s, gC, tiles, n_tiles, g2d);
     backward_params(s, g2d, out);
     if (g2d_out) memcpy(g2d_out, g2d, sizeof(double) * (size_t)s->V * s->G * NB2D);
     free(g2d);

@@ -32,7 +32,7 @@ import math
 
 import numpy as np
 
-__all__ = ["Scene", "make_scene", "CONFIG_NAMES", "c1_occlusion_toy", "c2_resplat_step",
+__all__ = ["Scene", "make_scene", "rotated_clip_scene", "CONFIG_NAMES", "c1_occlusion_toy", "c2_resplat_step",
            "c3_atsplat_compact", "c4_dense_pixel_aligned", "c5_multiview_layers", "view_sweep"]
 
 SH_C0 = 0.28209479177387814  # 1 / (2 sqrt(pi)); used only to draw degree-0 colours
@@ -289,6 +289,46 @@ CONFIG_NAMES = {
 
 _MAKERS = {1: c1_occlusion_toy, 2: c2_resplat_step, 3: c3_atsplat_compact,
            4: c4_dense_pixel_aligned, 5: c5_multiview_layers}
+
+
+def _rot_xyz(ax, ay, az) -> np.ndarray:
+    cx, sx, cy, sy, cz, sz = np.cos(ax), np.sin(ax), np.cos(ay), np.sin(ay), np.cos(az), np.sin(az)
+    Rx = np.array([[1, 0, 0], [0, cx, -sx], [0, sx, cx]])
+    Ry = np.array([[cy, 0, sy], [0, 1, 0], [-sy, 0, cy]])
+    Rz = np.array([[cz, -sz, 0], [sz, cz, 0], [0, 0, 1]])
+    return Rz @ Ry @ Rx
+
+
+def rotated_clip_scene(seed=21, n=16, W=32, H=32, sh_degree=3,
+                       angles=((0.04, -0.06, 0.03), (-0.03, 0.05, -0.02))) -> Scene:
+    """tiny_scene seen by rotated cameras (same centres; one per entry of `angles`,
+    rotations Rz Ry Rx), plus two large Gaussians whose centres lie beyond 1.3x
+    the half field of view of view 0, one in x and one in y."""
+    sc = tiny_scene(seed=seed, n=n, n_views=len(angles), W=W, H=H, sh_degree=sh_degree)
+    cams = np.array(sc.cams, dtype=np.float64)
+    for i, a in enumerate(angles):
+        R = _rot_xyz(*a)
+        centre = -cams[i, 9:12]               # identity-rotation camera: t = -centre
+        cams[i, 0:9] = R.reshape(-1)
+        cams[i, 9:12] = -R @ centre
+    cams = cams.astype(np.float32)
+    R0 = cams[0, 0:9].reshape(3, 3).astype(np.float64)
+    t0 = cams[0, 9:12].astype(np.float64)
+    extra = np.array([R0.T @ (np.array([tx * 3.0, ty * 3.0, 3.0]) - t0)
+                      for tx, ty in [(0.8, 0.1), (-0.1, -0.78)]], dtype=np.float32)
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    d = sc.d
+    sh_x = rng.normal(0, 0.3, size=(2, d, 3))
+    sh_x[:, 0, :] = 0.3 / SH_C0
+    q_x = _unit_quats(rng, 2)
+    return dataclasses.replace(
+        sc, name="rotated_clip", cams=cams,
+        means=np.concatenate([sc.means, extra]),
+        quats=np.concatenate([sc.quats, q_x.astype(np.float32)]),
+        scales=np.concatenate([sc.scales, np.array([[0.6, 0.45, 0.5], [0.5, 0.6, 0.4]], np.float32)]),
+        opacities=np.concatenate([sc.opacities, np.array([0.7, 0.6], np.float32)]),
+        sh=np.concatenate([sc.sh, sh_x.astype(np.float32)]),
+        means_perturbed=np.concatenate([sc.means_perturbed, extra]))
 
 
 def make_scene(config: int, **overrides) -> Scene:

@@ -94,6 +94,9 @@ def test_calls_out_of_order_are_rejected_without_launching():
         assert lib.gs_bin_sort(ctx, None, ctypes.byref(n)) == b.GS_ERR_STATE
         assert lib.gs_render(ctx, None, None, None, None) == b.GS_ERR_STATE
         assert lib.gs_score_replay(ctx, ctypes.c_void_p(256), ctypes.c_void_p(256), None) == b.GS_ERR_STATE
+        grads = b.gs_gaussian_grads(256, 256, 256, 256, 256)
+        assert lib.gs_backward(ctx, ctypes.c_void_p(256), ctypes.byref(grads), None) == b.GS_ERR_STATE
+        assert lib.gs_backward(None, ctypes.c_void_p(256), ctypes.byref(grads), None) == b.GS_ERR_INVALID_ARGUMENT
         # mismatched scene size and null parameters: rejected before any launch
         g = b.gs_gaussians(256, 256, 256, 256, 256, 999, 3)
         cams = b.make_cameras([[1, 0, 0, 0, 1, 0, 0, 0, 1, 0, 0, 0, 64, 64, 32, 24]] * 2)
@@ -115,11 +118,18 @@ def test_calls_out_of_order_are_rejected_without_launching():
         assert lib.gs_debug_export(ctx, b.GS_EXPORT_RECORDS, ctypes.c_void_p(256), 1 << 30, None) == b.GS_ERR_STATE
         assert lib.gs_debug_export(ctx, 99, ctypes.c_void_p(256), 16, None) == b.GS_ERR_INVALID_ARGUMENT
         # profiling with nothing recorded
-        ms = (ctypes.c_double * 9)()
-        calls = (ctypes.c_int64 * 9)()
+        # (the read writes only as many stages as the caller's arrays hold)
+        ms = (ctypes.c_double * 4)(*[-1.0] * 4)
+        calls = (ctypes.c_int64 * 4)(*[-1] * 4)
         assert lib.gs_profile_enable(ctx, 1) == b.GS_OK
-        assert lib.gs_profile_read(ctx, ms, calls) == b.GS_OK
-        assert list(calls) == [0] * 9
+        assert lib.gs_profile_read(ctx, ms, calls, 3) == b.GS_OK
+        assert list(calls) == [0, 0, 0, -1] and list(ms) == [0.0, 0.0, 0.0, -1.0]
+        assert lib.gs_profile_read(ctx, ms, calls, -1) == b.GS_ERR_INVALID_ARGUMENT
+        n = len(b.STAGES)
+        ms = (ctypes.c_double * n)()
+        calls = (ctypes.c_int64 * n)()
+        assert lib.gs_profile_read(ctx, ms, calls, n) == b.GS_OK
+        assert list(calls) == [0] * n
     finally:
         lib.gs_context_destroy(ctx)
 

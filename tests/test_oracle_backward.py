@@ -15,9 +15,6 @@ direction).  It is pinned here against things other than itself:
 """
 from __future__ import annotations
 
-import dataclasses
-import math
-
 import numpy as np
 import pytest
 
@@ -25,54 +22,9 @@ import oracle
 import scenes
 
 
-def _rot(ax, ay, az):
-    cx, sx, cy, sy, cz, sz = math.cos(ax), math.sin(ax), math.cos(ay), math.sin(ay), math.cos(az), math.sin(az)
-    Rx = np.array([[1, 0, 0], [0, cx, -sx], [0, sx, cx]])
-    Ry = np.array([[cy, 0, sy], [0, 1, 0], [-sy, 0, cy]])
-    Rz = np.array([[cz, -sz, 0], [sz, cz, 0], [0, 0, 1]])
-    return Rz @ Ry @ Rx
-
-
-def _rotated_cams(cams, angles):
-    out = np.array(cams, dtype=np.float64)
-    for i, a in enumerate(angles):
-        R = _rot(*a)
-        centre = -out[i, 9:12]              # identity-rotation camera: t = -centre
-        out[i, 0:9] = R.reshape(-1)
-        out[i, 9:12] = -R @ centre
-    return out.astype(np.float32)
-
-
-def _backward_scene():
-    """Tiny degree-3 scene seen by two rotated cameras, plus two large Gaussians
-    whose centres lie beyond the 1.3x field-of-view clamp in x (view 0) and y."""
-    sc = scenes.tiny_scene(seed=21, n=16, n_views=2, W=32, H=32, sh_degree=3)
-    cams = _rotated_cams(sc.cams, [(0.04, -0.06, 0.03), (-0.03, 0.05, -0.02)])
-    R0 = cams[0, 0:9].reshape(3, 3).astype(np.float64)
-    t0 = cams[0, 9:12].astype(np.float64)
-    extra = []
-    for tan_x, tan_y in [(0.8, 0.1), (-0.1, -0.78)]:
-        xc = np.array([tan_x * 3.0, tan_y * 3.0, 3.0])          # camera-0 space
-        extra.append(R0.T @ (xc - t0))
-    rng = np.random.default_rng(5)
-    d = sc.d
-    sh_x = rng.normal(0, 0.3, size=(2, d, 3))
-    sh_x[:, 0, :] = 0.3 / scenes.SH_C0
-    q_x = rng.normal(size=(2, 4))
-    q_x /= np.linalg.norm(q_x, axis=1, keepdims=True)
-    return dataclasses.replace(
-        sc, cams=cams,
-        means=np.concatenate([sc.means, np.array(extra, np.float32)]),
-        quats=np.concatenate([sc.quats, q_x.astype(np.float32)]),
-        scales=np.concatenate([sc.scales, np.array([[0.6, 0.45, 0.5], [0.5, 0.6, 0.4]], np.float32)]),
-        opacities=np.concatenate([sc.opacities, np.array([0.7, 0.6], np.float32)]),
-        sh=np.concatenate([sc.sh, sh_x.astype(np.float32)]),
-        means_perturbed=np.concatenate([sc.means_perturbed, np.array(extra, np.float32)]))
-
-
 @pytest.fixture(scope="module")
 def bw_setup():
-    sc = _backward_scene()
+    sc = scenes.rotated_clip_scene()
     gC = np.random.default_rng(2).uniform(-1, 1, size=(sc.n_views, sc.height, sc.width, 3)).astype(np.float32)
     o = oracle.OracleScene(sc)
     o.build_lists()
