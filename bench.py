@@ -6,7 +6,9 @@ written) over one synthetic scene whose parameters and observation already sit
 in HBM.  Prints ONE JSON line with the throughput (rendered+replayed Mpix/s),
 Gaussian-pixel contributions/s, per-stage times (HIP events on the stream the
 kernels run on), the roofline of the dominant kernel and the CPU oracle timed
-on a bounded sample on the host cores.
+on a bounded sample on the host cores.  The renderer backward (gs_backward of
+1/2 |C_hat - C_obs|^2 over the last step's render) is timed separately and
+reported under "backward"; it is not part of the step.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5]
 
@@ -33,6 +35,8 @@ OPS_EVAL = 8        # dx, dy, the quadratic form (2 mul, 2 fma, 1 mul) and the d
 OPS_NEAR = 15       # the exponential (rint, sub, 7 fma, cvt, ldexp), o*G, clamp (cmp, select), alpha cut
 OPS_CONTRIB_FWD = 20    # 1-alpha, T(1-alpha), cut, w, 3 products, 3 compensated adds (4 each), count
 OPS_CONTRIB_REPLAY = 58  # the same plus suffix, reciprocal, rho, mask, the 8 partials and their sums
+OPS_CONTRIB_BWD = 70     # forward 20, suffix 6, <g,c> and <g,S> 6, 1-alpha, reciprocal, u and its mask 4,
+                         # the 9 partials 8, their wave reduction 26 (eight-value reduce-scatter + one sum)
 
 
 def parse_args():
@@ -44,6 +48,8 @@ def parse_args():
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                    help="budget of rendering work for the CPU oracle sample (0 disables)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip the separately timed renderer backward (gs_backward of 1/2 |C_hat - C|^2)")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the benchmark line: view-count / resolution scaling (4, 8, 16, 32 views at "
                         "256x448 and 512x960 over a fixed Gaussian set), one JSON line per point")
@@ -87,7 +93,8 @@ def _sources_sha256(names):
 
 KERNEL_SOURCES = {"k_project": ["project.hip"], "k_render": ["render.hip"], "k_replay": ["replay.hip"],
                   "k_gather_slots": ["replay.hip"], "k_tokens": ["replay.hip"], "k_onesweep": ["binning.hip"],
-                  "k_emit": ["binning.hip"], "k_ranges": ["binning.hip"], "k_digit_hist": ["binning.hip"]}
+                  "k_emit": ["binning.hip"], "k_ranges": ["binning.hip"], "k_digit_hist": ["binning.hip"],
+                  "k_backward": ["backward.hip"], "k_grads": ["backward.hip"]}
 
 
 def kernel_source_sha256(kernel):
@@ -172,6 +179,27 @@ def main():
         prof = binding.gs_profile_read(r.ctx)
         binding.gs_profile_enable(r.ctx, False)
 
+        # renderer backward of 1/2 |C_hat - C_obs|^2 on the same render, timed on its own
+        bwd = None
+        if not args.no_backward:
+            grad_color = (outputs[0] - obs).contiguous()
+            grads = r.new_grads()
+            for _ in range(args.warmup):
+                r.backward(grad_color, grads)
+            stream.synchronize()
+            binding.gs_profile_enable(r.ctx, True)
+            binding.gs_profile_read(r.ctx)
+            tb = time.perf_counter()
+            for _ in range(args.steps):
+                r.backward(grad_color, grads)
+            stream.synchronize()
+            tb = time.perf_counter() - tb
+            bprof = binding.gs_profile_read(r.ctx)
+            binding.gs_profile_enable(r.ctx, False)
+            bwd = dict(ms=1e3 * tb / args.steps,
+                       stages={k: bprof[k][0] / max(bprof[k][1], 1) for k in ("backward", "backward_finalize")},
+                       finite=bool(all(torch.isfinite(t).all().item() for t in grads.values())))
+
         color, T, n = outputs
         stats = r.export(binding.GS_EXPORT_PIXEL_STATS).view(-1, 2).to(torch.int64)
         K = int(n.to(torch.int64).sum().item())
@@ -189,7 +217,7 @@ def main():
     contribs = K / (elapsed / args.steps)
 
     c = dict(G=sc.n, V=V, d=sc.d, P=P, T=T_tiles, n_live=n_live)
-    stages = {k: (ms / max(cnt, 1), cnt) for k, (ms, cnt) in prof.items()}
+    stages = {k: (ms / max(cnt, 1), cnt) for k, (ms, cnt) in prof.items() if cnt > 0}
     # The dominant single kernel is the score replay (one launch per step, the
     # "replay" stage): bound by fp32 VALU work, counted algorithmically.
     t_rep = stages["replay"][0] * 1e-3
@@ -214,6 +242,18 @@ def main():
                          "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": by,
                          "avg_launch_ms": round(stages[st][0], 4)}
 
+    backward = None
+    if bwd is not None:
+        t_b = bwd["stages"]["backward"] * 1e-3
+        ops_b = OPS_EVAL * E + OPS_NEAR * E_near + OPS_CONTRIB_BWD * K
+        backward = {"ms": round(bwd["ms"], 4), "mpix_per_s": round(V * H * W / (bwd["ms"] * 1e-3) / 1e6, 2),
+                    "stages_ms": {k: round(v, 4) for k, v in bwd["stages"].items()},
+                    "k_backward": {"bound": "alu", "achieved": round(ops_b / t_b / 1e12, 3),
+                                   "frac": round(ops_b / t_b / 1e12 / ALU_PEAK_TOPS, 4),
+                                   "traffic": measured_traffic("k_backward", workload),
+                                   "avg_launch_ms": round(bwd["stages"]["backward"], 4), "ops_per_launch": ops_b},
+                    "grads_finite": bwd["finite"], "loss": "1/2 |C_hat - C_obs|^2"}
+
     out = {
         "metric": "render+score-replay Mpix/s",
         "value": round(mpix, 2),
@@ -236,6 +276,8 @@ def main():
         "stage_rooflines": secondary,
         "tokens_finite": finite,
     }
+    if backward is not None:
+        out["backward"] = backward
 
     if not args.no_cpu_baseline and args.cpu_baseline_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(sc, args.cpu_baseline_seconds)

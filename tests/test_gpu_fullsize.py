@@ -3,7 +3,9 @@ one by one: every pixel of a set of sampled tiles (colour <= 1e-5, counts and
 final transmittance bit-exact), the complete tile lists (bit-exact, checked on
 the sampled tiles against per-tile brute-force scans), and the tokens of sampled
 Gaussians (<= 1e-3 relative L2; the oracle renders every tile their rectangles
-touch, in every view).  The GPU runs the same launch configuration as bench.py.
+touch, in every view), and the renderer-backward gradients of the same sampled
+Gaussians for a seeded upstream gradient (<= 1e-4 relative L2 per parameter
+group).  The GPU runs the same launch configuration as bench.py.
 
 The observation here is a synthetic image (0.5 plus the workload's pixel noise
 scaled by 5) rather than a render of the perturbed scene, so that the oracle
@@ -46,9 +48,15 @@ def _run(config):
     ranges = r.export(binding.GS_EXPORT_RANGES).cpu().numpy()
     color, T, n = r.render()
     tok = r.score_replay(torch.from_numpy(obs).cuda())
+    gC = np.random.default_rng(200 + config).uniform(
+        -1, 1, size=(sc.n_views, sc.height, sc.width, 3)).astype(np.float32)
+    grads = r.backward(torch.from_numpy(gC).cuda())
     torch.cuda.synchronize()
     gpu = dict(ids=ids, ranges=ranges, n_pairs=r.n_pairs, color=color.cpu().numpy(), T=T.cpu().numpy(),
-               n=n.cpu().numpy(), tokens=tok.cpu().numpy())
+               n=n.cpu().numpy(), tokens=tok.cpu().numpy(), gC=gC,
+               grads=np.concatenate([grads["means"].cpu().numpy(), grads["quats"].cpu().numpy(),
+                                     grads["scales"].cpu().numpy(), grads["opacities"].cpu().numpy()[:, None],
+                                     grads["sh"].cpu().numpy().reshape(sc.n, -1)], axis=1).astype(np.float64))
     r.close()
     del r
     torch.cuda.empty_cache()
@@ -69,7 +77,10 @@ def _run(config):
     c_ref, T_ref, n_ref, _ = o.render(tiles=render_tiles, obs=obs)
     tok_ref = o.tokens()
     starts, _ = o.lists()
-    ref = dict(o=o, tiles=tiles, pick=pick, color=c_ref, T=T_ref, n=n_ref, tokens=tok_ref, starts=starts)
+    # backward of the picked Gaussians: every tile of their rectangles, in every view
+    grads_ref = o.backward(gpu["gC"], tiles=o.tiles_of(pick))[pick]
+    ref = dict(o=o, tiles=tiles, pick=pick, color=c_ref, T=T_ref, n=n_ref, tokens=tok_ref, starts=starts,
+               grads=grads_ref)
     _CACHE[config] = (sc, obs, ref, gpu)
     return _CACHE[config]
 
@@ -122,3 +133,25 @@ def test_fullsize_tokens(config):
     print(f"config {config}: max token rel err {rel.max():.3e} over {len(rel)} Gaussians")
     assert np.all(np.isfinite(z))
     assert rel.max() <= TOKEN_RTOL, (rel.max(), ref["pick"][rel.argmax()])
+
+
+GRAD_RTOL = 1e-4
+
+
+@pytest.mark.parametrize("config", CONFIGS)
+def test_fullsize_backward(config):
+    """Renderer backward of a seeded uniform(-1, 1) upstream gradient: per parameter
+    group, relative L2 over the sampled Gaussians within 1e-4."""
+    sc, obs, ref, gpu = _run(config)
+    got = gpu["grads"][ref["pick"]]
+    want = ref["grads"]
+    assert np.all(np.isfinite(got))
+    groups = {"means": slice(0, 3), "quats": slice(3, 7), "scales": slice(7, 10), "opacities": slice(10, 11),
+              "sh": slice(11, 11 + 3 * sc.d)}
+    bad = []
+    for name, sl in groups.items():
+        rel = np.linalg.norm(got[:, sl] - want[:, sl]) / max(np.linalg.norm(want[:, sl]), 1e-30)
+        print(f"config {config} {name}: rel L2 {rel:.2e} over {len(ref['pick'])} Gaussians")
+        if not rel <= GRAD_RTOL:
+            bad.append((name, rel))
+    assert not bad, bad
