@@ -439,7 +439,7 @@ gs_status gs_backward(gs_context* ctx, const float* grad_color, const gs_gaussia
     ctx->timer.begin(stream);
     e = launch_gather_slots(ctx->s, ctx->ws, 3, stream);
     if (e != hipSuccess) return hip_fail(e, "backward gather");
-    e = launch_grads(ctx->scene, ctx->cams, ctx->s, ctx->ws, *grads, stream);
+    e = launch_backward_finalize(ctx->scene, ctx->cams, ctx->s, ctx->ws, *grads, stream);
     if (e != hipSuccess) return hip_fail(e, "gradients");
     ctx->timer.end(GS_STAGE_BACKWARD_FINALIZE, stream);
     return GS_OK;

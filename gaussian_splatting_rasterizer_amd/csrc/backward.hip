@@ -28,12 +28,21 @@
 // stored with plain stores at the pair's slot; the slot's bit is set in
 // slot_bits.  The slot gather then sums each record's partials in slot order.
 //
-// k_grads: one thread per Gaussian, float64 chain rule over the views:
-// projected centre -> camera-space centre; conic -> dilated 2D covariance
-// -> (perspective Jacobian at the clamped centre, camera covariance R Sigma R^T)
-// -> world covariance M M^T with M = R_q diag(s) -> scales and the unit
-// quaternion -> the input quaternion; SH colour -> coefficients and the view
-// direction -> centre.
+// k_grads: after the slot gather (per record, the sums of its flagged slots),
+// one thread per Gaussian loops over the views in float64: projected centre ->
+// camera-space centre; conic -> dilated 2D covariance -> (perspective Jacobian
+// at the clamped centre, camera covariance R Sigma R^T) -> world covariance;
+// SH colour -> coefficients and, through the basis, the view direction ->
+// centre.  The world-covariance gradient is summed over the views and pulled
+// back once through M M^T, M = R_q diag(s), to the scales and the unit
+// quaternion, then to the input quaternion.  The per-Gaussian work (R_q, M,
+// M M^T) is shared by all views, which is why the views are a loop and not
+// threads: the kernel is bound by float64 issue, so work per view is what
+// counts.  The SH part runs as a second pass over the views (re-reading its
+// three sums and the view direction), so that its 3 d accumulators are not
+// live during the covariance chain (204 instead of 256+ registers).  Its
+// arithmetic is value arithmetic only and is contracted to fused
+// multiply-adds.
 #include "gsr_internal.hpp"
 
 namespace gsr {
@@ -208,9 +217,6 @@ hipError_t launch_backward(const Sizes& s, const Workspace& ws, const uint32_t* 
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// per-Gaussian chain rule
-// ---------------------------------------------------------------------------
 constexpr int kGradThreads = 128;
 
 template <int D>
@@ -221,6 +227,7 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
                                                         int64_t G, int V, int W, int H, CamPack cams,
                                                         const uint64_t* __restrict__ rec_masks,
                                                         const float4* __restrict__ gv_sums, gs_gaussian_grads out) {
+#pragma clang fp contract(fast)
     const int64_t g = (int64_t)blockIdx.x * kGradThreads + threadIdx.x;
     if (g >= G) return;
     const double mu[3] = {means[3 * g], means[3 * g + 1], means[3 * g + 2]};
@@ -229,8 +236,8 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
     const double o = opac[g];
     const float* shg = sh + 3 * D * g;
 
-    const double qn = sqrt(qi[0] * qi[0] + qi[1] * qi[1] + qi[2] * qi[2] + qi[3] * qi[3]);
-    const double qw = qi[0] / qn, qx = qi[1] / qn, qy = qi[2] / qn, qz = qi[3] / qn;
+    const double iqn = 1.0 / sqrt(qi[0] * qi[0] + qi[1] * qi[1] + qi[2] * qi[2] + qi[3] * qi[3]);
+    const double qw = qi[0] * iqn, qx = qi[1] * iqn, qy = qi[2] * iqn, qz = qi[3] * iqn;
     const double Rq[9] = {1 - 2 * (qy * qy + qz * qz), 2 * (qx * qy - qw * qz), 2 * (qx * qz + qw * qy),
                           2 * (qx * qy + qw * qz), 1 - 2 * (qx * qx + qz * qz), 2 * (qy * qz - qw * qx),
                           2 * (qx * qz - qw * qy), 2 * (qy * qz + qw * qx), 1 - 2 * (qx * qx + qy * qy)};
@@ -249,9 +256,6 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
     double gmu[3] = {0.0, 0.0, 0.0};
     double GS[9] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};  // dL/d(M M^T)
     double sumU = 0.0;
-    float gsh[3 * D];
-#pragma unroll
-    for (int k = 0; k < 3 * D; ++k) gsh[k] = 0.0f;
     bool any = false;
 
     for (int v = 0; v < V; ++v) {
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
         const uint64_t bit = 1ull << (rid & 63);
         if (!(rec_masks[2 * (rid >> 6) + 1] & bit)) continue;  // culled or never reached: no gradient
         any = true;
-        const float4 p0 = gv_sums[3 * rid], p1 = gv_sums[3 * rid + 1], p2 = gv_sums[3 * rid + 2];
+        const float4 p0 = gv_sums[3 * rid], p1 = gv_sums[3 * rid + 1];
         const float* cam = cams.c[v];
         double R[9];
 #pragma unroll
@@ -280,7 +284,10 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
-            for (int j = 0; j < 3; ++j) Cc[3 * i + j] = Tm[3 * i] * R[3 * j] + Tm[3 * i + 1] * R[3 * j + 1] + Tm[3 * i + 2] * R[3 * j + 2];
+            for (int j = i; j < 3; ++j) {
+                Cc[3 * i + j] = Tm[3 * i] * R[3 * j] + Tm[3 * i + 1] * R[3 * j + 1] + Tm[3 * i + 2] * R[3 * j + 2];
+                Cc[3 * j + i] = Cc[3 * i + j];
+            }
 
         // perspective Jacobian at the centre clamped to 1.3x the half field of view
         const double limx = 1.3 * (0.5 * W / fx), limy = 1.3 * (0.5 * H / fy);
@@ -347,32 +354,6 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
 #pragma unroll
         for (int j = 0; j < 3; ++j) gmu[j] += R[j] * gtx + R[3 + j] * gty + R[6 + j] * gtz;
 
-        // SH colour along the view direction (colour clamp already applied to V)
-        const double ccx = -(R[0] * t0 + R[3] * t1 + R[6] * t2);
-        const double ccy = -(R[1] * t0 + R[4] * t1 + R[7] * t2);
-        const double ccz = -(R[2] * t0 + R[5] * t1 + R[8] * t2);
-        const double dvx = mu[0] - ccx, dvy = mu[1] - ccy, dvz = mu[2] - ccz;
-        const double len = sqrt(dvx * dvx + dvy * dvy + dvz * dvz), il = 1.0 / len;
-        const double dirx = dvx * il, diry = dvy * il, dirz = dvz * il;
-        const float gp0 = p1.z, gp1 = p1.w, gp2 = p2.x;
-        float B[D], dB[3 * D];
-        sh_basis_f32((float)dirx, (float)diry, (float)dirz, D, B);
-        sh_basis_grad_f32((float)dirx, (float)diry, (float)dirz, D, dB);
-        float gd0 = 0.f, gd1 = 0.f, gd2 = 0.f;
-#pragma unroll
-        for (int k = 0; k < D; ++k) {
-            gsh[3 * k] += B[k] * gp0;
-            gsh[3 * k + 1] += B[k] * gp1;
-            gsh[3 * k + 2] += B[k] * gp2;
-            const float gB = shg[3 * k] * gp0 + shg[3 * k + 1] * gp1 + shg[3 * k + 2] * gp2;
-            gd0 += gB * dB[3 * k];
-            gd1 += gB * dB[3 * k + 1];
-            gd2 += gB * dB[3 * k + 2];
-        }
-        const double dd = (double)gd0 * dirx + (double)gd1 * diry + (double)gd2 * dirz;
-        gmu[0] += ((double)gd0 - dirx * dd) * il;
-        gmu[1] += ((double)gd1 - diry * dd) * il;
-        gmu[2] += ((double)gd2 - dirz * dd) * il;
     }
 
     double gs_[3] = {0.0, 0.0, 0.0}, gq[4] = {0.0, 0.0, 0.0, 0.0};
@@ -400,11 +381,51 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
                                  qy * GR[5] + qx * GR[6] + qy * GR[7]);
         // q / |q|
         const double dot = qw * hw + qx * hx + qy * hy + qz * hz;
-        const double iqn = 1.0 / qn;
         gq[0] = (hw - qw * dot) * iqn;
         gq[1] = (hx - qx * dot) * iqn;
         gq[2] = (hy - qy * dot) * iqn;
         gq[3] = (hz - qz * dot) * iqn;
+    }
+    // second pass over the views: SH colour along the view direction (colour clamp already
+    // applied to the sums) -> coefficients, and the view-direction term of the centre
+    float gsh[3 * D];
+#pragma unroll
+    for (int k = 0; k < 3 * D; ++k) gsh[k] = 0.0f;
+    if (any) {
+        for (int v = 0; v < V; ++v) {
+            const int64_t rid = (int64_t)v * G + g;
+            if (!((rec_masks[2 * (rid >> 6) + 1] >> (rid & 63)) & 1ull)) continue;
+            const float4 p1 = gv_sums[3 * rid + 1], p2 = gv_sums[3 * rid + 2];
+            const float* cam = cams.c[v];
+            const double R0 = cam[0], R1 = cam[1], R2 = cam[2], R3 = cam[3], R4 = cam[4], R5 = cam[5];
+            const double R6 = cam[6], R7 = cam[7], R8 = cam[8];
+            const double t0 = cam[9], t1 = cam[10], t2 = cam[11];
+            const double ccx = -(R0 * t0 + R3 * t1 + R6 * t2);
+            const double ccy = -(R1 * t0 + R4 * t1 + R7 * t2);
+            const double ccz = -(R2 * t0 + R5 * t1 + R8 * t2);
+            const double dvx = mu[0] - ccx, dvy = mu[1] - ccy, dvz = mu[2] - ccz;
+            const double len = sqrt(dvx * dvx + dvy * dvy + dvz * dvz), il = 1.0 / len;
+            const double dirx = dvx * il, diry = dvy * il, dirz = dvz * il;
+            const float gp0 = p1.z, gp1 = p1.w, gp2 = p2.x;
+            float B[D], dB[3 * D];
+            sh_basis_f32((float)dirx, (float)diry, (float)dirz, D, B);
+            sh_basis_grad_f32((float)dirx, (float)diry, (float)dirz, D, dB);
+            float gd0 = 0.f, gd1 = 0.f, gd2 = 0.f;
+#pragma unroll
+            for (int k = 0; k < D; ++k) {
+                gsh[3 * k] += B[k] * gp0;
+                gsh[3 * k + 1] += B[k] * gp1;
+                gsh[3 * k + 2] += B[k] * gp2;
+                const float gB = shg[3 * k] * gp0 + shg[3 * k + 1] * gp1 + shg[3 * k + 2] * gp2;
+                gd0 += gB * dB[3 * k];
+                gd1 += gB * dB[3 * k + 1];
+                gd2 += gB * dB[3 * k + 2];
+            }
+            const double dd = (double)gd0 * dirx + (double)gd1 * diry + (double)gd2 * dirz;
+            gmu[0] += ((double)gd0 - dirx * dd) * il;
+            gmu[1] += ((double)gd1 - diry * dd) * il;
+            gmu[2] += ((double)gd2 - dirz * dd) * il;
+        }
     }
     if (out.means) {
         out.means[3 * g] = (float)gmu[0];
@@ -426,7 +447,7 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
     }
 }
 
-hipError_t launch_grads(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
+hipError_t launch_backward_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
                         const gs_gaussian_grads& out, hipStream_t st) {
     if (s.G == 0) return hipSuccess;
     const dim3 block(kGradThreads), grid((unsigned)((s.G + kGradThreads - 1) / kGradThreads));

@@ -136,8 +136,9 @@ hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* so
 hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, int nq, hipStream_t st);
 hipError_t launch_backward(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* grad_color,
                            hipStream_t st);
-hipError_t launch_grads(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
-                        const gs_gaussian_grads& out, hipStream_t st);
+// per (Gaussian, view): the record's backward sums and the chain rule to the parameters, summed over views
+hipError_t launch_backward_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s,
+                                    const Workspace& ws, const gs_gaussian_grads& out, hipStream_t st);
 hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
                          float eps, float lambda, float* tokens, hipStream_t st);
 hipError_t launch_exp2(const float* in, float* out, int64_t n, hipStream_t st);

@@ -224,6 +224,7 @@ hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* so
 // finalize
 // ---------------------------------------------------------------------------
 __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */, double ev[3]) {
+#pragma clang fp contract(fast)
     const double a00 = A[0], a01 = A[1], a02 = A[2], a11 = A[3], a12 = A[4], a22 = A[5];
     const double p1 = a01 * a01 + a02 * a02 + a12 * a12;
     const double q = (a00 + a11 + a22) / 3.0;
@@ -347,6 +348,7 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
                                                         const uint64_t* __restrict__ rec_masks,
                                                         const float4* __restrict__ gv_sums, double eps, double lambda,
                                                         float* __restrict__ tokens) {
+#pragma clang fp contract(fast)
     constexpr int DT = 9 + 3 * D;
     __shared__ float s_tok[kTokThreads * DT];
     const int64_t g0 = (int64_t)blockIdx.x * kTokThreads;
