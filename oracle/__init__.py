@@ -7,7 +7,8 @@ imports it; the two meet only through the seeded inputs of ``scenes``.
 
 The arithmetic lives in ``gsr_oracle.c`` (plain C, float64 values, float32
 canonical decisions, brute-force lists, explicit back-to-front suffix, literal
-score sums, Jacobi eigenvalues, an explicit chain-rule renderer backward);
+score sums, Jacobi eigenvalues, feature composite and attribution scatter, an
+explicit chain-rule renderer backward);
 this module builds it with gcc and wraps it
 with ctypes.  Everything here follows the page "Research Proposal: Renderer
 Score Tokens for Recurrent Gaussian Splatting" (Two-Stage Algorithm, Exact
@@ -92,6 +93,8 @@ def _load():
         lib.orc_set_mean2d64.argtypes = [P, I32, I32, F64, F64]
         lib.orc_set_mean3d64.argtypes = [P, I32, P]
         lib.orc_set_params64.argtypes = [P, I32, P]
+        lib.orc_render_features.argtypes = [P, P, I32, P, P]
+        lib.orc_attribute.argtypes = [P, P, I32, P]
         lib.orc_backward.argtypes = [P, P, P, I64, P, P]
         lib.orc_sh_basis_grad64.argtypes = [P, I64, I32, P]
         lib.orc_num_threads.restype = I32
@@ -278,6 +281,31 @@ class OracleScene:
                     for tx in range(x0, x1):
                         out.add(v * self.T + ty * self.TX + tx)
         return np.array(sorted(out), dtype=np.int64)
+
+    # -- feature composite and attribution scatter ----------------------------
+    def render_features(self, features, background=None):
+        """Composite per-Gaussian features [G, C] with the render weights:
+        [V, H, W, C] float64 = sum_k T_k alpha_k f_k + T_final * background."""
+        if self.n_pairs is None:
+            self.build_lists()
+        f = np.ascontiguousarray(features, dtype=np.float32).reshape(self.G, -1)
+        C = f.shape[1]
+        bg = None if background is None else np.ascontiguousarray(background, dtype=np.float32).reshape(C)
+        out = np.empty((self.V, self.H, self.W, C), dtype=np.float64)
+        self.lib.orc_render_features(self.handle, _ptr(f), C, _ptr(bg) if bg is not None else None, _ptr(out))
+        return out
+
+    def attribute(self, pixel_map):
+        """Attribution scatter of a per-pixel map [V, H, W, C]: [G, C] float64 =
+        sum over views and pixels of T alpha * map."""
+        if self.n_pairs is None:
+            self.build_lists()
+        m = np.ascontiguousarray(pixel_map, dtype=np.float32)
+        C = m.shape[-1]
+        assert m.shape == (self.V, self.H, self.W, C)
+        out = np.empty((self.G, C), dtype=np.float64)
+        self.lib.orc_attribute(self.handle, _ptr(m), C, _ptr(out))
+        return out
 
     # -- renderer backward -----------------------------------------------------
     def backward(self, grad_color, with_image_sums=False, tiles=None):

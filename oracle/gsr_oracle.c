@@ -37,6 +37,9 @@
  *    never by the subtraction formula of the replay.
  *  - Scores are the literal per-pixel sums of the score operators; tokens are
  *    the literal cross-view formulas; eigenvalues by cyclic Jacobi rotations.
+ *  - Feature composite and attribution scatter: per-Gaussian attribute vectors
+ *    composited with the render weights w = T alpha, and per-pixel maps sent
+ *    back to the Gaussians along the same weights (literal sums).
  *  - The renderer backward (the gradient of the image through the composite,
  *    the 2D Gaussian, the EWA projection, the covariance from quaternion and
  *    scales, and the SH colour including its view direction) is an explicit
@@ -978,6 +981,90 @@ void orc_tokens(const void* p, double eps, double lambda, double* tok, double* A
         z[8 + 3 * d] = log(tr + eps);
         if (Aout)
             for (int k = 0; k < 9; ++k) Aout[(int64_t)i * 9 + k] = A[k];
+    }
+}
+
+/* ----------------------------------------------------------------------------
+ * Scalar / feature attributes: composite and attribution scatter.
+ * The render weight of an accepted contribution is w = T alpha (Stage 1 with
+ * float32 decisions, float64 values).  A per-Gaussian attribute vector f_g is
+ * composited like the colour (the ATSplat summary page renders its per-anchor
+ * uncertainty score this way; ReCoSplat's feature channels are rendered the
+ * same way):  F(p) = sum_k w_k f_{g_k} + T_final bg.  The attribution scatter
+ * sends a per-pixel map m back along the same weights:
+ * a_g = sum_v sum_p w_{p,g,v} m(p) (alphaT scatter for m = 1; the mask-channel
+ * gain attribution of L2D2-GS for m = the gain map).
+ * ------------------------------------------------------------------------- */
+void orc_render_features(void* p, const float* feat, int C, const float* bg, double* out)
+{
+    scene* s = (scene*)p;
+    const int T = s->TX * s->TY;
+    int64_t maxlen = 0;
+    for (int64_t i = 0; i < (int64_t)s->V * T; ++i)
+        if (s->starts[i + 1] - s->starts[i] > maxlen) maxlen = s->starts[i + 1] - s->starts[i];
+    const int64_t n_tiles = (int64_t)s->V * T;
+#pragma omp parallel
+    {
+        contrib* cl = (contrib*)malloc(sizeof(contrib) * (size_t)maxlen + 1);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t tile = 0; tile < n_tiles; ++tile) {
+            int v = (int)(tile / T), t = (int)(tile % T);
+            int tx = t % s->TX, ty = t / s->TX;
+            const int32_t* list = s->ids + s->starts[tile];
+            int64_t L = s->starts[tile + 1] - s->starts[tile];
+            for (int yy = 0; yy < TILE; ++yy)
+                for (int xx = 0; xx < TILE; ++xx) {
+                    int x = tx * TILE + xx, y = ty * TILE + yy;
+                    if (x >= s->W || y >= s->H) continue;
+                    double Cc[3], T64;
+                    float T32;
+                    int n = composite_pixel(s, v, x, y, list, L, cl, Cc, &T32, &T64);
+                    double* o = out + (((int64_t)v * s->H + y) * s->W + x) * C;
+                    for (int c = 0; c < C; ++c) o[c] = T64 * (bg ? (double)bg[c] : 0.0);
+                    for (int k = 0; k < n; ++k) {
+                        const double w = cl[k].T * cl[k].alpha;
+                        const float* f = feat + (int64_t)cl[k].g * C;
+                        for (int c = 0; c < C; ++c) o[c] += w * (double)f[c];
+                    }
+                }
+        }
+        free(cl);
+    }
+}
+
+void orc_attribute(void* p, const float* map, int C, double* out /* [G][C], zeroed here */)
+{
+    scene* s = (scene*)p;
+    const int T = s->TX * s->TY;
+    int64_t maxlen = 0;
+    for (int64_t i = 0; i < (int64_t)s->V * T; ++i)
+        if (s->starts[i + 1] - s->starts[i] > maxlen) maxlen = s->starts[i + 1] - s->starts[i];
+    for (int64_t i = 0; i < (int64_t)s->G * C; ++i) out[i] = 0.0;
+    const int64_t n_tiles = (int64_t)s->V * T;
+#pragma omp parallel
+    {
+        contrib* cl = (contrib*)malloc(sizeof(contrib) * (size_t)maxlen + 1);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t tile = 0; tile < n_tiles; ++tile) {
+            int v = (int)(tile / T), t = (int)(tile % T);
+            int tx = t % s->TX, ty = t / s->TX;
+            const int32_t* list = s->ids + s->starts[tile];
+            int64_t L = s->starts[tile + 1] - s->starts[tile];
+            for (int yy = 0; yy < TILE; ++yy)
+                for (int xx = 0; xx < TILE; ++xx) {
+                    int x = tx * TILE + xx, y = ty * TILE + yy;
+                    if (x >= s->W || y >= s->H) continue;
+                    double Cc[3], T64;
+                    float T32;
+                    int n = composite_pixel(s, v, x, y, list, L, cl, Cc, &T32, &T64);
+                    const float* m = map + (((int64_t)v * s->H + y) * s->W + x) * C;
+                    for (int k = 0; k < n; ++k) {
+                        const double w = cl[k].T * cl[k].alpha;
+                        for (int c = 0; c < C; ++c) add(&out[(int64_t)cl[k].g * C + c], w * (double)m[c]);
+                    }
+                }
+        }
+        free(cl);
     }
 }
 
