@@ -8,7 +8,8 @@ Gaussian-pixel contributions/s, per-stage times (HIP events on the stream the
 kernels run on), the roofline of the dominant kernel and the CPU oracle timed
 on a bounded sample on the host cores.  The renderer backward (gs_backward of
 1/2 |C_hat - C_obs|^2 over the last step's render) is timed separately and
-reported under "backward"; it is not part of the step.
+reported under "backward", and so are a 9-channel feature composite and a
+2-channel attribution scatter ("attributes"); they are not part of the step.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5]
 
@@ -50,6 +51,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true",
                    help="skip the separately timed renderer backward (gs_backward of 1/2 |C_hat - C|^2)")
+    p.add_argument("--no-attributes", action="store_true",
+                   help="skip the separately timed 9-channel feature composite and 2-channel attribution scatter")
     p.add_argument("--sweep", action="store_true",
                    help="instead of the benchmark line: view-count / resolution scaling (4, 8, 16, 32 views at "
                         "256x448 and 512x960 over a fixed Gaussian set), one JSON line per point")
@@ -94,7 +97,9 @@ def _sources_sha256(names):
 KERNEL_SOURCES = {"k_project": ["project.hip"], "k_render": ["render.hip"], "k_replay": ["replay.hip"],
                   "k_gather_slots": ["replay.hip"], "k_tokens": ["replay.hip"], "k_onesweep": ["binning.hip"],
                   "k_emit": ["binning.hip"], "k_ranges": ["binning.hip"], "k_digit_hist": ["binning.hip"],
-                  "k_backward": ["backward.hip"], "k_grads": ["backward.hip"]}
+                  "k_backward": ["backward.hip"], "k_grads": ["backward.hip"],
+                  "k_render_features": ["attributes.hip"], "k_attribute": ["attributes.hip"],
+                  "k_sum_views": ["attributes.hip"]}
 
 
 def kernel_source_sha256(kernel):
@@ -200,6 +205,32 @@ def main():
                        stages={k: bprof[k][0] / max(bprof[k][1], 1) for k in ("backward", "backward_finalize")},
                        finite=bool(all(torch.isfinite(t).all().item() for t in grads.values())))
 
+        # feature composite of 9 channels (ReCoSplat-style conditioning features) and attribution scatter of a
+        # 2-channel map (squared residual, coverage: the error + coverage token), each timed on its own
+        attrs = None
+        if not args.no_attributes:
+            gen = torch.Generator(device=dev).manual_seed(5)
+            feats = torch.randn((sc.n, 9), generator=gen, device=dev, dtype=torch.float32)
+            feat_out = torch.empty((sc.n_views, sc.height, sc.width, 9), dtype=torch.float32, device=dev)
+            resid2 = ((outputs[0] - obs) ** 2).sum(-1)
+            amap = torch.stack([resid2, torch.ones_like(resid2)], dim=-1).contiguous()
+            aout = torch.empty((sc.n, 2), dtype=torch.float32, device=dev)
+            for _ in range(args.warmup):
+                r.render_features(feats, out=feat_out)
+                r.attribute(amap, out=aout)
+            stream.synchronize()
+            binding.gs_profile_enable(r.ctx, True)
+            binding.gs_profile_read(r.ctx)
+            for _ in range(args.steps):
+                r.render_features(feats, out=feat_out)
+            for _ in range(args.steps):
+                r.attribute(amap, out=aout)
+            stream.synchronize()
+            aprof = binding.gs_profile_read(r.ctx)
+            binding.gs_profile_enable(r.ctx, False)
+            attrs = {k: aprof[k][0] / max(aprof[k][1], 1) for k in ("features", "attribute")}
+            attrs["finite"] = bool(torch.isfinite(feat_out).all().item() and torch.isfinite(aout).all().item())
+
         color, T, n = outputs
         stats = r.export(binding.GS_EXPORT_PIXEL_STATS).view(-1, 2).to(torch.int64)
         K = int(n.to(torch.int64).sum().item())
@@ -278,6 +309,9 @@ def main():
     }
     if backward is not None:
         out["backward"] = backward
+    if attrs is not None:
+        out["attributes"] = {"feature_composite_9ch_ms": round(attrs["features"], 4),
+                             "attribution_2ch_ms": round(attrs["attribute"], 4), "finite": attrs["finite"]}
 
     if not args.no_cpu_baseline and args.cpu_baseline_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(sc, args.cpu_baseline_seconds)

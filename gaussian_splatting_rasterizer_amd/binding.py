@@ -32,10 +32,11 @@ GS_EXPORT_SORTED_IDS = 3
 GS_EXPORT_RANGES = 4
 GS_EXPORT_PIXEL_STATS = 5
 STAGES = ("project", "depth_sort", "scan", "emit", "tile_sort", "ranges", "render", "replay", "finalize",
-          "backward", "backward_finalize")
+          "backward", "backward_finalize", "features", "attribute")
 
 ABI_SYMBOLS = ("gs_default_params", "gs_workspace_size", "gs_context_create", "gs_context_destroy",
-               "gs_project", "gs_bin_sort", "gs_render", "gs_score_replay", "gs_backward", "gs_status_string",
+               "gs_project", "gs_bin_sort", "gs_render", "gs_score_replay", "gs_backward", "gs_render_features",
+               "gs_attribute", "gs_status_string",
                "gs_last_error", "gs_debug_exp2", "gs_debug_export", "gs_profile_enable", "gs_profile_read")
 
 
@@ -103,6 +104,10 @@ def load_library(path: str = LIB_PATH):
     lib.gs_score_replay.argtypes = [P, P, P, P]
     lib.gs_backward.restype = St
     lib.gs_backward.argtypes = [P, P, ctypes.POINTER(gs_gaussian_grads), P]
+    lib.gs_render_features.restype = St
+    lib.gs_render_features.argtypes = [P, P, ctypes.c_int32, P, P, P]
+    lib.gs_attribute.restype = St
+    lib.gs_attribute.argtypes = [P, P, ctypes.c_int32, P, P]
     lib.gs_status_string.restype = ctypes.c_char_p
     lib.gs_status_string.argtypes = [St]
     lib.gs_last_error.restype = ctypes.c_char_p
@@ -193,6 +198,20 @@ def gs_score_replay(ctx, observed, tokens, stream=None) -> None:
 def gs_backward(ctx, grad_color, grads: gs_gaussian_grads, stream=None) -> None:
     _check(load_library().gs_backward(ctx, _dev_ptr(grad_color), ctypes.byref(grads), _stream_handle(stream)),
            "gs_backward")
+
+
+def gs_render_features(ctx, features, n_channels, background, out, stream=None) -> None:
+    """background: None or a host sequence of n_channels floats."""
+    bg = None
+    if background is not None:
+        bg = (ctypes.c_float * n_channels)(*[float(x) for x in background])
+    _check(load_library().gs_render_features(ctx, _dev_ptr(features), int(n_channels), bg, _dev_ptr(out),
+                                             _stream_handle(stream)), "gs_render_features")
+
+
+def gs_attribute(ctx, pixel_map, n_channels, out, stream=None) -> None:
+    _check(load_library().gs_attribute(ctx, _dev_ptr(pixel_map), int(n_channels), _dev_ptr(out),
+                                       _stream_handle(stream)), "gs_attribute")
 
 
 def gs_debug_exp2(inp, out, stream=None) -> None:
@@ -332,6 +351,28 @@ class Rasterizer:
                                    for k in ("means", "quats", "scales", "opacities", "sh")])
         gs_backward(self.ctx, gC, ptrs, stream)
         return grads
+
+    def render_features(self, features, background=None, out=None, stream=None):
+        """Composite per-Gaussian features [n, C] with the render weights -> [V, H, W, C]."""
+        torch = self.torch
+        f = torch.as_tensor(features, dtype=torch.float32, device=self.device).contiguous()
+        if f.dim() == 1:
+            f = f.view(-1, 1)
+        C = int(f.shape[1])
+        if out is None:
+            out = torch.empty((self.V, self.H, self.W, C), dtype=torch.float32, device=self.device)
+        gs_render_features(self.ctx, f, C, background, out, stream)
+        return out
+
+    def attribute(self, pixel_map, out=None, stream=None):
+        """Scatter a per-pixel map [V, H, W, C] back along the render weights -> [n, C]."""
+        torch = self.torch
+        m = torch.as_tensor(pixel_map, dtype=torch.float32, device=self.device).contiguous()
+        C = int(m.shape[-1])
+        if out is None:
+            out = torch.empty((self.n, C), dtype=torch.float32, device=self.device)
+        gs_attribute(self.ctx, m, C, out, stream)
+        return out
 
     def step(self, observed, outputs=None, tokens=None, stream=None):
         """One pass of the whole path: project, bin/sort, render, replay -> tokens."""

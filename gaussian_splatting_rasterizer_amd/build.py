@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libgsr.so")
-SOURCES = ["api.hip", "project.hip", "binning.hip", "render.hip", "replay.hip", "backward.hip"]
+SOURCES = ["api.hip", "project.hip", "binning.hip", "render.hip", "replay.hip", "backward.hip", "attributes.hip"]
 ARCH = os.environ.get("GSR_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -445,6 +445,35 @@ gs_status gs_backward(gs_context* ctx, const float* grad_color, const gs_gaussia
     return GS_OK;
 }
 
+gs_status gs_render_features(gs_context* ctx, const float* features, int32_t n_channels, const float* background,
+                             float* out, hipStream_t stream) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    if (ctx->state < kRendered) return fail(GS_ERR_STATE, "gs_render_features before gs_render");
+    if (n_channels < 1) return fail(GS_ERR_INVALID_ARGUMENT, "n_channels must be >= 1");
+    if ((ctx->s.G > 0 && !features) || !out) return fail(GS_ERR_INVALID_ARGUMENT, "null features or out");
+    if ((features && !aligned(features, 4)) || !aligned(out, 4))
+        return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    ctx->timer.begin(stream);
+    hipError_t e = launch_render_features(ctx->s, ctx->ws, ctx->sorted_g, features, n_channels, background, out,
+                                          stream);
+    if (e != hipSuccess) return hip_fail(e, "feature composite");
+    ctx->timer.end(GS_STAGE_FEATURES, stream);
+    return GS_OK;
+}
+
+gs_status gs_attribute(gs_context* ctx, const float* pixel_map, int32_t n_channels, float* out, hipStream_t stream) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    if (ctx->state < kRendered) return fail(GS_ERR_STATE, "gs_attribute before gs_render");
+    if (n_channels < 1) return fail(GS_ERR_INVALID_ARGUMENT, "n_channels must be >= 1");
+    if (!pixel_map || (ctx->s.G > 0 && !out)) return fail(GS_ERR_INVALID_ARGUMENT, "null pixel_map or out");
+    if (!aligned(pixel_map, 4) || (out && !aligned(out, 4))) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    ctx->timer.begin(stream);
+    hipError_t e = launch_attribute(ctx->s, ctx->ws, ctx->sorted_g, pixel_map, n_channels, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "attribution");
+    ctx->timer.end(GS_STAGE_ATTRIBUTE, stream);
+    return GS_OK;
+}
+
 const char* gs_status_string(gs_status s) {
     switch (s) {
         case GS_OK: return "GS_OK";

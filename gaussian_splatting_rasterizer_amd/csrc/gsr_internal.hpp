@@ -142,5 +142,13 @@ hipError_t launch_backward_finalize(const gs_gaussians& sc, const CamPack& cams,
 hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
                          float eps, float lambda, float* tokens, hipStream_t st);
 hipError_t launch_exp2(const float* in, float* out, int64_t n, hipStream_t st);
+// per-channel background of one feature-composite launch (at most 16 channels)
+struct FeatBg {
+    float v[16];
+};
+hipError_t launch_render_features(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* feat,
+                                  int C, const float* bg_host, float* out, hipStream_t st);
+hipError_t launch_attribute(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* map, int C,
+                            float* out, hipStream_t st);
 
 }  // namespace gsr

@@ -20,7 +20,7 @@
  *     9 + 3 d_SH).
  *
  * Calling sequence, all on one stream:  gs_project -> gs_bin_sort -> gs_render
- * [-> gs_score_replay] [-> gs_backward].  Each call returns a status and never aborts.
+ * [-> gs_score_replay] [-> gs_backward] [-> gs_render_features] [-> gs_attribute].  Each call returns a status and never aborts.
  *
  * Memory: every array argument is a DEVICE pointer unless marked "host".
  * The caller owns every buffer (inputs, outputs and the workspace); the
@@ -199,6 +199,34 @@ typedef struct {
 GSR_API gs_status gs_backward(gs_context* ctx, const float* grad_color, const gs_gaussian_grads* grads,
                               hipStream_t stream);
 
+/* Feature composite: per-Gaussian attribute vectors `features` [n, n_channels]
+ * (float32 device, view-independent) composited with the render's weights,
+ *   out[v, y, x, c] = sum_k T_k alpha_k features[g_k, c] + T_final * background[c]
+ * into `out` [n_views, height, width, n_channels] (float32 device) -- the same
+ * contributors, order and float32 decisions as the colour of gs_render.  The
+ * ATSplat summary page ("核心方法": the uncertainty score rendered as a scalar
+ * attribute by alpha compositing) and ReCoSplat's render-and-compare module
+ * (9 learned feature channels rendered with the RGB) use this operation.
+ * `background` is a host array of n_channels floats, or null for zeros.
+ * n_channels >= 1 (slices of 16 channels are composited per launch).  Valid
+ * after gs_render; asynchronous on `stream`. */
+GSR_API gs_status gs_render_features(gs_context* ctx, const float* features, int32_t n_channels,
+                                     const float* background, float* out, hipStream_t stream);
+
+/* Attribution scatter: a per-pixel map `pixel_map` [n_views, height, width,
+ * n_channels] (float32 device) sent back to the Gaussians along the render's
+ * weights,
+ *   out[g, c] = sum over views v and pixels p of T alpha (p, g, v) * pixel_map[v, p, c]
+ * into `out` [n, n_channels] (float32 device, written).  The transpose of
+ * gs_render_features: the alphaT scatter (map = 1) and the scalar-attribution
+ * baselines of the Renderer Score Tokens plan (an error + coverage token for
+ * map = (|r|^2, 1)), and the mask-channel gain attribution of the L2D2-GS
+ * summary (map = the 2D gain).  n_channels >= 1 (passes of 8 channels).  Valid
+ * after gs_render; uses the workspace's partial and per-record sum areas, so it
+ * must not overlap gs_score_replay / gs_backward on the same context. */
+GSR_API gs_status gs_attribute(gs_context* ctx, const float* pixel_map, int32_t n_channels, float* out,
+                               hipStream_t stream);
+
 GSR_API const char* gs_status_string(gs_status s);
 GSR_API const char* gs_last_error(void);
 
@@ -252,7 +280,9 @@ typedef enum {
     GS_STAGE_FINALIZE = 8,
     GS_STAGE_BACKWARD = 9,          /* gs_backward traversal */
     GS_STAGE_BACKWARD_FINALIZE = 10, /* gs_backward slot gather and per-Gaussian chain rule */
-    GS_NUM_STAGES = 11
+    GS_STAGE_FEATURES = 11,          /* gs_render_features */
+    GS_STAGE_ATTRIBUTE = 12,         /* gs_attribute (traversal, gather, sum over views) */
+    GS_NUM_STAGES = 13
 } gs_stage;
 GSR_API gs_status gs_profile_enable(gs_context* ctx, int32_t enable);
 GSR_API gs_status gs_profile_read(gs_context* ctx, double* ms, int64_t* calls, int32_t n_stages);
