@@ -95,6 +95,7 @@ def _load():
         lib.orc_set_params64.argtypes = [P, I32, P]
         lib.orc_render_features.argtypes = [P, P, I32, P, P]
         lib.orc_attribute.argtypes = [P, P, I32, P]
+        lib.orc_topk.argtypes = [P, I32, P, P]
         lib.orc_backward.argtypes = [P, P, P, I64, P, P]
         lib.orc_sh_basis_grad64.argtypes = [P, I64, I32, P]
         lib.orc_num_threads.restype = I32
@@ -306,6 +307,16 @@ class OracleScene:
         out = np.empty((self.G, C), dtype=np.float64)
         self.lib.orc_attribute(self.handle, _ptr(m), C, _ptr(out))
         return out
+
+    def topk(self, K):
+        """Per pixel the K contributions of largest weight T alpha (decreasing, list order
+        on ties): ids [V, H, W, K] int32 (-1 unused), weights [V, H, W, K] float64."""
+        if self.n_pairs is None:
+            self.build_lists()
+        ids = np.empty((self.V, self.H, self.W, K), dtype=np.int32)
+        w = np.empty((self.V, self.H, self.W, K), dtype=np.float64)
+        self.lib.orc_topk(self.handle, int(K), _ptr(ids), _ptr(w))
+        return ids, w
 
     # -- renderer backward -----------------------------------------------------
     def backward(self, grad_color, with_image_sums=False, tiles=None):

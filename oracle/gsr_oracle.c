@@ -1068,6 +1068,60 @@ void orc_attribute(void* p, const float* map, int C, double* out /* [G][C], zero
     }
 }
 
+/* Debug top-K contributor metadata (the Renderer Score Tokens plan, Block 0:
+ * "debug top-K only on small tiles"): per pixel, the K accepted contributions
+ * with the largest weight w = T alpha, in decreasing weight; equal weights keep
+ * list order; unused entries are id -1, weight 0. */
+void orc_topk(void* p, int K, int32_t* ids, double* wts)
+{
+    scene* s = (scene*)p;
+    const int T = s->TX * s->TY;
+    int64_t maxlen = 0;
+    for (int64_t i = 0; i < (int64_t)s->V * T; ++i)
+        if (s->starts[i + 1] - s->starts[i] > maxlen) maxlen = s->starts[i + 1] - s->starts[i];
+    const int64_t n_tiles = (int64_t)s->V * T;
+#pragma omp parallel
+    {
+        contrib* cl = (contrib*)malloc(sizeof(contrib) * (size_t)maxlen + 1);
+        char* used = (char*)malloc((size_t)maxlen + 1);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t tile = 0; tile < n_tiles; ++tile) {
+            int v = (int)(tile / T), t = (int)(tile % T);
+            int tx = t % s->TX, ty = t / s->TX;
+            const int32_t* list = s->ids + s->starts[tile];
+            int64_t L = s->starts[tile + 1] - s->starts[tile];
+            for (int yy = 0; yy < TILE; ++yy)
+                for (int xx = 0; xx < TILE; ++xx) {
+                    int x = tx * TILE + xx, y = ty * TILE + yy;
+                    if (x >= s->W || y >= s->H) continue;
+                    double Cc[3], T64;
+                    float T32;
+                    int n = composite_pixel(s, v, x, y, list, L, cl, Cc, &T32, &T64);
+                    int64_t base = (((int64_t)v * s->H + y) * s->W + x) * K;
+                    for (int k = 0; k < n; ++k) used[k] = 0;
+                    /* selection: K times the largest unused weight, the earliest on ties */
+                    for (int r = 0; r < K; ++r) {
+                        int best = -1;
+                        for (int k = 0; k < n; ++k) {
+                            if (used[k]) continue;
+                            if (best < 0 || cl[k].T * cl[k].alpha > cl[best].T * cl[best].alpha) best = k;
+                        }
+                        if (best < 0) {
+                            ids[base + r] = -1;
+                            wts[base + r] = 0.0;
+                        } else {
+                            used[best] = 1;
+                            ids[base + r] = cl[best].g;
+                            wts[base + r] = cl[best].T * cl[best].alpha;
+                        }
+                    }
+                }
+        }
+        free(used);
+        free(cl);
+    }
+}
+
 /* ----------------------------------------------------------------------------
  * Renderer backward: the vector-Jacobian product of the colour image with an
  * upstream gradient dL/dC_hat, through the composite, the 2D Gaussian, the EWA

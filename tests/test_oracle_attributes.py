@@ -7,7 +7,10 @@
   * the scatter is the transpose of the composite: sum_p <m_p, F_p> equals
     sum_g <a_g, f_g> for any features f and map m (background 0);
   * the scatter of ones is the support the score replay accumulates (sum of
-    T alpha per Gaussian over pixels and views), and sums to sum_p (1 - T_final).
+    T alpha per Gaussian over pixels and views), and sums to sum_p (1 - T_final);
+  * top-K contributors: with K >= n_contrib the weights are all of a pixel's (they
+    sum to 1 - T_final, their count is n_contrib), decreasing, and a smaller K
+    keeps a prefix; two stacked Gaussians in closed form.
 """
 from __future__ import annotations
 
@@ -93,3 +96,44 @@ def test_scatter_of_ones_is_the_replay_support():
     a = o.attribute(np.ones((sc.n_views, sc.height, sc.width, 1), np.float32))[:, 0]
     assert np.allclose(a, W_support, rtol=1e-13, atol=1e-15)
     assert abs(a.sum() - np.sum(1.0 - T64)) <= 1e-10 * a.sum()
+
+
+def test_topk_weights_sum_and_counts():
+    """With K at least the contributor count, the top-K weights of a pixel are all its
+    weights: they sum to 1 - T_final and their number is n_contrib; weights decrease."""
+    sc = scenes.tiny_scene(seed=21, n=60, n_views=2, W=40, H=24, sh_degree=2)
+    o = oracle.OracleScene(sc)
+    _, _, n, T64 = o.render()
+    K = int(n.max())
+    ids, w = o.topk(K)
+    assert np.array_equal((ids >= 0).sum(axis=-1), n)
+    assert np.allclose(w.sum(axis=-1), 1.0 - T64, rtol=0, atol=1e-13)
+    assert np.all(np.diff(w, axis=-1) <= 0)
+    # a smaller K keeps the largest ones
+    ids3, w3 = o.topk(3)
+    assert np.array_equal(ids3, ids[..., :3]) and np.array_equal(w3, w[..., :3])
+
+
+def test_topk_two_gaussians_far_one_wins():
+    """A faint near Gaussian in front of an opaque far one: at the centre pixel the far
+    one has the larger weight (1 - a_near) * a_far and comes first."""
+    z1, z2, f, W = 2.0, 4.0, 64.0, 64
+    cams = np.zeros((1, 16))
+    cams[0, [0, 4, 8]] = 1.0
+    cams[0, 12:16] = [f, f, W / 2.0, W / 2.0]
+    sh = np.zeros((2, 1, 3), np.float32)
+    sc = scenes.Scene(
+        name="two", means=np.array([[0, 0, z1], [0, 0, z2]], np.float32),
+        quats=np.array([[1, 0, 0, 0]] * 2, np.float32), scales=np.full((2, 3), 0.05, np.float32),
+        opacities=np.array([0.2, 0.95], np.float32), sh=sh, sh_degree=0, cams=cams.astype(np.float32),
+        width=W, height=W, background=np.zeros(3, np.float32), means_perturbed=np.zeros((2, 3), np.float32),
+        pixel_noise=np.zeros((1, W, W, 3), np.float32), notes={})
+    o = oracle.OracleScene(sc)
+    ids, w = o.topk(2)
+    assert list(ids[0, 31, 31]) == [1, 0]
+    # closed form at the pixel centre (31.5, 31.5), offset 0.5 px in x and y from the centre (32, 32)
+    s32 = float(np.float32(0.05))
+    a_near = float(np.float32(0.2)) * math.exp(-0.25 / ((f * s32 / z1) ** 2 + 0.3))
+    a_far = float(np.float32(0.95)) * math.exp(-0.25 / ((f * s32 / z2) ** 2 + 0.3))
+    assert abs(w[0, 31, 31, 1] - a_near) <= 1e-12
+    assert abs(w[0, 31, 31, 0] - (1.0 - a_near) * a_far) <= 1e-12
