@@ -37,7 +37,8 @@ STAGES = ("project", "depth_sort", "scan", "emit", "tile_sort", "ranges", "rende
 ABI_SYMBOLS = ("gs_default_params", "gs_workspace_size", "gs_context_create", "gs_context_destroy",
                "gs_project", "gs_bin_sort", "gs_render", "gs_score_replay", "gs_backward", "gs_render_features",
                "gs_attribute", "gs_status_string",
-               "gs_last_error", "gs_debug_exp2", "gs_debug_export", "gs_profile_enable", "gs_profile_read")
+               "gs_last_error", "gs_debug_exp2", "gs_debug_export", "gs_debug_topk", "gs_profile_enable",
+               "gs_profile_read")
 
 
 class gs_gaussians(ctypes.Structure):
@@ -116,6 +117,8 @@ def load_library(path: str = LIB_PATH):
     lib.gs_debug_exp2.argtypes = [P, P, ctypes.c_int64, P]
     lib.gs_debug_export.restype = St
     lib.gs_debug_export.argtypes = [P, ctypes.c_int32, P, ctypes.c_size_t, P]
+    lib.gs_debug_topk.restype = St
+    lib.gs_debug_topk.argtypes = [P, ctypes.c_int32, P, P, P]
     lib.gs_profile_enable.restype = St
     lib.gs_profile_enable.argtypes = [P, ctypes.c_int32]
     lib.gs_profile_read.restype = St
@@ -222,6 +225,11 @@ def gs_debug_exp2(inp, out, stream=None) -> None:
 def gs_debug_export(ctx, kind, dst, stream=None) -> None:
     _check(load_library().gs_debug_export(ctx, int(kind), _dev_ptr(dst), dst.numel() * dst.element_size(),
                                           _stream_handle(stream)), "gs_debug_export")
+
+
+def gs_debug_topk(ctx, k, ids, weights, stream=None) -> None:
+    _check(load_library().gs_debug_topk(ctx, int(k), _dev_ptr(ids), _dev_ptr(weights), _stream_handle(stream)),
+           "gs_debug_topk")
 
 
 def gs_profile_enable(ctx, enable=True) -> None:
@@ -373,6 +381,14 @@ class Rasterizer:
             out = torch.empty((self.n, C), dtype=torch.float32, device=self.device)
         gs_attribute(self.ctx, m, C, out, stream)
         return out
+
+    def topk(self, k, stream=None):
+        """Debug: per pixel the k contributions of largest weight -> (ids [V,H,W,k] int32, weights [V,H,W,k])."""
+        torch = self.torch
+        ids = torch.empty((self.V, self.H, self.W, k), dtype=torch.int32, device=self.device)
+        w = torch.empty((self.V, self.H, self.W, k), dtype=torch.float32, device=self.device)
+        gs_debug_topk(self.ctx, k, ids, w, stream)
+        return ids, w
 
     def step(self, observed, outputs=None, tokens=None, stream=None):
         """One pass of the whole path: project, bin/sort, render, replay -> tokens."""

@@ -474,6 +474,17 @@ gs_status gs_attribute(gs_context* ctx, const float* pixel_map, int32_t n_channe
     return GS_OK;
 }
 
+gs_status gs_debug_topk(gs_context* ctx, int32_t k, int32_t* ids, float* weights, hipStream_t stream) {
+    if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
+    if (ctx->state < kRendered) return fail(GS_ERR_STATE, "gs_debug_topk before gs_render");
+    if (k < 1 || k > 16) return fail(GS_ERR_INVALID_ARGUMENT, "k must be 1..16");
+    if (!ids || !weights) return fail(GS_ERR_INVALID_ARGUMENT, "null ids or weights");
+    if (!aligned(ids, 4) || !aligned(weights, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    hipError_t e = launch_topk(ctx->s, ctx->ws, ctx->sorted_g, k, ids, weights, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k");
+    return GS_OK;
+}
+
 const char* gs_status_string(gs_status s) {
     switch (s) {
         case GS_OK: return "GS_OK";

@@ -304,4 +304,127 @@ hipError_t launch_attribute(const Sizes& s, const Workspace& ws, const uint32_t*
     return hipSuccess;
 }
 
+// Debug top-K contributor metadata: per pixel the K accepted contributions with
+// the largest weight w = T alpha, in decreasing weight (a new weight passes only
+// strictly smaller ones, so equal weights keep list order); unused entries are
+// id -1, weight 0.  Sorted insertion into K register slots per pixel.
+template <int K>
+__global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
+                                              const float4* __restrict__ rec0, const float4* __restrict__ rec1,
+                                              int64_t G, int T, int TX, int W, int H,
+                                              const uint8_t* __restrict__ events, int k_out,
+                                              int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+    __shared__ float4 s0[kAttrBatch];
+    __shared__ float2 s1[kAttrBatch];
+    __shared__ uint32_t s_g[kAttrBatch];
+    __shared__ uint8_t s_evb[kAttrBatch];
+    __shared__ uint8_t slist[4][kAttrBatch];
+
+    const int tile = blockIdx.x;
+    const int v = tile / T;
+    const int t = tile - v * T;
+    const int ty = t / TX, tx = t - ty * TX;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pxi = tx * kTile + (wave & 1) * 8 + (lane & 7);
+    const int pyi = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
+    const bool inside = pxi < W && pyi < H;
+    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    const uint2 rg = ranges[tile];
+    const int64_t vG = (int64_t)v * G;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    float tw[K];
+    int32_t tid[K];
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+        tw[q] = 0.0f;
+        tid[q] = -1;
+    }
+    float Tr = 1.0f;
+    bool done = !inside;
+
+    for (uint32_t base = rg.x; base < rg.y; base += kAttrBatch) {
+        if (__syncthreads_count(!done) == 0) break;
+        const uint32_t i = base + threadIdx.x;
+        if (threadIdx.x < kAttrBatch && i < rg.y) {
+            const uint32_t g = sorted_g[i];
+            s0[threadIdx.x] = rec0[vG + g];
+            const float4 b = rec1[vG + g];
+            s1[threadIdx.x] = make_float2(b.x, b.y);
+            s_g[threadIdx.x] = g;
+            s_evb[threadIdx.x] = events[i];
+        }
+        const int cnt = (int)min((uint32_t)kAttrBatch, rg.y - base);
+        __syncthreads();
+        if (__ballot(!done) != 0ull) {
+            int nw = 0;
+            for (int c = 0; c < cnt; c += 64) {
+                const int j = c + lane;
+                const bool hit = j < cnt && ((s_evb[j] >> wave) & 1u);
+                const uint64_t m = __ballot(hit);
+                if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
+                nw += __popcll(m);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int k = 0; k < nw; ++k) {
+                const int j = slist[wave][k];
+                const float4 a = s0[j];
+                const float2 b = s1[j];
+                const float dx = px - a.x, dy = py - a.y;
+                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
+                const bool near = !done && e >= kECutoff;
+                const float aG = b.y * exp2_spec(e);
+                const float alpha = !(aG < kAlphaMax) ? kAlphaMax : aG;
+                const bool pass = near && alpha >= kAlphaMin;
+                const float tT = Tr * (1.0f - alpha);
+                const bool sat = pass && tT < kTMin;
+                const bool contrib = pass && !sat;
+                done = done || sat;
+                if (contrib && alpha * Tr > tw[K - 1]) {
+                    float cw = alpha * Tr;
+                    int32_t ci = (int32_t)s_g[j];
+#pragma unroll
+                    for (int q = 0; q < K; ++q) {
+                        if (cw > tw[q]) {
+                            const float sw = tw[q];
+                            const int32_t si = tid[q];
+                            tw[q] = cw;
+                            tid[q] = ci;
+                            cw = sw;
+                            ci = si;
+                        }
+                    }
+                }
+                Tr = contrib ? tT : Tr;
+                if (__ballot(!done) == 0ull) break;
+            }
+        }
+        __syncthreads();
+    }
+    if (!inside) return;
+    const int64_t o = (((int64_t)v * H + pyi) * W + pxi) * k_out;
+#pragma unroll
+    for (int q = 0; q < K; ++q)
+        if (q < k_out) {
+            ids_out[o + q] = tid[q];
+            w_out[o + q] = tw[q];
+        }
+}
+
+hipError_t launch_topk(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, int k, int32_t* ids, float* w,
+                       hipStream_t st) {
+    const int64_t tiles = (int64_t)s.V * s.T;
+    if (tiles == 0) return hipSuccess;
+#define GSR_LAUNCH_TOPK(KK)                                                                                       \
+    hipLaunchKernelGGL(k_topk<KK>, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1, \
+                       s.G, s.T, s.TX, s.W, s.H, ws.events, k, ids, w)
+    if (k <= 4) GSR_LAUNCH_TOPK(4);
+    else if (k <= 8) GSR_LAUNCH_TOPK(8);
+    else GSR_LAUNCH_TOPK(16);
+#undef GSR_LAUNCH_TOPK
+    return hipGetLastError();
+}
+
 }  // namespace gsr

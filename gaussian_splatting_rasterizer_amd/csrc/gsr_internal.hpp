@@ -150,5 +150,7 @@ hipError_t launch_render_features(const Sizes& s, const Workspace& ws, const uin
                                   int C, const float* bg_host, float* out, hipStream_t st);
 hipError_t launch_attribute(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* map, int C,
                             float* out, hipStream_t st);
+hipError_t launch_topk(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, int k, int32_t* ids, float* w,
+                       hipStream_t st);
 
 }  // namespace gsr

@@ -262,6 +262,15 @@ typedef enum {
 } gs_export_kind;
 GSR_API gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes, hipStream_t stream);
 
+/* Debug top-K contributor metadata (the Renderer Score Tokens plan, Block 0,
+ * which enables it on small tiles only): per pixel the k accepted contributions
+ * of largest weight T alpha, in decreasing weight (equal weights in list order),
+ *   ids     [n_views, height, width, k] int32 Gaussian index, -1 where unused
+ *   weights [n_views, height, width, k] float32 T alpha, 0 where unused
+ * (device arrays).  1 <= k <= 16.  Valid after gs_render.  Costs a traversal
+ * and 8 k bytes per pixel: a diagnostic, not part of the path. */
+GSR_API gs_status gs_debug_topk(gs_context* ctx, int32_t k, int32_t* ids, float* weights, hipStream_t stream);
+
 /* Per-stage timing with HIP events recorded on the caller's stream around each
  * stage's launches (events are created by the library on first use and kept
  * until gs_context_destroy).  gs_profile_read waits for the recorded events,

@@ -100,6 +100,7 @@ def test_calls_out_of_order_are_rejected_without_launching():
         assert lib.gs_render_features(ctx, ctypes.c_void_p(256), 3, None, ctypes.c_void_p(256), None) == b.GS_ERR_STATE
         assert lib.gs_attribute(ctx, ctypes.c_void_p(256), 2, ctypes.c_void_p(256), None) == b.GS_ERR_STATE
         assert lib.gs_attribute(None, ctypes.c_void_p(256), 2, ctypes.c_void_p(256), None) == b.GS_ERR_INVALID_ARGUMENT
+        assert lib.gs_debug_topk(ctx, 4, ctypes.c_void_p(256), ctypes.c_void_p(256), None) == b.GS_ERR_STATE
         # mismatched scene size and null parameters: rejected before any launch
         g = b.gs_gaussians(256, 256, 256, 256, 256, 999, 3)
         cams = b.make_cameras([[1, 0, 0, 0, 1, 0, 0, 0, 1, 0, 0, 0, 64, 64, 32, 24]] * 2)

@@ -162,3 +162,38 @@ def test_fullsize_transpose_identity_and_sampled_parity():
     rel = np.linalg.norm(a - a_ref, axis=0) / np.linalg.norm(a_ref, axis=0)
     print(f"full-size scatter: rel L2 {rel}")
     assert rel.max() <= ATTR_RTOL
+
+
+TOPK_W_ATOL = 1e-5
+
+
+@pytest.mark.parametrize("k", [1, 4, 9, 16])
+@pytest.mark.parametrize("name", ["c1_toy", "tiny_bg_deg1", "c2_small", "c5_small"])
+def test_topk_parity(name, k):
+    """Per pixel: the number of filled entries is min(k, n_contrib) (exact), the weights
+    match the oracle's sorted weights position by position, and every id whose weight
+    is separated from its neighbours (> 2 TOPK_W_ATOL) is the oracle's id."""
+    _need_gpu()
+    from gaussian_splatting_rasterizer_amd import binding
+    sc = _scenes()[name]()
+    o = oracle.OracleScene(sc)
+    _, _, n_ref, _ = o.render()
+    ids_ref, w_ref = o.topk(k + 1)
+    o.close()
+    r = binding.rasterizer_for_scene(sc)
+    r.project_and_bin()
+    r.render()
+    ids, w = r.topk(k)
+    torch.cuda.synchronize()
+    ids, w = ids.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    r.close()
+    assert np.array_equal((ids >= 0).sum(axis=-1), np.minimum(n_ref, k))
+    assert np.all(w[ids < 0] == 0.0)
+    assert np.abs(w - w_ref[..., :k]).max() <= TOPK_W_ATOL
+    # uniqueness of each oracle position among its neighbours (the (k+1)-th included)
+    wr = w_ref
+    gap_prev = np.concatenate([np.full(wr.shape[:-1] + (1,), np.inf), wr[..., :-1] - wr[..., 1:]], axis=-1)
+    gap_next = np.concatenate([wr[..., :-1] - wr[..., 1:], np.full(wr.shape[:-1] + (1,), np.inf)], axis=-1)
+    unique = (np.minimum(gap_prev, gap_next) > 2 * TOPK_W_ATOL)[..., :k] & (ids_ref[..., :k] >= 0)
+    assert np.array_equal(ids[unique], ids_ref[..., :k][unique])
+    print(f"{name} k={k}: {unique.sum()} unique positions of {(ids >= 0).sum()} filled")
