@@ -68,7 +68,7 @@ def _load():
         P = ctypes.c_void_p
         I64, I32, F32, F64 = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
         lib.orc_scene_new.restype = P
-        lib.orc_scene_new.argtypes = [I32, I32, P, P, P, P, P, I32, P, I32, I32, F32, F32, P]
+        lib.orc_scene_new.argtypes = [I32, I32, P, P, P, P, P, I32, P, I32, I32, F32, F32, P, I32]
         lib.orc_scene_free.argtypes = [P]
         lib.orc_get_records32.argtypes = [P, P]
         lib.orc_get_records64.argtypes = [P, P]
@@ -157,7 +157,7 @@ class OracleScene:
     """One scene loaded into the oracle: per-(Gaussian, view) records, tile lists,
     per-pixel render/replay for chosen tiles, score sums for chosen Gaussians, tokens."""
 
-    def __init__(self, scene, near=0.01, far=1e10, background=None):
+    def __init__(self, scene, near=0.01, far=1e10, background=None, antialiased=False):
         lib = _load()
         self.lib = lib
         self.G, self.V = scene.n, scene.n_views
@@ -171,7 +171,8 @@ class OracleScene:
                       (scene.means, scene.quats, scene.scales, scene.opacities, scene.sh, scene.cams, bg)]
         m, q, s, o, sh, cams, bgc = self._keep
         self.handle = lib.orc_scene_new(self.G, scene.sh_degree, _ptr(m), _ptr(q), _ptr(s), _ptr(o), _ptr(sh),
-                                        self.V, _ptr(cams), self.W, self.H, near, far, _ptr(bgc))
+                                        self.V, _ptr(cams), self.W, self.H, near, far, _ptr(bgc),
+                                        1 if antialiased else 0)
         if not self.handle:
             raise ValueError("oracle rejected the scene")
         self.n_pairs = None
@@ -378,10 +379,10 @@ def render_observation(scene, **kw) -> np.ndarray:
     return (color + scene.pixel_noise.astype(np.float64)).astype(np.float32)
 
 
-def full_reference(scene, obs, eps=1e-6, den_min=1e-3, lam=1.0, gids=None, tiles=None):
+def full_reference(scene, obs, eps=1e-6, den_min=1e-3, lam=1.0, gids=None, tiles=None, antialiased=False):
     """Convenience: render + replay + tokens.  With `gids`, only those Gaussians'
     tokens are computed, from every tile their rectangles touch (plus `tiles`)."""
-    o = OracleScene(scene)
+    o = OracleScene(scene, antialiased=antialiased)
     t0 = time.perf_counter()
     o.build_lists()
     if gids is None:

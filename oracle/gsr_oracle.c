@@ -220,6 +220,7 @@ typedef struct {
     float pre[3];        /* SH colour + 0.5 before the clamp */
     float col[3];        /* clamped colour */
     int clamp_ok[3];     /* 1 where pre >= 0 (clamp inactive) */
+    int comp_ok;         /* antialiased mode: undilated 2D covariance determinant > 0 */
     float depth;
     float radius;
     int rect[4];         /* x0, y0, x1, y1 in tiles, half-open */
@@ -228,7 +229,9 @@ typedef struct {
 typedef struct {
     double mx, my;       /* projected centre */
     double ca, cb, cc;   /* conic */
-    double opac;
+    double opac;         /* opacity used in alpha (compensated in antialiased mode) */
+    double opac_raw;     /* the Gaussian's opacity o */
+    double comp;         /* antialiased mode: sqrt(det S2 / det(S2 + 0.3 I)), else 1 */
     double col[3];       /* colour value with the float32 clamp decision frozen */
     double J[6];         /* d(pixel)/d(mean), unclamped, row-major 2x3 */
     double B[16];        /* SH basis at the view direction */
@@ -236,6 +239,7 @@ typedef struct {
 
 typedef struct {
     int G, d, V, W, H, TX, TY;
+    int antialiased;     /* opacity-compensated 2D filter (see project32) */
     float near_plane, far_plane;
     double bg[3];
     float* means;  /* [G,3] */
@@ -331,6 +335,19 @@ static void project32(const scene* s, int g, int v, rec32* r)
     float c = (u11 * j11 + u12 * j12) + DILATION_F;
     float det = a * c - b * b;
     if (!(det > 0.0f)) return;
+    /* antialiased mode: the 0.3 px^2 dilation widens the footprint, so opacity is
+     * scaled by sqrt(det of the undilated 2D covariance / det of the dilated one),
+     * which keeps the integrated weight and depends on depth through the
+     * projected covariance (the depth-dependent antialiasing the Proposal's mean
+     * score stops gradient through) */
+    float opx = op;
+    if (s->antialiased) {
+        float a_r = u00 * j00 + u02 * j02;
+        float c_r = u11 * j11 + u12 * j12;
+        float det_r = a_r * c_r - b * b;
+        r->comp_ok = det_r > 0.0f;
+        opx = op * (r->comp_ok ? sqrtf(det_r / det) : 0.0f);
+    }
     float idet = 1.0f / det;
     float ca = c * idet, cb = -b * idet, cc = a * idet;
     float mid = 0.5f * (a + c);
@@ -374,7 +391,7 @@ static void project32(const scene* s, int g, int v, rec32* r)
     r->qa = ca * g_nhl2e;
     r->qb = cb * g_nl2e;
     r->qc = cc * g_nhl2e;
-    r->opac = op;
+    r->opac = opx;
     r->depth = tz;
     r->radius = rad;
     r->rect[0] = x0;
@@ -410,6 +427,7 @@ typedef struct {
     int clip_x, clip_y;    /* 1 where that clamp is active */
     double Jc[6];          /* perspective Jacobian at the clamped centre, 2x3 row-major */
     double a, b, c, det;   /* dilated 2D covariance [[a, b], [b, c]] and its determinant */
+    double ar, cr;         /* undilated diagonal entries (a - 0.3, c - 0.3 before rounding) */
     double dir[3], len;    /* unit view direction from the camera centre, distance */
 } fwd64;
 
@@ -486,6 +504,8 @@ static void forward64(const scene* s, int g, int v, fwd64* f)
                 for (int l = 0; l < 3; ++l) acc += Jc[3 * i + k] * f->Cc[3 * k + l] * Jc[3 * j + l];
             S2[2 * i + j] = acc;
         }
+    f->ar = S2[0];
+    f->cr = S2[3];
     f->a = S2[0] + 0.3;
     f->b = 0.5 * (S2[1] + S2[2]);
     f->c = S2[3] + 0.3;
@@ -501,10 +521,16 @@ static void project64(const scene* s, int g, int v, const rec32* r32, rec64* r)
 {
     memset(r, 0, sizeof *r);
     const double* sh = s->sh64 + (int64_t)g * s->d * 3;
-    r->opac = s->p64[11 * (int64_t)g + 10];
+    r->opac_raw = s->p64[11 * (int64_t)g + 10];
+    r->opac = r->opac_raw;
+    r->comp = 1.0;
     if (r32->culled) return;
     fwd64 f;
     forward64(s, g, v, &f);
+    if (s->antialiased) {
+        r->comp = r32->comp_ok ? sqrt((f.ar * f.cr - f.b * f.b) / f.det) : 0.0;
+        r->opac = r->opac_raw * r->comp;
+    }
     const double tx = f.tc[0], ty = f.tc[1], tz = f.tc[2];
     r->ca = f.c / f.det;
     r->cb = -f.b / f.det;
@@ -529,7 +555,7 @@ static void project64(const scene* s, int g, int v, const rec32* r32, rec64* r)
 
 void* orc_scene_new(int G, int sh_degree, const float* means, const float* quats, const float* scales,
                     const float* opac, const float* sh, int V, const float* cams, int W, int H,
-                    float near_plane, float far_plane, const float* bg)
+                    float near_plane, float far_plane, const float* bg, int antialiased)
 {
     init_constants();
     if (G < 0 || V <= 0 || W <= 0 || H <= 0 || sh_degree < 0 || sh_degree > 3) return NULL;
@@ -543,6 +569,7 @@ void* orc_scene_new(int G, int sh_degree, const float* means, const float* quats
     s->TY = (H + TILE - 1) / TILE;
     s->near_plane = near_plane;
     s->far_plane = far_plane;
+    s->antialiased = antialiased != 0;
     for (int i = 0; i < 3; ++i) s->bg[i] = bg[i];
     size_t Gs = (size_t)G;
     s->means = (float*)malloc(sizeof(float) * 3 * Gs + 1);
@@ -857,7 +884,7 @@ void orc_render_tiles(void* p, const int64_t* tiles, int64_t n_tiles, const floa
                         add(&A[7], 1.0);
                         if (Ma) {
                             /* opacity logit: T alpha (1 - o) rho */
-                            double ta = c->T * c->alpha * (1.0 - q->opac) * rho;
+                            double ta = c->T * c->alpha * (1.0 - q->opac_raw) * rho;
                             /* projected centre: T o grad G rho, grad G = G conic (p - mu) */
                             double dx = pxd - q->mx, dy = pyd - q->my;
                             double gx = c->G * (q->ca * dx + q->cb * dy);
@@ -1265,8 +1292,9 @@ static void backward_params(scene* s, const double* g2d, double* out)
             const double tx = f.tc[0], ty = f.tc[1], tz = f.tc[2];
             double gmu[3] = {0, 0, 0}, gt[3] = {0, 0, 0};
 
-            /* opacity */
-            o[10] += A[5];
+            /* opacity: alpha = o comp G, A[5] = dL/d(o comp) */
+            const double comp = s->r64[rid].comp, o_raw = s->r64[rid].opac_raw;
+            o[10] += comp * A[5];
 
             /* colour = max(0.5 + sum_k B_k(dir) sh_k, 0), clamp state frozen */
             double gpre[3];
@@ -1295,9 +1323,16 @@ static void backward_params(scene* s, const double* g2d, double* out)
             /* conic (ca, cb, cc) = (c, -b, a) / (a c - b^2) */
             const double a = f.a, b = f.b, c = f.c, D2 = f.det * f.det;
             const double gca = A[2], gcb = A[3], gcc = A[4];
-            const double ga = (-c * c * gca + b * c * gcb - b * b * gcc) / D2;
-            const double gb = (2.0 * b * c * gca - (a * c + b * b) * gcb + 2.0 * a * b * gcc) / D2;
-            const double gc = (-b * b * gca + a * b * gcb - a * a * gcc) / D2;
+            double ga = (-c * c * gca + b * c * gcb - b * b * gcc) / D2;
+            double gb = (2.0 * b * c * gca - (a * c + b * b) * gcb + 2.0 * a * b * gcc) / D2;
+            double gc = (-b * b * gca + a * b * gcb - a * a * gcc) / D2;
+            if (s->antialiased && comp > 0.0) {
+                /* comp = sqrt(det_r / det): d comp = comp (d log det_r - d log det) / 2 */
+                const double dr = f.ar * f.cr - b * b, gcomp = o_raw * A[5] * comp;
+                ga += gcomp * (0.5 * f.cr / dr - 0.5 * c / f.det);
+                gb += gcomp * (-b / dr + b / f.det);
+                gc += gcomp * (0.5 * f.ar / dr - 0.5 * a / f.det);
+            }
             /* a, b, c are the entries of S2 = Jc Cc Jc^T (+ dilation), b the mean of the two off-diagonals */
             const double G2[4] = {ga, 0.5 * gb, 0.5 * gb, gc};
             /* dL/dCc = Jc^T G2 Jc,  dL/dJc = 2 G2 Jc Cc (G2, Cc symmetric) */
@@ -1430,7 +1465,11 @@ void orc_set_opacity64(void* p, int g, double o)
 {
     scene* s = (scene*)p;
     s->p64[11 * (int64_t)g + 10] = o;
-    for (int v = 0; v < s->V; ++v) s->r64[(int64_t)v * s->G + g].opac = o;
+    for (int v = 0; v < s->V; ++v) {
+        rec64* r = &s->r64[(int64_t)v * s->G + g];
+        r->opac_raw = o;
+        r->opac = o * r->comp;
+    }
 }
 
 void orc_set_sh64(void* p, int g, int k, int ch, double value)

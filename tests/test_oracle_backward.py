@@ -12,6 +12,7 @@ direction).  It is pinned here against things other than itself:
   * the score replay's opacity-logit and SH scores, which are the same
     derivatives of 1/2 |C_hat - C|^2 reached through the suffix equation
     (epsilon -> 0, no suffix-denominator mask).
+Every check runs in the plain and the antialiased (opacity-compensated) mode.
 """
 from __future__ import annotations
 
@@ -22,11 +23,11 @@ import oracle
 import scenes
 
 
-@pytest.fixture(scope="module")
-def bw_setup():
+@pytest.fixture(scope="module", params=[False, True], ids=["plain", "antialiased"])
+def bw_setup(request):
     sc = scenes.rotated_clip_scene()
     gC = np.random.default_rng(2).uniform(-1, 1, size=(sc.n_views, sc.height, sc.width, 3)).astype(np.float32)
-    o = oracle.OracleScene(sc)
+    o = oracle.OracleScene(sc, antialiased=request.param)
     o.build_lists()
     grads, g2d = o.backward(gC, with_image_sums=True)
     return sc, gC, o, grads, g2d
@@ -125,14 +126,15 @@ def test_sh_basis_derivative_matches_finite_difference():
         assert np.allclose(dB[:, :, j], fd, rtol=1e-7, atol=1e-8)
 
 
-def test_backward_of_squared_residual_equals_replay_scores():
+@pytest.mark.parametrize("antialiased", [False, True])
+def test_backward_of_squared_residual_equals_replay_scores(antialiased):
     """With dL/dC_hat = C_hat - C_obs the backward is the gradient of
     1/2 |C_hat - C_obs|^2; the replay reaches the same opacity-logit and SH scores
     (summed over views) through the suffix equation when epsilon -> 0 and the
     suffix-denominator mask is off."""
     sc = scenes.tiny_scene(seed=7, n=14, n_views=2, W=32, H=32, sh_degree=2)
     obs = np.random.default_rng(1).uniform(0, 1, size=(2, 32, 32, 3)).astype(np.float32)
-    o = oracle.OracleScene(sc)
+    o = oracle.OracleScene(sc, antialiased=antialiased)
     o.build_lists()
     o.select(None)
     color, _, _, _ = o.render(obs=obs, eps=1e-30, den_min=0.0)
