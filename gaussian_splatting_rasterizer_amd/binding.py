@@ -65,7 +65,7 @@ class gs_dims(ctypes.Structure):
 class gs_params(ctypes.Structure):
     _fields_ = [("eps", ctypes.c_float), ("den_min", ctypes.c_float), ("lam", ctypes.c_float),
                 ("near_plane", ctypes.c_float), ("far_plane", ctypes.c_float),
-                ("background", ctypes.c_float * 3)]
+                ("background", ctypes.c_float * 3), ("antialiased", ctypes.c_int32)]
 
 
 class GsrError(RuntimeError):
@@ -417,10 +417,12 @@ class Rasterizer:
         return dst
 
 
-def rasterizer_for_scene(scene, params: gs_params | None = None, max_pairs=None, device="cuda") -> Rasterizer:
+def rasterizer_for_scene(scene, params: gs_params | None = None, max_pairs=None, device="cuda",
+                         antialiased=False) -> Rasterizer:
     """Build a Rasterizer from a `scenes.Scene`-like object (means, quats, ... attributes)."""
     p = params if params is not None else gs_default_params()
     if params is None:
         p.background[:] = [float(x) for x in np.asarray(scene.background, dtype=np.float32)]
+        p.antialiased = 1 if antialiased else 0
     return Rasterizer(scene.means, scene.quats, scene.scales, scene.opacities, scene.sh, scene.sh_degree,
                       scene.cams, scene.width, scene.height, params=p, max_pairs=max_pairs, device=device)

@@ -221,6 +221,7 @@ gs_status gs_default_params(gs_params* out) {
     out->near_plane = 0.01f;
     out->far_plane = 1e10f;
     out->background[0] = out->background[1] = out->background[2] = 0.0f;
+    out->antialiased = 0;
     return GS_OK;
 }
 
@@ -281,7 +282,8 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
         }
     }
     if (!(params->eps >= 0.0f) || !(params->den_min >= 0.0f) || !(params->lambda >= 0.0f) ||
-        !(params->near_plane > 0.0f) || !(params->far_plane > params->near_plane))
+        !(params->near_plane > 0.0f) || !(params->far_plane > params->near_plane) ||
+        (params->antialiased != 0 && params->antialiased != 1))
         return fail(GS_ERR_INVALID_ARGUMENT, "invalid params");
     for (int v = 0; v < s.V; ++v) {
         const gs_camera& c = cams[v];
@@ -297,7 +299,8 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
     ctx->params = *params;
     ctx->state = kCreated;
     ctx->timer.begin(stream);
-    hipError_t e = launch_project(*sc, ctx->cams, s, params->near_plane, params->far_plane, ctx->ws, stream);
+    hipError_t e = launch_project(*sc, ctx->cams, s, params->near_plane, params->far_plane, params->antialiased,
+                                  ctx->ws, stream);
     if (e != hipSuccess) return hip_fail(e, "project");
     ctx->timer.end(GS_STAGE_PROJECT, stream);
     ctx->state = kProjected;
@@ -439,7 +442,7 @@ gs_status gs_backward(gs_context* ctx, const float* grad_color, const gs_gaussia
     ctx->timer.begin(stream);
     e = launch_gather_slots(ctx->s, ctx->ws, 3, stream);
     if (e != hipSuccess) return hip_fail(e, "backward gather");
-    e = launch_backward_finalize(ctx->scene, ctx->cams, ctx->s, ctx->ws, *grads, stream);
+    e = launch_backward_finalize(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.antialiased, *grads, stream);
     if (e != hipSuccess) return hip_fail(e, "gradients");
     ctx->timer.end(GS_STAGE_BACKWARD_FINALIZE, stream);
     return GS_OK;

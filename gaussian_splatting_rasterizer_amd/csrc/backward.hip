@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
                                                         const float* __restrict__ scales,
                                                         const float* __restrict__ opac, const float* __restrict__ sh,
                                                         int64_t G, int V, int W, int H, CamPack cams,
-                                                        const uint64_t* __restrict__ rec_masks,
+                                                        int antialiased, const uint64_t* __restrict__ rec_masks,
                                                         const float4* __restrict__ gv_sums, gs_gaussian_grads out) {
 #pragma clang fp contract(fast)
     const int64_t g = (int64_t)blockIdx.x * kGradThreads + threadIdx.x;
@@ -299,9 +299,10 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
         // Jc Cc (rows 0, 1) and the dilated 2D covariance [[a, b], [b, c]]
         const double A0[3] = {j00 * Cc[0] + j02 * Cc[6], j00 * Cc[1] + j02 * Cc[7], j00 * Cc[2] + j02 * Cc[8]};
         const double A1[3] = {j11 * Cc[3] + j12 * Cc[6], j11 * Cc[4] + j12 * Cc[7], j11 * Cc[5] + j12 * Cc[8]};
-        const double a = A0[0] * j00 + A0[2] * j02 + 0.3;
+        const double ar = A0[0] * j00 + A0[2] * j02, cr = A1[1] * j11 + A1[2] * j12;  // undilated
+        const double a = ar + 0.3;
         const double b = A0[1] * j11 + A0[2] * j12;
-        const double c = A1[1] * j11 + A1[2] * j12 + 0.3;
+        const double c = cr + 0.3;
         const double det = a * c - b * b, idet = 1.0 / det;
         const double ca = c * idet, cb = -b * idet, cc = a * idet;
 
@@ -312,9 +313,19 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
         const double gca = -0.5 * Uxx, gcb = -Uxy, gcc = -0.5 * Uyy;
         // conic (c, -b, a) / det -> (a, b, c)
         const double id2 = idet * idet;
-        const double ga = (-c * c * gca + b * c * gcb - b * b * gcc) * id2;
-        const double gb = (2.0 * b * c * gca - (a * c + b * b) * gcb + 2.0 * a * b * gcc) * id2;
-        const double gc = (-b * b * gca + a * b * gcb - a * a * gcc) * id2;
+        double ga = (-c * c * gca + b * c * gcb - b * b * gcc) * id2;
+        double gb = (2.0 * b * c * gca - (a * c + b * b) * gcb + 2.0 * a * b * gcc) * id2;
+        double gc = (-b * b * gca + a * b * gcb - a * a * gcc) * id2;
+        if (antialiased) {
+            // alpha = o comp G with comp = sqrt(det_r / det): U d log comp, d log comp = (d log det_r - d log det) / 2
+            const double detr = ar * cr - b * b;
+            if (detr > 0.0) {
+                const double idr = 1.0 / detr;
+                ga += U * (0.5 * cr * idr - 0.5 * c * idet);
+                gb += U * (b * idet - b * idr);
+                gc += U * (0.5 * ar * idr - 0.5 * a * idet);
+            }
+        }
         const double g00 = ga, g01 = 0.5 * gb, g11 = gc;  // dL/dS2, S2 = Jc Cc Jc^T
         // dL/dCc = Jc^T G2 Jc
         const double GC00 = j00 * j00 * g00, GC01 = j00 * j11 * g01, GC02 = j00 * (g00 * j02 + g01 * j12);
@@ -448,12 +459,12 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
 }
 
 hipError_t launch_backward_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
-                        const gs_gaussian_grads& out, hipStream_t st) {
+                                    int antialiased, const gs_gaussian_grads& out, hipStream_t st) {
     if (s.G == 0) return hipSuccess;
     const dim3 block(kGradThreads), grid((unsigned)((s.G + kGradThreads - 1) / kGradThreads));
 #define GSR_LAUNCH_GRADS(DD)                                                                                   \
     hipLaunchKernelGGL(k_grads<DD>, grid, block, 0, st, sc.means, sc.quats, sc.scales, sc.opacities, sc.sh, s.G, \
-                       s.V, s.W, s.H, cams, ws.rec_masks, ws.gv_sums, out)
+                       s.V, s.W, s.H, cams, antialiased, ws.rec_masks, ws.gv_sums, out)
     switch (s.d) {
         case 1: GSR_LAUNCH_GRADS(1); break;
         case 4: GSR_LAUNCH_GRADS(4); break;

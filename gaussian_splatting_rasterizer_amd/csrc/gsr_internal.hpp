@@ -88,7 +88,7 @@ Sizes make_sizes(const gs_dims& d);
 // ---- launchers (return hipGetLastError of the launch) ----------------------
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
 hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, float near_plane,
-                          float far_plane, Workspace& ws, hipStream_t st);
+                          float far_plane, int antialiased, Workspace& ws, hipStream_t st);
 // exclusive scan of in (u32) into out (may alias); total -> *total (device u64)
 hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
                            hipStream_t st);
@@ -138,7 +138,8 @@ hipError_t launch_backward(const Sizes& s, const Workspace& ws, const uint32_t* 
                            hipStream_t st);
 // per (Gaussian, view): the record's backward sums and the chain rule to the parameters, summed over views
 hipError_t launch_backward_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s,
-                                    const Workspace& ws, const gs_gaussian_grads& out, hipStream_t st);
+                                    const Workspace& ws, int antialiased, const gs_gaussian_grads& out,
+                                    hipStream_t st);
 hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
                          float eps, float lambda, float* tokens, hipStream_t st);
 hipError_t launch_exp2(const float* in, float* out, int64_t n, hipStream_t st);

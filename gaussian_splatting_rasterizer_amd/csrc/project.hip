@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
                                                   const float* __restrict__ scales, const float* __restrict__ opac,
                                                   const float* __restrict__ sh, int64_t G, int V, CamPack cams,
                                                   int W, int H, int TX, int TY, float near_plane, float far_plane,
-                                                  float4* __restrict__ rec0, float4* __restrict__ rec1,
+                                                  int antialiased, float4* __restrict__ rec0, float4* __restrict__ rec1,
                                                   float2* __restrict__ rec2, uint2* __restrict__ rect,
                                                   uint32_t* __restrict__ depth_key,
                                                   uint32_t* __restrict__ tiles_touched) {
@@ -117,6 +117,14 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         const float cq = (u11 * j11 + u12 * j12) + kDilation;
         const float det = a * cq - b * b;
         ok = ok && (det > 0.0f);
+        // antialiased mode: opacity scaled by sqrt(det of the undilated covariance / det)
+        float opx = op;
+        if (antialiased) {
+            const float a_r = u00 * j00 + u02 * j02;
+            const float c_r = u11 * j11 + u12 * j12;
+            const float det_r = a_r * c_r - b * b;
+            opx = op * (det_r > 0.0f ? __builtin_sqrtf(det_r / det) : 0.0f);
+        }
         const float idet = 1.0f / det;
         const float ca = cq * idet, cb = -b * idet, cc = a * idet;
         const float mid = 0.5f * (a + cq);
@@ -166,8 +174,8 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         const float4 r0v = make_float4(mx, my, ca * kNegHalfLog2e, cb * kNegLog2e);
         const float qcv = cc * kNegHalfLog2e;
         rec0[rid] = r0v;
-        rec1[rid] = make_float4(qcv, op, pre[0], pre[1]);
-        rec2[rid] = make_float2(pre[2], __uint_as_float(entry_box_pack(r0v, qcv, op)));
+        rec1[rid] = make_float4(qcv, opx, pre[0], pre[1]);
+        rec2[rid] = make_float2(pre[2], __uint_as_float(entry_box_pack(r0v, qcv, opx)));
         rect[rid] = make_uint2((uint32_t)x0 | ((uint32_t)y0 << 16), (uint32_t)x1 | ((uint32_t)y1 << 16));
         depth_key[rid] = __float_as_uint(tz);
         tiles_touched[rid] = (uint32_t)((x1 - x0) * (y1 - y0));
@@ -175,13 +183,13 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
 }
 
 hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, float near_plane,
-                          float far_plane, Workspace& ws, hipStream_t st) {
+                          float far_plane, int antialiased, Workspace& ws, hipStream_t st) {
     if (s.G == 0) return hipSuccess;
     const dim3 block(256), grid((unsigned)((s.G + 255) / 256));
 #define GSR_LAUNCH_PROJECT(DD)                                                                             \
     hipLaunchKernelGGL(k_project<DD>, grid, block, 0, st, sc.means, sc.quats, sc.scales, sc.opacities, sc.sh, \
-                       s.G, s.V, cams, s.W, s.H, s.TX, s.TY, near_plane, far_plane, ws.rec0, ws.rec1,     \
-                       ws.rec2, ws.rect, ws.depth_key, ws.tiles_touched)
+                       s.G, s.V, cams, s.W, s.H, s.TX, s.TY, near_plane, far_plane, antialiased, ws.rec0,  \
+                       ws.rec1, ws.rec2, ws.rect, ws.depth_key, ws.tiles_touched)
     switch (s.d) {
         case 1: GSR_LAUNCH_PROJECT(1); break;
         case 4: GSR_LAUNCH_PROJECT(4); break;

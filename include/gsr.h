@@ -104,7 +104,14 @@ typedef struct {
  *              this is masked out of the opacity and mean scores (default 1e-3)
  *   lambda     ridge of the conditioning matrix A = lambda I + ... (default 1)
  *   near_plane, far_plane   depth culling range (defaults 0.01, 1e10)
- *   background colour added behind the last contributor (default 0). */
+ *   background colour added behind the last contributor (default 0)
+ *   antialiased  0 (default) or 1: opacity-compensated 2D filter -- the 0.3 px^2
+ *              dilation is kept and each (Gaussian, view) opacity is scaled by
+ *              sqrt(det S / det(S + 0.3 I)) (S the undilated projected
+ *              covariance; 0 when det S <= 0), so a footprint keeps the
+ *              integrated weight of the undilated Gaussian.  The score replay's
+ *              opacity score keeps the Gaussian's own o in (1 - o); gs_backward
+ *              differentiates the compensation too. */
 typedef struct {
     float eps;
     float den_min;
@@ -112,6 +119,7 @@ typedef struct {
     float near_plane;
     float far_plane;
     float background[3];
+    int32_t antialiased;
 } gs_params;
 
 typedef struct gs_context gs_context;

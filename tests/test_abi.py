@@ -37,6 +37,7 @@ def test_status_strings_and_defaults():
     p = b.gs_default_params()
     assert abs(p.eps - 1e-6) < 1e-12 and abs(p.den_min - 1e-3) < 1e-9 and p.lam == 1.0
     assert abs(p.near_plane - 0.01) < 1e-8 and list(p.background) == [0.0, 0.0, 0.0]
+    assert p.antialiased == 0
 
 
 def _dims(**kw):
@@ -116,6 +117,9 @@ def test_calls_out_of_order_are_rejected_without_launching():
         bad.near_plane = 0.0
         g = b.gs_gaussians(256, 256, 256, 256, 256, 1000, 3)
         assert lib.gs_project(ctx, ctypes.byref(g), cams, ctypes.byref(bad), None) == b.GS_ERR_INVALID_ARGUMENT
+        bad2 = b.gs_default_params()
+        bad2.antialiased = 2
+        assert lib.gs_project(ctx, ctypes.byref(g), cams, ctypes.byref(bad2), None) == b.GS_ERR_INVALID_ARGUMENT
         cams0 = b.make_cameras([[1, 0, 0, 0, 1, 0, 0, 0, 1, 0, 0, 0, 0, 64, 32, 24]] * 2)
         assert lib.gs_project(ctx, ctypes.byref(g), cams0, ctypes.byref(p), None) == b.GS_ERR_INVALID_ARGUMENT
         # exports before the data exists

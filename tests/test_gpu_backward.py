@@ -50,7 +50,14 @@ def _scenes():
         "elongated": lambda: scenes.tiny_scene(seed=8, n=400, n_views=2, W=96, H=80, sh_degree=3,
                                                log_scale=(-3.0, 1.6), spread=0.6),
         "tiny_deg0": lambda: scenes.tiny_scene(seed=13, n=50, n_views=2, W=48, H=40, sh_degree=0),
+        # antialiased (opacity-compensated) mode: the compensation's covariance path
+        "rotated_clip_aa": lambda: scenes.rotated_clip_scene(),
+        "c2_small_aa": lambda: scenes.c2_resplat_step(n_views=2, W=112, H=64),
     }
+
+
+def _aa(name):
+    return name.endswith("_aa")
 
 
 _CACHE = {}
@@ -59,9 +66,9 @@ _CACHE = {}
 def _grad_input(name, sc):
     """Upstream gradient: the residual of a rendered observation for the workloads
     (the gradient of 1/2 |C_hat - C|^2), uniform(-1, 1) for the synthetic cases."""
-    if name in ("c2_small", "c5_small", "c1_toy"):
-        obs = oracle.render_observation(sc)
-        o = oracle.OracleScene(sc)
+    if name in ("c2_small", "c5_small", "c1_toy", "c2_small_aa"):
+        obs = oracle.render_observation(sc, antialiased=_aa(name))
+        o = oracle.OracleScene(sc, antialiased=_aa(name))
         color, _, _, _ = o.render()
         o.close()
         return (color - obs.astype(np.float64)).astype(np.float32)
@@ -82,11 +89,11 @@ def _case(name):
         from gaussian_splatting_rasterizer_amd import binding
         sc = _scenes()[name]()
         gC = _grad_input(name, sc)
-        o = oracle.OracleScene(sc)
+        o = oracle.OracleScene(sc, antialiased=_aa(name))
         o.build_lists()
         ref, g2d = o.backward(gC, with_image_sums=True)
         o.close()
-        r = binding.rasterizer_for_scene(sc)
+        r = binding.rasterizer_for_scene(sc, antialiased=_aa(name))
         r.project_and_bin()
         r.render()
         grads = r.backward(torch.from_numpy(gC).cuda())

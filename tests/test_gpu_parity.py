@@ -37,9 +37,9 @@ def _binding():
     return binding
 
 
-def _run_gpu(sc, obs):
+def _run_gpu(sc, obs, antialiased=False):
     b = _binding()
-    r = b.rasterizer_for_scene(sc)
+    r = b.rasterizer_for_scene(sc, antialiased=antialiased)
     r.project_and_bin()
     rec = r.export(b.GS_EXPORT_RECORDS).cpu().numpy()
     keys = r.export(b.GS_EXPORT_DEPTH_KEYS).cpu().numpy().view(np.uint32)
@@ -70,7 +70,15 @@ def _small_scenes():
         # a tile grid wider than 256 tiles (4200 px): the depth sort gathers rectangles instead of carrying them
         "wide_grid": lambda: scenes.tiny_scene(seed=31, n=3000, n_views=1, W=4200, H=48, sh_degree=1,
                                                log_scale=(-5.5, 0.5)),
+        # antialiased (opacity-compensated) mode
+        "c2_small_aa": lambda: scenes.c2_resplat_step(n_views=2, W=112, H=64),
+        "tiny_ragged_aa": lambda: scenes.tiny_scene(seed=21, n=60, n_views=2, W=40, H=24, sh_degree=2),
+        "c5_small_aa": lambda: scenes.c5_multiview_layers(n_views=3, W=100, H=56, n=12000),
     }
+
+
+def _aa(name):
+    return name.endswith("_aa")
 
 
 _CACHE = {}
@@ -80,13 +88,13 @@ def _case(name):
     if name not in _CACHE:
         _need_gpu()
         sc = _small_scenes()[name]()
-        obs = oracle.render_observation(sc)
-        ref = oracle.full_reference(sc, obs)
+        obs = oracle.render_observation(sc, antialiased=_aa(name))
+        ref = oracle.full_reference(sc, obs, antialiased=_aa(name))
         o = ref["oracle"]
         starts, ids = o.lists()
         ref["starts"], ref["ids"] = starts, ids
         ref["rec32"] = o.records32()
-        gpu = _run_gpu(sc, obs)
+        gpu = _run_gpu(sc, obs, antialiased=_aa(name))
         _CACHE[name] = (sc, obs, ref, gpu)
     return _CACHE[name]
 
