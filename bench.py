@@ -51,6 +51,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true",
                    help="skip the separately timed renderer backward (gs_backward of 1/2 |C_hat - C|^2)")
+    p.add_argument("--antialiased", action="store_true",
+                   help="run the whole path in the antialiased (opacity-compensated) mode")
     p.add_argument("--no-attributes", action="store_true",
                    help="skip the separately timed 9-channel feature composite and 2-channel attribution scatter")
     p.add_argument("--sweep", action="store_true",
@@ -148,7 +150,7 @@ def main():
 
     with torch.cuda.stream(stream):
         # observation: render of the scene with perturbed means + pixel noise (setup, untimed)
-        rp = binding.rasterizer_for_scene(sc.perturbed(), device=dev)
+        rp = binding.rasterizer_for_scene(sc.perturbed(), device=dev, antialiased=args.antialiased)
         rp.project_and_bin()
         obs_col, _, _ = rp.render()
         obs = (obs_col + torch.from_numpy(sc.pixel_noise).to(dev)).contiguous()
@@ -163,7 +165,7 @@ def main():
             stream.synchronize()
             del src_buf, dst_buf
 
-        r = binding.rasterizer_for_scene(sc, device=dev)
+        r = binding.rasterizer_for_scene(sc, device=dev, antialiased=args.antialiased)
         r.project_and_bin()
         r._alloc(int(r.n_pairs * 1.1) + 4096)      # right-size the workspace once
         outputs = r.new_outputs()
@@ -299,7 +301,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": scenes.CONFIG_NAMES[args.config], "views": V, "height": H, "width": W,
-                   "gaussians": sc.n, "sh_degree": sc.sh_degree, "pairs": P, "parallelism": "none"},
+                   "gaussians": sc.n, "sh_degree": sc.sh_degree, "pairs": P, "parallelism": "none",
+                   "mode": "antialiased" if args.antialiased else "plain"},
         "contribs_per_s": round(contribs, 1),
         "work_per_step": {"contributions": K, "evaluations": E, "near_evaluations": E_near, "pairs": P},
         "stages_ms": {k: round(v[0], 4) for k, v in stages.items()},
@@ -314,7 +317,7 @@ def main():
                              "attribution_2ch_ms": round(attrs["attribute"], 4), "finite": attrs["finite"]}
 
     if not args.no_cpu_baseline and args.cpu_baseline_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(sc, args.cpu_baseline_seconds)
+        out["cpu_baseline"] = cpu_baseline(sc, args.cpu_baseline_seconds, antialiased=args.antialiased)
     print(json.dumps(out), flush=True)
     return 0
 
@@ -376,7 +379,7 @@ def sweep(args, dev, stream):
     return 0
 
 
-def cpu_baseline(sc, budget_s):
+def cpu_baseline(sc, budget_s, antialiased=False):
     """The oracle as it stands, timed on the host cores on a bounded sample of the
     same workload: full preprocess + tile lists, then render + replay of an
     evenly spaced subset of tiles (with score sums for every Gaussian), then
@@ -387,7 +390,7 @@ def cpu_baseline(sc, budget_s):
 
     obs = (0.5 + sc.pixel_noise).astype(np.float32)   # the oracle is only timed here
     t0 = time.perf_counter()
-    o = oracle.OracleScene(sc)
+    o = oracle.OracleScene(sc, antialiased=antialiased)
     o.build_lists()
     t_fixed = time.perf_counter() - t0
     o.select(None)
