@@ -392,17 +392,29 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     if (dgt < nbins) {
         uint32_t excl = 0;
         if (tile > 0) {
-            const uint64_t* prev = mine - kMaxBins;
+            // look back in windows of 8 predecessors, all loads in flight together
+            constexpr int kWin = 8;
+            int64_t j = tile - 1;
             for (;;) {
-                const uint64_t w = __hip_atomic_load(prev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint32_t h = (uint32_t)(w >> 32);
-                if ((h & ~1u) != tag) {
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
+                uint64_t w[kWin];
+#pragma unroll
+                for (int q = 0; q < kWin; ++q)
+                    w[q] = (j - q >= 0) ? __hip_atomic_load(lookback + (j - q) * kMaxBins + dgt, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0ull;
+                int used = 0;
+                bool fin = false;
+#pragma unroll
+                for (int q = 0; q < kWin; ++q) {
+                    const uint32_t h = (uint32_t)(w[q] >> 32);
+                    if (fin || used != q || (h & ~1u) != tag) continue;
+                    excl += (uint32_t)w[q];
+                    used = q + 1;
+                    fin = (h & 1u) != 0u;
                 }
-                excl += (uint32_t)w;
-                if (h & 1u) break;
-                prev -= kMaxBins;
+                if (fin) break;
+                j -= used;
+                if (used == 0) __builtin_amdgcn_s_sleep(1);
             }
             __hip_atomic_store(mine, ((uint64_t)(tag | 1u) << 32) | (excl + tot), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
