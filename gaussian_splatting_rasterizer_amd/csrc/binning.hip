@@ -302,7 +302,7 @@ __device__ __forceinline__ uint2 unpack_rect(uint32_t q) {
 // second round after the keys, and unpacked with their tile counts in the last
 // pass; or, when the tile grid is too large to pack, gathered by record in the
 // last pass.  keys_out may be null.
-enum RadixMode { kPlain = 0, kCarryRect = 1, kGatherRect = 2 };
+enum RadixMode { kPlain = 0, kCarryRect = 1, kGatherRect = 2, kRanges = 3 };
 
 template <int MODE>
 __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
@@ -476,6 +476,12 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         if (ok) {
             if (keys_out) keys_out[pos[i]] = k;
             vals_out[pos[i]] = sval[lp];
+            if (MODE == kRanges) {
+                // equal keys are adjacent in the tile and contiguous in the output across tiles:
+                // a key's range is the min / max over the tiles of its first / last position
+                if (lp == 0 || skey[lp - 1] != k) atomicMin(&rc.ranges[k].x, pos[i]);
+                if (lp == nblk - 1 || skey[lp + 1] != k) atomicMax(&rc.ranges[k].y, pos[i] + 1u);
+            }
         }
     }
     if (MODE == kGatherRect) {
@@ -498,8 +504,8 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
 
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const RectSort* rs, const SortScratch& sc, uint32_t* epoch, hipStream_t st,
-                             uint32_t** keys_out, uint32_t** vals_out) {
+                             const RectSort* rs, uint2* ranges, const SortScratch& sc, uint32_t* epoch,
+                             hipStream_t st, uint32_t** keys_out, uint32_t** vals_out) {
     if (bits < 1) bits = 1;
     const int passes = (bits + kMaxDigitBits - 1) / kMaxDigitBits;
     const int dbits = (bits + passes - 1) / passes;
@@ -546,13 +552,19 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
             rc.gather_src = rs->rect;
             rc.rect_out = rs->rect_out;
             rc.tt_out = rs->tt_out;
+        } else if (!rs && last) {
+            rc.ranges = ranges;
         }
-        const int mode = (rc.pack_src || rc.pay_in) ? kCarryRect : rc.gather_src ? kGatherRect : kPlain;
+        const int mode = (rc.pack_src || rc.pay_in) ? kCarryRect
+                         : rc.gather_src            ? kGatherRect
+                         : rc.ranges                ? kRanges
+                                                    : kPlain;
 #define GSR_ONESWEEP(M)                                                                                       \
     hipLaunchKernelGGL(k_onesweep<M>, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, vsrc, n, shift, pb, \
                        sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins, sc.lookback, ep, kdst, vdst, rc)
         if (mode == kCarryRect) GSR_ONESWEEP(kCarryRect);
         else if (mode == kGatherRect) GSR_ONESWEEP(kGatherRect);
+        else if (mode == kRanges) GSR_ONESWEEP(kRanges);
         else GSR_ONESWEEP(kPlain);
 #undef GSR_ONESWEEP
         ksrc = kdst;
@@ -614,18 +626,23 @@ hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted
     return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_ranges(const uint32_t* __restrict__ keys, int64_t n, uint2* __restrict__ ranges) {
+__global__ __launch_bounds__(256) void k_ranges_init(uint2* __restrict__ ranges, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const uint32_t k = keys[i];
-    if (i == 0 || keys[i - 1] != k) ranges[k].x = (uint32_t)i;
-    if (i == n - 1 || keys[i + 1] != k) ranges[k].y = (uint32_t)(i + 1);
+    if (i < n) ranges[i] = make_uint2(0xffffffffu, 0u);
 }
 
-hipError_t launch_ranges(const uint32_t* sorted_keys, int64_t n, uint2* ranges, int64_t n_tiles, hipStream_t st) {
-    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(ranges), 2 * n_tiles, 0u, st);
-    if (e != hipSuccess) return e;
-    if (n > 0) hipLaunchKernelGGL(k_ranges, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, sorted_keys, n, ranges);
+__global__ __launch_bounds__(256) void k_ranges_fix(uint2* __restrict__ ranges, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n && ranges[i].x > ranges[i].y) ranges[i] = make_uint2(0u, 0u);  // no key: empty range
+}
+
+hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, hipStream_t st) {
+    if (n_tiles > 0) hipLaunchKernelGGL(k_ranges_init, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, st, ranges, n_tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_ranges_fix(uint2* ranges, int64_t n_tiles, hipStream_t st) {
+    if (n_tiles > 0) hipLaunchKernelGGL(k_ranges_fix, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, st, ranges, n_tiles);
     return hipGetLastError();
 }
 

@@ -112,6 +112,7 @@ struct RectCarry {
     const uint2* gather_src; // last pass without carrying: gather rect[val]
     uint2* rect_out;         // last pass: unpacked rectangles
     uint32_t* tt_out;        // last pass: tile counts
+    uint2* ranges;           // last pass of a key sort: per-key [start, end) (atomic min / max)
 };
 // Stable LSD radix sort of (keys, vals) on bits [0, bits), digits of up to 8
 // bits; vals_in == null means identity values (the input index).  Pass p writes
@@ -120,13 +121,16 @@ struct RectCarry {
 // by pass 0).  rs (optional) moves tile rectangles along.  *keys_out /
 // *vals_out receive the arrays holding the result; with keys_out == null the
 // final pass does not write keys.  Each pass takes a new epoch from *epoch.
+// With ranges (and no rs), the last pass also records every key's output range
+// [start, end) in ranges[key], which the caller initialises to {~0u, 0}.
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const RectSort* rs, const SortScratch& sc, uint32_t* epoch, hipStream_t st,
-                             uint32_t** keys_out, uint32_t** vals_out);
+                             const RectSort* rs, uint2* ranges, const SortScratch& sc, uint32_t* epoch,
+                             hipStream_t st, uint32_t** keys_out, uint32_t** vals_out);
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st);
-hipError_t launch_ranges(const uint32_t* sorted_keys, int64_t n, uint2* ranges, int64_t n_tiles,
-                         hipStream_t st);
+// ranges before / after a sort that records them: {~0u, 0} everywhere, then empty ones to {0, 0}
+hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, hipStream_t st);
+hipError_t launch_ranges_fix(uint2* ranges, int64_t n_tiles, hipStream_t st);
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
                          const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st);
 hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* observed,
