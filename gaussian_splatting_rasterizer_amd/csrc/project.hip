@@ -20,12 +20,12 @@
 
 namespace gsr {
 
-template <int D>
+template <int D, bool AA>
 __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means, const float* __restrict__ quats,
                                                   const float* __restrict__ scales, const float* __restrict__ opac,
                                                   const float* __restrict__ sh, int64_t G, int V, CamPack cams,
                                                   int W, int H, int TX, int TY, float near_plane, float far_plane,
-                                                  int antialiased, float4* __restrict__ rec0, float4* __restrict__ rec1,
+                                                  float4* __restrict__ rec0, float4* __restrict__ rec1,
                                                   float2* __restrict__ rec2, uint2* __restrict__ rect,
                                                   uint32_t* __restrict__ depth_key,
                                                   uint32_t* __restrict__ tiles_touched) {
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         ok = ok && (det > 0.0f);
         // antialiased mode: opacity scaled by sqrt(det of the undilated covariance / det)
         float opx = op;
-        if (antialiased) {
+        if (AA) {
             const float a_r = u00 * j00 + u02 * j02;
             const float c_r = u11 * j11 + u12 * j12;
             const float det_r = a_r * c_r - b * b;
@@ -186,16 +186,21 @@ hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Siz
                           float far_plane, int antialiased, Workspace& ws, hipStream_t st) {
     if (s.G == 0) return hipSuccess;
     const dim3 block(256), grid((unsigned)((s.G + 255) / 256));
-#define GSR_LAUNCH_PROJECT(DD)                                                                             \
-    hipLaunchKernelGGL(k_project<DD>, grid, block, 0, st, sc.means, sc.quats, sc.scales, sc.opacities, sc.sh, \
-                       s.G, s.V, cams, s.W, s.H, s.TX, s.TY, near_plane, far_plane, antialiased, ws.rec0,  \
-                       ws.rec1, ws.rec2, ws.rect, ws.depth_key, ws.tiles_touched)
+#define GSR_LAUNCH_PROJECT(DD, AAA)                                                                        \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_project<DD, AAA>), grid, block, 0, st, sc.means, sc.quats, sc.scales,   \
+                       sc.opacities,                                                                      \
+                       sc.sh, s.G, s.V, cams, s.W, s.H, s.TX, s.TY, near_plane, far_plane, ws.rec0, ws.rec1, \
+                       ws.rec2, ws.rect, ws.depth_key, ws.tiles_touched)
+#define GSR_LAUNCH_PROJECT_D(DD)                 \
+    if (antialiased) GSR_LAUNCH_PROJECT(DD, true); \
+    else GSR_LAUNCH_PROJECT(DD, false)
     switch (s.d) {
-        case 1: GSR_LAUNCH_PROJECT(1); break;
-        case 4: GSR_LAUNCH_PROJECT(4); break;
-        case 9: GSR_LAUNCH_PROJECT(9); break;
-        default: GSR_LAUNCH_PROJECT(16); break;
+        case 1: GSR_LAUNCH_PROJECT_D(1); break;
+        case 4: GSR_LAUNCH_PROJECT_D(4); break;
+        case 9: GSR_LAUNCH_PROJECT_D(9); break;
+        default: GSR_LAUNCH_PROJECT_D(16); break;
     }
+#undef GSR_LAUNCH_PROJECT_D
 #undef GSR_LAUNCH_PROJECT
     return hipGetLastError();
 }
