@@ -77,10 +77,10 @@ def stage_bytes(stage, c):
         return VG * 8
     if stage == "emit":          # per record: id, rect, tile count, offset in; per pair: tile key and Gaussian out
         return VG * (4 + 8 + 4 + 4) + P * 8
-    if stage == "tile_sort":     # histogram + 2 passes of key+value in and out
-        return P * (4 + 2 * 16)
-    if stage == "ranges":
-        return P * 4 + V * c["T"] * 8
+    if stage == "tile_sort":     # histogram (keys), pass 1 key+value in and out, pass 2 key+value in, value out
+        return P * (4 + 16 + 12)
+    if stage == "ranges":        # empty-tile fix-up (the ranges come from the last tile-sort pass)
+        return V * c["T"] * 16
     return None
 
 
@@ -269,6 +269,8 @@ def main():
                               "traffic": measured_traffic("k_render", workload),
                               "avg_launch_ms": round(stages["render"][0], 4)}}
     for st in ("project", "depth_sort", "emit", "tile_sort", "ranges"):
+        if st not in stages:
+            continue
         by = stage_bytes(st, c)
         t = stages[st][0] * 1e-3
         secondary[st] = {"bound": "hbm", "achieved_gbs": round(by / t / 1e9, 1),
