@@ -324,19 +324,21 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     const int64_t tile = s_tile;
 
     const int64_t bbase = tile * kRadixTile;
-    const int64_t base = bbase + (int64_t)wave * (kRadixTile / kRadixWaves);
+    // element indices within the tile, 32-bit (cheap to recompute where needed)
+    const int nblk = (int)(n - bbase < kRadixTile ? n - bbase : kRadixTile);
+    const int wbase = wave * (kRadixTile / kRadixWaves) + lane;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t key[kRadixItems], val[kRadixItems], rank[kRadixItems];
 #pragma unroll
     for (int i = 0; i < kRadixItems; ++i) {
-        const int64_t k = base + i * 64 + lane;
-        const bool valid = k < n;
-        key[i] = valid ? keys_in[k] : 0u;
-        val[i] = valid ? (vals_in ? vals_in[k] : (uint32_t)k) : 0u;
+        const int e = wbase + i * 64;
+        const bool valid = e < nblk;
+        key[i] = valid ? keys_in[bbase + e] : 0u;
+        val[i] = valid ? (vals_in ? vals_in[bbase + e] : (uint32_t)(bbase + e)) : 0u;
     }
 #pragma unroll
     for (int i = 0; i < kRadixItems; ++i) {
-        const bool valid = base + i * 64 + lane < n;
+        const bool valid = wbase + i * 64 < nblk;
         const uint32_t dgt = (key[i] >> shift) & mask;
         const uint64_t peers = match_peers(dgt, bits, valid);
         const uint64_t lower = peers & lt_mask;
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     for (int i = 0; i < kRadixItems / 2; ++i) lpk[i] = 0u;
 #pragma unroll
     for (int i = 0; i < kRadixItems; ++i) {
-        if (base + i * 64 + lane >= n) continue;
+        if (wbase + i * 64 >= nblk) continue;
         const uint32_t lp = cnt[wave][(key[i] >> shift) & mask] + rank[i];
         skey[lp] = key[i];
         sval[lp] = val[i];
@@ -422,7 +424,6 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         gdelta[dgt] = digit_off + excl - loff;
     }
     __syncthreads();
-    const int64_t nblk = n - bbase < kRadixTile ? n - bbase : kRadixTile;
     if (MODE == kCarryRect) {
         // keys and values out; each element's output position is parked in the value buffer
 #pragma unroll 4
@@ -440,13 +441,13 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         uint32_t q[kRadixItems];
 #pragma unroll
         for (int i = 0; i < kRadixItems; ++i) {  // all loads in flight, then the LDS stores
-            const int64_t k = base + i * 64 + lane;
+            const int e = wbase + i * 64;
             q[i] = 0u;
-            if (k < n) q[i] = rc.pack_src ? pack_rect(rc.pack_src[k]) : rc.pay_in[k];
+            if (e < nblk) q[i] = rc.pack_src ? pack_rect(rc.pack_src[bbase + e]) : rc.pay_in[bbase + e];
         }
 #pragma unroll
         for (int i = 0; i < kRadixItems; ++i) {
-            if (base + i * 64 + lane >= n) continue;
+            if (wbase + i * 64 >= nblk) continue;
             skey[(lpk[i >> 1] >> (16 * (i & 1))) & 0xffffu] = q[i];
         }
         __syncthreads();
