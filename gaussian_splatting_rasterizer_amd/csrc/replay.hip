@@ -270,6 +270,12 @@ __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */,
 constexpr int kGatherThreads = 256;
 
 // NQ float4 per slot and per record: 2 for the score replay, 3 for the backward.
+// Each thread takes kGatherRecs records 64 apart (a wave covers kGatherRecs
+// runs of 64), so the records' independent loads -- tile count and slot base,
+// then the first bitmap word -- are in flight together, and the ballot over
+// one record index of the wave is exactly that run's 64-record mask word.
+constexpr int kGatherRecs = 4;
+
 template <int NQ>
 __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                                                                  const uint32_t* __restrict__ tiles_touched,
@@ -278,22 +284,33 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                                                                  const float4* __restrict__ partials,
                                                                  float4* __restrict__ gv_sums,
                                                                  uint64_t* __restrict__ rec_masks) {
-    const int64_t rid = (int64_t)blockIdx.x * kGatherThreads + threadIdx.x;
     const int lane = threadIdx.x & 63;
-    if (rid - lane >= VG) return;  // the whole wave is past the end
-    bool live = false, reached = false;
-    float4 a[NQ];
+    const int64_t wbase =
+        ((int64_t)blockIdx.x * (kGatherThreads / 64) + (threadIdx.x >> 6)) * (64 * kGatherRecs);
+    if (wbase >= VG) return;  // the whole wave is past the end
+    uint32_t tt[kGatherRecs], s0[kGatherRecs], w0[kGatherRecs];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) a[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (rid < VG) {
-        const uint32_t tt = tiles_touched[rid];
-        live = tt != 0u;  // culled records touch no tile
+    for (int j = 0; j < kGatherRecs; ++j) {
+        const int64_t rid = wbase + 64 * j + lane;
+        tt[j] = rid < VG ? tiles_touched[rid] : 0u;  // culled records touch no tile
+        s0[j] = rid < VG ? slot_base[rid] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kGatherRecs; ++j) w0[j] = tt[j] ? slot_bits[s0[j] >> 5] : 0u;
+#pragma unroll
+    for (int j = 0; j < kGatherRecs; ++j) {
+        const int64_t rid = wbase + 64 * j + lane;
+        const bool live = tt[j] != 0u;
+        bool reached = false;
+        float4 a[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) a[q] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (live) {
-            const uint32_t s0 = slot_base[rid], s1 = s0 + tt;
-            for (uint32_t w = s0 >> 5; w <= (s1 - 1u) >> 5; ++w) {
-                uint32_t bits = slot_bits[w];
-                const uint32_t lo = s0 > 32u * w ? s0 - 32u * w : 0u;
-                const uint32_t hi = s1 < 32u * w + 32u ? s1 - 32u * w : 32u;
+            const uint32_t sa = s0[j], sb = sa + tt[j];
+            for (uint32_t w = sa >> 5; w <= (sb - 1u) >> 5; ++w) {
+                uint32_t bits = w == (sa >> 5) ? w0[j] : slot_bits[w];
+                const uint32_t lo = sa > 32u * w ? sa - 32u * w : 0u;
+                const uint32_t hi = sb < 32u * w + 32u ? sb - 32u * w : 32u;
                 bits &= (hi >= 32u ? ~0u : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
                 while (bits) {
                     const uint32_t slot = 32u * w + (uint32_t)__builtin_ctz(bits);
@@ -312,23 +329,25 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                 }
             }
         }
-    }
-    // live / reached masks of the wave's 64 records (blocks start at multiples of 64)
-    const uint64_t live_mask = __ballot(live);
-    const uint64_t reached_mask = __ballot(reached);
-    if (lane == 0) {
-        rec_masks[2 * ((rid - lane) >> 6)] = live_mask;
-        rec_masks[2 * ((rid - lane) >> 6) + 1] = reached_mask;
-    }
-    if (reached) {
+        // live / reached masks of this run of 64 records
+        const uint64_t live_mask = __ballot(live);
+        const uint64_t reached_mask = __ballot(reached);
+        const int64_t run = wbase + 64 * j;
+        if (lane == 0 && run < VG) {
+            rec_masks[2 * (run >> 6)] = live_mask;
+            rec_masks[2 * (run >> 6) + 1] = reached_mask;
+        }
+        if (reached) {
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) gv_sums[NQ * rid + q] = a[q];
+            for (int q = 0; q < NQ; ++q) gv_sums[NQ * rid + q] = a[q];
+        }
     }
 }
 
 hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, int nq, hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
-    const dim3 grid((unsigned)((s.VG + kGatherThreads - 1) / kGatherThreads)), block(kGatherThreads);
+    const int64_t per_block = (int64_t)kGatherThreads * kGatherRecs;
+    const dim3 grid((unsigned)((s.VG + per_block - 1) / per_block)), block(kGatherThreads);
     if (nq == 3)
         hipLaunchKernelGGL(k_gather_slots<3>, grid, block, 0, st, s.VG, ws.tiles_touched, ws.slot_base,
                            ws.slot_bits, ws.partials, ws.gv_sums, ws.rec_masks);
@@ -365,20 +384,48 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
 #pragma unroll
         for (int k = 0; k < 3 * D; ++k) shnum[k] = 0.0f;
 
+        // every view's live / reached bit first (at most 32 views), the mask loads of 8 views in flight together
+        uint32_t live_bits = 0u, reach_bits = 0u;
+        for (int v0 = 0; v0 < V; v0 += 8) {
+            uint64_t lw[8], rw[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t rid = (int64_t)(v0 + u) * G + g;
+                lw[u] = v0 + u < V ? rec_masks[2 * (rid >> 6)] : 0ull;
+                rw[u] = v0 + u < V ? rec_masks[2 * (rid >> 6) + 1] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint64_t bit = 1ull << ((((int64_t)(v0 + u) * G + g)) & 63);
+                live_bits |= (uint32_t)((lw[u] & bit) != 0ull) << (v0 + u);
+                reach_bits |= (uint32_t)((rw[u] & bit) != 0ull) << (v0 + u);
+            }
+        }
+        // the reached views' sums are loaded one reached view ahead of the arithmetic (reached implies live)
+        const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        uint32_t pending = reach_bits;
+        float4 n0 = zero4, n1 = zero4;
+        if (pending) {
+            const int64_t rid = (int64_t)__builtin_ctz(pending) * G + g;
+            n0 = gv_sums[2 * rid];
+            n1 = gv_sums[2 * rid + 1];
+        }
         for (int v = 0; v < V; ++v) {
-            const int64_t rid = (int64_t)v * G + g;
-            const uint64_t bit = 1ull << (rid & 63);
-            const uint64_t live_w = rec_masks[2 * (rid >> 6)];
-            const uint64_t reach_w = rec_masks[2 * (rid >> 6) + 1];
-            if (!(live_w & bit)) {  // culled in this view: q = eps, J = 0, no scores
+            if (!((live_bits >> v) & 1u)) {  // culled in this view: q = eps, J = 0, no scores
                 Q += eps;
                 continue;
             }
-            const bool reached = (reach_w & bit) != 0;
-            float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = make_float4(0.f, 0.f, 0.f, 0.f);
+            const bool reached = ((reach_bits >> v) & 1u) != 0u;
+            float4 p0 = zero4, p1 = zero4;
             if (reached) {
-                p0 = gv_sums[2 * rid];
-                p1 = gv_sums[2 * rid + 1];
+                p0 = n0;
+                p1 = n1;
+                pending &= pending - 1u;  // v was the lowest pending view
+                if (pending) {
+                    const int64_t rid = (int64_t)__builtin_ctz(pending) * G + g;
+                    n0 = gv_sums[2 * rid];
+                    n1 = gv_sums[2 * rid + 1];
+                }
             }
             const double q = eps + (double)p0.x;
             Q += q;
