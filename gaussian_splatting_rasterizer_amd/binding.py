@@ -38,7 +38,7 @@ ABI_SYMBOLS = ("gs_default_params", "gs_workspace_size", "gs_context_create", "g
                "gs_project", "gs_bin_sort", "gs_render", "gs_score_replay", "gs_backward", "gs_render_features",
                "gs_attribute", "gs_status_string",
                "gs_last_error", "gs_debug_exp2", "gs_debug_export", "gs_debug_topk", "gs_profile_enable",
-               "gs_profile_read")
+               "gs_profile_stages", "gs_profile_read")
 
 
 class gs_gaussians(ctypes.Structure):
@@ -121,6 +121,8 @@ def load_library(path: str = LIB_PATH):
     lib.gs_debug_topk.argtypes = [P, ctypes.c_int32, P, P, P]
     lib.gs_profile_enable.restype = St
     lib.gs_profile_enable.argtypes = [P, ctypes.c_int32]
+    lib.gs_profile_stages.restype = St
+    lib.gs_profile_stages.argtypes = [P, ctypes.c_uint32]
     lib.gs_profile_read.restype = St
     lib.gs_profile_read.argtypes = [P, P, P, ctypes.c_int32]
     _lib = lib
@@ -234,6 +236,14 @@ def gs_debug_topk(ctx, k, ids, weights, stream=None) -> None:
 
 def gs_profile_enable(ctx, enable=True) -> None:
     _check(load_library().gs_profile_enable(ctx, int(bool(enable))), "gs_profile_enable")
+
+
+def gs_profile_stages(ctx, stages) -> None:
+    """Time only the named stages (names from STAGES)."""
+    mask = 0
+    for name in stages:
+        mask |= 1 << STAGES.index(name)
+    _check(load_library().gs_profile_stages(ctx, mask), "gs_profile_stages")
 
 
 def gs_profile_read(ctx) -> dict:

@@ -52,7 +52,7 @@ struct StageTimer {
         int stage;
         hipEvent_t a, b;
     };
-    bool on = false;
+    uint32_t mask = 0u;  // bit s: stage s is timed
     std::vector<hipEvent_t> pool;
     std::vector<Rec> pending;
     double ms[GS_NUM_STAGES] = {};
@@ -69,13 +69,15 @@ struct StageTimer {
         pool.pop_back();
         return e;
     }
-    void begin(hipStream_t st) {
-        if (!on) return;
+    void begin(int stage, hipStream_t st) {
+        if (open_ev) pool.push_back(open_ev);  // a stage left open by an early error return
+        open_ev = nullptr;
+        if (!((mask >> stage) & 1u)) return;
         open_ev = take();
         if (open_ev) (void)hipEventRecord(open_ev, st);
     }
     void end(int stage, hipStream_t st) {
-        if (!on || !open_ev) return;
+        if (!open_ev) return;  // begin left it unopened: the stage is not timed
         hipEvent_t e = take();
         if (!e) return;
         (void)hipEventRecord(e, st);
@@ -298,7 +300,7 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
     ctx->scene = *sc;
     ctx->params = *params;
     ctx->state = kCreated;
-    ctx->timer.begin(stream);
+    ctx->timer.begin(GS_STAGE_PROJECT, stream);
     hipError_t e = launch_project(*sc, ctx->cams, s, params->near_plane, params->far_plane, params->antialiased,
                                   ctx->ws, stream);
     if (e != hipSuccess) return hip_fail(e, "project");
@@ -334,7 +336,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     }
     const SortScratch sort_scratch{ws.lookback, ws.sort_ctl, ws.sort_part};
     // 0. slot bases of the replay's partials: tile counts scanned in record order
-    tm.begin(stream);
+    tm.begin(GS_STAGE_DEPTH_SORT, stream);
     e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream);
     if (e != hipSuccess) return hip_fail(e, "slot scan");
     // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
@@ -349,7 +351,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     if (e != hipSuccess) return hip_fail(e, "depth sort");
     tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
-    tm.begin(stream);
+    tm.begin(GS_STAGE_SCAN, stream);
     e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream);
     if (e != hipSuccess) return hip_fail(e, "scan");
     tm.end(GS_STAGE_SCAN, stream);
@@ -372,14 +374,14 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
                     (unsigned long long)s.max_pairs);
     }
     // 3. emit pairs in depth order, 4. stable sort by tile with the ranges, 5. empty ranges
-    tm.begin(stream);
+    tm.begin(GS_STAGE_EMIT, stream);
     e = launch_emit(s, ws, rid_sorted, stream);
     if (e != hipSuccess) return hip_fail(e, "emit");
     tm.end(GS_STAGE_EMIT, stream);
     const int64_t tiles = (int64_t)s.V * s.T;
     uint32_t* sorted_g = nullptr;
     // the last pass of the tile sort records every tile's [start, end) (sorted keys are not kept)
-    tm.begin(stream);
+    tm.begin(GS_STAGE_TILE_SORT, stream);
     e = launch_ranges_init(ws.ranges, tiles, stream);
     if (e != hipSuccess) return hip_fail(e, "ranges init");
     e = launch_radix_sort(ws.pkey_emit, ws.pair_g, (int64_t)total, bits_for((uint64_t)tiles), ws.pkey_b, ws.pkey_c,
@@ -387,7 +389,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
                           &sorted_g);
     if (e != hipSuccess) return hip_fail(e, "tile sort");
     tm.end(GS_STAGE_TILE_SORT, stream);
-    tm.begin(stream);
+    tm.begin(GS_STAGE_RANGES, stream);
     e = launch_ranges_fix(ws.ranges, tiles, stream);
     if (e != hipSuccess) return hip_fail(e, "ranges");
     tm.end(GS_STAGE_RANGES, stream);
@@ -401,7 +403,7 @@ gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_co
     if (ctx->state < kBinned) return fail(GS_ERR_STATE, "gs_render before gs_bin_sort");
     if ((color && !aligned(color, 4)) || (T_final && !aligned(T_final, 4)) || (n_contrib && !aligned(n_contrib, 4)))
         return fail(GS_ERR_INVALID_ARGUMENT, "misaligned output pointer");
-    ctx->timer.begin(stream);
+    ctx->timer.begin(GS_STAGE_RENDER, stream);
     hipError_t e = launch_render(ctx->s, ctx->ws, ctx->sorted_g, ctx->n_pairs, ctx->params.background, color,
                                  T_final, n_contrib, stream);
     if (e != hipSuccess) return hip_fail(e, "render");
@@ -415,12 +417,12 @@ gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens,
     if (ctx->state < kRendered) return fail(GS_ERR_STATE, "gs_score_replay before gs_render");
     if (!observed || !tokens) return fail(GS_ERR_INVALID_ARGUMENT, "null observed or tokens");
     if (!aligned(observed, 4) || !aligned(tokens, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
-    ctx->timer.begin(stream);
+    ctx->timer.begin(GS_STAGE_REPLAY, stream);
     hipError_t e = launch_replay(ctx->s, ctx->ws, ctx->sorted_g, observed, ctx->params.eps, ctx->params.den_min,
                                  stream);
     if (e != hipSuccess) return hip_fail(e, "replay");
     ctx->timer.end(GS_STAGE_REPLAY, stream);
-    ctx->timer.begin(stream);
+    ctx->timer.begin(GS_STAGE_FINALIZE, stream);
     e = launch_gather_slots(ctx->s, ctx->ws, 2, stream);
     if (e != hipSuccess) return hip_fail(e, "gather");
     e = launch_tokens(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.eps, ctx->params.lambda, tokens, stream);
@@ -437,11 +439,11 @@ gs_status gs_backward(gs_context* ctx, const float* grad_color, const gs_gaussia
     const float* outs[5] = {grads->means, grads->quats, grads->scales, grads->opacities, grads->sh};
     for (const float* p : outs)
         if (p && !aligned(p, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned gradient pointer");
-    ctx->timer.begin(stream);
+    ctx->timer.begin(GS_STAGE_BACKWARD, stream);
     hipError_t e = launch_backward(ctx->s, ctx->ws, ctx->sorted_g, grad_color, stream);
     if (e != hipSuccess) return hip_fail(e, "backward");
     ctx->timer.end(GS_STAGE_BACKWARD, stream);
-    ctx->timer.begin(stream);
+    ctx->timer.begin(GS_STAGE_BACKWARD_FINALIZE, stream);
     e = launch_gather_slots(ctx->s, ctx->ws, 3, stream);
     if (e != hipSuccess) return hip_fail(e, "backward gather");
     e = launch_backward_finalize(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.antialiased, *grads, stream);
@@ -458,7 +460,7 @@ gs_status gs_render_features(gs_context* ctx, const float* features, int32_t n_c
     if ((ctx->s.G > 0 && !features) || !out) return fail(GS_ERR_INVALID_ARGUMENT, "null features or out");
     if ((features && !aligned(features, 4)) || !aligned(out, 4))
         return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
-    ctx->timer.begin(stream);
+    ctx->timer.begin(GS_STAGE_FEATURES, stream);
     hipError_t e = launch_render_features(ctx->s, ctx->ws, ctx->sorted_g, features, n_channels, background, out,
                                           stream);
     if (e != hipSuccess) return hip_fail(e, "feature composite");
@@ -472,7 +474,7 @@ gs_status gs_attribute(gs_context* ctx, const float* pixel_map, int32_t n_channe
     if (n_channels < 1) return fail(GS_ERR_INVALID_ARGUMENT, "n_channels must be >= 1");
     if (!pixel_map || (ctx->s.G > 0 && !out)) return fail(GS_ERR_INVALID_ARGUMENT, "null pixel_map or out");
     if (!aligned(pixel_map, 4) || (out && !aligned(out, 4))) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
-    ctx->timer.begin(stream);
+    ctx->timer.begin(GS_STAGE_ATTRIBUTE, stream);
     hipError_t e = launch_attribute(ctx->s, ctx->ws, ctx->sorted_g, pixel_map, n_channels, out, stream);
     if (e != hipSuccess) return hip_fail(e, "attribution");
     ctx->timer.end(GS_STAGE_ATTRIBUTE, stream);
@@ -565,8 +567,13 @@ gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes
 }
 
 gs_status gs_profile_enable(gs_context* ctx, int32_t enable) {
+    return gs_profile_stages(ctx, enable != 0 ? (1u << GS_NUM_STAGES) - 1u : 0u);
+}
+
+gs_status gs_profile_stages(gs_context* ctx, uint32_t stage_mask) {
     if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
-    ctx->timer.on = enable != 0;
+    if (stage_mask >> GS_NUM_STAGES) return fail(GS_ERR_INVALID_ARGUMENT, "stage mask 0x%x names no stage", stage_mask);
+    ctx->timer.mask = stage_mask;
     return GS_OK;
 }
 

@@ -301,7 +301,13 @@ typedef enum {
     GS_STAGE_ATTRIBUTE = 12,         /* gs_attribute (traversal, gather, sum over views) */
     GS_NUM_STAGES = 13
 } gs_stage;
+/* gs_profile_enable: every stage (enable != 0) or none.  gs_profile_stages:
+ * only the stages whose bit (1 << stage) is set in stage_mask; each timed stage
+ * costs two event records on the stream (a few microseconds of idle GPU at its
+ * boundaries), so a caller timing the whole path selects the stages it needs.
+ * A bit at or above GS_NUM_STAGES is GS_ERR_INVALID_ARGUMENT. */
 GSR_API gs_status gs_profile_enable(gs_context* ctx, int32_t enable);
+GSR_API gs_status gs_profile_stages(gs_context* ctx, uint32_t stage_mask);
 GSR_API gs_status gs_profile_read(gs_context* ctx, double* ms, int64_t* calls, int32_t n_stages);
 
 #ifdef __cplusplus

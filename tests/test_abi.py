@@ -138,6 +138,12 @@ def test_calls_out_of_order_are_rejected_without_launching():
         calls = (ctypes.c_int64 * n)()
         assert lib.gs_profile_read(ctx, ms, calls, n) == b.GS_OK
         assert list(calls) == [0] * n
+        # a stage mask: any subset of the stages; a bit past the last stage is rejected
+        assert lib.gs_profile_stages(ctx, (1 << n) - 1) == b.GS_OK
+        assert lib.gs_profile_stages(ctx, 1 << 7) == b.GS_OK
+        assert lib.gs_profile_stages(ctx, 1 << n) == b.GS_ERR_INVALID_ARGUMENT
+        assert lib.gs_profile_stages(ctx, 0) == b.GS_OK
+        assert lib.gs_profile_stages(None, 1) == b.GS_ERR_INVALID_ARGUMENT
     finally:
         lib.gs_context_destroy(ctx)
 

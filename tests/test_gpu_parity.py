@@ -222,3 +222,32 @@ def test_exp2_bit_identical():
     want = oracle.exp2f(x)
     bad = np.nonzero(y.view(np.uint32) != want.view(np.uint32))[0]
     assert bad.size == 0, (bad.size, x[bad[:5]], y[bad[:5]], want[bad[:5]])
+
+
+def test_profile_stage_mask():
+    """Only the stages named in the mask record launches; with every stage timed, one
+    step records one launch of each of its nine stages."""
+    _need_gpu()
+    from gaussian_splatting_rasterizer_amd import binding
+    sc = scenes.tiny_scene(seed=3, n=40, n_views=2, W=40, H=24, sh_degree=1)
+    obs = torch.zeros((sc.n_views, sc.height, sc.width, 3), dtype=torch.float32, device="cuda")
+    r = binding.rasterizer_for_scene(sc)
+    try:
+        binding.gs_profile_stages(r.ctx, ["render", "finalize"])
+        r.step(obs)
+        torch.cuda.synchronize()
+        prof = binding.gs_profile_read(r.ctx)
+        assert {k for k, (ms, n) in prof.items() if n > 0} == {"render", "finalize"}
+        assert prof["render"][1] == 1 and prof["render"][0] > 0.0
+        binding.gs_profile_enable(r.ctx, True)
+        r.step(obs)
+        torch.cuda.synchronize()
+        prof = binding.gs_profile_read(r.ctx)
+        step_stages = ("project", "depth_sort", "scan", "emit", "tile_sort", "ranges", "render", "replay", "finalize")
+        assert all(prof[k][1] == 1 for k in step_stages), prof
+        binding.gs_profile_enable(r.ctx, False)
+        r.step(obs)
+        torch.cuda.synchronize()
+        assert all(n == 0 for ms, n in binding.gs_profile_read(r.ctx).values())
+    finally:
+        r.close()
