@@ -339,6 +339,13 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     tm.begin(GS_STAGE_DEPTH_SORT, stream);
     e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream);
     if (e != hipSuccess) return hip_fail(e, "slot scan");
+    // the pair count is this scan's total (the same tile counts as the depth-ordered scan below): copied into
+    // pinned host memory now and waited for only after the sort and the scan are queued, so that the GPU has
+    // work while the host waits
+    e = hipMemcpyAsync(ctx->host_count, ws.scan_total + 1, sizeof(uint64_t), hipMemcpyDeviceToHost, stream);
+    if (e != hipSuccess) return hip_fail(e, "pair count copy");
+    e = hipEventRecord(ctx->count_ev, stream);
+    if (e != hipSuccess) return hip_fail(e, "pair count event");
     // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
     //    scan rewrites next); the tile rectangles ride along (packed, or gathered by the last pass), and
     //    the last pass writes rectangles and tile counts in depth order but no keys
@@ -355,11 +362,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream);
     if (e != hipSuccess) return hip_fail(e, "scan");
     tm.end(GS_STAGE_SCAN, stream);
-    // the pair count: copied into pinned host memory, waited for by polling the event
-    e = hipMemcpyAsync(ctx->host_count, ws.scan_total, sizeof(uint64_t), hipMemcpyDeviceToHost, stream);
-    if (e != hipSuccess) return hip_fail(e, "pair count copy");
-    e = hipEventRecord(ctx->count_ev, stream);
-    if (e != hipSuccess) return hip_fail(e, "pair count event");
+    // wait for the pair count by polling its event
     for (;;) {
         e = hipEventQuery(ctx->count_ev);
         if (e == hipSuccess) break;

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
                                                         float* __restrict__ tokens) {
 #pragma clang fp contract(fast)
     constexpr int DT = 9 + 3 * D;
-    __shared__ float s_tok[kTokThreads * DT];
+    __shared__ __align__(16) float s_tok[kTokThreads * DT];
     const int64_t g0 = (int64_t)blockIdx.x * kTokThreads;
     const int64_t g = g0 + threadIdx.x;
     float* z = s_tok + threadIdx.x * DT;
@@ -502,9 +502,16 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
         z[8 + 3 * D] = (float)log(tr + eps);
     }
     __syncthreads();
-    const int64_t nvalid = (G - g0 < kTokThreads ? G - g0 : kTokThreads) * DT;
+    // the block's span starts g0 * DT floats (a multiple of 4) into the output: float4 stores when the
+    // caller's array is 16-byte aligned
+    static_assert((kTokThreads * DT) % 4 == 0, "whole float4 per block");
+    const int nvalid = (int)(G - g0 < kTokThreads ? G - g0 : kTokThreads) * DT;
     float* out = tokens + g0 * DT;
-    for (int64_t i = threadIdx.x; i < nvalid; i += kTokThreads) out[i] = s_tok[i];
+    const int n4 = (reinterpret_cast<uintptr_t>(tokens) & 15u) == 0u ? nvalid >> 2 : 0;
+    const float4* s4 = reinterpret_cast<const float4*>(s_tok);
+    float4* o4 = reinterpret_cast<float4*>(out);
+    for (int i = threadIdx.x; i < n4; i += kTokThreads) o4[i] = s4[i];
+    for (int i = 4 * n4 + threadIdx.x; i < nvalid; i += kTokThreads) out[i] = s_tok[i];
 }
 
 hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws, float eps,
