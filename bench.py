@@ -77,8 +77,8 @@ def stage_bytes(stage, c):
         return VG * 8
     if stage == "emit":          # per record: id, rect, tile count, offset in; per pair: tile key and Gaussian out
         return VG * (4 + 8 + 4 + 4) + P * 8
-    if stage == "tile_sort":     # histogram (keys), pass 1 key+value in and out, pass 2 key+value in, value out
-        return P * (4 + 16 + 12)
+    if stage == "tile_sort":     # pass 1 key+value in and out, pass 2 key+value in, value out (the digit counts
+        return P * (16 + 12)     # come from emit)
     if stage == "ranges":        # empty-tile fix-up (the ranges come from the last tile-sort pass)
         return V * c["T"] * 16
     return None

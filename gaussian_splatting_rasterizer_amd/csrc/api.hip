@@ -354,7 +354,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     const RectSort rs{ws.rect, ws.rect_sorted, ws.tt_sorted, packable ? ws.pay_a : nullptr,
                       packable ? ws.pay_b : nullptr};
     e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b, &rs, nullptr,
-                          sort_scratch, &ctx->epoch, stream, nullptr, &rid_sorted);
+                          false, sort_scratch, &ctx->epoch, stream, nullptr, &rid_sorted);
     if (e != hipSuccess) return hip_fail(e, "depth sort");
     tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
@@ -376,20 +376,21 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
         return fail(GS_ERR_WORKSPACE_TOO_SMALL, "%llu pairs exceed max_pairs %llu", (unsigned long long)total,
                     (unsigned long long)s.max_pairs);
     }
-    // 3. emit pairs in depth order, 4. stable sort by tile with the ranges, 5. empty ranges
+    // 3. emit pairs in depth order, counting the tile sort's digits on the way (the histogram rows and the
+    //    ranges are cleared first), 4. stable sort by tile with the ranges, 5. empty ranges
+    const int64_t tiles = (int64_t)s.V * s.T;
+    const RadixDigits td = radix_digits(bits_for((uint64_t)tiles));
     tm.begin(GS_STAGE_EMIT, stream);
-    e = launch_emit(s, ws, rid_sorted, stream);
+    e = launch_ranges_init(ws.ranges, tiles, ws.sort_part, stream);
+    if (e != hipSuccess) return hip_fail(e, "ranges init");
+    e = launch_emit(s, ws, rid_sorted, &td, stream);
     if (e != hipSuccess) return hip_fail(e, "emit");
     tm.end(GS_STAGE_EMIT, stream);
-    const int64_t tiles = (int64_t)s.V * s.T;
     uint32_t* sorted_g = nullptr;
     // the last pass of the tile sort records every tile's [start, end) (sorted keys are not kept)
     tm.begin(GS_STAGE_TILE_SORT, stream);
-    e = launch_ranges_init(ws.ranges, tiles, stream);
-    if (e != hipSuccess) return hip_fail(e, "ranges init");
-    e = launch_radix_sort(ws.pkey_emit, ws.pair_g, (int64_t)total, bits_for((uint64_t)tiles), ws.pkey_b, ws.pkey_c,
-                          ws.pval_a, ws.pval_b, nullptr, ws.ranges, sort_scratch, &ctx->epoch, stream, nullptr,
-                          &sorted_g);
+    e = launch_radix_sort(ws.pkey_emit, ws.pair_g, (int64_t)total, td.bits, ws.pkey_b, ws.pkey_c, ws.pval_a,
+                          ws.pval_b, nullptr, ws.ranges, true, sort_scratch, &ctx->epoch, stream, nullptr, &sorted_g);
     if (e != hipSuccess) return hip_fail(e, "tile sort");
     tm.end(GS_STAGE_TILE_SORT, stream);
     tm.begin(GS_STAGE_RANGES, stream);

@@ -45,6 +45,12 @@ constexpr int kMaxBins = 1 << kMaxDigitBits;
 constexpr int kMaxPasses = kSortMaxPasses;
 constexpr int kCtlTotals = kSortCtlTotals;
 
+RadixDigits radix_digits(int bits) {
+    if (bits < 1) bits = 1;
+    const int passes = (bits + kMaxDigitBits - 1) / kMaxDigitBits;
+    return RadixDigits{bits, passes, (bits + passes - 1) / passes};
+}
+
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t value) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = value;
@@ -505,11 +511,11 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
 
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const RectSort* rs, uint2* ranges, const SortScratch& sc, uint32_t* epoch,
-                             hipStream_t st, uint32_t** keys_out, uint32_t** vals_out) {
-    if (bits < 1) bits = 1;
-    const int passes = (bits + kMaxDigitBits - 1) / kMaxDigitBits;
-    const int dbits = (bits + passes - 1) / passes;
+                             const RectSort* rs, uint2* ranges, bool hist_ready, const SortScratch& sc,
+                             uint32_t* epoch, hipStream_t st, uint32_t** keys_out, uint32_t** vals_out) {
+    const RadixDigits rd = radix_digits(bits);
+    bits = rd.bits;
+    const int passes = rd.passes, dbits = rd.dbits;
     const int64_t nb = (n + kRadixTile - 1) / kRadixTile;
     uint32_t* kb[2] = {kbuf0, kbuf1};
     uint32_t* vb[2] = {vbuf0, vbuf1};
@@ -518,6 +524,8 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
     if (n <= 0) return hipSuccess;
     int64_t hb = (n + 8 * kHistThreads - 1) / (8 * kHistThreads);
     if (hb > kHistMaxBlocks) hb = kHistMaxBlocks;
+    if (hist_ready) hb = kHistMaxBlocks;  // the producer of the keys left their digit counts in every row
+    else
     switch (passes) {
         case 1: hipLaunchKernelGGL(k_digit_hist<1>, dim3((unsigned)hb), dim3(kHistThreads), 0, st, keys_in, n, dbits, bits, sc.part); break;
         case 2: hipLaunchKernelGGL(k_digit_hist<2>, dim3((unsigned)hb), dim3(kHistThreads), 0, st, keys_in, n, dbits, bits, sc.part); break;
@@ -577,29 +585,40 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
 // ---------------------------------------------------------------------------
 // pair emission and ranges
 // ---------------------------------------------------------------------------
-// One block per 256 consecutive records (depth order).  The block's pairs form
-// one contiguous span of the output; each thread takes every 256th pair of the
-// span, finds its record by binary search over the records' offsets in LDS, and
-// writes the pair's global tile id and Gaussian: coalesced stores whatever the
-// records' tile counts are.
+// One block per kEmitRecs consecutive records (depth order).  The block's pairs
+// form one contiguous span of the output; each thread takes every 256th pair of
+// the span, finds its record by binary search over the records' offsets in LDS,
+// and writes the pair's global tile id and Gaussian: coalesced stores whatever
+// the records' tile counts are.  With PASSES > 0 it also counts the digits of
+// the tile ids for the tile sort (LDS histogram, then atomics into the shared
+// rows, which k_ranges_init zeroed).
+constexpr int kEmitRecs = 1024;
+
+template <int PASSES>
 __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_sorted,
                                               const uint2* __restrict__ rect_sorted,
                                               const uint32_t* __restrict__ tt_sorted,
                                               const uint32_t* __restrict__ offsets, int64_t VG, uint32_t G, int T,
-                                              int TX, uint32_t* __restrict__ pkey, uint32_t* __restrict__ pair_g) {
-    __shared__ uint32_t s_off[256];
-    __shared__ uint32_t s_rid[256];
-    __shared__ uint2 s_rect[256];
+                                              int TX, uint32_t* __restrict__ pkey, uint32_t* __restrict__ pair_g,
+                                              RadixDigits rd, uint32_t* __restrict__ part) {
+    __shared__ uint32_t s_off[kEmitRecs];
+    __shared__ uint32_t s_rid[kEmitRecs];
+    __shared__ uint2 s_rect[kEmitRecs];
+    __shared__ uint32_t h[PASSES > 0 ? PASSES * kMaxBins : 1];
     __shared__ uint32_t s_end;
-    const int64_t k0 = (int64_t)blockIdx.x * 256;
-    const int64_t k = k0 + threadIdx.x;
-    const int last = (int)((VG - 1 - k0) < 255 ? (VG - 1 - k0) : 255);
-    if (k < VG) {
-        s_off[threadIdx.x] = offsets[k];
-        s_rid[threadIdx.x] = rid_sorted[k];
-        s_rect[threadIdx.x] = rect_sorted[k];
-        if (threadIdx.x == last) s_end = offsets[k] + tt_sorted[k];
+    const int64_t k0 = (int64_t)blockIdx.x * kEmitRecs;
+    const int last = (int)((VG - 1 - k0) < kEmitRecs - 1 ? (VG - 1 - k0) : kEmitRecs - 1);
+    for (int i = threadIdx.x; i < kEmitRecs; i += 256) {
+        const int64_t k = k0 + i;
+        if (k < VG) {
+            s_off[i] = offsets[k];
+            s_rid[i] = rid_sorted[k];
+            s_rect[i] = rect_sorted[k];
+            if (i == last) s_end = offsets[k] + tt_sorted[k];
+        }
     }
+    if (PASSES > 0)
+        for (int i = threadIdx.x; i < PASSES * kMaxBins; i += 256) h[i] = 0u;
     __syncthreads();
     const uint32_t pstart = s_off[0], pend = s_end;
     for (uint32_t p = pstart + threadIdx.x; p < pend; p += 256) {
@@ -615,21 +634,49 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
         const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
         const uint32_t wx = x1 - x0;
         const uint32_t v = rid / G;
-        pkey[p] = v * (uint32_t)T + (y0 + j / wx) * (uint32_t)TX + x0 + j % wx;
+        const uint32_t key = v * (uint32_t)T + (y0 + j / wx) * (uint32_t)TX + x0 + j % wx;
+        pkey[p] = key;
         pair_g[p] = rid - v * G;
+#pragma unroll
+        for (int q = 0; q < PASSES; ++q) {
+            const int shift = q * rd.dbits;
+            const int pb = shift + rd.dbits <= rd.bits ? rd.dbits : rd.bits - shift;
+            atomicAdd(&h[q * kMaxBins + ((key >> shift) & ((1u << pb) - 1u))], 1u);
+        }
+    }
+    if (PASSES > 0) {
+        __syncthreads();
+        uint32_t* row = part + (int64_t)(blockIdx.x % kHistMaxBlocks) * (kMaxPasses * kMaxBins);
+        for (int i = threadIdx.x; i < PASSES * kMaxBins; i += 256)
+            if (h[i]) atomicAdd(&row[i], h[i]);
     }
 }
 
-hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st) {
+hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, const RadixDigits* rd,
+                       hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_emit, dim3((unsigned)((s.VG + 255) / 256)), dim3(256), 0, st, rid_sorted, ws.rect_sorted,
-                       ws.tt_sorted, ws.offsets, s.VG, (uint32_t)s.G, s.T, s.TX, ws.pkey_emit, ws.pair_g);
+    const dim3 grid((unsigned)((s.VG + kEmitRecs - 1) / kEmitRecs)), block(256);
+    const RadixDigits d = rd ? *rd : RadixDigits{};
+#define GSR_EMIT(PP)                                                                                              \
+    hipLaunchKernelGGL(k_emit<PP>, grid, block, 0, st, rid_sorted, ws.rect_sorted, ws.tt_sorted, ws.offsets, s.VG, \
+                       (uint32_t)s.G, s.T, s.TX, ws.pkey_emit, ws.pair_g, d, ws.sort_part)
+    switch (rd ? rd->passes : 0) {
+        case 0: GSR_EMIT(0); break;
+        case 1: GSR_EMIT(1); break;
+        case 2: GSR_EMIT(2); break;
+        case 3: GSR_EMIT(3); break;
+        default: GSR_EMIT(4); break;
+    }
+#undef GSR_EMIT
     return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_ranges_init(uint2* __restrict__ ranges, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) ranges[i] = make_uint2(0xffffffffu, 0u);
+__global__ __launch_bounds__(256) void k_ranges_init(uint2* __restrict__ ranges, int64_t n, uint32_t* __restrict__ part,
+                                                     int64_t n_part) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        ranges[i] = make_uint2(0xffffffffu, 0u);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_part; i += stride) part[i] = 0u;
 }
 
 __global__ __launch_bounds__(256) void k_ranges_fix(uint2* __restrict__ ranges, int64_t n) {
@@ -637,8 +684,13 @@ __global__ __launch_bounds__(256) void k_ranges_fix(uint2* __restrict__ ranges, 
     if (i < n && ranges[i].x > ranges[i].y) ranges[i] = make_uint2(0u, 0u);  // no key: empty range
 }
 
-hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, hipStream_t st) {
-    if (n_tiles > 0) hipLaunchKernelGGL(k_ranges_init, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, st, ranges, n_tiles);
+hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hipStream_t st) {
+    const int64_t n_part = part ? (int64_t)kHistMaxBlocks * kMaxPasses * kMaxBins : 0;
+    const int64_t n = n_tiles > n_part ? n_tiles : n_part;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    if (n > 0)
+        hipLaunchKernelGGL(k_ranges_init, dim3((unsigned)blocks), dim3(256), 0, st, ranges, n_tiles, part, n_part);
     return hipGetLastError();
 }
 

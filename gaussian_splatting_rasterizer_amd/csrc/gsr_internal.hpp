@@ -114,6 +114,11 @@ struct RectCarry {
     uint32_t* tt_out;        // last pass: tile counts
     uint2* ranges;           // last pass of a key sort: per-key [start, end) (atomic min / max)
 };
+// Digit layout of the LSD radix sorts: `passes` passes of at most 8 bits, all `dbits` wide but the last.
+struct RadixDigits {
+    int bits, passes, dbits;
+};
+RadixDigits radix_digits(int bits);
 // Stable LSD radix sort of (keys, vals) on bits [0, bits), digits of up to 8
 // bits; vals_in == null means identity values (the input index).  Pass p writes
 // kbuf[p & 1] / vbuf[p & 1], so these must differ from each other and from
@@ -123,13 +128,19 @@ struct RectCarry {
 // final pass does not write keys.  Each pass takes a new epoch from *epoch.
 // With ranges (and no rs), the last pass also records every key's output range
 // [start, end) in ranges[key], which the caller initialises to {~0u, 0}.
+// With hist_ready, the keys' digit counts (layout radix_digits(bits)) are
+// already summed in the kSortPartBlocks rows of sc.part and are not recounted.
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const RectSort* rs, uint2* ranges, const SortScratch& sc, uint32_t* epoch,
-                             hipStream_t st, uint32_t** keys_out, uint32_t** vals_out);
-hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, hipStream_t st);
-// ranges before / after a sort that records them: {~0u, 0} everywhere, then empty ones to {0, 0}
-hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, hipStream_t st);
+                             const RectSort* rs, uint2* ranges, bool hist_ready, const SortScratch& sc,
+                             uint32_t* epoch, hipStream_t st, uint32_t** keys_out, uint32_t** vals_out);
+// (tile, Gaussian) pairs of the depth-ordered records into pkey_emit / pair_g; with rd, their tile ids'
+// digit counts (layout *rd) are added into the rows of sort_part, which must be zero beforehand.
+hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, const RadixDigits* rd,
+                       hipStream_t st);
+// ranges before / after a sort that records them: {~0u, 0} everywhere, then empty ones to {0, 0};
+// the init also zeroes the kSortPartBlocks histogram rows of part when given
+hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hipStream_t st);
 hipError_t launch_ranges_fix(uint2* ranges, int64_t n_tiles, hipStream_t st);
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
                          const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st);
