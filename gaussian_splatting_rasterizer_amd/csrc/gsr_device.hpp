@@ -148,36 +148,46 @@ __device__ __forceinline__ int eval_alpha(float4 r0, float qc, float opac, float
 // u = 2^-24 and Qabs <= cond(A) Q, and the float32 exponential and product
 // o * G add a few more units of u; so a pixel can pass only if
 // Q(d) <= t_eff = (t + 1e-5) / (1 - 8 u (cond + 1)).  The region Q <= t_eff has
-// half-widths sqrt(t_eff c' / det) and sqrt(t_eff a' / det); all of this is
-// computed in float64 from the exact float32 coefficients, once per record, and
-// the half-widths are widened by 0.01 px plus 1e-6 of (|centre| + half-width)
-// -- more than the rounding of the float32 centre +- half-width at use -- and
-// stored as two binary16 values rounded up (infinite when too large or when
-// 8 u (cond + 1) >= 1/2: never skip; -infinity when the entry can never pass,
-// o <= 1/255: the box is empty).
-__device__ __forceinline__ uint32_t half_bits_up(double v) {  // least binary16 >= v, for v > 0
-    if (!(v <= 65504.0)) return 0x7c00u;
-    const _Float16 h = (_Float16)(float)v;
+// half-widths sqrt(t_eff c' / det) and sqrt(t_eff a' / det), widened by 0.01 px
+// plus 1e-6 of (|centre| + half-width) -- more than the rounding of the float32
+// centre +- half-width at use -- and stored as two binary16 values rounded up
+// (infinite when too large or when 8 u (cond + 1) >= 1/2: never skip; -infinity
+// when the entry can never pass, o <= 1/255: the box is empty).
+//
+// All of it is evaluated in float32 from the exact float32 coefficients, every
+// operation rounded once (no contraction; IEEE division and square root), and
+// kept above the exact values: log2f is within 1 ulp (<= 1e-6 for |t| <= 8,
+// with the rounding of 255 o), so t gets 1.2e-5 instead of 1e-5; det = a'c' - b'^2
+// comes from Kahan's difference of products (fused multiply-adds; within 2u of
+// the exact value however much it cancels), so the radicand is within ~20u and
+// the half-width within ~11u, which the factor 1 + 2^-17 covers; the last sums
+// (4 roundings) get 1 + 2^-20.  Empty when log2(255 o) <= -1e-5 + 1e-6 < 0.
+__device__ __forceinline__ uint32_t half_bits_up(float v) {  // least binary16 >= v, for v > 0
+    if (!(v <= 65504.0f)) return 0x7c00u;
+    const _Float16 h = (_Float16)v;
     uint32_t b = (uint32_t)__builtin_bit_cast(uint16_t, h);
-    if ((double)(float)h < v) ++b;
+    if ((float)h < v) ++b;
     return b;
 }
 
 __device__ __forceinline__ uint32_t entry_box_pack(float4 r0, float qc, float opac) {
-    const double a = -(double)r0.z, b = -0.5 * (double)r0.w, c = -(double)qc;
-    const double det = a * c - b * b;
-    const double tt = log2(255.0 * (double)opac);
-    if (!(tt > -1e-5)) return 0xfc00fc00u;
-    if (!(det > 0.0) || !(a > 0.0) || !(c > 0.0)) return 0x7c007c00u;
-    const double t = (tt < 8.0 ? tt : 8.0) + 1e-5;
-    const double mid = 0.5 * (a + c), hd = sqrt(0.25 * (a - c) * (a - c) + b * b);
-    const double lmax = mid + hd, lmin = det / lmax;
-    const double grow = 8.0 * 5.9604644775390625e-8 * (lmax / lmin + 1.0);
-    if (!(grow < 0.5)) return 0x7c007c00u;
-    const double te = t / (1.0 - grow);
-    const double ex = sqrt(te * c / det), ey = sqrt(te * a / det);
-    const double wx = ex + 0.01 + 1e-6 * (fabs((double)r0.x) + ex);
-    const double wy = ey + 0.01 + 1e-6 * (fabs((double)r0.y) + ey);
+    const float a = -r0.z, b = -0.5f * r0.w, c = -qc;  // exact
+    const float tt = log2f(255.0f * opac);
+    if (!(tt > -1e-5f)) return 0xfc00fc00u;
+    const float w = b * b;
+    const float det = __builtin_fmaf(a, c, -w) + __builtin_fmaf(-b, b, w);
+    if (!(det > 0.0f) || !(a > 0.0f) || !(c > 0.0f)) return 0x7c007c00u;
+    const float t = (tt < 8.0f ? tt : 8.0f) + 1.2e-5f;
+    const float amc = a - c;
+    const float mid = 0.5f * (a + c), hd = __builtin_sqrtf(0.25f * (amc * amc) + b * b);
+    const float lmax = mid + hd, lmin = det / lmax;
+    const float grow = 0x1p-21f * (lmax / lmin + 1.0f);  // 8 u (cond + 1)
+    if (!(grow < 0.5f)) return 0x7c007c00u;
+    const float te = t / (1.0f - grow);
+    const float kw = 1.0f + 0x1p-17f, ks = 1.0f + 0x1p-20f;
+    const float ex = __builtin_sqrtf(te * c / det) * kw, ey = __builtin_sqrtf(te * a / det) * kw;
+    const float wx = ((ex + 0.01f) + 1e-6f * (__builtin_fabsf(r0.x) + ex)) * ks;
+    const float wy = ((ey + 0.01f) + 1e-6f * (__builtin_fabsf(r0.y) + ey)) * ks;
     return half_bits_up(wx) | (half_bits_up(wy) << 16);
 }
 

@@ -121,6 +121,54 @@ def test_records_bit_exact(name):
     assert np.array_equal(rect, r32[live][:, 15:19].astype(np.uint32))
 
 
+def _box_f64(a, b, c, opac, mx, my):
+    """Reference half-widths of the region where an entry can pass the alpha test:
+    Q(d) = a dx^2 + 2 b dx dy + c dy^2 <= t_eff with t_eff = (min(8, log2 255 o) + 1e-5) /
+    (1 - 8u (cond + 1)), u = 2^-24, widened by 0.01 px + 1e-6 (|centre| + half-width);
+    float64 from the float32 coefficients.  Returns (wx, wy, kind) with kind 0 finite,
+    1 unbounded (never skipped), -1 empty."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        tt = np.log2(255.0 * opac)
+        det = a * c - b * b
+        t = np.minimum(tt, 8.0) + 1e-5
+        mid, hd = 0.5 * (a + c), np.sqrt(0.25 * (a - c) ** 2 + b * b)
+        lmax = mid + hd
+        lmin = det / lmax
+        grow = 8.0 * 2.0 ** -24 * (lmax / lmin + 1.0)
+        te = t / (1.0 - grow)
+        ex, ey = np.sqrt(te * c / det), np.sqrt(te * a / det)
+    kind = np.where(~(tt > -1e-5), -1, np.where(~(det > 0) | ~(a > 0) | ~(c > 0) | ~(grow < 0.5), 1, 0))
+    wx = ex + 0.01 + 1e-6 * (np.abs(mx) + ex)
+    wy = ey + 0.01 + 1e-6 * (np.abs(my) + ey)
+    return wx, wy, kind
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_entry_boxes_conservative(name):
+    """Every live record's packed entry box (two binary16 half-widths, rounded up) holds
+    the float64 box computed from the record's own float32 coefficients: the render may
+    skip an entry only where it provably cannot pass the alpha test."""
+    sc, obs, ref, gpu = _case(name)
+    rec = gpu["rec"]
+    live = gpu["keys"] != 0xFFFFFFFF
+    r0, r1, r2 = rec[0, live].astype(np.float64), rec[1, live].astype(np.float64), rec[2, live]
+    a, b, c = -r0[:, 2], -0.5 * r0[:, 3], -r1[:, 0]
+    wx, wy, kind = _box_f64(a, b, c, r1[:, 1], r0[:, 0], r0[:, 1])
+    bits = r2[:, 1].view(np.uint32)
+    hx = (bits & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    hy = (bits >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+    fin = kind == 0
+    assert np.all(hx[fin] >= wx[fin]) and np.all(hy[fin] >= wy[fin]), \
+        (np.min(hx[fin] / wx[fin]), np.min(hy[fin] / wy[fin]))
+    assert np.all(np.isinf(hx[kind == 1]) & (hx[kind == 1] > 0)) and np.all(np.isinf(hy[kind == 1]))
+    # an empty box only where the opacity alone keeps alpha below 1/255
+    empty = np.isinf(hx) & (hx < 0)
+    assert np.all(r1[empty, 1] * 255.0 < 1.0)
+    print(f"{name}: {fin.sum()} finite boxes, min ratio to the float64 box "
+          f"{min(np.min(hx[fin] / wx[fin]), np.min(hy[fin] / wy[fin])) if fin.any() else float('nan'):.6f}, "
+          f"{(kind == 1).sum()} unbounded, {empty.sum()} empty")
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_tile_lists_bit_exact(name):
     sc, obs, ref, gpu = _case(name)
