@@ -120,6 +120,7 @@ struct gs_context {
     uint32_t epoch;               // last radix pass epoch; 0 = look-back words not cleared yet
     uint64_t* host_count;         // pinned host word receiving the pair count (allocated on first use)
     hipEvent_t count_ev;
+    bool packed_fresh;            // gs_project left the packed rectangles that the next depth sort reads
 };
 
 namespace gsr {
@@ -301,9 +302,13 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
     ctx->params = *params;
     ctx->state = kCreated;
     ctx->timer.begin(GS_STAGE_PROJECT, stream);
+    // tile grids of at most 256 x 256: the depth sort's first pass reads the rectangles packed by preprocess
+    // (into the depth-ordered tile counts' array, which the sort's last pass writes only afterwards)
+    const bool packable = s.TX <= 256 && s.TY <= 256;
     hipError_t e = launch_project(*sc, ctx->cams, s, params->near_plane, params->far_plane, params->antialiased,
-                                  ctx->ws, stream);
+                                  packable ? ctx->ws.tt_sorted : nullptr, ctx->ws, stream);
     if (e != hipSuccess) return hip_fail(e, "project");
+    ctx->packed_fresh = packable;
     ctx->timer.end(GS_STAGE_PROJECT, stream);
     ctx->state = kProjected;
     return GS_OK;
@@ -351,8 +356,10 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     //    the last pass writes rectangles and tile counts in depth order but no keys
     uint32_t* rid_sorted = nullptr;
     const bool packable = s.TX <= 256 && s.TY <= 256;
+    // (a second sort after one gs_project packs on load: the first sort's last pass overwrote the packed form)
     const RectSort rs{ws.rect, ws.rect_sorted, ws.tt_sorted, packable ? ws.pay_a : nullptr,
-                      packable ? ws.pay_b : nullptr};
+                      packable ? ws.pay_b : nullptr, packable && ctx->packed_fresh ? ws.tt_sorted : nullptr};
+    ctx->packed_fresh = false;
     e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b, &rs, nullptr,
                           false, sort_scratch, &ctx->epoch, stream, nullptr, &rid_sorted);
     if (e != hipSuccess) return hip_fail(e, "depth sort");

@@ -278,21 +278,6 @@ __global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restric
     if (blockIdx.x == 0 && threadIdx.x < kMaxPasses) ctl[threadIdx.x] = 0u;
 }
 
-// A tile rectangle in 32 bits, for tile grids of at most 256 x 256: x0, y0,
-// width - 1, height - 1 in bytes; 0xffffffff marks an empty rectangle (culled
-// record), which no real rectangle can encode (x0 + width <= 256).
-__device__ __forceinline__ uint32_t pack_rect(uint2 r) {
-    if (r.y == 0u) return 0xffffffffu;
-    const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu, y1 = r.y >> 16;
-    return x0 | (y0 << 8) | ((x1 - x0 - 1u) << 16) | ((y1 - y0 - 1u) << 24);
-}
-
-__device__ __forceinline__ uint2 unpack_rect(uint32_t q) {
-    if (q == 0xffffffffu) return make_uint2(0u, 0u);
-    const uint32_t x0 = q & 0xffu, y0 = (q >> 8) & 0xffu, x1 = x0 + ((q >> 16) & 0xffu) + 1u,
-                   y1 = y0 + (q >> 24) + 1u;
-    return make_uint2(x0 | (y0 << 16), x1 | (y1 << 16));
-}
 
 // One radix pass (see the file header).  Blocks take their tile of keys in
 // the order they start (a ticket counter), publish their per-digit counts and
@@ -545,17 +530,21 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
         const uint32_t ep = next_epoch(epoch);
         RectCarry rc{};
         if (rs && rs->pay_a) {  // carried: pack in pass 0, ping-pong, unpack in the last pass
-            if (p == 0) rc.pack_src = rs->rect;
-            else rc.pay_in = p & 1 ? rs->pay_a : rs->pay_b;
+            if (p == 0) {  // packed by the producer of the records, or packed here on load
+                if (rs->pay_init) rc.pay_in = rs->pay_init;
+                else rc.pack_src = rs->rect;
+            } else {
+                rc.pay_in = p & 1 ? rs->pay_a : rs->pay_b;
+            }
             if (last) {
                 rc.rect_out = rs->rect_out;
                 rc.tt_out = rs->tt_out;
             } else {
                 rc.pay_out = p & 1 ? rs->pay_b : rs->pay_a;
             }
-            if (passes == 1) {  // a single pass packs and unpacks
-                rc.pack_src = rs->rect;
-                rc.pay_in = nullptr;
+            if (passes == 1) {  // a single pass packs (or reads the packed form) and unpacks
+                rc.pack_src = rs->pay_init ? nullptr : rs->rect;
+                rc.pay_in = rs->pay_init;
             }
         } else if (rs && last) {
             rc.gather_src = rs->rect;

@@ -138,6 +138,22 @@ __device__ __forceinline__ int eval_alpha(float4 r0, float qc, float opac, float
     return alpha >= kAlphaMin ? 2 : 1;
 }
 
+// A tile rectangle in 32 bits, for tile grids of at most 256 x 256: x0, y0,
+// width - 1, height - 1 in bytes; 0xffffffff marks an empty rectangle (culled
+// record), which no real rectangle can encode (x0 + width <= 256).
+__device__ __forceinline__ uint32_t pack_rect(uint2 r) {
+    if (r.y == 0u) return 0xffffffffu;
+    const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu, y1 = r.y >> 16;
+    return x0 | (y0 << 8) | ((x1 - x0 - 1u) << 16) | ((y1 - y0 - 1u) << 24);
+}
+
+__device__ __forceinline__ uint2 unpack_rect(uint32_t q) {
+    if (q == 0xffffffffu) return make_uint2(0u, 0u);
+    const uint32_t x0 = q & 0xffu, y0 = (q >> 8) & 0xffu, x1 = x0 + ((q >> 16) & 0xffu) + 1u,
+                   y1 = y0 + (q >> 24) + 1u;
+    return make_uint2(x0 | (y0 << 16), x1 | (y1 << 16));
+}
+
 // Conservative pixel bounding box of the region where an entry can pass the
 // alpha test, used only to skip entries that cannot pass anywhere in a block
 // of pixels.  With Q(d) = a' dx^2 + 2 b' dx dy + c' dy^2 (a' = -qa, b' = -qb/2,

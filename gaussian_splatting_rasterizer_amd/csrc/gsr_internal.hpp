@@ -87,8 +87,9 @@ Sizes make_sizes(const gs_dims& d);
 
 // ---- launchers (return hipGetLastError of the launch) ----------------------
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t st);
+// pay_init (optional): also the packed rectangles (pack_rect) per record, for the depth sort's first pass
 hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, float near_plane,
-                          float far_plane, int antialiased, Workspace& ws, hipStream_t st);
+                          float far_plane, int antialiased, uint32_t* pay_init, Workspace& ws, hipStream_t st);
 // exclusive scan of in (u32) into out (may alias); total -> *total (device u64)
 hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
                            hipStream_t st);
@@ -103,6 +104,7 @@ struct RectSort {
     uint32_t* tt_out;
     uint32_t* pay_a;
     uint32_t* pay_b;
+    const uint32_t* pay_init;  // optional: the rectangles already packed, in input order (read by pass 0)
 };
 // Per-launch form of the same (device side).
 struct RectCarry {

@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
                                                   float4* __restrict__ rec0, float4* __restrict__ rec1,
                                                   float2* __restrict__ rec2, uint2* __restrict__ rect,
                                                   uint32_t* __restrict__ depth_key,
-                                                  uint32_t* __restrict__ tiles_touched) {
+                                                  uint32_t* __restrict__ tiles_touched,
+                                                  uint32_t* __restrict__ pay_init) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= G) return;
 
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
             rect[rid] = make_uint2(0u, 0u);
             depth_key[rid] = 0xffffffffu;
             tiles_touched[rid] = 0u;
+            if (pay_init) pay_init[rid] = pack_rect(make_uint2(0u, 0u));
             continue;
         }
 
@@ -176,21 +178,23 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         rec0[rid] = r0v;
         rec1[rid] = make_float4(qcv, opx, pre[0], pre[1]);
         rec2[rid] = make_float2(pre[2], __uint_as_float(entry_box_pack(r0v, qcv, opx)));
-        rect[rid] = make_uint2((uint32_t)x0 | ((uint32_t)y0 << 16), (uint32_t)x1 | ((uint32_t)y1 << 16));
+        const uint2 rc = make_uint2((uint32_t)x0 | ((uint32_t)y0 << 16), (uint32_t)x1 | ((uint32_t)y1 << 16));
+        rect[rid] = rc;
         depth_key[rid] = __float_as_uint(tz);
         tiles_touched[rid] = (uint32_t)((x1 - x0) * (y1 - y0));
+        if (pay_init) pay_init[rid] = pack_rect(rc);
     }
 }
 
 hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, float near_plane,
-                          float far_plane, int antialiased, Workspace& ws, hipStream_t st) {
+                          float far_plane, int antialiased, uint32_t* pay_init, Workspace& ws, hipStream_t st) {
     if (s.G == 0) return hipSuccess;
     const dim3 block(256), grid((unsigned)((s.G + 255) / 256));
 #define GSR_LAUNCH_PROJECT(DD, AAA)                                                                        \
     hipLaunchKernelGGL(HIP_KERNEL_NAME(k_project<DD, AAA>), grid, block, 0, st, sc.means, sc.quats, sc.scales,   \
                        sc.opacities,                                                                      \
                        sc.sh, s.G, s.V, cams, s.W, s.H, s.TX, s.TY, near_plane, far_plane, ws.rec0, ws.rec1, \
-                       ws.rec2, ws.rect, ws.depth_key, ws.tiles_touched)
+                       ws.rec2, ws.rect, ws.depth_key, ws.tiles_touched, pay_init)
 #define GSR_LAUNCH_PROJECT_D(DD)                 \
     if (antialiased) GSR_LAUNCH_PROJECT(DD, true); \
     else GSR_LAUNCH_PROJECT(DD, false)

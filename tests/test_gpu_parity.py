@@ -299,3 +299,24 @@ def test_profile_stage_mask():
         assert all(n == 0 for ms, n in binding.gs_profile_read(r.ctx).values())
     finally:
         r.close()
+
+
+def test_second_bin_sort_after_one_project():
+    """gs_bin_sort may run again on the same preprocess: the second sort (which cannot
+    reuse the packed rectangles the first consumed) gives identical lists and ranges."""
+    _need_gpu()
+    b = _binding()
+    sc = scenes.c2_resplat_step(n_views=2, W=112, H=64)
+    r = b.rasterizer_for_scene(sc)
+    try:
+        r.project_and_bin()
+        ids1 = r.export(b.GS_EXPORT_SORTED_IDS).cpu().numpy()[: r.n_pairs].copy()
+        rg1 = r.export(b.GS_EXPORT_RANGES).cpu().numpy().copy()
+        st, n = b.gs_bin_sort(r.ctx, None, raise_on_overflow=False)
+        assert st == b.GS_OK and n == r.n_pairs
+        ids2 = r.export(b.GS_EXPORT_SORTED_IDS).cpu().numpy()[: r.n_pairs]
+        rg2 = r.export(b.GS_EXPORT_RANGES).cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.array_equal(ids1, ids2) and np.array_equal(rg1, rg2)
+    finally:
+        r.close()
