@@ -111,27 +111,17 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __
     if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
 }
 
-__global__ __launch_bounds__(1024) void k_scan_top(uint64_t* __restrict__ bsum, int64_t nb,
-                                                   uint64_t* __restrict__ total) {
-    __shared__ uint64_t lds[16];
-    uint64_t carry = 0;
-    for (int64_t c = 0; c < nb; c += 1024) {
-        const int64_t k = c + threadIdx.x;
-        const uint64_t x = k < nb ? bsum[k] : 0;
-        uint64_t tot;
-        const uint64_t ex = block_exclusive_scan<uint64_t, 1024>(x, &tot, lds);
-        if (k < nb) bsum[k] = carry + ex;
-        carry += tot;
-    }
-    if (threadIdx.x == 0) *total = carry;
-}
-
-// `in` and `out` may alias (each block reads its whole slice before writing it)
+// `in` and `out` may alias (each block reads its whole slice before writing it).
+// Each block sums the totals of the blocks before it (at most a few thousand
+// words, L2-resident) instead of waiting for a separate scan of them; the last
+// block writes the grand total.
 __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, int64_t n,
-                                                            const uint64_t* __restrict__ boff, uint32_t* out) {
+                                                            const uint64_t* __restrict__ bsum, int64_t nb,
+                                                            uint32_t* out, uint64_t* __restrict__ total) {
     // padded so that thread t's 16 consecutive items (t*17 + i) are bank-conflict free
     __shared__ uint32_t s[kScanTile + kScanTile / 16];
     __shared__ uint32_t lds[kScanThreads / 64];
+    __shared__ uint64_t lds64[kScanThreads / 64];
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
@@ -139,13 +129,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
         const int64_t k = base + e;
         s[e + e / 16] = k < n ? in[k] : 0u;
     }
+    uint64_t before = 0;
+    for (int64_t j = threadIdx.x; j < (int64_t)blockIdx.x; j += kScanThreads) before += bsum[j];
+    uint64_t boff;
+    (void)block_exclusive_scan<uint64_t, kScanThreads>(before, &boff, lds64);
+    if (threadIdx.x == 0 && (int64_t)blockIdx.x == nb - 1) *total = boff + bsum[blockIdx.x];
     __syncthreads();
     const int t = threadIdx.x;
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) local += s[t * 17 + i];
     uint32_t tot;
-    uint32_t run = (uint32_t)boff[blockIdx.x] + block_exclusive_scan<uint32_t, kScanThreads>(local, &tot, lds);
+    uint32_t run = (uint32_t)boff + block_exclusive_scan<uint32_t, kScanThreads>(local, &tot, lds);
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const uint32_t v = s[t * 17 + i];
@@ -161,12 +156,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
     }
 }
 
+__global__ void k_zero_u64(uint64_t* __restrict__ p) { *p = 0ull; }
+
 hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
                            hipStream_t st) {
     const int64_t nb = (n + kScanTile - 1) / kScanTile;
-    if (nb > 0) hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch);
-    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(1024), 0, st, block_scratch, nb, total);
-    if (nb > 0) hipLaunchKernelGGL(k_scan_down, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch, out);
+    if (nb == 0) {
+        hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, st, total);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch);
+    hipLaunchKernelGGL(k_scan_down, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch, nb, out,
+                       total);
     return hipGetLastError();
 }
 
@@ -225,19 +226,22 @@ __global__ __launch_bounds__(kHistThreads) void k_digit_hist(const uint32_t* __r
     const int64_t n4 = n >> 2;
     const uint4* k4 = reinterpret_cast<const uint4*>(keys);
     const int64_t stride = (int64_t)gridDim.x * kHistThreads;
-    for (int64_t q = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; q < n4; q += 2 * stride) {
-        const bool second = q + stride < n4;
-        const uint4 x = k4[q];
-        const uint4 y = second ? k4[q + stride] : make_uint4(0u, 0u, 0u, 0u);
-        hist_count<PASSES>(x.x, dbits, bits, cur, run, h);
-        hist_count<PASSES>(x.y, dbits, bits, cur, run, h);
-        hist_count<PASSES>(x.z, dbits, bits, cur, run, h);
-        hist_count<PASSES>(x.w, dbits, bits, cur, run, h);
-        if (second) {
-            hist_count<PASSES>(y.x, dbits, bits, cur, run, h);
-            hist_count<PASSES>(y.y, dbits, bits, cur, run, h);
-            hist_count<PASSES>(y.z, dbits, bits, cur, run, h);
-            hist_count<PASSES>(y.w, dbits, bits, cur, run, h);
+    // eight 4-key vectors per thread and round, all loads in flight before the counting
+    constexpr int kU = 8;
+    for (int64_t q0 = (int64_t)blockIdx.x * kHistThreads + threadIdx.x; q0 < n4; q0 += kU * stride) {
+        uint4 x[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t q = q0 + u * stride;
+            x[u] = q < n4 ? k4[q] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            if (q0 + u * stride >= n4) break;
+            hist_count<PASSES>(x[u].x, dbits, bits, cur, run, h);
+            hist_count<PASSES>(x[u].y, dbits, bits, cur, run, h);
+            hist_count<PASSES>(x[u].z, dbits, bits, cur, run, h);
+            hist_count<PASSES>(x[u].w, dbits, bits, cur, run, h);
         }
     }
     if (blockIdx.x == 0 && threadIdx.x < (n & 3)) hist_count<PASSES>(keys[4 * n4 + threadIdx.x], dbits, bits, cur, run, h);
