@@ -361,7 +361,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
                       packable ? ws.pay_b : nullptr, packable && ctx->packed_fresh ? ws.tt_sorted : nullptr};
     ctx->packed_fresh = false;
     e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b, &rs, nullptr,
-                          false, sort_scratch, &ctx->epoch, stream, nullptr, &rid_sorted);
+                          false, 0, sort_scratch, &ctx->epoch, stream, nullptr, &rid_sorted);
     if (e != hipSuccess) return hip_fail(e, "depth sort");
     tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
@@ -387,17 +387,21 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     //    ranges are cleared first), 4. stable sort by tile with the ranges, 5. empty ranges
     const int64_t tiles = (int64_t)s.V * s.T;
     const RadixDigits td = radix_digits(bits_for((uint64_t)tiles));
+    // when a tile id and a Gaussian index fit one 32-bit word together, the pairs are sorted as such words
+    const int gbits = bits_for((uint64_t)s.G) > 0 ? bits_for((uint64_t)s.G) : 1;
+    const int packed_gbits = td.bits + gbits <= 32 ? gbits : 0;
     tm.begin(GS_STAGE_EMIT, stream);
     e = launch_ranges_init(ws.ranges, tiles, ws.sort_part, stream);
     if (e != hipSuccess) return hip_fail(e, "ranges init");
-    e = launch_emit(s, ws, rid_sorted, &td, stream);
+    e = launch_emit(s, ws, rid_sorted, &td, packed_gbits, stream);
     if (e != hipSuccess) return hip_fail(e, "emit");
     tm.end(GS_STAGE_EMIT, stream);
     uint32_t* sorted_g = nullptr;
     // the last pass of the tile sort records every tile's [start, end) (sorted keys are not kept)
     tm.begin(GS_STAGE_TILE_SORT, stream);
-    e = launch_radix_sort(ws.pkey_emit, ws.pair_g, (int64_t)total, td.bits, ws.pkey_b, ws.pkey_c, ws.pval_a,
-                          ws.pval_b, nullptr, ws.ranges, true, sort_scratch, &ctx->epoch, stream, nullptr, &sorted_g);
+    e = launch_radix_sort(ws.pkey_emit, packed_gbits > 0 ? nullptr : ws.pair_g, (int64_t)total, td.bits, ws.pkey_b,
+                          ws.pkey_c, ws.pval_a, ws.pval_b, nullptr, ws.ranges, true, packed_gbits, sort_scratch,
+                          &ctx->epoch, stream, nullptr, &sorted_g);
     if (e != hipSuccess) return hip_fail(e, "tile sort");
     tm.end(GS_STAGE_TILE_SORT, stream);
     tm.begin(GS_STAGE_RANGES, stream);

@@ -297,7 +297,9 @@ __global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restric
 // second round after the keys, and unpacked with their tile counts in the last
 // pass; or, when the tile grid is too large to pack, gathered by record in the
 // last pass.  keys_out may be null.
-enum RadixMode { kPlain = 0, kCarryRect = 1, kGatherRect = 2, kRanges = 3 };
+// kPackedMid / kPackedLast: 32-bit words (sort key above bit rc.key_shift, the value below) sorted with no
+// separate value array; the last pass writes the value bits and records every key's range.
+enum RadixMode { kPlain = 0, kCarryRect = 1, kGatherRect = 2, kRanges = 3, kPackedMid = 4, kPackedLast = 5 };
 
 template <int MODE>
 __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
@@ -308,7 +310,8 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     __shared__ uint32_t gdelta[kMaxBins];            // global position - block-local position, per digit
     __shared__ uint64_t scan_lds[kRadixThreads / 64];
     __shared__ uint32_t skey[kRadixTile];
-    __shared__ uint32_t sval[kRadixTile];
+    constexpr bool kPacked = MODE == kPackedMid || MODE == kPackedLast;
+    __shared__ uint32_t sval[kPacked ? 1 : kRadixTile];
     __shared__ uint32_t s_tile;
     const int nbins = 1 << bits;
     const uint32_t mask = (uint32_t)nbins - 1u;
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         const int e = wbase + i * 64;
         const bool valid = e < nblk;
         key[i] = valid ? keys_in[bbase + e] : 0u;
-        val[i] = valid ? (vals_in ? vals_in[bbase + e] : (uint32_t)(bbase + e)) : 0u;
+        val[i] = (valid && !kPacked) ? (vals_in ? vals_in[bbase + e] : (uint32_t)(bbase + e)) : 0u;
     }
 #pragma unroll
     for (int i = 0; i < kRadixItems; ++i) {
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         if (wbase + i * 64 >= nblk) continue;
         const uint32_t lp = cnt[wave][(key[i] >> shift) & mask] + rank[i];
         skey[lp] = key[i];
-        sval[lp] = val[i];
+        if (!kPacked) sval[lp] = val[i];
         lpk[i >> 1] |= lp << (16 * (i & 1));
     }
     // decoupled look-back over the earlier tiles' published counts
@@ -469,7 +472,17 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         const bool ok = lp < nblk;
         const uint32_t k = ok ? skey[lp] : 0u;
         pos[i] = gdelta[(k >> shift) & mask] + (uint32_t)lp;
-        if (ok) {
+        if (ok && kPacked) {
+            if (MODE == kPackedMid) {
+                keys_out[pos[i]] = k;
+            } else {
+                vals_out[pos[i]] = k & rc.low_mask;
+                const uint32_t key_k = k >> rc.key_shift;
+                if (lp == 0 || (skey[lp - 1] >> rc.key_shift) != key_k) atomicMin(&rc.ranges[key_k].x, pos[i]);
+                if (lp == nblk - 1 || (skey[lp + 1] >> rc.key_shift) != key_k)
+                    atomicMax(&rc.ranges[key_k].y, pos[i] + 1u);
+            }
+        } else if (ok) {
             if (keys_out) keys_out[pos[i]] = k;
             vals_out[pos[i]] = sval[lp];
             if (MODE == kRanges) {
@@ -500,12 +513,16 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
 
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const RectSort* rs, uint2* ranges, bool hist_ready, const SortScratch& sc,
-                             uint32_t* epoch, hipStream_t st, uint32_t** keys_out, uint32_t** vals_out) {
+                             const RectSort* rs, uint2* ranges, bool hist_ready, int key_shift,
+                             const SortScratch& sc, uint32_t* epoch, hipStream_t st, uint32_t** keys_out,
+                             uint32_t** vals_out) {
     const RadixDigits rd = radix_digits(bits);
     bits = rd.bits;
     const int passes = rd.passes, dbits = rd.dbits;
     const int64_t nb = (n + kRadixTile - 1) / kRadixTile;
+    // packed words: key bits [key_shift, key_shift + bits), counted beforehand, no value array, no rectangles
+    const bool packed = key_shift > 0;
+    if (packed && (!hist_ready || vals_in || rs || !ranges || key_shift + bits > 32)) return hipErrorInvalidValue;
     uint32_t* kb[2] = {kbuf0, kbuf1};
     uint32_t* vb[2] = {vbuf0, vbuf1};
     if (keys_out) *keys_out = kb[(passes - 1) & 1];
@@ -526,8 +543,8 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
     const uint32_t* ksrc = keys_in;
     const uint32_t* vsrc = vals_in;
     for (int p = 0; p < passes; ++p) {
-        const int shift = p * dbits;
-        const int pb = (shift + dbits <= bits) ? dbits : bits - shift;
+        const int shift = p * dbits + key_shift;
+        const int pb = (p * dbits + dbits <= bits) ? dbits : bits - p * dbits;
         const bool last = p == passes - 1;
         uint32_t* kdst = (last && !keys_out) ? nullptr : kb[p & 1];
         uint32_t* vdst = vb[p & 1];
@@ -557,7 +574,10 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
         } else if (!rs && last) {
             rc.ranges = ranges;
         }
-        const int mode = (rc.pack_src || rc.pay_in) ? kCarryRect
+        rc.key_shift = key_shift;
+        rc.low_mask = packed ? (1u << key_shift) - 1u : ~0u;
+        const int mode = packed                     ? (last ? kPackedLast : kPackedMid)
+                         : (rc.pack_src || rc.pay_in) ? kCarryRect
                          : rc.gather_src            ? kGatherRect
                          : rc.ranges                ? kRanges
                                                     : kPlain;
@@ -567,6 +587,8 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
         if (mode == kCarryRect) GSR_ONESWEEP(kCarryRect);
         else if (mode == kGatherRect) GSR_ONESWEEP(kGatherRect);
         else if (mode == kRanges) GSR_ONESWEEP(kRanges);
+        else if (mode == kPackedMid) GSR_ONESWEEP(kPackedMid);
+        else if (mode == kPackedLast) GSR_ONESWEEP(kPackedLast);
         else GSR_ONESWEEP(kPlain);
 #undef GSR_ONESWEEP
         ksrc = kdst;
@@ -593,7 +615,7 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
                                               const uint32_t* __restrict__ tt_sorted,
                                               const uint32_t* __restrict__ offsets, int64_t VG, uint32_t G, int T,
                                               int TX, uint32_t* __restrict__ pkey, uint32_t* __restrict__ pair_g,
-                                              RadixDigits rd, uint32_t* __restrict__ part) {
+                                              RadixDigits rd, int packed_gbits, uint32_t* __restrict__ part) {
     __shared__ uint32_t s_off[kEmitRecs];
     __shared__ uint32_t s_rid[kEmitRecs];
     __shared__ uint2 s_rect[kEmitRecs];
@@ -628,8 +650,12 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
         const uint32_t wx = x1 - x0;
         const uint32_t v = rid / G;
         const uint32_t key = v * (uint32_t)T + (y0 + j / wx) * (uint32_t)TX + x0 + j % wx;
-        pkey[p] = key;
-        pair_g[p] = rid - v * G;
+        if (packed_gbits > 0) {
+            pkey[p] = (key << packed_gbits) | (rid - v * G);
+        } else {
+            pkey[p] = key;
+            pair_g[p] = rid - v * G;
+        }
 #pragma unroll
         for (int q = 0; q < PASSES; ++q) {
             const int shift = q * rd.dbits;
@@ -646,13 +672,13 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
 }
 
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, const RadixDigits* rd,
-                       hipStream_t st) {
+                       int packed_gbits, hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
     const dim3 grid((unsigned)((s.VG + kEmitRecs - 1) / kEmitRecs)), block(256);
     const RadixDigits d = rd ? *rd : RadixDigits{};
 #define GSR_EMIT(PP)                                                                                              \
     hipLaunchKernelGGL(k_emit<PP>, grid, block, 0, st, rid_sorted, ws.rect_sorted, ws.tt_sorted, ws.offsets, s.VG, \
-                       (uint32_t)s.G, s.T, s.TX, ws.pkey_emit, ws.pair_g, d, ws.sort_part)
+                       (uint32_t)s.G, s.T, s.TX, ws.pkey_emit, ws.pair_g, d, packed_gbits, ws.sort_part)
     switch (rd ? rd->passes : 0) {
         case 0: GSR_EMIT(0); break;
         case 1: GSR_EMIT(1); break;

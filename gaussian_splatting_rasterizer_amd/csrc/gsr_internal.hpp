@@ -115,6 +115,8 @@ struct RectCarry {
     uint2* rect_out;         // last pass: unpacked rectangles
     uint32_t* tt_out;        // last pass: tile counts
     uint2* ranges;           // last pass of a key sort: per-key [start, end) (atomic min / max)
+    int key_shift;           // packed words: the key's lowest bit (the value lies below it)
+    uint32_t low_mask;       // packed words: (1 << key_shift) - 1
 };
 // Digit layout of the LSD radix sorts: `passes` passes of at most 8 bits, all `dbits` wide but the last.
 struct RadixDigits {
@@ -132,14 +134,20 @@ RadixDigits radix_digits(int bits);
 // [start, end) in ranges[key], which the caller initialises to {~0u, 0}.
 // With hist_ready, the keys' digit counts (layout radix_digits(bits)) are
 // already summed in the kSortPartBlocks rows of sc.part and are not recounted.
+// With key_shift > 0 the keys are packed words, key in bits [key_shift,
+// key_shift + bits) and a value below: no vals_in, no rs, hist_ready and ranges
+// required; the final pass writes each word's value bits to *vals_out (and no
+// keys) and records the ranges of the keys.
 hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int bits,
                              uint32_t* kbuf0, uint32_t* kbuf1, uint32_t* vbuf0, uint32_t* vbuf1,
-                             const RectSort* rs, uint2* ranges, bool hist_ready, const SortScratch& sc,
-                             uint32_t* epoch, hipStream_t st, uint32_t** keys_out, uint32_t** vals_out);
-// (tile, Gaussian) pairs of the depth-ordered records into pkey_emit / pair_g; with rd, their tile ids'
-// digit counts (layout *rd) are added into the rows of sort_part, which must be zero beforehand.
+                             const RectSort* rs, uint2* ranges, bool hist_ready, int key_shift,
+                             const SortScratch& sc, uint32_t* epoch, hipStream_t st, uint32_t** keys_out,
+                             uint32_t** vals_out);
+// (tile, Gaussian) pairs of the depth-ordered records into pkey_emit / pair_g, or, with packed_gbits > 0,
+// into pkey_emit alone as (tile << packed_gbits) | Gaussian; with rd, their tile ids' digit counts
+// (layout *rd) are added into the rows of sort_part, which must be zero beforehand.
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, const RadixDigits* rd,
-                       hipStream_t st);
+                       int packed_gbits, hipStream_t st);
 // ranges before / after a sort that records them: {~0u, 0} everywhere, then empty ones to {0, 0};
 // the init also zeroes the kSortPartBlocks histogram rows of part when given
 hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hipStream_t st);
