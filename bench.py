@@ -69,16 +69,17 @@ def stage_bytes(stage, c):
     read or write once, at its element size (the per-record and per-pair terms
     are listed in the design doc)."""
     G, V, d, P, VG = c["G"], c["V"], c["d"], c["P"], c["G"] * c["V"]
+    pk = 4 if c["packable"] else 0   # the rectangle packed to 32 bits by preprocess for the depth sort
     if stage == "project":       # Gaussian parameters in; 40-byte record, rectangle, depth key, tile count out
-        return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (40 + 8 + 4 + 4)
-    if stage == "depth_sort":    # slot scan 8, histogram 4, pass 0 (key+rect in, key+id+rect out) 24,
-        return VG * (8 + 4 + 24 + 2 * 24 + 28)   # passes 1-2 24 each, pass 3 (-> id, rect, tile count) 28
+        return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (40 + 8 + 4 + 4 + pk)
+    if stage == "depth_sort":    # slot scan 8, histogram 4, pass 0 (key+rect in, key+id+rect out) 24 (20 with the
+        return VG * (8 + 4 + 24 - pk + 2 * 24 + 28)  # packed rect), passes 1-2 24 each, pass 3 (-> id, rect, count) 28
     if stage == "scan":
         return VG * 8
     if stage == "emit":          # per record: id, rect, tile count, offset in; per pair: tile key and Gaussian out
-        return VG * (4 + 8 + 4 + 4) + P * 8
+        return VG * (4 + 8 + 4 + 4) + P * (4 if c["packed"] else 8)   # (one packed word when both fit 32 bits)
     if stage == "tile_sort":     # pass 1 key+value in and out, pass 2 key+value in, value out (the digit counts
-        return P * (16 + 12)     # come from emit)
+        return P * (8 + 8) if c["packed"] else P * (16 + 12)  # come from emit); packed words: 4 B in, 4 B out
     if stage == "ranges":        # empty-tile fix-up (the ranges come from the last tile-sort pass)
         return V * c["T"] * 16
     return None
@@ -263,7 +264,9 @@ def main():
     mpix = V * H * W / (elapsed / args.steps) / 1e6
     contribs = K / (elapsed / args.steps)
 
-    c = dict(G=sc.n, V=V, d=sc.d, P=P, T=T_tiles, n_live=n_live)
+    bits_for = lambda n: max(int(n - 1).bit_length(), 1)
+    c = dict(G=sc.n, V=V, d=sc.d, P=P, T=T_tiles, n_live=n_live,
+             packed=bits_for(V * T_tiles) + bits_for(sc.n) <= 32, packable=(W + 15) // 16 <= 256 and (H + 15) // 16 <= 256)
     stages = {k: (ms / max(cnt, 1), cnt) for k, (ms, cnt) in prof.items() if cnt > 0}
     # The dominant single kernel is the score replay (one launch per step, the
     # "replay" stage): bound by fp32 VALU work, counted algorithmically; its
