@@ -357,8 +357,10 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     uint32_t* rid_sorted = nullptr;
     const bool packable = s.TX <= 256 && s.TY <= 256;
     // (a second sort after one gs_project packs on load: the first sort's last pass overwrote the packed form)
+    // for such grids the last pass leaves the packed rectangles (in depth order) in tt_sorted, from which the
+    // offsets scan and emit take the tile counts and rectangles
     const RectSort rs{ws.rect, ws.rect_sorted, ws.tt_sorted, packable ? ws.pay_a : nullptr,
-                      packable ? ws.pay_b : nullptr, packable && ctx->packed_fresh ? ws.tt_sorted : nullptr};
+                      packable ? ws.pay_b : nullptr, packable && ctx->packed_fresh ? ws.tt_sorted : nullptr, packable};
     ctx->packed_fresh = false;
     e = launch_radix_sort(ws.depth_key, nullptr, s.VG, 32, ws.dkey_b, ws.offsets, ws.drid_a, ws.drid_b, &rs, nullptr,
                           false, 0, sort_scratch, &ctx->epoch, stream, nullptr, &rid_sorted);
@@ -366,7 +368,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
     tm.begin(GS_STAGE_SCAN, stream);
-    e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream);
+    e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream, packable);
     if (e != hipSuccess) return hip_fail(e, "scan");
     tm.end(GS_STAGE_SCAN, stream);
     // wait for the pair count by polling its event
@@ -393,7 +395,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     tm.begin(GS_STAGE_EMIT, stream);
     e = launch_ranges_init(ws.ranges, tiles, ws.sort_part, stream);
     if (e != hipSuccess) return hip_fail(e, "ranges init");
-    e = launch_emit(s, ws, rid_sorted, &td, packed_gbits, stream);
+    e = launch_emit(s, ws, rid_sorted, &td, packed_gbits, packable, stream);
     if (e != hipSuccess) return hip_fail(e, "emit");
     tm.end(GS_STAGE_EMIT, stream);
     uint32_t* sorted_g = nullptr;

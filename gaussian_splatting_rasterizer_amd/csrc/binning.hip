@@ -96,15 +96,21 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T* total, T* lds /* NT/64
     return base + inc - x;
 }
 
+// tile count of a scan item: the item itself, or the count of a packed rectangle
+__device__ __forceinline__ uint32_t scan_item(uint32_t x, bool packed_rect) {
+    if (!packed_rect) return x;
+    return x == 0xffffffffu ? 0u : (((x >> 16) & 0xffu) + 1u) * ((x >> 24) + 1u);
+}
+
 __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __restrict__ in, int64_t n,
-                                                              uint64_t* __restrict__ bsum) {
+                                                              uint64_t* __restrict__ bsum, bool packed_rect) {
     __shared__ uint64_t lds[kScanThreads / 64];
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
     uint64_t s = 0;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
         const int64_t k = base + i * kScanThreads + threadIdx.x;
-        if (k < n) s += in[k];
+        if (k < n) s += scan_item(in[k], packed_rect);
     }
     uint64_t tot;
     block_exclusive_scan<uint64_t, kScanThreads>(s, &tot, lds);
@@ -117,7 +123,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __
 // block writes the grand total.
 __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, int64_t n,
                                                             const uint64_t* __restrict__ bsum, int64_t nb,
-                                                            uint32_t* out, uint64_t* __restrict__ total) {
+                                                            uint32_t* out, uint64_t* __restrict__ total,
+                                                            bool packed_rect) {
     // padded so that thread t's 16 consecutive items (t*17 + i) are bank-conflict free
     __shared__ uint32_t s[kScanTile + kScanTile / 16];
     __shared__ uint32_t lds[kScanThreads / 64];
@@ -127,7 +134,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
     for (int i = 0; i < kScanItems; ++i) {
         const int e = i * kScanThreads + threadIdx.x;
         const int64_t k = base + e;
-        s[e + e / 16] = k < n ? in[k] : 0u;
+        s[e + e / 16] = k < n ? scan_item(in[k], packed_rect) : 0u;
     }
     uint64_t before = 0;
     for (int64_t j = threadIdx.x; j < (int64_t)blockIdx.x; j += kScanThreads) before += bsum[j];
@@ -159,15 +166,16 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
 __global__ void k_zero_u64(uint64_t* __restrict__ p) { *p = 0ull; }
 
 hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
-                           hipStream_t st) {
+                           hipStream_t st, bool packed_rect_in) {
     const int64_t nb = (n + kScanTile - 1) / kScanTile;
     if (nb == 0) {
         hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, st, total);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch);
+    hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch,
+                       packed_rect_in);
     hipLaunchKernelGGL(k_scan_down, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch, nb, out,
-                       total);
+                       total, packed_rect_in);
     return hipGetLastError();
 }
 
@@ -522,6 +530,8 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
     const int64_t nb = (n + kRadixTile - 1) / kRadixTile;
     // packed words: key bits [key_shift, key_shift + bits), counted beforehand, no value array, no rectangles
     const bool packed = key_shift > 0;
+    // a single pass cannot read the packed rectangles from the array it writes them to
+    if (rs && rs->out_packed && (!rs->pay_a || (passes == 1 && rs->pay_init == rs->tt_out))) return hipErrorInvalidValue;
     if (packed && (!hist_ready || vals_in || rs || !ranges || key_shift + bits > 32)) return hipErrorInvalidValue;
     uint32_t* kb[2] = {kbuf0, kbuf1};
     uint32_t* vb[2] = {vbuf0, vbuf1};
@@ -557,7 +567,9 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
             } else {
                 rc.pay_in = p & 1 ? rs->pay_a : rs->pay_b;
             }
-            if (last) {
+            if (last && rs->out_packed) {
+                rc.pay_out = rs->tt_out;
+            } else if (last) {
                 rc.rect_out = rs->rect_out;
                 rc.tt_out = rs->tt_out;
             } else {
@@ -628,8 +640,14 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
         if (k < VG) {
             s_off[i] = offsets[k];
             s_rid[i] = rid_sorted[k];
-            s_rect[i] = rect_sorted[k];
-            if (i == last) s_end = offsets[k] + tt_sorted[k];
+            if (rect_sorted) {
+                s_rect[i] = rect_sorted[k];
+                if (i == last) s_end = offsets[k] + tt_sorted[k];
+            } else {  // packed rectangles in tt_sorted
+                const uint32_t q = tt_sorted[k];
+                s_rect[i] = unpack_rect(q);
+                if (i == last) s_end = offsets[k] + scan_item(q, true);
+            }
         }
     }
     if (PASSES > 0)
@@ -672,12 +690,13 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
 }
 
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, const RadixDigits* rd,
-                       int packed_gbits, hipStream_t st) {
+                       int packed_gbits, bool rects_packed, hipStream_t st) {
     if (s.VG == 0) return hipSuccess;
     const dim3 grid((unsigned)((s.VG + kEmitRecs - 1) / kEmitRecs)), block(256);
     const RadixDigits d = rd ? *rd : RadixDigits{};
 #define GSR_EMIT(PP)                                                                                              \
-    hipLaunchKernelGGL(k_emit<PP>, grid, block, 0, st, rid_sorted, ws.rect_sorted, ws.tt_sorted, ws.offsets, s.VG, \
+    hipLaunchKernelGGL(k_emit<PP>, grid, block, 0, st, rid_sorted, rects_packed ? nullptr : ws.rect_sorted,      \
+                       ws.tt_sorted, ws.offsets, s.VG,                                                           \
                        (uint32_t)s.G, s.T, s.TX, ws.pkey_emit, ws.pair_g, d, packed_gbits, ws.sort_part)
     switch (rd ? rd->passes : 0) {
         case 0: GSR_EMIT(0); break;

@@ -90,9 +90,10 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s
 // pay_init (optional): also the packed rectangles (pack_rect) per record, for the depth sort's first pass
 hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, float near_plane,
                           float far_plane, int antialiased, uint32_t* pay_init, Workspace& ws, hipStream_t st);
-// exclusive scan of in (u32) into out (may alias); total -> *total (device u64)
+// exclusive scan of in (u32) into out (may alias); total -> *total (device u64).  With packed_rect_in the
+// items are packed rectangles (pack_rect) and their tile counts are scanned.
 hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
-                           hipStream_t st);
+                           hipStream_t st, bool packed_rect_in = false);
 // Tile rectangles that a record sort moves into sorted order with the values:
 // rect[val] becomes rect_out[pos] with its tile count tt_out[pos].  With
 // pay_a/pay_b (u32, n each) the rectangles are carried through the passes
@@ -105,6 +106,8 @@ struct RectSort {
     uint32_t* pay_a;
     uint32_t* pay_b;
     const uint32_t* pay_init;  // optional: the rectangles already packed, in input order (read by pass 0)
+    bool out_packed;           // with pay_a/pay_b: the last pass writes the packed words into tt_out instead of
+                               // the rectangles and tile counts (rect_out unused)
 };
 // Per-launch form of the same (device side).
 struct RectCarry {
@@ -143,11 +146,13 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
                              const RectSort* rs, uint2* ranges, bool hist_ready, int key_shift,
                              const SortScratch& sc, uint32_t* epoch, hipStream_t st, uint32_t** keys_out,
                              uint32_t** vals_out);
+// The depth-ordered rectangles are rect_sorted with their tile counts tt_sorted, or, with rects_packed, the
+// packed words in tt_sorted.
 // (tile, Gaussian) pairs of the depth-ordered records into pkey_emit / pair_g, or, with packed_gbits > 0,
 // into pkey_emit alone as (tile << packed_gbits) | Gaussian; with rd, their tile ids' digit counts
 // (layout *rd) are added into the rows of sort_part, which must be zero beforehand.
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, const RadixDigits* rd,
-                       int packed_gbits, hipStream_t st);
+                       int packed_gbits, bool rects_packed, hipStream_t st);
 // ranges before / after a sort that records them: {~0u, 0} everywhere, then empty ones to {0, 0};
 // the init also zeroes the kSortPartBlocks histogram rows of part when given
 hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hipStream_t st);
