@@ -244,8 +244,11 @@ __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */,
                           c02 * (c01 * c12 - c11 * c02));
         r = r < -1.0 ? -1.0 : (r > 1.0 ? 1.0 : r);
         const double phi = acos(r) / 3.0;
-        e0 = q + 2.0 * p * cos(phi);
-        e2 = q + 2.0 * p * cos(phi + 2.0943951023931954923);
+        double sn, cs;
+        sincos(phi, &sn, &cs);
+        e0 = q + 2.0 * p * cs;
+        // cos(phi + 2 pi / 3) = -cos(phi) / 2 - sin(phi) sqrt(3) / 2
+        e2 = q - p * (cs + 1.7320508075688772935 * sn);
         e1 = 3.0 * q - e0 - e2;
     }
     // sort descending
@@ -494,12 +497,14 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
         const float fiQ = (float)iQ;
 #pragma unroll
         for (int k = 0; k < 3 * D; ++k) z[4 + k] = shnum[k] * fiQ;
-        z[4 + 3 * D] = (float)log(Q);
+        // the logarithms in float32: the tokens are float32, and rounding the argument first moves the result
+        // by at most 2^-24 (absolute)
+        z[4 + 3 * D] = logf((float)Q);
         const double itr = 1.0 / (tr + eps);
         z[5 + 3 * D] = (float)(ev[0] * itr);
         z[6 + 3 * D] = (float)(ev[1] * itr);
         z[7 + 3 * D] = (float)(ev[2] * itr);
-        z[8 + 3 * D] = (float)log(tr + eps);
+        z[8 + 3 * D] = logf((float)(tr + eps));
     }
     __syncthreads();
     // the block's span starts g0 * DT floats (a multiple of 4) into the output: float4 stores when the
