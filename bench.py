@@ -73,11 +73,13 @@ def stage_bytes(stage, c):
     if stage == "project":       # Gaussian parameters in; 40-byte record, rectangle, depth key, tile count out
         return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (40 + 8 + 4 + 4 + pk)
     if stage == "depth_sort":    # slot scan 8, histogram 4, pass 0 (key+rect in, key+id+rect out) 24 (20 with the
-        return VG * (8 + 4 + 24 - pk + 2 * 24 + 28)  # packed rect), passes 1-2 24 each, pass 3 (-> id, rect, count) 28
+        return VG * (8 + 4 + 24 - pk + 2 * 24 + 28 - 2 * pk)  # packed rect), passes 1-2 24 each, pass 3 (-> id and
+                                                               # rect + count 28, or id and packed rect 20)
     if stage == "scan":
         return VG * 8
     if stage == "emit":          # per record: id, rect, tile count, offset in; per pair: tile key and Gaussian out
-        return VG * (4 + 8 + 4 + 4) + P * (4 if c["packed"] else 8)   # (one packed word when both fit 32 bits)
+        return VG * (4 + 4 + 4 + (0 if pk else 8)) + P * (4 if c["packed"] else 8)  # (packed rect 4 B instead of rect
+                                                                       # and count 12 B; one word per pair if it fits)
     if stage == "tile_sort":     # pass 1 key+value in and out, pass 2 key+value in, value out (the digit counts
         return P * (8 + 8) if c["packed"] else P * (16 + 12)  # come from emit); packed words: 4 B in, 4 B out
     if stage == "ranges":        # empty-tile fix-up (the ranges come from the last tile-sort pass)
