@@ -111,9 +111,12 @@ def kernel_source_sha256(kernel):
     return _sources_sha256(KERNEL_SOURCES[kernel])
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, antialiased=False):
     """HBM bytes per launch from the committed counter summary of this workload,
-    or None when there is none or the kernel's sources changed since."""
+    or None when there is none, the kernel's sources changed since, or the run
+    is in the antialiased mode (the counters are taken in the plain mode)."""
+    if antialiased:
+        return None
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -280,14 +283,14 @@ def main():
     workload = scenes.CONFIG_NAMES[args.config]
     roofline = {"kernel": "k_replay", "bound": "alu", "achieved": round(achieved, 3), "peak": round(ALU_PEAK_TOPS, 2),
                 "unit": "T lane-ops/s (fp32 VALU)", "frac": round(achieved / ALU_PEAK_TOPS, 4),
-                "traffic": measured_traffic("k_replay", workload), "avg_launch_ms": round(rep_ms, 4),
+                "traffic": measured_traffic("k_replay", workload, args.antialiased), "avg_launch_ms": round(rep_ms, 4),
                 "ops_per_launch": ops,
                 "units": {"evaluations": E, "near_evaluations": E_near, "contributions": K}}
     t_ren = stages["render"][0] * 1e-3
     ops_r = OPS_EVAL * E + OPS_NEAR * E_near + OPS_CONTRIB_FWD * K
     secondary = {"k_render": {"bound": "alu", "achieved": round(ops_r / t_ren / 1e12, 3),
                               "frac": round(ops_r / t_ren / 1e12 / ALU_PEAK_TOPS, 4),
-                              "traffic": measured_traffic("k_render", workload),
+                              "traffic": measured_traffic("k_render", workload, args.antialiased),
                               "avg_launch_ms": round(stages["render"][0], 4)}}
     for st in ("project", "depth_sort", "emit", "tile_sort", "ranges"):
         if st not in stages:
@@ -306,7 +309,7 @@ def main():
                     "stages_ms": {k: round(v, 4) for k, v in bwd["stages"].items()},
                     "k_backward": {"bound": "alu", "achieved": round(ops_b / t_b / 1e12, 3),
                                    "frac": round(ops_b / t_b / 1e12 / ALU_PEAK_TOPS, 4),
-                                   "traffic": measured_traffic("k_backward", workload),
+                                   "traffic": measured_traffic("k_backward", workload, args.antialiased),
                                    "avg_launch_ms": round(bwd["stages"]["backward"], 4), "ops_per_launch": ops_b},
                     "grads_finite": bwd["finite"], "loss": "1/2 |C_hat - C_obs|^2"}
 
