@@ -180,6 +180,8 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     ws->pval_b = (uint32_t*)take(4 * P);
     ws->pair_g = (uint32_t*)take(4 * P);
     ws->ranges = (uint2*)take(8 * tiles);
+    ws->tile_work = (uint32_t*)take(4 * tiles);
+    ws->tile_order = (uint32_t*)take(4 * tiles);
     ws->partials = (float4*)take(48 * P);
     ws->gv_sums = (float4*)take(48 * VG);
     ws->rec_masks = (uint64_t*)take(16 * ((VG + 63) / 64));

@@ -34,14 +34,15 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
                                                          const float4* __restrict__ rec1, int64_t G, int T, int TX,
                                                          int W, int H, const uint8_t* __restrict__ events,
                                                          const float* __restrict__ feat, int C, int c0, int nc,
-                                                         FeatBg bg, float* __restrict__ out) {
+                                                         FeatBg bg, float* __restrict__ out,
+                                                         const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s0[kAttrBatch];
     __shared__ float2 s1[kAttrBatch];
     __shared__ float sf[kAttrBatch][NC];
     __shared__ uint8_t s_evb[kAttrBatch];
     __shared__ uint8_t slist[4][kAttrBatch];
 
-    const int tile = blockIdx.x;
+    const int tile = (int)tile_order[blockIdx.x];
     const int v = tile / T;
     const int t = tile - v * T;
     const int ty = t / TX, tx = t - ty * TX;
@@ -128,7 +129,7 @@ hipError_t launch_render_features(const Sizes& s, const Workspace& ws, const uin
         for (int c = 0; c < 16; ++c) bg.v[c] = (bg_host && c < nc) ? bg_host[c0 + c] : 0.0f;
 #define GSR_LAUNCH_FEAT(NN)                                                                                       \
     hipLaunchKernelGGL(k_render_features<NN>, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,       \
-                       ws.rec0, ws.rec1, s.G, s.T, s.TX, s.W, s.H, ws.events, feat, C, c0, nc, bg, out)
+                       ws.rec0, ws.rec1, s.G, s.T, s.TX, s.W, s.H, ws.events, feat, C, c0, nc, bg, out, ws.tile_order)
         if (nc <= 4) GSR_LAUNCH_FEAT(4);
         else if (nc <= 8) GSR_LAUNCH_FEAT(8);
         else GSR_LAUNCH_FEAT(16);
@@ -147,7 +148,8 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
                                                    const uint2* __restrict__ rect, int64_t G, int T, int TX, int W,
                                                    int H, const uint8_t* __restrict__ events,
                                                    const float* __restrict__ map, int C, int c0, int nc,
-                                                   float4* __restrict__ partials, uint32_t* __restrict__ slot_bits) {
+                                                   float4* __restrict__ partials, uint32_t* __restrict__ slot_bits,
+                                                   const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s0[kAttrBatch];
     __shared__ float2 s1[kAttrBatch];
     __shared__ uint8_t s_evb[kAttrBatch];
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
     __shared__ uint8_t slist[4][kAttrBatch];
     __shared__ __align__(16) float sp[4][kAttrBatch][8];
 
-    const int tile = blockIdx.x;
+    const int tile = (int)tile_order[blockIdx.x];
     const int v = tile / T;
     const int t = tile - v * T;
     const int ty = t / TX, tx = t - ty * TX;
@@ -290,7 +292,7 @@ hipError_t launch_attribute(const Sizes& s, const Workspace& ws, const uint32_t*
         if (tiles > 0)
             hipLaunchKernelGGL(k_attribute, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,
                                ws.slot_base, ws.rec0, ws.rec1, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.events, map, C,
-                               c0, nc, ws.partials, ws.slot_bits);
+                               c0, nc, ws.partials, ws.slot_bits, ws.tile_order);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_gather_slots(s, ws, 2, st);

@@ -58,7 +58,8 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                                                   const float4* __restrict__ pixel,
                                                   const float* __restrict__ grad_color,
                                                   const uint8_t* __restrict__ events, float4* __restrict__ partials,
-                                                  uint32_t* __restrict__ slot_bits) {
+                                                  uint32_t* __restrict__ slot_bits,
+                                                  const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s0[kBwdBatch];
     __shared__ float4 s1[kBwdBatch];
     __shared__ float s2[kBwdBatch];
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
     __shared__ uint8_t slist[4][kBwdBatch];
     __shared__ __align__(16) float sp[4][kBwdBatch][12];
 
-    const int tile = blockIdx.x;
+    const int tile = (int)tile_order[blockIdx.x];
     const int v = tile / T;
     const int t = tile - v * T;
     const int ty = t / TX, tx = t - ty * TX;
@@ -213,7 +214,7 @@ hipError_t launch_backward(const Sizes& s, const Workspace& ws, const uint32_t* 
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_backward, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.slot_base,
                        ws.rec0, ws.rec1, ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.pixel, grad_color,
-                       ws.events, ws.partials, ws.slot_bits);
+                       ws.events, ws.partials, ws.slot_bits, ws.tile_order);
     return hipGetLastError();
 }
 

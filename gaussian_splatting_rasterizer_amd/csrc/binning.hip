@@ -732,6 +732,67 @@ hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hi
     return hipGetLastError();
 }
 
+// The traversals that follow the render (replay, backward, feature composite, attribution) take the tiles
+// in decreasing order of the work the render measured for them, so that the longest do not start last and
+// the final wave of blocks is short.  Work is bucketed (2 buckets per octave) and tiles keep their order
+// within a bucket, so tiles of similar work stay next to their neighbours.  One block; stable per-wave
+// ranking within each 1024-tile chunk.
+__device__ __forceinline__ uint32_t work_bucket(uint32_t w) {
+    const uint32_t b = (uint32_t)(log2f((float)w + 1.0f) * 2.0f);
+    return 63u - (b > 63u ? 63u : b);
+}
+
+__global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict__ work, int64_t n,
+                                                     uint32_t* __restrict__ order) {
+    __shared__ uint32_t base[64];
+    __shared__ uint32_t wcnt[16][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    if (threadIdx.x < 64) base[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < 16 * 64; i += 1024) (&wcnt[0][0])[i] = 0u;
+    __syncthreads();
+    for (int64_t t = threadIdx.x; t < n; t += 1024) atomicAdd(&base[work_bucket(work[t])], 1u);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t s = 0u;
+        for (int b = 0; b < 64; ++b) {
+            const uint32_t c = base[b];
+            base[b] = s;
+            s += c;
+        }
+    }
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < n; c0 += 1024) {
+        const int64_t t = c0 + threadIdx.x;
+        const bool valid = t < n;
+        const uint32_t b = valid ? work_bucket(work[t]) : 0u;
+        const uint64_t peers = match_peers(b, 6, valid);
+        const uint64_t lower = peers & lt_mask;
+        if (valid && lower == 0ull) wcnt[wave][b] = (uint32_t)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            uint32_t pos = base[b] + (uint32_t)__popcll(lower);
+            for (int w = 0; w < wave; ++w) pos += wcnt[w][b];
+            order[pos] = (uint32_t)t;
+        }
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            uint32_t s = 0u;
+            for (int w = 0; w < 16; ++w) {
+                s += wcnt[w][threadIdx.x];
+                wcnt[w][threadIdx.x] = 0u;
+            }
+            base[threadIdx.x] += s;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_tile_order(const uint32_t* work, int64_t n_tiles, uint32_t* order, hipStream_t st) {
+    if (n_tiles > 0) hipLaunchKernelGGL(k_tile_order, dim3(1), dim3(1024), 0, st, work, n_tiles, order);
+    return hipGetLastError();
+}
+
 hipError_t launch_ranges_fix(uint2* ranges, int64_t n_tiles, hipStream_t st) {
     if (n_tiles > 0) hipLaunchKernelGGL(k_ranges_fix, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, st, ranges, n_tiles);
     return hipGetLastError();

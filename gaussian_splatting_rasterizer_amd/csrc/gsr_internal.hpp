@@ -43,6 +43,8 @@ struct Workspace {
     uint32_t* pval_b;
     uint32_t* pair_g;      // Gaussian of each emitted pair, depth order
     uint2* ranges;         // per tile [start, end)
+    uint32_t* tile_work;   // per tile: list entries the render processed before its pixels were done
+    uint32_t* tile_order;  // tiles by decreasing tile_work: the order the traversals after the render take them
     float4* partials;      // per slot, score replay (2 float4): {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix};
                            // backward (3 float4): {U, U_x, U_y, U_xx}, {U_xy, U_yy, masked V_rg}, {masked V_b, 0, 0, 0}
     float4* gv_sums;       // per reached record: the sums of the same layout (2 or 3 float4)
@@ -157,6 +159,8 @@ hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted
 // the init also zeroes the kSortPartBlocks histogram rows of part when given
 hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hipStream_t st);
 hipError_t launch_ranges_fix(uint2* ranges, int64_t n_tiles, hipStream_t st);
+// tiles bucketed by work (2 buckets per octave), largest first, in tile order within a bucket
+hipError_t launch_tile_order(const uint32_t* work, int64_t n_tiles, uint32_t* order, hipStream_t st);
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
                          const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st);
 hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* observed,

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                                                 float* __restrict__ T_out, int32_t* __restrict__ n_out,
                                                 float4* __restrict__ pixel, uint2* __restrict__ pixel_stats,
                                                 uint8_t* __restrict__ events, uint32_t* __restrict__ slot_bits,
-                                                int64_t n_slot_words) {
+                                                int64_t n_slot_words, uint32_t* __restrict__ tile_work) {
     // clear the replay's written-slot bits (a grid-stride share per block)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slot_words;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
 
     uint32_t prev_base = 0;
     int prev_cnt = 0;
-    for (uint32_t base = rg.x;; base += kRenderBatch) {
+    uint32_t base = rg.x;
+    for (;; base += kRenderBatch) {
         const int live = __syncthreads_count(!done);
         // the previous batch's event bits (every wave finished it at the barrier above)
         if ((int)threadIdx.x < prev_cnt)
@@ -141,6 +142,8 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
         prev_base = base;
         prev_cnt = cnt;
     }
+    // the work of this tile, for the order of the traversals that follow: entries processed until done
+    if (threadIdx.x == 0) tile_work[tile] = (base < rg.y ? base : rg.y) - rg.x;
     if (!inside) return;
     kahan_add(h0, c0, Tr * bg0);
     kahan_add(h1, c1, Tr * bg1);
@@ -164,8 +167,10 @@ hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* so
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1,
                        ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel,
-                       ws.pixel_stats, ws.events, ws.slot_bits, (int64_t)((n_pairs + 31) / 32));
-    return hipGetLastError();
+                       ws.pixel_stats, ws.events, ws.slot_bits, (int64_t)((n_pairs + 31) / 32), ws.tile_work);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_tile_order(ws.tile_work, tiles, ws.tile_order, st);
 }
 
 }  // namespace gsr

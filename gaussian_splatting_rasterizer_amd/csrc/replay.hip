@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                                                 const float2* __restrict__ rec2, const uint2* __restrict__ rect,
                                                 int64_t G, int T, int TX, int W, int H, const float4* __restrict__ pixel, const float* __restrict__ observed,
                                                 const uint8_t* __restrict__ events, float eps, float den_min,
-                                                float4* __restrict__ partials, uint32_t* __restrict__ slot_bits) {
+                                                float4* __restrict__ partials, uint32_t* __restrict__ slot_bits,
+                                                const uint32_t* __restrict__ tile_order) {
     __shared__ float4 s0[kReplayBatch];
     __shared__ float4 s1[kReplayBatch];
     __shared__ float s2[kReplayBatch];
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     __shared__ uint8_t slist[4][kReplayBatch];
     __shared__ __align__(16) float sp[4][kReplayBatch][8];
 
-    const int tile = blockIdx.x;
+    const int tile = (int)tile_order[blockIdx.x];
     const int v = tile / T;
     const int t = tile - v * T;
     const int ty = t / TX, tx = t - ty * TX;
@@ -216,7 +217,7 @@ hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* so
     hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,
                        ws.slot_base, ws.rec0, ws.rec1,
                        ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, ws.events, eps, den_min,
-                       ws.partials, ws.slot_bits);
+                       ws.partials, ws.slot_bits, ws.tile_order);
     return hipGetLastError();
 }
 
