@@ -121,6 +121,7 @@ struct gs_context {
     uint64_t* host_count;         // pinned host word receiving the pair count (allocated on first use)
     hipEvent_t count_ev;
     bool packed_fresh;            // gs_project left the packed rectangles that the next depth sort reads
+    bool order_valid;             // tile_order holds the order a render of this context measured
 };
 
 namespace gsr {
@@ -424,8 +425,9 @@ gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_co
         return fail(GS_ERR_INVALID_ARGUMENT, "misaligned output pointer");
     ctx->timer.begin(GS_STAGE_RENDER, stream);
     hipError_t e = launch_render(ctx->s, ctx->ws, ctx->sorted_g, ctx->n_pairs, ctx->params.background, color,
-                                 T_final, n_contrib, stream);
+                                 T_final, n_contrib, stream, ctx->order_valid);
     if (e != hipSuccess) return hip_fail(e, "render");
+    ctx->order_valid = true;
     ctx->timer.end(GS_STAGE_RENDER, stream);
     ctx->state = kRendered;
     return GS_OK;

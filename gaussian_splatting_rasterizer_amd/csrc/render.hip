@@ -31,7 +31,8 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                                                 float* __restrict__ T_out, int32_t* __restrict__ n_out,
                                                 float4* __restrict__ pixel, uint2* __restrict__ pixel_stats,
                                                 uint8_t* __restrict__ events, uint32_t* __restrict__ slot_bits,
-                                                int64_t n_slot_words, uint32_t* __restrict__ tile_work) {
+                                                int64_t n_slot_words, uint32_t* __restrict__ tile_work,
+                                                const uint32_t* __restrict__ prev_order) {
     // clear the replay's written-slot bits (a grid-stride share per block)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slot_words;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -43,7 +44,9 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     __shared__ uint8_t slist[4][kRenderBatch];
     __shared__ uint8_t s_ev[4][kRenderBatch];  // per wave: some pixel contributed or saturated at the entry
 
-    const int tile = blockIdx.x;
+    // tiles in the order the previous render of this context measured (longest first), or the natural order;
+    // the order only changes how the blocks pack onto the GPU, never a result
+    const int tile = prev_order ? (int)prev_order[blockIdx.x] : (int)blockIdx.x;
     const int v = tile / T;
     const int t = tile - v * T;
     const int ty = t / TX, tx = t - ty * TX;
@@ -162,12 +165,14 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
 }
 
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
-                         const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st) {
+                         const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st,
+                         bool prev_order_valid) {
     const int64_t tiles = (int64_t)s.V * s.T;
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1,
                        ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel,
-                       ws.pixel_stats, ws.events, ws.slot_bits, (int64_t)((n_pairs + 31) / 32), ws.tile_work);
+                       ws.pixel_stats, ws.events, ws.slot_bits, (int64_t)((n_pairs + 31) / 32), ws.tile_work,
+                       prev_order_valid ? ws.tile_order : nullptr);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_tile_order(ws.tile_work, tiles, ws.tile_order, st);

@@ -159,7 +159,13 @@ GSR_API gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_p
  *   n_contrib  [n_views, height, width]    accepted contributions (int32)
  * The rendered colour is also kept in the workspace for gs_score_replay, with
  * one byte per processed list entry marking the 8x8 pixel blocks in which some
- * pixel's state changed there (the replay walks only those entries). */
+ * pixel's state changed there (the replay walks only those entries).
+ * Scheduling: the render records each tile's work (list entries processed)
+ * and the traversals that follow it (replay, backward, features, attribution)
+ * take the tiles longest first; the next gs_render on the same context starts
+ * from that order too (the first takes the tiles in index order).  The order
+ * changes only how the work packs onto the GPU: every tile is fully computed
+ * and all outputs are identical whatever the order. */
 GSR_API gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_contrib,
                     hipStream_t stream);
 
