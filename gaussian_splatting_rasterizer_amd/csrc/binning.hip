@@ -738,7 +738,10 @@ hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hi
 // within a bucket, so tiles of similar work stay next to their neighbours.  One block; stable per-wave
 // ranking within each 1024-tile chunk.
 __device__ __forceinline__ uint32_t work_bucket(uint32_t w) {
-    const uint32_t b = (uint32_t)(log2f((float)w + 1.0f) * 2.0f);
+    // half octaves of w + 1: twice the position k of its top bit, plus the bit below it (split at 1.5 * 2^k)
+    const uint32_t x = w + 1u;
+    const uint32_t k = 31u - (uint32_t)__builtin_clz(x);
+    const uint32_t b = 2u * k + (k > 0u ? (x >> (k - 1u)) & 1u : 0u);
     return 63u - (b > 63u ? 63u : b);
 }
 
@@ -753,13 +756,9 @@ __global__ __launch_bounds__(1024) void k_tile_order(const uint32_t* __restrict_
     __syncthreads();
     for (int64_t t = threadIdx.x; t < n; t += 1024) atomicAdd(&base[work_bucket(work[t])], 1u);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t s = 0u;
-        for (int b = 0; b < 64; ++b) {
-            const uint32_t c = base[b];
-            base[b] = s;
-            s += c;
-        }
+    if (wave == 0) {  // bucket starts: one wave's exclusive scan of the 64 counts
+        const uint32_t c = base[lane];
+        base[lane] = wave_inclusive_scan(c, lane) - c;
     }
     __syncthreads();
     for (int64_t c0 = 0; c0 < n; c0 += 1024) {
