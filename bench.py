@@ -82,8 +82,8 @@ def stage_bytes(stage, c):
                                                                        # and count 12 B; one word per pair if it fits)
     if stage == "tile_sort":     # pass 1 key+value in and out, pass 2 key+value in, value out (the digit counts
         return P * (8 + 8) if c["packed"] else P * (16 + 12)  # come from emit); packed words: 4 B in, 4 B out
-    if stage == "ranges":        # empty-tile fix-up (the ranges come from the last tile-sort pass)
-        return V * c["T"] * 16
+    if stage == "ranges":        # ranges set to {~0u, 0} (the last tile-sort pass records them) and the 1 MiB of
+        return V * c["T"] * 8 + (1 << 20)   # histogram rows zeroed for the tile sort's digit counts
     return None
 
 

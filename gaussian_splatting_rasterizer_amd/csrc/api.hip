@@ -119,6 +119,7 @@ struct gs_context {
     StageTimer timer;
     uint32_t epoch;               // last radix pass epoch; 0 = look-back words not cleared yet
     uint64_t* host_count;         // pinned host word receiving the pair count (allocated on first use)
+    uint64_t* host_count_dev;     // its device address: the slot scan writes the count there itself
     hipEvent_t count_ev;
     bool packed_fresh;            // gs_project left the packed rectangles that the next depth sort reads
     bool order_valid;             // tile_order holds the order a render of this context measured
@@ -331,11 +332,13 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
         ctx->epoch = 0;
     }
     if (!ctx->host_count) {
-        e = hipHostMalloc((void**)&ctx->host_count, 64, hipHostMallocDefault);
+        e = hipHostMalloc((void**)&ctx->host_count, 64, hipHostMallocMapped | hipHostMallocCoherent);
         if (e != hipSuccess) {
             ctx->host_count = nullptr;
             return hip_fail(e, "pinned count word");
         }
+        e = hipHostGetDevicePointer((void**)&ctx->host_count_dev, ctx->host_count, 0);
+        if (e != hipSuccess) return hip_fail(e, "pinned count word address");
         e = hipEventCreateWithFlags(&ctx->count_ev, hipEventDisableTiming);
         if (e != hipSuccess) {
             ctx->count_ev = nullptr;
@@ -345,13 +348,12 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     const SortScratch sort_scratch{ws.lookback, ws.sort_ctl, ws.sort_part};
     // 0. slot bases of the replay's partials: tile counts scanned in record order
     tm.begin(GS_STAGE_DEPTH_SORT, stream);
-    e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream);
+    // the pair count is this scan's total (the same tile counts as the depth-ordered scan below): the scan
+    // writes it into pinned host memory too, and the host waits for it only after the sort and the second scan
+    // are queued, so that the GPU has work while the host waits
+    e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream, false,
+                        ctx->host_count_dev);
     if (e != hipSuccess) return hip_fail(e, "slot scan");
-    // the pair count is this scan's total (the same tile counts as the depth-ordered scan below): copied into
-    // pinned host memory now and waited for only after the sort and the scan are queued, so that the GPU has
-    // work while the host waits
-    e = hipMemcpyAsync(ctx->host_count, ws.scan_total + 1, sizeof(uint64_t), hipMemcpyDeviceToHost, stream);
-    if (e != hipSuccess) return hip_fail(e, "pair count copy");
     e = hipEventRecord(ctx->count_ev, stream);
     if (e != hipSuccess) return hip_fail(e, "pair count event");
     // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
@@ -395,9 +397,13 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     // when a tile id and a Gaussian index fit one 32-bit word together, the pairs are sorted as such words
     const int gbits = bits_for((uint64_t)s.G) > 0 ? bits_for((uint64_t)s.G) : 1;
     const int packed_gbits = td.bits + gbits <= 32 ? gbits : 0;
-    tm.begin(GS_STAGE_EMIT, stream);
+    // the ranges start as {~0u, 0}: a tile the last pass never sees keeps start > end, an empty range for
+    // every traversal (they loop while start < end; the ranges export turns it into {0, 0})
+    tm.begin(GS_STAGE_RANGES, stream);
     e = launch_ranges_init(ws.ranges, tiles, ws.sort_part, stream);
     if (e != hipSuccess) return hip_fail(e, "ranges init");
+    tm.end(GS_STAGE_RANGES, stream);
+    tm.begin(GS_STAGE_EMIT, stream);
     e = launch_emit(s, ws, rid_sorted, &td, packed_gbits, packable, stream);
     if (e != hipSuccess) return hip_fail(e, "emit");
     tm.end(GS_STAGE_EMIT, stream);
@@ -409,10 +415,6 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
                           &ctx->epoch, stream, nullptr, &sorted_g);
     if (e != hipSuccess) return hip_fail(e, "tile sort");
     tm.end(GS_STAGE_TILE_SORT, stream);
-    tm.begin(GS_STAGE_RANGES, stream);
-    e = launch_ranges_fix(ws.ranges, tiles, stream);
-    if (e != hipSuccess) return hip_fail(e, "ranges");
-    tm.end(GS_STAGE_RANGES, stream);
     ctx->sorted_g = sorted_g;
     ctx->state = kBinned;
     return GS_OK;
@@ -570,7 +572,7 @@ gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes
             const size_t tiles = (size_t)s.V * s.T;
             if (ctx->state < kBinned) return fail(GS_ERR_STATE, "ranges exist after gs_bin_sort");
             if (bytes < 8 * tiles) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
-            e = hipMemcpyAsync(dst, ws.ranges, 8 * tiles, hipMemcpyDeviceToDevice, stream);
+            e = launch_ranges_export(ws.ranges, (uint2*)dst, (int64_t)tiles, stream);
             break;
         }
         case GS_EXPORT_PIXEL_STATS: {

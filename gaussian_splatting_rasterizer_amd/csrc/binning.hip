@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __
 __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, int64_t n,
                                                             const uint64_t* __restrict__ bsum, int64_t nb,
                                                             uint32_t* out, uint64_t* __restrict__ total,
-                                                            bool packed_rect) {
+                                                            bool packed_rect, uint64_t* host_total) {
     // padded so that thread t's 16 consecutive items (t*17 + i) are bank-conflict free
     __shared__ uint32_t s[kScanTile + kScanTile / 16];
     __shared__ uint32_t lds[kScanThreads / 64];
@@ -140,7 +140,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
     for (int64_t j = threadIdx.x; j < (int64_t)blockIdx.x; j += kScanThreads) before += bsum[j];
     uint64_t boff;
     (void)block_exclusive_scan<uint64_t, kScanThreads>(before, &boff, lds64);
-    if (threadIdx.x == 0 && (int64_t)blockIdx.x == nb - 1) *total = boff + bsum[blockIdx.x];
+    if (threadIdx.x == 0 && (int64_t)blockIdx.x == nb - 1) {
+        const uint64_t t = boff + bsum[blockIdx.x];
+        *total = t;
+        if (host_total) __hip_atomic_store(host_total, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     __syncthreads();
     const int t = threadIdx.x;
     uint32_t local = 0;
@@ -163,19 +167,22 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
     }
 }
 
-__global__ void k_zero_u64(uint64_t* __restrict__ p) { *p = 0ull; }
+__global__ void k_zero_u64(uint64_t* __restrict__ p, uint64_t* host_p) {
+    *p = 0ull;
+    if (host_p) __hip_atomic_store(host_p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
-                           hipStream_t st, bool packed_rect_in) {
+                           hipStream_t st, bool packed_rect_in, uint64_t* host_total) {
     const int64_t nb = (n + kScanTile - 1) / kScanTile;
     if (nb == 0) {
-        hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, st, total);
+        hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, st, total, host_total);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch,
                        packed_rect_in);
     hipLaunchKernelGGL(k_scan_down, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch, nb, out,
-                       total, packed_rect_in);
+                       total, packed_rect_in, host_total);
     return hipGetLastError();
 }
 
@@ -717,9 +724,14 @@ __global__ __launch_bounds__(256) void k_ranges_init(uint2* __restrict__ ranges,
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_part; i += stride) part[i] = 0u;
 }
 
-__global__ __launch_bounds__(256) void k_ranges_fix(uint2* __restrict__ ranges, int64_t n) {
+// a copy of the ranges with the ones no key reached ({~0u, 0}) as {0, 0}
+__global__ __launch_bounds__(256) void k_ranges_export(const uint2* __restrict__ ranges, uint2* __restrict__ out,
+                                                       int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n && ranges[i].x > ranges[i].y) ranges[i] = make_uint2(0u, 0u);  // no key: empty range
+    if (i < n) {
+        const uint2 r = ranges[i];
+        out[i] = r.x > r.y ? make_uint2(0u, 0u) : r;
+    }
 }
 
 hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hipStream_t st) {
@@ -792,8 +804,10 @@ hipError_t launch_tile_order(const uint32_t* work, int64_t n_tiles, uint32_t* or
     return hipGetLastError();
 }
 
-hipError_t launch_ranges_fix(uint2* ranges, int64_t n_tiles, hipStream_t st) {
-    if (n_tiles > 0) hipLaunchKernelGGL(k_ranges_fix, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, st, ranges, n_tiles);
+hipError_t launch_ranges_export(const uint2* ranges, uint2* out, int64_t n_tiles, hipStream_t st) {
+    if (n_tiles > 0)
+        hipLaunchKernelGGL(k_ranges_export, dim3((unsigned)((n_tiles + 255) / 256)), dim3(256), 0, st, ranges, out,
+                           n_tiles);
     return hipGetLastError();
 }
 

@@ -94,8 +94,9 @@ hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Siz
                           float far_plane, int antialiased, uint32_t* pay_init, Workspace& ws, hipStream_t st);
 // exclusive scan of in (u32) into out (may alias); total -> *total (device u64).  With packed_rect_in the
 // items are packed rectangles (pack_rect) and their tile counts are scanned.
+// host_total (optional): a device address of pinned host memory that receives the total as well.
 hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
-                           hipStream_t st, bool packed_rect_in = false);
+                           hipStream_t st, bool packed_rect_in = false, uint64_t* host_total = nullptr);
 // Tile rectangles that a record sort moves into sorted order with the values:
 // rect[val] becomes rect_out[pos] with its tile count tt_out[pos].  With
 // pay_a/pay_b (u32, n each) the rectangles are carried through the passes
@@ -155,10 +156,11 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
 // (layout *rd) are added into the rows of sort_part, which must be zero beforehand.
 hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted, const RadixDigits* rd,
                        int packed_gbits, bool rects_packed, hipStream_t st);
-// ranges before / after a sort that records them: {~0u, 0} everywhere, then empty ones to {0, 0};
-// the init also zeroes the kSortPartBlocks histogram rows of part when given
+// ranges before a sort that records them: {~0u, 0} everywhere (those no key reaches stay so: start > end is
+// an empty range); the init also zeroes the kSortPartBlocks histogram rows of part when given
 hipError_t launch_ranges_init(uint2* ranges, int64_t n_tiles, uint32_t* part, hipStream_t st);
-hipError_t launch_ranges_fix(uint2* ranges, int64_t n_tiles, hipStream_t st);
+// a copy of the ranges with the empty ones as {0, 0}
+hipError_t launch_ranges_export(const uint2* ranges, uint2* out, int64_t n_tiles, hipStream_t st);
 // tiles bucketed by work (2 buckets per octave), largest first, in tile order within a bucket
 hipError_t launch_tile_order(const uint32_t* work, int64_t n_tiles, uint32_t* order, hipStream_t st);
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
         prev_cnt = cnt;
     }
     // the work of this tile, for the order of the traversals that follow: entries processed until done
-    if (threadIdx.x == 0) tile_work[tile] = (base < rg.y ? base : rg.y) - rg.x;
+    if (threadIdx.x == 0) tile_work[tile] = rg.y > rg.x ? (base < rg.y ? base : rg.y) - rg.x : 0u;
     if (!inside) return;
     kahan_add(h0, c0, Tr * bg0);
     kahan_add(h1, c1, Tr * bg1);
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     if (T_out) T_out[pix] = Tr;
     if (n_out) n_out[pix] = n;
     pixel[pix] = make_float4(o0, o1, o2, Tr);
-    pixel_stats[pix] = make_uint2(stop != 0xffffffffu ? stop - rg.x + 1u : rg.y - rg.x, n_near);
+    pixel_stats[pix] = make_uint2(stop != 0xffffffffu ? stop - rg.x + 1u : (rg.y > rg.x ? rg.y - rg.x : 0u), n_near);
 }
 
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
