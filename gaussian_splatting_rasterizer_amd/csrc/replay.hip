@@ -262,23 +262,31 @@ __device__ void sym3_eigen_desc(const double A[6] /* a00 a01 a02 a11 a12 a22 */,
     ev[2] = e2;
 }
 
-// Per (view, Gaussian) record, in record order: the eight sums over the record's
-// tiles that the replay reached.  The record's slots are contiguous and
-// consecutive records' slots are adjacent, so reads and writes are coalesced.
-// Tile lists are ordered by the (depth bits, Gaussian) key, so a pair was
-// reached iff its key is below the key at which its tile's replay stopped.
-// The slot gather: one thread per record, in record order.  A record's slots
-// [slot_base, slot_base + tile count) are contiguous and the replay set a bit
-// for every slot it wrote, so each thread reads the one or two bit words of its
-// range and adds the partials of the set bits in slot order.
+// Per (view, Gaussian) record, in record order: the sums of the partials the
+// replay (or the backward traversal) wrote at the record's slots.  A record's
+// slots [slot_base, slot_base + tile count) are contiguous, consecutive
+// records' slots are adjacent, and the traversal set a bit for every slot it
+// wrote.
 constexpr int kGatherThreads = 256;
 
 // NQ float4 per slot and per record: 2 for the score replay, 3 for the backward.
 // Each thread takes kGatherRecs records 64 apart (a wave covers kGatherRecs
-// runs of 64), so the records' independent loads -- tile count and slot base,
-// then the first bitmap word -- are in flight together, and the ballot over
-// one record index of the wave is exactly that run's 64-record mask word.
+// runs of 64).  Per record a lane reads the bit words of its range (the first
+// three together with those of its other records) and decides whether any slot
+// was written; the ballot over one record index of the wave is then exactly that
+// run's live and reached mask words.  The few reached records are summed by the
+// whole wave, one record at a time: lane l takes slots l, l + 64, ... of the
+// record, loads the partials of the set bits, and a fixed-order wave reduction
+// leaves the sums in eight lanes, which store them together.  A record's loads
+// are thus one round of independent loads instead of a chain of one per slot.
 constexpr int kGatherRecs = 4;
+
+__device__ __forceinline__ uint32_t bit_range_mask(int32_t lo, int32_t hi) {  // bits [lo, hi) of a word, clipped
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > 32 ? 32 : hi;
+    if (hi <= lo) return 0u;
+    return (hi >= 32 ? ~0u : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
+}
 
 template <int NQ>
 __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
@@ -288,62 +296,91 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                                                                  const float4* __restrict__ partials,
                                                                  float4* __restrict__ gv_sums,
                                                                  uint64_t* __restrict__ rec_masks) {
+    static_assert(NQ == 2 || NQ == 3, "two or three float4 per slot");
     const int lane = threadIdx.x & 63;
     const int64_t wbase =
         ((int64_t)blockIdx.x * (kGatherThreads / 64) + (threadIdx.x >> 6)) * (64 * kGatherRecs);
     if (wbase >= VG) return;  // the whole wave is past the end
-    uint32_t tt[kGatherRecs], s0[kGatherRecs], w0[kGatherRecs];
+    uint32_t tt[kGatherRecs], sa[kGatherRecs], b0[kGatherRecs], b1[kGatherRecs], b2[kGatherRecs];
 #pragma unroll
     for (int j = 0; j < kGatherRecs; ++j) {
         const int64_t rid = wbase + 64 * j + lane;
         tt[j] = rid < VG ? tiles_touched[rid] : 0u;  // culled records touch no tile
-        s0[j] = rid < VG ? slot_base[rid] : 0u;
+        sa[j] = rid < VG ? slot_base[rid] : 0u;
     }
-#pragma unroll
-    for (int j = 0; j < kGatherRecs; ++j) w0[j] = tt[j] ? slot_bits[s0[j] >> 5] : 0u;
+    // the first three bit words of each record's range (a word past the range reads as zero)
 #pragma unroll
     for (int j = 0; j < kGatherRecs; ++j) {
-        const int64_t rid = wbase + 64 * j + lane;
+        const uint32_t nwords = tt[j] ? ((sa[j] + tt[j] - 1u) >> 5) - (sa[j] >> 5) + 1u : 0u;
+        b0[j] = nwords >= 1u ? slot_bits[sa[j] >> 5] : 0u;
+        b1[j] = nwords >= 2u ? slot_bits[(sa[j] >> 5) + 1u] : 0u;
+        b2[j] = nwords >= 3u ? slot_bits[(sa[j] >> 5) + 2u] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kGatherRecs; ++j) {
+        const int64_t run = wbase + 64 * j;
         const bool live = tt[j] != 0u;
-        bool reached = false;
-        float4 a[NQ];
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) a[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (live) {
-            const uint32_t sa = s0[j], sb = sa + tt[j];
-            for (uint32_t w = sa >> 5; w <= (sb - 1u) >> 5; ++w) {
-                uint32_t bits = w == (sa >> 5) ? w0[j] : slot_bits[w];
-                const uint32_t lo = sa > 32u * w ? sa - 32u * w : 0u;
-                const uint32_t hi = sb < 32u * w + 32u ? sb - 32u * w : 32u;
-                bits &= (hi >= 32u ? ~0u : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
-                while (bits) {
-                    const uint32_t slot = 32u * w + (uint32_t)__builtin_ctz(bits);
-                    bits &= bits - 1u;
-                    float4 p[NQ];
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) p[q] = partials[NQ * (int64_t)slot + q];
-                    reached = true;
-#pragma unroll
-                    for (int q = 0; q < NQ; ++q) {
-                        a[q].x += p[q].x;
-                        a[q].y += p[q].y;
-                        a[q].z += p[q].z;
-                        a[q].w += p[q].w;
-                    }
-                }
+        // word k of the range holds bits [lo - 32 k, lo - 32 k + tt) of the record's slots
+        const int32_t lo = (int32_t)(sa[j] & 31u), hi = lo + (int32_t)tt[j];
+        b0[j] &= bit_range_mask(lo, hi);
+        b1[j] &= bit_range_mask(lo - 32, hi - 32);
+        b2[j] &= bit_range_mask(lo - 64, hi - 64);
+        bool reached = (b0[j] | b1[j] | b2[j]) != 0u;
+        if (!reached && hi > 96) {  // a range of more than three words: read on until a set bit
+            for (uint32_t w = (sa[j] >> 5) + 3u; w <= (sa[j] + tt[j] - 1u) >> 5 && !reached; ++w) {
+                const int32_t k = (int32_t)(w - (sa[j] >> 5));
+                reached = (slot_bits[w] & bit_range_mask(lo - 32 * k, hi - 32 * k)) != 0u;
             }
         }
-        // live / reached masks of this run of 64 records
         const uint64_t live_mask = __ballot(live);
-        const uint64_t reached_mask = __ballot(reached);
-        const int64_t run = wbase + 64 * j;
+        uint64_t reached_mask = __ballot(reached);
         if (lane == 0 && run < VG) {
             rec_masks[2 * (run >> 6)] = live_mask;
             rec_masks[2 * (run >> 6) + 1] = reached_mask;
         }
-        if (reached) {
+        // the wave sums each reached record of this run
+        while (reached_mask) {
+            const int src = __builtin_ctzll(reached_mask);
+            reached_mask &= reached_mask - 1ull;
+            const uint32_t r_sa = __builtin_amdgcn_readlane(sa[j], src);
+            const uint32_t r_tt = __builtin_amdgcn_readlane(tt[j], src);
+            const uint32_t r_b0 = __builtin_amdgcn_readlane(b0[j], src);
+            const uint32_t r_b1 = __builtin_amdgcn_readlane(b1[j], src);
+            const uint32_t r_b2 = __builtin_amdgcn_readlane(b2[j], src);
+            const uint32_t r_lo = r_sa & 31u;
+            float4 acc[NQ];
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) gv_sums[NQ * rid + q] = a[q];
+            for (int q = 0; q < NQ; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (uint32_t o0 = 0; o0 < r_tt; o0 += 64u) {
+                const uint32_t o = o0 + (uint32_t)lane;  // slot offset within the record
+                bool set = false;
+                if (o < r_tt) {
+                    const uint32_t ob = r_lo + o, wi = ob >> 5;
+                    const uint32_t word = wi == 0u ? r_b0 : wi == 1u ? r_b1 : wi == 2u ? r_b2
+                                                                                      : slot_bits[(r_sa >> 5) + wi];
+                    set = ((word >> (ob & 31u)) & 1u) != 0u;
+                }
+                if (set) {
+                    const int64_t slot = (int64_t)(r_sa + o);
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q) {
+                        const float4 p = partials[NQ * slot + q];
+                        acc[q].x += p.x;
+                        acc[q].y += p.y;
+                        acc[q].z += p.z;
+                        acc[q].w += p.w;
+                    }
+                }
+            }
+            float* out = reinterpret_cast<float*>(gv_sums + NQ * (run + src));
+            const float x0[8] = {acc[0].x, acc[0].y, acc[0].z, acc[0].w, acc[1].x, acc[1].y, acc[1].z, acc[1].w};
+            const float s0 = wave_reduce8(x0, lane);
+            if ((lane & 7) == 0) out[lane >> 3] = s0;
+            if constexpr (NQ == 3) {
+                const float x1[8] = {acc[2].x, acc[2].y, acc[2].z, acc[2].w, 0.f, 0.f, 0.f, 0.f};
+                const float s1 = wave_reduce8(x1, lane);
+                if ((lane & 7) == 0 && lane < 32) out[8 + (lane >> 3)] = s1;
+            }
         }
     }
 }
