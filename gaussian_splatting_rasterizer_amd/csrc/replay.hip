@@ -34,7 +34,8 @@
 // k_gather_slots: per record (record order), the sums of the pairs the replay
 // wrote, stored only for records with such a pair; plus, per 64 records, a
 // mask of the records that are live (not culled) and one of those reached.
-// k_tokens: one thread per Gaussian, in float64
+// k_tokens: one thread per Gaussian; each view's terms in float32, their sums
+// over the views, 1/Q and the eigenvalues in float64:
 //     q_v = eps + W_v,  Q = eps + sum_v q_v,  gamma_v = q_v / Q
 //     b_mu = sum_v gamma_v J_v^T s_mu_v = (1/Q) sum_v J_v^T (conic_v U_mu_v)
 //     s_a  = (1/Q) sum_v (1 - o) U_a_v,   s_SH = (1/Q) sum_v M_color (B_v (x) U_c_v)
@@ -145,7 +146,9 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 const bool sat = pass && tT < kTMin;
                 const bool contrib = pass && !sat;
                 done = done || sat;
-                if (__ballot(contrib) != 0ull) {
+                // some lane of the wave contributes or saturates at every listed entry (a wave's list ends
+                // at its last such entry), so the partials are formed without testing for a contribution
+                {
                     const float cr = b.z, cg = b.w, cbl = s2[j];
                     const float w = contrib ? alpha * Tr : 0.0f;
                     const float x0 = cr * w, x1 = cg * w, x2 = cbl * w;
@@ -177,7 +180,6 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                         Tr = tT;
                     }
                 }
-                if (__ballot(!done) == 0ull) break;
             }
         }
         __syncthreads();
@@ -415,8 +417,8 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
     const int64_t g = g0 + threadIdx.x;
     float* z = s_tok + threadIdx.x * DT;
     if (g < G) {
-        const double mu[3] = {means[3 * g], means[3 * g + 1], means[3 * g + 2]};
-        const double one_minus_o = 1.0 - (double)opac[g];
+        const float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
+        const float one_minus_o = 1.0f - opac[g];
         double Q = eps;
         double bnum[3] = {0.0, 0.0, 0.0};
         double anum = 0.0;
@@ -468,47 +470,42 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
                     n1 = gv_sums[2 * rid + 1];
                 }
             }
-            const double q = eps + (double)p0.x;
-            Q += q;
-            const double smx = p0.z, smy = p0.w;  // conic * U_mu
+            // this view's terms in float32 (each within a few ulp), summed over the views in float64
+            const float q = (float)eps + p0.x;
+            Q += (double)q;
+            const float smx = p0.z, smy = p0.w;  // conic * U_mu
 
             const float* cam = cams.c[v];
-            double R[9];
+            const float R0 = cam[0], R1 = cam[1], R2 = cam[2], R3 = cam[3], R4 = cam[4], R5 = cam[5], R6 = cam[6],
+                        R7 = cam[7], R8 = cam[8];
+            const float t0 = cam[9], t1 = cam[10], t2 = cam[11];
+            const float fx = cam[12], fy = cam[13];
+            const float tcx = R0 * mx + R1 * my + R2 * mz + t0;
+            const float tcy = R3 * mx + R4 * my + R5 * mz + t1;
+            const float tcz = R6 * mx + R7 * my + R8 * mz + t2;
+            const float iz = __builtin_amdgcn_rcpf(tcz);  // tcz >= the near plane for a live record
+            const float jp00 = fx * iz, jp02 = -fx * tcx * iz * iz;
+            const float jp11 = fy * iz, jp12 = -fy * tcy * iz * iz;
+            const float J0[3] = {jp00 * R0 + jp02 * R6, jp00 * R1 + jp02 * R7, jp00 * R2 + jp02 * R8};
+            const float J1[3] = {jp11 * R3 + jp12 * R6, jp11 * R4 + jp12 * R7, jp11 * R5 + jp12 * R8};
 #pragma unroll
-            for (int k = 0; k < 9; ++k) R[k] = cam[k];
-            const double t0 = cam[9], t1 = cam[10], t2 = cam[11];
-            const double fx = cam[12], fy = cam[13];
-            const double tcx = R[0] * mu[0] + R[1] * mu[1] + R[2] * mu[2] + t0;
-            const double tcy = R[3] * mu[0] + R[4] * mu[1] + R[5] * mu[2] + t1;
-            const double tcz = R[6] * mu[0] + R[7] * mu[1] + R[8] * mu[2] + t2;
-            const double iz = 1.0 / tcz;
-            const double jp00 = fx * iz, jp02 = -fx * tcx * iz * iz;
-            const double jp11 = fy * iz, jp12 = -fy * tcy * iz * iz;
-            double J0[3], J1[3];
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                J0[k] = jp00 * R[k] + jp02 * R[6 + k];
-                J1[k] = jp11 * R[3 + k] + jp12 * R[6 + k];
-            }
-#pragma unroll
-            for (int k = 0; k < 3; ++k) bnum[k] += J0[k] * smx + J1[k] * smy;
-            anum += one_minus_o * (double)p0.y;
-            Anum[0] += q * (J0[0] * J0[0] + J1[0] * J1[0]);
-            Anum[1] += q * (J0[0] * J0[1] + J1[0] * J1[1]);
-            Anum[2] += q * (J0[0] * J0[2] + J1[0] * J1[2]);
-            Anum[3] += q * (J0[1] * J0[1] + J1[1] * J1[1]);
-            Anum[4] += q * (J0[1] * J0[2] + J1[1] * J1[2]);
-            Anum[5] += q * (J0[2] * J0[2] + J1[2] * J1[2]);
+            for (int k = 0; k < 3; ++k) bnum[k] += (double)(J0[k] * smx + J1[k] * smy);
+            anum += (double)(one_minus_o * p0.y);
+            Anum[0] += (double)(q * (J0[0] * J0[0] + J1[0] * J1[0]));
+            Anum[1] += (double)(q * (J0[0] * J0[1] + J1[0] * J1[1]));
+            Anum[2] += (double)(q * (J0[0] * J0[2] + J1[0] * J1[2]));
+            Anum[3] += (double)(q * (J0[1] * J0[1] + J1[1] * J1[1]));
+            Anum[4] += (double)(q * (J0[1] * J0[2] + J1[1] * J1[2]));
+            Anum[5] += (double)(q * (J0[2] * J0[2] + J1[2] * J1[2]));
 
             if (reached) {
-                // SH basis along the view direction times the masked colour sums
-                const double ccx = -(R[0] * t0 + R[3] * t1 + R[6] * t2);
-                const double ccy = -(R[1] * t0 + R[4] * t1 + R[7] * t2);
-                const double ccz = -(R[2] * t0 + R[5] * t1 + R[8] * t2);
-                const double dx = mu[0] - ccx, dy = mu[1] - ccy, dz = mu[2] - ccz;
-                const double il = 1.0 / sqrt(dx * dx + dy * dy + dz * dz);
+                // SH basis along the view direction (from the camera centre -R^T t) times the masked colour sums
+                const float dx = mx + (R0 * t0 + R3 * t1 + R6 * t2);
+                const float dy = my + (R1 * t0 + R4 * t1 + R7 * t2);
+                const float dz = mz + (R2 * t0 + R5 * t1 + R8 * t2);
+                const float il = __builtin_amdgcn_rsqf(dx * dx + dy * dy + dz * dz);
                 float B[D];
-                sh_basis_f32((float)(dx * il), (float)(dy * il), (float)(dz * il), D, B);
+                sh_basis_f32(dx * il, dy * il, dz * il, D, B);
 #pragma unroll
                 for (int k = 0; k < D; ++k) {
                     shnum[3 * k] += B[k] * p1.x;
