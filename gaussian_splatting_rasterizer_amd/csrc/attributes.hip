@@ -16,7 +16,8 @@
 //
 // Both walk, per wave, only the entries at which the render flagged an event
 // for that wave (every other entry changes no pixel of the wave), exactly as
-// the score replay does.  The composite keeps NC channel accumulators per
+// the score replay does; a wave's list ends at its last event, so the walk
+// does not test for the wave being done.  The composite keeps NC channel accumulators per
 // pixel (channel slices of at most 16 per launch); the scatter reduces eight
 // channels per pass over the wave (the replay's reduce-scatter), stores one
 // 32-byte partial per event pair at the pair's slot, and the slot gather and a
@@ -107,7 +108,6 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
 #pragma unroll
                 for (int c = 0; c < NC; ++c) acc[c] = __builtin_fmaf(w, sf[j][c], acc[c]);
                 Tr = contrib ? tT : Tr;
-                if (__ballot(!done) == 0ull) break;
             }
         }
         __syncthreads();
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
                 const bool sat = pass && tT < kTMin;
                 const bool contrib = pass && !sat;
                 done = done || sat;
-                if (__ballot(contrib) != 0ull) {
+                {  // every listed entry has a contribution or saturation in some lane of the wave
                     const float w = contrib ? alpha * Tr : 0.0f;
                     float x[8];
 #pragma unroll
@@ -233,7 +233,6 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
                     if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
                     Tr = contrib ? tT : Tr;
                 }
-                if (__ballot(!done) == 0ull) break;
             }
         }
         __syncthreads();
@@ -400,7 +399,6 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
                     }
                 }
                 Tr = contrib ? tT : Tr;
-                if (__ballot(!done) == 0ull) break;
             }
         }
         __syncthreads();

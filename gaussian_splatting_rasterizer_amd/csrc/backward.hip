@@ -26,7 +26,9 @@
 // The wave reduces the nine values (reduce-scatter of eight plus one full
 // sum), the four waves meet in LDS and one 48-byte partial per event entry is
 // stored with plain stores at the pair's slot; the slot's bit is set in
-// slot_bits.  The slot gather then sums each record's partials in slot order.
+// slot_bits.  The slot gather then sums each record's partials.  Every listed
+// entry has a contribution or a saturation in some lane of the wave and a
+// wave's list ends at its last one, so the walk tests for neither.
 //
 // k_grads: after the slot gather (per record, the sums of its flagged slots),
 // one thread per Gaussian loops over the views in float64: projected centre ->
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                 const bool sat = pass && tT < kTMin;
                 const bool contrib = pass && !sat;
                 done = done || sat;
-                if (__ballot(contrib) != 0ull) {
+                {  // every listed entry has a contribution or saturation in some lane of the wave
                     const float cr = b.z, cg = b.w, cbl = s2[j];
                     const float w = contrib ? alpha * Tr : 0.0f;
                     float n0 = h0, n1 = h1, n2 = h2, k0 = c0, k1 = c1, k2 = c2;
@@ -177,7 +179,6 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                         Tr = tT;
                     }
                 }
-                if (__ballot(!done) == 0ull) break;
             }
         }
         __syncthreads();

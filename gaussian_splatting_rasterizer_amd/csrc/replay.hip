@@ -400,8 +400,10 @@ hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, int nq, hipS
     return hipGetLastError();
 }
 
-// One thread per Gaussian: cross-view aggregation and the token, staged through
-// LDS so that the block's tokens leave as one coalesced span.
+// One thread per Gaussian: cross-view aggregation and the token.  Each wave
+// stages the tokens of half its lanes at a time in LDS and stores them as one
+// coalesced span (half a wave's tokens take 32 * DT floats, so the staging
+// leaves room for the waves the registers allow).
 constexpr int kTokThreads = 128;
 
 template <int D>
@@ -412,10 +414,10 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
                                                         float* __restrict__ tokens) {
 #pragma clang fp contract(fast)
     constexpr int DT = 9 + 3 * D;
-    __shared__ __align__(16) float s_tok[kTokThreads * DT];
+    __shared__ __align__(16) float s_tok[kTokThreads / 64][32 * DT];
     const int64_t g0 = (int64_t)blockIdx.x * kTokThreads;
     const int64_t g = g0 + threadIdx.x;
-    float* z = s_tok + threadIdx.x * DT;
+    float z[DT];
     if (g < G) {
         const float mx = means[3 * g], my = means[3 * g + 1], mz = means[3 * g + 2];
         const float one_minus_o = 1.0f - opac[g];
@@ -541,17 +543,36 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
         z[7 + 3 * D] = (float)(ev[2] * itr);
         z[8 + 3 * D] = logf((float)(tr + eps));
     }
-    __syncthreads();
-    // the block's span starts g0 * DT floats (a multiple of 4) into the output: float4 stores when the
-    // caller's array is 16-byte aligned
-    static_assert((kTokThreads * DT) % 4 == 0, "whole float4 per block");
-    const int nvalid = (int)(G - g0 < kTokThreads ? G - g0 : kTokThreads) * DT;
-    float* out = tokens + g0 * DT;
-    const int n4 = (reinterpret_cast<uintptr_t>(tokens) & 15u) == 0u ? nvalid >> 2 : 0;
-    const float4* s4 = reinterpret_cast<const float4*>(s_tok);
-    float4* o4 = reinterpret_cast<float4*>(out);
-    for (int i = threadIdx.x; i < n4; i += kTokThreads) o4[i] = s4[i];
-    for (int i = 4 * n4 + threadIdx.x; i < nvalid; i += kTokThreads) out[i] = s_tok[i];
+    // copy-out: lanes 0-31, then lanes 32-63, stage their tokens and the wave stores them as one span; a
+    // half's span starts a multiple of 32 * DT floats (a multiple of 4) into the output, so it leaves in float4
+    // stores when the caller's array is 16-byte aligned
+    static_assert((32 * DT) % 4 == 0, "whole float4 per half wave");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float* st = s_tok[wave];
+    const bool aligned = (reinterpret_cast<uintptr_t>(tokens) & 15u) == 0u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t gh = g0 + 64 * wave + 32 * h;  // first Gaussian of this half
+        if ((lane >> 5) == h && g < G) {
+#pragma unroll
+            for (int k = 0; k < DT; ++k) st[(lane & 31) * DT + k] = z[k];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int64_t left = G - gh;
+        const int nvalid = left <= 0 ? 0 : (int)(left < 32 ? left : 32) * DT;
+        float* out = tokens + gh * DT;
+        const int n4 = aligned ? nvalid >> 2 : 0;
+        const float4* s4 = reinterpret_cast<const float4*>(st);
+        float4* o4 = reinterpret_cast<float4*>(out);
+        for (int i = lane; i < n4; i += 64) o4[i] = s4[i];
+        for (int i = 4 * n4 + lane; i < nvalid; i += 64) out[i] = st[i];
+        // every lane has read the staged half before the next one overwrites it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 }
 
 hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws, float eps,
