@@ -79,6 +79,7 @@ def _load():
         lib.orc_tile_list_scan.argtypes = [P, I64, P]
         lib.orc_select.argtypes = [P, P, I32]
         lib.orc_render_tiles.argtypes = [P, P, I64, P, F32, F32, P, P, P, P]
+        lib.orc_pixel_work.argtypes = [P, P, I64, P]
         lib.orc_get_acc.argtypes = [P, P]
         lib.orc_tokens.argtypes = [P, F64, F64, P, P, P]
         lib.orc_eig3.argtypes = [P, P]
@@ -251,6 +252,20 @@ class OracleScene:
                                   _ptr(obs) if obs is not None else None, eps, den_min,
                                   _ptr(color), _ptr(T), _ptr(n), _ptr(T64))
         return color, T, n, T64
+
+    def pixel_work(self, tiles=None) -> np.ndarray:
+        """Work counts of the render pass per pixel of the chosen tiles (all by default):
+        [V,H,W,2] uint32 = (list entries examined up to and including the one at which the
+        pixel stopped, or the whole list; those of them past the distance cut).  Pixels
+        outside the chosen tiles hold 0xffffffff."""
+        if self.n_pairs is None:
+            self.build_lists()
+        if tiles is None:
+            tiles = np.arange(self.V * self.T, dtype=np.int64)
+        tiles = np.ascontiguousarray(tiles, dtype=np.int64)
+        out = np.full((self.V, self.H, self.W, 2), 0xFFFFFFFF, dtype=np.uint32)
+        self.lib.orc_pixel_work(self.handle, _ptr(tiles), tiles.size, _ptr(out))
+        return out
 
     def acc(self) -> np.ndarray:
         na = NACC_FIXED + 6 * self.d

@@ -774,8 +774,12 @@ static void add(double* a, double x)
  * (distance cut, alpha clamp and floor, transmittance stop), float64 values.
  * Fills the accepted contributions in front-to-back order and returns their
  * count; C gets the colour including the background. */
-static int composite_pixel(const scene* s, int v, int x, int y, const int32_t* list, int64_t L, contrib* cl,
-                           double C[3], float* T32_out, double* T64_out)
+/* Front-to-back composite of one pixel over its tile's list.  With work != NULL
+ * it also counts the pass's work: work[0] = list entries examined up to and
+ * including the one at which the pixel stopped (the whole list if it never
+ * did), work[1] = those of them past the distance cut. */
+static int composite_pixel_counted(const scene* s, int v, int x, int y, const int32_t* list, int64_t L,
+                                   contrib* cl, double C[3], float* T32_out, double* T64_out, uint32_t work[2])
 {
     float px = (float)x + 0.5f, py = (float)y + 0.5f;
     double pxd = x + 0.5, pyd = y + 0.5;
@@ -788,7 +792,9 @@ static int composite_pixel(const scene* s, int v, int x, int y, const int32_t* l
         const rec32* r = &s->r32[(int64_t)v * s->G + g];
         float dx = px - r->mx, dy = py - r->my;
         float e = fmaf(dx, fmaf(r->qa, dx, r->qb * dy), (r->qc * dy) * dy);
+        if (work) work[0] = (uint32_t)(k + 1);
         if (!(e >= E_CUTOFF_F)) continue;
+        if (work) work[1]++;
         float aG = r->opac * orc_exp2f(e);
         int clamped = !(aG < ALPHA_MAX_F);
         float a32 = clamped ? ALPHA_MAX_F : aG;
@@ -815,6 +821,50 @@ static int composite_pixel(const scene* s, int v, int x, int y, const int32_t* l
     *T32_out = T32;
     *T64_out = T64;
     return n;
+}
+
+static int composite_pixel(const scene* s, int v, int x, int y, const int32_t* list, int64_t L, contrib* cl,
+                           double C[3], float* T32_out, double* T64_out)
+{
+    return composite_pixel_counted(s, v, x, y, list, L, cl, C, T32_out, T64_out, NULL);
+}
+
+/* Work counts of the render pass for every pixel of the given tiles, written at
+ * out[2 * pix] (entries examined until the pixel stopped) and out[2 * pix + 1]
+ * (those past the distance cut). */
+void orc_pixel_work(void* p, const int64_t* tiles, int64_t n_tiles, uint32_t* out)
+{
+    scene* s = (scene*)p;
+    const int T = s->TX * s->TY;
+    int64_t maxlen = 0;
+    for (int64_t i = 0; i < (int64_t)s->V * T; ++i)
+        if (s->starts[i + 1] - s->starts[i] > maxlen) maxlen = s->starts[i + 1] - s->starts[i];
+#pragma omp parallel
+    {
+        contrib* cl = (contrib*)malloc(sizeof(contrib) * (size_t)maxlen + 1);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t it = 0; it < n_tiles; ++it) {
+            int64_t tile = tiles[it];
+            int v = (int)(tile / T), t = (int)(tile % T);
+            int tx = t % s->TX, ty = t / s->TX;
+            const int32_t* list = s->ids + s->starts[tile];
+            int64_t L = s->starts[tile + 1] - s->starts[tile];
+            for (int yy = 0; yy < TILE; ++yy)
+                for (int xx = 0; xx < TILE; ++xx) {
+                    int x = tx * TILE + xx, y = ty * TILE + yy;
+                    if (x >= s->W || y >= s->H) continue;
+                    double C[3];
+                    float T32;
+                    double T64;
+                    uint32_t work[2] = {0u, 0u};
+                    composite_pixel_counted(s, v, x, y, list, L, cl, C, &T32, &T64, work);
+                    int64_t pix = ((int64_t)v * s->H + y) * s->W + x;
+                    out[2 * pix] = work[0];
+                    out[2 * pix + 1] = work[1];
+                }
+        }
+        free(cl);
+    }
 }
 
 /* Render (and, with obs != NULL, replay) the pixels of the given tiles.
