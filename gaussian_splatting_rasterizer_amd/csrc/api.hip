@@ -579,7 +579,9 @@ gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes
             const size_t pixels = (size_t)s.V * s.W * s.H;
             if (ctx->state < kRendered) return fail(GS_ERR_STATE, "pixel stats exist after gs_render");
             if (bytes < 8 * pixels) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
-            e = hipMemcpyAsync(dst, ws.pixel_stats, 8 * pixels, hipMemcpyDeviceToDevice, stream);
+            // counted by a statistics pass over the same lists with the render's decisions
+            e = launch_render_stats(s, ws, ctx->sorted_g, stream);
+            if (e == hipSuccess) e = hipMemcpyAsync(dst, ws.pixel_stats, 8 * pixels, hipMemcpyDeviceToDevice, stream);
             break;
         }
         default:

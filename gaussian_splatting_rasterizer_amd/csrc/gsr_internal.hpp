@@ -166,6 +166,8 @@ hipError_t launch_tile_order(const uint32_t* work, int64_t n_tiles, uint32_t* or
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
                          const float bg[3], float* color, float* T_final, int32_t* n_contrib, hipStream_t st,
                          bool prev_order_valid);  // tile_order holds an order a previous render measured
+// per-pixel work counts of the render's traversal (same decisions) into ws.pixel_stats
+hipError_t launch_render_stats(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, hipStream_t st);
 hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, const float* observed,
                          float eps, float den_min, hipStream_t st);
 // per record, the sums of the NQ-float4 partials of the slots flagged in slot_bits, plus the

@@ -18,12 +18,19 @@
 // For every entry it processes, the render also leaves one byte whose bit w
 // says whether any pixel of wave w contributed or saturated there: the replay
 // walks only those entries, since at every other one no pixel's state changes.
+//
+// The statistics variant (STATS) evaluates every list entry, takes the same
+// decisions, and writes only, per pixel, the list entries examined up to the
+// one at which the pixel stopped and how many of them passed the distance cut
+// (the plain algorithm's work counts); it runs when those counts are exported,
+// so the render itself carries no bookkeeping for them.
 #include "gsr_internal.hpp"
 
 namespace gsr {
 
 constexpr int kRenderBatch = 256;
 
+template <bool STATS>
 __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
                                                 const float2* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
@@ -34,9 +41,11 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                                                 int64_t n_slot_words, uint32_t* __restrict__ tile_work,
                                                 const uint32_t* __restrict__ prev_order) {
     // clear the replay's written-slot bits (a grid-stride share per block)
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slot_words;
-         i += (int64_t)gridDim.x * blockDim.x)
-        slot_bits[i] = 0u;
+    if constexpr (!STATS) {
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slot_words;
+             i += (int64_t)gridDim.x * blockDim.x)
+            slot_bits[i] = 0u;
+    }
     __shared__ float4 s0[kRenderBatch];   // {mx, my, qa, qb}
     __shared__ float4 s1[kRenderBatch];   // {qc, opacity, colour r, colour g}
     __shared__ float s2[kRenderBatch];    // colour b
@@ -75,7 +84,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     for (;; base += kRenderBatch) {
         const int live = __syncthreads_count(!done);
         // the previous batch's event bits (every wave finished it at the barrier above)
-        if ((int)threadIdx.x < prev_cnt)
+        if (!STATS && (int)threadIdx.x < prev_cnt)
             events[prev_base + threadIdx.x] = (uint8_t)(s_ev[0][threadIdx.x] | (s_ev[1][threadIdx.x] << 1) |
                                                         (s_ev[2][threadIdx.x] << 2) | (s_ev[3][threadIdx.x] << 3));
         if (base >= rg.y || live == 0) break;
@@ -101,8 +110,11 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                 const int j = c + lane;
                 bool hit = false;
                 if (j < cnt) {
+                    // the statistics pass evaluates every entry, so its distance-cut count is the plain
+                    // algorithm's (the skipped entries fail the alpha test at every pixel of the quadrant, so
+                    // the decisions are the same)
                     const float4 bx = sbox[j];
-                    hit = bx.x <= qx1 && bx.y >= qx0 && bx.z <= qy1 && bx.w >= qy0;
+                    hit = STATS || (bx.x <= qx1 && bx.y >= qx0 && bx.z <= qy1 && bx.w >= qy0);
                 }
                 const uint64_t m = __ballot(hit);
                 if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
@@ -125,25 +137,35 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                 const float tT = Tr * (1.0f - alpha);
                 const bool sat = pass && tT < kTMin;
                 const bool contrib = pass && !sat;
-                n_near += near ? 1u : 0u;
-                if (sat) {
-                    done = true;
-                    stop = base + (uint32_t)j;
+                if constexpr (STATS) {
+                    n_near += near ? 1u : 0u;
+                    if (sat) stop = base + (uint32_t)j;
                 }
+                done = done || sat;
                 if (contrib) {
-                    const float w = alpha * Tr;
-                    kahan_add(h0, c0, b.z * w);
-                    kahan_add(h1, c1, b.w * w);
-                    kahan_add(h2, c2, s2[j] * w);
+                    if constexpr (!STATS) {
+                        const float w = alpha * Tr;
+                        kahan_add(h0, c0, b.z * w);
+                        kahan_add(h1, c1, b.w * w);
+                        kahan_add(h2, c2, s2[j] * w);
+                        ++n;
+                    }
                     Tr = tT;
-                    ++n;
                 }
-                if (pass) s_ev[wave][j] = 1;  // contributed or saturated (every such lane writes the same byte)
+                if (!STATS && pass) s_ev[wave][j] = 1;  // contributed or saturated (every such lane writes the same byte)
                 if (__ballot(!done) == 0ull) break;
             }
         }
         prev_base = base;
         prev_cnt = cnt;
+    }
+    if constexpr (STATS) {
+        if (inside) {
+            const int64_t pix = ((int64_t)v * H + pyi) * W + pxi;
+            pixel_stats[pix] =
+                make_uint2(stop != 0xffffffffu ? stop - rg.x + 1u : (rg.y > rg.x ? rg.y - rg.x : 0u), n_near);
+        }
+        return;
     }
     // the work of this tile, for the order of the traversals that follow: entries processed until done
     if (threadIdx.x == 0) tile_work[tile] = rg.y > rg.x ? (base < rg.y ? base : rg.y) - rg.x : 0u;
@@ -161,7 +183,6 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     if (T_out) T_out[pix] = Tr;
     if (n_out) n_out[pix] = n;
     pixel[pix] = make_float4(o0, o1, o2, Tr);
-    pixel_stats[pix] = make_uint2(stop != 0xffffffffu ? stop - rg.x + 1u : (rg.y > rg.x ? rg.y - rg.x : 0u), n_near);
 }
 
 hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, uint64_t n_pairs,
@@ -169,13 +190,22 @@ hipError_t launch_render(const Sizes& s, const Workspace& ws, const uint32_t* so
                          bool prev_order_valid) {
     const int64_t tiles = (int64_t)s.V * s.T;
     if (tiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_render, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1,
-                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib, ws.pixel,
-                       ws.pixel_stats, ws.events, ws.slot_bits, (int64_t)((n_pairs + 31) / 32), ws.tile_work,
+    hipLaunchKernelGGL(k_render<false>, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0,
+                       ws.rec1, ws.rec2, s.G, s.T, s.TX, s.W, s.H, bg[0], bg[1], bg[2], color, T_final, n_contrib,
+                       ws.pixel, nullptr, ws.events, ws.slot_bits, (int64_t)((n_pairs + 31) / 32), ws.tile_work,
                        prev_order_valid ? ws.tile_order : nullptr);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_tile_order(ws.tile_work, tiles, ws.tile_order, st);
+}
+
+hipError_t launch_render_stats(const Sizes& s, const Workspace& ws, const uint32_t* sorted_g, hipStream_t st) {
+    const int64_t tiles = (int64_t)s.V * s.T;
+    if (tiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_render<true>, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0,
+                       ws.rec1, ws.rec2, s.G, s.T, s.TX, s.W, s.H, 0.0f, 0.0f, 0.0f, nullptr, nullptr, nullptr,
+                       nullptr, ws.pixel_stats, nullptr, nullptr, (int64_t)0, nullptr, nullptr);
+    return hipGetLastError();
 }
 
 }  // namespace gsr

@@ -265,7 +265,9 @@ GSR_API gs_status gs_debug_exp2(const float* in, float* out, int64_t n, hipStrea
  *   GS_EXPORT_RANGES    after gs_bin_sort: [n_views*tiles] x 2 uint32 [start, end)
  *   GS_EXPORT_PIXEL_STATS after gs_render: [n_views*height*width] x 2 uint32:
  *       list entries evaluated before the pixel stopped, and how many of those
- *       passed the distance cut (exponent >= -8) -- the work counts of the pass
+ *       passed the distance cut (exponent >= -8) -- the work counts of the pass,
+ *       counted on export by a pass over the same lists with the render's
+ *       decisions (the render itself keeps no such counts)
  */
 typedef enum {
     GS_EXPORT_RECORDS = 1,

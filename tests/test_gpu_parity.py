@@ -47,9 +47,10 @@ def _run_gpu(sc, obs, antialiased=False):
     ranges = r.export(b.GS_EXPORT_RANGES).cpu().numpy()
     color, T, n = r.render()
     tok = r.score_replay(torch.from_numpy(obs).cuda())
+    work = r.export(b.GS_EXPORT_PIXEL_STATS).cpu().numpy().view(np.uint32)
     torch.cuda.synchronize()
     out = dict(rec=rec, keys=keys, ids=ids, ranges=ranges, n_pairs=r.n_pairs, color=color.cpu().numpy(),
-               T=T.cpu().numpy(), n=n.cpu().numpy(), tokens=tok.cpu().numpy())
+               T=T.cpu().numpy(), n=n.cpu().numpy(), tokens=tok.cpu().numpy(), work=work)
     r.close()
     return out
 
@@ -94,6 +95,7 @@ def _case(name):
         starts, ids = o.lists()
         ref["starts"], ref["ids"] = starts, ids
         ref["rec32"] = o.records32()
+        ref["work"] = o.pixel_work()
         gpu = _run_gpu(sc, obs, antialiased=_aa(name))
         _CACHE[name] = (sc, obs, ref, gpu)
     return _CACHE[name]
@@ -181,6 +183,15 @@ def test_tile_lists_bit_exact(name):
     assert np.array_equal(rg[nonempty, 0], starts[:-1][nonempty])
     assert np.array_equal(rg[nonempty, 1], starts[1:][nonempty])
     assert np.all(rg[~nonempty, 0] == rg[~nonempty, 1])
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_pixel_work_bit_exact(name):
+    """The exported per-pixel work counts (entries examined until the pixel stopped, and those
+    past the distance cut) equal the oracle's, pixel for pixel."""
+    sc, obs, ref, gpu = _case(name)
+    assert gpu["work"].shape == ref["work"].shape
+    assert np.array_equal(gpu["work"], ref["work"])
 
 
 # The needle-like stress scene has conics with condition numbers up to ~7e4; the
