@@ -623,9 +623,13 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
 // form one contiguous span of the output; each thread takes every 256th pair of
 // the span, finds its record by binary search over the records' offsets in LDS,
 // and writes the pair's global tile id and Gaussian: coalesced stores whatever
-// the records' tile counts are.  With PASSES > 0 it also counts the digits of
-// the tile ids for the tile sort (LDS histogram, then atomics into the shared
-// rows, which k_ranges_init zeroed).
+// the records' tile counts are.  Per record the staging splits the record index
+// into view and Gaussian and keeps the global id of the rectangle's first tile,
+// its width and the width's reciprocal, so a pair's row and column in the
+// rectangle take a float estimate and an exact integer correction instead of
+// two integer divisions.  With PASSES > 0 it also counts the digits of the tile
+// ids for the tile sort (LDS histogram, then atomics into the shared rows,
+// which k_ranges_init zeroed).
 constexpr int kEmitRecs = 1024;
 
 template <int PASSES>
@@ -636,8 +640,10 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
                                               int TX, uint32_t* __restrict__ pkey, uint32_t* __restrict__ pair_g,
                                               RadixDigits rd, int packed_gbits, uint32_t* __restrict__ part) {
     __shared__ uint32_t s_off[kEmitRecs];
-    __shared__ uint32_t s_rid[kEmitRecs];
-    __shared__ uint2 s_rect[kEmitRecs];
+    __shared__ uint32_t s_g[kEmitRecs];     // Gaussian index
+    __shared__ uint32_t s_key0[kEmitRecs];  // global tile id of the rectangle's first tile
+    __shared__ uint32_t s_wx[kEmitRecs];    // rectangle width in tiles
+    __shared__ float s_inv[kEmitRecs];      // its reciprocal (an estimate, corrected per pair)
     __shared__ uint32_t h[PASSES > 0 ? PASSES * kMaxBins : 1];
     __shared__ uint32_t s_end;
     const int64_t k0 = (int64_t)blockIdx.x * kEmitRecs;
@@ -645,16 +651,24 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
     for (int i = threadIdx.x; i < kEmitRecs; i += 256) {
         const int64_t k = k0 + i;
         if (k < VG) {
-            s_off[i] = offsets[k];
-            s_rid[i] = rid_sorted[k];
+            const uint32_t off = offsets[k];
+            uint2 r;
             if (rect_sorted) {
-                s_rect[i] = rect_sorted[k];
-                if (i == last) s_end = offsets[k] + tt_sorted[k];
+                r = rect_sorted[k];
+                if (i == last) s_end = off + tt_sorted[k];
             } else {  // packed rectangles in tt_sorted
                 const uint32_t q = tt_sorted[k];
-                s_rect[i] = unpack_rect(q);
-                if (i == last) s_end = offsets[k] + scan_item(q, true);
+                r = unpack_rect(q);
+                if (i == last) s_end = off + scan_item(q, true);
             }
+            const uint32_t rid = rid_sorted[k];
+            const uint32_t v = rid / G;
+            const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, wx = (r.y & 0xffffu) - x0;
+            s_off[i] = off;
+            s_g[i] = rid - v * G;
+            s_key0[i] = v * (uint32_t)T + y0 * (uint32_t)TX + x0;
+            s_wx[i] = wx;
+            s_inv[i] = wx ? __builtin_amdgcn_rcpf((float)wx) : 0.0f;  // a record with pairs has wx >= 1
         }
     }
     if (PASSES > 0)
@@ -668,18 +682,26 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
             if (s_off[mid] <= p) lo = mid;
             else hi = mid - 1;
         }
-        const uint32_t j = p - s_off[lo];
-        const uint32_t rid = s_rid[lo];
-        const uint2 r = s_rect[lo];
-        const uint32_t x0 = r.x & 0xffffu, y0 = r.x >> 16, x1 = r.y & 0xffffu;
-        const uint32_t wx = x1 - x0;
-        const uint32_t v = rid / G;
-        const uint32_t key = v * (uint32_t)T + (y0 + j / wx) * (uint32_t)TX + x0 + j % wx;
+        const uint32_t j = p - s_off[lo];  // the pair's index in its rectangle, row-major
+        const uint32_t wx = s_wx[lo];
+        // row = floor(j / wx) from the float estimate (off by a few at most), made exact by the remainder
+        uint32_t row = (uint32_t)((float)j * s_inv[lo]);
+        int32_t col = (int32_t)(j - row * wx);
+        while (col < 0) {
+            --row;
+            col += (int32_t)wx;
+        }
+        while (col >= (int32_t)wx) {
+            ++row;
+            col -= (int32_t)wx;
+        }
+        const uint32_t key = s_key0[lo] + row * (uint32_t)TX + (uint32_t)col;
+        const uint32_t g = s_g[lo];
         if (packed_gbits > 0) {
-            pkey[p] = (key << packed_gbits) | (rid - v * G);
+            pkey[p] = (key << packed_gbits) | g;
         } else {
             pkey[p] = key;
-            pair_g[p] = rid - v * G;
+            pair_g[p] = g;
         }
 #pragma unroll
         for (int q = 0; q < PASSES; ++q) {

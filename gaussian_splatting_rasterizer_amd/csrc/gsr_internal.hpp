@@ -45,7 +45,7 @@ struct Workspace {
     uint2* ranges;         // per tile [start, end)
     uint32_t* tile_work;   // per tile: list entries the render processed before its pixels were done
     uint32_t* tile_order;  // tiles by decreasing tile_work: the order the traversals after the render take them
-    float4* partials;      // per slot, score replay (2 float4): {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), n_pix};
+    float4* partials;      // per slot, score replay (2 float4): {W, U_a, conic * U_mu (2)}, {masked U_rgb (3), 0};
                            // backward (3 float4): {U, U_x, U_y, U_xx}, {U_xy, U_yy, masked V_rg}, {masked V_b, 0, 0, 0}
     float4* gv_sums;       // per reached record: the sums of the same layout (2 or 3 float4)
     uint64_t* rec_masks;   // per 64 records: {live mask, reached mask}

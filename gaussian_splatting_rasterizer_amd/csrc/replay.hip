@@ -12,8 +12,8 @@
 //     rho = <r, c - C+>,  r = C_hat - C_obs            (residual-suffix contrast)
 //     w   = T alpha                                   (visibility weight)
 //     M   = [o G < 0.99] and [T (1 - alpha) >= den_min]   (mask)
-// and the eight per-pixel partials
-//     W += w, U_a += M w rho, U_mu += M w rho (p - mu), U_c += w r, n_pix += 1;
+// and the seven per-pixel partials (the eighth slot of the reduction stays zero)
+//     W += w, U_a += M w rho, U_mu += M w rho (p - mu), U_c += w r;
 // the pair's partial then gets the conic applied to U_mu and the colour clamp
 // mask applied to U_c (both constant over the pair).
 // These suffice for every score block: with M set, alpha = o G, so
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                     const float rS = __builtin_fmaf(r2, S2, __builtin_fmaf(r1, S1, r0 * S0));
                     const float rho = __builtin_fmaf(-rS, inv_den, rc);
                     const float mw = (contrib && !clamped && tT >= den_min) ? w * rho : 0.0f;
-                    const float x[8] = {w, mw, mw * dx, mw * dy, w * r0, w * r1, w * r2, contrib ? 1.0f : 0.0f};
+                    const float x[8] = {w, mw, mw * dx, mw * dy, w * r0, w * r1, w * r2, 0.0f};
                     const float red = wave_reduce8(x, lane);
                     if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
                     if (contrib) {
@@ -199,7 +199,10 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             // per pair: the conic applied to U_mu (undoing the exponent scaling of the
             // stored coefficients) and the colour clamp mask applied to U_c
             if (h == 0) {
-                const float ca = s0[j].z / kNegHalfLog2e, cb = s0[j].w / kNegLog2e, cc = s1[j].x / kNegHalfLog2e;
+                // (the scale back is a product with the constants' reciprocals: these values take no decision)
+                constexpr float kInvNegHalfLog2e = 1.0f / kNegHalfLog2e, kInvNegLog2e = 1.0f / kNegLog2e;
+                const float ca = s0[j].z * kInvNegHalfLog2e, cb = s0[j].w * kInvNegLog2e,
+                            cc = s1[j].x * kInvNegHalfLog2e;
                 acc = make_float4(acc.x, acc.y, ca * acc.z + cb * acc.w, cb * acc.z + cc * acc.w);
             } else {
                 const uint32_t m = s_mask[j];
