@@ -35,7 +35,7 @@ ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12     # fp32 VALU lane-ops/s (256 CU x 4 S
 OPS_EVAL = 8        # dx, dy, the quadratic form (2 mul, 2 fma, 1 mul) and the distance cut
 OPS_NEAR = 15       # the exponential (rint, sub, 7 fma, cvt, ldexp), o*G, clamp (cmp, select), alpha cut
 OPS_CONTRIB_FWD = 20    # 1-alpha, T(1-alpha), cut, w, 3 products, 3 compensated adds (4 each), count
-OPS_CONTRIB_REPLAY = 58  # the same plus suffix, reciprocal, rho, mask, the 8 partials and their sums
+OPS_CONTRIB_REPLAY = 57  # the same plus suffix, reciprocal, rho, mask, the 7 partials and their sums
 OPS_CONTRIB_BWD = 70     # forward 20, suffix 6, <g,c> and <g,S> 6, 1-alpha, reciprocal, u and its mask 4,
                          # the 9 partials 8, their wave reduction 26 (eight-value reduce-scatter + one sum)
 
@@ -123,7 +123,8 @@ def measured_traffic(kernel, workload, antialiased=False):
     with open(path) as f:
         data = json.load(f)
     entry = data.get("kernels", {}).get(kernel)
-    if not entry or entry.get("source_sha256") != kernel_source_sha256(kernel):
+    base = kernel.split("<", 1)[0]  # a template instance hashes its template's sources
+    if not entry or entry.get("source_sha256") != kernel_source_sha256(base):
         return None
     return int(entry["bytes_per_launch"])
 
@@ -290,7 +291,7 @@ def main():
     ops_r = OPS_EVAL * E + OPS_NEAR * E_near + OPS_CONTRIB_FWD * K
     secondary = {"k_render": {"bound": "alu", "achieved": round(ops_r / t_ren / 1e12, 3),
                               "frac": round(ops_r / t_ren / 1e12 / ALU_PEAK_TOPS, 4),
-                              "traffic": measured_traffic("k_render", workload, args.antialiased),
+                              "traffic": measured_traffic("k_render<false>", workload, args.antialiased),
                               "avg_launch_ms": round(stages["render"][0], 4)}}
     for st in ("project", "depth_sort", "emit", "tile_sort", "ranges"):
         if st not in stages:
