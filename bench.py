@@ -377,13 +377,18 @@ def sweep(args, dev, stream):
                 for _ in range(2):
                     r.step(obs, outputs, tokens)
                 stream.synchronize()
-                binding.gs_profile_enable(r.ctx, True)
-                binding.gs_profile_read(r.ctx)
+                # the step time without stage events (each timed stage adds two event records to the stream),
+                # then the same number of steps with every stage timed for the breakdown
                 t0 = time.perf_counter()
                 for _ in range(steps):
                     r.step(obs, outputs, tokens)
                 stream.synchronize()
                 elapsed = (time.perf_counter() - t0) / steps
+                binding.gs_profile_enable(r.ctx, True)
+                binding.gs_profile_read(r.ctx)
+                for _ in range(steps):
+                    r.step(obs, outputs, tokens)
+                stream.synchronize()
                 prof = binding.gs_profile_read(r.ctx)
                 binding.gs_profile_enable(r.ctx, False)
                 K = int(outputs[2].to(torch.int64).sum().item())
