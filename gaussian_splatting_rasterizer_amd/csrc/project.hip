@@ -69,7 +69,8 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                S3[3 * i + j] = (M[3 * i] * M[3 * j] + M[3 * i + 1] * M[3 * j + 1]) + M[3 * i + 2] * M[3 * j + 2];
+                S3[3 * i + j] = __builtin_fmaf(M[3 * i + 2], M[3 * j + 2],
+                                               __builtin_fmaf(M[3 * i + 1], M[3 * j + 1], M[3 * i] * M[3 * j]));
     }
 
     for (int v = 0; v < V; ++v) {
@@ -80,9 +81,10 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         const float t0 = cam[9], t1 = cam[10], t2 = cam[11];
         const float fx = cam[12], fy = cam[13], cx = cam[14], cy = cam[15];
 
-        const float tx = ((R0 * mu0 + R1 * mu1) + R2 * mu2) + t0;
-        const float ty = ((R3 * mu0 + R4 * mu1) + R5 * mu2) + t1;
-        const float tz = ((R6 * mu0 + R7 * mu1) + R8 * mu2) + t2;
+        // three-term dot products as fused multiply-add chains: fma(a2, b2, fma(a1, b1, a0 b0))
+        const float tx = __builtin_fmaf(R2, mu2, __builtin_fmaf(R1, mu1, R0 * mu0)) + t0;
+        const float ty = __builtin_fmaf(R5, mu2, __builtin_fmaf(R4, mu1, R3 * mu0)) + t1;
+        const float tz = __builtin_fmaf(R8, mu2, __builtin_fmaf(R7, mu1, R6 * mu0)) + t2;
         bool ok = ok_g && (tz >= near_plane) && (tz <= far_plane);
 
         // camera-frame covariance Rv S3 Rv^T
@@ -92,12 +94,14 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                Tm[3 * i + j] = (Rv[3 * i] * S3[j] + Rv[3 * i + 1] * S3[3 + j]) + Rv[3 * i + 2] * S3[6 + j];
+                Tm[3 * i + j] = __builtin_fmaf(Rv[3 * i + 2], S3[6 + j],
+                                               __builtin_fmaf(Rv[3 * i + 1], S3[3 + j], Rv[3 * i] * S3[j]));
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                Cc[3 * i + j] = (Tm[3 * i] * Rv[3 * j] + Tm[3 * i + 1] * Rv[3 * j + 1]) + Tm[3 * i + 2] * Rv[3 * j + 2];
+                Cc[3 * i + j] = __builtin_fmaf(Tm[3 * i + 2], Rv[3 * j + 2],
+                                               __builtin_fmaf(Tm[3 * i + 1], Rv[3 * j + 1], Tm[3 * i] * Rv[3 * j]));
 
         const float limx = kFovClamp * ((0.5f * (float)W) / fx);
         const float limy = kFovClamp * ((0.5f * (float)H) / fy);
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         for (int ch = 0; ch < 3; ++ch) {
             float acc = B[0] * c[ch];
 #pragma unroll
-            for (int k = 1; k < D; ++k) acc = acc + B[k] * c[3 * k + ch];
+            for (int k = 1; k < D; ++k) acc = __builtin_fmaf(B[k], c[3 * k + ch], acc);
             pre[ch] = acc + 0.5f;
         }
 

@@ -281,9 +281,10 @@ static void project32(const scene* s, int g, int v, rec32* r)
 
     memset(r, 0, sizeof *r);
     r->culled = 1;
-    float tx = ((R[0] * mu[0] + R[1] * mu[1]) + R[2] * mu[2]) + t[0];
-    float ty = ((R[3] * mu[0] + R[4] * mu[1]) + R[5] * mu[2]) + t[1];
-    float tz = ((R[6] * mu[0] + R[7] * mu[1]) + R[8] * mu[2]) + t[2];
+    /* three-term dot products as fused multiply-add chains: fma(a2, b2, fma(a1, b1, a0 b0)) */
+    float tx = fmaf(R[2], mu[2], fmaf(R[1], mu[1], R[0] * mu[0])) + t[0];
+    float ty = fmaf(R[5], mu[2], fmaf(R[4], mu[1], R[3] * mu[0])) + t[1];
+    float tz = fmaf(R[8], mu[2], fmaf(R[7], mu[1], R[6] * mu[0])) + t[2];
     if (!(tz >= s->near_plane) || !(tz <= s->far_plane)) return;
     if (!(op >= 0.0f) || !(op <= 1.0f)) return;
 
@@ -307,14 +308,14 @@ static void project32(const scene* s, int g, int v, rec32* r)
     float S3[9];
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j)
-            S3[3 * i + j] = (M[3 * i] * M[3 * j] + M[3 * i + 1] * M[3 * j + 1]) + M[3 * i + 2] * M[3 * j + 2];
+            S3[3 * i + j] = fmaf(M[3 * i + 2], M[3 * j + 2], fmaf(M[3 * i + 1], M[3 * j + 1], M[3 * i] * M[3 * j]));
     float Tm[9], Cc[9];
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j)
-            Tm[3 * i + j] = (R[3 * i] * S3[j] + R[3 * i + 1] * S3[3 + j]) + R[3 * i + 2] * S3[6 + j];
+            Tm[3 * i + j] = fmaf(R[3 * i + 2], S3[6 + j], fmaf(R[3 * i + 1], S3[3 + j], R[3 * i] * S3[j]));
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j)
-            Cc[3 * i + j] = (Tm[3 * i] * R[3 * j] + Tm[3 * i + 1] * R[3 * j + 1]) + Tm[3 * i + 2] * R[3 * j + 2];
+            Cc[3 * i + j] = fmaf(Tm[3 * i + 2], R[3 * j + 2], fmaf(Tm[3 * i + 1], R[3 * j + 1], Tm[3 * i] * R[3 * j]));
 
     float limx = FOV_CLAMP_F * ((0.5f * (float)s->W) / fx);
     float limy = FOV_CLAMP_F * ((0.5f * (float)s->H) / fy);
@@ -376,7 +377,7 @@ static void project32(const scene* s, int g, int v, rec32* r)
     sh_basis32(dx * il, dy * il, dz * il, s->d, B);
     for (int ch = 0; ch < 3; ++ch) {
         float acc = B[0] * sh[ch];
-        for (int k = 1; k < s->d; ++k) acc = acc + B[k] * sh[3 * k + ch];
+        for (int k = 1; k < s->d; ++k) acc = fmaf(B[k], sh[3 * k + ch], acc);
         float pre = acc + 0.5f;
         r->pre[ch] = pre;
         r->clamp_ok[ch] = pre >= 0.0f;
