@@ -301,6 +301,9 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
         ctx->cams.c[v][14] = c.cx;
         ctx->cams.c[v][15] = c.cy;
         if (!(c.fx > 0.0f) || !(c.fy > 0.0f)) return fail(GS_ERR_INVALID_ARGUMENT, "focal lengths must be > 0");
+        // the same float32 operations preprocess would otherwise repeat for every Gaussian (IEEE division)
+        ctx->cams.lim[v][0] = kFovClamp * ((0.5f * (float)s.W) / c.fx);
+        ctx->cams.lim[v][1] = kFovClamp * ((0.5f * (float)s.H) / c.fy);
     }
     ctx->scene = *sc;
     ctx->params = *params;

@@ -111,7 +111,9 @@ __device__ __forceinline__ void sh_basis_f64(double x, double y, double z, int d
 
 // Camera as passed by value to the kernels: [R (9), t (3), fx, fy, cx, cy].
 struct CamPack {
-    float c[kMaxViews][16];
+    float c[kMaxViews][16];    // R (9, row-major), t (3), fx, fy, cx, cy
+    float lim[kMaxViews][2];   // field-of-view clamp kFovClamp ((W / 2) / fx), kFovClamp ((H / 2) / fy),
+                               // evaluated on the host in that float32 order
 };
 
 // Per-(view, Gaussian) record, three float4 (48 B) at index rid = v * G + g:

@@ -103,8 +103,7 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
                 Cc[3 * i + j] = __builtin_fmaf(Tm[3 * i + 2], Rv[3 * j + 2],
                                                __builtin_fmaf(Tm[3 * i + 1], Rv[3 * j + 1], Tm[3 * i] * Rv[3 * j]));
 
-        const float limx = kFovClamp * ((0.5f * (float)W) / fx);
-        const float limy = kFovClamp * ((0.5f * (float)H) / fy);
+        const float limx = cams.lim[v][0], limy = cams.lim[v][1];  // kFovClamp ((W / 2) / fx), likewise y
         const float ux = tx / tz, uy = ty / tz;
         const float uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
         const float uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
