@@ -66,8 +66,8 @@ def parse_args():
 
 def stage_bytes(stage, c):
     """Algorithmic HBM bytes per launch of a stage: every array the stage must
-    read or write once, at its element size (the per-record and per-pair terms
-    are listed in the design doc)."""
+    read or write once, at its element size (per-record and per-pair terms,
+    annotated line by line below)."""
     G, V, d, P, VG = c["G"], c["V"], c["d"], c["P"], c["G"] * c["V"]
     pk = 4 if c["packable"] else 0   # the rectangle packed to 32 bits by preprocess for the depth sort
     if stage == "project":       # Gaussian parameters in; 40-byte record, rectangle, depth key, tile count out
@@ -132,8 +132,8 @@ def measured_traffic(kernel, workload, antialiased=False):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              f"(the multi-GPU sharding is described in DESIGN.md but not implemented)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the path is not sharded across GPUs)", file=sys.stderr)
         return 2
 
     import numpy as np
