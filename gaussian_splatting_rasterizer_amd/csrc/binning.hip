@@ -630,7 +630,7 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
 // two integer divisions.  With PASSES > 0 it also counts the digits of the tile
 // ids for the tile sort (LDS histogram, then atomics into the shared rows,
 // which k_ranges_init zeroed).
-constexpr int kEmitRecs = 1024;
+constexpr int kEmitRecs = 512;
 
 template <int PASSES>
 __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_sorted,
