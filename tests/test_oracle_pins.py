@@ -389,6 +389,81 @@ def test_single_gaussian_opacity_score_closed_form():
     assert abs(o.acc()[0, 0, 0] - want_w) <= 1e-9 * want_w
 
 
+@pytest.mark.parametrize("op,den_min", [(0.8, 0.204), (0.995, 1e-3)])
+def test_single_gaussian_masks_closed_form(op, den_min):
+    """Exact Score Operators: the opacity and centre scores carry M^alpha (alpha clamp not
+    saturated, suffix denominator T(1 - alpha) not below the threshold), the support q and
+    the SH score do not; the SH score carries the per-channel colour clamp instead.  One
+    broad isotropic Gaussian centred on a pixel corner (var = 150 px^2), bg = 0, so T = 1,
+    C+ = 0 and rho = <r, c>.  The four pixels nearest the centre have d^2 = 0.5 and the
+    next ring d^2 = 2.5: with o = 0.8 the threshold 0.204 lies between their 1 - alpha
+    (0.2013 and 0.2066), with o = 0.995 the alpha clamp o G >= 0.99 holds for d^2 <= 1.51
+    only.  Channel 2's colour is negative before the clamp."""
+    f, z = 64.0, 3.0
+    var = 150.0
+    s = math.sqrt(var - 0.3) * z / f
+    sh = np.zeros((1, 1, 3))
+    sh[0, 0, :] = (np.array([0.9, 0.5, -0.2]) - 0.5) / scenes.SH_C0
+    sc = _single([0.0, 0.0, z], [1, 0, 0, 0], [s, s, s], opac=op, f=f, sh=sh)
+    obs = np.random.default_rng(8).uniform(0, 1, size=(1, 64, 64, 3)).astype(np.float32)
+    o = oracle.OracleScene(sc)
+    o.select(None)
+    color, _, n, _ = o.render(obs=obs, eps=EPS0, den_min=den_min)
+    acc = o.acc()[0, 0]
+    r64 = o.records64()[0, 0]
+    assert np.allclose(r64[[2, 3, 4]], [1 / var, 0, 1 / var], rtol=1e-6, atol=1e-12)
+    ys, xs = np.mgrid[0:64, 0:64]
+    dx, dy = xs + 0.5 - r64[0], ys + 0.5 - r64[1]
+    o32 = float(np.float32(op))
+    ca, cb, cc = r64[2], r64[3], r64[4]            # 1/var up to the float32 rounding of the scale
+    G = np.exp(-0.5 * (ca * dx * dx + 2 * cb * dx * dy + cc * dy * dy))
+    clamped = o32 * G >= 0.99
+    alpha = np.where(clamped, 0.99, o32 * G)
+    live = n[0] == 1
+    # every decision is far from its threshold (no float32 tie to resolve)
+    assert np.all(np.abs(o32 * G - 0.99) > 1e-4)
+    assert np.all(np.abs((1 - alpha) - den_min) > 1e-3)
+    c = np.maximum(r64[6:9], 0.0)
+    assert c[2] == 0.0
+    r = color[0] - obs[0]
+    rho = r @ c
+    M = live & ~clamped & ((1 - alpha) >= den_min)
+    assert 0 < (live & ~M).sum() <= 8          # the masked pixels are the centre ones
+    assert abs(acc[0] - alpha[live].sum()) <= 1e-9 * alpha[live].sum()
+    want_a = np.sum((alpha * (1 - o32) * rho)[M])
+    want_mx = np.sum((o32 * G * (ca * dx + cb * dy) * rho)[M])
+    want_my = np.sum((o32 * G * (cb * dx + cc * dy) * rho)[M])
+    scale = np.sum(np.abs(alpha * rho)[live])
+    assert abs(acc[1] - want_a) <= 1e-9 * scale, (acc[1], want_a)
+    assert abs(acc[2] - want_mx) <= 1e-9 * scale, (acc[2], want_mx)
+    assert abs(acc[3] - want_my) <= 1e-9 * scale, (acc[3], want_my)
+    B0 = scenes.SH_C0
+    for ch in range(3):
+        want = 0.0 if ch == 2 else np.sum((alpha * B0 * r[..., ch])[live])
+        assert abs(acc[oracle.NACC_FIXED + ch] - want) <= 1e-9 * scale, (ch, acc[oracle.NACC_FIXED + ch], want)
+
+
+def test_all_masked_replay_keeps_support_and_sh():
+    """With the suffix-denominator threshold at 1 every contribution is masked
+    (T(1 - alpha) <= 1 - 1/255): the opacity and centre sums vanish exactly while the
+    support and the SH sums equal those of the unmasked replay."""
+    sc = scenes.tiny_scene(seed=12, n=20, n_views=2, sh_degree=1)
+    obs = np.random.default_rng(9).uniform(0, 1, size=(2, 32, 32, 3)).astype(np.float32)
+    res = []
+    for den in (0.0, 1.0):
+        o = oracle.OracleScene(sc)
+        o.select(None)
+        o.render(obs=obs, eps=1e-6, den_min=den)
+        res.append(o.acc())
+    a0, a1 = res
+    assert a0[:, :, 0].sum() > 1.0 and np.abs(a0[:, :, 1:4]).sum() > 0
+    assert np.all(a1[:, :, 1:4] == 0.0)
+    # (the oracle's per-pixel sums run in a thread-dependent order: equal up to rounding)
+    assert np.allclose(a1[:, :, 0], a0[:, :, 0], rtol=1e-12, atol=1e-12)
+    k = oracle.NACC_FIXED
+    assert np.allclose(a1[:, :, k:k + 3 * sc.d], a0[:, :, k:k + 3 * sc.d], rtol=1e-12, atol=1e-12)
+
+
 # --------------------------------------------------------------------------
 # token statistics: eigenvalues, single-view null direction, zero support
 # --------------------------------------------------------------------------
@@ -422,6 +497,107 @@ def test_single_view_conditioning_has_lambda_along_the_ray():
         ray = sc.means[g].astype(np.float64) - (-sc.cams[0, 9:12].astype(np.float64))
         ray /= np.linalg.norm(ray)
         assert abs(ray @ A[g] @ ray - lam) <= 1e-6 * ev[-1]
+
+
+def _isotropic_support(o, v, n, op, var, cx, cy, W, H):
+    """W_gv = sum of alpha over the pixels where the single Gaussian contributes (n == 1),
+    alpha = o exp(-|p - centre|^2 / (2 var)) for an isotropic footprint centred at (cx, cy)."""
+    ys, xs = np.mgrid[0:H, 0:W]
+    d2 = (xs + 0.5 - cx) ** 2 + (ys + 0.5 - cy) ** 2
+    alpha = op * np.exp(-0.5 * d2 / var)
+    return float(alpha[n[v] == 1].sum())
+
+
+def _token_stats_closed_form(tok, d, lam, eps, ev):
+    """The statistics block of the token: e~ = eig(A)/(tr A + eps) (descending) and log(tr A + eps)."""
+    ev = np.sort(np.asarray(ev, dtype=np.float64))[::-1]
+    tr = ev.sum()
+    assert np.allclose(tok[5 + 3 * d: 8 + 3 * d], ev / (tr + eps), rtol=2e-6, atol=0), \
+        (tok[5 + 3 * d: 8 + 3 * d], ev / (tr + eps))
+    assert abs(tok[8 + 3 * d] - math.log(tr + eps)) <= 2e-6, (tok[8 + 3 * d], math.log(tr + eps))
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_single_view_on_axis_conditioning_closed_form(eps):
+    """One isotropic Gaussian on the optical axis of one camera (Exact Score Operators:
+    q = eps + sum_p w, gamma = q / Q with Q = eps + sum_v q_v, A = lambda I + sum_v gamma J^T J).
+    There J^T J = (f/z)^2 diag(1, 1, 0), so A = diag(lam + gamma k, lam + gamma k, lam) with
+    k = (f/z)^2; the support W is summed from the closed-form footprint.  The large eps makes
+    gamma = q / (eps + q) far from 1, so dropping gamma, or weighting by q, fails."""
+    z, s, f, op, lam = 3.0, 0.0625, 64.0, 0.8, 1.0
+    sc = _single([0.0, 0.0, z], [1, 0, 0, 0], [s, s, s], opac=op, f=f)
+    obs = np.random.default_rng(5).uniform(0, 1, size=(1, 64, 64, 3)).astype(np.float32)
+    o = oracle.OracleScene(sc)
+    o.select(None)
+    _, _, n, _ = o.render(obs=obs)
+    var = (f * s / z) ** 2 + 0.3
+    Wsum = _isotropic_support(o, 0, n, float(np.float32(op)), var, 32.0, 32.0, 64, 64)
+    assert Wsum > 1.0
+    tok, A, q = o.tokens(eps=eps, lam=lam, with_A=True)
+    q_want = eps + Wsum
+    assert abs(q[0, 0] - q_want) <= 1e-9 * q_want
+    gamma = q_want / (eps + q_want)
+    k = (f / z) ** 2
+    A_want = np.diag([lam + gamma * k, lam + gamma * k, lam])
+    assert np.allclose(A[0], A_want, rtol=1e-9, atol=1e-9), (A[0], A_want)
+    _token_stats_closed_form(tok[0], sc.d, lam, eps, np.diag(A_want))
+    assert abs(tok[0, 4 + 3 * sc.d] - math.log(eps + q_want)) <= 1e-9
+
+
+def _look_at_camera(centre, direction, f, W, H):
+    """Camera at `centre` whose optical axis is the unit vector `direction` in the x-z plane."""
+    dx, _, dz = direction
+    R = np.array([[dz, 0.0, -dx], [0.0, 1.0, 0.0], [dx, 0.0, dz]])  # rows: camera x, y, z axes
+    row = np.zeros(16)
+    row[0:9] = R.reshape(-1)
+    row[9:12] = -R @ np.asarray(centre, dtype=np.float64)
+    row[12:16] = [f, f, W / 2.0, H / 2.0]
+    return row
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_two_view_conditioning_gamma_weighting_closed_form(eps):
+    """One isotropic Gaussian on the optical axes of two cameras at distances z1 = 3 and
+    z2 = 4.5, the second axis tilted by 30 degrees.  For a camera looking straight at the
+    Gaussian, J = (f/z) (rows 1, 2 of R), so J^T J = (f/z)^2 (I - d d^T) with d the viewing
+    direction, and A = lam I + a1 (I - d1 d1^T) + a2 (I - d2 d2^T), a_v = gamma_v (f/z_v)^2,
+    gamma_v = q_v / (eps + q1 + q2).  Its eigenvalues are lam + a1 + a2 (along y) and
+    lam + a1 + a2 - m for m the eigenvalues of a1 d1 d1^T + a2 d2 d2^T (trace a1 + a2,
+    determinant a1 a2 sin^2 30deg).  The supports differ (q1 != q2), so replacing gamma by 1
+    or by q fails."""
+    mu = np.array([0.0, 0.0, 3.0])
+    s, f, op, lam, W = 0.0625, 64.0, 0.8, 1.0, 64
+    th = math.radians(30.0)
+    d2 = np.array([math.sin(th), 0.0, math.cos(th)])
+    z = [3.0, 4.5]
+    cams = np.stack([_look_at_camera([0, 0, 0], [0.0, 0.0, 1.0], f, W, W),
+                     _look_at_camera(mu - z[1] * d2, d2, f, W, W)])
+    sc = _single(mu, [1, 0, 0, 0], [s, s, s], opac=op, W=W, H=W, f=f, cams=cams)
+    obs = np.random.default_rng(6).uniform(0, 1, size=(2, W, W, 3)).astype(np.float32)
+    o = oracle.OracleScene(sc)
+    o.select(None)
+    _, _, n, _ = o.render(obs=obs)
+    r64 = o.records64()
+    Ws = []
+    for v in range(2):
+        var = (f * s / z[v]) ** 2 + 0.3
+        assert np.allclose(r64[v, 0, 0:2], [32.0, 32.0], atol=2e-4)
+        Ws.append(_isotropic_support(o, v, n, float(np.float32(op)), var, r64[v, 0, 0], r64[v, 0, 1], W, W))
+    q_want = np.array([eps + Ws[0], eps + Ws[1]])
+    assert abs(q_want[0] - q_want[1]) > 0.2 * q_want.max()      # unequal supports
+    tok, A, q = o.tokens(eps=eps, lam=lam, with_A=True)
+    assert np.allclose(q[0], q_want, rtol=1e-6)
+    Q = eps + q_want.sum()
+    a = q_want / Q * (f / np.array(z)) ** 2
+    dirs = [np.array([0.0, 0.0, 1.0]), d2]
+    A_want = lam * np.eye(3) + sum(a[v] * (np.eye(3) - np.outer(dirs[v], dirs[v])) for v in range(2))
+    assert np.allclose(A[0], A_want, rtol=2e-6, atol=2e-6 * np.abs(A_want).max()), (A[0], A_want)
+    tr_m, det_m = a.sum(), a[0] * a[1] * math.sin(th) ** 2
+    disc = math.sqrt(tr_m ** 2 - 4 * det_m)
+    m = [(tr_m + disc) / 2, (tr_m - disc) / 2]
+    base = lam + a.sum()
+    _token_stats_closed_form(tok[0], sc.d, lam, eps, [base, base - m[1], base - m[0]])
+    assert abs(tok[0, 4 + 3 * sc.d] - math.log(Q)) <= 1e-6
 
 
 def test_zero_support_token_closed_form():
