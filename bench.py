@@ -262,7 +262,7 @@ def main():
         P = int(r.n_pairs)
         finite = bool(torch.isfinite(tokens).all().item())
         rec = r.export(binding.GS_EXPORT_RECORDS)
-        n_live = int((rec[2, :, 3] != 0).sum().item())
+        n_live = int((rec[3, :, 1] != 0).sum().item())
 
     V, H, W = sc.n_views, sc.height, sc.width
     T_tiles = ((W + 15) // 16) * ((H + 15) // 16)

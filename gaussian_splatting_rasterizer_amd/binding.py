@@ -411,7 +411,7 @@ class Rasterizer:
         torch = self.torch
         VG = self.V * self.n
         if kind == GS_EXPORT_RECORDS:
-            dst = torch.empty((3, VG, 4), dtype=torch.float32, device=self.device)
+            dst = torch.empty((4, VG, 4), dtype=torch.float32, device=self.device)
         elif kind == GS_EXPORT_DEPTH_KEYS:
             dst = torch.empty((VG,), dtype=torch.int32, device=self.device)
         elif kind == GS_EXPORT_SORTED_IDS:

@@ -157,7 +157,7 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
     const size_t tiles = (size_t)s.V * s.T, pixels = (size_t)s.V * s.W * s.H;
     ws->rec0 = (float4*)take(16 * VG);
     ws->rec1 = (float4*)take(16 * VG);
-    ws->rec2 = (float2*)take(8 * VG);
+    ws->rec2 = (float4*)take(16 * VG);
     ws->rect = (uint2*)take(8 * VG);
     ws->depth_key = (uint32_t*)take(4 * VG);
     ws->tiles_touched = (uint32_t*)take(4 * VG);
@@ -302,8 +302,8 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
         ctx->cams.c[v][15] = c.cy;
         if (!(c.fx > 0.0f) || !(c.fy > 0.0f)) return fail(GS_ERR_INVALID_ARGUMENT, "focal lengths must be > 0");
         // the same float32 operations preprocess would otherwise repeat for every Gaussian (IEEE division)
-        ctx->cams.lim[v][0] = kFovClamp * ((0.5f * (float)s.W) / c.fx);
-        ctx->cams.lim[v][1] = kFovClamp * ((0.5f * (float)s.H) / c.fy);
+        ctx->cams.lim[v][0] = kFovClamp * ((0.5 * (double)s.W) / (double)c.fx);
+        ctx->cams.lim[v][1] = kFovClamp * ((0.5 * (double)s.H) / (double)c.fy);
     }
     ctx->scene = *sc;
     ctx->params = *params;
@@ -441,7 +441,7 @@ gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_co
 gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens, hipStream_t stream) {
     if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
     if (ctx->state < kRendered) return fail(GS_ERR_STATE, "gs_score_replay before gs_render");
-    if (!observed || !tokens) return fail(GS_ERR_INVALID_ARGUMENT, "null observed or tokens");
+    if (!observed || (!tokens && ctx->s.G > 0)) return fail(GS_ERR_INVALID_ARGUMENT, "null observed or tokens");
     if (!aligned(observed, 4) || !aligned(tokens, 4)) return fail(GS_ERR_INVALID_ARGUMENT, "misaligned pointer");
     ctx->timer.begin(GS_STAGE_REPLAY, stream);
     hipError_t e = launch_replay(ctx->s, ctx->ws, ctx->sorted_g, observed, ctx->params.eps, ctx->params.den_min,
@@ -549,15 +549,14 @@ gs_status gs_debug_export(gs_context* ctx, int32_t kind, void* dst, size_t bytes
     switch (kind) {
         case GS_EXPORT_RECORDS: {
             if (ctx->state < kProjected) return fail(GS_ERR_STATE, "records exist after gs_project");
-            if (bytes < 48 * VG) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
+            if (bytes < 64 * VG) return fail(GS_ERR_INVALID_ARGUMENT, "destination too small");
             char* d = (char*)dst;
             e = hipMemcpyAsync(d, ws.rec0, 16 * VG, hipMemcpyDeviceToDevice, stream);
             if (e == hipSuccess) e = hipMemcpyAsync(d + 16 * VG, ws.rec1, 16 * VG, hipMemcpyDeviceToDevice, stream);
-            // third plane {colour b, entry box, rect lo, rect hi} interleaved from its two arrays
+            if (e == hipSuccess) e = hipMemcpyAsync(d + 32 * VG, ws.rec2, 16 * VG, hipMemcpyDeviceToDevice, stream);
+            // fourth plane {rect lo, rect hi, -, -}
             if (e == hipSuccess && VG > 0)
-                e = hipMemcpy2DAsync(d + 32 * VG, 16, ws.rec2, 8, 8, VG, hipMemcpyDeviceToDevice, stream);
-            if (e == hipSuccess && VG > 0)
-                e = hipMemcpy2DAsync(d + 32 * VG + 8, 16, ws.rect, 8, 8, VG, hipMemcpyDeviceToDevice, stream);
+                e = hipMemcpy2DAsync(d + 48 * VG, 16, ws.rect, 8, 8, VG, hipMemcpyDeviceToDevice, stream);
             break;
         }
         case GS_EXPORT_DEPTH_KEYS:

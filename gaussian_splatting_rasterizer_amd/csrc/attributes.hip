@@ -32,7 +32,8 @@ template <int NC>
 __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict__ ranges,
                                                          const uint32_t* __restrict__ sorted_g,
                                                          const float4* __restrict__ rec0,
-                                                         const float4* __restrict__ rec1, int64_t G, int T, int TX,
+                                                         const float4* __restrict__ rec1,
+                                                         const float4* __restrict__ rec2, int64_t G, int T, int TX,
                                                          int W, int H, const uint8_t* __restrict__ events,
                                                          const float* __restrict__ feat, int C, int c0, int nc,
                                                          FeatBg bg, float* __restrict__ out,
@@ -51,7 +52,8 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
     const int pxi = tx * kTile + (wave & 1) * 8 + (lane & 7);
     const int pyi = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
+    const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -68,7 +70,9 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
         if (threadIdx.x < kAttrBatch && i < rg.y) {
             const uint32_t g = sorted_g[i];
             const int64_t rid = vG + g;
-            s0[threadIdx.x] = rec0[rid];
+            const float4 a = rec0[rid];
+            const float4 c = rec2[rid];
+            s0[threadIdx.x] = make_float4(tile_centre(a.x, c.z, tx), tile_centre(a.y, c.w, ty), a.z, a.w);
             const float4 b = rec1[rid];
             s1[threadIdx.x] = make_float2(b.x, b.y);
             s_evb[threadIdx.x] = events[i];
@@ -95,9 +99,9 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
                 const float4 a = s0[j];
                 const float2 b = s1[j];
                 const float dx = px - a.x, dy = py - a.y;
-                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
-                const bool near = !done && e >= kECutoff;
-                const float aG = b.y * exp2_spec(e);
+                const float S = quad_S(a.z, a.w, b.x, dx, dy);
+                const bool near = !done && S <= kSCutoff;
+                const float aG = b.y * exp2_spec(-S);
                 const float alpha = !(aG < kAlphaMax) ? kAlphaMax : aG;
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
@@ -129,7 +133,8 @@ hipError_t launch_render_features(const Sizes& s, const Workspace& ws, const uin
         for (int c = 0; c < 16; ++c) bg.v[c] = (bg_host && c < nc) ? bg_host[c0 + c] : 0.0f;
 #define GSR_LAUNCH_FEAT(NN)                                                                                       \
     hipLaunchKernelGGL(k_render_features<NN>, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,       \
-                       ws.rec0, ws.rec1, s.G, s.T, s.TX, s.W, s.H, ws.events, feat, C, c0, nc, bg, out, ws.tile_order)
+                       ws.rec0, ws.rec1, ws.rec2, s.G, s.T, s.TX, s.W, s.H, ws.events, feat, C, c0, nc, bg, out,      \
+                       ws.tile_order)
         if (nc <= 4) GSR_LAUNCH_FEAT(4);
         else if (nc <= 8) GSR_LAUNCH_FEAT(8);
         else GSR_LAUNCH_FEAT(16);
@@ -145,6 +150,7 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
                                                    const uint32_t* __restrict__ sorted_g,
                                                    const uint32_t* __restrict__ slot_base,
                                                    const float4* __restrict__ rec0, const float4* __restrict__ rec1,
+                                                   const float4* __restrict__ rec2,
                                                    const uint2* __restrict__ rect, int64_t G, int T, int TX, int W,
                                                    int H, const uint8_t* __restrict__ events,
                                                    const float* __restrict__ map, int C, int c0, int nc,
@@ -165,7 +171,8 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
     const int pxi = tx * kTile + (wave & 1) * 8 + (lane & 7);
     const int pyi = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
+    const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -187,7 +194,9 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
         const uint32_t i = base + threadIdx.x;
         if (threadIdx.x < kAttrBatch && i < rg.y) {
             const int64_t rid = vG + sorted_g[i];
-            s0[threadIdx.x] = rec0[rid];
+            const float4 a = rec0[rid];
+            const float4 c = rec2[rid];
+            s0[threadIdx.x] = make_float4(tile_centre(a.x, c.z, tx), tile_centre(a.y, c.w, ty), a.z, a.w);
             const float4 b = rec1[rid];
             s1[threadIdx.x] = make_float2(b.x, b.y);
             s_evb[threadIdx.x] = events[i];
@@ -215,9 +224,9 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
                 const float4 a = s0[j];
                 const float2 b = s1[j];
                 const float dx = px - a.x, dy = py - a.y;
-                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
-                const bool near = !done && e >= kECutoff;
-                const float aG = b.y * exp2_spec(e);
+                const float S = quad_S(a.z, a.w, b.x, dx, dy);
+                const bool near = !done && S <= kSCutoff;
+                const float aG = b.y * exp2_spec(-S);
                 const float alpha = !(aG < kAlphaMax) ? kAlphaMax : aG;
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
@@ -290,7 +299,8 @@ hipError_t launch_attribute(const Sizes& s, const Workspace& ws, const uint32_t*
         const int nc = C - c0 < 8 ? C - c0 : 8;
         if (tiles > 0)
             hipLaunchKernelGGL(k_attribute, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,
-                               ws.slot_base, ws.rec0, ws.rec1, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.events, map, C,
+                               ws.slot_base, ws.rec0, ws.rec1, ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.events,
+                               map, C,
                                c0, nc, ws.partials, ws.slot_bits, ws.tile_order);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -312,7 +322,7 @@ hipError_t launch_attribute(const Sizes& s, const Workspace& ws, const uint32_t*
 template <int K>
 __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
                                               const float4* __restrict__ rec0, const float4* __restrict__ rec1,
-                                              int64_t G, int T, int TX, int W, int H,
+                                              const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
                                               const uint8_t* __restrict__ events, int k_out,
                                               int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
     __shared__ float4 s0[kAttrBatch];
@@ -329,7 +339,8 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
     const int pxi = tx * kTile + (wave & 1) * 8 + (lane & 7);
     const int pyi = ty * kTile + (wave >> 1) * 8 + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
+    const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -349,7 +360,9 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
         const uint32_t i = base + threadIdx.x;
         if (threadIdx.x < kAttrBatch && i < rg.y) {
             const uint32_t g = sorted_g[i];
-            s0[threadIdx.x] = rec0[vG + g];
+            const float4 a = rec0[vG + g];
+            const float4 c = rec2[vG + g];
+            s0[threadIdx.x] = make_float4(tile_centre(a.x, c.z, tx), tile_centre(a.y, c.w, ty), a.z, a.w);
             const float4 b = rec1[vG + g];
             s1[threadIdx.x] = make_float2(b.x, b.y);
             s_g[threadIdx.x] = g;
@@ -374,9 +387,9 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
                 const float4 a = s0[j];
                 const float2 b = s1[j];
                 const float dx = px - a.x, dy = py - a.y;
-                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
-                const bool near = !done && e >= kECutoff;
-                const float aG = b.y * exp2_spec(e);
+                const float S = quad_S(a.z, a.w, b.x, dx, dy);
+                const bool near = !done && S <= kSCutoff;
+                const float aG = b.y * exp2_spec(-S);
                 const float alpha = !(aG < kAlphaMax) ? kAlphaMax : aG;
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
@@ -419,7 +432,7 @@ hipError_t launch_topk(const Sizes& s, const Workspace& ws, const uint32_t* sort
     if (tiles == 0) return hipSuccess;
 #define GSR_LAUNCH_TOPK(KK)                                                                                       \
     hipLaunchKernelGGL(k_topk<KK>, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1, \
-                       s.G, s.T, s.TX, s.W, s.H, ws.events, k, ids, w)
+                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, ws.events, k, ids, w)
     if (k <= 4) GSR_LAUNCH_TOPK(4);
     else if (k <= 8) GSR_LAUNCH_TOPK(8);
     else GSR_LAUNCH_TOPK(16);

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                                                   const uint32_t* __restrict__ sorted_g,
                                                   const uint32_t* __restrict__ slot_base,
                                                   const float4* __restrict__ rec0, const float4* __restrict__ rec1,
-                                                  const float2* __restrict__ rec2, const uint2* __restrict__ rect,
+                                                  const float4* __restrict__ rec2, const uint2* __restrict__ rect,
                                                   int64_t G, int T, int TX, int W, int H,
                                                   const float4* __restrict__ pixel,
                                                   const float* __restrict__ grad_color,
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
     __shared__ float s2[kBwdBatch];
     __shared__ uint8_t s_evb[kBwdBatch];    // event bits of each staged entry (bit w: wave w)
     __shared__ uint32_t s_slot[kBwdBatch];  // partial slot of each staged pair
-    __shared__ uint8_t s_mask[kBwdBatch];   // colour clamp mask bits (pre-clamp colour >= 0), r g b
+    __shared__ uint8_t s_mask[kBwdBatch];   // colour clamp mask bits (pre-clamp colour finite and >= 0), r g b
     __shared__ uint8_t slist[4][kBwdBatch];
     __shared__ __align__(16) float sp[4][kBwdBatch][12];
 
@@ -80,7 +80,8 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
     const int pxi = qx + (lane & 7);
     const int pyi = qy + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
+    const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -107,15 +108,15 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
-            const float2 c = rec2[rid];
+            const float4 c = rec2[rid];
             const uint2 rc = rect[rid];
-            s0[threadIdx.x] = a;
+            s0[threadIdx.x] = make_float4(tile_centre(a.x, c.z, tx), tile_centre(a.y, c.w, ty), a.z, a.w);
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(c.x);
             s_evb[threadIdx.x] = events[i];
             const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16, wx = (rc.y & 0xffffu) - x0;
             s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
-            s_mask[threadIdx.x] = (uint8_t)((b.z >= 0.0f ? 1u : 0u) | (b.w >= 0.0f ? 2u : 0u) | (c.x >= 0.0f ? 4u : 0u));
+            s_mask[threadIdx.x] = (uint8_t)((colour_ok(b.z) ? 1u : 0u) | (colour_ok(b.w) ? 2u : 0u) | (colour_ok(c.x) ? 4u : 0u));
         }
         const int cnt = (int)min((uint32_t)kBwdBatch, rg.y - base);
         for (int e = lane; e < cnt * 12; e += 64) (&sp[wave][0][0])[e] = 0.0f;
@@ -137,9 +138,9 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                 const float4 a = s0[j];
                 const float4 b = s1[j];
                 const float dx = px - a.x, dy = py - a.y;
-                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
-                const bool near = !done && e >= kECutoff;
-                const float aG = b.y * exp2_spec(e);
+                const float S = quad_S(a.z, a.w, b.x, dx, dy);
+                const bool near = !done && S <= kSCutoff;
+                const float aG = b.y * exp2_spec(-S);
                 const bool clamped = !(aG < kAlphaMax);
                 const float alpha = clamped ? kAlphaMax : aG;
                 const bool pass = near && alpha >= kAlphaMin;
@@ -292,11 +293,16 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
             }
 
         // perspective Jacobian at the centre clamped to 1.3x the half field of view
-        const double limx = 1.3 * (0.5 * W / fx), limy = 1.3 * (0.5 * H / fy);
+        // the clamp state is the preprocess decision, re-taken by the same function from the same inputs
+        // (its float64 operations are not contracted), so the backward differentiates the rendered branch
+        double tdec[3];
+        camera_centre_f64(cam, mu, tdec);
+        const int clip = fov_clip_bits(tdec, cams.lim[v]);
+        const bool clip_x = (clip & 1) != 0, clip_y = (clip & 2) != 0;
+        const double limx = cams.lim[v][0], limy = cams.lim[v][1];
         const double ux = tx * iz, uy = ty * iz;
-        const bool clip_x = ux < -limx || ux > limx, clip_y = uy < -limy || uy > limy;
-        const double uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
-        const double uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
+        const double uxc = clip_x ? (ux < 0.0 ? -limx : limx) : ux;
+        const double uyc = clip_y ? (uy < 0.0 ? -limy : limy) : uy;
         const double j00 = fx * iz, j02 = -fx * uxc * iz, j11 = fy * iz, j12 = -fy * uyc * iz;
         // Jc Cc (rows 0, 1) and the dilated 2D covariance [[a, b], [b, c]]
         const double A0[3] = {j00 * Cc[0] + j02 * Cc[6], j00 * Cc[1] + j02 * Cc[7], j00 * Cc[2] + j02 * Cc[8]};
@@ -429,7 +435,10 @@ __global__ __launch_bounds__(kGradThreads) void k_grads(const float* __restrict_
                 gsh[3 * k] += B[k] * gp0;
                 gsh[3 * k + 1] += B[k] * gp1;
                 gsh[3 * k + 2] += B[k] * gp2;
-                const float gB = shg[3 * k] * gp0 + shg[3 * k + 1] * gp1 + shg[3 * k + 2] * gp2;
+                // a masked (clamped) channel has a zero colour gradient and no direction term, also when
+                // its coefficients are not finite
+                const float gB = (gp0 != 0.0f ? shg[3 * k] * gp0 : 0.0f) + (gp1 != 0.0f ? shg[3 * k + 1] * gp1 : 0.0f) +
+                                 (gp2 != 0.0f ? shg[3 * k + 2] * gp2 : 0.0f);
                 gd0 += gB * dB[3 * k];
                 gd1 += gB * dB[3 * k + 1];
                 gd2 += gB * dB[3 * k + 2];

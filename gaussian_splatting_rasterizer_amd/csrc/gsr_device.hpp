@@ -1,11 +1,13 @@
 // gsr_device.hpp -- device-side definitions shared by the gfx950 kernels.
 //
-// Floating-point decisions (culling, radius, tile rectangle, colour clamp,
-// alpha skip/clamp, early termination, suffix-denominator mask) follow a fixed
-// float32 operation order with no FMA contraction (the library is compiled
-// with -ffp-contract=off; fused multiply-adds appear only where written as
-// __builtin_fmaf).  This makes every such integer decision reproducible by any
-// implementation of the same order.
+// Floating-point decisions (culling, field-of-view clamp, radius, tile
+// rectangle, colour clamp, alpha skip/clamp, early termination,
+// suffix-denominator mask) follow a fixed operation order with no FMA
+// contraction (the library is compiled with -ffp-contract=off; fused
+// multiply-adds appear only where written as __builtin_fmaf / __builtin_fma):
+// preprocess geometry in float64, everything per pixel in float32.  This makes
+// every such integer decision reproducible by any implementation of the same
+// order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,12 +23,12 @@ constexpr int kMaxViews = 32;
 constexpr float kAlphaMax = 0.99f;
 constexpr float kAlphaMin = 0x1.010102p-8f;   // float32 nearest to 1/255
 constexpr float kTMin = 1e-4f;
-constexpr float kDilation = 0.3f;
+constexpr double kDilation = 0.3;             // px^2 added to the projected covariance (float64 geometry)
 constexpr float kEigFloor = 0.1f;
-constexpr float kFovClamp = 1.3f;
-constexpr float kECutoff = -8.0f;             // 2^-8 < 1/255: no alpha can pass below this
-constexpr float kNegLog2e = -0x1.715476p+0f;  // float32 nearest to -log2(e)
-constexpr float kNegHalfLog2e = -0x1.715476p-1f;
+constexpr double kFovClamp = 1.3;
+constexpr float kSCutoff = 8.0f;              // 2^-8 < 1/255: no alpha can pass beyond this exponent
+constexpr float kHalfLog2e = 0x1.715476p-1f;  // float32 nearest to log2(e) / 2
+constexpr float kInvHalfLog2e = 1.0f / kHalfLog2e;
 
 // 2^e for e in [-8, 1/2]: k = rint(e), f = e - k (exact, |f| <= 1/2), 2^f by
 // the degree-7 Taylor polynomial sum_j (f ln 2)^j / j! with each coefficient
@@ -112,33 +114,54 @@ __device__ __forceinline__ void sh_basis_f64(double x, double y, double z, int d
 // Camera as passed by value to the kernels: [R (9), t (3), fx, fy, cx, cy].
 struct CamPack {
     float c[kMaxViews][16];    // R (9, row-major), t (3), fx, fy, cx, cy
-    float lim[kMaxViews][2];   // field-of-view clamp kFovClamp ((W / 2) / fx), kFovClamp ((H / 2) / fy),
-                               // evaluated on the host in that float32 order
+    double lim[kMaxViews][2];  // field-of-view clamp kFovClamp ((W / 2) / fx), kFovClamp ((H / 2) / fy),
+                               // evaluated on the host in that float64 order
 };
 
-// Per-(view, Gaussian) record, three float4 (48 B) at index rid = v * G + g:
-//   r0 = {mx, my, qa, qb}
-//   r1 = {qc, opacity, pre_r, pre_g}
-//   r2 = {pre_b, bits(pair offset), bits(x0 | y0 << 16), bits(x1 | y1 << 16)}
-// The Gaussian weight at pixel offset (dx, dy) = p - mu is 2^(qa dx^2 + qb dx dy + qc dy^2),
-// i.e. qa = -log2(e)/2 A, qb = -log2(e) B, qc = -log2(e)/2 C for the conic [[A, B], [B, C]].
+// Per-(view, Gaussian) record, three float4 at index rid = v * G + g:
+//   r0 = {mx, my, s1, s2}
+//   r1 = {s3, opacity, pre_r, pre_g}
+//   r2 = {pre_b, entry box (two binary16 half-widths), mx_lo, my_lo}
+// The projected centre is the float64 value mx + mx_lo (likewise y) split into two float32s.
+// The Gaussian weight at pixel offset (dx, dy) = p - mu is 2^-S with
+// S = (s1 dx + s2 dy)^2 + (s3 dy)^2 = k (dx, dy) Sigma2^-1 (dx, dy)^T, k = log2(e) / 2:
+// [[s1, 0], [s2, s3]] is the Cholesky factor of k times the conic, so S is a sum of squares
+// and keeps its relative precision however elongated the footprint.
 
-__device__ __forceinline__ float clamp_colour(float pre) { return pre >= 0.0f ? pre : 0.0f; }
-
-// Evaluate one list entry at one pixel with the canonical float32 order.
-// Returns 0 when the pixel is beyond the distance cut, 1 when alpha < 1/255,
-// 2 when the entry contributes (alpha, clamped and the offset (dx, dy) set).
-__device__ __forceinline__ int eval_alpha(float4 r0, float qc, float opac, float px, float py, float& dx,
-                                          float& dy, float& alpha, bool& clamped) {
-    dx = px - r0.x;
-    dy = py - r0.y;
-    const float e = __builtin_fmaf(dx, __builtin_fmaf(r0.z, dx, r0.w * dy), (qc * dy) * dy);
-    if (!(e >= kECutoff)) return 0;
-    const float aG = opac * exp2_spec(e);
-    clamped = !(aG < kAlphaMax);
-    alpha = clamped ? kAlphaMax : aG;
-    return alpha >= kAlphaMin ? 2 : 1;
+// Camera-space centre t = R mu + t_v in float64 from the float32 inputs, in the written order
+// (each product of two float32 values is exact; the sums round once each, left to right).
+__device__ __forceinline__ void camera_centre_f64(const float* cam, const double mu[3], double t[3]) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        t[i] = (((double)cam[3 * i] * mu[0] + (double)cam[3 * i + 1] * mu[1]) + (double)cam[3 * i + 2] * mu[2]) +
+               (double)cam[9 + i];
 }
+
+// Field-of-view clamp of the perspective Jacobian's lateral offset: bit 0 when |tx / tz| exceeds
+// lim[0], bit 1 likewise in y.  One function for the preprocess and the backward, so both take
+// the same decision from the same float64 operations.
+__device__ __forceinline__ int fov_clip_bits(const double t[3], const double lim[2]) {
+    const double ux = t[0] / t[2], uy = t[1] / t[2];
+    return ((ux < -lim[0] || ux > lim[0]) ? 1 : 0) | ((uy < -lim[1] || uy > lim[1]) ? 2 : 0);
+}
+
+// The centre relative to the origin of the tile with index tc along that axis: hi - 16 tc is exact
+// whenever the entry can reach the tile, then lo is added with one rounding.
+__device__ __forceinline__ float tile_centre(float hi, float lo, int tc) {
+    return (hi - (float)(kTile * tc)) + lo;
+}
+
+// S at the offset (dx, dy), in the written order.
+__device__ __forceinline__ float quad_S(float s1, float s2, float s3, float dx, float dy) {
+    const float u = __builtin_fmaf(s1, dx, s2 * dy);
+    const float w = s3 * dy;
+    return __builtin_fmaf(u, u, w * w);
+}
+
+// colour clamp: a pre-clamp colour that is negative or not finite is clamped to 0 and its
+// clamp bit cleared (the clamp mask of the SH score)
+__device__ __forceinline__ bool colour_ok(float pre) { return pre >= 0.0f && pre <= 3.40282347e+38f; }
+__device__ __forceinline__ float clamp_colour(float pre) { return colour_ok(pre) ? pre : 0.0f; }
 
 // A tile rectangle in 32 bits, for tile grids of at most 256 x 256: x0, y0,
 // width - 1, height - 1 in bytes; 0xffffffff marks an empty rectangle (culled
@@ -158,28 +181,22 @@ __device__ __forceinline__ uint2 unpack_rect(uint32_t q) {
 
 // Conservative pixel bounding box of the region where an entry can pass the
 // alpha test, used only to skip entries that cannot pass anywhere in a block
-// of pixels.  With Q(d) = a' dx^2 + 2 b' dx dy + c' dy^2 (a' = -qa, b' = -qb/2,
-// c' = -qc, positive definite) the exact exponent is -Q(d), and alpha = o G >=
-// 1/255 needs it to be >= -t with t = min(8, log2(255 o)).  The float32
-// evaluation of the exponent (offsets rounded once, then three products and two
-// fused multiply-adds) differs from -Q(d) by at most 3u Qabs(d) + 3u Q(d) with
-// u = 2^-24 and Qabs <= cond(A) Q, and the float32 exponential and product
-// o * G add a few more units of u; so a pixel can pass only if
-// Q(d) <= t_eff = (t + 1e-5) / (1 - 8 u (cond + 1)).  The region Q <= t_eff has
-// half-widths sqrt(t_eff c' / det) and sqrt(t_eff a' / det), widened by 0.01 px
-// plus 1e-6 of (|centre| + half-width) -- more than the rounding of the float32
-// centre +- half-width at use -- and stored as two binary16 values rounded up
-// (infinite when too large or when 8 u (cond + 1) >= 1/2: never skip; -infinity
-// when the entry can never pass, o <= 1/255: the box is empty).
-//
-// All of it is evaluated in float32 from the exact float32 coefficients, every
-// operation rounded once (no contraction; IEEE division and square root), and
-// kept above the exact values: log2f is within 1 ulp (<= 1e-6 for |t| <= 8,
-// with the rounding of 255 o), so t gets 1.2e-5 instead of 1e-5; det = a'c' - b'^2
-// comes from Kahan's difference of products (fused multiply-adds; within 2u of
-// the exact value however much it cancels), so the radicand is within ~20u and
-// the half-width within ~11u, which the factor 1 + 2^-17 covers; the last sums
-// (4 roundings) get 1 + 2^-20.  Empty when log2(255 o) <= -1e-5 + 1e-6 < 0.
+// of pixels.  With K = L L^T, L = [[s1, 0], [s2, s3]] (the record's float32
+// factors taken as exact), the exact exponent magnitude is S*(d) = d^T K d and
+// alpha = o 2^-S >= 1/255 needs S <= t with t = min(8, log2(255 o)).  The
+// float32 evaluation (offsets rounded once, the products and two fused
+// multiply-adds of quad_S) differs from S* by at most
+// u (6.1 S* + 4.04 E sqrt(S*)) with u = 2^-24 and E = |s1 dx| + |s2 dy| <=
+// 2 sqrt(kappa S*), kappa = max(Kinv_xx, Kinv_yy)^2 / det(Kinv); so a pixel can
+// pass only if S*(d) <= t_eff = (t + 1e-5) / (1 - u (8 + 10 sqrt(kappa))) (1e-5
+// covers the float32 exponential and the product o * G).  The region S* <= t_eff
+// has half-widths sqrt(t_eff Kinv_xx) and sqrt(t_eff Kinv_yy), widened by
+// 0.01 px (more than the rounding of the float32 box edges around a
+// tile-relative centre) and stored as two binary16 values rounded up (infinite
+// when too large or when the growth factor reaches 1/2: never skip; -infinity
+// when the entry can never pass, o <= 1/255: the box is empty).  Evaluated in
+// float64 from the float32 factors; every float64 rounding is far below the
+// margins.
 __device__ __forceinline__ uint32_t half_bits_up(float v) {  // least binary16 >= v, for v > 0
     if (!(v <= 65504.0f)) return 0x7c00u;
     const _Float16 h = (_Float16)v;
@@ -188,28 +205,23 @@ __device__ __forceinline__ uint32_t half_bits_up(float v) {  // least binary16 >
     return b;
 }
 
-__device__ __forceinline__ uint32_t entry_box_pack(float4 r0, float qc, float opac) {
-    const float a = -r0.z, b = -0.5f * r0.w, c = -qc;  // exact
-    const float tt = log2f(255.0f * opac);
-    if (!(tt > -1e-5f)) return 0xfc00fc00u;
-    const float w = b * b;
-    const float det = __builtin_fmaf(a, c, -w) + __builtin_fmaf(-b, b, w);
-    if (!(det > 0.0f) || !(a > 0.0f) || !(c > 0.0f)) return 0x7c007c00u;
-    const float t = (tt < 8.0f ? tt : 8.0f) + 1.2e-5f;
-    const float amc = a - c;
-    const float mid = 0.5f * (a + c), hd = __builtin_sqrtf(0.25f * (amc * amc) + b * b);
-    const float lmax = mid + hd, lmin = det / lmax;
-    const float grow = 0x1p-21f * (lmax / lmin + 1.0f);  // 8 u (cond + 1)
-    if (!(grow < 0.5f)) return 0x7c007c00u;
-    const float te = t / (1.0f - grow);
-    const float kw = 1.0f + 0x1p-17f, ks = 1.0f + 0x1p-20f;
-    const float ex = __builtin_sqrtf(te * c / det) * kw, ey = __builtin_sqrtf(te * a / det) * kw;
-    const float wx = ((ex + 0.01f) + 1e-6f * (__builtin_fabsf(r0.x) + ex)) * ks;
-    const float wy = ((ey + 0.01f) + 1e-6f * (__builtin_fabsf(r0.y) + ey)) * ks;
-    return half_bits_up(wx) | (half_bits_up(wy) << 16);
+__device__ __forceinline__ uint32_t entry_box_pack(float s1f, float s2f, float s3f, float opac) {
+    const double tt = log2(255.0 * (double)opac);
+    if (!(tt > -1e-5)) return 0xfc00fc00u;
+    const double s1 = s1f, s2 = s2f, s3 = s3f;
+    const double p1 = s1 * s1, p3 = s3 * s3;
+    if (!(p1 > 0.0) || !(p3 > 0.0)) return 0x7c007c00u;
+    const double kxx = (s2 * s2 + p3) / (p1 * p3), kyy = 1.0 / p3, kdet = 1.0 / (p1 * p3);
+    const double kmax = kxx > kyy ? kxx : kyy;
+    const double grow = 0x1p-24 * (8.0 + 10.0 * sqrt(kmax * kmax / kdet));
+    if (!(grow < 0.5)) return 0x7c007c00u;
+    const double te = ((tt < 8.0 ? tt : 8.0) + 1e-5) / (1.0 - grow);
+    // (1 + 1e-6) keeps the float32 rounding above the float64 value
+    const double wx = (sqrt(te * kxx) + 0.01) * (1.0 + 1e-6), wy = (sqrt(te * kyy) + 0.01) * (1.0 + 1e-6);
+    return half_bits_up((float)wx) | (half_bits_up((float)wy) << 16);
 }
 
-// {x0, x1, y0, y1} of the packed box around the centre (mx, my).
+// {x0, x1, y0, y1} of the packed box around the (tile-relative) centre (mx, my).
 __device__ __forceinline__ float4 entry_box_unpack(float mx, float my, uint32_t packed) {
     const float ex = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed & 0xffffu));
     const float ey = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed >> 16));

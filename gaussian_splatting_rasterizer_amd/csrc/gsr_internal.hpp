@@ -13,9 +13,9 @@ namespace gsr {
 // Workspace carve-up.  Every array lives in caller-owned device memory.
 struct Workspace {
     // per (view, Gaussian) record, rid = v * G + g
-    float4* rec0;          // {mx, my, qa, qb}: centre and exponent coefficients (x, y terms)
-    float4* rec1;          // {qc, opacity, colour r, colour g} (colour before clamping)
-    float2* rec2;          // {colour b, entry box: two binary16 half-widths}
+    float4* rec0;          // {mx, my, s1, s2}: centre (float32 part) and exponent factors
+    float4* rec1;          // {s3, opacity, colour r, colour g} (colour before clamping)
+    float4* rec2;          // {colour b, entry box: two binary16 half-widths, mx_lo, my_lo}
     uint2* rect;           // tile rectangle: {x0 | y0 << 16, x1 | y1 << 16}, zero when culled
     uint32_t* depth_key;   // depth bits, 0xffffffff when culled
     uint32_t* tiles_touched;

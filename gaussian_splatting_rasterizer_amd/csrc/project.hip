@@ -2,20 +2,24 @@
 //
 // One thread per Gaussian reads its parameters once (SH coefficients in
 // registers, the degree is a template parameter so nothing is indexed
-// dynamically) and loops over the views, writing per (view, Gaussian) a 40-byte
+// dynamically) and loops over the views, writing per (view, Gaussian) a 48-byte
 // record, its tile rectangle, the depth sort key and the tile count with
 // coalesced stores.
 //
 // Math: EWA splatting of the 3D covariance R(q) S S^T R(q)^T through the
 // view rotation and the perspective Jacobian (lateral offset clamped to 1.3x the
-// field of view), plus a 0.3 px^2 dilation; the conic is the inverse 2D
-// covariance; the radius is 3 sqrt(lambda_max) rounded up (eigenvalue gap
-// floored at 0.1); colour is the SH expansion along the unit direction from the
-// camera centre, +0.5, clamped below at 0 with the clamp state kept.  The 2D
-// Gaussian kernel and the SH colour are those of the Exact Score Operators of
-// the Renderer Score Tokens proposal; the rest is the standard 3DGS preprocess
-// that Stage 1 ("original gsplat tile binning") refers to.  Operation order
-// and rounding are fixed (see gsr_device.hpp).
+// field of view), plus a 0.3 px^2 dilation, all in float64 from the float32
+// inputs; the radius is 3 sqrt(lambda_max) rounded up (eigenvalue gap floored
+// at 0.1) in float32 from the rounded covariance; the exponent is kept as the
+// Cholesky factor of log2(e)/2 times the inverse covariance and the centre as a
+// float32 pair, so that the float32 evaluation per pixel keeps its precision
+// for elongated footprints and far from the image origin; colour is the SH
+// expansion along the unit direction from the camera centre, +0.5, clamped
+// below at 0 with the clamp state kept.  The 2D Gaussian kernel and the SH
+// colour are those of the Exact Score Operators of the Renderer Score Tokens
+// proposal; the rest is the standard 3DGS preprocess that Stage 1 ("original
+// gsplat tile binning") refers to.  Operation order and rounding are fixed
+// (see gsr_device.hpp).
 #include "gsr_internal.hpp"
 
 namespace gsr {
@@ -26,39 +30,39 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
                                                   const float* __restrict__ sh, int64_t G, int V, CamPack cams,
                                                   int W, int H, int TX, int TY, float near_plane, float far_plane,
                                                   float4* __restrict__ rec0, float4* __restrict__ rec1,
-                                                  float2* __restrict__ rec2, uint2* __restrict__ rect,
+                                                  float4* __restrict__ rec2, uint2* __restrict__ rect,
                                                   uint32_t* __restrict__ depth_key,
                                                   uint32_t* __restrict__ tiles_touched,
                                                   uint32_t* __restrict__ pay_init) {
     const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= G) return;
 
-    const float mu0 = means[3 * g], mu1 = means[3 * g + 1], mu2 = means[3 * g + 2];
+    const double mu[3] = {means[3 * g], means[3 * g + 1], means[3 * g + 2]};
     const float op = opac[g];
     float c[3 * D];
 #pragma unroll
     for (int k = 0; k < 3 * D; ++k) c[k] = sh[(int64_t)3 * D * g + k];
 
-    // view-independent part: normalised quaternion, rotation, 3D covariance
-    const float q0 = quats[4 * g], q1 = quats[4 * g + 1], q2 = quats[4 * g + 2], q3 = quats[4 * g + 3];
-    const float n2 = ((q0 * q0 + q1 * q1) + q2 * q2) + q3 * q3;
-    bool ok_g = (n2 > 0.0f) && (n2 <= 3.40282347e+38f) && (op >= 0.0f) && (op <= 1.0f);
-    float S3[9];
+    // view-independent part (float64): rotation of the unnormalised quaternion scaled by 2 / |q|^2,
+    // M = R(q) diag(s), Sigma3 = M M^T
+    const double qw = quats[4 * g], qx = quats[4 * g + 1], qy = quats[4 * g + 2], qz = quats[4 * g + 3];
+    const double n2 = ((qw * qw + qx * qx) + qy * qy) + qz * qz;
+    bool ok_g = (n2 > 0.0) && (n2 <= 1.7976931348623157e308) && (op >= 0.0f) && (op <= 1.0f);
+    double S3[9];
     {
-        const float inv = 1.0f / __builtin_sqrtf(n2);
-        const float w = q0 * inv, x = q1 * inv, y = q2 * inv, z = q3 * inv;
-        float Rq[9];
-        Rq[0] = 1.0f - 2.0f * (y * y + z * z);
-        Rq[1] = 2.0f * (x * y - w * z);
-        Rq[2] = 2.0f * (x * z + w * y);
-        Rq[3] = 2.0f * (x * y + w * z);
-        Rq[4] = 1.0f - 2.0f * (x * x + z * z);
-        Rq[5] = 2.0f * (y * z - w * x);
-        Rq[6] = 2.0f * (x * z - w * y);
-        Rq[7] = 2.0f * (y * z + w * x);
-        Rq[8] = 1.0f - 2.0f * (x * x + y * y);
-        const float s0 = scales[3 * g], s1 = scales[3 * g + 1], s2 = scales[3 * g + 2];
-        float M[9];
+        const double q2 = 2.0 / n2;
+        double Rq[9];
+        Rq[0] = 1.0 - q2 * (qy * qy + qz * qz);
+        Rq[1] = q2 * (qx * qy - qw * qz);
+        Rq[2] = q2 * (qx * qz + qw * qy);
+        Rq[3] = q2 * (qx * qy + qw * qz);
+        Rq[4] = 1.0 - q2 * (qx * qx + qz * qz);
+        Rq[5] = q2 * (qy * qz - qw * qx);
+        Rq[6] = q2 * (qx * qz - qw * qy);
+        Rq[7] = q2 * (qy * qz + qw * qx);
+        Rq[8] = 1.0 - q2 * (qx * qx + qy * qy);
+        const double s0 = scales[3 * g], s1 = scales[3 * g + 1], s2 = scales[3 * g + 2];
+        double M[9];
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
             M[3 * i] = Rq[3 * i] * s0;
@@ -69,77 +73,75 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                S3[3 * i + j] = __builtin_fmaf(M[3 * i + 2], M[3 * j + 2],
-                                               __builtin_fmaf(M[3 * i + 1], M[3 * j + 1], M[3 * i] * M[3 * j]));
+                S3[3 * i + j] = (M[3 * i] * M[3 * j] + M[3 * i + 1] * M[3 * j + 1]) + M[3 * i + 2] * M[3 * j + 2];
     }
 
     for (int v = 0; v < V; ++v) {
         const float* cam = cams.c[v];
         const int64_t rid = (int64_t)v * G + g;
-        const float R0 = cam[0], R1 = cam[1], R2 = cam[2], R3 = cam[3], R4 = cam[4], R5 = cam[5];
-        const float R6 = cam[6], R7 = cam[7], R8 = cam[8];
-        const float t0 = cam[9], t1 = cam[10], t2 = cam[11];
+        const double R[9] = {cam[0], cam[1], cam[2], cam[3], cam[4], cam[5], cam[6], cam[7], cam[8]};
         const float fx = cam[12], fy = cam[13], cx = cam[14], cy = cam[15];
+        double t[3];
+        camera_centre_f64(cam, mu, t);
+        const double tx = t[0], ty = t[1], tz = t[2];
+        bool ok = ok_g && (tz >= (double)near_plane) && (tz <= (double)far_plane);
 
-        // three-term dot products as fused multiply-add chains: fma(a2, b2, fma(a1, b1, a0 b0))
-        const float tx = __builtin_fmaf(R2, mu2, __builtin_fmaf(R1, mu1, R0 * mu0)) + t0;
-        const float ty = __builtin_fmaf(R5, mu2, __builtin_fmaf(R4, mu1, R3 * mu0)) + t1;
-        const float tz = __builtin_fmaf(R8, mu2, __builtin_fmaf(R7, mu1, R6 * mu0)) + t2;
-        bool ok = ok_g && (tz >= near_plane) && (tz <= far_plane);
-
-        // camera-frame covariance Rv S3 Rv^T
-        const float Rv[9] = {R0, R1, R2, R3, R4, R5, R6, R7, R8};
-        float Tm[9], Cc[9];
+        // camera-frame covariance Rv Sigma3 Rv^T
+        double Tm[9], Cc[9];
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                Tm[3 * i + j] = __builtin_fmaf(Rv[3 * i + 2], S3[6 + j],
-                                               __builtin_fmaf(Rv[3 * i + 1], S3[3 + j], Rv[3 * i] * S3[j]));
+                Tm[3 * i + j] = (R[3 * i] * S3[j] + R[3 * i + 1] * S3[3 + j]) + R[3 * i + 2] * S3[6 + j];
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                Cc[3 * i + j] = __builtin_fmaf(Tm[3 * i + 2], Rv[3 * j + 2],
-                                               __builtin_fmaf(Tm[3 * i + 1], Rv[3 * j + 1], Tm[3 * i] * Rv[3 * j]));
+                Cc[3 * i + j] = (Tm[3 * i] * R[3 * j] + Tm[3 * i + 1] * R[3 * j + 1]) + Tm[3 * i + 2] * R[3 * j + 2];
 
-        const float limx = cams.lim[v][0], limy = cams.lim[v][1];  // kFovClamp ((W / 2) / fx), likewise y
-        const float ux = tx / tz, uy = ty / tz;
-        const float uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
-        const float uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
-        const float txc = uxc * tz, tyc = uyc * tz;
-        const float tz2 = tz * tz;
-        const float j00 = fx / tz, j02 = -(fx * txc) / tz2;
-        const float j11 = fy / tz, j12 = -(fy * tyc) / tz2;
-        const float u00 = j00 * Cc[0] + j02 * Cc[6];
-        const float u01 = j00 * Cc[1] + j02 * Cc[7];
-        const float u02 = j00 * Cc[2] + j02 * Cc[8];
-        const float u11 = j11 * Cc[4] + j12 * Cc[7];
-        const float u12 = j11 * Cc[5] + j12 * Cc[8];
-        const float a = (u00 * j00 + u02 * j02) + kDilation;
-        const float b = u01 * j11 + u02 * j12;
-        const float cq = (u11 * j11 + u12 * j12) + kDilation;
-        const float det = a * cq - b * b;
-        ok = ok && (det > 0.0f);
+        // perspective Jacobian at the centre clamped to kFovClamp x the half field of view
+        const double limx = cams.lim[v][0], limy = cams.lim[v][1];
+        const int clip = fov_clip_bits(t, cams.lim[v]);
+        const double ux = tx / tz, uy = ty / tz;
+        const double uxc = (clip & 1) ? (ux < 0.0 ? -limx : limx) : ux;
+        const double uyc = (clip & 2) ? (uy < 0.0 ? -limy : limy) : uy;
+        const double txc = uxc * tz, tyc = uyc * tz;
+        const double tz2 = tz * tz;
+        const double j00 = (double)fx / tz, j02 = -((double)fx * txc) / tz2;
+        const double j11 = (double)fy / tz, j12 = -((double)fy * tyc) / tz2;
+        const double u00 = j00 * Cc[0] + j02 * Cc[6];
+        const double u01 = j00 * Cc[1] + j02 * Cc[7];
+        const double u02 = j00 * Cc[2] + j02 * Cc[8];
+        const double u11 = j11 * Cc[4] + j12 * Cc[7];
+        const double u12 = j11 * Cc[5] + j12 * Cc[8];
+        const double ar = u00 * j00 + u02 * j02, cr = u11 * j11 + u12 * j12;
+        const double a = ar + kDilation;
+        const double b = u01 * j11 + u02 * j12;
+        const double cq = cr + kDilation;
+        const double det = a * cq - b * b;
+        const double kDblMax = 1.7976931348623157e308;
+        ok = ok && (det > 0.0) && (det <= kDblMax) && (a <= kDblMax) && (cq <= kDblMax);
+        const float a32 = (float)a, b32 = (float)b, c32 = (float)cq, d32 = (float)det;
+        ok = ok && (d32 > 0.0f) && (d32 <= 3.40282347e+38f) && (a32 <= 3.40282347e+38f) && (c32 <= 3.40282347e+38f);
         // antialiased mode: opacity scaled by sqrt(det of the undilated covariance / det)
         float opx = op;
         if (AA) {
-            const float a_r = u00 * j00 + u02 * j02;
-            const float c_r = u11 * j11 + u12 * j12;
-            const float det_r = a_r * c_r - b * b;
-            opx = op * (det_r > 0.0f ? __builtin_sqrtf(det_r / det) : 0.0f);
+            const double det_r = ar * cr - b * b;
+            opx = op * (det_r > 0.0 ? __builtin_sqrtf((float)(det_r / det)) : 0.0f);
         }
-        const float idet = 1.0f / det;
-        const float ca = cq * idet, cb = -b * idet, cc = a * idet;
-        const float mid = 0.5f * (a + cq);
-        const float disc = mid * mid - det;
+        // 3-sigma radius (float32)
+        const float mid = 0.5f * (a32 + c32);
+        const float disc = mid * mid - d32;
         const float lam = mid + __builtin_sqrtf(disc > kEigFloor ? disc : kEigFloor);
         const float rad = __builtin_ceilf(3.0f * __builtin_sqrtf(lam));
-        const float mx = fx * (tx / tz) + cx;
-        const float my = fy * (ty / tz) + cy;
+        // projected centre in float64, kept as the float32 pair hi + lo
+        const double mx = (double)fx * ux + (double)cx;
+        const double my = (double)fy * uy + (double)cy;
+        const float hx = (float)mx, hy = (float)my;
+        const float lx = (float)(mx - (double)hx), ly = (float)(my - (double)hy);
 
-        const float fx0 = (mx - rad) * 0.0625f, fx1 = ((mx + rad) + 15.0f) * 0.0625f;
-        const float fy0 = (my - rad) * 0.0625f, fy1 = ((my + rad) + 15.0f) * 0.0625f;
+        const float fx0 = (hx - rad) * 0.0625f, fx1 = ((hx + rad) + 15.0f) * 0.0625f;
+        const float fy0 = (hy - rad) * 0.0625f, fy1 = ((hy + rad) + 15.0f) * 0.0625f;
         auto clamp_tile = [](float f, int n) -> int {
             return !(f > 0.0f) ? 0 : (f >= (float)n ? n : (int)f);
         };
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         if (!ok) {
             rec0[rid] = make_float4(0.f, 0.f, 0.f, 0.f);
             rec1[rid] = make_float4(0.f, 0.f, 0.f, 0.f);
-            rec2[rid] = make_float2(0.f, 0.f);
+            rec2[rid] = make_float4(0.f, 0.f, 0.f, 0.f);
             rect[rid] = make_uint2(0u, 0u);
             depth_key[rid] = 0xffffffffu;
             tiles_touched[rid] = 0u;
@@ -158,11 +160,19 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
             continue;
         }
 
-        // colour along the direction from the camera centre -Rv^T t
+        // exponent factors (float32): k Sigma2^-1 = L L^T, L = [[s1, 0], [s2, s3]]
+        const float s3 = __builtin_sqrtf(kHalfLog2e / c32);
+        const float s1 = __builtin_sqrtf((kHalfLog2e * c32) / d32);
+        const float s2 = -((kHalfLog2e * b32) / d32) / s1;
+
+        // colour along the direction from the camera centre -Rv^T t (float32)
+        const float R0 = cam[0], R1 = cam[1], R2 = cam[2], R3 = cam[3], R4 = cam[4], R5 = cam[5];
+        const float R6 = cam[6], R7 = cam[7], R8 = cam[8];
+        const float t0 = cam[9], t1 = cam[10], t2 = cam[11];
         const float ccx = -((R0 * t0 + R3 * t1) + R6 * t2);
         const float ccy = -((R1 * t0 + R4 * t1) + R7 * t2);
         const float ccz = -((R2 * t0 + R5 * t1) + R8 * t2);
-        const float dx = mu0 - ccx, dy = mu1 - ccy, dz = mu2 - ccz;
+        const float dx = means[3 * g] - ccx, dy = means[3 * g + 1] - ccy, dz = means[3 * g + 2] - ccz;
         const float len = __builtin_sqrtf((dx * dx + dy * dy) + dz * dz);
         const float il = 1.0f / len;
         float B[D];
@@ -176,14 +186,12 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
             pre[ch] = acc + 0.5f;
         }
 
-        const float4 r0v = make_float4(mx, my, ca * kNegHalfLog2e, cb * kNegLog2e);
-        const float qcv = cc * kNegHalfLog2e;
-        rec0[rid] = r0v;
-        rec1[rid] = make_float4(qcv, opx, pre[0], pre[1]);
-        rec2[rid] = make_float2(pre[2], __uint_as_float(entry_box_pack(r0v, qcv, opx)));
+        rec0[rid] = make_float4(hx, hy, s1, s2);
+        rec1[rid] = make_float4(s3, opx, pre[0], pre[1]);
+        rec2[rid] = make_float4(pre[2], __uint_as_float(entry_box_pack(s1, s2, s3, opx)), lx, ly);
         const uint2 rc = make_uint2((uint32_t)x0 | ((uint32_t)y0 << 16), (uint32_t)x1 | ((uint32_t)y1 << 16));
         rect[rid] = rc;
-        depth_key[rid] = __float_as_uint(tz);
+        depth_key[rid] = __float_as_uint((float)tz);
         tiles_touched[rid] = (uint32_t)((x1 - x0) * (y1 - y0));
         if (pay_init) pay_init[rid] = pack_rect(rc);
     }

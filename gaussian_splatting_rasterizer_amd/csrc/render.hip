@@ -7,8 +7,9 @@
 // One 256-thread block per tile; the four wave64s each own an 8x8 pixel
 // quadrant, so a wave's lanes stay spatially coherent and a wave whose 64
 // pixels are all saturated stops.  Batches of 256 list entries are gathered
-// (one per thread) into LDS -- centre, exponent coefficients, opacity, clamped
-// colour, and a conservative box of the pixels the entry can reach -- and each
+// (one per thread) into LDS -- centre relative to the tile, exponent factors,
+// opacity, clamped colour, and a conservative box of the pixels the entry can
+// reach -- and each
 // wave compacts, in list order, the entries whose box meets its quadrant, then
 // walks only those with broadcast LDS reads.  The box is conservative for the
 // float32 evaluation, so the skipped entries are exactly ones every pixel of
@@ -33,7 +34,7 @@ constexpr int kRenderBatch = 256;
 template <bool STATS>
 __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
-                                                const float2* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
+                                                const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
                                                 float bg0, float bg1, float bg2, float* __restrict__ color,
                                                 float* __restrict__ T_out, int32_t* __restrict__ n_out,
                                                 float4* __restrict__ pixel, uint2* __restrict__ pixel_stats,
@@ -46,8 +47,8 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
              i += (int64_t)gridDim.x * blockDim.x)
             slot_bits[i] = 0u;
     }
-    __shared__ float4 s0[kRenderBatch];   // {mx, my, qa, qb}
-    __shared__ float4 s1[kRenderBatch];   // {qc, opacity, colour r, colour g}
+    __shared__ float4 s0[kRenderBatch];   // {tile-relative centre (2), s1, s2}
+    __shared__ float4 s1[kRenderBatch];   // {s3, opacity, colour r, colour g}
     __shared__ float s2[kRenderBatch];    // colour b
     __shared__ float4 sbox[kRenderBatch]; // conservative box of the pixels the entry can reach
     __shared__ uint8_t slist[4][kRenderBatch];
@@ -64,9 +65,11 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     const int pxi = qx + (lane & 7);
     const int pyi = qy + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
-    // pixel-centre range of this wave's 8x8 quadrant
-    const float qx0 = (float)qx + 0.5f, qx1 = (float)qx + 7.5f, qy0 = (float)qy + 0.5f, qy1 = (float)qy + 7.5f;
+    // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
+    const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
+    // pixel-centre range of this wave's 8x8 quadrant, tile-relative
+    const float qx0 = (float)((wave & 1) * 8) + 0.5f, qx1 = qx0 + 7.0f;
+    const float qy0 = (float)((wave >> 1) * 8) + 0.5f, qy1 = qy0 + 7.0f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -95,11 +98,12 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
-            const float2 c = rec2[rid];
-            s0[threadIdx.x] = a;
+            const float4 c = rec2[rid];
+            const float mxt = tile_centre(a.x, c.z, tx), myt = tile_centre(a.y, c.w, ty);
+            s0[threadIdx.x] = make_float4(mxt, myt, a.z, a.w);
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(c.x);
-            sbox[threadIdx.x] = entry_box_unpack(a.x, a.y, __float_as_uint(c.y));
+            sbox[threadIdx.x] = entry_box_unpack(mxt, myt, __float_as_uint(c.y));
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kRenderBatch, rg.y - base);
@@ -129,9 +133,9 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                 const float4 b = s1[j];
                 // evaluated in every lane; the decisions below mask lanes that are done or beyond the cut
                 const float dx = px - a.x, dy = py - a.y;
-                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
-                const bool near = !done && e >= kECutoff;
-                const float aG = b.y * exp2_spec(e);
+                const float S = quad_S(a.z, a.w, b.x, dx, dy);
+                const bool near = !done && S <= kSCutoff;
+                const float aG = b.y * exp2_spec(-S);
                 const float alpha = aG < kAlphaMax ? aG : kAlphaMax;
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);

@@ -52,7 +52,7 @@ constexpr int kReplayBatch = 128;
 __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
                                                 const uint32_t* __restrict__ slot_base,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
-                                                const float2* __restrict__ rec2, const uint2* __restrict__ rect,
+                                                const float4* __restrict__ rec2, const uint2* __restrict__ rect,
                                                 int64_t G, int T, int TX, int W, int H, const float4* __restrict__ pixel, const float* __restrict__ observed,
                                                 const uint8_t* __restrict__ events, float eps, float den_min,
                                                 float4* __restrict__ partials, uint32_t* __restrict__ slot_bits,
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     __shared__ float s2[kReplayBatch];
     __shared__ uint8_t s_evb[kReplayBatch];    // event bits of each staged entry (bit w: wave w)
     __shared__ uint32_t s_slot[kReplayBatch];  // partial slot of each staged pair
-    __shared__ uint8_t s_mask[kReplayBatch];   // colour clamp mask bits (pre-clamp colour >= 0), r g b
+    __shared__ uint8_t s_mask[kReplayBatch];   // colour clamp mask bits (pre-clamp colour finite and >= 0), r g b
     __shared__ uint8_t slist[4][kReplayBatch];
     __shared__ __align__(16) float sp[4][kReplayBatch][8];
 
@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     const int pxi = qx + (lane & 7);
     const int pyi = qy + (lane >> 3);
     const bool inside = pxi < W && pyi < H;
-    const float px = (float)pxi + 0.5f, py = (float)pyi + 0.5f;
+    // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
+    const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -103,16 +104,16 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
-            const float2 c = rec2[rid];
+            const float4 c = rec2[rid];
             const uint2 rc = rect[rid];
-            s0[threadIdx.x] = a;
+            s0[threadIdx.x] = make_float4(tile_centre(a.x, c.z, tx), tile_centre(a.y, c.w, ty), a.z, a.w);
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = clamp_colour(c.x);
             s_evb[threadIdx.x] = events[i];
             // slot of this (tile, Gaussian) pair: the record's slot base + row-major tile index
             const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16, wx = (rc.y & 0xffffu) - x0;
             s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
-            s_mask[threadIdx.x] = (uint8_t)((b.z >= 0.0f ? 1u : 0u) | (b.w >= 0.0f ? 2u : 0u) | (c.x >= 0.0f ? 4u : 0u));
+            s_mask[threadIdx.x] = (uint8_t)((colour_ok(b.z) ? 1u : 0u) | (colour_ok(b.w) ? 2u : 0u) | (colour_ok(c.x) ? 4u : 0u));
         }
         const int cnt = (int)min((uint32_t)kReplayBatch, rg.y - base);
         // this wave's partial rows start at zero; entries it contributes to overwrite theirs
@@ -136,9 +137,9 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 const float4 b = s1[j];
                 // evaluated in every lane; the decisions mask lanes that are done or beyond the cut
                 const float dx = px - a.x, dy = py - a.y;
-                const float e = __builtin_fmaf(dx, __builtin_fmaf(a.z, dx, a.w * dy), (b.x * dy) * dy);
-                const bool near = !done && e >= kECutoff;
-                const float aG = b.y * exp2_spec(e);
+                const float S = quad_S(a.z, a.w, b.x, dx, dy);
+                const bool near = !done && S <= kSCutoff;
+                const float aG = b.y * exp2_spec(-S);
                 const bool clamped = !(aG < kAlphaMax);
                 const float alpha = clamped ? kAlphaMax : aG;
                 const bool pass = near && alpha >= kAlphaMin;
@@ -196,13 +197,13 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 acc.z += q.z;
                 acc.w += q.w;
             }
-            // per pair: the conic applied to U_mu (undoing the exponent scaling of the
-            // stored coefficients) and the colour clamp mask applied to U_c
+            // per pair: the conic applied to U_mu (from the exponent factors, k conic = L L^T) and the
+            // colour clamp mask applied to U_c
             if (h == 0) {
-                // (the scale back is a product with the constants' reciprocals: these values take no decision)
-                constexpr float kInvNegHalfLog2e = 1.0f / kNegHalfLog2e, kInvNegLog2e = 1.0f / kNegLog2e;
-                const float ca = s0[j].z * kInvNegHalfLog2e, cb = s0[j].w * kInvNegLog2e,
-                            cc = s1[j].x * kInvNegHalfLog2e;
+                // (values only: no decision is taken on them)
+                const float f1 = s0[j].z, f2 = s0[j].w, f3 = s1[j].x;
+                const float ca = (f1 * f1) * kInvHalfLog2e, cb = (f1 * f2) * kInvHalfLog2e,
+                            cc = __builtin_fmaf(f2, f2, f3 * f3) * kInvHalfLog2e;
                 acc = make_float4(acc.x, acc.y, ca * acc.z + cb * acc.w, cb * acc.z + cc * acc.w);
             } else {
                 const uint32_t m = s_mask[j];

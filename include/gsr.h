@@ -252,12 +252,13 @@ GSR_API gs_status gs_debug_exp2(const float* in, float* out, int64_t n, hipStrea
 
 /* Copy an internal workspace array into the caller's device buffer `dst`
  * (`bytes` must be at least the array size; the call fails otherwise):
- *   GS_EXPORT_RECORDS   after gs_project:  [3, n_views*n, 4] float32, planes
- *       {mx, my, qa, qb}, {qc, opacity, pre_r, pre_g},
- *       {pre_b, <entry box: two binary16 half-widths, x low>, <x0 | y0 << 16>,
- *       <x1 | y1 << 16>} (tile rectangle [x0, x1) x [y0, y1)), record index
- *       v*n + g, qa..qc scaled so that the Gaussian weight at offset
- *       (dx, dy) = pixel - centre is 2^(qa dx^2 + qb dx dy + qc dy^2); culled
+ *   GS_EXPORT_RECORDS   after gs_project:  [4, n_views*n, 4] float32, planes
+ *       {mx, my, s1, s2}, {s3, opacity, pre_r, pre_g},
+ *       {pre_b, <entry box: two binary16 half-widths, x low>, mx_lo, my_lo},
+ *       {<x0 | y0 << 16>, <x1 | y1 << 16>, -, -} (tile rectangle
+ *       [x0, x1) x [y0, y1)), record index v*n + g; the projected centre is
+ *       (mx + mx_lo, my + my_lo) and the Gaussian weight at offset
+ *       (dx, dy) = pixel - centre is 2^-((s1 dx + s2 dy)^2 + (s3 dy)^2); culled
  *       records are all zero
  *   GS_EXPORT_DEPTH_KEYS after gs_project: [n_views*n] uint32 depth bits
  *       (0xffffffff when culled)

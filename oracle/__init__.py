@@ -38,9 +38,11 @@ _LIB_PATH = os.path.join(_OUT_DIR, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
-REC32_FIELDS = ["culled", "mx", "my", "ca", "cb", "cc", "qa", "qb", "qc", "opac", "pre_r", "pre_g",
+REC32_FIELDS = ["culled", "mx", "my", "mx_lo", "my_lo", "s1", "s2", "s3", "clip_bits", "opac", "pre_r", "pre_g",
                 "pre_b", "depth", "radius", "x0", "y0", "x1", "y1", "clamp_bits"]
 NACC_FIXED = 8  # W, A_alpha, A_mu_x, A_mu_y, |A_alpha|, |A_mu_x|, |A_mu_y|, n_pix
+NACC_SENS = 9   # after the 6d SH sums: sensitivity of (A_alpha, A_mu_x, A_mu_y) to the residual, to the suffix,
+                # and to the projected centre
 
 
 def build(force: bool = False) -> str:
@@ -121,8 +123,7 @@ def constants() -> dict:
     lib = _load()
     out = np.zeros(28, dtype=np.float32)
     lib.orc_constants(_ptr(out))
-    return {"alpha_min": out[0], "exp2_coef": out[1:9].copy(), "neg_log2e": out[9],
-            "neg_half_log2e": out[10], "sh": out[11:27].copy()}
+    return {"alpha_min": out[0], "exp2_coef": out[1:9].copy(), "half_log2e": out[9], "sh": out[11:27].copy()}
 
 
 def sh_basis64(dirs: np.ndarray, d: int) -> np.ndarray:
@@ -178,6 +179,7 @@ class OracleScene:
             raise ValueError("oracle rejected the scene")
         self.n_pairs = None
         self.n_sel = None
+        self._sel = None
 
     def close(self):
         if self.handle:
@@ -224,6 +226,7 @@ class OracleScene:
         if gids is None:
             self.lib.orc_select(self.handle, None, -1)
             self.n_sel = self.G
+            self._sel = None
         else:
             gids = np.ascontiguousarray(gids, dtype=np.int32)
             self._sel = gids
@@ -268,7 +271,7 @@ class OracleScene:
         return out
 
     def acc(self) -> np.ndarray:
-        na = NACC_FIXED + 6 * self.d
+        na = NACC_FIXED + 6 * self.d + NACC_SENS
         out = np.empty((self.n_sel, self.V, na), dtype=np.float64)
         self.lib.orc_get_acc(self.handle, _ptr(out))
         return out
@@ -413,3 +416,76 @@ def full_reference(scene, obs, eps=1e-6, den_min=1e-3, lam=1.0, gids=None, tiles
     elapsed = time.perf_counter() - t0
     return {"oracle": o, "color": color, "T": T, "n": n, "T64": T64, "tokens": tok,
             "seconds": elapsed}
+
+
+TOKEN_RTOL = 1e-3          # per block, relative to the block's own norm (Renderer Score Tokens plan, Block 0)
+TERM_RTOL = 1e-4           # float32 rounding of one signed per-pixel score term, relative to its magnitude
+
+
+CENTRE_ATOL = 2.0 ** -20    # px: half an ulp of a tile-relative coordinate below 16 (float32)
+
+
+def token_block_errors(o, z, zr, eps=1e-6, catol=1e-5, term_rtol=TERM_RTOL, centre_atol=CENTRE_ATOL):
+    """Per-block comparison of tokens `z` [n_sel, 9 + 3d] with the oracle's `zr` for the
+    Gaussians selected in the OracleScene `o` (after its render + replay).
+
+    Blocks (Final Token and Updater): b_mu (3), s_alpha (1), s_SH (3d), stats (log Q,
+    e~ (3), log(tr A + eps)).  Each block's error norm is held to TOKEN_RTOL of the
+    block's own norm plus a floor that bounds what a correct float32 evaluation may
+    move it by:
+      * the signed-sum blocks (b_mu, s_alpha, s_SH) are sums of per-pixel terms that may
+        cancel: `term_rtol` (default TERM_RTOL) of the sum of the terms' magnitudes, plus what the residual
+        and the suffix may move when the rendered colour is off by at most `catol` per
+        channel (the colour tolerance; the suffix is a tail of the same composite): the
+        oracle's sensitivity sums times `catol`, plus what moving the projected centre by
+        `centre_atol` px (the float32 rounding of a tile-relative centre; it decides the
+        sign of the centre terms at pixels that sit on the centre) moves them by; for b_mu
+        these are pulled back through |J| like the score itself;
+      * the statistics block: 10 * catol absolute per entry (logarithms of float32 sums
+        of positive terms, and eigenvalue ratios <= 1).
+    Returns {block: (max ratio of error to bound, argmax)}; a ratio <= 1 passes."""
+    acc = o.acc()                                   # [n_sel, V, na]
+    d, V = o.d, o.V
+    na = acc.shape[2]
+    sens = acc[:, :, na - NACC_SENS:]
+    Q = eps + np.sum(eps + acc[:, :, 0], axis=1)    # [n_sel]
+    sel = np.arange(o.G) if o._sel is None else o._sel
+    r64 = o.records64()[:, sel]                     # [V, n_sel, 15]
+    culled = o.records32()[:, sel, 0] != 0          # [V, n_sel]
+    J = np.where(culled[:, :, None], 0.0, r64[:, :, 9:15]).reshape(V, -1, 2, 3)
+    z = np.asarray(z, dtype=np.float64)
+    zr = np.asarray(zr, dtype=np.float64)
+    out = {}
+
+    def report(name, err, bound):
+        ratio = err / bound
+        k = int(np.argmax(ratio)) if ratio.size else 0
+        out[name] = (float(ratio.max()) if ratio.size else 0.0, k)
+
+    # b_mu = (1/Q) sum_v J_v^T A_mu,v
+    f_mu = (term_rtol * acc[:, :, 5:7] + catol * (sens[:, :, 1:3] + sens[:, :, 4:6])
+            + centre_atol * sens[:, :, 7:9])                                              # [n_sel, V, 2]
+    floor_mu = np.einsum("vgrj,gvr->gj", np.abs(J), f_mu) / Q[:, None]
+    report("b_mu", np.linalg.norm(z[:, 0:3] - zr[:, 0:3], axis=1),
+           TOKEN_RTOL * np.linalg.norm(zr[:, 0:3], axis=1) + np.linalg.norm(floor_mu, axis=1) + 1e-12)
+    # s_alpha = (1/Q) sum_v A_alpha,v
+    floor_a = (term_rtol * acc[:, :, 4] + catol * (sens[:, :, 0] + sens[:, :, 3])
+               + centre_atol * sens[:, :, 6]).sum(axis=1) / Q
+    report("s_alpha", np.abs(z[:, 3] - zr[:, 3]), TOKEN_RTOL * np.abs(zr[:, 3]) + floor_a + 1e-12)
+    # s_SH = (1/Q) sum_v M^color B (x) U_c,v ; |B_k| <= 1 for degree <= 3
+    k0 = NACC_FIXED
+    abs_sh = acc[:, :, k0 + 3 * d: k0 + 6 * d].sum(axis=1)
+    W = acc[:, :, 0].sum(axis=1)
+    floor_sh = (term_rtol * abs_sh + catol * W[:, None]) / Q[:, None]
+    sh = slice(4, 4 + 3 * d)
+    report("s_sh", np.linalg.norm(z[:, sh] - zr[:, sh], axis=1),
+           TOKEN_RTOL * np.linalg.norm(zr[:, sh], axis=1) + np.linalg.norm(floor_sh, axis=1) + 1e-12)
+    report("s_sh_elementwise", np.abs(z[:, sh] - zr[:, sh]).ravel(),
+           (TOKEN_RTOL * np.abs(zr[:, sh]) + floor_sh + 1e-12).ravel())
+    # statistics block
+    st = slice(4 + 3 * d, 9 + 3 * d)
+    report("stats", np.linalg.norm(z[:, st] - zr[:, st], axis=1),
+           TOKEN_RTOL * np.linalg.norm(zr[:, st], axis=1) + 1e-12)
+    report("stats_elementwise", np.abs(z[:, st] - zr[:, st]).ravel(),
+           np.full(z[:, st].size, 10.0 * catol))
+    return out

@@ -64,15 +64,14 @@
 #define ALPHA_MAX_F 0.99f
 #define ALPHA_MAX_D 0.99
 #define T_MIN_F 1e-4f
-#define DILATION_F 0.3f
 #define EIG_FLOOR_F 0.1f
-#define FOV_CLAMP_F 1.3f
-#define E_CUTOFF_F (-8.0f)
+#define FOV_CLAMP_D 1.3
+#define DILATION_D 0.3
+#define S_CUTOFF_F 8.0f
 
 static float g_alpha_min;     /* float32 nearest to 1/255 */
 static float g_exp2_coef[8];  /* float32 nearest to ln(2)^j / j! */
-static float g_nl2e;          /* float32 nearest to -log2(e) */
-static float g_nhl2e;         /* float32 nearest to -log2(e) / 2 */
+static float g_hl2e;          /* float32 nearest to log2(e) / 2 */
 static float g_sh32[16];      /* float32 SH normalisation constants (signed) */
 static double g_sh64[16];
 
@@ -88,8 +87,7 @@ static void init_constants(void)
         c = c * ln2 / (long double)(j + 1);
     }
     const long double log2e = 1.442695040888963407359924681001892137L;
-    g_nl2e = (float)(-log2e);
-    g_nhl2e = (float)(-0.5L * log2e);
+    g_hl2e = (float)(0.5L * log2e);
     const long double pi = 3.141592653589793238462643383279502884L;
     long double k[16];
     /* real spherical harmonics, l <= 3, m = -l..l, classic graphics sign convention */
@@ -141,8 +139,8 @@ void orc_constants(float* out /* [28] */)
     init_constants();
     out[0] = g_alpha_min;
     for (int j = 0; j < 8; ++j) out[1 + j] = g_exp2_coef[j];
-    out[9] = g_nl2e;
-    out[10] = g_nhl2e;
+    out[9] = g_hl2e;
+    out[10] = 0.0f;
     for (int i = 0; i < 16; ++i) out[11 + i] = g_sh32[i];
     out[27] = 0.0f;
 }
@@ -213,13 +211,14 @@ void orc_sh_basis64(const double* dirs, int64_t n, int d, double* out)
  * ------------------------------------------------------------------------- */
 typedef struct {
     int culled;
-    float mx, my;        /* projected centre, pixels */
-    float ca, cb, cc;    /* conic: inverse of the dilated 2D covariance */
-    float qa, qb, qc;    /* G = 2^(qa dx^2 + qb dx dy + qc dy^2) */
+    float mx, my;        /* projected centre, pixels: the float32 nearest to the float64 centre */
+    float mx_lo, my_lo;  /* the float64 centre minus (mx, my), rounded to float32 */
+    float s1, s2, s3;    /* G = 2^-((s1 dx + s2 dy)^2 + (s3 dy)^2) */
+    int clip[2];         /* field-of-view clamp of the Jacobian active in x, y */
     float opac;
     float pre[3];        /* SH colour + 0.5 before the clamp */
     float col[3];        /* clamped colour */
-    int clamp_ok[3];     /* 1 where pre >= 0 (clamp inactive) */
+    int clamp_ok[3];     /* 1 where 0 <= pre <= FLT_MAX (clamp inactive) */
     int comp_ok;         /* antialiased mode: undilated 2D covariance determinant > 0 */
     float depth;
     float radius;
@@ -265,8 +264,29 @@ typedef struct {
 } scene;
 
 #define NACC_FIXED 8   /* W, Aa, Amu_x, Amu_y, |Aa|, |Amu_x|, |Amu_y|, n_pix */
-static int nacc(const scene* s) { return NACC_FIXED + 6 * s->d; } /* + ASH[d][3] + |ASH|[d][3] */
+#define NACC_SENS 9    /* sensitivity sums, after the SH sums (see orc_render_tiles) */
+static int nacc(const scene* s) { return NACC_FIXED + 6 * s->d + NACC_SENS; } /* + ASH[d][3] + |ASH|[d][3] + sens */
 
+/* The decision record of one (Gaussian, view) -- the written specification the
+ * GPU preprocess implements independently:
+ *  - geometry in float64 from the float32 inputs, every operation rounded once
+ *    in the order written (no fused multiply-adds): camera-space centre, the
+ *    quaternion's rotation (R(q) of the unnormalised quaternion scaled by
+ *    2 / |q|^2, which equals the rotation of q / |q|), M = R(q) diag(s),
+ *    Sigma3 = M M^T, Sigma_cam = R_v Sigma3 R_v^T, the perspective Jacobian at
+ *    the centre clamped to 1.3x the half field of view, the dilated 2D
+ *    covariance [[a, b], [b, c]] and its determinant, the projected centre;
+ *  - the 2D covariance and determinant rounded to float32, then in float32
+ *    (correctly rounded division and square root): the 3-sigma radius, the
+ *    exponent factors s1 = sqrt(k c / det), s2 = -((k b) / det) / s1,
+ *    s3 = sqrt(k / c) with k = RN(log2(e) / 2), so that the exponent at offset
+ *    (dx, dy) is -((s1 dx + s2 dy)^2 + (s3 dy)^2) = -k (dx, dy) Sigma2^-1 (dx, dy)^T
+ *    without the cancellation of the expanded quadratic form;
+ *  - the centre as a float32 pair hi + lo (hi = RN(mx), lo = RN(mx - hi)): the
+ *    rectangle is taken from hi, and evaluation uses the centre relative to the
+ *    tile, (hi - 16 tx) + lo, so that pixel offsets keep their precision far
+ *    from the image origin;
+ *  - the SH colour in float32 as before. */
 static void project32(const scene* s, int g, int v, rec32* r)
 {
     const float* mu = s->means + 3 * (int64_t)g;
@@ -281,61 +301,69 @@ static void project32(const scene* s, int g, int v, rec32* r)
 
     memset(r, 0, sizeof *r);
     r->culled = 1;
-    /* three-term dot products as fused multiply-add chains: fma(a2, b2, fma(a1, b1, a0 b0)) */
-    float tx = fmaf(R[2], mu[2], fmaf(R[1], mu[1], R[0] * mu[0])) + t[0];
-    float ty = fmaf(R[5], mu[2], fmaf(R[4], mu[1], R[3] * mu[0])) + t[1];
-    float tz = fmaf(R[8], mu[2], fmaf(R[7], mu[1], R[6] * mu[0])) + t[2];
-    if (!(tz >= s->near_plane) || !(tz <= s->far_plane)) return;
+    double Rd[9];
+    for (int i = 0; i < 9; ++i) Rd[i] = R[i];
+    const double m0 = mu[0], m1 = mu[1], m2 = mu[2];
+    const double tx = ((Rd[0] * m0 + Rd[1] * m1) + Rd[2] * m2) + (double)t[0];
+    const double ty = ((Rd[3] * m0 + Rd[4] * m1) + Rd[5] * m2) + (double)t[1];
+    const double tz = ((Rd[6] * m0 + Rd[7] * m1) + Rd[8] * m2) + (double)t[2];
+    if (!(tz >= (double)s->near_plane) || !(tz <= (double)s->far_plane)) return;
     if (!(op >= 0.0f) || !(op <= 1.0f)) return;
 
-    float n2 = ((qi[0] * qi[0] + qi[1] * qi[1]) + qi[2] * qi[2]) + qi[3] * qi[3];
-    if (!(n2 > 0.0f) || !(n2 <= FLT_MAX)) return;
-    float inv = 1.0f / sqrtf(n2);
-    float w = qi[0] * inv, x = qi[1] * inv, y = qi[2] * inv, z = qi[3] * inv;
-    float Rq[9];
-    Rq[0] = 1.0f - 2.0f * (y * y + z * z);
-    Rq[1] = 2.0f * (x * y - w * z);
-    Rq[2] = 2.0f * (x * z + w * y);
-    Rq[3] = 2.0f * (x * y + w * z);
-    Rq[4] = 1.0f - 2.0f * (x * x + z * z);
-    Rq[5] = 2.0f * (y * z - w * x);
-    Rq[6] = 2.0f * (x * z - w * y);
-    Rq[7] = 2.0f * (y * z + w * x);
-    Rq[8] = 1.0f - 2.0f * (x * x + y * y);
-    float M[9];
+    const double w = qi[0], x = qi[1], y = qi[2], z = qi[3];
+    const double n2 = ((w * w + x * x) + y * y) + z * z;
+    if (!(n2 > 0.0) || !(n2 <= DBL_MAX)) return;
+    const double q2 = 2.0 / n2;
+    double Rq[9];
+    Rq[0] = 1.0 - q2 * (y * y + z * z);
+    Rq[1] = q2 * (x * y - w * z);
+    Rq[2] = q2 * (x * z + w * y);
+    Rq[3] = q2 * (x * y + w * z);
+    Rq[4] = 1.0 - q2 * (x * x + z * z);
+    Rq[5] = q2 * (y * z - w * x);
+    Rq[6] = q2 * (x * z - w * y);
+    Rq[7] = q2 * (y * z + w * x);
+    Rq[8] = 1.0 - q2 * (x * x + y * y);
+    double M[9];
     for (int i = 0; i < 3; ++i)
-        for (int j = 0; j < 3; ++j) M[3 * i + j] = Rq[3 * i + j] * sc[j];
-    float S3[9];
-    for (int i = 0; i < 3; ++i)
-        for (int j = 0; j < 3; ++j)
-            S3[3 * i + j] = fmaf(M[3 * i + 2], M[3 * j + 2], fmaf(M[3 * i + 1], M[3 * j + 1], M[3 * i] * M[3 * j]));
-    float Tm[9], Cc[9];
+        for (int j = 0; j < 3; ++j) M[3 * i + j] = Rq[3 * i + j] * (double)sc[j];
+    double S3[9];
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j)
-            Tm[3 * i + j] = fmaf(R[3 * i + 2], S3[6 + j], fmaf(R[3 * i + 1], S3[3 + j], R[3 * i] * S3[j]));
+            S3[3 * i + j] = (M[3 * i] * M[3 * j] + M[3 * i + 1] * M[3 * j + 1]) + M[3 * i + 2] * M[3 * j + 2];
+    double Tm[9], Cc[9];
     for (int i = 0; i < 3; ++i)
         for (int j = 0; j < 3; ++j)
-            Cc[3 * i + j] = fmaf(Tm[3 * i + 2], R[3 * j + 2], fmaf(Tm[3 * i + 1], R[3 * j + 1], Tm[3 * i] * R[3 * j]));
+            Tm[3 * i + j] = (Rd[3 * i] * S3[j] + Rd[3 * i + 1] * S3[3 + j]) + Rd[3 * i + 2] * S3[6 + j];
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            Cc[3 * i + j] = (Tm[3 * i] * Rd[3 * j] + Tm[3 * i + 1] * Rd[3 * j + 1]) + Tm[3 * i + 2] * Rd[3 * j + 2];
 
-    float limx = FOV_CLAMP_F * ((0.5f * (float)s->W) / fx);
-    float limy = FOV_CLAMP_F * ((0.5f * (float)s->H) / fy);
-    float ux = tx / tz, uy = ty / tz;
-    float uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
-    float uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
-    float txc = uxc * tz, tyc = uyc * tz;
-    float tz2 = tz * tz;
-    float j00 = fx / tz, j02 = -(fx * txc) / tz2;
-    float j11 = fy / tz, j12 = -(fy * tyc) / tz2;
-    float u00 = j00 * Cc[0] + j02 * Cc[6];
-    float u01 = j00 * Cc[1] + j02 * Cc[7];
-    float u02 = j00 * Cc[2] + j02 * Cc[8];
-    float u11 = j11 * Cc[4] + j12 * Cc[7];
-    float u12 = j11 * Cc[5] + j12 * Cc[8];
-    float a = (u00 * j00 + u02 * j02) + DILATION_F;
-    float b = u01 * j11 + u02 * j12;
-    float c = (u11 * j11 + u12 * j12) + DILATION_F;
-    float det = a * c - b * b;
-    if (!(det > 0.0f)) return;
+    /* field-of-view clamp of the Jacobian's lateral offset (decision shared with the backward) */
+    const double limx = FOV_CLAMP_D * ((0.5 * (double)s->W) / (double)fx);
+    const double limy = FOV_CLAMP_D * ((0.5 * (double)s->H) / (double)fy);
+    const double ux = tx / tz, uy = ty / tz;
+    r->clip[0] = ux < -limx || ux > limx;
+    r->clip[1] = uy < -limy || uy > limy;
+    const double uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
+    const double uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
+    const double txc = uxc * tz, tyc = uyc * tz;
+    const double tz2 = tz * tz;
+    const double j00 = (double)fx / tz, j02 = -((double)fx * txc) / tz2;
+    const double j11 = (double)fy / tz, j12 = -((double)fy * tyc) / tz2;
+    const double u00 = j00 * Cc[0] + j02 * Cc[6];
+    const double u01 = j00 * Cc[1] + j02 * Cc[7];
+    const double u02 = j00 * Cc[2] + j02 * Cc[8];
+    const double u11 = j11 * Cc[4] + j12 * Cc[7];
+    const double u12 = j11 * Cc[5] + j12 * Cc[8];
+    const double ar = u00 * j00 + u02 * j02, cr = u11 * j11 + u12 * j12;
+    const double a = ar + DILATION_D;
+    const double b = u01 * j11 + u02 * j12;
+    const double c = cr + DILATION_D;
+    const double det = a * c - b * b;
+    if (!(det > 0.0) || !(det <= DBL_MAX) || !(a <= DBL_MAX) || !(c <= DBL_MAX)) return;
+    const float a32 = (float)a, b32 = (float)b, c32 = (float)c, d32 = (float)det;
+    if (!(d32 > 0.0f) || !(d32 <= FLT_MAX) || !(a32 <= FLT_MAX) || !(c32 <= FLT_MAX)) return;
     /* antialiased mode: the 0.3 px^2 dilation widens the footprint, so opacity is
      * scaled by sqrt(det of the undilated 2D covariance / det of the dilated one),
      * which keeps the integrated weight and depends on depth through the
@@ -343,30 +371,35 @@ static void project32(const scene* s, int g, int v, rec32* r)
      * score stops gradient through) */
     float opx = op;
     if (s->antialiased) {
-        float a_r = u00 * j00 + u02 * j02;
-        float c_r = u11 * j11 + u12 * j12;
-        float det_r = a_r * c_r - b * b;
-        r->comp_ok = det_r > 0.0f;
-        opx = op * (r->comp_ok ? sqrtf(det_r / det) : 0.0f);
+        const double det_r = ar * cr - b * b;
+        r->comp_ok = det_r > 0.0;
+        opx = op * (r->comp_ok ? sqrtf((float)(det_r / det)) : 0.0f);
     }
-    float idet = 1.0f / det;
-    float ca = c * idet, cb = -b * idet, cc = a * idet;
-    float mid = 0.5f * (a + c);
-    float disc = mid * mid - det;
-    float lam = mid + sqrtf(disc > EIG_FLOOR_F ? disc : EIG_FLOOR_F);
-    float rad = ceilf(3.0f * sqrtf(lam));
-    float mx = fx * (tx / tz) + cx;
-    float my = fy * (ty / tz) + cy;
+    /* 3-sigma radius (float32) */
+    const float mid = 0.5f * (a32 + c32);
+    const float disc = mid * mid - d32;
+    const float lam = mid + sqrtf(disc > EIG_FLOOR_F ? disc : EIG_FLOOR_F);
+    const float rad = ceilf(3.0f * sqrtf(lam));
+    /* projected centre: float64, kept as hi + lo */
+    const double mx = (double)fx * ux + (double)cx;
+    const double my = (double)fy * uy + (double)cy;
+    const float hx = (float)mx, hy = (float)my;
+    const float lx = (float)(mx - (double)hx), ly = (float)(my - (double)hy);
 
-    float fx0 = (mx - rad) * 0.0625f, fx1 = ((mx + rad) + 15.0f) * 0.0625f;
-    float fy0 = (my - rad) * 0.0625f, fy1 = ((my + rad) + 15.0f) * 0.0625f;
+    const float fx0 = (hx - rad) * 0.0625f, fx1 = ((hx + rad) + 15.0f) * 0.0625f;
+    const float fy0 = (hy - rad) * 0.0625f, fy1 = ((hy + rad) + 15.0f) * 0.0625f;
 #define CLAMP_TILE(f, n) (!((f) > 0.0f) ? 0 : ((f) >= (float)(n) ? (n) : (int)(f)))
     int x0 = CLAMP_TILE(fx0, s->TX), x1 = CLAMP_TILE(fx1, s->TX);
     int y0 = CLAMP_TILE(fy0, s->TY), y1 = CLAMP_TILE(fy1, s->TY);
 #undef CLAMP_TILE
     if (x1 <= x0 || y1 <= y0) return;
 
-    /* view direction from the camera centre -R^T t */
+    /* exponent factors (float32) */
+    const float s3 = sqrtf(g_hl2e / c32);
+    const float s1 = sqrtf((g_hl2e * c32) / d32);
+    const float s2 = -((g_hl2e * b32) / d32) / s1;
+
+    /* view direction from the camera centre -R^T t (float32) */
     float ccx = -((R[0] * t[0] + R[3] * t[1]) + R[6] * t[2]);
     float ccy = -((R[1] * t[0] + R[4] * t[1]) + R[7] * t[2]);
     float ccz = -((R[2] * t[0] + R[5] * t[1]) + R[8] * t[2]);
@@ -380,20 +413,20 @@ static void project32(const scene* s, int g, int v, rec32* r)
         for (int k = 1; k < s->d; ++k) acc = fmaf(B[k], sh[3 * k + ch], acc);
         float pre = acc + 0.5f;
         r->pre[ch] = pre;
-        r->clamp_ok[ch] = pre >= 0.0f;
-        r->col[ch] = pre >= 0.0f ? pre : 0.0f;
+        /* the colour clamp: negative or non-finite colours are clamped to 0 and masked */
+        r->clamp_ok[ch] = pre >= 0.0f && pre <= FLT_MAX;
+        r->col[ch] = r->clamp_ok[ch] ? pre : 0.0f;
     }
     r->culled = 0;
-    r->mx = mx;
-    r->my = my;
-    r->ca = ca;
-    r->cb = cb;
-    r->cc = cc;
-    r->qa = ca * g_nhl2e;
-    r->qb = cb * g_nl2e;
-    r->qc = cc * g_nhl2e;
+    r->mx = hx;
+    r->my = hy;
+    r->mx_lo = lx;
+    r->my_lo = ly;
+    r->s1 = s1;
+    r->s2 = s2;
+    r->s3 = s3;
     r->opac = opx;
-    r->depth = tz;
+    r->depth = (float)tz;
     r->radius = rad;
     r->rect[0] = x0;
     r->rect[1] = y0;
@@ -486,10 +519,13 @@ static void forward64(const scene* s, int g, int v, fwd64* f)
         }
     const double limx = 1.3 * (0.5 * s->W / f->fx), limy = 1.3 * (0.5 * s->H / f->fy);
     const double ux = tx / tz, uy = ty / tz;
-    f->clip_x = ux < -limx || ux > limx;
-    f->clip_y = uy < -limy || uy > limy;
-    f->uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
-    f->uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
+    /* the clamp state is the record's decision, frozen (it equals this test at the unperturbed inputs:
+     * the same float64 operations) */
+    const rec32* r32 = &s->r32[(int64_t)v * s->G + g];
+    f->clip_x = r32->clip[0];
+    f->clip_y = r32->clip[1];
+    f->uxc = f->clip_x ? (ux < 0.0 ? -limx : limx) : ux;
+    f->uyc = f->clip_y ? (uy < 0.0 ? -limy : limy) : uy;
     double* Jc = f->Jc;
     Jc[0] = f->fx / tz;
     Jc[1] = 0;
@@ -616,7 +652,8 @@ void orc_scene_free(void* p)
 }
 
 /* Export the float32 records: per (v, g) 20 floats
- * [culled, mx, my, ca, cb, cc, qa, qb, qc, opac, pre r, g, b, depth, radius, x0, y0, x1, y1, clamp bits] */
+ * [culled, mx, my, mx_lo, my_lo, s1, s2, s3, clip bits (x | y << 1), opac, pre r, g, b, depth, radius,
+ *  x0, y0, x1, y1, clamp bits] */
 void orc_get_records32(const void* p, float* out)
 {
     const scene* s = (const scene*)p;
@@ -626,8 +663,9 @@ void orc_get_records32(const void* p, float* out)
         float* o = out + 20 * i;
         o[0] = (float)r->culled;
         o[1] = r->mx; o[2] = r->my;
-        o[3] = r->ca; o[4] = r->cb; o[5] = r->cc;
-        o[6] = r->qa; o[7] = r->qb; o[8] = r->qc;
+        o[3] = r->mx_lo; o[4] = r->my_lo;
+        o[5] = r->s1; o[6] = r->s2; o[7] = r->s3;
+        o[8] = (float)(r->clip[0] | (r->clip[1] << 1));
         o[9] = r->opac;
         o[10] = r->pre[0]; o[11] = r->pre[1]; o[12] = r->pre[2];
         o[13] = r->depth; o[14] = r->radius;
@@ -782,7 +820,11 @@ static void add(double* a, double x)
 static int composite_pixel_counted(const scene* s, int v, int x, int y, const int32_t* list, int64_t L,
                                    contrib* cl, double C[3], float* T32_out, double* T64_out, uint32_t work[2])
 {
-    float px = (float)x + 0.5f, py = (float)y + 0.5f;
+    /* float32 decisions at tile-relative coordinates: the pixel centre (x - 16 tx) + 1/2 and
+     * the entry's centre (mx - 16 tx) + mx_lo, likewise in y */
+    const int tx = x / TILE, ty = y / TILE;
+    const float tox = (float)(TILE * tx), toy = (float)(TILE * ty);
+    const float pxl = (float)(x - TILE * tx) + 0.5f, pyl = (float)(y - TILE * ty) + 0.5f;
     double pxd = x + 0.5, pyd = y + 0.5;
     float T32 = 1.0f;
     double T64 = 1.0;
@@ -791,12 +833,14 @@ static int composite_pixel_counted(const scene* s, int v, int x, int y, const in
     for (int64_t k = 0; k < L; ++k) {
         int g = list[k];
         const rec32* r = &s->r32[(int64_t)v * s->G + g];
-        float dx = px - r->mx, dy = py - r->my;
-        float e = fmaf(dx, fmaf(r->qa, dx, r->qb * dy), (r->qc * dy) * dy);
+        float mxt = (r->mx - tox) + r->mx_lo, myt = (r->my - toy) + r->my_lo;
+        float dx = pxl - mxt, dy = pyl - myt;
+        float u = fmaf(r->s1, dx, r->s2 * dy), w = r->s3 * dy;
+        float S = fmaf(u, u, w * w);
         if (work) work[0] = (uint32_t)(k + 1);
-        if (!(e >= E_CUTOFF_F)) continue;
+        if (!(S <= S_CUTOFF_F)) continue;
         if (work) work[1]++;
-        float aG = r->opac * orc_exp2f(e);
+        float aG = r->opac * orc_exp2f(-S);
         int clamped = !(aG < ALPHA_MAX_F);
         float a32 = clamped ? ALPHA_MAX_F : aG;
         if (!(a32 >= g_alpha_min)) continue;
@@ -948,6 +992,34 @@ void orc_render_tiles(void* p, const int64_t* tiles, int64_t n_tiles, const floa
                             add(&A[4], fabs(ta));
                             add(&A[5], fabs(tmx));
                             add(&A[6], fabs(tmy));
+                        }
+                        if (Ma) {
+                            /* Sensitivity sums (test diagnostics, not scores): how far each masked score
+                             * term can move when the residual moves by at most 1 per channel (weight
+                             * |factor| * |c - C+|_1) and when the suffix moves by at most 1 per channel
+                             * (weight |factor| * |r|_1 / den), for the opacity and the two centre terms. */
+                            double cd = 0, rn = 0;
+                            for (int ch = 0; ch < 3; ++ch) {
+                                cd += fabs(q->col[ch] - Cp[ch]);
+                                rn += fabs(rr[ch]);
+                            }
+                            double dx = pxd - q->mx, dy = pyd - q->my;
+                            double f3[3] = {c->T * c->alpha * (1.0 - q->opac_raw),
+                                            c->T * q->opac * c->G * (q->ca * dx + q->cb * dy),
+                                            c->T * q->opac * c->G * (q->cb * dx + q->cc * dy)};
+                            double* Sx = &A[NACC_FIXED + 6 * d];
+                            for (int j = 0; j < 3; ++j) {
+                                add(&Sx[j], fabs(f3[j]) * cd);
+                                add(&Sx[3 + j], fabs(f3[j]) * rn / den);
+                            }
+                            /* and when the projected centre moves by at most 1 along each axis: the
+                             * magnitudes of the terms' derivatives in (mx, my), summed over both axes
+                             * (g = conic (p - mu), dG/dmu = G g, dg_x/dmx = -ca, dg_x/dmy = -cb) */
+                            const double gx = q->ca * dx + q->cb * dy, gy = q->cb * dx + q->cc * dy;
+                            const double ag = fabs(gx) + fabs(gy), toGr = c->T * q->opac * c->G * fabs(rho);
+                            add(&Sx[6], c->T * (1.0 - q->opac_raw) * fabs(rho) * q->opac * c->G * ag);
+                            add(&Sx[7], toGr * (fabs(gx) * ag + fabs(q->ca) + fabs(q->cb)));
+                            add(&Sx[8], toGr * (fabs(gy) * ag + fabs(q->cb) + fabs(q->cc)));
                         }
                         const rec32* r = &s->r32[(int64_t)v * s->G + c->g];
                         for (int k2 = 0; k2 < d; ++k2)
@@ -1358,7 +1430,8 @@ static void backward_params(scene* s, const double* g2d, double* out)
                 double gB = 0.0;
                 for (int ch = 0; ch < 3; ++ch) {
                     o[11 + 3 * k + ch] += B[k] * gpre[ch];
-                    gB += sh[3 * k + ch] * gpre[ch];
+                    /* a clamped channel (also one with non-finite coefficients) has no direction term */
+                    if (s->r32[rid].clamp_ok[ch]) gB += sh[3 * k + ch] * gpre[ch];
                 }
                 for (int j = 0; j < 3; ++j) gdir[j] += gB * dB[k][j];
             }

@@ -114,48 +114,44 @@ def test_records_bit_exact(name):
     assert np.array_equal(keys == 0xFFFFFFFF, ~live)
     assert np.array_equal(keys[live], r32[live, 13].view(np.uint32))
     got = np.stack([rec[0, :, 0], rec[0, :, 1], rec[0, :, 2], rec[0, :, 3], rec[1, :, 0], rec[1, :, 1],
-                    rec[1, :, 2], rec[1, :, 3], rec[2, :, 0]], axis=1)[live]
-    want = r32[live][:, [1, 2, 6, 7, 8, 9, 10, 11, 12]]
+                    rec[1, :, 2], rec[1, :, 3], rec[2, :, 0], rec[2, :, 2], rec[2, :, 3]], axis=1)[live]
+    want = r32[live][:, [1, 2, 5, 6, 7, 9, 10, 11, 12, 3, 4]]
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), np.argwhere(got != want)[:5]
-    lo = rec[2, live, 2].view(np.uint32)
-    hi = rec[2, live, 3].view(np.uint32)
+    lo = rec[3, live, 0].view(np.uint32)
+    hi = rec[3, live, 1].view(np.uint32)
     rect = np.stack([lo & 0xFFFF, lo >> 16, hi & 0xFFFF, hi >> 16], axis=1)
     assert np.array_equal(rect, r32[live][:, 15:19].astype(np.uint32))
 
 
-def _box_f64(a, b, c, opac, mx, my):
-    """Reference half-widths of the region where an entry can pass the alpha test:
-    Q(d) = a dx^2 + 2 b dx dy + c dy^2 <= t_eff with t_eff = (min(8, log2 255 o) + 1e-5) /
-    (1 - 8u (cond + 1)), u = 2^-24, widened by 0.01 px + 1e-6 (|centre| + half-width);
-    float64 from the float32 coefficients.  Returns (wx, wy, kind) with kind 0 finite,
-    1 unbounded (never skipped), -1 empty."""
-    with np.errstate(divide="ignore", invalid="ignore"):
+def _box_f64(s1, s2, s3, opac):
+    """Reference half-widths of the region where an entry can pass the alpha test: with
+    K = L L^T, L = [[s1, 0], [s2, s3]], S*(d) = d^T K d <= t_eff,
+    t_eff = (min(8, log2 255 o) + 1e-5) / (1 - u (8 + 10 sqrt(kappa))), u = 2^-24,
+    kappa = max(Kinv_xx, Kinv_yy)^2 / det(Kinv), widened by 0.01 px; float64 from the
+    float32 factors.  Returns (wx, wy, kind) with kind 0 finite, 1 unbounded (never
+    skipped), -1 empty."""
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         tt = np.log2(255.0 * opac)
-        det = a * c - b * b
-        t = np.minimum(tt, 8.0) + 1e-5
-        mid, hd = 0.5 * (a + c), np.sqrt(0.25 * (a - c) ** 2 + b * b)
-        lmax = mid + hd
-        lmin = det / lmax
-        grow = 8.0 * 2.0 ** -24 * (lmax / lmin + 1.0)
-        te = t / (1.0 - grow)
-        ex, ey = np.sqrt(te * c / det), np.sqrt(te * a / det)
-    kind = np.where(~(tt > -1e-5), -1, np.where(~(det > 0) | ~(a > 0) | ~(c > 0) | ~(grow < 0.5), 1, 0))
-    wx = ex + 0.01 + 1e-6 * (np.abs(mx) + ex)
-    wy = ey + 0.01 + 1e-6 * (np.abs(my) + ey)
+        p1, p3 = s1 * s1, s3 * s3
+        kxx, kyy, kdet = (s2 * s2 + p3) / (p1 * p3), 1.0 / p3, 1.0 / (p1 * p3)
+        kmax = np.maximum(kxx, kyy)
+        grow = 2.0 ** -24 * (8.0 + 10.0 * np.sqrt(kmax * kmax / kdet))
+        te = (np.minimum(tt, 8.0) + 1e-5) / (1.0 - grow)
+        wx, wy = np.sqrt(te * kxx) + 0.01, np.sqrt(te * kyy) + 0.01
+    kind = np.where(~(tt > -1e-5), -1, np.where(~(p1 > 0) | ~(p3 > 0) | ~(grow < 0.5), 1, 0))
     return wx, wy, kind
 
 
 @pytest.mark.parametrize("name", SMALL)
 def test_entry_boxes_conservative(name):
     """Every live record's packed entry box (two binary16 half-widths, rounded up) holds
-    the float64 box computed from the record's own float32 coefficients: the render may
-    skip an entry only where it provably cannot pass the alpha test."""
+    the float64 box computed from the record's own float32 factors: the render may skip
+    an entry only where it provably cannot pass the alpha test."""
     sc, obs, ref, gpu = _case(name)
     rec = gpu["rec"]
     live = gpu["keys"] != 0xFFFFFFFF
     r0, r1, r2 = rec[0, live].astype(np.float64), rec[1, live].astype(np.float64), rec[2, live]
-    a, b, c = -r0[:, 2], -0.5 * r0[:, 3], -r1[:, 0]
-    wx, wy, kind = _box_f64(a, b, c, r1[:, 1], r0[:, 0], r0[:, 1])
+    wx, wy, kind = _box_f64(r0[:, 2], r0[:, 3], r1[:, 0], r1[:, 1])
     bits = r2[:, 1].view(np.uint32)
     hx = (bits & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
     hy = (bits >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
@@ -194,19 +190,10 @@ def test_pixel_work_bit_exact(name):
     assert np.array_equal(gpu["work"], ref["work"])
 
 
-# The needle-like stress scene has conics with condition numbers up to ~7e4; the
-# float32 quadratic form of the exponent (like the float32 conic entries
-# themselves) then carries a relative error of order 2^-24 * cond, so its colour
-# is held to 1e-3 instead of 1e-5.  Its decisions (counts, transmittance, lists)
-# remain bit-exact.  Every workload configuration is held to 1e-5.
-# The 4200-px-wide scene evaluates Gaussians at offsets from float32 centres of
-# magnitude up to ~4200 px, rounded to half an ulp (1.2e-4 px) while the
-# oracle's values use the float64 centre; with offsets of a few px and conic
-# entries ~0.05-0.5 px^-2 that moves each alpha by up to ~1e-5 relative, summed
-# over ~16 contributions per pixel: held to 5e-5.
-COLOR_ATOL_OVERRIDE = {"elongated": 1e-3, "wide_grid": 5e-5}
-
-
+# Every scene, the needle-like footprints (conic condition numbers up to ~7e4) and the
+# 4200-px-wide image included, is held to the same colour bar: the exponent is evaluated as a
+# sum of squares from its Cholesky factor and the centre relative to the tile (see the
+# preprocess), so neither the conditioning nor the distance from the image origin costs precision.
 @pytest.mark.parametrize("name", SMALL)
 def test_render_parity(name):
     sc, obs, ref, gpu = _case(name)
@@ -214,53 +201,28 @@ def test_render_parity(name):
     assert np.array_equal(gpu["T"].view(np.uint32), ref["T"].view(np.uint32))
     err = np.abs(gpu["color"] - ref["color"]).max()
     print(name, "max colour error", err)
-    assert err <= COLOR_ATOL_OVERRIDE.get(name, COLOR_ATOL), err
+    assert err <= COLOR_ATOL, err
 
 
-def token_errors(z, zr, d):
-    """Per-Gaussian relative L2 error of the whole token and per block."""
-    blocks = {"b_mu": slice(0, 3), "s_alpha": slice(3, 4), "s_sh": slice(4, 4 + 3 * d),
-              "stats": slice(4 + 3 * d, 9 + 3 * d)}
-    denom = np.maximum(np.linalg.norm(zr, axis=1), 1e-6)
-    rel = np.linalg.norm(z - zr, axis=1) / denom
-    per_block = {}
-    for k, s in blocks.items():
-        e = np.linalg.norm(z[:, s] - zr[:, s], axis=1)
-        nrm = np.linalg.norm(zr[:, s], axis=1)
-        per_block[k] = float(np.max(e / np.maximum(nrm, 1e-3 * np.median(nrm) + 1e-30)))
-    return rel, per_block
+
 
 
 @pytest.mark.parametrize("name", SMALL)
 def test_token_parity(name):
+    """Every Gaussian's token: the whole token within 1e-3 relative L2, and each block
+    (b_mu, s_alpha, s_SH, the statistics) within 1e-3 of its own norm plus the float32
+    floor derived in oracle.token_block_errors (cancelling per-pixel terms, and what the
+    colour tolerance moves the residual and the suffix by)."""
     sc, obs, ref, gpu = _case(name)
     z = gpu["tokens"].astype(np.float64)
     zr = ref["tokens"]
-    rel, per_block = token_errors(z, zr, sc.d)
-    print(name, "max rel", rel.max(), "per block", per_block)
+    rel = np.linalg.norm(z - zr, axis=1) / np.maximum(np.linalg.norm(zr, axis=1), 1e-6)
+    blocks = oracle.token_block_errors(ref["oracle"], z, zr, catol=COLOR_ATOL)
+    print(name, "max rel", rel.max(), "per block (error / bound)", {k: round(v[0], 4) for k, v in blocks.items()})
     assert np.all(np.isfinite(gpu["tokens"]))
-    assert rel.max() <= TOKEN_RTOL, (rel.max(), int(rel.argmax()), per_block)
-    # Per block, each score is a sum of signed per-pixel terms, so the block is
-    # held to 1e-3 of its value, plus 1e-4 of the sum of the terms' magnitudes
-    # (float32 sums may cancel; the oracle accumulates both), plus what the
-    # colour tolerance (1e-5 on C_hat, hence on r) moves it: |B| <= 1 and
-    # |c - C+| <= 2 give 1e-5 W / Q for the SH block and 2e-5 (1 - o) W / Q for
-    # the opacity block.
-    acc = ref["oracle"].acc()                       # [G, V, 8 + 6d]
-    d = sc.d
-    W = acc[:, :, 0].sum(axis=1)
-    Q = 1e-6 + np.sum(1e-6 + acc[:, :, 0], axis=1)
-    o = sc.opacities.astype(np.float64)
-    abs_alpha = acc[:, :, 4].sum(axis=1) / Q
-    catol = COLOR_ATOL_OVERRIDE.get(name, COLOR_ATOL)
-    bound_a = 1e-3 * np.abs(zr[:, 3]) + 1e-4 * abs_alpha + 2 * catol * (1 - o) * W / Q + 1e-9
-    ratio_a = np.abs(z[:, 3] - zr[:, 3]) / bound_a
-    assert ratio_a.max() <= 1.0, (ratio_a.max(), int(ratio_a.argmax()))
-    abs_sh = acc[:, :, 8 + 3 * d: 8 + 6 * d].sum(axis=1) / Q[:, None]
-    bound = 1e-3 * np.abs(zr[:, 4:4 + 3 * d]) + 1e-4 * abs_sh + (catol * W / Q)[:, None] + 1e-9
-    ratio = np.abs(z[:, 4:4 + 3 * d] - zr[:, 4:4 + 3 * d]) / bound
-    g, k = np.unravel_index(np.argmax(ratio), ratio.shape)
-    assert ratio.max() <= 1.0, (ratio.max(), int(g), int(k), z[g, 4 + k], zr[g, 4 + k], abs_sh[g, k])
+    assert rel.max() <= TOKEN_RTOL, (rel.max(), int(rel.argmax()))
+    bad = {k: v for k, v in blocks.items() if not v[0] <= 1.0}
+    assert not bad, bad
 
 
 def test_exp2_bit_identical():

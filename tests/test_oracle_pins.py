@@ -99,7 +99,10 @@ def test_isotropic_on_axis_closed_form():
     assert np.allclose(r64[[0, 1]], [32.0, 32.0], rtol=0, atol=1e-12)
     r32 = o.records32()[0, 0]
     assert r32[0] == 0
-    assert np.allclose(r32[[3, 4, 5]], [1 / var, 0.0, 1 / var], rtol=2e-7, atol=1e-7)
+    # exponent factors: k Sigma2^-1 = L L^T with L = [[s1, 0], [s2, s3]], k = log2(e) / 2
+    k = math.log2(math.e) / 2
+    assert np.allclose(r32[[5, 6, 7]], [math.sqrt(k / var), 0.0, math.sqrt(k / var)], rtol=3e-7, atol=1e-7)
+    assert r32[1] == 32.0 and r32[2] == 32.0 and r32[3] == 0.0 and r32[4] == 0.0
     lam = var + math.sqrt(0.1)             # disc = 0 -> floor 0.1
     assert r32[14] == math.ceil(3 * math.sqrt(lam))
     assert r32[13] == np.float32(z)
@@ -158,6 +161,50 @@ def test_projection_jacobian_matches_finite_difference():
                 J[:, j] = (proj(mu + e) - proj(mu - e)) / 2e-6
             assert np.allclose(r64[v, g, 9:15].reshape(2, 3), J, rtol=1e-6, atol=1e-6)
             assert np.allclose(r64[v, g, 0:2], proj(mu), rtol=1e-12)
+
+
+def test_exponent_factors_and_split_centre_reproduce_the_float64_projection():
+    """The decision record keeps the exponent as -((s1 dx + s2 dy)^2 + (s3 dy)^2): the factors
+    must satisfy L L^T = k conic (k = log2(e) / 2) for the float64 conic, and the centre is
+    kept as a float32 pair whose sum is the float64 centre."""
+    sc = scenes.tiny_scene(seed=8, n=400, n_views=2, W=96, H=80, sh_degree=1, log_scale=(-3.0, 1.6), spread=0.6)
+    o = oracle.OracleScene(sc)
+    r32, r64 = o.records32(), o.records64()
+    live = r32[:, :, 0] == 0
+    s1, s2, s3 = (r32[:, :, i].astype(np.float64) for i in (5, 6, 7))
+    k = math.log2(math.e) / 2
+    ca, cb, cc = (r64[:, :, i][live] for i in (2, 3, 4))
+    cond = (ca + cc) ** 2 / (ca * cc - cb * cb)          # >= the conic's condition number
+    assert cond.max() > 1e3                             # needle-like footprints are in the sample
+    # each factor within a few float32 rounding units of the float64 conic's Cholesky factor
+    L11, L21 = np.sqrt(k * ca), k * cb / np.sqrt(k * ca)
+    L22 = np.sqrt(k * (ca * cc - cb * cb) / ca)
+    for got, want in ((s1[live], L11), (s2[live], L21), (s3[live], L22)):
+        assert np.all(np.abs(got - want) <= 1e-6 * np.abs(want)), np.max(np.abs(got - want) / np.abs(want))
+    hi = r32[:, :, 1:3].astype(np.float64)
+    lo = r32[:, :, 3:5].astype(np.float64)
+    assert np.all(np.abs(hi + lo - r64[:, :, 0:2])[live] <= 1e-12 * np.abs(r64[:, :, 0:2])[live] + 1e-12)
+    assert np.all(np.abs(lo)[live] <= np.spacing(np.abs(hi).astype(np.float32))[live])
+
+
+def test_fov_clamp_state_matches_its_definition():
+    """The clamp of the Jacobian's lateral offset is active where |t_x / t_z| > 1.3 (W/2) / f_x
+    (likewise y); Gaussians are placed on both sides of the boundary."""
+    f, W, H = 64.0, 64, 48
+    lim_x, lim_y = 1.3 * (W / 2) / f, 1.3 * (H / 2) / f
+    z = 3.0
+    xs = np.array([0.0, 0.9, 0.99, 1.01, 1.2]) * lim_x * z
+    ys = np.array([0.0, 0.95, 1.05, -1.05, -0.5]) * lim_y * z
+    means = np.stack([xs, ys, np.full(5, z)], axis=1)
+    sc = _single(means, [1, 0, 0, 0], [0.8, 0.8, 0.8], W=W, H=H, f=f)
+    o = oracle.OracleScene(sc)
+    r32 = o.records32()[0]
+    m = sc.means.astype(np.float64)
+    want = (np.abs(m[:, 0] / m[:, 2]) > 1.3 * ((0.5 * W) / f)).astype(int) | \
+           ((np.abs(m[:, 1] / m[:, 2]) > 1.3 * ((0.5 * H) / f)).astype(int) << 1)
+    live = r32[:, 0] == 0
+    assert live.sum() >= 4
+    assert np.array_equal(r32[live, 8].astype(int), want[live])
 
 
 def test_behind_camera_is_culled():
@@ -656,3 +703,112 @@ def test_occlusion_toy_mean_score_sign_accuracy():
     # Gaussians behind two saturated layers receive (almost) no support
     back = sc.means[:, 2] > 3.5
     assert np.median(logq[back]) < np.median(logq[~back])
+
+
+# --------------------------------------------------------------------------
+# degenerate inputs: non-finite parameters, nothing visible, no Gaussians
+# (boundary reading: non-finite values are not an error; the affected
+# (Gaussian, view) pairs are culled or masked -- Proposal, Stage 2: explicit
+# masks for numerically unstable contributions)
+# --------------------------------------------------------------------------
+NONFINITE_CULLED = [("means", (0, 0), np.nan), ("means", (1, 2), np.inf), ("means", (2, 0), -np.inf),
+                    ("quats", (3, 1), np.nan), ("quats", (4, 0), np.inf), ("quats", (5, slice(None)), 0.0),
+                    ("scales", (6, 0), np.nan), ("scales", (7, 1), np.inf), ("opacities", (8,), np.nan),
+                    ("opacities", (9,), 1.5)]
+NONFINITE_SH = [((10, 0, 1), np.nan), ((11, 0, 2), np.inf), ((12, 1, 0), -np.inf)]
+
+
+def nonfinite_scene(base=None):
+    """A small scene whose Gaussians 0..9 carry a non-finite (or out-of-range) mean,
+    quaternion, scale or opacity and 10..12 a non-finite SH coefficient."""
+    import dataclasses
+    sc = base if base is not None else scenes.tiny_scene(seed=21, n=30, n_views=2, W=40, H=24, sh_degree=1)
+    arrs = {k: getattr(sc, k).copy() for k in ("means", "quats", "scales", "opacities", "sh")}
+    for field, idx, val in NONFINITE_CULLED:
+        arrs[field][idx] = val
+    for idx, val in NONFINITE_SH:
+        arrs["sh"][idx] = val
+    return dataclasses.replace(sc, means_perturbed=arrs["means"], **arrs)
+
+
+def _drop(sc, keep):
+    import dataclasses
+    return dataclasses.replace(sc, means=sc.means[keep], quats=sc.quats[keep], scales=sc.scales[keep],
+                               opacities=sc.opacities[keep], sh=sc.sh[keep], means_perturbed=sc.means_perturbed[keep])
+
+
+def test_nonfinite_parameters_are_culled_like_absent_gaussians():
+    sc = nonfinite_scene()
+    obs = np.random.default_rng(1).uniform(0, 1, size=(2, 24, 40, 3)).astype(np.float32)
+    full = oracle.full_reference(sc, obs)
+    r32 = full["oracle"].records32()
+    assert np.all(r32[:, :10, 0] == 1) and np.all(r32[:, 10:, 0] == 0)
+    keep = np.arange(10, sc.n)
+    part = oracle.full_reference(_drop(sc, keep), obs)
+    assert np.array_equal(full["n"], part["n"]) and np.array_equal(full["T"], part["T"])
+    assert np.allclose(full["color"], part["color"], rtol=0, atol=1e-14)
+    assert np.allclose(full["tokens"][10:], part["tokens"], rtol=1e-12, atol=1e-14)
+    # culled in every view: the zero-support token
+    d, V, eps, lam = sc.d, sc.n_views, 1e-6, 1.0
+    want = np.zeros(9 + 3 * d)
+    want[4 + 3 * d] = math.log((V + 1) * eps)
+    want[5 + 3 * d: 8 + 3 * d] = lam / (3 * lam + eps)
+    want[8 + 3 * d] = math.log(3 * lam + eps)
+    assert np.allclose(full["tokens"][:10], want[None, :], rtol=1e-14, atol=0)
+    assert np.all(np.isfinite(full["tokens"]))
+
+
+def test_nonfinite_sh_is_clamped_and_masked_like_a_negative_colour():
+    """A non-finite SH coefficient makes its channel's pre-clamp colour non-finite: the colour
+    clamp sends it to 0 and clears the clamp bit, exactly as a large negative coefficient does."""
+    sc = nonfinite_scene()
+    neg = nonfinite_scene()
+    for idx, _ in NONFINITE_SH:
+        neg.sh[idx] = -1e3
+    obs = np.random.default_rng(2).uniform(0, 1, size=(2, 24, 40, 3)).astype(np.float32)
+    a = oracle.full_reference(sc, obs)
+    b = oracle.full_reference(neg, obs)
+    r32 = a["oracle"].records32()
+    for (g, k, ch), _ in NONFINITE_SH:
+        assert np.all((r32[:, g, 19].astype(int) >> ch) & 1 == 0)
+    assert np.array_equal(r32[:, :, 19], b["oracle"].records32()[:, :, 19])
+    assert np.array_equal(a["n"], b["n"]) and np.array_equal(a["T"], b["T"])
+    assert np.allclose(a["color"], b["color"], rtol=0, atol=1e-14)
+    assert np.allclose(a["tokens"], b["tokens"], rtol=1e-12, atol=1e-14)
+    for (g, k, ch), _ in NONFINITE_SH:
+        assert np.all(a["tokens"][g, 4 + ch: 4 + 3 * sc.d: 3] == 0.0)    # the clamped channel's SH score
+    # the renderer backward: a clamped channel passes no gradient, finite or not
+    gC = np.random.default_rng(5).uniform(-1, 1, size=obs.shape).astype(np.float32)
+    ga, gb = a["oracle"].backward(gC), b["oracle"].backward(gC)
+    assert np.all(np.isfinite(ga))
+    assert np.allclose(ga, gb, rtol=1e-12, atol=1e-14)
+
+
+def test_all_culled_scene_renders_background():
+    """Every Gaussian behind the cameras: no pair, every pixel the background with T = 1 and
+    no contributor, every token the zero-support closed form."""
+    import dataclasses
+    sc = scenes.tiny_scene(seed=21, n=30, n_views=2, W=40, H=24, sh_degree=1, background=(0.3, 0.6, 0.1))
+    m = sc.means.copy()
+    m[:, 2] = -m[:, 2]
+    sc = dataclasses.replace(sc, means=m, means_perturbed=m)
+    obs = np.random.default_rng(3).uniform(0, 1, size=(2, 24, 40, 3)).astype(np.float32)
+    ref = oracle.full_reference(sc, obs)
+    assert ref["oracle"].n_pairs == 0
+    assert np.all(ref["n"] == 0) and np.all(ref["T"] == 1.0)
+    assert np.array_equal(ref["color"], np.broadcast_to(sc.background.astype(np.float64), ref["color"].shape))
+    d, V, eps, lam = sc.d, sc.n_views, 1e-6, 1.0
+    assert np.allclose(ref["tokens"][:, 4 + 3 * d], math.log((V + 1) * eps), rtol=1e-14)
+    assert np.all(ref["tokens"][:, :4 + 3 * d] == 0.0)
+
+
+def test_no_gaussians_renders_background():
+    import dataclasses
+    sc = scenes.tiny_scene(seed=21, n=30, n_views=2, W=40, H=24, sh_degree=2, background=(0.3, 0.6, 0.1))
+    sc = _drop(sc, np.zeros(0, dtype=np.int64))
+    assert sc.n == 0
+    obs = np.random.default_rng(3).uniform(0, 1, size=(2, 24, 40, 3)).astype(np.float32)
+    ref = oracle.full_reference(sc, obs)
+    assert ref["oracle"].n_pairs == 0 and ref["tokens"].shape == (0, 9 + 3 * sc.d)
+    assert np.all(ref["n"] == 0) and np.all(ref["T"] == 1.0)
+    assert np.array_equal(ref["color"], np.broadcast_to(sc.background.astype(np.float64), ref["color"].shape))
