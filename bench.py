@@ -5,16 +5,21 @@ One step = gs_project -> gs_bin_sort -> gs_render -> gs_score_replay (tokens
 written) over one synthetic scene whose parameters and observation already sit
 in HBM.  Prints ONE JSON line with the throughput (rendered+replayed Mpix/s),
 Gaussian-pixel contributions/s, per-stage times (HIP events on the stream the
-kernels run on), the roofline of the dominant kernel and the CPU oracle timed
-on a bounded sample on the host cores.  The renderer backward (gs_backward of
-1/2 |C_hat - C_obs|^2 over the last step's render) is timed separately and
-reported under "backward", and so are a 9-channel feature composite and a
-2-channel attribution scatter ("attributes"); they are not part of the step.
+kernels run on), the roofline of the dominant kernel (the score replay: its
+fp32 VALU fraction and its HBM fraction), the score overhead (replay + finalize
+over the render path), the workspace and peak device memory, and the CPU oracle
+timed on a bounded sample on the host cores.  The other workload
+configurations are measured the same way and reported under "configs".  The
+renderer backward (gs_backward of 1/2 |C_hat - C_obs|^2 over the last step's
+render) is timed separately and reported under "backward", and so are a
+9-channel feature composite and a 2-channel attribution scatter
+("attributes"); they are not part of the step.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1..5] [--configs 1,2,4,5]
 
-The default workload is the ReSplat-like step: 8 views 256x448, 917,504
-pixel-aligned Gaussians, SH degree 3.  Only one GPU is supported.
+The default workload is the ATSplat-like compact scene: one 512x960 view of
+311,296 Gaussians (19,456 anchors x 16 offsets), SH degree 3.  Only one GPU is
+supported.
 """
 from __future__ import annotations
 
@@ -31,21 +36,30 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, 8 TB/s
 ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12     # fp32 VALU lane-ops/s (256 CU x 4 SIMD x 16 lanes x 2.4 GHz)
 
-# Algorithmic fp32 operations of the specified arithmetic (one VALU op per lane each):
-OPS_EVAL = 8        # dx, dy, the quadratic form (2 mul, 2 fma, 1 mul) and the distance cut
-OPS_NEAR = 15       # the exponential (rint, sub, 7 fma, cvt, ldexp), o*G, clamp (cmp, select), alpha cut
-OPS_CONTRIB_FWD = 20    # 1-alpha, T(1-alpha), cut, w, 3 products, 3 compensated adds (4 each), count
-OPS_CONTRIB_REPLAY = 57  # the same plus suffix, reciprocal, rho, mask, the 7 partials and their sums
-OPS_CONTRIB_BWD = 70     # forward 20, suffix 6, <g,c> and <g,S> 6, 1-alpha, reciprocal, u and its mask 4,
-                         # the 9 partials 8, their wave reduction 26 (eight-value reduce-scatter + one sum)
-
+# Algorithmic fp32 operations per unit of work (one VALU lane-op each), the method's own counts:
+OPS_EVAL = 12           # per evaluated (pixel, list entry): offsets, exponent, exponential, alpha, tests
+OPS_CONTRIB_FWD = 10    # per contribution, the forward accumulation (T (1 - alpha), w, colour sums, count)
+OPS_CONTRIB_SCORE = 40  # per contribution, the replay's suffix, rho, masks and 7 accumulators
+OPS_CONTRIB_REPLAY = OPS_CONTRIB_FWD + OPS_CONTRIB_SCORE   # the replay re-accumulates the prefix as it goes
+OPS_CONTRIB_BWD = 70    # forward 20, suffix 6, <g,c> and <g,S> 6, 1-alpha, reciprocal, u and its mask 4,
+                        # the 9 partials 8, their wave reduction 26 (eight-value reduce-scatter + one sum)
+# Algorithmic HBM bytes of the replay: per (tile, Gaussian) pair its sorted Gaussian id (4) and the 40 B of
+# the record it evaluates (centre 8, exponent factors 12, opacity 4, colour 12, slot 4); per pixel the rendered
+# colour and transmittance (16) and the observation (12); per (Gaussian, view) record its 7 accumulated
+# partial scores, written once (28)
+REPLAY_BYTES_PAIR = 44
+REPLAY_BYTES_PIXEL = 28
+REPLAY_BYTES_RECORD = 28
 
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--configs", default="1,2,4,5",
+                   help="further workload configurations measured the same way (fewer steps) and reported "
+                        "under 'configs'; empty to skip")
     p.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                    help="budget of rendering work for the CPU oracle sample (0 disables)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,8 +84,8 @@ def stage_bytes(stage, c):
     annotated line by line below)."""
     G, V, d, P, VG = c["G"], c["V"], c["d"], c["P"], c["G"] * c["V"]
     pk = 4 if c["packable"] else 0   # the rectangle packed to 32 bits by preprocess for the depth sort
-    if stage == "project":       # Gaussian parameters in; 40-byte record, rectangle, depth key, tile count out
-        return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (40 + 8 + 4 + 4 + pk)
+    if stage == "project":       # Gaussian parameters in; 48-byte record, rectangle, depth key, tile count out
+        return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (48 + 8 + 4 + 4 + pk)
     if stage == "depth_sort":    # slot scan 8, histogram 4, pass 0 (key+rect in, key+id+rect out) 24 (20 with the
         return VG * (8 + 4 + 24 - pk + 2 * 24 + 28 - 2 * pk)  # packed rect), passes 1-2 24 each, pass 3 (-> id and
                                                                # rect + count 28, or id and packed rect 20)
@@ -129,32 +143,16 @@ def measured_traffic(kernel, workload, antialiased=False):
     return int(entry["bytes_per_launch"])
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              f"(the path is not sharded across GPUs)", file=sys.stderr)
-        return 2
-
-    import numpy as np
+def measure(config, args, dev, stream, steps, warmup, extras):
+    """Time `steps` steps of workload `config` after `warmup` untimed ones; with `extras`, also
+    the renderer backward and the attribute kernels.  Returns (scene, result dict)."""
     import torch
 
     import scenes
     from gaussian_splatting_rasterizer_amd import binding
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.Stream(device=dev)
-    if args.sweep:
-        return sweep(args, dev, stream)
-
-    t_gen = time.perf_counter()
-    sc = scenes.make_scene(args.config)
-    t_gen = time.perf_counter() - t_gen
-
+    sc = scenes.make_scene(config)
+    torch.cuda.reset_peak_memory_stats(dev)
     with torch.cuda.stream(stream):
         # observation: render of the scene with perturbed means + pixel noise (setup, untimed)
         rp = binding.rasterizer_for_scene(sc.perturbed(), device=dev, antialiased=args.antialiased)
@@ -164,7 +162,7 @@ def main():
         rp.close()
         del rp, obs_col
 
-        if args.copy_calibration_mib > 0:
+        if extras and args.copy_calibration_mib > 0:
             n = args.copy_calibration_mib * (1 << 20) // 4
             src_buf = torch.ones(n, dtype=torch.float32, device=dev)
             dst_buf = torch.empty_like(src_buf)
@@ -175,9 +173,10 @@ def main():
         r = binding.rasterizer_for_scene(sc, device=dev, antialiased=args.antialiased)
         r.project_and_bin()
         r._alloc(int(r.n_pairs * 1.1) + 4096)      # right-size the workspace once
+        workspace_bytes = int(r.workspace.numel())
         outputs = r.new_outputs()
         tokens = torch.empty((sc.n, 9 + 3 * sc.d), dtype=torch.float32, device=dev)
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             r.step(obs, outputs, tokens)
         stream.synchronize()
 
@@ -187,14 +186,14 @@ def main():
         binding.gs_profile_read(r.ctx)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             r.step(obs, outputs, tokens)
         stream.synchronize()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         prof_timed = binding.gs_profile_read(r.ctx)
         # per-stage breakdown from separate steps with every stage timed
-        n_prof = min(args.steps, 10)
+        n_prof = min(steps, 10)
         binding.gs_profile_enable(r.ctx, True)
         for _ in range(n_prof):
             r.step(obs, outputs, tokens)
@@ -204,16 +203,16 @@ def main():
 
         # renderer backward of 1/2 |C_hat - C_obs|^2 on the same render, timed on its own
         bwd = None
-        if not args.no_backward:
+        if extras and not args.no_backward:
             grad_color = (outputs[0] - obs).contiguous()
             grads = r.new_grads()
-            for _ in range(args.warmup):
+            for _ in range(warmup):
                 r.backward(grad_color, grads)
             stream.synchronize()
             binding.gs_profile_stages(r.ctx, ["backward"])
             binding.gs_profile_read(r.ctx)
             tb = time.perf_counter()
-            for _ in range(args.steps):
+            for _ in range(steps):
                 r.backward(grad_color, grads)
             stream.synchronize()
             tb = time.perf_counter() - tb
@@ -224,29 +223,29 @@ def main():
             stream.synchronize()
             bprof["backward_finalize"] = binding.gs_profile_read(r.ctx)["backward_finalize"]
             binding.gs_profile_enable(r.ctx, False)
-            bwd = dict(ms=1e3 * tb / args.steps,
+            bwd = dict(ms=1e3 * tb / steps,
                        stages={k: bprof[k][0] / max(bprof[k][1], 1) for k in ("backward", "backward_finalize")},
                        finite=bool(all(torch.isfinite(t).all().item() for t in grads.values())))
 
         # feature composite of 9 channels (ReCoSplat-style conditioning features) and attribution scatter of a
         # 2-channel map (squared residual, coverage: the error + coverage token), each timed on its own
         attrs = None
-        if not args.no_attributes:
+        if extras and not args.no_attributes:
             gen = torch.Generator(device=dev).manual_seed(5)
             feats = torch.randn((sc.n, 9), generator=gen, device=dev, dtype=torch.float32)
             feat_out = torch.empty((sc.n_views, sc.height, sc.width, 9), dtype=torch.float32, device=dev)
             resid2 = ((outputs[0] - obs) ** 2).sum(-1)
             amap = torch.stack([resid2, torch.ones_like(resid2)], dim=-1).contiguous()
             aout = torch.empty((sc.n, 2), dtype=torch.float32, device=dev)
-            for _ in range(args.warmup):
+            for _ in range(warmup):
                 r.render_features(feats, out=feat_out)
                 r.attribute(amap, out=aout)
             stream.synchronize()
             binding.gs_profile_enable(r.ctx, True)
             binding.gs_profile_read(r.ctx)
-            for _ in range(args.steps):
+            for _ in range(steps):
                 r.render_features(feats, out=feat_out)
-            for _ in range(args.steps):
+            for _ in range(steps):
                 r.attribute(amap, out=aout)
             stream.synchronize()
             aprof = binding.gs_profile_read(r.ctx)
@@ -258,37 +257,47 @@ def main():
         stats = r.export(binding.GS_EXPORT_PIXEL_STATS).view(-1, 2).to(torch.int64)
         K = int(n.to(torch.int64).sum().item())
         E = int(stats[:, 0].sum().item())
-        E_near = int(stats[:, 1].sum().item())
         P = int(r.n_pairs)
         finite = bool(torch.isfinite(tokens).all().item())
         rec = r.export(binding.GS_EXPORT_RECORDS)
         n_live = int((rec[3, :, 1] != 0).sum().item())
+        stream.synchronize()
+        peak_bytes = int(torch.cuda.max_memory_allocated(dev))
+        r.close()
+        del r, rec, stats, outputs, tokens, obs
+    torch.cuda.empty_cache()
 
     V, H, W = sc.n_views, sc.height, sc.width
     T_tiles = ((W + 15) // 16) * ((H + 15) // 16)
-    ms_step = 1e3 * elapsed / args.steps
-    mpix = V * H * W / (elapsed / args.steps) / 1e6
-    contribs = K / (elapsed / args.steps)
-
-    bits_for = lambda n: max(int(n - 1).bit_length(), 1)
+    N_px = V * H * W
+    ms_step = 1e3 * elapsed / steps
+    workload = scenes.CONFIG_NAMES[config]
+    bits_for = lambda x: max(int(x - 1).bit_length(), 1)
     c = dict(G=sc.n, V=V, d=sc.d, P=P, T=T_tiles, n_live=n_live,
-             packed=bits_for(V * T_tiles) + bits_for(sc.n) <= 32, packable=(W + 15) // 16 <= 256 and (H + 15) // 16 <= 256)
+             packed=bits_for(V * T_tiles) + bits_for(sc.n) <= 32,
+             packable=(W + 15) // 16 <= 256 and (H + 15) // 16 <= 256)
     stages = {k: (ms / max(cnt, 1), cnt) for k, (ms, cnt) in prof.items() if cnt > 0}
-    # The dominant single kernel is the score replay (one launch per step, the
-    # "replay" stage): bound by fp32 VALU work, counted algorithmically; its
-    # duration is the one measured live over the timed steps.
+    # The dominant single kernel is the score replay (one launch per step, the "replay" stage); its duration
+    # is the one measured live over the timed steps.  Bound: fp32 VALU (each gathered record is evaluated by up
+    # to 256 pixels), counted with the method's per-unit operations; its HBM fraction is reported beside it.
     rep_ms = prof_timed["replay"][0] / max(prof_timed["replay"][1], 1)
     t_rep = rep_ms * 1e-3
-    ops = OPS_EVAL * E + OPS_NEAR * E_near + OPS_CONTRIB_REPLAY * K
+    ops = OPS_EVAL * E + OPS_CONTRIB_REPLAY * K
     achieved = ops / t_rep / 1e12
-    workload = scenes.CONFIG_NAMES[args.config]
-    roofline = {"kernel": "k_replay", "bound": "alu", "achieved": round(achieved, 3), "peak": round(ALU_PEAK_TOPS, 2),
-                "unit": "T lane-ops/s (fp32 VALU)", "frac": round(achieved / ALU_PEAK_TOPS, 4),
-                "traffic": measured_traffic("k_replay", workload, args.antialiased), "avg_launch_ms": round(rep_ms, 4),
-                "ops_per_launch": ops,
-                "units": {"evaluations": E, "near_evaluations": E_near, "contributions": K}}
+    rep_bytes = REPLAY_BYTES_PAIR * P + REPLAY_BYTES_PIXEL * N_px + REPLAY_BYTES_RECORD * V * sc.n
+    traffic = measured_traffic("k_replay", workload, args.antialiased)
+    roofline = {"kernel": "k_replay", "bound": "alu", "achieved": round(achieved, 3),
+                "peak": round(ALU_PEAK_TOPS, 2), "unit": "T lane-ops/s (fp32 VALU)",
+                "frac": round(achieved / ALU_PEAK_TOPS, 4), "traffic": traffic,
+                "avg_launch_ms": round(rep_ms, 4), "ops_per_launch": ops,
+                "ops_per_unit": {"evaluation": OPS_EVAL, "contribution": OPS_CONTRIB_REPLAY},
+                "units": {"evaluations": E, "contributions": K},
+                "hbm": {"algorithmic_bytes": rep_bytes, "achieved_gbs": round(rep_bytes / t_rep / 1e9, 1),
+                        "peak_gbs": HBM_PEAK_GBS, "frac": round(rep_bytes / t_rep / 1e9 / HBM_PEAK_GBS, 4),
+                        "measured_gbs": None if traffic is None else round(traffic / t_rep / 1e9, 1),
+                        "measured_frac": None if traffic is None else round(traffic / t_rep / 1e9 / HBM_PEAK_GBS, 4)}}
     t_ren = stages["render"][0] * 1e-3
-    ops_r = OPS_EVAL * E + OPS_NEAR * E_near + OPS_CONTRIB_FWD * K
+    ops_r = OPS_EVAL * E + OPS_CONTRIB_FWD * K
     secondary = {"k_render": {"bound": "alu", "achieved": round(ops_r / t_ren / 1e12, 3),
                               "frac": round(ops_r / t_ren / 1e12 / ALU_PEAK_TOPS, 4),
                               "traffic": measured_traffic("k_render<false>", workload, args.antialiased),
@@ -301,48 +310,91 @@ def main():
         secondary[st] = {"bound": "hbm", "achieved_gbs": round(by / t / 1e9, 1),
                          "frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4), "bytes_per_launch": by,
                          "avg_launch_ms": round(stages[st][0], 4)}
+    render_ms = sum(stages[k][0] for k in RENDER_STAGES if k in stages)
+    score_ms = sum(stages[k][0] for k in SCORE_STAGES if k in stages)
 
-    backward = None
+    out = {
+        "value": round(N_px / (elapsed / steps) / 1e6, 2),
+        "ms_per_step": round(ms_step, 4),
+        "steps": steps,
+        "config": {"workload": workload, "views": V, "height": H, "width": W, "gaussians": sc.n,
+                   "sh_degree": sc.sh_degree, "pairs": P, "parallelism": "none",
+                   "mode": "antialiased" if args.antialiased else "plain"},
+        "contribs_per_s": round(K / (elapsed / steps), 1),
+        "work_per_step": {"contributions": K, "evaluations": E, "pairs": P},
+        "stages_ms": {k: round(v[0], 4) for k, v in stages.items()},
+        "score_overhead": round(score_ms / render_ms, 4),
+        "roofline": roofline,
+        "stage_rooflines": secondary,
+        "memory": {"workspace_bytes": workspace_bytes, "peak_device_bytes": peak_bytes},
+        "tokens_finite": finite,
+    }
     if bwd is not None:
         t_b = bwd["stages"]["backward"] * 1e-3
-        ops_b = OPS_EVAL * E + OPS_NEAR * E_near + OPS_CONTRIB_BWD * K
-        backward = {"ms": round(bwd["ms"], 4), "mpix_per_s": round(V * H * W / (bwd["ms"] * 1e-3) / 1e6, 2),
-                    "stages_ms": {k: round(v, 4) for k, v in bwd["stages"].items()},
-                    "k_backward": {"bound": "alu", "achieved": round(ops_b / t_b / 1e12, 3),
-                                   "frac": round(ops_b / t_b / 1e12 / ALU_PEAK_TOPS, 4),
-                                   "traffic": measured_traffic("k_backward", workload, args.antialiased),
-                                   "avg_launch_ms": round(bwd["stages"]["backward"], 4), "ops_per_launch": ops_b},
-                    "grads_finite": bwd["finite"], "loss": "1/2 |C_hat - C_obs|^2"}
+        ops_b = OPS_EVAL * E + OPS_CONTRIB_BWD * K
+        out["backward"] = {"ms": round(bwd["ms"], 4), "mpix_per_s": round(N_px / (bwd["ms"] * 1e-3) / 1e6, 2),
+                           "stages_ms": {k: round(v, 4) for k, v in bwd["stages"].items()},
+                           "k_backward": {"bound": "alu", "achieved": round(ops_b / t_b / 1e12, 3),
+                                          "frac": round(ops_b / t_b / 1e12 / ALU_PEAK_TOPS, 4),
+                                          "traffic": measured_traffic("k_backward", workload, args.antialiased),
+                                          "avg_launch_ms": round(bwd["stages"]["backward"], 4),
+                                          "ops_per_launch": ops_b},
+                           "grads_finite": bwd["finite"], "loss": "1/2 |C_hat - C_obs|^2"}
+    if attrs is not None:
+        out["attributes"] = {"feature_composite_9ch_ms": round(attrs["features"], 4),
+                             "attribution_2ch_ms": round(attrs["attribute"], 4), "finite": attrs["finite"]}
+    return sc, out
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(the path is not sharded across GPUs)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(device=dev)
+    if args.sweep:
+        return sweep(args, dev, stream)
+
+    sc, main_res = measure(args.config, args, dev, stream, args.steps, args.warmup, extras=True)
+    others = {}
+    for cfg in [int(x) for x in args.configs.split(",") if x.strip()]:
+        if cfg == args.config:
+            continue
+        _, res = measure(cfg, args, dev, stream, max(1, min(args.steps, 10)), max(1, min(args.warmup, 2)),
+                         extras=False)
+        others[res["config"]["workload"]] = {k: res[k] for k in (
+            "value", "ms_per_step", "steps", "config", "contribs_per_s", "work_per_step", "stages_ms",
+            "score_overhead", "roofline", "stage_rooflines", "memory", "tokens_finite")}
 
     out = {
         "metric": "render+score-replay Mpix/s",
-        "value": round(mpix, 2),
+        "value": main_res["value"],
         "unit": "Mpix/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": scenes.CONFIG_NAMES[args.config], "views": V, "height": H, "width": W,
-                   "gaussians": sc.n, "sh_degree": sc.sh_degree, "pairs": P, "parallelism": "none",
-                   "mode": "antialiased" if args.antialiased else "plain"},
-        "contribs_per_s": round(contribs, 1),
-        "work_per_step": {"contributions": K, "evaluations": E, "near_evaluations": E_near, "pairs": P},
-        "stages_ms": {k: round(v[0], 4) for k, v in stages.items()},
-        "roofline": roofline,
-        "stage_rooflines": secondary,
-        "tokens_finite": finite,
     }
-    if backward is not None:
-        out["backward"] = backward
-    if attrs is not None:
-        out["attributes"] = {"feature_composite_9ch_ms": round(attrs["features"], 4),
-                             "attribution_2ch_ms": round(attrs["attribute"], 4), "finite": attrs["finite"]}
-
+    for k in ("config", "contribs_per_s", "work_per_step", "stages_ms", "score_overhead", "roofline",
+              "stage_rooflines", "memory", "tokens_finite", "backward", "attributes"):
+        if k in main_res:
+            out[k] = main_res[k]
+    if others:
+        out["configs"] = others
     if not args.no_cpu_baseline and args.cpu_baseline_seconds > 0:
         out["cpu_baseline"] = cpu_baseline(sc, args.cpu_baseline_seconds, antialiased=args.antialiased)
     print(json.dumps(out), flush=True)
@@ -411,11 +463,20 @@ def sweep(args, dev, stream):
     return 0
 
 
-def cpu_baseline(sc, budget_s, antialiased=False):
-    """The oracle as it stands, timed on the host cores on a bounded sample of the
-    same workload: full preprocess + tile lists, then render + replay of an
-    evenly spaced subset of tiles (with score sums for every Gaussian), then
-    tokens; the per-tile part is scaled to the whole frame."""
+def _host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_rate(sc, budget_s, antialiased=False):
+    """Oracle time of one frame of `sc`: full preprocess + tile lists, render + replay of an evenly
+    spaced subset of tiles (score sums for every Gaussian) scaled to the frame, then tokens."""
     import numpy as np
 
     import oracle
@@ -444,13 +505,35 @@ def cpu_baseline(sc, budget_s, antialiased=False):
     t_tok = time.perf_counter() - t3
     full = t_fixed + t_tiles * (n_tiles / len(sample)) + t_tok
     pixels = o.V * o.H * o.W
-    threads = oracle.num_threads()
     o.close()
-    return {"value": round(pixels / full / 1e6, 4), "unit": "Mpix/s", "cores": threads, "kind": "oracle",
+    return {"value": round(pixels / full / 1e6, 4), "unit": "Mpix/s",
             "sample": f"preprocess + lists of all {sc.n} Gaussians x {sc.n_views} views, render+replay of "
                       f"{len(sample)}/{n_tiles} tiles (every {stride}th) scaled to the frame, tokens of all",
             "seconds": {"preprocess_lists": round(t_fixed, 3), "tiles": round(t_tiles, 3),
                         "tokens": round(t_tok, 3), "extrapolated_frame": round(full, 3)}}
+
+
+def cpu_baseline(sc, budget_s, antialiased=False):
+    """The oracle as it stands, timed on the host cores on a bounded sample of the same
+    workload (all threads), plus single-thread rates of the same workload and of the
+    occlusion toy on smaller samples."""
+    import oracle
+    import scenes
+
+    threads = oracle.num_threads()
+    res = _oracle_rate(sc, budget_s, antialiased)
+    res.update({"cores": threads, "kind": "oracle", "host_cpu": _host_cpu_model()})
+    one = {}
+    oracle.set_num_threads(1)
+    try:
+        for name, s1 in ((scenes.CONFIG_NAMES[1], scenes.make_scene(1)), (sc.name, sc)):
+            r1 = _oracle_rate(s1, budget_s / 5, antialiased)
+            one[name] = {"value": r1["value"], "unit": "Mpix/s", "sample": r1["sample"],
+                         "extrapolated_frame_s": r1["seconds"]["extrapolated_frame"]}
+    finally:
+        oracle.set_num_threads(threads)
+    res["one_thread"] = one
+    return res
 
 
 if __name__ == "__main__":

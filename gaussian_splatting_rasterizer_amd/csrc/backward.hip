@@ -10,8 +10,8 @@
 // colour clamp, field-of-view clamp).
 //
 // k_backward: the same tiles, lists, order and decisions as the render, and
-// the same traversal as the score replay (event entries only, compensated
-// prefix, suffix from the rendered colour).  With g = dL/dC_hat and, for each
+// the same traversal as the score replay (event entries only, the suffix
+// tracked as the rendered colour minus the prefix).  With g = dL/dC_hat and, for each
 // contribution,
 //     S = C_hat - P - T alpha c          (everything composited behind it, background included)
 //     dL/dalpha = T <g, c> - <g, S> / (1 - alpha)
@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
         g2 = grad_color[3 * pix + 2];
     }
     float Tr = 1.0f;
-    float h0 = 0.f, h1 = 0.f, h2 = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
+    // the suffix composite times the transmittance in front of it: C_hat minus the prefix colour
+    float S0 = Ch0, S1 = Ch1, S2 = Ch2;
     bool done = !inside;
 
     for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
@@ -151,13 +152,10 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                 {  // every listed entry has a contribution or saturation in some lane of the wave
                     const float cr = b.z, cg = b.w, cbl = s2[j];
                     const float w = contrib ? alpha * Tr : 0.0f;
-                    float n0 = h0, n1 = h1, n2 = h2, k0 = c0, k1 = c1, k2 = c2;
-                    kahan_add(n0, k0, cr * w);
-                    kahan_add(n1, k1, cg * w);
-                    kahan_add(n2, k2, cbl * w);
-                    const float S0 = (Ch0 - n0) + k0;
-                    const float S1 = (Ch1 - n1) + k1;
-                    const float S2 = (Ch2 - n2) + k2;
+                    // the suffix behind this entry: C_hat minus the prefix including it
+                    S0 = __builtin_fmaf(-cr, w, S0);
+                    S1 = __builtin_fmaf(-cg, w, S1);
+                    S2 = __builtin_fmaf(-cbl, w, S2);
                     const float gc = __builtin_fmaf(g2, cbl, __builtin_fmaf(g1, cg, g0 * cr));
                     const float gS = __builtin_fmaf(g2, S2, __builtin_fmaf(g1, S1, g0 * S0));
                     // u = alpha (T <g, c> - <g, S> / (1 - alpha)) = w <g, c> - alpha <g, S> / (1 - alpha)
@@ -170,15 +168,7 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                     const float red8 = wave_sum1(w * g2);
                     if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
                     if (lane == 0) sp[wave][j][8] = red8;
-                    if (contrib) {
-                        h0 = n0;
-                        h1 = n1;
-                        h2 = n2;
-                        c0 = k0;
-                        c1 = k1;
-                        c2 = k2;
-                        Tr = tT;
-                    }
+                    Tr = contrib ? tT : Tr;
                 }
             }
         }

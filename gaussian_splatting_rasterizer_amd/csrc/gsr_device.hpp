@@ -228,14 +228,6 @@ __device__ __forceinline__ float4 entry_box_unpack(float mx, float my, uint32_t 
     return make_float4(mx - ex, mx + ex, my - ey, my + ey);
 }
 
-// Compensated (Kahan) accumulation of the prefix colour; the true sum is hi - comp.
-__device__ __forceinline__ void kahan_add(float& hi, float& comp, float x) {
-    const float y = x - comp;
-    const float t = hi + y;
-    comp = (t - hi) - y;
-    hi = t;
-}
-
 // Reduce eight values over the 64 lanes; returns in every lane the total of
 // component (lane >> 3) & 7.  Reduce-scatter with gfx950 lane permutations:
 //   permlane32_swap pairs component i (kept in lanes 0-31) with i + 4 (lanes 32-63),

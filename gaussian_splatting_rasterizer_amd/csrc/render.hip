@@ -14,8 +14,7 @@
 // walks only those with broadcast LDS reads.  The box is conservative for the
 // float32 evaluation, so the skipped entries are exactly ones every pixel of
 // the quadrant would have skipped.  Alpha decisions use the float32 canonical order and the
-// specified exponential; the prefix colour is accumulated with compensated
-// (Kahan) summation so that the replay can recover the suffix accurately.
+// specified exponential; the colour is accumulated with fused multiply-adds.
 // For every entry it processes, the render also leaves one byte whose bit w
 // says whether any pixel of wave w contributed or saturated there: the replay
 // walks only those entries, since at every other one no pixel's state changes.
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     float Tr = 1.0f;
-    float h0 = 0.f, h1 = 0.f, h2 = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
+    float h0 = 0.f, h1 = 0.f, h2 = 0.f;
     int n = 0;
     uint32_t n_near = 0;          // entries past the distance cut
     uint32_t stop = 0xffffffffu;  // list index at which the pixel saturated
@@ -146,16 +145,15 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                     if (sat) stop = base + (uint32_t)j;
                 }
                 done = done || sat;
-                if (contrib) {
-                    if constexpr (!STATS) {
-                        const float w = alpha * Tr;
-                        kahan_add(h0, c0, b.z * w);
-                        kahan_add(h1, c1, b.w * w);
-                        kahan_add(h2, c2, s2[j] * w);
-                        ++n;
-                    }
-                    Tr = tT;
+                if constexpr (!STATS) {
+                    // branch-free: lanes without a contribution add zero
+                    const float w = contrib ? alpha * Tr : 0.0f;
+                    h0 = __builtin_fmaf(b.z, w, h0);
+                    h1 = __builtin_fmaf(b.w, w, h1);
+                    h2 = __builtin_fmaf(s2[j], w, h2);
+                    n += contrib ? 1 : 0;
                 }
+                Tr = contrib ? tT : Tr;
                 if (!STATS && pass) s_ev[wave][j] = 1;  // contributed or saturated (every such lane writes the same byte)
                 if (__ballot(!done) == 0ull) break;
             }
@@ -174,10 +172,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     // the work of this tile, for the order of the traversals that follow: entries processed until done
     if (threadIdx.x == 0) tile_work[tile] = rg.y > rg.x ? (base < rg.y ? base : rg.y) - rg.x : 0u;
     if (!inside) return;
-    kahan_add(h0, c0, Tr * bg0);
-    kahan_add(h1, c1, Tr * bg1);
-    kahan_add(h2, c2, Tr * bg2);
-    const float o0 = h0 - c0, o1 = h1 - c1, o2 = h2 - c2;
+    const float o0 = __builtin_fmaf(Tr, bg0, h0), o1 = __builtin_fmaf(Tr, bg1, h1), o2 = __builtin_fmaf(Tr, bg2, h2);
     const int64_t pix = ((int64_t)v * H + pyi) * W + pxi;
     if (color) {
         color[3 * pix] = o0;

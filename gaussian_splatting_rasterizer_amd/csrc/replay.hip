@@ -4,9 +4,9 @@
 // Analytic Score Replay) and the "Exact Score Operators" / "Final Token".
 //
 // k_replay: the same tiles, lists, order and float32 decisions as the render.
-// Each pixel re-walks its list keeping the prefix colour P (compensated, so it
-// is bit-identical to the render's) and the transmittance T, and for every
-// contribution forms
+// Each pixel re-walks its list keeping the transmittance T and S = C_hat - P,
+// the rendered colour minus the prefix colour (one fused multiply-add per
+// channel and entry), and for every contribution forms
 //     S   = C_hat - P - T alpha c                     (suffix times T(1-alpha))
 //     C+  = S / (T (1 - alpha) + eps)                 (suffix equation)
 //     rho = <r, c - C+>,  r = C_hat - C_obs            (residual-suffix contrast)
@@ -93,7 +93,8 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
         r2 = Ch2 - observed[3 * pix + 2];
     }
     float Tr = 1.0f;
-    float h0 = 0.f, h1 = 0.f, h2 = 0.f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
+    // the suffix composite times the transmittance in front of it: C_hat minus the prefix colour
+    float S0 = Ch0, S1 = Ch1, S2 = Ch2;
     bool done = !inside;
 
     uint32_t base = rg.x;
@@ -152,16 +153,11 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 {
                     const float cr = b.z, cg = b.w, cbl = s2[j];
                     const float w = contrib ? alpha * Tr : 0.0f;
-                    const float x0 = cr * w, x1 = cg * w, x2 = cbl * w;
-                    // prefix including this entry (compensated: true value hi - comp); the suffix
-                    // times T (1 - alpha) is then C_hat minus that prefix
-                    float n0 = h0, n1 = h1, n2 = h2, k0 = c0, k1 = c1, k2 = c2;
-                    kahan_add(n0, k0, x0);
-                    kahan_add(n1, k1, x1);
-                    kahan_add(n2, k2, x2);
-                    const float S0 = (Ch0 - n0) + k0;
-                    const float S1 = (Ch1 - n1) + k1;
-                    const float S2 = (Ch2 - n2) + k2;
+                    // the suffix behind this entry, times T (1 - alpha): C_hat minus the prefix including it
+                    // (lanes without a contribution subtract zero)
+                    S0 = __builtin_fmaf(-cr, w, S0);
+                    S1 = __builtin_fmaf(-cg, w, S1);
+                    S2 = __builtin_fmaf(-cbl, w, S2);
                     const float inv_den = __builtin_amdgcn_rcpf(tT + eps);
                     // rho = <r, c - S / den> = <r, c> - <r, S> / den
                     const float rc = __builtin_fmaf(r2, cbl, __builtin_fmaf(r1, cg, r0 * cr));
@@ -171,15 +167,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                     const float x[8] = {w, mw, mw * dx, mw * dy, w * r0, w * r1, w * r2, 0.0f};
                     const float red = wave_reduce8(x, lane);
                     if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
-                    if (contrib) {
-                        h0 = n0;
-                        h1 = n1;
-                        h2 = n2;
-                        c0 = k0;
-                        c1 = k1;
-                        c2 = k2;
-                        Tr = tT;
-                    }
+                    Tr = contrib ? tT : Tr;
                 }
             }
         }
@@ -285,7 +273,12 @@ constexpr int kGatherThreads = 256;
 // record, loads the partials of the set bits, and a fixed-order wave reduction
 // leaves the sums in eight lanes, which store them together.  A record's loads
 // are thus one round of independent loads instead of a chain of one per slot.
+// Where most records are reached (single views with every Gaussian visible) a
+// run with more than kGatherDenseRun reached records is summed lane per
+// record instead, each lane keeping four slots' loads in flight.
 constexpr int kGatherRecs = 4;
+// A run with more reached records than this is summed lane per record instead.
+constexpr int kGatherDenseRun = 8;
 
 __device__ __forceinline__ uint32_t bit_range_mask(int32_t lo, int32_t hi) {  // bits [lo, hi) of a word, clipped
     lo = lo < 0 ? 0 : lo;
@@ -344,7 +337,56 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
             rec_masks[2 * (run >> 6)] = live_mask;
             rec_masks[2 * (run >> 6) + 1] = reached_mask;
         }
-        // the wave sums each reached record of this run
+        if (__popcll(reached_mask) > kGatherDenseRun) {
+            // many reached records in this run: each lane sums its own record's flagged slots, four
+            // slots' loads in flight at a time
+            if (reached) {
+                float4 acc[NQ];
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+                const uint32_t w0 = sa[j] >> 5, wlast = (sa[j] + tt[j] - 1u) >> 5;
+                const int32_t lo = (int32_t)(sa[j] & 31u), hi = lo + (int32_t)tt[j];
+                uint32_t bits = b0[j];
+                uint32_t w = w0;
+                for (;;) {
+                    int64_t sl[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        while (bits == 0u && w < wlast) {
+                            ++w;
+                            const int32_t k = (int32_t)(w - w0);
+                            bits = k == 1 ? b1[j] : k == 2 ? b2[j]
+                                                           : slot_bits[w] & bit_range_mask(lo - 32 * k, hi - 32 * k);
+                        }
+                        sl[u] = -1;
+                        if (bits) {
+                            sl[u] = (int64_t)w * 32 + __builtin_ctz(bits);
+                            bits &= bits - 1u;
+                        }
+                    }
+                    float4 p[4][NQ];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int q = 0; q < NQ; ++q)
+                            p[u][q] = sl[u] >= 0 ? partials[NQ * sl[u] + q] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int q = 0; q < NQ; ++q) {
+                            acc[q].x += p[u][q].x;
+                            acc[q].y += p[u][q].y;
+                            acc[q].z += p[u][q].z;
+                            acc[q].w += p[u][q].w;
+                        }
+                    if (sl[3] < 0) break;
+                }
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) gv_sums[NQ * (run + lane) + q] = acc[q];
+            }
+            continue;
+        }
+        // few reached records: the wave sums each reached record of this run
         while (reached_mask) {
             const int src = __builtin_ctzll(reached_mask);
             reached_mask &= reached_mask - 1ull;

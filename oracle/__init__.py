@@ -102,6 +102,7 @@ def _load():
         lib.orc_backward.argtypes = [P, P, P, I64, P, P]
         lib.orc_sh_basis_grad64.argtypes = [P, I64, I32, P]
         lib.orc_num_threads.restype = I32
+        lib.orc_set_num_threads.argtypes = [I32]
         _lib = lib
         return lib
 
@@ -153,6 +154,11 @@ def eig3(A: np.ndarray) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (used only to time it)."""
+    _load().orc_set_num_threads(int(n))
 
 
 class OracleScene:

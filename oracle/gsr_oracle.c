@@ -1644,3 +1644,13 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads used by the oracle's parallel loops from now on (timing only). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
