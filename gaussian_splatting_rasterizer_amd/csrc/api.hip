@@ -4,6 +4,7 @@
 // kernel launches on the caller's stream.  No device memory is allocated or
 // freed here (a context holds one pinned host word for the pair count); the
 // only host/device synchronisation is the read of that count in gs_bin_sort.
+#include <sched.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -292,19 +293,22 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
         !(params->near_plane > 0.0f) || !(params->far_plane > params->near_plane) ||
         (params->antialiased != 0 && params->antialiased != 1))
         return fail(GS_ERR_INVALID_ARGUMENT, "invalid params");
+    // every camera is validated before the context changes, so a rejected call leaves it as it was
+    CamPack cp;
     for (int v = 0; v < s.V; ++v) {
         const gs_camera& c = cams[v];
-        for (int k = 0; k < 9; ++k) ctx->cams.c[v][k] = c.R[k];
-        for (int k = 0; k < 3; ++k) ctx->cams.c[v][9 + k] = c.t[k];
-        ctx->cams.c[v][12] = c.fx;
-        ctx->cams.c[v][13] = c.fy;
-        ctx->cams.c[v][14] = c.cx;
-        ctx->cams.c[v][15] = c.cy;
         if (!(c.fx > 0.0f) || !(c.fy > 0.0f)) return fail(GS_ERR_INVALID_ARGUMENT, "focal lengths must be > 0");
-        // the same float32 operations preprocess would otherwise repeat for every Gaussian (IEEE division)
-        ctx->cams.lim[v][0] = kFovClamp * ((0.5 * (double)s.W) / (double)c.fx);
-        ctx->cams.lim[v][1] = kFovClamp * ((0.5 * (double)s.H) / (double)c.fy);
+        for (int k = 0; k < 9; ++k) cp.c[v][k] = c.R[k];
+        for (int k = 0; k < 3; ++k) cp.c[v][9 + k] = c.t[k];
+        cp.c[v][12] = c.fx;
+        cp.c[v][13] = c.fy;
+        cp.c[v][14] = c.cx;
+        cp.c[v][15] = c.cy;
+        // the same float64 operations preprocess would otherwise repeat for every Gaussian (IEEE division)
+        cp.lim[v][0] = kFovClamp * ((0.5 * (double)s.W) / (double)c.fx);
+        cp.lim[v][1] = kFovClamp * ((0.5 * (double)s.H) / (double)c.fy);
     }
+    ctx->cams = cp;
     ctx->scene = *sc;
     ctx->params = *params;
     ctx->state = kCreated;
@@ -321,7 +325,14 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
     return GS_OK;
 }
 
-gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out) {
+}  // extern "C"
+
+namespace {
+
+// Binning and sorting.  With `count_by_copy` the pair count is read back with a copy into host
+// stack memory after the depth sort is queued (nothing allocated: the no-allocation path); otherwise
+// the slot scan writes it into the context's mapped pinned word and the host polls an event.
+gs_status bin_sort_impl(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out, bool count_by_copy) {
     if (!ctx) return fail(GS_ERR_INVALID_ARGUMENT, "context is null");
     if (ctx->state < kProjected) return fail(GS_ERR_STATE, "gs_bin_sort before gs_project");
     const Sizes& s = ctx->s;
@@ -334,7 +345,7 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
         if (e != hipSuccess) return hip_fail(e, "look-back clear");
         ctx->epoch = 0;
     }
-    if (!ctx->host_count) {
+    if (!count_by_copy && !ctx->host_count) {
         e = hipHostMalloc((void**)&ctx->host_count, 64, hipHostMallocMapped | hipHostMallocCoherent);
         if (e != hipSuccess) {
             ctx->host_count = nullptr;
@@ -355,10 +366,12 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     // writes it into pinned host memory too, and the host waits for it only after the sort and the second scan
     // are queued, so that the GPU has work while the host waits
     e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream, false,
-                        ctx->host_count_dev);
+                        count_by_copy ? nullptr : ctx->host_count_dev);
     if (e != hipSuccess) return hip_fail(e, "slot scan");
-    e = hipEventRecord(ctx->count_ev, stream);
-    if (e != hipSuccess) return hip_fail(e, "pair count event");
+    if (!count_by_copy) {
+        e = hipEventRecord(ctx->count_ev, stream);
+        if (e != hipSuccess) return hip_fail(e, "pair count event");
+    }
     // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
     //    scan rewrites next); the tile rectangles ride along (packed, or gathered by the last pass), and
     //    the last pass writes rectangles and tile counts in depth order but no keys
@@ -379,13 +392,21 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream, packable);
     if (e != hipSuccess) return hip_fail(e, "scan");
     tm.end(GS_STAGE_SCAN, stream);
-    // wait for the pair count by polling its event
-    for (;;) {
-        e = hipEventQuery(ctx->count_ev);
-        if (e == hipSuccess) break;
-        if (e != hipErrorNotReady) return hip_fail(e, "pair count wait");
+    uint64_t total = 0;
+    if (count_by_copy) {
+        e = hipMemcpyAsync(&total, ws.scan_total + 1, sizeof total, hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "pair count copy");
+    } else {
+        // wait for the pair count by polling its event, yielding the core between polls
+        for (;;) {
+            e = hipEventQuery(ctx->count_ev);
+            if (e == hipSuccess) break;
+            if (e != hipErrorNotReady) return hip_fail(e, "pair count wait");
+            sched_yield();
+        }
+        total = *(volatile uint64_t*)ctx->host_count;
     }
-    const uint64_t total = *(volatile uint64_t*)ctx->host_count;
     if (n_pairs_out) *n_pairs_out = total;
     ctx->n_pairs = total;
     if (total > s.max_pairs) {
@@ -421,6 +442,14 @@ gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out
     ctx->sorted_g = sorted_g;
     ctx->state = kBinned;
     return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out) {
+    return bin_sort_impl(ctx, stream, n_pairs_out, false);
 }
 
 gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_contrib, hipStream_t stream) {

@@ -10,6 +10,7 @@ Small configurations are compared element by element; the full-size
 configurations on sampled tiles and sampled Gaussians the oracle computes
 one by one.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -314,5 +315,30 @@ def test_tile_order_leaves_outputs_unchanged(name):
         for a, c in zip(outs[0], outs[1]):
             assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
                                   c.view(np.uint32) if c.dtype == np.float32 else c)
+    finally:
+        r.close()
+
+
+def test_rejected_project_leaves_the_context_unchanged():
+    """gs_project validates every camera before it changes the context: a call rejected for a
+    bad camera of its last view leaves the cameras and the state of the previous render, so a
+    following score replay gives the same tokens as one without the rejected call."""
+    _need_gpu()
+    b = _binding()
+    sc = scenes.tiny_scene(seed=5, n=30, n_views=3, W=33, H=17, sh_degree=1, background=(0.3, 0.6, 0.1))
+    obs = torch.from_numpy(oracle.render_observation(sc)).cuda()
+    r = b.rasterizer_for_scene(sc)
+    try:
+        r.project_and_bin()
+        r.render()
+        want = r.score_replay(obs).clone()
+        bad = sc.cams.copy()
+        bad[2, 12] = 0.0                      # focal length of the last view
+        st = b.load_library().gs_project(r.ctx, ctypes.byref(r.gauss), b.make_cameras(bad), ctypes.byref(r.params),
+                                         None)
+        assert st == b.GS_ERR_INVALID_ARGUMENT
+        got = r.score_replay(obs)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)
     finally:
         r.close()
