@@ -38,7 +38,7 @@ ABI_SYMBOLS = ("gs_default_params", "gs_workspace_size", "gs_context_create", "g
                "gs_project", "gs_bin_sort", "gs_render", "gs_score_replay", "gs_backward", "gs_render_features",
                "gs_attribute", "gs_status_string",
                "gs_last_error", "gs_debug_exp2", "gs_debug_export", "gs_debug_topk", "gs_profile_enable",
-               "gs_profile_stages", "gs_profile_read")
+               "gs_profile_stages", "gs_profile_read", "gs_render_score_noalloc")
 
 
 class gs_gaussians(ctypes.Structure):
@@ -125,6 +125,10 @@ def load_library(path: str = LIB_PATH):
     lib.gs_profile_stages.argtypes = [P, ctypes.c_uint32]
     lib.gs_profile_read.restype = St
     lib.gs_profile_read.argtypes = [P, P, P, ctypes.c_int32]
+    lib.gs_render_score_noalloc.restype = St
+    lib.gs_render_score_noalloc.argtypes = [ctypes.POINTER(gs_gaussians), ctypes.POINTER(gs_camera), ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(gs_params), P, P, P, P,
+                                            P, P]
     _lib = lib
     return lib
 
@@ -198,6 +202,14 @@ def gs_render(ctx, color, T_final, n_contrib, stream=None) -> None:
 def gs_score_replay(ctx, observed, tokens, stream=None) -> None:
     _check(load_library().gs_score_replay(ctx, _dev_ptr(observed), _dev_ptr(tokens), _stream_handle(stream)),
            "gs_score_replay")
+
+
+def gs_render_score_noalloc(gauss: gs_gaussians, cams, n_views, width, height, params: gs_params, observed,
+                            color, T_final, n_contrib, tokens, stream=None) -> None:
+    _check(load_library().gs_render_score_noalloc(ctypes.byref(gauss), cams, int(n_views), int(width), int(height),
+                                                  ctypes.byref(params), _dev_ptr(observed), _dev_ptr(color),
+                                                  _dev_ptr(T_final), _dev_ptr(n_contrib), _dev_ptr(tokens),
+                                                  _stream_handle(stream)), "gs_render_score_noalloc")
 
 
 def gs_backward(ctx, grad_color, grads: gs_gaussian_grads, stream=None) -> None:

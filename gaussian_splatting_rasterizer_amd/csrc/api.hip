@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -450,6 +451,96 @@ extern "C" {
 
 gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out) {
     return bin_sort_impl(ctx, stream, n_pairs_out, false);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The path without any allocation: the workspace is a file-scope device array
+// (one per GPU, held until the process ends) and the context lives on the stack.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)GS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's copy of `scratch`, looked up once per device with that device
+// current (the array's name is a host-side stand-in, not a device address).
+gs_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(GS_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "scratch address");
+        if (!ptr || !aligned(ptr, 256)) return fail(GS_ERR_HIP, "scratch address is null or misaligned");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gs_status gs_render_score_noalloc(const gs_gaussians* scene, const gs_camera* cams, int32_t n_views, int32_t width,
+                                  int32_t height, const gs_params* params, const float* observed, float* color,
+                                  float* T_final, int32_t* n_contrib, float* tokens, hipStream_t stream) {
+    if (!scene || !cams || !params || !observed) return fail(GS_ERR_INVALID_ARGUMENT, "null argument");
+    gs_dims d;
+    d.n_gaussians = scene->n;
+    d.sh_degree = scene->sh_degree;
+    d.n_views = n_views;
+    d.width = width;
+    d.height = height;
+    d.max_pairs = 1;
+    gs_status st = check_dims(&d);
+    if (st != GS_OK) return st;
+    // the largest pair capacity whose workspace fits the scratch array (the workspace grows linearly in it)
+    Workspace probe;
+    const size_t base = carve_workspace(make_sizes(d), nullptr, &probe);
+    d.max_pairs = 1025;
+    const size_t per_1024 = carve_workspace(make_sizes(d), nullptr, &probe) - base;
+    if (base > kScratchBytes)
+        return fail(GS_ERR_WORKSPACE_TOO_SMALL,
+                    "gs_render_score_noalloc: %lld Gaussians x %d views of %dx%d need %zu bytes before any pair, "
+                    "the scratch array holds %zu", (long long)scene->n, n_views, width, height, base, kScratchBytes);
+    uint64_t cap = 1 + (uint64_t)((kScratchBytes - base) / (per_1024 + 1)) * 1024;
+    if (cap > (1ull << 32) - (1ull << 16)) cap = (1ull << 32) - (1ull << 16);
+    for (;;) {
+        d.max_pairs = cap;
+        if (carve_workspace(make_sizes(d), nullptr, &probe) <= kScratchBytes || cap <= 1) break;
+        cap = cap > 1024 ? cap - 1024 : 1;
+    }
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != GS_OK) return st;
+    // a context on the stack: no timers, no pinned word, no events (the pair count is copied back)
+    gs_context ctx{};
+    ctx.s = make_sizes(d);
+    carve_workspace(ctx.s, (char*)ws, &ctx.ws);
+    ctx.state = kCreated;
+    ctx.epoch = 0;  // clears the look-back words: the previous call's contents are not trusted
+    st = gs_project(&ctx, scene, cams, params, stream);
+    if (st != GS_OK) return st;
+    uint64_t n_pairs = 0;
+    st = bin_sort_impl(&ctx, stream, &n_pairs, true);
+    if (st == GS_ERR_WORKSPACE_TOO_SMALL)
+        return fail(GS_ERR_WORKSPACE_TOO_SMALL,
+                    "gs_render_score_noalloc: %llu (tile, Gaussian) pairs exceed the %llu the %zu-byte scratch array "
+                    "holds for this problem", (unsigned long long)n_pairs, (unsigned long long)cap, kScratchBytes);
+    if (st != GS_OK) return st;
+    st = gs_render(&ctx, color, T_final, n_contrib, stream);
+    if (st != GS_OK) return st;
+    return gs_score_replay(&ctx, observed, tokens, stream);
 }
 
 gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_contrib, hipStream_t stream) {

@@ -59,6 +59,8 @@ typedef enum {
 
 /* Limits of this implementation. */
 #define GS_MAX_VIEWS 32
+/* Size of the device array gs_render_score_noalloc works in (one per GPU). */
+#define GS_NOALLOC_SCRATCH_BYTES (64u << 20)
 #define GS_TILE 16
 
 /* Scene: n Gaussians, parameters already activated.
@@ -178,6 +180,26 @@ GSR_API gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32
  *                           log(tr A + eps) (1) ]
  * with Q = eps + sum_v q_gv the cross-view support. */
 GSR_API gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens, hipStream_t stream);
+
+/* The whole path -- gs_project, gs_bin_sort, gs_render, gs_score_replay --
+ * in one call that allocates nothing, for callers that cannot allocate device
+ * or pinned memory (tight serving loops, harnesses that forbid allocation).
+ * It takes the same inputs and writes the same outputs as that sequence
+ * (`color`, `T_final`, `n_contrib` may be null; `tokens` [n, 9 + 3 d] may be
+ * null only when n = 0), with a context on the host stack and, as workspace,
+ * a file-scope device array of GS_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU
+ * the library runs on holds until the process ends.  The pair count is read
+ * back with a copy into host stack memory (the call synchronises `stream`).
+ * Problems whose workspace does not fit -- the records of n x n_views, or the
+ * (tile, Gaussian) pairs the binning finds -- return
+ * GS_ERR_WORKSPACE_TOO_SMALL with the sizes in gs_last_error(); the outputs
+ * are then not written.  Every call on a GPU uses that GPU's one array, so
+ * calls that overlap on one GPU (several threads or streams) race; the array
+ * keeps the last call's contents, and the call clears what it needs cleared. */
+GSR_API gs_status gs_render_score_noalloc(const gs_gaussians* scene, const gs_camera* cams, int32_t n_views,
+                                          int32_t width, int32_t height, const gs_params* params,
+                                          const float* observed, float* color, float* T_final, int32_t* n_contrib,
+                                          float* tokens, hipStream_t stream);
 
 /* Gradients of a scalar loss with respect to the scene parameters, laid out
  * like the gs_gaussians arrays they belong to (float32 device arrays, written,
