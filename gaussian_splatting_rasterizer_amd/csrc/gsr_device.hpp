@@ -137,11 +137,12 @@ __device__ __forceinline__ void camera_centre_f64(const float* cam, const double
                (double)cam[9 + i];
 }
 
-// Field-of-view clamp of the perspective Jacobian's lateral offset: bit 0 when |tx / tz| exceeds
+// Field-of-view clamp of the perspective Jacobian's lateral offset: bit 0 when |tx (1 / tz)| exceeds
 // lim[0], bit 1 likewise in y.  One function for the preprocess and the backward, so both take
 // the same decision from the same float64 operations.
 __device__ __forceinline__ int fov_clip_bits(const double t[3], const double lim[2]) {
-    const double ux = t[0] / t[2], uy = t[1] / t[2];
+    const double iz = 1.0 / t[2];
+    const double ux = t[0] * iz, uy = t[1] * iz;
     return ((ux < -lim[0] || ux > lim[0]) ? 1 : 0) | ((uy < -lim[1] || uy > lim[1]) ? 2 : 0);
 }
 

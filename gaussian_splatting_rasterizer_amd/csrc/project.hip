@@ -102,13 +102,12 @@ __global__ __launch_bounds__(256) void k_project(const float* __restrict__ means
         // perspective Jacobian at the centre clamped to kFovClamp x the half field of view
         const double limx = cams.lim[v][0], limy = cams.lim[v][1];
         const int clip = fov_clip_bits(t, cams.lim[v]);
-        const double ux = tx / tz, uy = ty / tz;
+        const double iz = 1.0 / tz;
+        const double ux = tx * iz, uy = ty * iz;
         const double uxc = (clip & 1) ? (ux < 0.0 ? -limx : limx) : ux;
         const double uyc = (clip & 2) ? (uy < 0.0 ? -limy : limy) : uy;
-        const double txc = uxc * tz, tyc = uyc * tz;
-        const double tz2 = tz * tz;
-        const double j00 = (double)fx / tz, j02 = -((double)fx * txc) / tz2;
-        const double j11 = (double)fy / tz, j12 = -((double)fy * tyc) / tz2;
+        const double j00 = (double)fx * iz, j02 = -((double)fx * uxc) * iz;
+        const double j11 = (double)fy * iz, j12 = -((double)fy * uyc) * iz;
         const double u00 = j00 * Cc[0] + j02 * Cc[6];
         const double u01 = j00 * Cc[1] + j02 * Cc[7];
         const double u02 = j00 * Cc[2] + j02 * Cc[8];

@@ -274,7 +274,8 @@ static int nacc(const scene* s) { return NACC_FIXED + 6 * s->d + NACC_SENS; } /*
  *    quaternion's rotation (R(q) of the unnormalised quaternion scaled by
  *    2 / |q|^2, which equals the rotation of q / |q|), M = R(q) diag(s),
  *    Sigma3 = M M^T, Sigma_cam = R_v Sigma3 R_v^T, the perspective Jacobian at
- *    the centre clamped to 1.3x the half field of view, the dilated 2D
+ *    the centre clamped to 1.3x the half field of view (with 1/t_z taken once:
+ *    u = t_x (1/t_z), j00 = f_x (1/t_z), j02 = -(f_x u_c) (1/t_z)), the dilated 2D
  *    covariance [[a, b], [b, c]] and its determinant, the projected centre;
  *  - the 2D covariance and determinant rounded to float32, then in float32
  *    (correctly rounded division and square root): the 3-sigma radius, the
@@ -342,15 +343,14 @@ static void project32(const scene* s, int g, int v, rec32* r)
     /* field-of-view clamp of the Jacobian's lateral offset (decision shared with the backward) */
     const double limx = FOV_CLAMP_D * ((0.5 * (double)s->W) / (double)fx);
     const double limy = FOV_CLAMP_D * ((0.5 * (double)s->H) / (double)fy);
-    const double ux = tx / tz, uy = ty / tz;
+    const double iz = 1.0 / tz;
+    const double ux = tx * iz, uy = ty * iz;
     r->clip[0] = ux < -limx || ux > limx;
     r->clip[1] = uy < -limy || uy > limy;
     const double uxc = ux < -limx ? -limx : (ux > limx ? limx : ux);
     const double uyc = uy < -limy ? -limy : (uy > limy ? limy : uy);
-    const double txc = uxc * tz, tyc = uyc * tz;
-    const double tz2 = tz * tz;
-    const double j00 = (double)fx / tz, j02 = -((double)fx * txc) / tz2;
-    const double j11 = (double)fy / tz, j12 = -((double)fy * tyc) / tz2;
+    const double j00 = (double)fx * iz, j02 = -((double)fx * uxc) * iz;
+    const double j11 = (double)fy * iz, j12 = -((double)fy * uyc) * iz;
     const double u00 = j00 * Cc[0] + j02 * Cc[6];
     const double u01 = j00 * Cc[1] + j02 * Cc[7];
     const double u02 = j00 * Cc[2] + j02 * Cc[8];
