@@ -9,7 +9,7 @@
 // pixels are all saturated stops.  Batches of 256 list entries are gathered
 // (one per thread) into LDS -- centre relative to the tile, exponent factors,
 // opacity, clamped colour, and a conservative box of the pixels the entry can
-// reach -- and each
+// reach, in half pixels packed into one word -- and each
 // wave compacts, in list order, the entries whose box meets its quadrant, then
 // walks only those with broadcast LDS reads.  The box is conservative for the
 // float32 evaluation, so the skipped entries are exactly ones every pixel of
@@ -30,6 +30,17 @@ namespace gsr {
 
 constexpr int kRenderBatch = 256;
 
+// A tile-relative box {x0, x1, y0, y1} in half pixels, as four signed bytes ceil(2 x0), floor(2 x1),
+// ceil(2 y0), floor(2 y1) clamped to [-2, 40].  Pixel centres sit at odd half-pixel counts c, and for an
+// integer c, x0 <= c/2 exactly when ceil(2 x0) <= c and x1 >= c/2 exactly when floor(2 x1) >= c; the clamp
+// keeps every outcome against the tile's counts 1 .. 31.  So the byte test decides as the float box test.
+// (A NaN edge becomes -2: the entry is kept.)
+__device__ __forceinline__ uint32_t box_half_pixels(float4 b) {
+    const auto lo = [](float v) { return (uint32_t)(int)fminf(fmaxf(ceilf(2.0f * v), -2.0f), 40.0f) & 0xffu; };
+    const auto hi = [](float v) { return (uint32_t)(int)fminf(fmaxf(floorf(2.0f * v), -2.0f), 40.0f) & 0xffu; };
+    return lo(b.x) | (hi(b.y) << 8) | (lo(b.z) << 16) | (hi(b.w) << 24);
+}
+
 template <bool STATS>
 __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
                                                 const float4* __restrict__ rec0, const float4* __restrict__ rec1,
@@ -46,12 +57,15 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
              i += (int64_t)gridDim.x * blockDim.x)
             slot_bits[i] = 0u;
     }
+    // an entry's staged vectors sit at the same byte offset (16 j, kept in the wave's list) of each array
     __shared__ float4 s0[kRenderBatch];   // {tile-relative centre (2), s1, s2}
     __shared__ float4 s1[kRenderBatch];   // {s3, opacity, colour r, colour g}
-    __shared__ float s2[kRenderBatch];    // colour b
-    __shared__ float4 sbox[kRenderBatch]; // conservative box of the pixels the entry can reach
-    __shared__ uint8_t slist[4][kRenderBatch];
+    __shared__ float4 s2[kRenderBatch];   // {colour b, unused}
+    __shared__ uint32_t sbox[kRenderBatch];  // conservative box of the pixels the entry can reach, in half pixels
+    __shared__ uint16_t slist[4][kRenderBatch];
     __shared__ uint8_t s_ev[4][kRenderBatch];  // per wave: some pixel contributed or saturated at the entry
+    // the same per position of the wave's list (laid out like the list, so both share one address)
+    __shared__ uint16_t s_evk[4][kRenderBatch];
 
     // tiles in the order the previous render of this context measured (longest first), or the natural order;
     // the order only changes how the blocks pack onto the GPU, never a result
@@ -67,8 +81,9 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
     const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     // pixel-centre range of this wave's 8x8 quadrant, tile-relative
-    const float qx0 = (float)((wave & 1) * 8) + 0.5f, qx1 = qx0 + 7.0f;
-    const float qy0 = (float)((wave >> 1) * 8) + 0.5f, qy1 = qy0 + 7.0f;
+    // (in half pixels: the centres 0.5 .. 7.5 of the first quadrant column are 1 .. 15)
+    const int qx0 = (wave & 1) * 16 + 1, qx1 = qx0 + 14;
+    const int qy0 = (wave >> 1) * 16 + 1, qy1 = qy0 + 14;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -101,8 +116,8 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
             const float mxt = tile_centre(a.x, c.z, tx), myt = tile_centre(a.y, c.w, ty);
             s0[threadIdx.x] = make_float4(mxt, myt, a.z, a.w);
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
-            s2[threadIdx.x] = clamp_colour(c.x);
-            sbox[threadIdx.x] = entry_box_unpack(mxt, myt, __float_as_uint(c.y));
+            s2[threadIdx.x] = make_float4(clamp_colour(c.x), 0.0f, 0.0f, 0.0f);
+            sbox[threadIdx.x] = box_half_pixels(entry_box_unpack(mxt, myt, __float_as_uint(c.y)));
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kRenderBatch, rg.y - base);
@@ -116,20 +131,25 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                     // the statistics pass evaluates every entry, so its distance-cut count is the plain
                     // algorithm's (the skipped entries fail the alpha test at every pixel of the quadrant, so
                     // the decisions are the same)
-                    const float4 bx = sbox[j];
-                    hit = STATS || (bx.x <= qx1 && bx.y >= qx0 && bx.z <= qy1 && bx.w >= qy0);
+                    const uint32_t bx = sbox[j];
+                    hit = STATS || ((int)(int8_t)bx <= qx1 && (int)(int8_t)(bx >> 8) >= qx0 &&
+                                    (int)(int8_t)(bx >> 16) <= qy1 && (int)(int8_t)(bx >> 24) >= qy0);
                 }
                 const uint64_t m = __ballot(hit);
-                if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
+                if (hit) {
+                    const int pos = nw + __popcll(m & lt_mask);
+                    slist[wave][pos] = (uint16_t)(j * sizeof(float4));
+                    s_evk[wave][pos] = 0;
+                }
                 nw += __popcll(m);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             for (int k = 0; k < nw; ++k) {
-                const int j = slist[wave][k];
-                const float4 a = s0[j];
-                const float4 b = s1[j];
+                const uint32_t off = slist[wave][k];  // 16 j
+                const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s0) + off);
+                const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s1) + off);
                 // evaluated in every lane; the decisions below mask lanes that are done or beyond the cut
                 const float dx = px - a.x, dy = py - a.y;
                 const float S = quad_S(a.z, a.w, b.x, dx, dy);
@@ -142,7 +162,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                 const bool contrib = pass && !sat;
                 if constexpr (STATS) {
                     n_near += near ? 1u : 0u;
-                    if (sat) stop = base + (uint32_t)j;
+                    if (sat) stop = base + off / (uint32_t)sizeof(float4);
                 }
                 done = done || sat;
                 if constexpr (!STATS) {
@@ -150,12 +170,20 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                     const float w = contrib ? alpha * Tr : 0.0f;
                     h0 = __builtin_fmaf(b.z, w, h0);
                     h1 = __builtin_fmaf(b.w, w, h1);
-                    h2 = __builtin_fmaf(s2[j], w, h2);
+                    h2 = __builtin_fmaf(reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s2) + off)->x, w, h2);
                     n += contrib ? 1 : 0;
                 }
                 Tr = contrib ? tT : Tr;
-                if (!STATS && pass) s_ev[wave][j] = 1;  // contributed or saturated (every such lane writes the same byte)
+                if (!STATS && pass) s_evk[wave][k] = 1;  // contributed or saturated (every such lane writes the same)
                 if (__ballot(!done) == 0ull) break;
+            }
+            if constexpr (!STATS) {
+                // the events by list position, moved to the entries they name
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                for (int k = lane; k < nw; k += 64)
+                    if (s_evk[wave][k]) s_ev[wave][slist[wave][k] / sizeof(float4)] = 1;
             }
         }
         prev_base = base;

@@ -4,15 +4,17 @@
 // Analytic Score Replay) and the "Exact Score Operators" / "Final Token".
 //
 // k_replay: the same tiles, lists, order and float32 decisions as the render.
-// Each pixel re-walks its list keeping the transmittance T and S = C_hat - P,
-// the rendered colour minus the prefix colour (one fused multiply-add per
-// channel and entry), and for every contribution forms
+// Each pixel re-walks its list keeping the transmittance T and, for every
+// contribution, forms
 //     S   = C_hat - P - T alpha c                     (suffix times T(1-alpha))
 //     C+  = S / (T (1 - alpha) + eps)                 (suffix equation)
 //     rho = <r, c - C+>,  r = C_hat - C_obs            (residual-suffix contrast)
 //     w   = T alpha                                   (visibility weight)
 //     M   = [o G < 0.99] and [T (1 - alpha) >= den_min]   (mask)
-// and the seven per-pixel partials (the eighth slot of the reduction stays zero)
+// The suffix enters rho only through <r, S>, so each pixel keeps that scalar,
+// q = <r, C_hat - P>: it starts at <r, C_hat> and every contribution takes
+// w <r, c> off it (one fused multiply-add per entry instead of three).
+// and the seven per-pixel partials (the eighth slot of a stored partial is zero)
 //     W += w, U_a += M w rho, U_mu += M w rho (p - mu), U_c += w r;
 // the pair's partial then gets the conic applied to U_mu and the colour clamp
 // mask applied to U_c (both constant over the pair).
@@ -47,7 +49,9 @@
 
 namespace gsr {
 
-constexpr int kReplayBatch = 128;
+// Entries staged per batch: 96 keeps the block's LDS (about 19 KB) small enough for eight blocks per CU.
+constexpr int kReplayBatch = 96;
+static_assert(2 * kReplayBatch <= 256, "two flush threads per staged entry");
 
 __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
                                                 const uint32_t* __restrict__ slot_base,
@@ -57,13 +61,15 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                                                 const uint8_t* __restrict__ events, float eps, float den_min,
                                                 float4* __restrict__ partials, uint32_t* __restrict__ slot_bits,
                                                 const uint32_t* __restrict__ tile_order) {
-    __shared__ float4 s0[kReplayBatch];
-    __shared__ float4 s1[kReplayBatch];
-    __shared__ float s2[kReplayBatch];
+    // an entry's three staged vectors sit at the same byte offset of three arrays, so one offset (16 j,
+    // kept in the wave's list) addresses all of them
+    __shared__ float4 s0[kReplayBatch];        // {tile-relative centre (2), s1, s2}
+    __shared__ float4 s1[kReplayBatch];        // {s3, opacity, colour r, colour g}
+    __shared__ float4 s2[kReplayBatch];        // {colour b, unused}
     __shared__ uint8_t s_evb[kReplayBatch];    // event bits of each staged entry (bit w: wave w)
     __shared__ uint32_t s_slot[kReplayBatch];  // partial slot of each staged pair
     __shared__ uint8_t s_mask[kReplayBatch];   // colour clamp mask bits (pre-clamp colour finite and >= 0), r g b
-    __shared__ uint8_t slist[4][kReplayBatch];
+    __shared__ uint32_t slist[4][kReplayBatch];
     __shared__ __align__(16) float sp[4][kReplayBatch][8];
 
     const int tile = (int)tile_order[blockIdx.x];
@@ -93,8 +99,8 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
         r2 = Ch2 - observed[3 * pix + 2];
     }
     float Tr = 1.0f;
-    // the suffix composite times the transmittance in front of it: C_hat minus the prefix colour
-    float S0 = Ch0, S1 = Ch1, S2 = Ch2;
+    // <r, S> with S the suffix composite times the transmittance in front of it (C_hat minus the prefix colour)
+    float q = __builtin_fmaf(r2, Ch2, __builtin_fmaf(r1, Ch1, r0 * Ch0));
     bool done = !inside;
 
     uint32_t base = rg.x;
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             const uint2 rc = rect[rid];
             s0[threadIdx.x] = make_float4(tile_centre(a.x, c.z, tx), tile_centre(a.y, c.w, ty), a.z, a.w);
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
-            s2[threadIdx.x] = clamp_colour(c.x);
+            s2[threadIdx.x] = make_float4(clamp_colour(c.x), 0.0f, 0.0f, 0.0f);
             s_evb[threadIdx.x] = events[i];
             // slot of this (tile, Gaussian) pair: the record's slot base + row-major tile index
             const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16, wx = (rc.y & 0xffffu) - x0;
@@ -126,16 +132,17 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 const int j = c + lane;
                 const bool hit = j < cnt && ((s_evb[j] >> wave) & 1u);
                 const uint64_t m = __ballot(hit);
-                if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
+                if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint32_t)(j * sizeof(float4));
                 nw += __popcll(m);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             for (int k = 0; k < nw; ++k) {
-                const int j = slist[wave][k];
-                const float4 a = s0[j];
-                const float4 b = s1[j];
+                const uint32_t off = slist[wave][k];  // 16 j
+                const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s0) + off);
+                const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s1) + off);
+                const float cbl = reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s2) + off)->x;
                 // evaluated in every lane; the decisions mask lanes that are done or beyond the cut
                 const float dx = px - a.x, dy = py - a.y;
                 const float S = quad_S(a.z, a.w, b.x, dx, dy);
@@ -151,22 +158,24 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 // some lane of the wave contributes or saturates at every listed entry (a wave's list ends
                 // at its last such entry), so the partials are formed without testing for a contribution
                 {
-                    const float cr = b.z, cg = b.w, cbl = s2[j];
+                    const float cr = b.z, cg = b.w;
                     const float w = contrib ? alpha * Tr : 0.0f;
-                    // the suffix behind this entry, times T (1 - alpha): C_hat minus the prefix including it
-                    // (lanes without a contribution subtract zero)
-                    S0 = __builtin_fmaf(-cr, w, S0);
-                    S1 = __builtin_fmaf(-cg, w, S1);
-                    S2 = __builtin_fmaf(-cbl, w, S2);
+                    const float rc = __builtin_fmaf(r2, cbl, __builtin_fmaf(r1, cg, r0 * cr));
+                    // <r, S> behind this entry: the prefix now includes it (lanes without a contribution
+                    // subtract zero)
+                    q = __builtin_fmaf(-w, rc, q);
                     const float inv_den = __builtin_amdgcn_rcpf(tT + eps);
                     // rho = <r, c - S / den> = <r, c> - <r, S> / den
-                    const float rc = __builtin_fmaf(r2, cbl, __builtin_fmaf(r1, cg, r0 * cr));
-                    const float rS = __builtin_fmaf(r2, S2, __builtin_fmaf(r1, S1, r0 * S0));
-                    const float rho = __builtin_fmaf(-rS, inv_den, rc);
+                    const float rho = __builtin_fmaf(-q, inv_den, rc);
                     const float mw = (contrib && !clamped && tT >= den_min) ? w * rho : 0.0f;
-                    const float x[8] = {w, mw, mw * dx, mw * dy, w * r0, w * r1, w * r2, 0.0f};
+                    // the eighth component is never read (the flush stores zero there): rho, a value that
+                    // dies here, fills it without a register move
+                    const float x[8] = {w, mw, mw * dx, mw * dy, w * r0, w * r1, w * r2, rho};
                     const float red = wave_reduce8(x, lane);
-                    if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
+                    // every lane of a group of eight holds its component's sum: all store (the same value to
+                    // the same word), so no lane mask is set up for the store
+                    // (sp[wave][j][lane >> 3]: rows of 32 bytes, so the row's byte offset is 2 off)
+                    *reinterpret_cast<float*>(reinterpret_cast<char*>(&sp[wave][0][0]) + 2 * off + 4 * (lane >> 3)) = red;
                     Tr = contrib ? tT : Tr;
                 }
             }
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 acc = make_float4(acc.x, acc.y, ca * acc.z + cb * acc.w, cb * acc.z + cc * acc.w);
             } else {
                 const uint32_t m = s_mask[j];
-                acc = make_float4(m & 1u ? acc.x : 0.0f, m & 2u ? acc.y : 0.0f, m & 4u ? acc.z : 0.0f, acc.w);
+                acc = make_float4(m & 1u ? acc.x : 0.0f, m & 2u ? acc.y : 0.0f, m & 4u ? acc.z : 0.0f, 0.0f);
             }
             const uint32_t slot = s_slot[j];
             partials[2 * (int64_t)slot + h] = acc;
@@ -265,8 +274,9 @@ constexpr int kGatherThreads = 256;
 
 // NQ float4 per slot and per record: 2 for the score replay, 3 for the backward.
 // Each thread takes kGatherRecs records 64 apart (a wave covers kGatherRecs
-// runs of 64).  Per record a lane reads the bit words of its range (the first
-// three together with those of its other records) and decides whether any slot
+// runs of 64; one run per wave measured fastest: more waves, shorter chains of
+// dependent loads per wave).  Per record a lane reads the bit words of its
+// range (the first three together) and decides whether any slot
 // was written; the ballot over one record index of the wave is then exactly that
 // run's live and reached mask words.  The few reached records are summed by the
 // whole wave, one record at a time: lane l takes slots l, l + 64, ... of the
@@ -276,7 +286,7 @@ constexpr int kGatherThreads = 256;
 // Where most records are reached (single views with every Gaussian visible) a
 // run with more than kGatherDenseRun reached records is summed lane per
 // record instead, each lane keeping four slots' loads in flight.
-constexpr int kGatherRecs = 4;
+constexpr int kGatherRecs = 1;
 // A run with more reached records than this is summed lane per record instead.
 constexpr int kGatherDenseRun = 8;
 
