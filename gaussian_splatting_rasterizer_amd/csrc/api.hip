@@ -45,6 +45,7 @@ int bits_for(uint64_t n) {  // bits needed to represent values 0..n-1
 }
 
 constexpr int64_t kBlockItems = 4096;  // items per scan block (radix blocks are larger)
+constexpr uint64_t kCountPending = ~0ull;  // the pinned pair-count word before the slot scan writes it
 
 }  // namespace
 
@@ -122,7 +123,6 @@ struct gs_context {
     uint32_t epoch;               // last radix pass epoch; 0 = look-back words not cleared yet
     uint64_t* host_count;         // pinned host word receiving the pair count (allocated on first use)
     uint64_t* host_count_dev;     // its device address: the slot scan writes the count there itself
-    hipEvent_t count_ev;
     bool packed_fresh;            // gs_project left the packed rectangles that the next depth sort reads
     bool order_valid;             // tile_order holds the order a render of this context measured
 };
@@ -267,7 +267,6 @@ gs_status gs_context_create(const gs_dims* dims, void* workspace, size_t workspa
 gs_status gs_context_destroy(gs_context* ctx) {
     if (ctx) {
         ctx->timer.destroy();
-        if (ctx->count_ev) (void)hipEventDestroy(ctx->count_ev);
         if (ctx->host_count) (void)hipHostFree(ctx->host_count);
     }
     delete ctx;
@@ -354,12 +353,9 @@ gs_status bin_sort_impl(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_o
         }
         e = hipHostGetDevicePointer((void**)&ctx->host_count_dev, ctx->host_count, 0);
         if (e != hipSuccess) return hip_fail(e, "pinned count word address");
-        e = hipEventCreateWithFlags(&ctx->count_ev, hipEventDisableTiming);
-        if (e != hipSuccess) {
-            ctx->count_ev = nullptr;
-            return hip_fail(e, "count event");
-        }
     }
+    // the pinned word holds kCountPending until the slot scan writes the count into it
+    if (!count_by_copy) *(volatile uint64_t*)ctx->host_count = kCountPending;
     const SortScratch sort_scratch{ws.lookback, ws.sort_ctl, ws.sort_part};
     // 0. slot bases of the replay's partials: tile counts scanned in record order
     tm.begin(GS_STAGE_DEPTH_SORT, stream);
@@ -369,10 +365,6 @@ gs_status bin_sort_impl(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_o
     e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream, false,
                         count_by_copy ? nullptr : ctx->host_count_dev);
     if (e != hipSuccess) return hip_fail(e, "slot scan");
-    if (!count_by_copy) {
-        e = hipEventRecord(ctx->count_ev, stream);
-        if (e != hipSuccess) return hip_fail(e, "pair count event");
-    }
     // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
     //    scan rewrites next); the tile rectangles ride along (packed, or gathered by the last pass), and
     //    the last pass writes rectangles and tile counts in depth order but no keys
@@ -399,14 +391,21 @@ gs_status bin_sort_impl(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_o
         if (e == hipSuccess) e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return hip_fail(e, "pair count copy");
     } else {
-        // wait for the pair count by polling its event, yielding the core between polls
+        // wait for the pair count by polling the pinned word (no event in the stream, so no gap between the
+        // kernels), yielding the core between polls; a stream that fails or drains without writing it ends
+        // the wait with an error
         for (;;) {
-            e = hipEventQuery(ctx->count_ev);
-            if (e == hipSuccess) break;
+            total = *(volatile uint64_t*)ctx->host_count;
+            if (total != kCountPending) break;
+            e = hipStreamQuery(stream);
+            if (e == hipSuccess) {
+                total = *(volatile uint64_t*)ctx->host_count;
+                if (total == kCountPending) return fail(GS_ERR_HIP, "the slot scan did not write the pair count");
+                break;
+            }
             if (e != hipErrorNotReady) return hip_fail(e, "pair count wait");
             sched_yield();
         }
-        total = *(volatile uint64_t*)ctx->host_count;
     }
     if (n_pairs_out) *n_pairs_out = total;
     ctx->n_pairs = total;
