@@ -40,6 +40,10 @@ constexpr int kRadixWaves = kRadixThreads / 64;
 constexpr int kRadixItems = 16;
 constexpr int kRadixTile = kRadixThreads * kRadixItems;  // 8192
 static_assert(kRadixTile == kSortTile, "radix tile size");
+// Sorts of at most kSmallSortKeys keys use tiles of half the size: a pass over few tiles takes about as long
+// as one tile does (ranking, look-back and scatter in series), and a half tile halves its ranking.
+constexpr int kSmallRadixItems = kRadixItems / 2;
+static_assert(kRadixThreads * kSmallRadixItems == kSmallSortTile, "small radix tile size");
 constexpr int kMaxDigitBits = 8;
 constexpr int kMaxBins = 1 << kMaxDigitBits;
 constexpr int kMaxPasses = kSortMaxPasses;
@@ -316,17 +320,18 @@ __global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restric
 // separate value array; the last pass writes the value bits and records every key's range.
 enum RadixMode { kPlain = 0, kCarryRect = 1, kGatherRect = 2, kRanges = 3, kPackedMid = 4, kPackedLast = 5 };
 
-template <int MODE>
+template <int MODE, int ITEMS>
 __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift, int bits,
     uint32_t* __restrict__ ticket, const uint32_t* __restrict__ digit_tot, uint64_t* __restrict__ lookback,
     uint32_t epoch, uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, RectCarry rc) {
+    constexpr int kTileKeys = kRadixThreads * ITEMS;
     __shared__ uint32_t cnt[kRadixWaves][kMaxBins];  // per-wave counts, then per-wave block-local bases
     __shared__ uint32_t gdelta[kMaxBins];            // global position - block-local position, per digit
     __shared__ uint64_t scan_lds[kRadixThreads / 64];
-    __shared__ uint32_t skey[kRadixTile];
+    __shared__ uint32_t skey[kTileKeys];
     constexpr bool kPacked = MODE == kPackedMid || MODE == kPackedLast;
-    __shared__ uint32_t sval[kPacked ? 1 : kRadixTile];
+    __shared__ uint32_t sval[kPacked ? 1 : kTileKeys];
     __shared__ uint32_t s_tile;
     const int nbins = 1 << bits;
     const uint32_t mask = (uint32_t)nbins - 1u;
@@ -336,21 +341,21 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     __syncthreads();
     const int64_t tile = s_tile;
 
-    const int64_t bbase = tile * kRadixTile;
+    const int64_t bbase = tile * kTileKeys;
     // element indices within the tile, 32-bit (cheap to recompute where needed)
-    const int nblk = (int)(n - bbase < kRadixTile ? n - bbase : kRadixTile);
-    const int wbase = wave * (kRadixTile / kRadixWaves) + lane;
+    const int nblk = (int)(n - bbase < kTileKeys ? n - bbase : kTileKeys);
+    const int wbase = wave * (kTileKeys / kRadixWaves) + lane;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint32_t key[kRadixItems], val[kRadixItems], rank[kRadixItems];
+    uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
         const int e = wbase + i * 64;
         const bool valid = e < nblk;
         key[i] = valid ? keys_in[bbase + e] : 0u;
         val[i] = (valid && !kPacked) ? (vals_in ? vals_in[bbase + e] : (uint32_t)(bbase + e)) : 0u;
     }
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
         const bool valid = wbase + i * 64 < nblk;
         const uint32_t dgt = (key[i] >> shift) & mask;
         const uint64_t peers = match_peers(dgt, bits, valid);
@@ -392,11 +397,11 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     __syncthreads();
     // block-local reorder: each digit's keys become one contiguous run; the LDS
     // positions (< 8192) are kept two to a register for a carried second reorder
-    uint32_t lpk[kRadixItems / 2];
+    uint32_t lpk[ITEMS / 2];
 #pragma unroll
-    for (int i = 0; i < kRadixItems / 2; ++i) lpk[i] = 0u;
+    for (int i = 0; i < ITEMS / 2; ++i) lpk[i] = 0u;
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
         if (wbase + i * 64 >= nblk) continue;
         const uint32_t lp = cnt[wave][(key[i] >> shift) & mask] + rank[i];
         skey[lp] = key[i];
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     if (MODE == kCarryRect) {
         // keys and values out; each element's output position is parked in the value buffer
 #pragma unroll 4
-        for (int i = 0; i < kRadixItems; ++i) {
+        for (int i = 0; i < ITEMS; ++i) {
             const int lp = i * kRadixThreads + threadIdx.x;
             if (lp >= nblk) break;
             const uint32_t k = skey[lp];
@@ -451,21 +456,21 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         }
         // second reorder, through the key buffer: the carried rectangles, loaded only now
         __syncthreads();
-        uint32_t q[kRadixItems];
+        uint32_t q[ITEMS];
 #pragma unroll
-        for (int i = 0; i < kRadixItems; ++i) {  // all loads in flight, then the LDS stores
+        for (int i = 0; i < ITEMS; ++i) {  // all loads in flight, then the LDS stores
             const int e = wbase + i * 64;
             q[i] = 0u;
             if (e < nblk) q[i] = rc.pack_src ? pack_rect(rc.pack_src[bbase + e]) : rc.pay_in[bbase + e];
         }
 #pragma unroll
-        for (int i = 0; i < kRadixItems; ++i) {
+        for (int i = 0; i < ITEMS; ++i) {
             if (wbase + i * 64 >= nblk) continue;
             skey[(lpk[i >> 1] >> (16 * (i & 1))) & 0xffffu] = q[i];
         }
         __syncthreads();
 #pragma unroll 4
-        for (int i = 0; i < kRadixItems; ++i) {
+        for (int i = 0; i < ITEMS; ++i) {
             const int lp = i * kRadixThreads + threadIdx.x;
             if (lp >= nblk) break;
             const uint32_t q = skey[lp];
@@ -480,9 +485,9 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         }
         return;
     }
-    uint32_t pos[kRadixItems];
+    uint32_t pos[ITEMS];
 #pragma unroll
-    for (int i = 0; i < kRadixItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
         const int lp = i * kRadixThreads + threadIdx.x;
         const bool ok = lp < nblk;
         const uint32_t k = ok ? skey[lp] : 0u;
@@ -510,14 +515,14 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     }
     if (MODE == kGatherRect) {
         // final depth pass without a carried rectangle: gather it by record, all gathers in flight together
-        uint2 r[kRadixItems];
+        uint2 r[ITEMS];
 #pragma unroll
-        for (int i = 0; i < kRadixItems; ++i) {
+        for (int i = 0; i < ITEMS; ++i) {
             const int lp = i * kRadixThreads + threadIdx.x;
             r[i] = lp < nblk ? rc.gather_src[sval[lp]] : make_uint2(0u, 0u);
         }
 #pragma unroll
-        for (int i = 0; i < kRadixItems; ++i) {
+        for (int i = 0; i < ITEMS; ++i) {
             const int lp = i * kRadixThreads + threadIdx.x;
             if (lp >= nblk) continue;
             rc.rect_out[pos[i]] = r[i];
@@ -534,7 +539,9 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
     const RadixDigits rd = radix_digits(bits);
     bits = rd.bits;
     const int passes = rd.passes, dbits = rd.dbits;
-    const int64_t nb = (n + kRadixTile - 1) / kRadixTile;
+    const bool small = n <= kSmallSortKeys;
+    const int64_t tile_keys = small ? kSmallSortTile : kRadixTile;
+    const int64_t nb = (n + tile_keys - 1) / tile_keys;
     // packed words: key bits [key_shift, key_shift + bits), counted beforehand, no value array, no rectangles
     const bool packed = key_shift > 0;
     // a single pass cannot read the packed rectangles from the array it writes them to
@@ -600,9 +607,17 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
                          : rc.gather_src            ? kGatherRect
                          : rc.ranges                ? kRanges
                                                     : kPlain;
-#define GSR_ONESWEEP(M)                                                                                       \
-    hipLaunchKernelGGL(k_onesweep<M>, dim3((unsigned)nb), dim3(kRadixThreads), 0, st, ksrc, vsrc, n, shift, pb, \
-                       sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins, sc.lookback, ep, kdst, vdst, rc)
+#define GSR_ONESWEEP(M)                                                                                        \
+    do {                                                                                                       \
+        if (small)                                                                                             \
+            hipLaunchKernelGGL((k_onesweep<M, kSmallRadixItems>), dim3((unsigned)nb), dim3(kRadixThreads), 0, st, \
+                               ksrc, vsrc, n, shift, pb, sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins,         \
+                               sc.lookback, ep, kdst, vdst, rc);                                               \
+        else                                                                                                   \
+            hipLaunchKernelGGL((k_onesweep<M, kRadixItems>), dim3((unsigned)nb), dim3(kRadixThreads), 0, st,     \
+                               ksrc, vsrc, n, shift, pb, sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins,         \
+                               sc.lookback, ep, kdst, vdst, rc);                                               \
+    } while (0)
         if (mode == kCarryRect) GSR_ONESWEEP(kCarryRect);
         else if (mode == kGatherRect) GSR_ONESWEEP(kGatherRect);
         else if (mode == kRanges) GSR_ONESWEEP(kRanges);
