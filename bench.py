@@ -43,10 +43,11 @@ OPS_CONTRIB_SCORE = 40  # per contribution, the replay's suffix, rho, masks and 
 OPS_CONTRIB_REPLAY = OPS_CONTRIB_FWD + OPS_CONTRIB_SCORE   # the replay re-accumulates the prefix as it goes
 OPS_CONTRIB_BWD = 70    # forward 20, suffix 6, <g,c> and <g,S> 6, 1-alpha, reciprocal, u and its mask 4,
                         # the 9 partials 8, their wave reduction 26 (eight-value reduce-scatter + one sum)
-# Algorithmic HBM bytes of the replay: per (tile, Gaussian) pair its sorted Gaussian id (4) and the 40 B of
-# the record it evaluates (centre 8, exponent factors 12, opacity 4, colour 12, slot 4); per pixel the rendered
-# colour and transmittance (16) and the observation (12); per (Gaussian, view) record its 7 accumulated
-# partial scores, written once (28)
+# Algorithmic HBM bytes of the replay: per (tile, Gaussian) pair it walks -- in each tile, the list entries up
+# to the deepest one any of the tile's pixels evaluates before it stops -- its sorted Gaussian id (4) and the
+# 40 B of the record it evaluates (centre 8, exponent factors 12, opacity 4, colour 12, slot 4); per pixel the
+# rendered colour and transmittance (16) and the observation (12); per (Gaussian, view) record its 7
+# accumulated partial scores, written once (28)
 REPLAY_BYTES_PAIR = 44
 REPLAY_BYTES_PIXEL = 28
 REPLAY_BYTES_RECORD = 28
@@ -257,6 +258,12 @@ def measure(config, args, dev, stream, steps, warmup, extras):
         stats = r.export(binding.GS_EXPORT_PIXEL_STATS).view(-1, 2).to(torch.int64)
         K = int(n.to(torch.int64).sum().item())
         E = int(stats[:, 0].sum().item())
+        E_cut = int(stats[:, 1].sum().item())
+        # pairs walked: per tile, the deepest list entry any of its pixels evaluates
+        V_, H_, W_ = sc.n_views, sc.height, sc.width
+        ev = stats[:, 0].view(V_, H_, W_)
+        ev = torch.nn.functional.pad(ev, (0, (-W_) % 16, 0, (-H_) % 16))
+        P_walk = int(ev.view(V_, ev.shape[1] // 16, 16, ev.shape[2] // 16, 16).amax(dim=(2, 4)).sum().item())
         P = int(r.n_pairs)
         finite = bool(torch.isfinite(tokens).all().item())
         rec = r.export(binding.GS_EXPORT_RECORDS)
@@ -284,7 +291,7 @@ def measure(config, args, dev, stream, steps, warmup, extras):
     t_rep = rep_ms * 1e-3
     ops = OPS_EVAL * E + OPS_CONTRIB_REPLAY * K
     achieved = ops / t_rep / 1e12
-    rep_bytes = REPLAY_BYTES_PAIR * P + REPLAY_BYTES_PIXEL * N_px + REPLAY_BYTES_RECORD * V * sc.n
+    rep_bytes = REPLAY_BYTES_PAIR * P_walk + REPLAY_BYTES_PIXEL * N_px + REPLAY_BYTES_RECORD * V * sc.n
     traffic = measured_traffic("k_replay", workload, args.antialiased)
     roofline = {"kernel": "k_replay", "bound": "alu", "achieved": round(achieved, 3),
                 "peak": round(ALU_PEAK_TOPS, 2), "unit": "T lane-ops/s (fp32 VALU)",
@@ -297,9 +304,12 @@ def measure(config, args, dev, stream, steps, warmup, extras):
                         "measured_gbs": None if traffic is None else round(traffic / t_rep / 1e9, 1),
                         "measured_frac": None if traffic is None else round(traffic / t_rep / 1e9 / HBM_PEAK_GBS, 4)}}
     t_ren = stages["render"][0] * 1e-3
-    ops_r = OPS_EVAL * E + OPS_CONTRIB_FWD * K
+    # the render skips, by its quadrant boxes, entries that fail the distance cut at every pixel of a quadrant,
+    # so its evaluations are counted as those inside the cut (the ones no exact culling can skip)
+    ops_r = OPS_EVAL * E_cut + OPS_CONTRIB_FWD * K
     secondary = {"k_render": {"bound": "alu", "achieved": round(ops_r / t_ren / 1e12, 3),
                               "frac": round(ops_r / t_ren / 1e12 / ALU_PEAK_TOPS, 4),
+                              "units": {"evaluations_in_cut": E_cut, "contributions": K},
                               "traffic": measured_traffic("k_render<false>", workload, args.antialiased),
                               "avg_launch_ms": round(stages["render"][0], 4)}}
     for st in ("project", "depth_sort", "emit", "tile_sort", "ranges"):
@@ -321,7 +331,9 @@ def measure(config, args, dev, stream, steps, warmup, extras):
                    "sh_degree": sc.sh_degree, "pairs": P, "parallelism": "none",
                    "mode": "antialiased" if args.antialiased else "plain"},
         "contribs_per_s": round(K / (elapsed / steps), 1),
-        "work_per_step": {"contributions": K, "evaluations": E, "pairs": P},
+        "work_per_step": {"contributions": K, "evaluations": E, "evaluations_in_cut": E_cut, "pairs": P,
+                          "pairs_walked": P_walk,
+                          "live_records": n_live},
         "stages_ms": {k: round(v[0], 4) for k, v in stages.items()},
         "score_overhead": round(score_ms / render_ms, 4),
         "roofline": roofline,

@@ -222,6 +222,65 @@ __device__ __forceinline__ uint32_t entry_box_pack(float s1f, float s2f, float s
     return half_bits_up((float)wx) | (half_bits_up((float)wy) << 16);
 }
 
+// Whether some point of the rectangle [x0, x1] x [y0, y1] (the tile-relative pixel-centre bounds of a
+// quadrant) can pass an entry's alpha test, decided in float32 with margins that make a false result safe.
+// The region that can pass is S*(p - m) <= t_eff (see above), S*(d) = (s1 dx + s2 dy)^2 + (s3 dy)^2 exact
+// on the float32 values.  The packed box bounds t_eff from above: its half-widths are at least
+// sqrt(t_eff Kinv_xx) and sqrt(t_eff Kinv_yy), so t_eff <= min(ex^2 / Kinv_xx, ey^2 / Kinv_yy) =
+// min(ex^2 s1^2 s3^2 / (s2^2 + s3^2), ey^2 s3^2), taken here with a relative 1e-4 and an absolute 1e-3 on
+// top (infinite half-widths: never skip; an empty box never reaches this test).  S* is convex with its
+// minimum 0 at m, so over a rectangle that does not hold m its minimum lies on an edge facing m (the
+// segment from m to any other point of the rectangle crosses such an edge first, where S* is no larger):
+// at most two edges, each a one-dimensional quadratic minimised at a clamped point.  That float32 minimum
+// is compared after subtracting 2^-16 of the sum of its terms' magnitudes, far above its rounding
+// (including the rounding of the edge offsets and of the minimiser, whose error moves a quadratic's value
+// at its minimum only to second order).  The minimum over the rectangle is no larger than over its pixel
+// centres, so a false result means no pixel of the quadrant passes.
+// (The reciprocals are the hardware approximation, within an ulp or two: the threshold's margin covers it,
+// and an approximate minimiser changes an edge quadratic's minimum only to second order.)
+struct EntryConic {
+    float a, b, c, ra, rc;  // S* = a dx^2 + 2 b dx dy + c dy^2, ra = 1/a, rc = 1/c
+    float te;               // the bound on t_eff (infinite: never skip)
+};
+
+__device__ __forceinline__ EntryConic entry_conic_from_box(float s1, float s2, float s3, uint32_t packed) {
+    EntryConic k;
+    k.a = s1 * s1;
+    k.b = s1 * s2;
+    const float p3 = s3 * s3;
+    k.c = s2 * s2 + p3;
+    k.ra = __builtin_amdgcn_rcpf(k.a);
+    k.rc = __builtin_amdgcn_rcpf(k.c);
+    const float ex = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed & 0xffffu));
+    const float ey = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed >> 16));
+    const float tx = ex * ex * k.a * p3 * k.rc, ty = ey * ey * p3;
+    const float t = tx < ty ? tx : ty;
+    k.te = (ex < __builtin_inff() && ey < __builtin_inff() && t == t) ? t * (1.0f + 1e-4f) + 1e-3f
+                                                                      : __builtin_inff();
+    return k;
+}
+
+__device__ __forceinline__ bool ellipse_meets_rect(float mx, float my, const EntryConic& k, float x0, float x1,
+                                                   float y0, float y1) {
+    if (!(k.te < __builtin_inff())) return true;
+    const float cx = fminf(fmaxf(mx, x0), x1), cy = fminf(fmaxf(my, y0), y1);
+    if (cx == mx && cy == my) return true;
+    bool meets = false;
+    if (cx != mx) {  // the vertical edge x = cx faces m
+        const float dx = cx - mx;
+        const float dy = fminf(fmaxf(-k.b * dx * k.rc, y0 - my), y1 - my);
+        const float t0 = k.a * dx * dx, t1 = 2.0f * k.b * dx * dy, t2 = k.c * dy * dy;
+        meets = meets || (t0 + t1) + t2 - 0x1p-16f * (t0 + fabsf(t1) + t2) <= k.te;
+    }
+    if (cy != my) {  // the horizontal edge y = cy faces m
+        const float dy = cy - my;
+        const float dx = fminf(fmaxf(-k.b * dy * k.ra, x0 - mx), x1 - mx);
+        const float t0 = k.a * dx * dx, t1 = 2.0f * k.b * dx * dy, t2 = k.c * dy * dy;
+        meets = meets || (t0 + t1) + t2 - 0x1p-16f * (t0 + fabsf(t1) + t2) <= k.te;
+    }
+    return meets;
+}
+
 // {x0, x1, y0, y1} of the packed box around the (tile-relative) centre (mx, my).
 __device__ __forceinline__ float4 entry_box_unpack(float mx, float my, uint32_t packed) {
     const float ex = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed & 0xffffu));

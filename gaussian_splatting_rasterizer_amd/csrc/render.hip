@@ -8,12 +8,13 @@
 // quadrant, so a wave's lanes stay spatially coherent and a wave whose 64
 // pixels are all saturated stops.  Batches of 256 list entries are gathered
 // (one per thread) into LDS -- centre relative to the tile, exponent factors,
-// opacity, clamped colour, and a conservative box of the pixels the entry can
-// reach, in half pixels packed into one word -- and each
-// wave compacts, in list order, the entries whose box meets its quadrant, then
-// walks only those with broadcast LDS reads.  The box is conservative for the
-// float32 evaluation, so the skipped entries are exactly ones every pixel of
-// the quadrant would have skipped.  Alpha decisions use the float32 canonical order and the
+// opacity, clamped colour -- and the gathering thread decides which quadrants
+// the entry can reach: its conservative box must meet the quadrant's pixel
+// centres, and so must the region of its ellipse where the float32 alpha test
+// can pass (its minimum over the quadrant's rectangle, with error margins).  Each wave compacts, in list order, the entries that can
+// reach its quadrant, then walks only those with broadcast LDS reads.  Both
+// tests are conservative for the float32 evaluation, so the skipped entries are
+// exactly ones every pixel of the quadrant would have skipped.  Alpha decisions use the float32 canonical order and the
 // specified exponential; the colour is accumulated with fused multiply-adds.
 // For every entry it processes, the render also leaves one byte whose bit w
 // says whether any pixel of wave w contributed or saturated there: the replay
@@ -29,17 +30,6 @@
 namespace gsr {
 
 constexpr int kRenderBatch = 256;
-
-// A tile-relative box {x0, x1, y0, y1} in half pixels, as four signed bytes ceil(2 x0), floor(2 x1),
-// ceil(2 y0), floor(2 y1) clamped to [-2, 40].  Pixel centres sit at odd half-pixel counts c, and for an
-// integer c, x0 <= c/2 exactly when ceil(2 x0) <= c and x1 >= c/2 exactly when floor(2 x1) >= c; the clamp
-// keeps every outcome against the tile's counts 1 .. 31.  So the byte test decides as the float box test.
-// (A NaN edge becomes -2: the entry is kept.)
-__device__ __forceinline__ uint32_t box_half_pixels(float4 b) {
-    const auto lo = [](float v) { return (uint32_t)(int)fminf(fmaxf(ceilf(2.0f * v), -2.0f), 40.0f) & 0xffu; };
-    const auto hi = [](float v) { return (uint32_t)(int)fminf(fmaxf(floorf(2.0f * v), -2.0f), 40.0f) & 0xffu; };
-    return lo(b.x) | (hi(b.y) << 8) | (lo(b.z) << 16) | (hi(b.w) << 24);
-}
 
 template <bool STATS>
 __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
@@ -61,7 +51,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     __shared__ float4 s0[kRenderBatch];   // {tile-relative centre (2), s1, s2}
     __shared__ float4 s1[kRenderBatch];   // {s3, opacity, colour r, colour g}
     __shared__ float4 s2[kRenderBatch];   // {colour b, unused}
-    __shared__ uint32_t sbox[kRenderBatch];  // conservative box of the pixels the entry can reach, in half pixels
+    __shared__ uint8_t squad[kRenderBatch];  // bit q: some pixel of quadrant q may pass the entry's alpha test
     __shared__ uint16_t slist[4][kRenderBatch];
     __shared__ uint8_t s_ev[4][kRenderBatch];  // per wave: some pixel contributed or saturated at the entry
     // the same per position of the wave's list (laid out like the list, so both share one address)
@@ -81,9 +71,6 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
     // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
     const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     // pixel-centre range of this wave's 8x8 quadrant, tile-relative
-    // (in half pixels: the centres 0.5 .. 7.5 of the first quadrant column are 1 .. 15)
-    const int qx0 = (wave & 1) * 16 + 1, qx1 = qx0 + 14;
-    const int qy0 = (wave >> 1) * 16 + 1, qy1 = qy0 + 14;
     const uint2 rg = ranges[tile];
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -117,7 +104,22 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
             s0[threadIdx.x] = make_float4(mxt, myt, a.z, a.w);
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
             s2[threadIdx.x] = make_float4(clamp_colour(c.x), 0.0f, 0.0f, 0.0f);
-            sbox[threadIdx.x] = box_half_pixels(entry_box_unpack(mxt, myt, __float_as_uint(c.y)));
+            if constexpr (!STATS) {
+                // the quadrants the entry can reach: its box first, then the exact test of its ellipse against
+                // the quadrant's pixel-centre rectangle (tile-relative)
+                const float4 bx = entry_box_unpack(mxt, myt, __float_as_uint(c.y));
+                const EntryConic kq = entry_conic_from_box(a.z, a.w, b.x, __float_as_uint(c.y));
+                uint32_t qm = 0u;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float x0 = (float)((q & 1) * 8) + 0.5f, x1 = x0 + 7.0f;
+                    const float y0 = (float)((q >> 1) * 8) + 0.5f, y1 = y0 + 7.0f;
+                    if (bx.x <= x1 && bx.y >= x0 && bx.z <= y1 && bx.w >= y0 &&
+                        ellipse_meets_rect(mxt, myt, kq, x0, x1, y0, y1))
+                        qm |= 1u << q;
+                }
+                squad[threadIdx.x] = (uint8_t)qm;
+            }
         }
         __syncthreads();
         const int cnt = (int)min((uint32_t)kRenderBatch, rg.y - base);
@@ -131,9 +133,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                     // the statistics pass evaluates every entry, so its distance-cut count is the plain
                     // algorithm's (the skipped entries fail the alpha test at every pixel of the quadrant, so
                     // the decisions are the same)
-                    const uint32_t bx = sbox[j];
-                    hit = STATS || ((int)(int8_t)bx <= qx1 && (int)(int8_t)(bx >> 8) >= qx0 &&
-                                    (int)(int8_t)(bx >> 16) <= qy1 && (int)(int8_t)(bx >> 24) >= qy0);
+                    hit = STATS || ((squad[j] >> wave) & 1u);
                 }
                 const uint64_t m = __ballot(hit);
                 if (hit) {
