@@ -125,6 +125,8 @@ struct gs_context {
     uint64_t* host_count_dev;     // its device address: the slot scan writes the count there itself
     bool packed_fresh;            // gs_project left the packed rectangles that the next depth sort reads
     bool order_valid;             // tile_order holds the order a render of this context measured
+    uint32_t scan_epoch;          // last single-pass scan tag; 0 = its tile words not cleared yet
+    uint32_t scan_ticket_base;    // scan tickets handed out since they were cleared
 };
 
 namespace gsr {
@@ -360,12 +362,15 @@ gs_status bin_sort_impl(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_o
     // the pinned word holds kCountPending until the slot scan writes the count into it
     if (!count_by_copy) *(volatile uint64_t*)ctx->host_count = kCountPending;
     const SortScratch sort_scratch{ws.lookback, ws.sort_ctl, ws.sort_part};
+    // (scan_total[3] holds the scans' ticket counter)
+    ScanState scan_state{ws.scan_blocks, s.scan_blocks_cap, reinterpret_cast<uint32_t*>(ws.scan_total + 3),
+                         &ctx->scan_epoch, &ctx->scan_ticket_base};
     // 0. slot bases of the replay's partials: tile counts scanned in record order
     tm.begin(GS_STAGE_DEPTH_SORT, stream);
     // the pair count is this scan's total (the same tile counts as the depth-ordered scan below): the scan
     // writes it into pinned host memory too, and the host waits for it only after the sort and the second scan
     // are queued, so that the GPU has work while the host waits
-    e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, ws.scan_blocks, ws.scan_total + 1, stream, false,
+    e = launch_scan_u32(ws.tiles_touched, s.VG, ws.slot_base, scan_state, ws.scan_total + 1, stream, false,
                         count_by_copy ? nullptr : ctx->host_count_dev);
     if (e != hipSuccess) return hip_fail(e, "slot scan");
     // 1. depth sort of the records (four 8-bit passes; keys ping-pong through offsets, which the
@@ -385,7 +390,7 @@ gs_status bin_sort_impl(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_o
     tm.end(GS_STAGE_DEPTH_SORT, stream);
     // 2. pair offsets in depth order
     tm.begin(GS_STAGE_SCAN, stream);
-    e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, ws.scan_blocks, ws.scan_total, stream, packable);
+    e = launch_scan_u32(ws.tt_sorted, s.VG, ws.offsets, scan_state, ws.scan_total, stream, packable);
     if (e != hipSuccess) return hip_fail(e, "scan");
     tm.end(GS_STAGE_SCAN, stream);
     uint64_t total = 0;
@@ -424,12 +429,16 @@ gs_status bin_sort_impl(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_o
     // when a tile id and a Gaussian index fit one 32-bit word together, the pairs are sorted as such words
     const int gbits = bits_for((uint64_t)s.G) > 0 ? bits_for((uint64_t)s.G) : 1;
     const int packed_gbits = td.bits + gbits <= 32 ? gbits : 0;
-    // the ranges start as {~0u, 0}: a tile the last pass never sees keeps start > end, an empty range for
-    // every traversal (they loop while start < end; the ranges export turns it into {0, 0})
-    tm.begin(GS_STAGE_RANGES, stream);
-    e = launch_ranges_init(ws.ranges, tiles, ws.sort_part, stream);
-    if (e != hipSuccess) return hip_fail(e, "ranges init");
-    tm.end(GS_STAGE_RANGES, stream);
+    // the ranges start as {~0u, 0} (set by the emission, or here when there is no record to emit): a tile the
+    // last pass never sees keeps start > end, an empty range for every traversal (they loop while start < end;
+    // the ranges export turns it into {0, 0}).  The depth sort left the histogram rows the emission adds the
+    // tile sort's digit counts into at zero.
+    if (s.VG == 0) {
+        tm.begin(GS_STAGE_RANGES, stream);
+        e = launch_ranges_init(ws.ranges, tiles, nullptr, stream);
+        if (e != hipSuccess) return hip_fail(e, "ranges init");
+        tm.end(GS_STAGE_RANGES, stream);
+    }
     tm.begin(GS_STAGE_EMIT, stream);
     e = launch_emit(s, ws, rid_sorted, &td, packed_gbits, packable, stream);
     if (e != hipSuccess) return hip_fail(e, "emit");

@@ -106,6 +106,8 @@ __device__ __forceinline__ uint32_t scan_item(uint32_t x, bool packed_rect) {
     return x == 0xffffffffu ? 0u : (((x >> 16) & 0xffu) + 1u) * ((x >> 24) + 1u);
 }
 
+// Two-kernel exclusive scan for large inputs: per-block totals, then each block's offset from the totals
+// before it and the block's own scan.
 __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t* __restrict__ in, int64_t n,
                                                               uint64_t* __restrict__ bsum, bool packed_rect) {
     __shared__ uint64_t lds[kScanThreads / 64];
@@ -171,22 +173,139 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(const uint32_t* in, 
     }
 }
 
+// Single-pass exclusive scan.  Blocks take 4096-item tiles in the order they
+// start (a ticket counter that only grows: this launch's tickets start at
+// ticket_base), load their tile into LDS and publish its total; then every
+// thread of the block waits for and adds a strided share of the totals of all
+// earlier tiles (at most a few thousand words, up to 8 per thread in flight at
+// once), so a block's offset takes one round of loads whatever its position.
+// A tile waits only on tiles that started before it, and every tile publishes
+// its total before it waits, so the waits always end.  A word is
+// tag << 48 | value (48 bits, saturating: the pair count of any workspace fits
+// far below, and a saturated total only fails the capacity check, never a
+// tag).  `in` and `out` may alias (each block reads its whole slice before
+// writing it).  The last tile writes the grand total (and to pinned host
+// memory when host_total is given).
+constexpr uint64_t kScanValueMask = (1ull << 48) - 1ull;
+constexpr int64_t kScanOnePassTiles = 512;  // the single pass for up to 2M items
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_onepass(const uint32_t* in, int64_t n, uint32_t* out,
+                                                               uint64_t* __restrict__ flags, uint32_t* ticket,
+                                                               uint32_t ticket_base, uint32_t tag, int64_t nb,
+                                                               uint64_t* __restrict__ total, bool packed_rect,
+                                                               uint64_t* host_total) {
+    // padded so that thread t's 16 consecutive items (t*17 + i) are bank-conflict free
+    __shared__ uint32_t s[kScanTile + kScanTile / 16];
+    __shared__ uint32_t lds[kScanThreads / 64];
+    __shared__ uint64_t lds64[kScanThreads / 64];
+    __shared__ uint32_t s_tile;
+    __shared__ uint64_t s_excl;
+    if (threadIdx.x == 0) s_tile = atomicAdd(ticket, 1u) - ticket_base;
+    __syncthreads();
+    const int64_t tile = s_tile;
+    const int64_t base = tile * kScanTile;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int e = i * kScanThreads + threadIdx.x;
+        const int64_t k = base + e;
+        s[e + e / 16] = k < n ? scan_item(in[k], packed_rect) : 0u;
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) local += s[t * 17 + i];
+    uint64_t btot;
+    (void)block_exclusive_scan<uint64_t, kScanThreads>((uint64_t)local, &btot, lds64);
+    btot = btot < kScanValueMask ? btot : kScanValueMask;
+    const uint64_t agg_tag = (uint64_t)tag << 48;
+    if (threadIdx.x == 0)
+        __hip_atomic_store(flags + tile, agg_tag | btot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the totals of every earlier tile
+    constexpr int kLB = 8;
+    uint64_t acc = 0;
+    for (int64_t k0 = 0; k0 < tile; k0 += (int64_t)kScanThreads * kLB) {
+        uint64_t w[kLB];
+#pragma unroll
+        for (int u = 0; u < kLB; ++u) {
+            const int64_t k = k0 + u * kScanThreads + threadIdx.x;
+            w[u] = k < tile ? __hip_atomic_load(flags + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : agg_tag;
+        }
+#pragma unroll
+        for (int u = 0; u < kLB; ++u) {
+            const int64_t k = k0 + u * kScanThreads + threadIdx.x;
+            while ((w[u] & ~kScanValueMask) != agg_tag) {  // not published yet (a word past tile is agg_tag | 0)
+                __builtin_amdgcn_s_sleep(1);
+                w[u] = __hip_atomic_load(flags + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            acc += w[u] & kScanValueMask;
+        }
+    }
+    uint64_t excl;
+    (void)block_exclusive_scan<uint64_t, kScanThreads>(acc, &excl, lds64);
+    excl = excl < kScanValueMask ? excl : kScanValueMask;
+    if (threadIdx.x == 0) {
+        s_excl = excl;
+        if (tile == nb - 1) {
+            const uint64_t inc = excl + btot < kScanValueMask ? excl + btot : kScanValueMask;
+            *total = inc;
+            if (host_total) __hip_atomic_store(host_total, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+    __syncthreads();
+    const uint64_t boff = s_excl;
+    uint32_t tot;
+    uint32_t run = (uint32_t)boff + block_exclusive_scan<uint32_t, kScanThreads>(local, &tot, lds);
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const uint32_t v = s[t * 17 + i];
+        s[t * 17 + i] = run;
+        run += v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        const int e = i * kScanThreads + threadIdx.x;
+        const int64_t k = base + e;
+        if (k < n) out[k] = s[e + e / 16];
+    }
+}
+
 __global__ void k_zero_u64(uint64_t* __restrict__ p, uint64_t* host_p) {
     *p = 0ull;
     if (host_p) __hip_atomic_store(host_p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
+hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, ScanState& ss, uint64_t* total,
                            hipStream_t st, bool packed_rect_in, uint64_t* host_total) {
     const int64_t nb = (n + kScanTile - 1) / kScanTile;
     if (nb == 0) {
         hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, st, total, host_total);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch,
-                       packed_rect_in);
-    hipLaunchKernelGGL(k_scan_down, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, block_scratch, nb, out,
-                       total, packed_rect_in, host_total);
+    if (nb > kScanOnePassTiles) {
+        // many tiles: the single pass's ticket and waits cost more than a second launch (measured)
+        hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, ss.flags,
+                           packed_rect_in);
+        hipLaunchKernelGGL(k_scan_down, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, ss.flags, nb, out,
+                           total, packed_rect_in, host_total);
+        // the block totals overwrote the tagged words: clear them before the next single pass
+        *ss.epoch = 0;
+        return hipGetLastError();
+    }
+    // the tile words and the ticket are cleared on first use and before the tag or the ticket could wrap
+    if (*ss.epoch == 0 || *ss.epoch >= kScanEpochLimit || *ss.ticket_base > 0xc0000000u) {
+        hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(ss.flags), 2 * ss.flags_cap, 0u, st);
+        if (e == hipSuccess) e = launch_fill_u32(ss.ticket, 1, 0u, st);
+        if (e != hipSuccess) return e;
+        *ss.epoch = 0;
+        *ss.ticket_base = 0;
+    }
+    const uint32_t tag = ++*ss.epoch;
+    const uint32_t tb = *ss.ticket_base;
+    *ss.ticket_base += (uint32_t)nb;
+    hipLaunchKernelGGL(k_scan_onepass, dim3((unsigned)nb), dim3(kScanThreads), 0, st, in, n, out, ss.flags, ss.ticket,
+                       tb, tag, nb, total, packed_rect_in, host_total);
     return hipGetLastError();
 }
 
@@ -274,9 +393,11 @@ __global__ __launch_bounds__(kHistThreads) void k_digit_hist(const uint32_t* __r
 
 // Totals of the per-block histograms: block b sums bins [64 b, 64 b + 64) of
 // the pass-major table, its 16 waves over 16 histogram blocks each with every
-// load in flight at once; block 0 also zeroes the passes' tile tickets.
-__global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restrict__ part, int nblocks,
-                                                       uint32_t* __restrict__ ctl) {
+// load in flight at once; block 0 also zeroes the passes' tile tickets.  With
+// zero_rows it then clears its bins in all kHistMaxBlocks rows, which leaves
+// the table zero for the next producer that adds into it (the pair emission).
+__global__ __launch_bounds__(1024) void k_digit_totals(uint32_t* __restrict__ part, int nblocks,
+                                                       uint32_t* __restrict__ ctl, bool zero_rows) {
     static_assert(kHistMaxBlocks <= 16 * 16, "one load per wave and row");
     __shared__ uint32_t s[16][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -290,6 +411,10 @@ __global__ __launch_bounds__(1024) void k_digit_totals(const uint32_t* __restric
     uint32_t acc = 0u;
 #pragma unroll
     for (int u = 0; u < 16; ++u) acc += x[u];
+    if (zero_rows) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) part[(int64_t)(wave * 16 + u) * (kMaxPasses * kMaxBins) + bin] = 0u;
+    }
     s[wave][lane] = acc;
     __syncthreads();
     if (wave == 0) {
@@ -562,8 +687,9 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
         case 3: hipLaunchKernelGGL(k_digit_hist<3>, dim3((unsigned)hb), dim3(kHistThreads), 0, st, keys_in, n, dbits, bits, sc.part); break;
         default: hipLaunchKernelGGL(k_digit_hist<4>, dim3((unsigned)hb), dim3(kHistThreads), 0, st, keys_in, n, dbits, bits, sc.part); break;
     }
+    // a sort that counted its own digits leaves the histogram table zero for the pair emission
     hipLaunchKernelGGL(k_digit_totals, dim3((unsigned)(passes * kMaxBins / 64)), dim3(1024), 0, st, sc.part, (int)hb,
-                       sc.ctl);
+                       sc.ctl, !hist_ready);
     const uint32_t* ksrc = keys_in;
     const uint32_t* vsrc = vals_in;
     for (int p = 0; p < passes; ++p) {
@@ -653,7 +779,11 @@ __global__ __launch_bounds__(256) void k_emit(const uint32_t* __restrict__ rid_s
                                               const uint32_t* __restrict__ tt_sorted,
                                               const uint32_t* __restrict__ offsets, int64_t VG, uint32_t G, int T,
                                               int TX, uint32_t* __restrict__ pkey, uint32_t* __restrict__ pair_g,
-                                              RadixDigits rd, int packed_gbits, uint32_t* __restrict__ part) {
+                                              RadixDigits rd, int packed_gbits, uint32_t* __restrict__ part,
+                                              uint2* __restrict__ ranges, int64_t n_tiles) {
+    // the tile ranges start as {~0u, 0} (a grid-stride share per block): the tile sort's last pass records them
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_tiles; i += (int64_t)gridDim.x * 256)
+        ranges[i] = make_uint2(0xffffffffu, 0u);
     __shared__ uint32_t s_off[kEmitRecs];
     __shared__ uint32_t s_g[kEmitRecs];     // Gaussian index
     __shared__ uint32_t s_key0[kEmitRecs];  // global tile id of the rectangle's first tile
@@ -741,7 +871,8 @@ hipError_t launch_emit(const Sizes& s, Workspace& ws, const uint32_t* rid_sorted
 #define GSR_EMIT(PP)                                                                                              \
     hipLaunchKernelGGL(k_emit<PP>, grid, block, 0, st, rid_sorted, rects_packed ? nullptr : ws.rect_sorted,      \
                        ws.tt_sorted, ws.offsets, s.VG,                                                           \
-                       (uint32_t)s.G, s.T, s.TX, ws.pkey_emit, ws.pair_g, d, packed_gbits, ws.sort_part)
+                       (uint32_t)s.G, s.T, s.TX, ws.pkey_emit, ws.pair_g, d, packed_gbits, ws.sort_part, ws.ranges, \
+                       (int64_t)s.V * s.T)
     switch (rd ? rd->passes : 0) {
         case 0: GSR_EMIT(0); break;
         case 1: GSR_EMIT(1); break;

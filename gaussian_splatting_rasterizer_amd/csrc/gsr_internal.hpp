@@ -30,8 +30,8 @@ struct Workspace {
     uint32_t* pay_a;       // packed rectangles carried through the depth sort (ping-pong)
     uint32_t* pay_b;
     // scan / histogram scratch
-    uint64_t* scan_blocks; // per-block sums (u64), then exclusive offsets
-    uint64_t* scan_total;  // [0] pair count, [1] slot total, [2] scratch of the radix scans
+    uint64_t* scan_blocks; // single-pass scan: one tagged word per 4096-item tile
+    uint64_t* scan_total;  // [0] pair count, [1] slot total, [3] the scans' ticket counter (low word)
     uint64_t* lookback;    // radix look-back words, [radix tile][256 digits]
     uint32_t* sort_ctl;    // radix control: per-pass tile tickets, then per-pass digit offsets
     uint32_t* sort_part;   // per-block digit histograms of the radix sorts
@@ -94,10 +94,20 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s
 // pay_init (optional): also the packed rectangles (pack_rect) per record, for the depth sort's first pass
 hipError_t launch_project(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, float near_plane,
                           float far_plane, int antialiased, uint32_t* pay_init, Workspace& ws, hipStream_t st);
+// State of the single-pass scans of a context: one tagged word per 4096-item tile (flags_cap words), a ticket
+// counter that only grows, the last tag and the tickets handed out since the last clear (host side).
+struct ScanState {
+    uint64_t* flags;
+    int64_t flags_cap;
+    uint32_t* ticket;
+    uint32_t* epoch;
+    uint32_t* ticket_base;
+};
+constexpr uint32_t kScanEpochLimit = 0x7ff0u;  // tags fit 15 bits
 // exclusive scan of in (u32) into out (may alias); total -> *total (device u64).  With packed_rect_in the
 // items are packed rectangles (pack_rect) and their tile counts are scanned.
 // host_total (optional): a device address of pinned host memory that receives the total as well.
-hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, uint64_t* block_scratch, uint64_t* total,
+hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, ScanState& ss, uint64_t* total,
                            hipStream_t st, bool packed_rect_in = false, uint64_t* host_total = nullptr);
 // Tile rectangles that a record sort moves into sorted order with the values:
 // rect[val] becomes rect_out[pos] with its tile count tt_out[pos].  With

@@ -322,7 +322,7 @@ typedef enum {
     GS_STAGE_SCAN = 2,
     GS_STAGE_EMIT = 3,
     GS_STAGE_TILE_SORT = 4,
-    GS_STAGE_RANGES = 5,
+    GS_STAGE_RANGES = 5,             /* tile ranges set on their own: only without records (else the pair emission sets them) */
     GS_STAGE_RENDER = 6,
     GS_STAGE_REPLAY = 7,
     GS_STAGE_FINALIZE = 8,

@@ -265,8 +265,9 @@ def test_profile_stage_mask():
         r.step(obs)
         torch.cuda.synchronize()
         prof = binding.gs_profile_read(r.ctx)
-        step_stages = ("project", "depth_sort", "scan", "emit", "tile_sort", "ranges", "render", "replay", "finalize")
+        step_stages = ("project", "depth_sort", "scan", "emit", "tile_sort", "render", "replay", "finalize")
         assert all(prof[k][1] == 1 for k in step_stages), prof
+        assert prof["ranges"][1] == 0, prof  # the emission sets the ranges: no launch of its own
         binding.gs_profile_enable(r.ctx, False)
         r.step(obs)
         torch.cuda.synchronize()
