@@ -138,24 +138,45 @@ GSR_API gs_status gs_context_create(const gs_dims* dims, void* workspace, size_t
                             gs_context** out);
 GSR_API gs_status gs_context_destroy(gs_context* ctx);
 
-/* Preprocess every (Gaussian, view): EWA projection of the 3D covariance to
- * the image (+0.3 px^2 dilation), inverse 2D covariance, 3-sigma radius and
- * tile rectangle, depth, SH colour along the view direction (+0.5, clamped at
- * 0, clamp state kept for the SH score).  `cams` is a host array [n_views].
- * Asynchronous on `stream`. */
+/* Preprocess every (Gaussian, view).  Follows the page "Research Proposal:
+ * Renderer Score Tokens for Recurrent Gaussian Splatting", Two-Stage Algorithm,
+ * Stage 1 (Standard Render: project the Gaussians, evaluate their colours),
+ * with the projection conventions of the ATSplat summary page (section
+ * 前置知识: EWA covariance projection, SH colour): EWA projection of the 3D
+ * covariance to the image (+0.3 px^2 dilation), inverse 2D covariance as
+ * exponent factors, 3-sigma radius and tile rectangle, depth, SH colour along
+ * the view direction (+0.5, clamped at 0, clamp state kept for the SH score).
+ *   scene   device arrays of scene->n Gaussians (layouts in gs_gaussians), read
+ *           only; they must stay valid until the last call that reads them
+ *           (gs_score_replay and gs_backward read means and opacities again)
+ *   cams    host array [n_views], copied into the context
+ *   params  host struct, copied (gs_default_params gives the defaults)
+ * Asynchronous on `stream`.  Errors: GS_ERR_INVALID_ARGUMENT (null or
+ * misaligned pointers, n or sh_degree not those of the context, invalid params,
+ * a camera whose focal lengths are not > 0 -- then nothing in the context
+ * changes); GS_ERR_HIP on a launch failure. */
 GSR_API gs_status gs_project(gs_context* ctx, const gs_gaussians* scene, const gs_camera* cams,
                      const gs_params* params, hipStream_t stream);
 
-/* Tile binning and contributor sorting: order (Gaussian, view) records by
- * depth, emit one (tile, Gaussian) pair per covered tile, stable-sort the pairs
- * by tile and build per-tile ranges.  Blocks the host once to read the pair
- * count (through a pinned host word the context allocates on its first call;
- * written to *n_pairs_out, which may be null).  Returns
- * GS_ERR_WORKSPACE_TOO_SMALL (with the count) when it exceeds max_pairs; the
- * caller then creates a larger context and starts again from gs_project. */
+/* Tile binning and contributor sorting.  Follows the Proposal page's
+ * Two-Stage Algorithm, Stage 1 (tile binning and per-tile depth order of the
+ * standard render, which the score replay re-traverses unchanged): order the
+ * (Gaussian, view) records by depth, emit one (tile, Gaussian) pair per
+ * covered tile, stable-sort the pairs by tile and build per-tile ranges; the
+ * lists and ranges stay in the workspace.  Waits on the host for the pair
+ * count (polling a pinned host word the context allocates on its first call,
+ * while the GPU sorts; written to *n_pairs_out, which may be null).  Errors:
+ * GS_ERR_STATE before gs_project; GS_ERR_WORKSPACE_TOO_SMALL (with the count)
+ * when it exceeds max_pairs -- the caller then creates a larger context and
+ * starts again from gs_project; GS_ERR_HIP on a launch or stream failure. */
 GSR_API gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_out);
 
-/* Front-to-back compositing per 16x16 tile.  Outputs (any may be null):
+/* Front-to-back compositing per 16x16 tile.  Follows the Proposal page's
+ * Two-Stage Algorithm, Stage 1 (Standard Render: rendered colour, final
+ * transmittance and contributor count per pixel), with the alpha rules of its
+ * Exact Score Operators section (alpha = o G clamped at 0.99, contributions
+ * below 1/255 skipped, a pixel stops before its transmittance falls below
+ * 1e-4).  Outputs are caller-owned device arrays (any may be null):
  *   color      [n_views, height, width, 3] rendered colour incl. background
  *   T_final    [n_views, height, width]    final transmittance
  *   n_contrib  [n_views, height, width]    accepted contributions (int32)
@@ -167,18 +188,28 @@ GSR_API gs_status gs_bin_sort(gs_context* ctx, hipStream_t stream, uint64_t* n_p
  * take the tiles longest first; the next gs_render on the same context starts
  * from that order too (the first takes the tiles in index order).  The order
  * changes only how the work packs onto the GPU: every tile is fully computed
- * and all outputs are identical whatever the order. */
+ * and all outputs are identical whatever the order.  Errors: GS_ERR_STATE
+ * before gs_bin_sort; GS_ERR_INVALID_ARGUMENT for a misaligned output;
+ * GS_ERR_HIP on a launch failure. */
 GSR_API gs_status gs_render(gs_context* ctx, float* color, float* T_final, int32_t* n_contrib,
                     hipStream_t stream);
 
-/* Analytic score replay against `observed` [n_views, height, width, 3]: the
- * residual r = C_hat - C, the suffix C+ = (C_hat - P - T alpha c) /
+/* Analytic score replay.  Follows the Proposal page's Two-Stage Algorithm,
+ * Stage 2 (Analytic Score Replay: re-traverse the same lists, residual, prefix
+ * and suffix composites, masks), its Exact Score Operators (the mean, opacity
+ * and SH scores, the cross-view weights and the conditioning matrix) and its
+ * Final Token section.  `observed` is a caller-owned device array
+ * [n_views, height, width, 3] (float32); `tokens` a caller-owned device array
+ * [n, 9 + 3 d] (may be null only when n = 0).  Computes the residual
+ * r = C_hat - C, the suffix C+ = (C_hat - P - T alpha c) /
  * (T (1 - alpha) + eps), masked per-Gaussian partial scores, cross-view
  * aggregation and the token
  *   tokens [n, 9 + 3 d] = [ b_mu (3), s_alpha (1), s_SH (3 d, index k*3 + channel),
  *                           log Q (1), eig(A) / (tr A + eps) (3, descending),
  *                           log(tr A + eps) (1) ]
  * with Q = eps + sum_v q_gv the cross-view support. */
+/* Errors: GS_ERR_STATE before gs_render; GS_ERR_INVALID_ARGUMENT for null or
+ * misaligned arrays; GS_ERR_HIP on a launch failure. */
 GSR_API gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens, hipStream_t stream);
 
 /* The whole path -- gs_project, gs_bin_sort, gs_render, gs_score_replay --
