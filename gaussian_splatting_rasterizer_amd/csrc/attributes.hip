@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
                 const bool sat = pass && tT < kTMin;
-                const bool contrib = pass && !sat;
+                const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 done = done || sat;
                 const float w = contrib ? alpha * Tr : 0.0f;
 #pragma unroll
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
                 const bool sat = pass && tT < kTMin;
-                const bool contrib = pass && !sat;
+                const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 done = done || sat;
                 {  // every listed entry has a contribution or saturation in some lane of the wave
                     const float w = contrib ? alpha * Tr : 0.0f;
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
                 const bool sat = pass && tT < kTMin;
-                const bool contrib = pass && !sat;
+                const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 done = done || sat;
                 if (contrib && alpha * Tr > tw[K - 1]) {
                     float cw = alpha * Tr;

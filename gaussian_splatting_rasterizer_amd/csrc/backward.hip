@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
                 const bool sat = pass && tT < kTMin;
-                const bool contrib = pass && !sat;
+                const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 done = done || sat;
                 {  // every listed entry has a contribution or saturation in some lane of the wave
                     const float cr = b.z, cg = b.w, cbl = s2[j];

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
                 const bool sat = pass && tT < kTMin;
-                const bool contrib = pass && !sat;
+                const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 if constexpr (STATS) {
                     n_near += near ? 1u : 0u;
                     if (sat) stop = base + off / (uint32_t)sizeof(float4);

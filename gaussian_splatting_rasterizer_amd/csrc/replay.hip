@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 const bool pass = near && alpha >= kAlphaMin;
                 const float tT = Tr * (1.0f - alpha);
                 const bool sat = pass && tT < kTMin;
-                const bool contrib = pass && !sat;
+                const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 done = done || sat;
                 // some lane of the wave contributes or saturates at every listed entry (a wave's list ends
                 // at its last such entry), so the partials are formed without testing for a contribution
