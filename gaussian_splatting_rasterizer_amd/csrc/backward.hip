@@ -10,8 +10,9 @@
 // colour clamp, field-of-view clamp).
 //
 // k_backward: the same tiles, lists, order and decisions as the render, and
-// the same traversal as the score replay (event entries only, the suffix
-// tracked as the rendered colour minus the prefix).  With g = dL/dC_hat and, for each
+// the same traversal as the score replay (event entries only; the suffix
+// enters only through <g, S>, so each pixel carries that scalar, <g, C_hat - P>,
+// and takes w <g, c> off it per contribution).  With g = dL/dC_hat and, for each
 // contribution,
 //     S = C_hat - P - T alpha c          (everything composited behind it, background included)
 //     dL/dalpha = T <g, c> - <g, S> / (1 - alpha)
@@ -49,7 +50,8 @@
 
 namespace gsr {
 
-constexpr int kBwdBatch = 128;
+// Entries staged per batch: 96 keeps the block's LDS near 25 KB (six blocks per CU).
+constexpr int kBwdBatch = 96;
 
 __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ ranges,
                                                   const uint32_t* __restrict__ sorted_g,
@@ -62,13 +64,15 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                                                   const uint8_t* __restrict__ events, float4* __restrict__ partials,
                                                   uint32_t* __restrict__ slot_bits,
                                                   const uint32_t* __restrict__ tile_order) {
-    __shared__ float4 s0[kBwdBatch];
-    __shared__ float4 s1[kBwdBatch];
-    __shared__ float s2[kBwdBatch];
+    // an entry's three staged vectors sit at the same byte offset of three arrays, so one offset (16 j,
+    // kept in the wave's list) addresses all of them
+    __shared__ float4 s0[kBwdBatch];  // {tile-relative centre (2), s1, s2}
+    __shared__ float4 s1[kBwdBatch];  // {s3, opacity, colour r, colour g}
+    __shared__ float4 s2[kBwdBatch];  // {colour b, unused}
     __shared__ uint8_t s_evb[kBwdBatch];    // event bits of each staged entry (bit w: wave w)
     __shared__ uint32_t s_slot[kBwdBatch];  // partial slot of each staged pair
     __shared__ uint8_t s_mask[kBwdBatch];   // colour clamp mask bits (pre-clamp colour finite and >= 0), r g b
-    __shared__ uint8_t slist[4][kBwdBatch];
+    __shared__ uint32_t slist[4][kBwdBatch];
     __shared__ __align__(16) float sp[4][kBwdBatch][12];
 
     const int tile = (int)tile_order[blockIdx.x];
@@ -98,8 +102,8 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
         g2 = grad_color[3 * pix + 2];
     }
     float Tr = 1.0f;
-    // the suffix composite times the transmittance in front of it: C_hat minus the prefix colour
-    float S0 = Ch0, S1 = Ch1, S2 = Ch2;
+    // <g, S> with S the suffix composite times the transmittance in front of it (C_hat minus the prefix colour)
+    float qg = __builtin_fmaf(g2, Ch2, __builtin_fmaf(g1, Ch1, g0 * Ch0));
     bool done = !inside;
 
     for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
@@ -113,14 +117,14 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
             const uint2 rc = rect[rid];
             s0[threadIdx.x] = make_float4(tile_centre(a.x, c.z, tx), tile_centre(a.y, c.w, ty), a.z, a.w);
             s1[threadIdx.x] = make_float4(b.x, b.y, clamp_colour(b.z), clamp_colour(b.w));
-            s2[threadIdx.x] = clamp_colour(c.x);
+            s2[threadIdx.x] = make_float4(clamp_colour(c.x), 0.0f, 0.0f, 0.0f);
             s_evb[threadIdx.x] = events[i];
             const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16, wx = (rc.y & 0xffffu) - x0;
             s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
             s_mask[threadIdx.x] = (uint8_t)((colour_ok(b.z) ? 1u : 0u) | (colour_ok(b.w) ? 2u : 0u) | (colour_ok(c.x) ? 4u : 0u));
         }
         const int cnt = (int)min((uint32_t)kBwdBatch, rg.y - base);
-        for (int e = lane; e < cnt * 12; e += 64) (&sp[wave][0][0])[e] = 0.0f;
+        // (a wave writes the partial row of every entry it walks; the flush reads only those rows)
         __syncthreads();
         if (__ballot(!done) != 0ull) {
             int nw = 0;
@@ -128,16 +132,17 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                 const int j = c + lane;
                 const bool hit = j < cnt && ((s_evb[j] >> wave) & 1u);
                 const uint64_t m = __ballot(hit);
-                if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint8_t)j;
+                if (hit) slist[wave][nw + __popcll(m & lt_mask)] = (uint32_t)(j * sizeof(float4));
                 nw += __popcll(m);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             for (int k = 0; k < nw; ++k) {
-                const int j = slist[wave][k];
-                const float4 a = s0[j];
-                const float4 b = s1[j];
+                const uint32_t off = slist[wave][k];  // 16 j
+                const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s0) + off);
+                const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s1) + off);
+                const float cbl = reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s2) + off)->x;
                 const float dx = px - a.x, dy = py - a.y;
                 const float S = quad_S(a.z, a.w, b.x, dx, dy);
                 const bool near = !done && S <= kSCutoff;
@@ -150,14 +155,12 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                 const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 done = done || sat;
                 {  // every listed entry has a contribution or saturation in some lane of the wave
-                    const float cr = b.z, cg = b.w, cbl = s2[j];
+                    const float cr = b.z, cg = b.w;
                     const float w = contrib ? alpha * Tr : 0.0f;
-                    // the suffix behind this entry: C_hat minus the prefix including it
-                    S0 = __builtin_fmaf(-cr, w, S0);
-                    S1 = __builtin_fmaf(-cg, w, S1);
-                    S2 = __builtin_fmaf(-cbl, w, S2);
                     const float gc = __builtin_fmaf(g2, cbl, __builtin_fmaf(g1, cg, g0 * cr));
-                    const float gS = __builtin_fmaf(g2, S2, __builtin_fmaf(g1, S1, g0 * S0));
+                    // <g, S> behind this entry: the prefix now includes it (lanes without a contribution subtract 0)
+                    qg = __builtin_fmaf(-w, gc, qg);
+                    const float gS = qg;
                     // u = alpha (T <g, c> - <g, S> / (1 - alpha)) = w <g, c> - alpha <g, S> / (1 - alpha)
                     const float u = (contrib && !clamped)
                                         ? __builtin_fmaf(-alpha * gS, __builtin_amdgcn_rcpf(1.0f - alpha), w * gc)
@@ -166,8 +169,10 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                     const float x[8] = {u, ux, uy, ux * dx, ux * dy, uy * dy, w * g0, w * g1};
                     const float red = wave_reduce8(x, lane);
                     const float red8 = wave_sum1(w * g2);
-                    if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
-                    if (lane == 0) sp[wave][j][8] = red8;
+                    // every lane of a group of eight holds its component's sum: all store (the same value to the
+                    // same word); sp[wave][j] rows are 48 bytes, 3 off
+                    *reinterpret_cast<float*>(reinterpret_cast<char*>(&sp[wave][0][0]) + 3 * off + 4 * (lane >> 3)) = red;
+                    if (lane == 0) *reinterpret_cast<float*>(reinterpret_cast<char*>(&sp[wave][0][0]) + 3 * off + 32) = red8;
                     Tr = contrib ? tT : Tr;
                 }
             }
@@ -176,10 +181,13 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
         // one 48-byte partial per entry at which some wave had an event, flagged in the slot bits
         for (int idx = threadIdx.x; idx < 3 * cnt; idx += 256) {
             const int j = idx / 3, h = idx - 3 * j;
-            if (s_evb[j] == 0) continue;
-            float4 acc = *reinterpret_cast<const float4*>(&sp[0][j][4 * h]);
+            const uint32_t evb = s_evb[j];
+            if (evb == 0) continue;
+            // the rows of the waves that walked the entry (every other wave's share is zero)
+            float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-            for (int w = 1; w < 4; ++w) {
+            for (int w = 0; w < 4; ++w) {
+                if (!((evb >> w) & 1u)) continue;
                 const float4 q = *reinterpret_cast<const float4*>(&sp[w][j][4 * h]);
                 acc.x += q.x;
                 acc.y += q.y;
@@ -190,8 +198,8 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
             if (h == 1) {
                 acc.z = (m & 1u) ? acc.z : 0.0f;
                 acc.w = (m & 2u) ? acc.w : 0.0f;
-            } else if (h == 2) {
-                acc.x = (m & 4u) ? acc.x : 0.0f;
+            } else if (h == 2) {  // components 9-11 of a row are never written
+                acc = make_float4((m & 4u) ? acc.x : 0.0f, 0.0f, 0.0f, 0.0f);
             }
             const uint32_t slot = s_slot[j];
             partials[3 * (int64_t)slot + h] = acc;

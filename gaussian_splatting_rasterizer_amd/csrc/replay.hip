@@ -123,8 +123,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             s_mask[threadIdx.x] = (uint8_t)((colour_ok(b.z) ? 1u : 0u) | (colour_ok(b.w) ? 2u : 0u) | (colour_ok(c.x) ? 4u : 0u));
         }
         const int cnt = (int)min((uint32_t)kReplayBatch, rg.y - base);
-        // this wave's partial rows start at zero; entries it contributes to overwrite theirs
-        for (int e = lane; e < cnt * 8; e += 64) (&sp[wave][0][0])[e] = 0.0f;
+        // (a wave writes the partial row of every entry it walks; the flush reads only those rows)
         __syncthreads();
         if (__ballot(!done) != 0ull) {
             int nw = 0;
@@ -185,9 +184,12 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
         // flagged in the slot bits for the gather
         if (threadIdx.x < 2 * cnt && s_evb[threadIdx.x >> 1] != 0) {
             const int j = threadIdx.x >> 1, h = threadIdx.x & 1;
-            float4 acc = *reinterpret_cast<const float4*>(&sp[0][j][4 * h]);
+            const uint32_t evb = s_evb[j];
+            // the rows of the waves that walked the entry (every other wave's share is zero)
+            float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-            for (int w = 1; w < 4; ++w) {
+            for (int w = 0; w < 4; ++w) {
+                if (!((evb >> w) & 1u)) continue;
                 const float4 q = *reinterpret_cast<const float4*>(&sp[w][j][4 * h]);
                 acc.x += q.x;
                 acc.y += q.y;
@@ -289,6 +291,8 @@ constexpr int kGatherThreads = 256;
 constexpr int kGatherRecs = 1;
 // A run with more reached records than this is summed lane per record instead.
 constexpr int kGatherDenseRun = 8;
+// Slots whose loads a lane keeps in flight at once in that dense case.
+constexpr int kGatherInFlight = 4;
 
 __device__ __forceinline__ uint32_t bit_range_mask(int32_t lo, int32_t hi) {  // bits [lo, hi) of a word, clipped
     lo = lo < 0 ? 0 : lo;
@@ -359,9 +363,9 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                 uint32_t bits = b0[j];
                 uint32_t w = w0;
                 for (;;) {
-                    int64_t sl[4];
+                    int64_t sl[kGatherInFlight];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
+                    for (int u = 0; u < kGatherInFlight; ++u) {
                         while (bits == 0u && w < wlast) {
                             ++w;
                             const int32_t k = (int32_t)(w - w0);
@@ -374,14 +378,14 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                             bits &= bits - 1u;
                         }
                     }
-                    float4 p[4][NQ];
+                    float4 p[kGatherInFlight][NQ];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
+                    for (int u = 0; u < kGatherInFlight; ++u)
 #pragma unroll
                         for (int q = 0; q < NQ; ++q)
                             p[u][q] = sl[u] >= 0 ? partials[NQ * sl[u] + q] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
+                    for (int u = 0; u < kGatherInFlight; ++u)
 #pragma unroll
                         for (int q = 0; q < NQ; ++q) {
                             acc[q].x += p[u][q].x;
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_slots(int64_t VG,
                             acc[q].z += p[u][q].z;
                             acc[q].w += p[u][q].w;
                         }
-                    if (sl[3] < 0) break;
+                    if (sl[kGatherInFlight - 1] < 0) break;
                 }
 #pragma unroll
                 for (int q = 0; q < NQ; ++q) gv_sums[NQ * (run + lane) + q] = acc[q];
