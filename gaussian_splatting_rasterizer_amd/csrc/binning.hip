@@ -312,15 +312,25 @@ hipError_t launch_scan_u32(const uint32_t* in, int64_t n, uint32_t* out, ScanSta
 // ---------------------------------------------------------------------------
 // radix sort
 // ---------------------------------------------------------------------------
-// Lanes of the wave holding the same digit (one ballot per digit bit); invalid lanes never match.
+// Lanes of the wave holding the same digit (one ballot per digit bit); invalid lanes never match.  A lane
+// differs from this one where some bit's ballot disagrees with this lane's bit: the ballot XOR this lane's bit
+// sign-extended, ORed over the bits (a bit extract, a compare and two 32-bit XOR / OR halves per bit).
 __device__ __forceinline__ uint64_t match_peers(uint32_t dgt, int bits, bool valid) {
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-        const bool bit = (dgt >> b) & 1u;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
+    uint32_t dlo = ~(uint32_t)__ballot(valid), dhi = ~(uint32_t)(__ballot(valid) >> 32);
+#pragma unroll
+    for (int b = 0; b < kMaxDigitBits; ++b) {
+        if (b >= bits) break;
+        const uint32_t s = (uint32_t)__builtin_amdgcn_sbfe((int)dgt, b, 1);  // this lane's bit, sign-extended
+        const uint64_t m = __ballot(s != 0u);
+        dlo |= (uint32_t)m ^ s;
+        dhi |= (uint32_t)(m >> 32) ^ s;
     }
-    return peers;
+    return ~(((uint64_t)dhi << 32) | dlo);
+}
+
+// Number of lanes below this one set in m.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Digit counts of every pass in one read of the keys: per-block LDS
@@ -470,7 +480,6 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
     // element indices within the tile, 32-bit (cheap to recompute where needed)
     const int nblk = (int)(n - bbase < kTileKeys ? n - bbase : kTileKeys);
     const int wbase = wave * (kTileKeys / kRadixWaves) + lane;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
@@ -484,10 +493,10 @@ __global__ __launch_bounds__(kRadixThreads, 4) void k_onesweep(
         const bool valid = wbase + i * 64 < nblk;
         const uint32_t dgt = (key[i] >> shift) & mask;
         const uint64_t peers = match_peers(dgt, bits, valid);
-        const uint64_t lower = peers & lt_mask;
+        const uint32_t below = lanes_below(peers);
         const uint32_t c = valid ? cnt[wave][dgt] : 0u;
-        rank[i] = c + (uint32_t)__popcll(lower);
-        if (valid && lower == 0ull) cnt[wave][dgt] = c + (uint32_t)__popcll(peers);
+        rank[i] = c + below;
+        if (valid && below == 0u) cnt[wave][dgt] = c + (uint32_t)__popcll(peers);
     }
     __syncthreads();
     // publish this tile's digit counts first, so later tiles can look past it
