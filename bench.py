@@ -7,7 +7,8 @@ in HBM.  Prints ONE JSON line with the throughput (rendered+replayed Mpix/s),
 Gaussian-pixel contributions/s, per-stage times (HIP events on the stream the
 kernels run on), the roofline of the dominant kernel (the score replay: its
 fp32 VALU fraction and its HBM fraction), the score overhead (replay + finalize
-over the render path), the workspace and peak device memory, and the CPU oracle
+over the render path, and over the render path plus the renderer backward: a
+render/update step), the workspace and peak device memory, and the CPU oracle
 timed on a bounded sample on the host cores.  The other workload
 configurations are measured the same way and reported under "configs".  The
 renderer backward (gs_backward of 1/2 |C_hat - C_obs|^2 over the last step's
@@ -202,9 +203,10 @@ def measure(config, args, dev, stream, steps, warmup, extras):
         prof = binding.gs_profile_read(r.ctx)
         binding.gs_profile_enable(r.ctx, False)
 
-        # renderer backward of 1/2 |C_hat - C_obs|^2 on the same render, timed on its own
+        # renderer backward of 1/2 |C_hat - C_obs|^2 on the same render, timed on its own (every configuration:
+        # the score overhead is also reported against the render plus this backward, a gradient update step)
         bwd = None
-        if extras and not args.no_backward:
+        if not args.no_backward:
             grad_color = (outputs[0] - obs).contiguous()
             grads = r.new_grads()
             for _ in range(warmup):
@@ -336,6 +338,8 @@ def measure(config, args, dev, stream, steps, warmup, extras):
                           "live_records": n_live},
         "stages_ms": {k: round(v[0], 4) for k, v in stages.items()},
         "score_overhead": round(score_ms / render_ms, 4),
+        # the same over a render/update step: the render path plus the renderer backward of the same frame
+        "score_overhead_vs_update": None if bwd is None else round(score_ms / (render_ms + bwd["ms"]), 4),
         "roofline": roofline,
         "stage_rooflines": secondary,
         "memory": {"workspace_bytes": workspace_bytes, "peak_device_bytes": peak_bytes},
@@ -385,7 +389,10 @@ def main():
                          extras=False)
         others[res["config"]["workload"]] = {k: res[k] for k in (
             "value", "ms_per_step", "steps", "config", "contribs_per_s", "work_per_step", "stages_ms",
-            "score_overhead", "roofline", "stage_rooflines", "memory", "tokens_finite")}
+            "score_overhead", "score_overhead_vs_update", "roofline", "stage_rooflines", "memory",
+            "tokens_finite")}
+        if "backward" in res:
+            others[res["config"]["workload"]]["backward_ms"] = res["backward"]["ms"]
 
     out = {
         "metric": "render+score-replay Mpix/s",
@@ -401,8 +408,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
     }
-    for k in ("config", "contribs_per_s", "work_per_step", "stages_ms", "score_overhead", "roofline",
-              "stage_rooflines", "memory", "tokens_finite", "backward", "attributes"):
+    for k in ("config", "contribs_per_s", "work_per_step", "stages_ms", "score_overhead", "score_overhead_vs_update",
+              "roofline", "stage_rooflines", "memory", "tokens_finite", "backward", "attributes"):
         if k in main_res:
             out[k] = main_res[k]
     if others:
@@ -455,10 +462,20 @@ def sweep(args, dev, stream):
                 stream.synchronize()
                 prof = binding.gs_profile_read(r.ctx)
                 binding.gs_profile_enable(r.ctx, False)
+                # the renderer backward of the same frame (a render/update step's other half), timed on its own
+                grad_color = (outputs[0] - obs).contiguous()
+                grads = r.new_grads()
+                r.backward(grad_color, grads)
+                stream.synchronize()
+                tb = time.perf_counter()
+                for _ in range(steps):
+                    r.backward(grad_color, grads)
+                stream.synchronize()
+                bwd_ms = 1e3 * (time.perf_counter() - tb) / steps
                 K = int(outputs[2].to(torch.int64).sum().item())
                 P = int(r.n_pairs)
                 r.close()
-            del r, obs, outputs, tokens
+            del r, obs, outputs, tokens, grad_color, grads
             torch.cuda.empty_cache()
             st = {k: ms / max(cnt, 1) for k, (ms, cnt) in prof.items()}
             render_ms = sum(st[k] for k in RENDER_STAGES)
@@ -468,6 +485,8 @@ def sweep(args, dev, stream):
                               "gaussians": sc.n, "pairs": P, "contributions": K,
                               "ms_per_step": round(1e3 * elapsed, 4), "render_path_ms": round(render_ms, 4),
                               "score_ms": round(score_ms, 4), "score_overhead": round(score_ms / render_ms, 4),
+                              "backward_ms": round(bwd_ms, 4),
+                              "score_overhead_vs_update": round(score_ms / (render_ms + bwd_ms), 4),
                               "mpix_per_s": round(pix / elapsed / 1e6, 2),
                               "ns_per_pixel": round(1e9 * elapsed / pix, 3),
                               "stages_ms": {k: round(v, 4) for k, v in st.items()}}), flush=True)
