@@ -580,8 +580,10 @@ gs_status gs_score_replay(gs_context* ctx, const float* observed, float* tokens,
     if (e != hipSuccess) return hip_fail(e, "replay");
     ctx->timer.end(GS_STAGE_REPLAY, stream);
     ctx->timer.begin(GS_STAGE_FINALIZE, stream);
-    e = launch_gather_slots(ctx->s, ctx->ws, 2, stream);
-    if (e != hipSuccess) return hip_fail(e, "gather");
+    if (!tokens_gather(ctx->s)) {  // (otherwise the token kernel sums each record's slots itself)
+        e = launch_gather_slots(ctx->s, ctx->ws, 2, stream);
+        if (e != hipSuccess) return hip_fail(e, "gather");
+    }
     e = launch_tokens(ctx->scene, ctx->cams, ctx->s, ctx->ws, ctx->params.eps, ctx->params.lambda, tokens, stream);
     if (e != hipSuccess) return hip_fail(e, "tokens");
     ctx->timer.end(GS_STAGE_FINALIZE, stream);

@@ -191,6 +191,9 @@ hipError_t launch_backward(const Sizes& s, const Workspace& ws, const uint32_t* 
 hipError_t launch_backward_finalize(const gs_gaussians& sc, const CamPack& cams, const Sizes& s,
                                     const Workspace& ws, int antialiased, const gs_gaussian_grads& out,
                                     hipStream_t st);
+// Tokens from the per-record sums of k_gather_slots, or, where tokens_gather(s) holds (one view, up to 2M
+// Gaussians), from the slots directly (the gather kernel is then not needed).
+bool tokens_gather(const Sizes& s);
 hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws,
                          float eps, float lambda, float* tokens, hipStream_t st);
 hipError_t launch_exp2(const float* in, float* out, int64_t n, hipStream_t st);

@@ -463,14 +463,78 @@ hipError_t launch_gather_slots(const Sizes& s, const Workspace& ws, int nq, hipS
 // One thread per Gaussian: cross-view aggregation and the token.  Each wave
 // stages the tokens of half its lanes at a time in LDS and stores them as one
 // coalesced span (half a wave's tokens take 32 * DT floats, so the staging
-// leaves room for the waves the registers allow).
+// leaves room for the waves the registers allow).  With GATHER (one view: a
+// Gaussian is one record) the thread also sums its record's flagged slots
+// itself, in slot order with kGatherInFlight slots' loads in flight, instead of
+// reading the sums k_gather_slots left (no separate launch, no sums through
+// memory): for up to kTokGatherMaxG Gaussians (measured: the 512x960 compact
+// scene's finalize 50 -> 36 us; on 5.9M Gaussians, where the token stores bound
+// the kernel, the gather's load chains cost 297 -> 356 us).
 constexpr int kTokThreads = 128;
+constexpr int64_t kTokGatherMaxG = 1 << 21;
 
-template <int D>
+// Sums of the flagged partials (two float4 per slot) of a record's slots [sa, sa + tt); false if none is flagged.
+__device__ __forceinline__ bool sum_record_slots(uint32_t tt, uint32_t sa, const uint32_t* __restrict__ slot_bits,
+                                                 const float4* __restrict__ partials, float4& s0, float4& s1) {
+    s0 = make_float4(0.f, 0.f, 0.f, 0.f);
+    s1 = s0;
+    if (tt == 0u) return false;
+    const uint32_t w0 = sa >> 5, wlast = (sa + tt - 1u) >> 5;
+    const int32_t lo = (int32_t)(sa & 31u), hi = lo + (int32_t)tt;
+    // the first three words of the range together (a word past the range reads as zero)
+    const uint32_t c1 = w0 + 1u <= wlast ? slot_bits[w0 + 1u] : 0u;
+    const uint32_t c2 = w0 + 2u <= wlast ? slot_bits[w0 + 2u] : 0u;
+    uint32_t bits = slot_bits[w0] & bit_range_mask(lo, hi);
+    const uint32_t b1 = c1 & bit_range_mask(lo - 32, hi - 32), b2 = c2 & bit_range_mask(lo - 64, hi - 64);
+    uint32_t w = w0;
+    bool any = false;
+    for (;;) {
+        int64_t sl[kGatherInFlight];
+#pragma unroll
+        for (int u = 0; u < kGatherInFlight; ++u) {
+            while (bits == 0u && w < wlast) {
+                ++w;
+                const int32_t k = (int32_t)(w - w0);
+                bits = k == 1 ? b1 : k == 2 ? b2 : slot_bits[w] & bit_range_mask(lo - 32 * k, hi - 32 * k);
+            }
+            sl[u] = -1;
+            if (bits) {
+                sl[u] = (int64_t)w * 32 + __builtin_ctz(bits);
+                bits &= bits - 1u;
+            }
+        }
+        float4 p[kGatherInFlight][2];
+#pragma unroll
+        for (int u = 0; u < kGatherInFlight; ++u) {
+            p[u][0] = sl[u] >= 0 ? partials[2 * sl[u]] : make_float4(0.f, 0.f, 0.f, 0.f);
+            p[u][1] = sl[u] >= 0 ? partials[2 * sl[u] + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kGatherInFlight; ++u) {
+            s0.x += p[u][0].x;
+            s0.y += p[u][0].y;
+            s0.z += p[u][0].z;
+            s0.w += p[u][0].w;
+            s1.x += p[u][1].x;
+            s1.y += p[u][1].y;
+            s1.z += p[u][1].z;
+            s1.w += p[u][1].w;
+        }
+        any = any || sl[0] >= 0;
+        if (sl[kGatherInFlight - 1] < 0) break;
+    }
+    return any;
+}
+
+template <int D, bool GATHER>
 __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict__ means, const float* __restrict__ opac,
                                                         int64_t G, int V, CamPack cams,
                                                         const uint64_t* __restrict__ rec_masks,
-                                                        const float4* __restrict__ gv_sums, double eps, double lambda,
+                                                        const float4* __restrict__ gv_sums,
+                                                        const uint32_t* __restrict__ tiles_touched,
+                                                        const uint32_t* __restrict__ slot_base,
+                                                        const uint32_t* __restrict__ slot_bits,
+                                                        const float4* __restrict__ partials, double eps, double lambda,
                                                         float* __restrict__ tokens) {
 #pragma clang fp contract(fast)
     constexpr int DT = 9 + 3 * D;
@@ -491,6 +555,12 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
 
         // every view's live / reached bit first (at most 32 views), the mask loads of 8 views in flight together
         uint32_t live_bits = 0u, reach_bits = 0u;
+        float4 n0 = make_float4(0.f, 0.f, 0.f, 0.f), n1 = n0;
+        if constexpr (GATHER) {  // one view: the record is the Gaussian
+            const uint32_t tt = tiles_touched[g];
+            live_bits = tt != 0u ? 1u : 0u;
+            reach_bits = sum_record_slots(tt, slot_base[g], slot_bits, partials, n0, n1) ? 1u : 0u;
+        } else
         for (int v0 = 0; v0 < V; v0 += 8) {
             uint64_t lw[8], rw[8];
 #pragma unroll
@@ -509,8 +579,7 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
         // the reached views' sums are loaded one reached view ahead of the arithmetic (reached implies live)
         const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
         uint32_t pending = reach_bits;
-        float4 n0 = zero4, n1 = zero4;
-        if (pending) {
+        if (!GATHER && pending) {
             const int64_t rid = (int64_t)__builtin_ctz(pending) * G + g;
             n0 = gv_sums[2 * rid];
             n1 = gv_sums[2 * rid + 1];
@@ -526,7 +595,7 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
                 p0 = n0;
                 p1 = n1;
                 pending &= pending - 1u;  // v was the lowest pending view
-                if (pending) {
+                if (!GATHER && pending) {
                     const int64_t rid = (int64_t)__builtin_ctz(pending) * G + g;
                     n0 = gv_sums[2 * rid];
                     n1 = gv_sums[2 * rid + 1];
@@ -635,13 +704,20 @@ __global__ __launch_bounds__(kTokThreads) void k_tokens(const float* __restrict_
     }
 }
 
+bool tokens_gather(const Sizes& s) { return s.V == 1 && s.G <= kTokGatherMaxG; }
+
 hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Sizes& s, const Workspace& ws, float eps,
                          float lambda, float* tokens, hipStream_t st) {
     if (s.G == 0) return hipSuccess;
     const dim3 block(kTokThreads), grid((unsigned)((s.G + kTokThreads - 1) / kTokThreads));
-#define GSR_LAUNCH_TOKENS(DD)                                                                              \
-    hipLaunchKernelGGL(k_tokens<DD>, grid, block, 0, st, sc.means, sc.opacities, s.G, s.V, cams, ws.rec_masks, \
-                       ws.gv_sums, (double)eps, (double)lambda, tokens)
+    const bool gather = tokens_gather(s);  // the token kernel sums the records' slots itself
+#define GSR_LAUNCH_TOKENS_G(DD, GG)                                                                              \
+    hipLaunchKernelGGL((k_tokens<DD, GG>), grid, block, 0, st, sc.means, sc.opacities, s.G, s.V, cams, ws.rec_masks, \
+                       ws.gv_sums, ws.tiles_touched, ws.slot_base, ws.slot_bits, ws.partials, (double)eps,          \
+                       (double)lambda, tokens)
+#define GSR_LAUNCH_TOKENS(DD)                   \
+    if (gather) GSR_LAUNCH_TOKENS_G(DD, true);  \
+    else GSR_LAUNCH_TOKENS_G(DD, false)
     switch (s.d) {
         case 1: GSR_LAUNCH_TOKENS(1); break;
         case 4: GSR_LAUNCH_TOKENS(4); break;
@@ -649,6 +725,7 @@ hipError_t launch_tokens(const gs_gaussians& sc, const CamPack& cams, const Size
         default: GSR_LAUNCH_TOKENS(16); break;
     }
 #undef GSR_LAUNCH_TOKENS
+#undef GSR_LAUNCH_TOKENS_G
     return hipGetLastError();
 }
 
