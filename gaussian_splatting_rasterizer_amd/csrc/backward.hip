@@ -138,8 +138,9 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            for (int k = 0; k < nw; ++k) {
-                const uint32_t off = slist[wave][k];  // 16 j
+            // one entry: the float32 decisions and the state updates of every lane, and the nine values whose
+            // wave sums are the entry's partial row
+            auto step = [&](uint32_t off, float (&x)[8], float& x8) {
                 const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s0) + off);
                 const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s1) + off);
                 const float cbl = reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s2) + off)->x;
@@ -154,27 +155,55 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                 const bool sat = pass && tT < kTMin;
                 const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 done = done || sat;
-                {  // every listed entry has a contribution or saturation in some lane of the wave
-                    const float cr = b.z, cg = b.w;
-                    const float w = contrib ? alpha * Tr : 0.0f;
-                    const float gc = __builtin_fmaf(g2, cbl, __builtin_fmaf(g1, cg, g0 * cr));
-                    // <g, S> behind this entry: the prefix now includes it (lanes without a contribution subtract 0)
-                    qg = __builtin_fmaf(-w, gc, qg);
-                    const float gS = qg;
-                    // u = alpha (T <g, c> - <g, S> / (1 - alpha)) = w <g, c> - alpha <g, S> / (1 - alpha)
-                    const float u = (contrib && !clamped)
-                                        ? __builtin_fmaf(-alpha * gS, __builtin_amdgcn_rcpf(1.0f - alpha), w * gc)
-                                        : 0.0f;
-                    const float ux = u * dx, uy = u * dy;
-                    const float x[8] = {u, ux, uy, ux * dx, ux * dy, uy * dy, w * g0, w * g1};
-                    const float red = wave_reduce8(x, lane);
-                    const float red8 = wave_sum1(w * g2);
-                    // every lane of a group of eight holds its component's sum: all store (the same value to the
-                    // same word); sp[wave][j] rows are 48 bytes, 3 off
-                    *reinterpret_cast<float*>(reinterpret_cast<char*>(&sp[wave][0][0]) + 3 * off + 4 * (lane >> 3)) = red;
-                    if (lane == 0) *reinterpret_cast<float*>(reinterpret_cast<char*>(&sp[wave][0][0]) + 3 * off + 32) = red8;
-                    Tr = contrib ? tT : Tr;
-                }
+                // every listed entry has a contribution or saturation in some lane of the wave
+                const float cr = b.z, cg = b.w;
+                const float w = contrib ? alpha * Tr : 0.0f;
+                const float gc = __builtin_fmaf(g2, cbl, __builtin_fmaf(g1, cg, g0 * cr));
+                // <g, S> behind this entry: the prefix now includes it (lanes without a contribution subtract 0)
+                qg = __builtin_fmaf(-w, gc, qg);
+                const float gS = qg;
+                // u = alpha (T <g, c> - <g, S> / (1 - alpha)) = w <g, c> - alpha <g, S> / (1 - alpha)
+                const float u = (contrib && !clamped)
+                                    ? __builtin_fmaf(-alpha * gS, __builtin_amdgcn_rcpf(1.0f - alpha), w * gc)
+                                    : 0.0f;
+                const float ux = u * dx, uy = u * dy;
+                x[0] = u;
+                x[1] = ux;
+                x[2] = uy;
+                x[3] = ux * dx;
+                x[4] = ux * dy;
+                x[5] = uy * dy;
+                x[6] = w * g0;
+                x[7] = w * g1;
+                x8 = w * g2;
+                Tr = contrib ? tT : Tr;
+            };
+            // every lane of a group of eight holds its component's sum: all store (the same value to the same
+            // word); sp[wave][j] rows are 48 bytes, 3 off
+            char* spw = reinterpret_cast<char*>(&sp[wave][0][0]);
+            auto put = [&](uint32_t off, float red, float red8) {
+                *reinterpret_cast<float*>(spw + 3 * off + 4 * (lane >> 3)) = red;
+                if (lane == 0) *reinterpret_cast<float*>(spw + 3 * off + 32) = red8;
+            };
+            // two entries per round: the second entry's decisions follow the first's state updates, and the
+            // wave reductions of the two, independent of each other, run interleaved
+            int k = 0;
+            for (; k + 1 < nw; k += 2) {
+                const uint32_t o0 = slist[wave][k], o1 = slist[wave][k + 1];
+                float x0[8], x1[8], y0, y1;
+                step(o0, x0, y0);
+                step(o1, x1, y1);
+                const float red0 = wave_reduce8(x0, lane), red1 = wave_reduce8(x1, lane);
+                const float s0v = wave_sum1(y0), s1v = wave_sum1(y1);
+                put(o0, red0, s0v);
+                put(o1, red1, s1v);
+            }
+            if (k < nw) {
+                const uint32_t o0 = slist[wave][k];
+                float x0[8], y0;
+                step(o0, x0, y0);
+                const float red0 = wave_reduce8(x0, lane);
+                put(o0, red0, wave_sum1(y0));
             }
         }
         __syncthreads();

@@ -146,18 +146,30 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            for (int k = 0; k < nw; ++k) {
-                const uint32_t off = slist[wave][k];  // 16 j
+            // one entry's geometry (no state): the exponent, alpha and the colour
+            struct Geo {
+                float S, alpha, cr, cg, cb;
+            };
+            auto geo = [&](uint32_t off) {
                 const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s0) + off);
                 const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s1) + off);
                 // evaluated in every lane; the decisions below mask lanes that are done or beyond the cut
                 const float dx = px - a.x, dy = py - a.y;
-                const float S = quad_S(a.z, a.w, b.x, dx, dy);
-                const bool near = !done && S <= kSCutoff;
-                const float aG = b.y * exp2_spec(-S);
-                const float alpha = aG < kAlphaMax ? aG : kAlphaMax;
-                const bool pass = near && alpha >= kAlphaMin;
-                const float tT = Tr * (1.0f - alpha);
+                Geo g;
+                g.S = quad_S(a.z, a.w, b.x, dx, dy);
+                const float aG = b.y * exp2_spec(-g.S);
+                g.alpha = aG < kAlphaMax ? aG : kAlphaMax;
+                g.cr = b.z;
+                g.cg = b.w;
+                g.cb = reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s2) + off)->x;
+                return g;
+            };
+            // the entry at list position k: its decisions on the lane's state, and the state update; false once
+            // every pixel of the wave is done
+            auto apply = [&](int k, uint32_t off, const Geo& g) {
+                const bool near = !done && g.S <= kSCutoff;
+                const bool pass = near && g.alpha >= kAlphaMin;
+                const float tT = Tr * (1.0f - g.alpha);
                 const bool sat = pass && tT < kTMin;
                 const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 if constexpr (STATS) {
@@ -167,15 +179,25 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                 done = done || sat;
                 if constexpr (!STATS) {
                     // branch-free: lanes without a contribution add zero
-                    const float w = contrib ? alpha * Tr : 0.0f;
-                    h0 = __builtin_fmaf(b.z, w, h0);
-                    h1 = __builtin_fmaf(b.w, w, h1);
-                    h2 = __builtin_fmaf(reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s2) + off)->x, w, h2);
+                    const float w = contrib ? g.alpha * Tr : 0.0f;
+                    h0 = __builtin_fmaf(g.cr, w, h0);
+                    h1 = __builtin_fmaf(g.cg, w, h1);
+                    h2 = __builtin_fmaf(g.cb, w, h2);
                     n += contrib ? 1 : 0;
                 }
                 Tr = contrib ? tT : Tr;
                 if (!STATS && pass) s_evk[wave][k] = 1;  // contributed or saturated (every such lane writes the same)
-                if (__ballot(!done) == 0ull) break;
+                return __ballot(!done) != 0ull;
+            };
+            // two entries per round: the second entry's geometry, which needs no state, is evaluated beside the
+            // first's, and its decisions follow the first's state update
+            for (int k = 0; k < nw; k += 2) {
+                const uint32_t o0 = slist[wave][k];
+                const bool two = k + 1 < nw;
+                const uint32_t o1 = two ? (uint32_t)slist[wave][k + 1] : o0;
+                const Geo g0 = geo(o0), g1 = geo(o1);
+                if (!apply(k, o0, g0)) break;
+                if (two && !apply(k + 1, o1, g1)) break;
             }
             if constexpr (!STATS) {
                 // the events by list position, moved to the entries they name

@@ -137,8 +137,9 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            for (int k = 0; k < nw; ++k) {
-                const uint32_t off = slist[wave][k];  // 16 j
+            // one entry: the float32 decisions and the state updates of every lane, and the eight values
+            // whose wave sums are the entry's partial row
+            auto step = [&](uint32_t off, float (&x)[8]) {
                 const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s0) + off);
                 const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s1) + off);
                 const float cbl = reinterpret_cast<const float4*>(reinterpret_cast<const char*>(s2) + off)->x;
@@ -156,27 +157,50 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                 done = done || sat;
                 // some lane of the wave contributes or saturates at every listed entry (a wave's list ends
                 // at its last such entry), so the partials are formed without testing for a contribution
-                {
-                    const float cr = b.z, cg = b.w;
-                    const float w = contrib ? alpha * Tr : 0.0f;
-                    const float rc = __builtin_fmaf(r2, cbl, __builtin_fmaf(r1, cg, r0 * cr));
-                    // <r, S> behind this entry: the prefix now includes it (lanes without a contribution
-                    // subtract zero)
-                    q = __builtin_fmaf(-w, rc, q);
-                    const float inv_den = __builtin_amdgcn_rcpf(tT + eps);
-                    // rho = <r, c - S / den> = <r, c> - <r, S> / den
-                    const float rho = __builtin_fmaf(-q, inv_den, rc);
-                    const float mw = (contrib && !clamped && tT >= den_min) ? w * rho : 0.0f;
-                    // the eighth component is never read (the flush stores zero there): rho, a value that
-                    // dies here, fills it without a register move
-                    const float x[8] = {w, mw, mw * dx, mw * dy, w * r0, w * r1, w * r2, rho};
-                    const float red = wave_reduce8(x, lane);
-                    // every lane of a group of eight holds its component's sum: all store (the same value to
-                    // the same word), so no lane mask is set up for the store
-                    // (sp[wave][j][lane >> 3]: rows of 32 bytes, so the row's byte offset is 2 off)
-                    *reinterpret_cast<float*>(reinterpret_cast<char*>(&sp[wave][0][0]) + 2 * off + 4 * (lane >> 3)) = red;
-                    Tr = contrib ? tT : Tr;
-                }
+                const float cr = b.z, cg = b.w;
+                const float w = contrib ? alpha * Tr : 0.0f;
+                const float rc = __builtin_fmaf(r2, cbl, __builtin_fmaf(r1, cg, r0 * cr));
+                // <r, S> behind this entry: the prefix now includes it (lanes without a contribution
+                // subtract zero)
+                q = __builtin_fmaf(-w, rc, q);
+                const float inv_den = __builtin_amdgcn_rcpf(tT + eps);
+                // rho = <r, c - S / den> = <r, c> - <r, S> / den
+                const float rho = __builtin_fmaf(-q, inv_den, rc);
+                const float mw = (contrib && !clamped && tT >= den_min) ? w * rho : 0.0f;
+                // the eighth component is never read (the flush stores zero there): rho, a value that
+                // dies here, fills it without a register move
+                x[0] = w;
+                x[1] = mw;
+                x[2] = mw * dx;
+                x[3] = mw * dy;
+                x[4] = w * r0;
+                x[5] = w * r1;
+                x[6] = w * r2;
+                x[7] = rho;
+                Tr = contrib ? tT : Tr;
+            };
+            // every lane of a group of eight holds its component's sum: all store (the same value to the
+            // same word), so no lane mask is set up for the store
+            // (sp[wave][j][lane >> 3]: rows of 32 bytes, so the row's byte offset is 2 off)
+            char* spw = reinterpret_cast<char*>(&sp[wave][0][0]) + 4 * (lane >> 3);
+            // two entries per round: the second entry's decisions follow the first's state updates, and the
+            // two wave reductions, independent of each other, run interleaved
+            int k = 0;
+            for (; k + 1 < nw; k += 2) {
+                const uint32_t o0 = slist[wave][k], o1 = slist[wave][k + 1];
+                float x0[8], x1[8];
+                step(o0, x0);
+                step(o1, x1);
+                const float red0 = wave_reduce8(x0, lane);
+                const float red1 = wave_reduce8(x1, lane);
+                *reinterpret_cast<float*>(spw + 2 * o0) = red0;
+                *reinterpret_cast<float*>(spw + 2 * o1) = red1;
+            }
+            if (k < nw) {
+                const uint32_t o0 = slist[wave][k];
+                float x0[8];
+                step(o0, x0);
+                *reinterpret_cast<float*>(spw + 2 * o0) = wave_reduce8(x0, lane);
             }
         }
         __syncthreads();
