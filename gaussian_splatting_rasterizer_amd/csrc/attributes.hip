@@ -219,8 +219,9 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            for (int k = 0; k < nw; ++k) {
-                const int j = slist[wave][k];
+            // one entry: the decisions and state updates of every lane, and its weight (every listed entry has
+            // a contribution or saturation in some lane of the wave)
+            auto step = [&](int j) {
                 const float4 a = s0[j];
                 const float2 b = s1[j];
                 const float dx = px - a.x, dy = py - a.y;
@@ -233,15 +234,32 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
                 const bool sat = pass && tT < kTMin;
                 const bool contrib = pass != sat;  // (sat implies pass: a mask difference, no second compare)
                 done = done || sat;
-                {  // every listed entry has a contribution or saturation in some lane of the wave
-                    const float w = contrib ? alpha * Tr : 0.0f;
-                    float x[8];
+                const float w = contrib ? alpha * Tr : 0.0f;
+                Tr = contrib ? tT : Tr;
+                return w;
+            };
+            auto reduce = [&](float w) {
+                float x[8];
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) x[c] = w * m[c];
-                    const float red = wave_reduce8(x, lane);
-                    if ((lane & 7) == 0) sp[wave][j][lane >> 3] = red;
-                    Tr = contrib ? tT : Tr;
+                for (int c = 0; c < 8; ++c) x[c] = w * m[c];
+                return wave_reduce8(x, lane);
+            };
+            // two entries per round: the two wave reductions, independent of each other, run interleaved
+            int k = 0;
+            for (; k + 1 < nw; k += 2) {
+                const int j0 = slist[wave][k], j1 = slist[wave][k + 1];
+                const float w0 = step(j0);
+                const float w1 = step(j1);
+                const float red0 = reduce(w0), red1 = reduce(w1);
+                if ((lane & 7) == 0) {
+                    sp[wave][j0][lane >> 3] = red0;
+                    sp[wave][j1][lane >> 3] = red1;
                 }
+            }
+            if (k < nw) {
+                const int j0 = slist[wave][k];
+                const float red0 = reduce(step(j0));
+                if ((lane & 7) == 0) sp[wave][j0][lane >> 3] = red0;
             }
         }
         __syncthreads();

@@ -30,6 +30,7 @@
 namespace gsr {
 
 constexpr int kRenderBatch = 256;
+constexpr int kRenderAhead = 3;  // list entries whose geometry is evaluated in one round
 
 template <bool STATS>
 __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges, const uint32_t* __restrict__ sorted_g,
@@ -189,15 +190,21 @@ __global__ __launch_bounds__(256) void k_render(const uint2* __restrict__ ranges
                 if (!STATS && pass) s_evk[wave][k] = 1;  // contributed or saturated (every such lane writes the same)
                 return __ballot(!done) != 0ull;
             };
-            // two entries per round: the second entry's geometry, which needs no state, is evaluated beside the
-            // first's, and its decisions follow the first's state update
-            for (int k = 0; k < nw; k += 2) {
-                const uint32_t o0 = slist[wave][k];
-                const bool two = k + 1 < nw;
-                const uint32_t o1 = two ? (uint32_t)slist[wave][k + 1] : o0;
-                const Geo g0 = geo(o0), g1 = geo(o1);
-                if (!apply(k, o0, g0)) break;
-                if (two && !apply(k + 1, o1, g1)) break;
+            // kRenderAhead entries per round: their geometry, which needs no state, is evaluated together, and
+            // their decisions follow in list order (3 measured fastest: 2 leaves latency exposed, 4 adds
+            // registers without gain)
+            bool live = true;
+            for (int k = 0; k < nw && live; k += kRenderAhead) {
+                uint32_t o[kRenderAhead];
+                Geo g[kRenderAhead];
+#pragma unroll
+                for (int u = 0; u < kRenderAhead; ++u) {
+                    o[u] = slist[wave][min(k + u, nw - 1)];
+                    g[u] = geo(o[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < kRenderAhead; ++u)
+                    if (live && k + u < nw) live = apply(k + u, o[u], g[u]);
             }
             if constexpr (!STATS) {
                 // the events by list position, moved to the entries they name
