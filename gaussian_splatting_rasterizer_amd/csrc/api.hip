@@ -144,10 +144,14 @@ Sizes make_sizes(const gs_dims& d) {
     s.VG = (int64_t)s.V * s.G;
     s.max_pairs = d.max_pairs;
     const int64_t nmax = s.VG > (int64_t)s.max_pairs ? s.VG : (int64_t)s.max_pairs;
-    // look-back rows for the larger of: the tiles of the largest sort, those of a small sort in half tiles
+    // look-back rows for the largest of: the tiles of the largest sort, those of a small sort in half tiles,
+    // those of a tiny sort in quarter tiles
     const int64_t nsmall = nmax < kSmallSortKeys ? nmax : kSmallSortKeys;
-    const int64_t tiles_large = (nmax + kSortTile - 1) / kSortTile, tiles_small = (nsmall + kSmallSortTile - 1) / kSmallSortTile;
+    const int64_t ntiny = nmax < kTinySortKeys ? nmax : kTinySortKeys;
+    const int64_t tiles_large = (nmax + kSortTile - 1) / kSortTile, tiles_small = (nsmall + kSmallSortTile - 1) / kSmallSortTile,
+                  tiles_tiny = (ntiny + kTinySortTile - 1) / kTinySortTile;
     s.sort_tiles_cap = tiles_large > tiles_small ? tiles_large : tiles_small;
+    if (tiles_tiny > s.sort_tiles_cap) s.sort_tiles_cap = tiles_tiny;
     s.scan_blocks_cap = (s.VG + kBlockItems - 1) / kBlockItems + 1;
     return s;
 }

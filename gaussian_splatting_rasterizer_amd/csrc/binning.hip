@@ -44,6 +44,9 @@ static_assert(kRadixTile == kSortTile, "radix tile size");
 // as one tile does (ranking, look-back and scatter in series), and a half tile halves its ranking.
 constexpr int kSmallRadixItems = kRadixItems / 2;
 static_assert(kRadixThreads * kSmallRadixItems == kSmallSortTile, "small radix tile size");
+// and sorts of at most kTinySortKeys keys (a depth sort of a few hundred thousand records) quarter tiles
+constexpr int kTinyRadixItems = kRadixItems / 4;
+static_assert(kRadixThreads * kTinyRadixItems == kTinySortTile, "tiny radix tile size");
 constexpr int kMaxDigitBits = 8;
 constexpr int kMaxBins = 1 << kMaxDigitBits;
 constexpr int kMaxPasses = kSortMaxPasses;
@@ -673,8 +676,9 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
     const RadixDigits rd = radix_digits(bits);
     bits = rd.bits;
     const int passes = rd.passes, dbits = rd.dbits;
+    const bool tiny = n <= kTinySortKeys;
     const bool small = n <= kSmallSortKeys;
-    const int64_t tile_keys = small ? kSmallSortTile : kRadixTile;
+    const int64_t tile_keys = tiny ? kTinySortTile : small ? kSmallSortTile : kRadixTile;
     const int64_t nb = (n + tile_keys - 1) / tile_keys;
     // packed words: key bits [key_shift, key_shift + bits), counted beforehand, no value array, no rectangles
     const bool packed = key_shift > 0;
@@ -744,7 +748,11 @@ hipError_t launch_radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, i
                                                     : kPlain;
 #define GSR_ONESWEEP(M)                                                                                        \
     do {                                                                                                       \
-        if (small)                                                                                             \
+        if (tiny)                                                                                              \
+            hipLaunchKernelGGL((k_onesweep<M, kTinyRadixItems>), dim3((unsigned)nb), dim3(kRadixThreads), 0, st,  \
+                               ksrc, vsrc, n, shift, pb, sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins,         \
+                               sc.lookback, ep, kdst, vdst, rc);                                               \
+        else if (small)                                                                                        \
             hipLaunchKernelGGL((k_onesweep<M, kSmallRadixItems>), dim3((unsigned)nb), dim3(kRadixThreads), 0, st, \
                                ksrc, vsrc, n, shift, pb, sc.ctl + p, sc.ctl + kCtlTotals + p * kMaxBins,         \
                                sc.lookback, ep, kdst, vdst, rc);                                               \

@@ -71,6 +71,8 @@ struct Sizes {
 constexpr int kSortTile = 8192;       // keys per radix tile (512 threads x 16)
 constexpr int kSmallSortTile = 4096;  // keys per radix tile of a sort of at most kSmallSortKeys keys
 constexpr int64_t kSmallSortKeys = 1 << 21;
+constexpr int kTinySortTile = 2048;   // keys per radix tile of a sort of at most kTinySortKeys keys
+constexpr int64_t kTinySortKeys = 1 << 19;
 constexpr int kSortMaxPasses = 4;     // 8-bit digits of 32-bit keys
 constexpr int kSortCtlTotals = 8;     // sort_ctl: [0, 8) tickets, then kSortMaxPasses x 256 digit totals
 constexpr int kSortCtlWords = kSortCtlTotals + kSortMaxPasses * 256;
