@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
                                                          int W, int H, const uint8_t* __restrict__ events,
                                                          const float* __restrict__ feat, int C, int c0, int nc,
                                                          FeatBg bg, float* __restrict__ out,
-                                                         const uint32_t* __restrict__ tile_order) {
+                                                         const uint32_t* __restrict__ tile_order,
+                                                         const uint32_t* __restrict__ tile_work) {
     __shared__ float4 s0[kAttrBatch];
     __shared__ float2 s1[kAttrBatch];
     __shared__ float sf[kAttrBatch][NC];
@@ -55,6 +56,8 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
     // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
     const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
+    // the entries the render processed (every event lies there); an empty range ({~0u, 0}) has none
+    const uint32_t rend = rg.x + min(tile_work[tile], rg.y > rg.x ? rg.y - rg.x : 0u);
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
@@ -64,10 +67,10 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
     float Tr = 1.0f;
     bool done = !inside;
 
-    for (uint32_t base = rg.x; base < rg.y; base += kAttrBatch) {
+    for (uint32_t base = rg.x; base < rend; base += kAttrBatch) {
         if (__syncthreads_count(!done) == 0) break;
         const uint32_t i = base + threadIdx.x;
-        if (threadIdx.x < kAttrBatch && i < rg.y) {
+        if (threadIdx.x < kAttrBatch && i < rend) {
             const uint32_t g = sorted_g[i];
             const int64_t rid = vG + g;
             const float4 a = rec0[rid];
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
 #pragma unroll
             for (int c = 0; c < NC; ++c) sf[threadIdx.x][c] = c < nc ? fg[c] : 0.0f;
         }
-        const int cnt = (int)min((uint32_t)kAttrBatch, rg.y - base);
+        const int cnt = (int)min((uint32_t)kAttrBatch, rend - base);
         __syncthreads();
         if (__ballot(!done) != 0ull) {
             int nw = 0;
@@ -134,7 +137,7 @@ hipError_t launch_render_features(const Sizes& s, const Workspace& ws, const uin
 #define GSR_LAUNCH_FEAT(NN)                                                                                       \
     hipLaunchKernelGGL(k_render_features<NN>, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,       \
                        ws.rec0, ws.rec1, ws.rec2, s.G, s.T, s.TX, s.W, s.H, ws.events, feat, C, c0, nc, bg, out,      \
-                       ws.tile_order)
+                       ws.tile_order, ws.tile_work)
         if (nc <= 4) GSR_LAUNCH_FEAT(4);
         else if (nc <= 8) GSR_LAUNCH_FEAT(8);
         else GSR_LAUNCH_FEAT(16);
@@ -155,7 +158,8 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
                                                    int H, const uint8_t* __restrict__ events,
                                                    const float* __restrict__ map, int C, int c0, int nc,
                                                    float4* __restrict__ partials, uint32_t* __restrict__ slot_bits,
-                                                   const uint32_t* __restrict__ tile_order) {
+                                                   const uint32_t* __restrict__ tile_order,
+                                                   const uint32_t* __restrict__ tile_work) {
     __shared__ float4 s0[kAttrBatch];
     __shared__ float2 s1[kAttrBatch];
     __shared__ uint8_t s_evb[kAttrBatch];
@@ -174,6 +178,8 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
     // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
     const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
+    // the entries the render processed (every event lies there); an empty range ({~0u, 0}) has none
+    const uint32_t rend = rg.x + min(tile_work[tile], rg.y > rg.x ? rg.y - rg.x : 0u);
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
@@ -189,10 +195,10 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
     float Tr = 1.0f;
     bool done = !inside;
 
-    for (uint32_t base = rg.x; base < rg.y; base += kAttrBatch) {
+    for (uint32_t base = rg.x; base < rend; base += kAttrBatch) {
         if (__syncthreads_count(!done) == 0) break;
         const uint32_t i = base + threadIdx.x;
-        if (threadIdx.x < kAttrBatch && i < rg.y) {
+        if (threadIdx.x < kAttrBatch && i < rend) {
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 c = rec2[rid];
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(256) void k_attribute(const uint2* __restrict__ ran
             const uint32_t x0 = rc.x & 0xffffu, y0 = rc.x >> 16, wx = (rc.y & 0xffffu) - x0;
             s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
         }
-        const int cnt = (int)min((uint32_t)kAttrBatch, rg.y - base);
+        const int cnt = (int)min((uint32_t)kAttrBatch, rend - base);
         for (int e = lane; e < cnt * 8; e += 64) (&sp[wave][0][0])[e] = 0.0f;
         __syncthreads();
         if (__ballot(!done) != 0ull) {
@@ -319,7 +325,7 @@ hipError_t launch_attribute(const Sizes& s, const Workspace& ws, const uint32_t*
             hipLaunchKernelGGL(k_attribute, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,
                                ws.slot_base, ws.rec0, ws.rec1, ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.events,
                                map, C,
-                               c0, nc, ws.partials, ws.slot_bits, ws.tile_order);
+                               c0, nc, ws.partials, ws.slot_bits, ws.tile_order, ws.tile_work);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         e = launch_gather_slots(s, ws, 2, st);
@@ -342,7 +348,8 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
                                               const float4* __restrict__ rec0, const float4* __restrict__ rec1,
                                               const float4* __restrict__ rec2, int64_t G, int T, int TX, int W, int H,
                                               const uint8_t* __restrict__ events, int k_out,
-                                              int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+                                              int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+                                              const uint32_t* __restrict__ tile_work) {
     __shared__ float4 s0[kAttrBatch];
     __shared__ float2 s1[kAttrBatch];
     __shared__ uint32_t s_g[kAttrBatch];
@@ -360,6 +367,8 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
     // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
     const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
+    // the entries the render processed (every event lies there); an empty range ({~0u, 0}) has none
+    const uint32_t rend = rg.x + min(tile_work[tile], rg.y > rg.x ? rg.y - rg.x : 0u);
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
@@ -373,10 +382,10 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
     float Tr = 1.0f;
     bool done = !inside;
 
-    for (uint32_t base = rg.x; base < rg.y; base += kAttrBatch) {
+    for (uint32_t base = rg.x; base < rend; base += kAttrBatch) {
         if (__syncthreads_count(!done) == 0) break;
         const uint32_t i = base + threadIdx.x;
-        if (threadIdx.x < kAttrBatch && i < rg.y) {
+        if (threadIdx.x < kAttrBatch && i < rend) {
             const uint32_t g = sorted_g[i];
             const float4 a = rec0[vG + g];
             const float4 c = rec2[vG + g];
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(256) void k_topk(const uint2* __restrict__ ranges, 
             s_g[threadIdx.x] = g;
             s_evb[threadIdx.x] = events[i];
         }
-        const int cnt = (int)min((uint32_t)kAttrBatch, rg.y - base);
+        const int cnt = (int)min((uint32_t)kAttrBatch, rend - base);
         __syncthreads();
         if (__ballot(!done) != 0ull) {
             int nw = 0;
@@ -450,7 +459,7 @@ hipError_t launch_topk(const Sizes& s, const Workspace& ws, const uint32_t* sort
     if (tiles == 0) return hipSuccess;
 #define GSR_LAUNCH_TOPK(KK)                                                                                       \
     hipLaunchKernelGGL(k_topk<KK>, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.rec0, ws.rec1, \
-                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, ws.events, k, ids, w)
+                       ws.rec2, s.G, s.T, s.TX, s.W, s.H, ws.events, k, ids, w, ws.tile_work)
     if (k <= 4) GSR_LAUNCH_TOPK(4);
     else if (k <= 8) GSR_LAUNCH_TOPK(8);
     else GSR_LAUNCH_TOPK(16);

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
                                                   const float* __restrict__ grad_color,
                                                   const uint8_t* __restrict__ events, float4* __restrict__ partials,
                                                   uint32_t* __restrict__ slot_bits,
-                                                  const uint32_t* __restrict__ tile_order) {
+                                                  const uint32_t* __restrict__ tile_order,
+                                                  const uint32_t* __restrict__ tile_work) {
     // an entry's three staged vectors sit at the same byte offset of three arrays, so one offset (16 j,
     // kept in the wave's list) addresses all of them
     __shared__ float4 s0[kBwdBatch];  // {tile-relative centre (2), s1, s2}
@@ -106,10 +107,14 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
     float qg = __builtin_fmaf(g2, Ch2, __builtin_fmaf(g1, Ch1, g0 * Ch0));
     bool done = !inside;
 
-    for (uint32_t base = rg.x; base < rg.y; base += kBwdBatch) {
+    // the entries the render processed (every event lies there: past them the event bytes are not this frame's,
+    // and a wave whose pixels are all done would leave its partial rows unwritten for one it names); an empty
+    // range ({~0u, 0}) has none
+    const uint32_t rend = rg.x + min(tile_work[tile], rg.y > rg.x ? rg.y - rg.x : 0u);
+    for (uint32_t base = rg.x; base < rend; base += kBwdBatch) {
         if (__syncthreads_count(!done) == 0) break;
         const uint32_t i = base + threadIdx.x;
-        if (threadIdx.x < kBwdBatch && i < rg.y) {
+        if (threadIdx.x < kBwdBatch && i < rend) {
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(256) void k_backward(const uint2* __restrict__ rang
             s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
             s_mask[threadIdx.x] = (uint8_t)((colour_ok(b.z) ? 1u : 0u) | (colour_ok(b.w) ? 2u : 0u) | (colour_ok(c.x) ? 4u : 0u));
         }
-        const int cnt = (int)min((uint32_t)kBwdBatch, rg.y - base);
+        const int cnt = (int)min((uint32_t)kBwdBatch, rend - base);
         // (a wave writes the partial row of every entry it walks; the flush reads only those rows)
         __syncthreads();
         if (__ballot(!done) != 0ull) {
@@ -243,7 +248,7 @@ hipError_t launch_backward(const Sizes& s, const Workspace& ws, const uint32_t* 
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_backward, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g, ws.slot_base,
                        ws.rec0, ws.rec1, ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.pixel, grad_color,
-                       ws.events, ws.partials, ws.slot_bits, ws.tile_order);
+                       ws.events, ws.partials, ws.slot_bits, ws.tile_order, ws.tile_work);
     return hipGetLastError();
 }
 

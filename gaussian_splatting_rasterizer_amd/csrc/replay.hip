@@ -60,7 +60,8 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
                                                 int64_t G, int T, int TX, int W, int H, const float4* __restrict__ pixel, const float* __restrict__ observed,
                                                 const uint8_t* __restrict__ events, float eps, float den_min,
                                                 float4* __restrict__ partials, uint32_t* __restrict__ slot_bits,
-                                                const uint32_t* __restrict__ tile_order) {
+                                                const uint32_t* __restrict__ tile_order,
+                                                const uint32_t* __restrict__ tile_work) {
     // an entry's three staged vectors sit at the same byte offset of three arrays, so one offset (16 j,
     // kept in the wave's list) addresses all of them
     __shared__ float4 s0[kReplayBatch];        // {tile-relative centre (2), s1, s2}
@@ -84,6 +85,10 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     // pixel centre relative to the tile origin (entry centres are staged tile-relative too)
     const float px = (float)(pxi - tx * kTile) + 0.5f, py = (float)(pyi - ty * kTile) + 0.5f;
     const uint2 rg = ranges[tile];
+    // the entries the render processed (every event lies there: past them the event bytes are not this frame's,
+    // and a wave whose pixels are all done would leave its partial rows unwritten for one it names); an empty
+    // range ({~0u, 0}) has none
+    const uint32_t rend = rg.x + min(tile_work[tile], rg.y > rg.x ? rg.y - rg.x : 0u);
     const int64_t vG = (int64_t)v * G;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
@@ -104,10 +109,10 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
     bool done = !inside;
 
     uint32_t base = rg.x;
-    for (; base < rg.y; base += kReplayBatch) {
+    for (; base < rend; base += kReplayBatch) {
         if (__syncthreads_count(!done) == 0) break;
         const uint32_t i = base + threadIdx.x;
-        if (threadIdx.x < kReplayBatch && i < rg.y) {
+        if (threadIdx.x < kReplayBatch && i < rend) {
             const int64_t rid = vG + sorted_g[i];
             const float4 a = rec0[rid];
             const float4 b = rec1[rid];
@@ -122,7 +127,7 @@ __global__ __launch_bounds__(256) void k_replay(const uint2* __restrict__ ranges
             s_slot[threadIdx.x] = slot_base[rid] + ((uint32_t)ty - y0) * wx + ((uint32_t)tx - x0);
             s_mask[threadIdx.x] = (uint8_t)((colour_ok(b.z) ? 1u : 0u) | (colour_ok(b.w) ? 2u : 0u) | (colour_ok(c.x) ? 4u : 0u));
         }
-        const int cnt = (int)min((uint32_t)kReplayBatch, rg.y - base);
+        const int cnt = (int)min((uint32_t)kReplayBatch, rend - base);
         // (a wave writes the partial row of every entry it walks; the flush reads only those rows)
         __syncthreads();
         if (__ballot(!done) != 0ull) {
@@ -246,7 +251,7 @@ hipError_t launch_replay(const Sizes& s, const Workspace& ws, const uint32_t* so
     hipLaunchKernelGGL(k_replay, dim3((unsigned)tiles), dim3(256), 0, st, ws.ranges, sorted_g,
                        ws.slot_base, ws.rec0, ws.rec1,
                        ws.rec2, ws.rect, s.G, s.T, s.TX, s.W, s.H, ws.pixel, observed, ws.events, eps, den_min,
-                       ws.partials, ws.slot_bits, ws.tile_order);
+                       ws.partials, ws.slot_bits, ws.tile_order, ws.tile_work);
     return hipGetLastError();
 }
 

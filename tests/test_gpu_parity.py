@@ -72,6 +72,14 @@ def _small_scenes():
         # a tile grid wider than 256 tiles (4200 px): the depth sort gathers rectangles instead of carrying them
         "wide_grid": lambda: scenes.tiny_scene(seed=31, n=3000, n_views=1, W=4200, H=48, sh_degree=1,
                                                log_scale=(-5.5, 0.5)),
+        # tile lists of 4,710-5,000 faint Gaussians, every entry processed (no pixel saturates): the score
+        # replay walks each list as the most segments the render leaves checkpoints for, the last one long
+        "deep_lists": lambda: scenes.tiny_scene(seed=41, n=5000, n_views=2, W=40, H=32, sh_degree=1,
+                                                log_scale=(-0.7, 0.2), logit=(-6.0, 0.5), spread=0.2),
+        # 3,000-entry lists whose tiles are done after 324-1,997 entries: segments that end where the render
+        # stopped
+        "deep_saturating": lambda: scenes.tiny_scene(seed=42, n=3000, n_views=1, W=48, H=40, sh_degree=2,
+                                                     log_scale=(-0.3, 0.2), logit=(-3.0, 0.5), spread=0.3),
         # antialiased (opacity-compensated) mode
         "c2_small_aa": lambda: scenes.c2_resplat_step(n_views=2, W=112, H=64),
         "tiny_ragged_aa": lambda: scenes.tiny_scene(seed=21, n=60, n_views=2, W=40, H=24, sh_degree=2),
@@ -297,7 +305,7 @@ def test_second_bin_sort_after_one_project():
         r.close()
 
 
-@pytest.mark.parametrize("name", ["c2_small", "c5_small", "elongated"])
+@pytest.mark.parametrize("name", ["c2_small", "c5_small", "elongated", "deep_saturating"])
 def test_tile_order_leaves_outputs_unchanged(name):
     """The first render of a context takes the tiles in index order, the next one in the
     order the first measured (longest first), and the traversals after each render in
@@ -341,5 +349,43 @@ def test_rejected_project_leaves_the_context_unchanged():
         got = r.score_replay(obs)
         torch.cuda.synchronize()
         assert torch.equal(got, want)
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("name", ["deep_saturating", "c2_small"])
+def test_workspace_contents_are_never_assumed(name):
+    """A workspace filled with 0xff bytes before the first call (so that every event byte past the entries the
+    render processes names all four waves) gives the oracle's outputs, and a second step and a second
+    backward on it are bit-identical to the first: the traversals after the render read only the entries it
+    processed."""
+    sc, obs, ref, _ = _case(name)
+    b = _binding()
+    r = b.rasterizer_for_scene(sc)
+    try:
+        r.workspace.fill_(255)
+        torch.cuda.synchronize()
+        obs_d = torch.from_numpy(obs).cuda()
+        gC = torch.from_numpy(np.random.default_rng(7).uniform(-1, 1, size=obs.shape).astype(np.float32)).cuda()
+        outs, grads = [], []
+        for _ in range(2):
+            (color, T, n), tok = r.step(obs_d)
+            g = r.backward(gC)
+            torch.cuda.synchronize()
+            outs.append([x.cpu().numpy().copy() for x in (color, T, n, tok)])
+            grads.append({k: v.cpu().numpy().copy() for k, v in g.items()})
+        color, T, n, tok = outs[0]
+        assert np.array_equal(n, ref["n"]) and np.array_equal(T.view(np.uint32), ref["T"].view(np.uint32))
+        assert np.abs(color - ref["color"]).max() <= COLOR_ATOL
+        z, zr = tok.astype(np.float64), ref["tokens"]
+        rel = np.linalg.norm(z - zr, axis=1) / np.maximum(np.linalg.norm(zr, axis=1), 1e-6)
+        assert rel.max() <= TOKEN_RTOL, rel.max()
+        blocks = oracle.token_block_errors(ref["oracle"], z, zr, catol=COLOR_ATOL)
+        assert all(v[0] <= 1.0 for v in blocks.values()), blocks
+        for a, c in zip(outs[0], outs[1]):
+            assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  c.view(np.uint32) if c.dtype == np.float32 else c)
+        for k in grads[0]:
+            assert np.array_equal(grads[0][k].view(np.uint32), grads[1][k].view(np.uint32)), k
     finally:
         r.close()
