@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
     __shared__ float4 s0[kAttrBatch];
     __shared__ float2 s1[kAttrBatch];
     __shared__ float sf[kAttrBatch][NC];
+    __shared__ uint32_t s_gid[kAttrBatch];
     __shared__ uint8_t s_evb[kAttrBatch];
     __shared__ uint8_t slist[4][kAttrBatch];
 
@@ -79,11 +80,16 @@ __global__ __launch_bounds__(256) void k_render_features(const uint2* __restrict
             const float4 b = rec1[rid];
             s1[threadIdx.x] = make_float2(b.x, b.y);
             s_evb[threadIdx.x] = events[i];
-            const float* fg = feat + (int64_t)g * C + c0;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) sf[threadIdx.x][c] = c < nc ? fg[c] : 0.0f;
+            s_gid[threadIdx.x] = g;
         }
         const int cnt = (int)min((uint32_t)kAttrBatch, rend - base);
+        __syncthreads();
+        // the staged entries' channels, one float per thread in row-major order: consecutive threads write
+        // consecutive LDS words (no bank conflicts) and read each Gaussian's channels as one contiguous run
+        for (int f = threadIdx.x; f < cnt * NC; f += 256) {
+            const int j = f / NC, c = f % NC;
+            sf[j][c] = c < nc ? feat[(int64_t)s_gid[j] * C + c0 + c] : 0.0f;
+        }
         __syncthreads();
         if (__ballot(!done) != 0ull) {
             int nw = 0;
