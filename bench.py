@@ -88,9 +88,11 @@ def stage_bytes(stage, c):
     pk = 4 if c["packable"] else 0   # the rectangle packed to 32 bits by preprocess for the depth sort
     if stage == "project":       # Gaussian parameters in; 48-byte record, rectangle, depth key, tile count out
         return G * (4 * 3 + 4 * 4 + 4 * 3 + 4 + 4 * 3 * d) + VG * (48 + 8 + 4 + 4 + pk)
-    if stage == "depth_sort":    # slot scan 8, histogram 4, pass 0 (key+rect in, key+id+rect out) 24 (20 with the
-        return VG * (8 + 4 + 24 - pk + 2 * 24 + 28 - 2 * pk)  # packed rect), passes 1-2 24 each, pass 3 (-> id and
-                                                               # rect + count 28, or id and packed rect 20)
+    if stage == "depth_sort":    # slot scan 8, histogram 4, then with carried packed rectangles: pass 0 (key+rect
+        if pk:                   # in, key+id+rect out) 20, passes 1-2 24 each, pass 3 (key+id+rect in, id and rect out) 20
+            return VG * (8 + 4 + 20 + 2 * 24 + 20)
+        # gathered: pass 0 (key in, key+id out) 12, passes 1-2 16 each, pass 3 (key+id in, id out, the 8-byte
+        return VG * (8 + 4 + 12 + 2 * 16 + 32)   # rectangle gathered by record, rectangle + tile count out) 32
     if stage == "scan":
         return VG * 8
     if stage == "emit":          # per record: id, rect, tile count, offset in; per pair: tile key and Gaussian out
@@ -284,7 +286,7 @@ def measure(config, args, dev, stream, steps, warmup, extras):
     bits_for = lambda x: max(int(x - 1).bit_length(), 1)
     c = dict(G=sc.n, V=V, d=sc.d, P=P, T=T_tiles, n_live=n_live,
              packed=bits_for(V * T_tiles) + bits_for(sc.n) <= 32,
-             packable=(W + 15) // 16 <= 256 and (H + 15) // 16 <= 256)
+             packable=(W + 15) // 16 <= 256 and (H + 15) // 16 <= 256 and sc.n * V > (1 << 19))
     stages = {k: (ms / max(cnt, 1), cnt) for k, (ms, cnt) in prof.items() if cnt > 0}
     # The dominant single kernel is the score replay (one launch per step, the "replay" stage); its duration
     # is the one measured live over the timed steps.  Bound: fp32 VALU (each gathered record is evaluated by up

@@ -209,6 +209,13 @@ size_t carve_workspace(const Sizes& s, char* base, Workspace* ws) {
 
 namespace {
 
+// The depth sort carries the tile rectangles through its passes, packed to 32 bits, for tile grids of at most
+// 256 x 256 and more than kTinySortKeys records; it gathers them by record in its last pass otherwise (too wide to
+// pack, or so few records that a pass is latency-bound and the carry's second reorder costs more than the
+// gather: 68 against 72 us for the depth sort of the 311,296-record 512x960 compact scene, while the gather costs
+// 0.38 against 0.29 ms for the 7.3 M records of the 8-view 256x448 step).
+bool carries_packed_rects(const gsr::Sizes& s) { return s.TX <= 256 && s.TY <= 256 && s.VG > gsr::kTinySortKeys; }
+
 gs_status check_dims(const gs_dims* d) {
     if (!d) return fail(GS_ERR_INVALID_ARGUMENT, "dims is null");
     if (d->n_gaussians < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n_gaussians < 0");
@@ -322,9 +329,9 @@ gs_status gs_project(gs_context* ctx, const gs_gaussians* sc, const gs_camera* c
     ctx->params = *params;
     ctx->state = kCreated;
     ctx->timer.begin(GS_STAGE_PROJECT, stream);
-    // tile grids of at most 256 x 256: the depth sort's first pass reads the rectangles packed by preprocess
-    // (into the depth-ordered tile counts' array, which the sort's last pass writes only afterwards)
-    const bool packable = s.TX <= 256 && s.TY <= 256;
+    // the depth sort's first pass reads the rectangles packed by preprocess (into the depth-ordered tile counts'
+    // array, which the sort's last pass writes only afterwards) when it carries them
+    const bool packable = carries_packed_rects(s);
     hipError_t e = launch_project(*sc, ctx->cams, s, params->near_plane, params->far_plane, params->antialiased,
                                   packable ? ctx->ws.tt_sorted : nullptr, ctx->ws, stream);
     if (e != hipSuccess) return hip_fail(e, "project");
@@ -381,7 +388,7 @@ gs_status bin_sort_impl(gs_context* ctx, hipStream_t stream, uint64_t* n_pairs_o
     //    scan rewrites next); the tile rectangles ride along (packed, or gathered by the last pass), and
     //    the last pass writes rectangles and tile counts in depth order but no keys
     uint32_t* rid_sorted = nullptr;
-    const bool packable = s.TX <= 256 && s.TY <= 256;
+    const bool packable = carries_packed_rects(s);
     // (a second sort after one gs_project packs on load: the first sort's last pass overwrote the packed form)
     // for such grids the last pass leaves the packed rectangles (in depth order) in tt_sorted, from which the
     // offsets scan and emit take the tile counts and rectangles
