@@ -65,7 +65,9 @@ struct StageTimer {
     hipEvent_t take() {
         if (pool.empty()) {
             hipEvent_t e = nullptr;
-            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            // timing only: no system-scope fence (cache write-back) at the record, which would idle the GPU
+            // between the stages and count that write-back in the stage's time
+            if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
             return e;
         }
         hipEvent_t e = pool.back();
